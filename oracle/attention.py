@@ -1,0 +1,125 @@
+"""fp64 reference for PagedAttention decode.
+
+What is computed (PagedAttention: The vLLM Paper, "Background and Motivation":
+each new token attends over all previous tokens; "The Core Idea": attention is
+computed through block-table indirection over non-contiguous blocks;
+vLLM: PagedAttention and continuous batching, "Direct answer": PagedAttention
+follows the logical->physical block mapping while computing attention).  Paging
+changes where K/V live, not the attention result, so the oracle gathers each
+sequence's tokens back into contiguous arrays and applies the textbook
+definition softmax(q K^T * scale) V in fp64.
+
+Readings where the pages are silent:
+  * pool layout (the library's ABI): K pool [N, Hkv, D/x, B, x] and V pool
+    [N, Hkv, D, B], x = elements per 16 bytes; token at logical position t of a
+    sequence lives in physical block table[t // B], slot t % B;
+  * L_s counts every cached token including the one written this step;
+  * query head h reads KV head h // (Hq / Hkv) (consecutive heads share);
+  * bf16 values are held as raw uint16 bit patterns and widened exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening: float32 -> fp64, or bf16 bit patterns (uint16) -> fp64."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype == np.float32 or a.dtype == np.float64:
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported element type {a.dtype}")
+
+
+def gather_kv(k_pool, v_pool, table, L: int, g: int):
+    """Contiguous K, V [L, D] (fp64) of one sequence and KV head `g`.
+
+    Logical block j of the sequence is physical block table[j]; it holds
+    tokens j*B .. j*B+B-1, of which only the first L - j*B are valid when it is
+    the last block (only the last block may be partially filled)."""
+    N, Hkv, Dx, B, x = k_pool.shape
+    D = Dx * x
+    K = np.empty((L, D), dtype=np.float64)
+    V = np.empty((L, D), dtype=np.float64)
+    nblocks = -(-L // B)
+    for j in range(nblocks):
+        pb = int(table[j])
+        n = min(B, L - j * B)
+        # K block [D/x, B, x] -> tokens x dims
+        kb = k_pool[pb, g, :, :n, :]                 # [D/x, n, x]
+        K[j * B:j * B + n] = to_f64(np.transpose(kb, (1, 0, 2)).reshape(n, D))
+        vb = v_pool[pb, g, :, :n]                    # [D, n]
+        V[j * B:j * B + n] = to_f64(vb.T)
+    return K, V
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(q K^T * scale) V for one query vector, fp64, max-subtracted."""
+    z = (K @ q) * scale
+    z = z - z.max()
+    p = np.exp(z)
+    return (p @ V) / p.sum()
+
+
+def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale=None,
+                           rows=None):
+    """Decode attention for every (sequence, query head), or only `rows`
+    (a list of (s, h) pairs).  Returns fp64 [S, Hq, D] (unsampled rows are NaN)."""
+    S, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.full((S, Hq, D), np.nan)
+    want = None if rows is None else {}
+    if rows is not None:
+        for s, h in rows:
+            want.setdefault(int(s), set()).add(int(h))
+    qf = to_f64(q)
+    for s in range(S):
+        if want is not None and s not in want:
+            continue
+        L = int(context_lens[s])
+        for g in range(Hkv):
+            heads = [h for h in range(g * G, (g + 1) * G) if want is None or h in want[s]]
+            if not heads:
+                continue
+            K, V = gather_kv(k_pool, v_pool, block_tables[s], L, g)
+            for h in heads:
+                out[s, h] = attention(qf[s, h], K, V, scale)
+    return out
+
+
+def partition_partials(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, P: int):
+    """Split the context into partitions of P tokens and return, per partition,
+    (m, l, acc): the max score, the sum of exp(score - m) and the unnormalised
+    exp-weighted sum of V rows.  This split is not on the pages; it is the
+    standard way to cut one long context across many workgroups."""
+    L = K.shape[0]
+    parts = []
+    for start in range(0, L, P):
+        z = (K[start:start + P] @ q) * scale
+        m = z.max()
+        p = np.exp(z - m)
+        parts.append((m, p.sum(), p @ V[start:start + P]))
+    return parts
+
+
+def combine_partials(parts) -> np.ndarray:
+    """Log-sum-exp combine: rescale each partition to the global max M, then
+    divide the summed numerators by the summed denominators."""
+    M = max(m for m, _, _ in parts)
+    num = sum(np.exp(m - M) * acc for m, _, acc in parts)
+    den = sum(np.exp(m - M) * l for m, l, _ in parts)
+    return num / den
+
+
+def valid_slot_mask(block_tables, context_lens, num_blocks: int, B: int) -> np.ndarray:
+    """bool [N, B]: which (physical block, slot) pairs hold a token of some
+    sequence.  Everything else is free or past a sequence's end."""
+    mask = np.zeros((num_blocks, B), dtype=bool)
+    for table, L in zip(block_tables, context_lens):
+        L = int(L)
+        for t in range(L):
+            mask[int(table[t // B]), t % B] = True
+    return mask

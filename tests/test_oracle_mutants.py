@@ -1,0 +1,105 @@
+"""Planted mistakes: each plausible slip in the oracle must fail some pin.
+
+Every mutant below is a copy of an oracle function with one deliberate error
+(wrong GQA head map, transposed K block, dropped scale, one token short, LIFO
+free list, a CoW that forgets to release its source).  The pins are re-run
+against the mutant and at least one of them has to fail."""
+import numpy as np
+import pytest
+
+import oracle.attention as oa
+import oracle.block_manager as obm
+import tests.test_oracle_attention as ta
+import tests.test_oracle_block_manager as tb
+
+
+def _mutant_decode(head_of=None, drop_scale=False, short=False):
+    def decode(q, k_pool, v_pool, block_tables, context_lens, scale=None, rows=None):
+        S, Hq, D = q.shape
+        Hkv = k_pool.shape[1]
+        G = Hq // Hkv
+        if scale is None or drop_scale:
+            scale = 1.0 if drop_scale else 1.0 / np.sqrt(D)
+        out = np.full((S, Hq, D), np.nan)
+        qf = oa.to_f64(q)
+        for s in range(S):
+            L = int(context_lens[s]) - (1 if short and int(context_lens[s]) > 1 else 0)
+            for h in range(Hq):
+                g = head_of(h, G, Hkv) if head_of else h // G
+                K, V = oa.gather_kv(k_pool, v_pool, block_tables[s], L, g)
+                out[s, h] = oa.attention(qf[s, h], K, V, scale)
+        return out
+    return decode
+
+
+def _gather_transposed(k_pool, v_pool, table, L, g):
+    N, Hkv, Dx, B, x = k_pool.shape
+    D = Dx * x
+    K = np.empty((L, D))
+    V = np.empty((L, D))
+    for j in range(-(-L // B)):
+        pb, n = int(table[j]), min(B, L - j * B)
+        K[j * B:j * B + n] = oa.to_f64(k_pool[pb, g].reshape(B, D)[:n])   # wrong: no transpose
+        V[j * B:j * B + n] = oa.to_f64(v_pool[pb, g, :, :n].T)
+    return K, V
+
+
+def _attention_pins():
+    ta.test_paged_equals_contiguous_sdpa("bf16", 16, 4)
+    ta.test_paged_equals_contiguous_sdpa("f32", 16, 1)
+    ta.test_brute_force_scalar_loops()
+    ta.test_gqa_head_map()
+
+
+@pytest.mark.parametrize("mutant", ["head_mod", "no_scale", "short"])
+def test_attention_mutants_fail_pins(monkeypatch, mutant):
+    dec = {"head_mod": _mutant_decode(head_of=lambda h, G, Hkv: h % Hkv),
+           "no_scale": _mutant_decode(drop_scale=True),
+           "short": _mutant_decode(short=True)}[mutant]
+    monkeypatch.setattr(ta, "paged_attention_decode", dec)
+    with pytest.raises(AssertionError):
+        _attention_pins()
+
+
+def test_transposed_gather_fails_pins(monkeypatch):
+    monkeypatch.setattr(oa, "gather_kv", _gather_transposed)
+    with pytest.raises(AssertionError):
+        ta.test_paged_equals_contiguous_sdpa("bf16", 16, 4)
+
+
+class _LifoBM(obm.BlockManager):
+    def _take(self):
+        b = self.free.pop()
+        self.ref[b] = 1
+        return b
+
+
+class _LeakyCowBM(obm.BlockManager):
+    def append_slot(self, sid):
+        if sid not in self.tables:
+            raise obm.BMError(obm.ENOSEQ)
+        table, L, B = self.tables[sid], self.lens[sid], self.B
+        if L % B and self.ref[table[-1]] > 1:
+            if not self.free:
+                raise obm.BMError(obm.ENOBLOCKS)
+            dst = self._take()                  # forgets ref[src] -= 1
+            src = table[-1]
+            table[-1] = dst
+            slot = dst * B + L % B
+            self.lens[sid] = L + 1
+            return slot, src, dst
+        return super().append_slot(sid)
+
+
+@pytest.mark.parametrize("cls", [_LifoBM, _LeakyCowBM])
+def test_block_manager_mutants_fail_pins(monkeypatch, cls):
+    monkeypatch.setattr(tb, "BlockManager", cls)
+    failed = 0
+    for pin in (tb.test_block_pool_figure, tb.test_copy_on_write_fork,
+                lambda: tb.test_invariants_random_scripts(0),
+                lambda: tb.test_invariants_random_scripts(1)):
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0
