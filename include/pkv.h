@@ -1,0 +1,203 @@
+/*
+ * pkv.h -- C ABI of the PagedAttention decode library (libpkv.so, MI355X / gfx950).
+ *
+ * What the library does comes from three accounts of "Efficient Memory Management
+ * for Large Language Model Serving with PagedAttention" (Kwon, Li et al., SOSP 2023):
+ *   [RTI]  "PagedAttention and Continuous Batching" (roadtointelligence.com)
+ *   [LLMS] "vLLM: PagedAttention and continuous batching" (llmstudy)
+ *   [ZENO] "PagedAttention: The vLLM Paper" (zenoagi)
+ * Each entry point below names the passage that defines its operation.
+ *
+ * Conventions shared by every call
+ *   - Every call returns pkv_status (PKV_OK == 0); pkv_status_string() names it.
+ *   - Host validation runs before any launch; a rejected call changes nothing.
+ *   - The library never allocates device memory.  Pools, tables, outputs and
+ *     workspace are owned by the caller (the pool is allocated once, up front:
+ *     [ZENO] "Implementation Essentials", pre-allocated memory pool).  The only
+ *     memory the library owns is the host heap behind a pkv_bm handle.
+ *   - Device calls take raw device pointers and a hipStream_t (passed as void*,
+ *     NULL = the null stream); they are asynchronous with respect to the host and
+ *     ordered on that stream.  Device pointers must be 16-byte aligned.
+ *   - Device-side indices (block-table entries, slots, copy pairs) cannot be
+ *     checked on the host without a sync.  The kernels never access memory
+ *     outside the buffers described here: out-of-range block ids are clamped
+ *     into [0, num_blocks) and out-of-range slots or pairs are skipped.  The
+ *     numerical result of such a call is undefined.
+ *
+ * KV pool layout (a choice of this library; the pages do not fix one)
+ *   x = 16 / sizeof(element): 8 for bf16, 4 for fp32.
+ *   K pool: [num_blocks, Hkv, D/x, B, x]   element (b, h, t, d) at
+ *           ((b*Hkv + h)*(D/x) + d/x)*B*x + t*x + d%x
+ *   V pool: [num_blocks, Hkv, D, B]        element (b, h, t, d) at
+ *           ((b*Hkv + h)*D + d)*B + t
+ *   (b = physical block, h = KV head, t = slot within the block, d = dim.)
+ *   One (block, head) is a contiguous B*D run in both pools.  The K layout keeps
+ *   16 bytes of one token's dims together; the V layout keeps each dim's B
+ *   tokens together, so both operands of the attention contraction load as
+ *   whole 16-byte vectors.
+ *   A token at logical position t of a sequence lives in physical block
+ *   block_table[t / B], slot t % B; its slot number is block*B + t % B.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* bad argument (null pointer, size, alignment, bad id) */
+  PKV_ENOBLOCKS = -2,     /* not enough free blocks; block-manager state unchanged */
+  PKV_ENOSEQ = -3,        /* unknown sequence id */
+  PKV_EEXIST = -4,        /* sequence id already in use */
+  PKV_EUNSUPPORTED = -5,  /* shape or dtype without a compiled kernel */
+  PKV_EHIP = -6           /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+const char* pkv_status_string(pkv_status s);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager ([ZENO] "Implementation Essentials": a pre-allocated pool,
+ * block allocation and reclamation, refcounts that let sequences share blocks;
+ * [RTI] "The solution" and "Pages, from operating systems": fixed-size blocks,
+ * a per-request block table, blocks allocated as tokens are generated, shared
+ * blocks copied only when one sharer writes them; [ZENO] "The Core Idea":
+ * blocks claimed on demand, returned when done, reusable by any request, and
+ * only the last block of a sequence partially filled).
+ *
+ * Semantics fixed by this library where the pages are silent:
+ *   - free blocks form a FIFO queue; its initial order is given at creation
+ *     (NULL = ascending) and freed blocks are appended in release order;
+ *   - add_seq is all-or-nothing; every failing call leaves the state unchanged;
+ *   - append_slot: when the length is a multiple of B a new private block is
+ *     taken; otherwise, if the last block is shared (refcount > 1), a new block
+ *     dst is taken, the pair (src, dst) is returned for the device copy
+ *     (pkv_copy_blocks, to be ordered before the token's cache write), src loses
+ *     one reference and dst replaces it in the table; a private last block is
+ *     written in place.
+ * A handle is not thread-safe: one scheduler thread owns it.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_bm pkv_bm;
+
+/* Create a manager for num_blocks blocks of block_size tokens.  init_free_order
+ * (host, num_blocks entries, a permutation of 0..num_blocks-1) or NULL. */
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t* init_free_order, pkv_bm** out);
+void pkv_bm_destroy(pkv_bm* bm);
+
+/* Admit sequence seq_id holding num_tokens (>= 0) tokens: ceil(n/B) blocks. */
+pkv_status pkv_bm_add_seq(pkv_bm* bm, int64_t seq_id, int32_t num_tokens);
+
+/* Reserve the slot of the sequence's next token.  *slot = block*B + offset;
+ * *cow_src / *cow_dst = the block pair to copy first, or -1 / -1. */
+pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq_id, int64_t* slot,
+                              int32_t* cow_src, int32_t* cow_dst);
+
+/* append_slot for n sequences in order (one decode step).  slots[n] receives each
+ * slot; cow_pairs[2*k], cow_pairs[2*k+1] the k-th copy (room for n pairs);
+ * *n_cow the number of copies; *n_done the sequences processed.  Stops at the
+ * first failure and returns its status (the first *n_done appends stand). */
+pkv_status pkv_bm_append_slots(pkv_bm* bm, const int64_t* seq_ids, int32_t n,
+                               int64_t* slots, int32_t* cow_pairs, int32_t* n_cow,
+                               int32_t* n_done);
+
+/* Share the parent's blocks with a new sequence (parallel sampling): the child
+ * gets a copy of the table and every block gains one reference. */
+pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent_id, int64_t child_id);
+
+/* Finish a sequence: each block loses one reference; blocks reaching zero go to
+ * the back of the free queue in logical order. */
+pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id);
+
+pkv_status pkv_bm_num_free(const pkv_bm* bm, int32_t* out);
+pkv_status pkv_bm_refcount(const pkv_bm* bm, int32_t block, int32_t* out);
+pkv_status pkv_bm_seq_info(const pkv_bm* bm, int64_t seq_id, int32_t* len, int32_t* nblocks);
+/* Copy the sequence's table into out[cap]; PKV_EINVAL if cap is too small. */
+pkv_status pkv_bm_block_table(const pkv_bm* bm, int64_t seq_id, int32_t* out, int32_t cap);
+
+/* Host arrays for a decode batch: block_tables[n*max_blocks] (row i = seq_ids[i],
+ * padded with -1) and context_lens[n]. */
+pkv_status pkv_bm_fill_batch(const pkv_bm* bm, const int64_t* seq_ids, int32_t n,
+                             int32_t max_blocks, int32_t* block_tables,
+                             int32_t* context_lens);
+
+/* Whole-pool state for parity checks: refcounts[num_blocks] and the free queue
+ * front to back in free_queue[0 .. *n_free) (room for num_blocks entries). */
+pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_queue,
+                           int32_t* n_free);
+
+/* ---------------------------------------------------------------------------
+ * Device operations.
+ * ------------------------------------------------------------------------- */
+
+/* Write each new token's K/V into its slot ([ZENO] "Background and Motivation":
+ * every generated token adds K/V vectors to the cache; [RTI] "Pages, from
+ * operating systems": blocks are allocated as tokens are generated).
+ *   key, value    device [T, Hkv, D], pool dtype
+ *   k_pool/v_pool device pools (layout above), updated in place
+ *   slot_mapping  device int64 [T]; slot < 0 = skip; slot >= num_blocks*B skipped
+ * A bit copy: no conversion, NaN payloads kept.  Two tokens with the same slot
+ * in one call race (caller's responsibility). */
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
+                                 void* v_pool, const int64_t* slot_mapping, int32_t T,
+                                 int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                                 pkv_dtype dtype, void* hip_stream);
+
+/* Copy-on-write block copies ([RTI] "Pages, from operating systems": shared
+ * blocks are copied only when one sequence needs to modify them; [ZENO] OS-paging
+ * analogy table: page sharing with fork and copy-on-write).  For each pair k,
+ * block pairs[2k+1] := block pairs[2k] in both pools (all heads, all slots).
+ *   pairs  device int32 [n, 2] (src, dst); a pair with an id outside
+ *          [0, num_blocks) is skipped.  dst ids must be distinct and must not
+ *          appear as a src in the same call (the copies run concurrently). */
+pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n,
+                           int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
+                           pkv_dtype dtype, void* hip_stream);
+
+/* Bytes of workspace pkv_paged_attention_decode needs: 0 when every sequence
+ * fits one partition, else S*Hq*nparts*(D+2)*4 with
+ * nparts = ceil(max_context_len / partition) (partition_size 0 = default 512). */
+size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
+                                     int32_t max_context_len, int32_t partition_size);
+
+/* Decode attention through the block table ([LLMS] "Direct answer":
+ * PagedAttention follows the logical-to-physical block mapping while computing
+ * attention; [ZENO] "The Core Idea": attention computed through block-table
+ * indirection, reading KV non-contiguously; [ZENO] "Background and Motivation":
+ * each new token attends over all previous tokens).
+ *   out           device fp32 [S, Hq, D]: softmax(q K^T * scale) V per (s, h)
+ *   q             device [S, Hq, D], pool dtype
+ *   block_tables  device int32 [S, max_blocks]
+ *   context_lens  device int32 [S]: tokens of sequence s (the one written this
+ *                 step included); 0 gives a zero row; at most
+ *                 min(max_context_len, max_blocks*B) (larger values are clamped
+ *                 to max_blocks*B and tokens past max_context_len are not read)
+ *   Query head h reads KV head h / (Hq/Hkv).
+ *   max_context_len  host-known bound on context_lens; sizes the grid (no sync)
+ *   scale         score scale, usually 1/sqrt(D)
+ *   partition_size   tokens per workgroup partition: 0 = default (512), else a
+ *                 positive multiple of 32 and of B.  Sequences longer than one
+ *                 partition are split and merged by a log-sum-exp reduce launch.
+ *   workspace     device buffer of workspace_bytes >= pkv_attention_workspace_bytes
+ *                 (may be NULL when that is 0)
+ * Compiled shapes: D in {64, 128}, B in {16, 32}; bf16 with Hq/Hkv in
+ * {1, 2, 4, 8}; fp32 with Hq/Hkv in {1, 2, 4, 8}.  Others: PKV_EUNSUPPORTED. */
+pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t S, int32_t Hq,
+                                      int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
+                                      int32_t num_blocks, int32_t max_context_len,
+                                      float scale, int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, pkv_dtype dtype,
+                                      void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

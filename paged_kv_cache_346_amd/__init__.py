@@ -1,0 +1,306 @@
+"""PagedAttention decode for AMD MI355X (gfx950): Python binding of libpkv.so.
+
+Argument marshalling only.  Every step of the path runs inside the library:
+the HIP kernels (reshape_and_cache, copy_blocks, paged_attention_decode) and the
+host block manager (allocate, free, refcount, fork, copy-on-write).  PyTorch
+supplies device memory and the current stream.  The names match the C entry
+points declared in include/pkv.h (short aliases without the pkv_ prefix are
+provided too).  There is no fallback: if libpkv.so is missing, importing this
+package raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch  # imported before the library so both share torch's HIP runtime
+
+__all__ = [
+    "PkvError", "BlockManager", "pkv_reshape_and_cache", "pkv_copy_blocks",
+    "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pool_shapes",
+    "reshape_and_cache", "copy_blocks", "attention_workspace_bytes", "paged_attention_decode",
+    "LIB_PATH", "lib",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_ENOBLOCKS, PKV_ENOSEQ, PKV_EEXIST, PKV_EUNSUPPORTED, PKV_EHIP = (
+    0, -1, -2, -3, -4, -5, -6)
+PKV_F32, PKV_BF16 = 0, 1
+
+_i32, _i64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                              ctypes.c_size_t)
+_pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+
+# name -> (restype, argtypes); mirrors include/pkv.h
+SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [_i32]),
+    "pkv_bm_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_vp)]),
+    "pkv_bm_destroy": (None, [_vp]),
+    "pkv_bm_add_seq": (_i32, [_vp, _i64, _i32]),
+    "pkv_bm_append_slot": (_i32, [_vp, _i64, _pi64, _pi32, _pi32]),
+    "pkv_bm_append_slots": (_i32, [_vp, _pi64, _i32, _pi64, _pi32, _pi32, _pi32]),
+    "pkv_bm_fork": (_i32, [_vp, _i64, _i64]),
+    "pkv_bm_free_seq": (_i32, [_vp, _i64]),
+    "pkv_bm_num_free": (_i32, [_vp, _pi32]),
+    "pkv_bm_refcount": (_i32, [_vp, _i32, _pi32]),
+    "pkv_bm_seq_info": (_i32, [_vp, _i64, _pi32, _pi32]),
+    "pkv_bm_block_table": (_i32, [_vp, _i64, _pi32, _i32]),
+    "pkv_bm_fill_batch": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
+    "pkv_bm_snapshot": (_i32, [_vp, _pi32, _pi32, _pi32]),
+    "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _vp]),
+    "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
+                                          _vp]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_346_amd.build`")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = int(code)
+        super().__init__(f"{where}: {lib.pkv_status_string(self.code).decode()}")
+
+
+def _check(code: int, where: str) -> None:
+    if code != PKV_OK:
+        raise PkvError(code, where)
+
+
+def _np_ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# ---------------------------------------------------------------------------
+# host block manager
+# ---------------------------------------------------------------------------
+class BlockManager:
+    """Owner of a pkv_bm handle: the pool's refcounts, free queue and tables."""
+
+    def __init__(self, num_blocks: int, block_size: int, init_free_order=None):
+        h = _vp()
+        order = None
+        if init_free_order is not None:
+            order = np.ascontiguousarray(init_free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("init_free_order must hold num_blocks entries")
+        _check(lib.pkv_bm_create(num_blocks, block_size,
+                                 None if order is None else _np_ptr(order, ctypes.c_int32),
+                                 ctypes.byref(h)), "pkv_bm_create")
+        self._h = h
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_seq(self, seq_id: int, num_tokens: int) -> None:
+        _check(lib.pkv_bm_add_seq(self._h, seq_id, num_tokens), "pkv_bm_add_seq")
+
+    def append_slot(self, seq_id: int):
+        slot, src, dst = _i64(), _i32(), _i32()
+        _check(lib.pkv_bm_append_slot(self._h, seq_id, ctypes.byref(slot), ctypes.byref(src),
+                                      ctypes.byref(dst)), "pkv_bm_append_slot")
+        return slot.value, src.value, dst.value
+
+    def append_slots(self, seq_ids):
+        """One decode step: (slots int64 [n], cow pairs int32 [k, 2])."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        slots = np.empty(n, np.int64)
+        pairs = np.empty((max(n, 1), 2), np.int32)
+        n_cow, n_done = _i32(), _i32()
+        _check(lib.pkv_bm_append_slots(self._h, _np_ptr(ids, ctypes.c_int64), n,
+                                       _np_ptr(slots, ctypes.c_int64),
+                                       _np_ptr(pairs, ctypes.c_int32), ctypes.byref(n_cow),
+                                       ctypes.byref(n_done)), "pkv_bm_append_slots")
+        return slots, pairs[:n_cow.value].copy()
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        _check(lib.pkv_bm_fork(self._h, parent_id, child_id), "pkv_bm_fork")
+
+    def free_seq(self, seq_id: int) -> None:
+        _check(lib.pkv_bm_free_seq(self._h, seq_id), "pkv_bm_free_seq")
+
+    def num_free(self) -> int:
+        out = _i32()
+        _check(lib.pkv_bm_num_free(self._h, ctypes.byref(out)), "pkv_bm_num_free")
+        return out.value
+
+    def refcount(self, block: int) -> int:
+        out = _i32()
+        _check(lib.pkv_bm_refcount(self._h, block, ctypes.byref(out)), "pkv_bm_refcount")
+        return out.value
+
+    def seq_info(self, seq_id: int):
+        ln, nb = _i32(), _i32()
+        _check(lib.pkv_bm_seq_info(self._h, seq_id, ctypes.byref(ln), ctypes.byref(nb)),
+               "pkv_bm_seq_info")
+        return ln.value, nb.value
+
+    def block_table(self, seq_id: int):
+        _, nb = self.seq_info(seq_id)
+        out = np.empty(max(nb, 1), np.int32)
+        _check(lib.pkv_bm_block_table(self._h, seq_id, _np_ptr(out, ctypes.c_int32), nb),
+               "pkv_bm_block_table")
+        return out[:nb].tolist()
+
+    def fill_batch(self, seq_ids, max_blocks: int):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        tables = np.empty((n, max_blocks), np.int32)
+        lens = np.empty(n, np.int32)
+        _check(lib.pkv_bm_fill_batch(self._h, _np_ptr(ids, ctypes.c_int64), n, max_blocks,
+                                     _np_ptr(tables, ctypes.c_int32),
+                                     _np_ptr(lens, ctypes.c_int32)), "pkv_bm_fill_batch")
+        return tables, lens
+
+    def snapshot(self):
+        ref = np.empty(self.num_blocks, np.int32)
+        fq = np.empty(self.num_blocks, np.int32)
+        nf = _i32()
+        _check(lib.pkv_bm_snapshot(self._h, _np_ptr(ref, ctypes.c_int32),
+                                   _np_ptr(fq, ctypes.c_int32), ctypes.byref(nf)),
+               "pkv_bm_snapshot")
+        return ref.tolist(), fq[:nf.value].tolist()
+
+
+# ---------------------------------------------------------------------------
+# device operations
+# ---------------------------------------------------------------------------
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def pool_shapes(num_blocks: int, Hkv: int, D: int, B: int, dtype: torch.dtype):
+    """Tensor shapes of the K and V pools (K [N, Hkv, D/x, B, x], V [N, Hkv, D, B])."""
+    x = 16 // (4 if dtype == torch.float32 else 2)
+    return (num_blocks, Hkv, D // x, B, x), (num_blocks, Hkv, D, B)
+
+
+def _pool_geometry(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    if k_pool.dim() != 5 or v_pool.dim() != 4:
+        raise ValueError("k_pool must be [N, Hkv, D/x, B, x] and v_pool [N, Hkv, D, B]")
+    N, Hkv, Dx, B, x = k_pool.shape
+    D = Dx * x
+    if tuple(v_pool.shape) != (N, Hkv, D, B) or k_pool.dtype != v_pool.dtype:
+        raise ValueError("k_pool and v_pool disagree in shape or dtype")
+    if x * k_pool.element_size() != 16:
+        raise ValueError("k_pool's last dim must span 16 bytes")
+    return N, Hkv, D, B
+
+
+def pkv_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, stream=None) -> None:
+    """Write token i's K/V ([T, Hkv, D]) into slot slot_mapping[i] (int64; <0 skips)."""
+    N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise ValueError("key/value must be [T, Hkv, D]")
+    if key.dtype != k_pool.dtype or value.dtype != k_pool.dtype:
+        raise ValueError("key/value dtype must match the pools")
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    _check(lib.pkv_reshape_and_cache(_dev(key, "key"), _dev(value, "value"),
+                                     _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                     _dev(slot_mapping, "slot_mapping"), T, Hkv, D, B, N,
+                                     _dtype_code(k_pool), _stream(stream)),
+           "pkv_reshape_and_cache")
+
+
+def pkv_copy_blocks(k_pool, v_pool, pairs, stream=None) -> None:
+    """Copy block pairs[k, 0] onto pairs[k, 1] in both pools (int32 [n, 2] on device)."""
+    N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [n, 2]")
+    n = pairs.shape[0]
+    if n == 0:
+        return
+    _check(lib.pkv_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                               _dev(pairs, "pairs"), n, Hkv, D, B, N, _dtype_code(k_pool),
+                               _stream(stream)), "pkv_copy_blocks")
+
+
+def pkv_attention_workspace_bytes(S: int, Hq: int, D: int, max_context_len: int,
+                                  partition_size: int = 0) -> int:
+    return int(lib.pkv_attention_workspace_bytes(S, Hq, D, max_context_len, partition_size))
+
+
+def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
+                               max_context_len: int, scale: float | None = None,
+                               partition_size: int = 0, workspace=None, stream=None) -> None:
+    """out[s, h] = softmax(q[s, h] K_s^T * scale) V_s through the block tables.
+
+    out fp32 [S, Hq, D]; q [S, Hq, D] in the pool dtype; block_tables int32
+    [S, max_blocks]; context_lens int32 [S].  `workspace` (a uint8 device tensor)
+    is needed when max_context_len exceeds one partition."""
+    N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
+    S, Hq = q.shape[0], q.shape[1]
+    if tuple(q.shape) != (S, Hq, D) or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [S, Hq, D] in the pool dtype")
+    if out.dtype != torch.float32 or tuple(out.shape) != (S, Hq, D):
+        raise ValueError("out must be float32 [S, Hq, D]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S, max_blocks]")
+    if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B,
+        block_tables.shape[1], N, int(max_context_len), float(scale), int(partition_size), ws_ptr,
+        ws_bytes, _dtype_code(k_pool), _stream(stream)), "pkv_paged_attention_decode")
+
+
+reshape_and_cache = pkv_reshape_and_cache
+copy_blocks = pkv_copy_blocks
+attention_workspace_bytes = pkv_attention_workspace_bytes
+paged_attention_decode = pkv_paged_attention_decode

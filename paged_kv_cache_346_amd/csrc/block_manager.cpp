@@ -1,0 +1,234 @@
+// Host block manager behind the pkv_bm_* entry points.
+//
+// Bookkeeping for a pool of fixed-size KV blocks (PagedAttention: The vLLM
+// Paper, "Implementation Essentials": pre-allocated pool, block allocation and
+// reclamation, refcounts for cross-sequence sharing; "The Core Idea": blocks
+// claimed on demand and returned when done; PagedAttention and Continuous
+// Batching, "Pages, from operating systems": block tables, allocation as tokens
+// arrive, copy-on-write of shared blocks).
+//
+// All integer work, O(1) per token except fork/free (O(blocks of the sequence)).
+// The free queue is a ring buffer of capacity num_blocks: a block id is in it
+// exactly when its refcount is zero, so it can never overflow.
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/pkv.h"
+
+struct pkv_bm {
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+  };
+  int32_t N = 0, B = 0;
+  std::vector<int32_t> ref;
+  std::vector<int32_t> ring;  // free queue: ring[(head + i) % N], i < nfree
+  int32_t head = 0, nfree = 0;
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t pop_free() {
+    int32_t b = ring[head];
+    head = (head + 1 == N) ? 0 : head + 1;
+    --nfree;
+    ref[b] = 1;
+    return b;
+  }
+  void push_free(int32_t b) {
+    int32_t tail = head + nfree;
+    if (tail >= N) tail -= N;
+    ring[tail] = b;
+    ++nfree;
+  }
+};
+
+extern "C" {
+
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* init_free_order,
+                         pkv_bm** out) {
+  if (!out || num_blocks <= 0 || block_size <= 0) return PKV_EINVAL;
+  *out = nullptr;
+  pkv_bm* bm = new (std::nothrow) pkv_bm();
+  if (!bm) return PKV_EINVAL;
+  bm->N = num_blocks;
+  bm->B = block_size;
+  bm->ref.assign(num_blocks, 0);
+  bm->ring.resize(num_blocks);
+  if (init_free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = init_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        return PKV_EINVAL;
+      }
+      seen[b] = 1;
+      bm->ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) bm->ring[i] = i;
+  }
+  bm->nfree = num_blocks;
+  *out = bm;
+  return PKV_OK;
+}
+
+void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
+
+pkv_status pkv_bm_add_seq(pkv_bm* bm, int64_t seq_id, int32_t num_tokens) {
+  if (!bm || num_tokens < 0) return PKV_EINVAL;
+  if (bm->seqs.count(seq_id)) return PKV_EEXIST;
+  int32_t need = num_tokens / bm->B + (num_tokens % bm->B != 0);
+  if (need > bm->nfree) return PKV_ENOBLOCKS;
+  pkv_bm::Seq s;
+  s.table.reserve(need + 1);
+  for (int32_t i = 0; i < need; ++i) s.table.push_back(bm->pop_free());
+  s.len = num_tokens;
+  bm->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+static pkv_status append_one(pkv_bm* bm, pkv_bm::Seq& s, int64_t* slot, int32_t* src,
+                             int32_t* dst) {
+  const int32_t B = bm->B, L = s.len;
+  *src = -1;
+  *dst = -1;
+  if (L % B == 0) {
+    if (bm->nfree == 0) return PKV_ENOBLOCKS;
+    s.table.push_back(bm->pop_free());
+  } else {
+    int32_t last = s.table.back();
+    if (bm->ref[last] > 1) {
+      if (bm->nfree == 0) return PKV_ENOBLOCKS;
+      int32_t nb = bm->pop_free();
+      bm->ref[last] -= 1;
+      s.table.back() = nb;
+      *src = last;
+      *dst = nb;
+    }
+  }
+  *slot = (int64_t)s.table[L / B] * B + L % B;
+  s.len = L + 1;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq_id, int64_t* slot, int32_t* cow_src,
+                              int32_t* cow_dst) {
+  if (!bm || !slot || !cow_src || !cow_dst) return PKV_EINVAL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  return append_one(bm, it->second, slot, cow_src, cow_dst);
+}
+
+pkv_status pkv_bm_append_slots(pkv_bm* bm, const int64_t* seq_ids, int32_t n, int64_t* slots,
+                               int32_t* cow_pairs, int32_t* n_cow, int32_t* n_done) {
+  if (!bm || n < 0 || !n_cow || !n_done || (n > 0 && (!seq_ids || !slots || !cow_pairs)))
+    return PKV_EINVAL;
+  *n_cow = 0;
+  *n_done = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PKV_ENOSEQ;
+    int32_t src, dst;
+    pkv_status st = append_one(bm, it->second, &slots[i], &src, &dst);
+    if (st != PKV_OK) return st;
+    if (src >= 0) {
+      cow_pairs[2 * *n_cow] = src;
+      cow_pairs[2 * *n_cow + 1] = dst;
+      ++*n_cow;
+    }
+    ++*n_done;
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent_id, int64_t child_id) {
+  if (!bm) return PKV_EINVAL;
+  auto it = bm->seqs.find(parent_id);
+  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  if (bm->seqs.count(child_id)) return PKV_EEXIST;
+  pkv_bm::Seq child = it->second;  // copy before emplace may rehash
+  for (int32_t b : child.table) bm->ref[b] += 1;
+  bm->seqs.emplace(child_id, std::move(child));
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id) {
+  if (!bm) return PKV_EINVAL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  for (int32_t b : it->second.table) {
+    if (--bm->ref[b] == 0) bm->push_free(b);
+  }
+  bm->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_num_free(const pkv_bm* bm, int32_t* out) {
+  if (!bm || !out) return PKV_EINVAL;
+  *out = bm->nfree;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_refcount(const pkv_bm* bm, int32_t block, int32_t* out) {
+  if (!bm || !out || block < 0 || block >= bm->N) return PKV_EINVAL;
+  *out = bm->ref[block];
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_seq_info(const pkv_bm* bm, int64_t seq_id, int32_t* len, int32_t* nblocks) {
+  if (!bm || !len || !nblocks) return PKV_EINVAL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  *len = it->second.len;
+  *nblocks = (int32_t)it->second.table.size();
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_block_table(const pkv_bm* bm, int64_t seq_id, int32_t* out, int32_t cap) {
+  if (!bm || cap < 0 || (cap > 0 && !out)) return PKV_EINVAL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  const auto& t = it->second.table;
+  if ((int32_t)t.size() > cap) return PKV_EINVAL;
+  if (!t.empty()) std::memcpy(out, t.data(), t.size() * sizeof(int32_t));
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_fill_batch(const pkv_bm* bm, const int64_t* seq_ids, int32_t n,
+                             int32_t max_blocks, int32_t* block_tables, int32_t* context_lens) {
+  if (!bm || n < 0 || max_blocks < 0) return PKV_EINVAL;
+  if (n > 0 && (!seq_ids || !context_lens || (max_blocks > 0 && !block_tables)))
+    return PKV_EINVAL;
+  // validate everything first so a failing call writes nothing
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PKV_ENOSEQ;
+    if ((int32_t)it->second.table.size() > max_blocks) return PKV_EINVAL;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& s = bm->seqs.find(seq_ids[i])->second;
+    int32_t* row = block_tables + (size_t)i * max_blocks;
+    size_t nb = s.table.size();
+    if (nb) std::memcpy(row, s.table.data(), nb * sizeof(int32_t));
+    for (size_t j = nb; j < (size_t)max_blocks; ++j) row[j] = -1;
+    context_lens[i] = s.len;
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_queue,
+                           int32_t* n_free) {
+  if (!bm || !refcounts || !free_queue || !n_free) return PKV_EINVAL;
+  std::memcpy(refcounts, bm->ref.data(), (size_t)bm->N * sizeof(int32_t));
+  for (int32_t i = 0; i < bm->nfree; ++i) {
+    int32_t k = bm->head + i;
+    if (k >= bm->N) k -= bm->N;
+    free_queue[i] = bm->ring[k];
+  }
+  *n_free = bm->nfree;
+  return PKV_OK;
+}
+
+}  // extern "C"

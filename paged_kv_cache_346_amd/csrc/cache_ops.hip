@@ -1,0 +1,121 @@
+// reshape_and_cache and copy_blocks for gfx950.
+//
+// Both are bit copies bound by HBM bandwidth: every thread moves one 16-byte
+// vector (dwordx4), so a wave moves 1 KiB per instruction.
+//   reshape_and_cache: each new token's K/V goes into its slot (PagedAttention:
+//     The vLLM Paper, "Background and Motivation": every generated token adds
+//     K/V vectors to the cache).  K keeps 16-byte groups of dims, so the K write
+//     is one 16-byte store; V stores each dim's element into the dim's row of B
+//     tokens (x scalar stores of 2 or 4 bytes).
+//   copy_blocks: copy-on-write of whole blocks (PagedAttention and Continuous
+//     Batching, "Pages, from operating systems": a shared block is copied only
+//     when one sequence needs to modify it).  A (block, all heads) run is
+//     contiguous in both pools, so a pair is two straight 16-byte-vector copies.
+#include "../../include/pkv.h"
+#include "device_common.h"
+#include "launch_check.h"
+
+namespace pkv {
+
+template <typename E>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ k_pool,
+    E* __restrict__ v_pool, const int64_t* __restrict__ slot_mapping, int64_t total, int Hkv,
+    int D, int B, int64_t num_slots) {
+  constexpr int X = 16 / sizeof(E);
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int nch = D / X;
+  const int c = (int)(gid % nch);
+  const int64_t ih = gid / nch;  // token * Hkv + head
+  const int h = (int)(ih % Hkv);
+  const int64_t i = ih / Hkv;
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t pb = slot / B;
+  const int off = (int)(slot % B);
+  const int64_t src = ih * D + (int64_t)c * X;
+  const u32x4 kv = *reinterpret_cast<const u32x4*>(key + src);
+  const u32x4 vv = *reinterpret_cast<const u32x4*>(value + src);
+  const int64_t kb = ((pb * Hkv + h) * nch + c) * B * X + (int64_t)off * X;
+  *reinterpret_cast<u32x4*>(k_pool + kb) = kv;
+  E* vrow = v_pool + ((pb * Hkv + h) * D + (int64_t)c * X) * B + off;
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int e = 0; e < X; ++e) {
+      const uint32_t w = vv[e >> 1];
+      reinterpret_cast<uint16_t*>(vrow)[(int64_t)e * B] = (uint16_t)((e & 1) ? (w >> 16) : w);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < X; ++e) reinterpret_cast<uint32_t*>(vrow)[(int64_t)e * B] = vv[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_pool,
+                                                          u32x4* __restrict__ v_pool,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t total, int64_t units,
+                                                          int num_blocks) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int64_t k = gid / units;
+  const int64_t u = gid % units;
+  const int src = pairs[2 * k];
+  const int dst = pairs[2 * k + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const u32x4 a = k_pool[(int64_t)src * units + u];
+  const u32x4 b = v_pool[(int64_t)src * units + u];
+  k_pool[(int64_t)dst * units + u] = a;
+  v_pool[(int64_t)dst * units + u] = b;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
+                                            void* v_pool, const int64_t* slot_mapping,
+                                            int32_t T, int32_t Hkv, int32_t D, int32_t B,
+                                            int32_t num_blocks, pkv_dtype dtype,
+                                            void* hip_stream) {
+  if (T < 0 || Hkv <= 0 || D <= 0 || B <= 0 || num_blocks <= 0) return PKV_EINVAL;
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_EINVAL;
+  const int es = dtype == PKV_F32 ? 4 : 2;
+  if ((D * es) % 16 != 0) return PKV_EINVAL;
+  if (T == 0) return PKV_OK;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !slot_mapping)
+    return PKV_EINVAL;
+  const int64_t total = (int64_t)T * Hkv * (D * es / 16);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  hipStream_t st = (hipStream_t)hip_stream;
+  const int64_t slots = (int64_t)num_blocks * B;
+  if (dtype == PKV_F32)
+    reshape_and_cache_kernel<float><<<grid, 256, 0, st>>>(
+        (const float*)key, (const float*)value, (float*)k_pool, (float*)v_pool, slot_mapping,
+        total, Hkv, D, B, slots);
+  else
+    reshape_and_cache_kernel<uint16_t><<<grid, 256, 0, st>>>(
+        (const uint16_t*)key, (const uint16_t*)value, (uint16_t*)k_pool, (uint16_t*)v_pool,
+        slot_mapping, total, Hkv, D, B, slots);
+  return launch_status();
+}
+
+extern "C" pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs,
+                                      int32_t n, int32_t Hkv, int32_t D, int32_t B,
+                                      int32_t num_blocks, pkv_dtype dtype, void* hip_stream) {
+  if (n < 0 || Hkv <= 0 || D <= 0 || B <= 0 || num_blocks <= 0) return PKV_EINVAL;
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_EINVAL;
+  const int es = dtype == PKV_F32 ? 4 : 2;
+  const int64_t block_bytes = (int64_t)Hkv * D * B * es;
+  if (block_bytes % 16 != 0) return PKV_EINVAL;
+  if (n == 0) return PKV_OK;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !pairs) return PKV_EINVAL;
+  const int64_t units = block_bytes / 16;
+  const int64_t total = units * n;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  copy_blocks_kernel<<<grid, 256, 0, (hipStream_t)hip_stream>>>(
+      (u32x4*)k_pool, (u32x4*)v_pool, pairs, total, units, num_blocks);
+  return launch_status();
+}

@@ -1,0 +1,64 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16 bit
+// manipulation and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// bf16 is carried as raw 16-bit patterns; a 32-bit word holds two of them,
+// element 0 in the low half.  Widening to fp32 is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element e of a 16-byte vector, widened to fp32 (bf16: 8 elements; fp32: 4).
+template <typename E>
+__device__ __forceinline__ float vec_elem(const u32x4& v, int e);
+template <>
+__device__ __forceinline__ float vec_elem<uint16_t>(const u32x4& v, int e) {
+  const uint32_t w = v[e >> 1];
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+template <>
+__device__ __forceinline__ float vec_elem<float>(const u32x4& v, int e) {
+  return __uint_as_float(v[e]);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+
+// Value of `v` held by lane `src` (wave-uniform index), as a scalar.
+__device__ __forceinline__ float read_lane(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace pkv

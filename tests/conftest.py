@@ -18,3 +18,14 @@ def gpu_available() -> bool:
         return torch.cuda.is_available()
     except Exception:
         return False
+
+
+@pytest.fixture(scope="session")
+def pkv():
+    """The product binding; builds libpkv.so first only when nothing is built."""
+    lib_path = os.path.join(ROOT, "paged_kv_cache_346_amd", "libpkv.so")
+    if not os.path.exists(lib_path):
+        from paged_kv_cache_346_amd.build import build
+        build(verbose=False)
+    import paged_kv_cache_346_amd
+    return paged_kv_cache_346_amd

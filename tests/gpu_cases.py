@@ -1,0 +1,126 @@
+"""Shared set-up for the GPU parity tests: run a workload's request script
+through the product's block manager, poison every slot that holds no token with
+NaN, run the device path, and run the oracle on the same inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle.attention import paged_attention_decode as ref_decode, valid_slot_mask
+from oracle.cache_ops import copy_blocks as ref_copy, reshape_and_cache as ref_cache
+
+NAN_BF16 = np.uint16(0x7FC1)
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def poison(k_pool, v_pool, tables, lens, B):
+    mask = valid_slot_mask(tables, lens, k_pool.shape[0], B)
+    bi, oi = np.nonzero(~mask)
+    nan = NAN_BF16 if k_pool.dtype == np.uint16 else np.float32("nan")
+    k_pool[bi, :, :, oi, :] = nan
+    v_pool[bi, :, :, oi] = nan
+
+
+class Case:
+    """A workload taken through the product block manager (host side only)."""
+
+    def __init__(self, pkv, w: W.Workload, poison_unused: bool = True):
+        self.w = w
+        c = w.cfg
+        bm = pkv.BlockManager(w.num_blocks, c.B, w.free_order)
+        for op in w.ops:
+            if op[0] == "add":
+                bm.add_seq(op[1], op[2])
+            elif op[0] == "fork":
+                bm.fork(op[1], op[2])
+            elif op[0] == "extend":
+                for _ in range(op[2]):
+                    bm.append_slot(op[1])
+        ids = list(range(c.S))
+        self.max_blocks = max(1, max(-(-int(L) // c.B) for L in w.lengths))
+        pre_tables, pre_lens = bm.fill_batch(ids, self.max_blocks)
+        if w.step_ids:
+            self.slots, self.pairs = bm.append_slots(w.step_ids)
+        else:
+            self.slots = np.zeros(0, np.int64)
+            self.pairs = np.zeros((0, 2), np.int32)
+        self.tables, self.lens = bm.fill_batch(ids, self.max_blocks)
+        assert self.lens.tolist() == w.lengths.tolist()
+        self.k_pool, self.v_pool = w.k_pool, w.v_pool
+        if poison_unused:
+            self.k_pool, self.v_pool = w.k_pool.copy(), w.v_pool.copy()
+            poison(self.k_pool, self.v_pool, pre_tables, pre_lens, c.B)
+        self.bm = bm
+
+    # -- device path -----------------------------------------------------------
+    def run_device(self, pkv, partition_size=None):
+        c = self.w.cfg
+        P = c.partition_size if partition_size is None else partition_size
+        kp, vp = to_dev(self.k_pool), to_dev(self.v_pool)
+        if len(self.pairs):
+            pkv.copy_blocks(kp, vp, torch.from_numpy(self.pairs).cuda())
+        if len(self.slots):
+            pkv.reshape_and_cache(to_dev(self.w.k_new), to_dev(self.w.v_new), kp, vp,
+                                  torch.from_numpy(self.slots).cuda())
+        q = to_dev(self.w.q)
+        out = torch.full((c.S, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
+        mcl = int(self.lens.max())
+        nbytes = pkv.attention_workspace_bytes(c.S, c.Hq, c.D, mcl, P)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(self.tables).cuda(),
+                                   torch.from_numpy(self.lens).cuda(), mcl, partition_size=P,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), kp, vp
+
+    # -- oracle ----------------------------------------------------------------
+    def oracle_pools(self):
+        kp, vp = self.k_pool, self.v_pool
+        if len(self.pairs):
+            kp, vp = ref_copy(kp, vp, self.pairs)
+        if len(self.slots):
+            kp, vp = ref_cache(kp, vp, self.w.k_new, self.w.v_new, self.slots)
+        return kp, vp
+
+    def oracle_out(self, kp, vp, rows=None):
+        return ref_decode(self.w.q, kp, vp, self.tables, self.lens, rows=rows)
+
+
+def check_attention(got: np.ndarray, ref: np.ndarray, dtype: str, rows=None) -> float:
+    """Max abs error (bf16) or max per-row relative error (fp32) over the
+    compared rows; asserts the stated bound."""
+    if rows is None:
+        S, H, _ = ref.shape
+        rows = [(s, h) for s in range(S) for h in range(H)]
+    worst = 0.0
+    for s, h in rows:
+        g, r = got[s, h].astype(np.float64), ref[s, h]
+        assert np.isfinite(g).all(), (s, h)
+        err = np.abs(g - r).max()
+        if dtype == "bf16":
+            worst = max(worst, err)
+            assert err <= 2e-3, (s, h, err)
+        else:
+            rel = err / np.abs(r).max()
+            worst = max(worst, rel)
+            assert rel <= 1e-5, (s, h, rel)
+    return worst

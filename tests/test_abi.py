@@ -1,0 +1,85 @@
+"""The C ABI library: loads, exports every declared symbol, validates on the host
+(CPU only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks",
+                     "pkv_bm_create", "pkv_bm_fork", "pkv_bm_free_seq", "pkv_bm_append_slot",
+                     "pkv_bm_refcount"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(pkv):
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+    # and the binding declares a signature for each of them
+    assert sorted(pkv.SIGNATURES) == declared_functions()
+
+
+def test_single_hip_runtime_in_process(pkv):
+    maps = open("/proc/self/maps").read()
+    runtimes = set(re.findall(r"\S*libamdhip64\.so\S*", maps))
+    assert len(runtimes) <= 1, runtimes
+
+
+def test_host_validation_rejects_before_launch(pkv):
+    lib = pkv.lib
+    fake = ctypes.c_void_p(4096)            # never dereferenced: every call below fails validation
+    tbl = ctypes.c_void_p(4096)
+    # unsupported head dim / block size / group size
+    for D, B, Hq, Hkv in ((96, 16, 8, 8), (128, 8, 8, 8), (128, 16, 24, 8)):
+        st = lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, Hq, Hkv, D, B, 4,
+                                            8, 16, 0.1, 0, None, 0, pkv.PKV_BF16, None)
+        assert st == pkv.PKV_EUNSUPPORTED
+    # Hq not a multiple of Hkv, bad partition size, misaligned pointer, bad dtype
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 6, 4, 128, 16, 4,
+                                          8, 16, 0.1, 0, None, 0, 1, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 4,
+                                          8, 16, 0.1, 48, None, 0, 1, None) == pkv.PKV_EINVAL
+    odd = ctypes.c_void_p(4098)
+    assert lib.pkv_paged_attention_decode(odd, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 4,
+                                          8, 16, 0.1, 0, None, 0, 1, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 4,
+                                          8, 16, 0.1, 0, None, 0, 7, None) == pkv.PKV_EINVAL
+    # long contexts need a workspace
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 64,
+                                          128, 1024, 0.1, 512, None, 0, 1, None) == pkv.PKV_EINVAL
+    # empty batches are a no-op success
+    assert lib.pkv_paged_attention_decode(None, None, None, None, None, None, 0, 8, 8, 128, 16, 4,
+                                          8, 16, 0.1, 0, None, 0, 1, None) == pkv.PKV_OK
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 8, 1,
+                                     None) == pkv.PKV_OK
+    assert lib.pkv_copy_blocks(None, None, None, 0, 8, 128, 16, 8, 1, None) == pkv.PKV_OK
+    assert lib.pkv_reshape_and_cache(odd, fake, fake, fake, tbl, 4, 8, 128, 16, 8, 1,
+                                     None) == pkv.PKV_EINVAL
+    assert lib.pkv_copy_blocks(fake, odd, tbl, 3, 8, 128, 16, 8, 1, None) == pkv.PKV_EINVAL
+
+
+def test_workspace_size_formula(pkv):
+    f = pkv.pkv_attention_workspace_bytes
+    assert f(256, 32, 128, 512, 0) == 0                 # one partition: no workspace
+    assert f(16, 64, 128, 32768, 512) == 16 * 64 * 64 * 130 * 4
+    assert f(4, 8, 64, 513, 512) == 4 * 8 * 2 * 66 * 4
+    assert f(0, 8, 64, 5000, 0) == 0
+
+
+def test_status_strings(pkv):
+    for code in range(-6, 1):
+        assert pkv.lib.pkv_status_string(code).decode().startswith("PKV_")

@@ -1,0 +1,92 @@
+"""The C++ block manager (through the C ABI) against the reference block
+manager: bit-exact tables, lengths, refcounts, free-queue order, slots, CoW
+pairs and status codes on seeded random op scripts and on every workload's
+script (CPU only)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle.block_manager import BlockManager as RefBM, run_ops as ref_run
+
+
+def run_native(pkv, bm, ops):
+    codes, appends = [], []
+    for op in ops:
+        try:
+            if op[0] == "add":
+                bm.add_seq(op[1], op[2])
+            elif op[0] == "fork":
+                bm.fork(op[1], op[2])
+            elif op[0] == "append":
+                appends.append(bm.append_slot(op[1]))
+            elif op[0] == "extend":
+                for _ in range(op[2]):
+                    appends.append(bm.append_slot(op[1]))
+            elif op[0] == "free":
+                bm.free_seq(op[1])
+            codes.append(0)
+        except pkv.PkvError as e:
+            codes.append(e.code)
+    return codes, appends
+
+
+def assert_same_state(native, ref, ids):
+    ref_counts, free = native.snapshot()
+    assert ref_counts == ref.ref
+    assert free == list(ref.free)
+    for sid in ids:
+        if sid in ref.tables:
+            assert native.seq_info(sid) == (ref.lens[sid], len(ref.tables[sid]))
+            assert native.block_table(sid) == ref.tables[sid]
+        else:
+            with pytest.raises(Exception):
+                native.seq_info(sid)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_scripts_bit_exact(pkv, seed):
+    rng = np.random.default_rng(500 + seed)
+    N, B = int(rng.integers(3, 48)), int(rng.choice([1, 3, 16, 32]))
+    order = rng.permutation(N)
+    native, ref = pkv.BlockManager(N, B, order), RefBM(N, B, order)
+    ops = W.random_script(rng, 400, max_seqs=7, max_add=4 * B)
+    for chunk in range(0, len(ops), 25):
+        part = ops[chunk:chunk + 25]
+        assert run_native(pkv, native, part) == ref_run(ref, part)
+        assert_same_state(native, ref, range(7))
+
+
+@pytest.mark.parametrize("name", ["tiny_mha_f32", "opt13b_mha", "llama8b_gqa", "sampling_steady",
+                                  "sampling_fork"])
+def test_workload_scripts_bit_exact(pkv, name):
+    w = W.make(name, pools=False)
+    native = pkv.BlockManager(w.num_blocks, w.cfg.B, w.free_order)
+    ref = RefBM(w.num_blocks, w.cfg.B, w.free_order)
+    assert run_native(pkv, native, w.ops) == ref_run(ref, w.ops)
+    slots, pairs = native.append_slots(w.step_ids)
+    want = [ref.append_slot(s) for s in w.step_ids]
+    assert slots.tolist() == [x[0] for x in want]
+    assert pairs.tolist() == [[a, b] for _, a, b in want if a >= 0]
+    maxb = max(len(t) for t in ref.tables.values())
+    tables, lens = native.fill_batch(range(w.cfg.S), maxb)
+    rt, rl = ref.fill_batch(range(w.cfg.S), maxb)
+    assert tables.tolist() == rt and lens.tolist() == rl
+    assert lens.tolist() == w.lengths.tolist()
+    assert_same_state(native, ref, range(w.cfg.S))
+
+
+def test_append_slots_stops_at_first_failure(pkv):
+    bm = pkv.BlockManager(3, 4)
+    bm.add_seq(0, 4)
+    bm.add_seq(1, 4)
+    with pytest.raises(pkv.PkvError) as e:
+        bm.append_slots([0, 1])       # 0 takes the last free block; 1 finds none
+    assert e.value.code == pkv.PKV_ENOBLOCKS
+    assert bm.seq_info(0) == (5, 2) and bm.seq_info(1) == (4, 1)
+
+
+def test_create_rejects_bad_free_order(pkv):
+    with pytest.raises(pkv.PkvError):
+        pkv.BlockManager(4, 16, [0, 1, 1, 3])
+    with pytest.raises(pkv.PkvError):
+        pkv.BlockManager(0, 16)

@@ -1,0 +1,140 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bit-exact: reshape_and_cache and copy_blocks (whole pools compared as bytes).
+Attention: bf16 max abs error <= 2e-3; fp32 per-row max error <= 1e-5 of the
+row's max (same rounded inputs on both sides).  Every slot that holds no token
+is NaN, so any read past a sequence's end or into a free block shows up."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.conftest import gpu_available
+from tests.gpu_cases import Case, check_attention, say, to_dev, to_host_bits
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def ragged(name, seed, lens, Hq, Hkv, D, B, dtype, P, kind="step"):
+    return W.Config(name, seed, S=len(lens), Hq=Hq, Hkv=Hkv, D=D, B=B, dtype=dtype, kind=kind,
+                    partition_size=P, fixed_lengths=tuple(lens))
+
+
+RAGGED_LENS = (1, 2, 15, 16, 17, 31, 32, 33, 63, 100, 511, 512, 513, 1030, 1300)
+
+# (dtype, G, D, B, P): every compiled family, both kernels, multi-partition
+KERNEL_CASES = [
+    ("bf16", 1, 128, 16, 512), ("bf16", 1, 64, 32, 256), ("bf16", 2, 128, 32, 512),
+    ("bf16", 4, 128, 16, 512), ("bf16", 4, 64, 16, 128), ("bf16", 8, 128, 16, 512),
+    ("bf16", 8, 128, 32, 512), ("bf16", 8, 64, 32, 64), ("bf16", 4, 128, 32, 32),
+    ("f32", 1, 64, 16, 512), ("f32", 2, 128, 16, 256), ("f32", 4, 64, 32, 512),
+    ("f32", 8, 64, 16, 96),
+]
+
+
+@pytest.mark.parametrize("dtype,G,D,B,P", KERNEL_CASES)
+def test_ragged_all_rows(pkv, dtype, G, D, B, P):
+    Hkv = 2
+    cfg = ragged(f"ragged_{dtype}_G{G}_D{D}_B{B}_P{P}", 100 + G + D + B, RAGGED_LENS, Hkv * G,
+                 Hkv, D, B, dtype, P)
+    say(f"case {cfg.name}")
+    case = Case(pkv, W.make(cfg))
+    got, kp, vp = case.run_device(pkv)
+    rkp, rvp = case.oracle_pools()
+    assert np.array_equal(to_host_bits(kp).view(np.uint8), rkp.view(np.uint8))
+    assert np.array_equal(to_host_bits(vp).view(np.uint8), rvp.view(np.uint8))
+    ref = case.oracle_out(rkp, rvp)
+    worst = check_attention(got, ref, dtype)
+    say(f"  worst error {worst:.3e}")
+
+
+def test_tiny_mha_config(pkv):
+    """Four sequences of 1, 15, 16 and 70 tokens, fp32, with the step's
+    reshape_and_cache of 4 new tokens at positions 0, 14, 15 and 69."""
+    say("case tiny_mha_f32")
+    case = Case(pkv, W.make("tiny_mha_f32"))
+    assert [int(s) % 16 for s in case.slots] == [0, 14, 15, 69 % 16]
+    got, kp, vp = case.run_device(pkv)
+    rkp, rvp = case.oracle_pools()
+    assert np.array_equal(to_host_bits(kp).view(np.uint8), rkp.view(np.uint8))
+    assert np.array_equal(to_host_bits(vp).view(np.uint8), rvp.view(np.uint8))
+    check_attention(got, case.oracle_out(rkp, rvp), "f32")
+
+
+def test_empty_and_degenerate(pkv):
+    """Zero-length sequences give zero rows; one-token sequences return V[0]."""
+    import torch
+    cfg = ragged("zero_len", 7, (0, 1, 0, 40, 1), 8, 2, 128, 16, "bf16", 0, kind="decode")
+    say("case zero_len")
+    case = Case(pkv, W.make(cfg))
+    got, kp, vp = case.run_device(pkv)
+    assert np.all(got[[0, 2]] == 0.0)
+    rows = [(s, h) for s in (1, 3, 4) for h in range(8)]
+    check_attention(got, case.oracle_out(case.k_pool, case.v_pool, rows), "bf16", rows)
+    # an empty batch is a no-op
+    out = torch.empty(0, 8, 128, dtype=torch.float32, device="cuda")
+    q = torch.empty(0, 8, 128, dtype=torch.bfloat16, device="cuda")
+    t = torch.empty(0, 4, dtype=torch.int32, device="cuda")
+    l = torch.empty(0, dtype=torch.int32, device="cuda")
+    pkv.paged_attention_decode(out, q, kp, vp, t, l, 0)
+    torch.cuda.synchronize()
+
+
+def test_reject_bad_calls_without_launch(pkv):
+    import torch
+    cfg = ragged("reject", 8, (5, 9), 8, 2, 128, 16, "bf16", 0, kind="decode")
+    case = Case(pkv, W.make(cfg))
+    kp, vp = to_dev(case.k_pool), to_dev(case.v_pool)
+    out = torch.empty(2, 8, 128, dtype=torch.float32, device="cuda")
+    q = to_dev(case.w.q)
+    wide = np.full((2, 64), -1, np.int32)
+    wide[:, :case.tables.shape[1]] = case.tables
+    t = torch.from_numpy(wide).cuda()
+    l = torch.from_numpy(case.lens).cuda()
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attention_decode(out, q, kp, vp, t, l, 1024, partition_size=512)
+    assert e.value.code == pkv.PKV_EINVAL          # needs a workspace
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attention_decode(out, q, kp, vp, t, l, 9, partition_size=40)
+    assert e.value.code == pkv.PKV_EINVAL
+
+
+def _sample_rows(case, n, seed):
+    c = case.w.cfg
+    rng = np.random.default_rng(seed)
+    lens = case.lens
+    picks = {int(np.argmax(lens)), int(np.argmin(lens))}
+    picks |= set(rng.choice(c.S, size=min(c.S, n), replace=False).tolist())
+    rows = []
+    for s in sorted(picks):
+        for h in sorted(set(rng.choice(c.Hq, size=min(c.Hq, 3), replace=False).tolist()) |
+                        {0, c.Hq - 1}):
+            rows.append((s, h))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["llama8b_gqa", "sampling_fork", "sampling_steady",
+                                  "opt13b_mha", "long70b_b16", "long70b_b32"])
+def test_full_config(pkv, name):
+    """Full-size workload in the benchmark's launch configuration: whole pools
+    compared bit for bit after the step's cache writes, attention compared on
+    sampled rows (the longest and shortest sequences included)."""
+    say(f"case {name} (full size)")
+    case = Case(pkv, W.make(name))
+    got, kp, vp = case.run_device(pkv)
+    say("  device done")
+    assert np.isfinite(got).all()
+    if len(case.slots) or len(case.pairs):
+        rkp, rvp = case.oracle_pools()
+        assert np.array_equal(to_host_bits(kp).view(np.uint8), rkp.view(np.uint8))
+        assert np.array_equal(to_host_bits(vp).view(np.uint8), rvp.view(np.uint8))
+        say("  pools bit-exact")
+    else:
+        rkp, rvp = case.k_pool, case.v_pool
+    rows = _sample_rows(case, 12 if case.w.cfg.S > 16 else 4, 42)
+    worst = check_attention(got, case.oracle_out(rkp, rvp, rows), case.w.cfg.dtype, rows)
+    say(f"  {len(rows)} rows, worst error {worst:.3e}")
+    if name == "sampling_fork":
+        assert len(case.pairs) == 224
