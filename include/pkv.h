@@ -197,6 +197,31 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_p
                                       size_t workspace_bytes, pkv_dtype dtype,
                                       void* hip_stream);
 
+/* The two launches of pkv_paged_attention_decode, callable one at a time (for
+ * per-kernel timing, or to put other work between them on the stream).
+ * pkv_paged_attention_main takes exactly pkv_paged_attention_decode's arguments
+ * and runs the main kernel: rows of sequences that fit one partition are final
+ * in `out` when it completes; longer sequences leave per-partition
+ * (max, sum, accumulator) partials in `workspace`.
+ * pkv_paged_attention_reduce then merges those partials into `out` (log-sum-exp
+ * combine of the partitions; the split itself is not on the pages, which only
+ * note that long contexts are hard: [ZENO] "Limitations").  Its arguments must
+ * repeat the values given to the main call (same S, Hq, D, B, max_blocks,
+ * max_context_len, partition_size, context_lens, workspace); it reads nothing
+ * else and is a no-op when every sequence fits one partition. */
+pkv_status pkv_paged_attention_main(float* out, const void* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* block_tables,
+                                    const int32_t* context_lens, int32_t S, int32_t Hq,
+                                    int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
+                                    int32_t num_blocks, int32_t max_context_len, float scale,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, pkv_dtype dtype, void* hip_stream);
+pkv_status pkv_paged_attention_reduce(float* out, const int32_t* context_lens, int32_t S,
+                                      int32_t Hq, int32_t D, int32_t B, int32_t max_blocks,
+                                      int32_t max_context_len, int32_t partition_size,
+                                      const void* workspace, size_t workspace_bytes,
+                                      void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

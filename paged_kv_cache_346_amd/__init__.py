@@ -19,7 +19,8 @@ import torch  # imported before the library so both share torch's HIP runtime
 
 __all__ = [
     "PkvError", "BlockManager", "pkv_reshape_and_cache", "pkv_copy_blocks",
-    "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pool_shapes",
+    "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pkv_paged_attention_main",
+    "pkv_paged_attention_reduce", "pool_shapes", "paged_attention_main", "paged_attention_reduce",
     "reshape_and_cache", "copy_blocks", "attention_workspace_bytes", "paged_attention_decode",
     "LIB_PATH", "lib",
 ]
@@ -57,12 +58,16 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
                                           _vp]),
+    "pkv_paged_attention_main": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
+    "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _vp, _sz, _vp]),
 }
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_346_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python paged_kv_cache_346_amd/build.py`")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(handle, name)
@@ -269,14 +274,8 @@ def pkv_attention_workspace_bytes(S: int, Hq: int, D: int, max_context_len: int,
     return int(lib.pkv_attention_workspace_bytes(S, Hq, D, max_context_len, partition_size))
 
 
-def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
-                               max_context_len: int, scale: float | None = None,
-                               partition_size: int = 0, workspace=None, stream=None) -> None:
-    """out[s, h] = softmax(q[s, h] K_s^T * scale) V_s through the block tables.
-
-    out fp32 [S, Hq, D]; q [S, Hq, D] in the pool dtype; block_tables int32
-    [S, max_blocks]; context_lens int32 [S].  `workspace` (a uint8 device tensor)
-    is needed when max_context_len exceeds one partition."""
+def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                    scale, partition_size, workspace):
     N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
     S, Hq = q.shape[0], q.shape[1]
     if tuple(q.shape) != (S, Hq, D) or q.dtype != k_pool.dtype:
@@ -293,14 +292,56 @@ def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_len
     if workspace is not None:
         ws_ptr = _dev(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.pkv_paged_attention_decode(
-        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B,
-        block_tables.shape[1], N, int(max_context_len), float(scale), int(partition_size), ws_ptr,
-        ws_bytes, _dtype_code(k_pool), _stream(stream)), "pkv_paged_attention_decode")
+    return (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, D,
+            B, block_tables.shape[1], N, int(max_context_len), float(scale), int(partition_size),
+            ws_ptr, ws_bytes, _dtype_code(k_pool))
+
+
+def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
+                               max_context_len: int, scale: float | None = None,
+                               partition_size: int = 0, workspace=None, stream=None) -> None:
+    """out[s, h] = softmax(q[s, h] K_s^T * scale) V_s through the block tables.
+
+    out fp32 [S, Hq, D]; q [S, Hq, D] in the pool dtype; block_tables int32
+    [S, max_blocks]; context_lens int32 [S].  `workspace` (a uint8 device tensor)
+    is needed when max_context_len exceeds one partition."""
+    args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                           scale, partition_size, workspace)
+    _check(lib.pkv_paged_attention_decode(*args, _stream(stream)), "pkv_paged_attention_decode")
+
+
+def pkv_paged_attention_main(out, q, k_pool, v_pool, block_tables, context_lens,
+                             max_context_len: int, scale: float | None = None,
+                             partition_size: int = 0, workspace=None, stream=None) -> None:
+    """The main launch of pkv_paged_attention_decode alone (same arguments)."""
+    args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                           scale, partition_size, workspace)
+    _check(lib.pkv_paged_attention_main(*args, _stream(stream)), "pkv_paged_attention_main")
+
+
+def pkv_paged_attention_reduce(out, context_lens, B: int, max_blocks: int, max_context_len: int,
+                               partition_size: int = 0, workspace=None, stream=None) -> None:
+    """The partition merge of pkv_paged_attention_decode alone; the arguments
+    repeat those of the preceding pkv_paged_attention_main call."""
+    S, Hq, D = out.shape
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32 [S, Hq, D]")
+    if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attention_reduce(_dev(out, "out"), _dev(context_lens, "context_lens"),
+                                          S, Hq, D, int(B), int(max_blocks), int(max_context_len),
+                                          int(partition_size), ws_ptr, ws_bytes, _stream(stream)),
+           "pkv_paged_attention_reduce")
 
 
 reshape_and_cache = pkv_reshape_and_cache
 copy_blocks = pkv_copy_blocks
 attention_workspace_bytes = pkv_attention_workspace_bytes
 paged_attention_decode = pkv_paged_attention_decode
+paged_attention_main = pkv_paged_attention_main
+paged_attention_reduce = pkv_paged_attention_reduce

@@ -497,12 +497,19 @@ extern "C" size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D
   return (size_t)S * Hq * np * (D + 2) * sizeof(float);
 }
 
-extern "C" pkv_status pkv_paged_attention_decode(
-    float* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
-    const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
-    int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-    void* hip_stream) {
+namespace pkv {
+
+// Host validation and argument set-up shared by the three attention entry
+// points.  On PKV_OK, *a and *groups describe the main launch (groups == 0 when
+// S == 0: nothing to launch).
+static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, const void* q,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                 int32_t max_blocks, int32_t num_blocks, int32_t max_context_len,
+                                 float scale, int32_t partition_size, void* workspace,
+                                 size_t workspace_bytes, pkv_dtype dtype) {
+  *groups = 0;
   if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 || num_blocks <= 0 ||
       max_context_len < 0 || partition_size < 0 || !std::isfinite(scale))
     return PKV_EINVAL;
@@ -517,38 +524,110 @@ extern "C" pkv_status pkv_paged_attention_decode(
     return PKV_EINVAL;
   const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
   const int64_t nparts = num_partitions(mcl, P);
-  const int64_t groups = (int64_t)S * Hkv * nparts;
-  if (groups > 0x7fffffffLL || (int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
-  DecodeArgs a{};
-  a.out = out;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.Hkv = Hkv;
-  a.max_blocks = max_blocks;
-  a.num_blocks = num_blocks;
-  a.nparts = (int)nparts;
-  a.P = P;
-  a.scale_log2e = scale * 1.4426950408889634f;
+  const int64_t g = (int64_t)S * Hkv * nparts;
+  if (g > 0x7fffffffLL || (int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
+  *a = DecodeArgs{};
+  a->out = out;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->Hkv = Hkv;
+  a->max_blocks = max_blocks;
+  a->num_blocks = num_blocks;
+  a->nparts = (int)nparts;
+  a->P = P;
+  a->scale_log2e = scale * 1.4426950408889634f;
   if (nparts > 1) {
     const size_t need = (size_t)S * Hq * nparts * (D + 2) * sizeof(float);
     if (!aligned16(workspace) || workspace_bytes < need) return PKV_EINVAL;
-    a.part_acc = (float*)workspace;
-    a.part_ml = a.part_acc + (size_t)S * Hq * nparts * D;
+    a->part_acc = (float*)workspace;
+    a->part_ml = a->part_acc + (size_t)S * Hq * nparts * D;
   }
-  hipStream_t st = (hipStream_t)hip_stream;
+  *groups = g;
+  return PKV_OK;
+}
+
+static pkv_status launch_main_kernel(const DecodeArgs& a, int64_t groups, const void* q,
+                                     const void* k_pool, const void* v_pool, int D, int B, int G,
+                                     pkv_dtype dtype, hipStream_t st) {
   const bool ok = dtype == PKV_F32
                       ? dispatch_d<float>(D, B, G, a, (unsigned)groups, q, k_pool, v_pool, st)
                       : dispatch_d<uint16_t>(D, B, G, a, (unsigned)groups, q, k_pool, v_pool, st);
   if (!ok) return PKV_EUNSUPPORTED;
-  if (launch_status() != PKV_OK) return PKV_EHIP;
-  if (nparts > 1) {
-    if (D == 64)
-      pa_reduce_kernel<64><<<(unsigned)(S * Hq), kWave, 0, st>>>(
-          out, a.part_acc, a.part_ml, context_lens, Hq, max_blocks, B, (int)nparts, P);
-    else
-      pa_reduce_kernel<128><<<(unsigned)(S * Hq), kWave, 0, st>>>(
-          out, a.part_acc, a.part_ml, context_lens, Hq, max_blocks, B, (int)nparts, P);
-    if (launch_status() != PKV_OK) return PKV_EHIP;
-  }
-  return PKV_OK;
+  return launch_status();
+}
+
+static pkv_status launch_reduce_kernel(const DecodeArgs& a, int S, int Hq, int D, int B,
+                                       hipStream_t st) {
+  if (a.nparts <= 1) return PKV_OK;
+  if (D == 64)
+    pa_reduce_kernel<64><<<(unsigned)(S * Hq), kWave, 0, st>>>(
+        a.out, a.part_acc, a.part_ml, a.context_lens, Hq, a.max_blocks, B, a.nparts, a.P);
+  else
+    pa_reduce_kernel<128><<<(unsigned)(S * Hq), kWave, 0, st>>>(
+        a.out, a.part_acc, a.part_ml, a.context_lens, Hq, a.max_blocks, B, a.nparts, a.P);
+  return launch_status();
+}
+
+}  // namespace pkv
+
+extern "C" pkv_status pkv_paged_attention_decode(
+    float* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+    int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+    void* hip_stream) {
+  DecodeArgs a;
+  int64_t groups;
+  pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, block_tables, context_lens,
+                                 S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
+                                 partition_size, workspace, workspace_bytes, dtype);
+  if (st != PKV_OK || groups == 0) return st;
+  hipStream_t hs = (hipStream_t)hip_stream;
+  st = launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, hs);
+  if (st != PKV_OK) return st;
+  return launch_reduce_kernel(a, S, Hq, D, B, hs);
+}
+
+extern "C" pkv_status pkv_paged_attention_main(
+    float* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+    int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+    void* hip_stream) {
+  DecodeArgs a;
+  int64_t groups;
+  pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, block_tables, context_lens,
+                                 S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
+                                 partition_size, workspace, workspace_bytes, dtype);
+  if (st != PKV_OK || groups == 0) return st;
+  return launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype,
+                            (hipStream_t)hip_stream);
+}
+
+extern "C" pkv_status pkv_paged_attention_reduce(
+    float* out, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t D, int32_t B,
+    int32_t max_blocks, int32_t max_context_len, int32_t partition_size, const void* workspace,
+    size_t workspace_bytes, void* hip_stream) {
+  if (S < 0 || Hq <= 0 || max_blocks <= 0 || max_context_len < 0 || partition_size < 0)
+    return PKV_EINVAL;
+  if (!(D == 64 || D == 128) || !(B == 16 || B == 32)) return PKV_EUNSUPPORTED;
+  const int P = partition_size > 0 ? partition_size : kDefaultPartition;
+  if (P % 32 != 0 || P % B != 0) return PKV_EINVAL;
+  if (S == 0) return PKV_OK;
+  if (!aligned16(out) || !context_lens) return PKV_EINVAL;
+  const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
+  const int64_t nparts = num_partitions(mcl, P);
+  if ((int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
+  if (nparts <= 1) return PKV_OK;
+  const size_t need = (size_t)S * Hq * nparts * (D + 2) * sizeof(float);
+  if (!aligned16(workspace) || workspace_bytes < need) return PKV_EINVAL;
+  DecodeArgs a{};
+  a.out = out;
+  a.context_lens = context_lens;
+  a.max_blocks = max_blocks;
+  a.nparts = (int)nparts;
+  a.P = P;
+  a.part_acc = (float*)workspace;
+  a.part_ml = a.part_acc + (size_t)S * Hq * nparts * D;
+  return launch_reduce_kernel(a, S, Hq, D, B, (hipStream_t)hip_stream);
 }
