@@ -6,8 +6,14 @@
 One step is one pass of the whole device path over one batch that already sits
 in HBM: copy-on-write block copies (when the batch has any), reshape_and_cache
 of the step's new tokens (when it has any), the paged-attention main kernel and
-the log-sum-exp reduce.  The host block manager builds the batch (slots, copy
-pairs, block tables) once before timing; its cost is reported separately.
+the log-sum-exp reduce, for one attention layer.  The host block manager builds
+the batch (slots, copy pairs, block tables) once before timing; its cost is
+reported separately.
+
+As in a model, every layer has its own K/V pool while all layers share the
+block tables; consecutive steps take consecutive layers, and there are enough
+layers that at least 4 GiB of pool lies between two visits of one layer.  So a
+step never finds the previous step's KV in the 256 MB last-level cache.
 
 Prints ONE JSON line.  `value` is KV-read GB/s over the whole step: the
 algorithmic KV bytes of the batch (valid tokens only, sum_s L_s * Hkv * D * 2 *
@@ -84,7 +90,7 @@ class Batch:
     """One decode batch, built through the product's block manager and resident
     on the device."""
 
-    def __init__(self, pkv, torch, W, name: str):
+    def __init__(self, pkv, torch, W, name: str, partition_size=None, layers=0):
         self.cfg = c = W.CONFIGS[name]
         self.w = w = W.make(name, pools=False)
         t0 = time.perf_counter()
@@ -128,8 +134,12 @@ class Batch:
                                           dtype=torch.float32).to(tdt)
             return x
 
-        self.k_pool = normal(ks)
-        self.v_pool = normal(vs)
+        esize = 4 if c.dtype == "f32" else 2
+        pool_bytes = 2 * w.num_blocks * c.Hkv * c.D * c.B * esize
+        self.layers = layers or max(2, min(16, -(-(4 << 30) // pool_bytes)))
+        self.pools = [(normal(ks), normal(vs)) for _ in range(self.layers)]
+        self.pool_bytes = pool_bytes
+        self.k_pool, self.v_pool = self.pools[0]
         self.q = self._to_dev(torch, w.q)
         self.slots = None if slots is None else torch.from_numpy(slots).to(dev)
         self.k_new = self._to_dev(torch, w.k_new) if slots is not None else None
@@ -140,7 +150,7 @@ class Batch:
         self.tables = torch.from_numpy(tables).to(dev)
         self.lens = torch.from_numpy(lens).to(dev)
         self.mcl = int(lens.max())
-        self.P = c.partition_size
+        self.P = c.partition_size if partition_size is None else partition_size
         nbytes = pkv.attention_workspace_bytes(c.S, c.Hq, c.D, self.mcl, self.P)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((c.S, c.Hq, c.D), dtype=torch.float32, device=dev)
@@ -154,10 +164,11 @@ class Batch:
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(a).cuda()
 
-    def step(self, pkv, ev=None, main_ev=None):
-        """Launch one step.  `ev` (5 events) brackets copy_blocks, reshape_and_cache,
-        the attention main kernel and the reduce; `main_ev` (2 events) brackets
-        the main kernel only."""
+    def step(self, pkv, layer=0, ev=None, main_ev=None):
+        """Launch one step on `layer`'s pools.  `ev` (5 events) brackets
+        copy_blocks, reshape_and_cache, the attention main kernel and the reduce;
+        `main_ev` (2 events) brackets the main kernel only."""
+        self.k_pool, self.v_pool = self.pools[layer % self.layers]
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
         if self.pairs is not None:
@@ -200,26 +211,29 @@ def cpu_baseline(batch, torch, budget_s: float):
     order = np.random.default_rng(7).permutation(c.S)
     done_bytes, done_seqs, elapsed = 0, 0, 0.0
     per_tok = c.Hkv * c.D * 2 * c.elem_bytes
+    passes = 0
     with threadpool_limits(limits=1):
-        for s in order:
-            s = int(s)
-            rows = [(s, h) for h in range(c.Hq)]
-            t0 = time.perf_counter()
-            oracle_decode(q, kp, vp, batch.tables_host, batch.lens_host, rows=rows)
-            elapsed += time.perf_counter() - t0
-            done_bytes += int(batch.lens_host[s]) * per_tok
-            done_seqs += 1
-            if elapsed >= budget_s:
-                break
+        while elapsed < budget_s and passes < 100:
+            for s in order:
+                s = int(s)
+                rows = [(s, h) for h in range(c.Hq)]
+                t0 = time.perf_counter()
+                oracle_decode(q, kp, vp, batch.tables_host, batch.lens_host, rows=rows)
+                elapsed += time.perf_counter() - t0
+                done_bytes += int(batch.lens_host[s]) * per_tok
+                done_seqs += 1
+                if elapsed >= budget_s:
+                    break
+            passes += 1
     return {
         "value": round(done_bytes / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": f"fp64 oracle decode attention (gather through the block table + "
-                  f"softmax(qK^T*scale)V) for {done_seqs} of {c.S} sequences, all {c.Hq} "
-                  f"heads each, {done_bytes / 1e6:.1f} MB of KV, {elapsed:.1f} s; "
-                  f"single BLAS thread; cache writes not included",
+                  f"softmax(qK^T*scale)V) of the same batch, {done_seqs} sequence rows "
+                  f"({c.S} per pass, all {c.Hq} heads each), {done_bytes / 1e6:.1f} MB of "
+                  f"KV, {elapsed:.1f} s; single BLAS thread; cache writes not included",
         "seconds": round(elapsed, 3),
         "tokens_per_s": round(done_seqs / elapsed, 4),
     }
@@ -231,10 +245,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama8b_gqa", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="override the workload's partition size (tokens per workgroup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--flushed-steps", type=int, default=20,
-                    help="extra steps with a 1 GiB cache-evicting write between them")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="K/V pools the steps rotate through (0 = enough for 4 GiB)")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
@@ -263,7 +279,7 @@ def main() -> int:
 
     name = args.config
     log(f"bench: building workload {name}")
-    batch = Batch(pkv, torch, W, name)
+    batch = Batch(pkv, torch, W, name, args.partition_size, args.layers)
     c = batch.cfg
     log(f"bench: N={batch.w.num_blocks} blocks, KV {batch.kv_bytes / 1e6:.1f} MB, "
         f"{batch.n_pairs} CoW pairs, max L {batch.mcl}")
@@ -278,8 +294,8 @@ def main() -> int:
         del src, dst
         log(f"bench: copy probe of {args.copy_probe_mib} MiB done")
 
-    for _ in range(args.warmup):
-        batch.step(pkv)
+    for i in range(args.warmup):
+        batch.step(pkv, i)
     torch.cuda.synchronize()
 
     # contract timing: K steps back to back; two events bracket each main-kernel
@@ -289,7 +305,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        batch.step(pkv, main_ev=mev[i])
+        batch.step(pkv, args.warmup + i, main_ev=mev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log("bench: timed steps done")
@@ -302,29 +318,11 @@ def main() -> int:
     n_bd = min(args.steps, 20)
     bev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_bd)]
     for i in range(n_bd):
-        batch.step(pkv, ev=bev[i])
+        batch.step(pkv, i, ev=bev[i])
     torch.cuda.synchronize()
     names = ("copy_blocks", "reshape_and_cache", "attention_main", "attention_reduce")
     kernel_us = {n: (round(avg_ms(bev, i) * 1e3, 2) if used else None)
                  for i, (n, used) in enumerate(zip(names, batch.launches()))}
-
-    # the same kernels with L2 and the 256 MB last-level cache evicted before each step
-    flushed = None
-    if args.flushed_steps > 0:
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
-               for _ in range(args.flushed_steps)]
-        for i in range(args.flushed_steps):
-            scratch.fill_(i & 0xFF)
-            batch.step(pkv, ev=fev[i])
-        torch.cuda.synchronize()
-        del scratch
-        used = batch.launches()
-        flushed = {"steps": args.flushed_steps,
-                   "main_kernel_us": round(avg_ms(fev, 2) * 1e3, 2),
-                   "step_kernels_us": round(sum(avg_ms(fev, i) for i in range(4) if used[i])
-                                            * 1e3, 2)}
-        log("bench: flushed steps done")
 
     ms_per_step = wall * 1e3 / args.steps
     value = batch.kv_bytes * args.steps / wall / 1e9
@@ -346,9 +344,10 @@ def main() -> int:
         "seqs": c.S, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D, "block_size": c.B,
         "kv_dtype": c.dtype, "context_tokens": int(batch.lens_host.sum()),
         "max_context": batch.mcl, "pool_blocks": batch.w.num_blocks,
-        "partition_size": c.partition_size or 512, "new_tokens": 0 if batch.slots is None
+        "partition_size": batch.P or 512, "new_tokens": 0 if batch.slots is None
         else int(batch.slots.shape[0]), "cow_copies": batch.n_pairs,
         "kv_bytes_per_step": batch.kv_bytes,
+        "pool_bytes_per_layer": batch.pool_bytes,
     }
     rec = {
         "metric": METRIC,
@@ -367,7 +366,7 @@ def main() -> int:
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(c.S / (ms_per_step * 1e-3), 1),
         "kernel_us": kernel_us,
-        "flushed": flushed,
+        "layers": batch.layers,
         "host_bookkeeping_us": round(batch.host_bookkeeping_us, 1),
         "roofline": roofline,
         "cpu_baseline": None,

@@ -182,8 +182,9 @@ size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
  *   max_context_len  host-known bound on context_lens; sizes the grid (no sync)
  *   scale         score scale, usually 1/sqrt(D)
  *   partition_size   tokens per workgroup partition: 0 = default (512), else a
- *                 positive multiple of 32 and of B.  Sequences longer than one
- *                 partition are split and merged by a log-sum-exp reduce launch.
+ *                 positive multiple of 32 and of B spanning at most 64 blocks
+ *                 (<= 64*B tokens).  Sequences longer than one partition are
+ *                 split and merged by a log-sum-exp reduce launch.
  *   workspace     device buffer of workspace_bytes >= pkv_attention_workspace_bytes
  *                 (may be NULL when that is 0)
  * Compiled shapes: D in {64, 128}, B in {16, 32}; bf16 with Hq/Hkv in

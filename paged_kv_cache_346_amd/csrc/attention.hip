@@ -10,26 +10,39 @@
 // all previous tokens).  Query head h reads KV head h / G, G = Hq / Hkv (GQA,
 // named in "Impact and Follow-Ups" as a way to shrink KV size).
 //
-// Work decomposition (not on the pages): one workgroup of NW wave64s per
-// (sequence, KV head, partition of P tokens).  The whole GQA group of a KV head
-// lives in one workgroup, so each K/V byte is fetched from HBM once.  Waves take
-// the partition's tiles round-robin, each keeping an online-softmax state
-// (running max m, running sum l, unnormalised accumulator), merged in LDS at the
-// end.  A sequence with one partition writes its output directly; longer ones
-// write (m, l, acc) partials that pa_reduce_kernel combines (log-sum-exp merge).
-// Scores are kept in base 2 (scale * log2 e folded in) so exp is one v_exp_f32.
+// Work decomposition (not on the pages).  A work item is one (sequence, KV
+// head, partition of P tokens); ONE wave64 owns an item from start to finish, so
+// there is no cross-wave merge, no LDS and no barrier.  The whole GQA group of a
+// KV head lives in that wave, so each K/V byte is fetched from HBM once.  Items
+// are numbered partition-major and workgroups hold NW consecutive items; the
+// dispatcher deals consecutive workgroups round-robin to the 8 XCDs, so every XCD
+// gets a like share of each partition index (with the partition index fastest,
+// the partition-0 items -- most of the work when sequences are short -- would
+// pile onto a few XCDs).
+//
+// Each wave
+//   * reads the partition's slice of the block table once, one entry per lane,
+//     and takes each physical block id with readlane (a scalar) when needed;
+//   * keeps two tiles of K/V in registers: the loads of tile k+1 are issued
+//     before tile k is computed, so HBM traffic overlaps the arithmetic;
+//   * keeps an online-softmax state (running max m, running sum l, unnormalised
+//     accumulator).
+// An item that covers its whole sequence writes the output rows; otherwise it
+// writes its (m, l, acc) partial and pa_reduce_kernel merges the partitions
+// (log-sum-exp combine).  Scores are kept in base 2 (scale * log2 e folded in)
+// so exp is one v_exp_f32.
 //
 // Two main kernels:
-//   pa_valu_kernel  fp32 pools, and bf16 with G < 4.  Lanes (token, dim-chunk)
-//                   for q.k with a 2-step cross-lane sum; lanes own output dims
-//                   for p.v with the token weights read back as scalars.
+//   pa_valu_kernel  fp32 pools, and bf16 with G < 4.  Tile = one KV block.  Lanes
+//                   (token, dim-chunk) for q.k with a cross-lane sum; lanes own
+//                   output dims for p.v with the token weights read back as
+//                   scalars.
 //   pa_mfma_kernel  bf16 with G in {4, 8}: the GQA group x KV tile contraction is
 //                   a small dense GEMM, run on v_mfma_f32_16x16x32_bf16 (group
-//                   padded to 16).  S^T = K Q^T takes K straight from HBM as the
-//                   A operand (16 tokens x 8 dims per lane-row); O^T = V^T P^T
-//                   takes V straight from HBM as the A operand (the V layout keeps
-//                   8 consecutive tokens of one dim in 16 bytes).  P is split into
-//                   bf16 hi + lo parts (two MFMAs) so the weights keep ~16 bits.
+//                   padded to 16).  Tile = 32 tokens.  S^T = K Q^T takes K
+//                   straight from HBM as the A operand; O^T = V^T P^T takes V
+//                   straight from HBM as the A operand.  P is split into bf16 hi +
+//                   lo parts (two MFMAs) so the weights keep ~16 bits.
 // Masking: tokens at or past the partition end get score -inf by selection and
 // their V elements are zeroed before the product, so NaN in unused slots never
 // reaches the output.
@@ -43,7 +56,10 @@
 namespace pkv {
 
 constexpr int kDefaultPartition = 512;
-constexpr int kWavesPerGroup = 4;
+// One wave per workgroup: the dispatcher then balances the ragged items wave by
+// wave (measured faster than four-item workgroups on ragged batches).
+constexpr int kWavesPerGroup = 1;           // items per workgroup
+constexpr int kMaxPartitionBlocks = kWave;  // one table entry per lane
 
 struct DecodeArgs {
   float* out;
@@ -51,72 +67,109 @@ struct DecodeArgs {
   float* part_ml;    // [S, Hq, nparts, 2]
   const int* block_tables;
   const int* context_lens;
+  int SG;            // S * Hkv: items per partition index
+  int items;         // SG * nparts
   int Hkv, max_blocks, num_blocks, nparts, P;
   float scale_log2e;
 };
 
-// Sequence geometry shared by both main kernels.  Returns false when the
-// workgroup has nothing to do.
-template <int D, int B, int G, int NW>
-__device__ __forceinline__ bool decode_setup(const DecodeArgs& a, int& s, int& g, int& p,
-                                             int& start, int& end, int& nps) {
-  const int bid = blockIdx.x;
-  p = bid % a.nparts;
-  const int sg = bid / a.nparts;
-  g = sg % a.Hkv;
-  s = sg / a.Hkv;
-  int L = a.context_lens[s];
-  L = min(L, a.max_blocks * B);
-  if (L <= 0) {
-    if (p == 0) {
-      float* o = a.out + ((size_t)s * a.Hkv * G + (size_t)g * G) * D;
-      for (int i = threadIdx.x; i < G * D; i += NW * kWave) o[i] = 0.f;
-    }
-    return false;
-  }
-  start = p * a.P;
-  if (start >= L) return false;
-  end = min(L, start + a.P);
-  nps = min((L + a.P - 1) / a.P, a.nparts);
+// One wave's share: sequence s, KV head g, partition p, tokens [start, end).
+struct WorkItem {
+  int s, g, p, start, end, nps;
+};
+
+// Item of this wave (partition-major numbering); false past the last item.
+template <int NW>
+__device__ __forceinline__ bool item_ids(const DecodeArgs& a, WorkItem& it) {
+  const int item = (int)blockIdx.x * NW + uniform((int)threadIdx.x / kWave);
+  if (item >= a.items) return false;
+  it.p = item / a.SG;
+  const int sg = item - it.p * a.SG;
+  it.g = sg % a.Hkv;
+  it.s = sg / a.Hkv;
+  it.start = it.p * a.P;
   return true;
 }
 
-// Merge the per-wave (m, l, acc) states held in LDS and write the output row or
-// the partition's partial.
-template <int D, int G, int NW>
-__device__ __forceinline__ void merge_and_store(const DecodeArgs& a, int s, int g, int p, int nps,
-                                                const float (*sm_m)[16], const float (*sm_l)[16],
-                                                const float (*sm_acc)[G][D]) {
+// Token extent of the item given the sequence length; false when the wave has
+// nothing to do (a zero-length sequence gets zero output rows).
+template <int D, int B, int G>
+__device__ __forceinline__ bool item_extent(const DecodeArgs& a, WorkItem& it, int L) {
+  L = min(L, a.max_blocks * B);
+  if (L <= 0) {
+    if (it.p == 0) {
+      float* o = a.out + ((size_t)it.s * a.Hkv * G + (size_t)it.g * G) * D;
+      for (int i = threadIdx.x & (kWave - 1); i < G * D; i += kWave) o[i] = 0.f;
+    }
+    return false;
+  }
+  if (it.start >= L) return false;
+  it.end = min(L, it.start + a.P);
+  it.nps = min((L + a.P - 1) / a.P, a.nparts);
+  return true;
+}
+
+// Physical block ids of up to 64 consecutive logical blocks, one per lane: each
+// table entry is read from memory once per wave and taken as a scalar with
+// readlane when its block is loaded.  A partition spans at most 64 blocks.
+struct TableWindow {
+  int base, v;
+  __device__ __forceinline__ void load(const int* row, int b, int limit) {
+    base = b;
+    const int i = b + (int)(threadIdx.x & (kWave - 1));
+    v = i < limit ? row[i] : 0;
+  }
+  // Block of logical block lb (wave-uniform, base <= lb < base + 64), clamped
+  // into the pool so a corrupt entry can never address outside it.
+  __device__ __forceinline__ int at(int lb, int num_blocks) const {
+    const int pb = __builtin_amdgcn_readlane(v, lb - base);
+    return min(max(pb, 0), num_blocks - 1);
+  }
+};
+
+// Where an item's result row for query head h goes: the output (the item covers
+// the whole sequence) or its partition's partial slot.
+struct RowSink {
+  float* acc;  // D floats
+  float* ml;   // (m, l) or nullptr for a final row
+};
+
+template <int D, int G>
+__device__ __forceinline__ RowSink row_sink(const DecodeArgs& a, const WorkItem& it, int gi) {
   const int Hq = a.Hkv * G;
-  for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
-    const int gi = i / D, d = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][gi]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = sm_m[w][gi];
-      const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-      num = fmaf(f, sm_acc[w][gi][d], num);
-      den = fmaf(f, sm_l[w][gi], den);
-    }
-    const int h = g * G + gi;
-    if (nps == 1) {
-      a.out[((size_t)s * Hq + h) * D + d] = num / den;
-    } else {
-      const size_t row = ((size_t)s * Hq + h) * a.nparts + p;
-      a.part_acc[row * D + d] = num;
-      if (d == 0) {
-        a.part_ml[2 * row] = M;
-        a.part_ml[2 * row + 1] = den;
-      }
-    }
+  const size_t h = (size_t)it.s * Hq + it.g * G + gi;
+  if (it.nps == 1) return RowSink{a.out + h * D, nullptr};
+  const size_t row = h * a.nparts + it.p;
+  return RowSink{a.part_acc + row * D, a.part_ml + 2 * row};
+}
+
+// Run `compute(k, tile)` over a wave's n tiles with the loads of tile k+1 issued
+// before tile k is computed.  Two register buffers alternate; every load in the
+// steady loop is unconditional, so the compiler's wait before each compute only
+// covers the tile it needs.
+template <typename Tile, typename Load, typename Compute>
+__device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute) {
+  if (n <= 0) return;
+  Tile ta, tb;
+  load(0, ta);
+  int k = 0;
+  for (; k + 2 < n; k += 2) {
+    load(k + 1, tb);
+    compute(k, ta);
+    load(k + 2, ta);
+    compute(k + 1, tb);
+  }
+  if (k + 1 < n) {
+    load(k + 1, tb);
+    compute(k, ta);
+    compute(k + 1, tb);
+  } else {
+    compute(k, ta);
   }
 }
 
 // ---------------------------------------------------------------------------
-// VALU main kernel.  E = float or uint16_t (bf16 bits).
+// VALU main kernel.  E = float or uint16_t (bf16 bits).  Tile = one KV block.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int B, int G, int NW>
 __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
@@ -131,27 +184,26 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
   constexpr int ND = D / kWave;      // output dims per lane
   static_assert(NCH % NCG == 0 && D % kWave == 0 && B % X == 0, "unsupported shape");
 
-  __shared__ float sm_m[NW][16], sm_l[NW][16];
-  __shared__ float sm_acc[NW][G][D];
-
-  int s, g, p, start, end, nps;
-  if (!decode_setup<D, B, G, NW>(a, s, g, p, start, end, nps)) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = uniform(threadIdx.x / kWave);
-  const int Hq = a.Hkv * G;
   const int t = lane % B;   // token of this lane in q.k
   const int cg = lane / B;  // its chunk group
+  WorkItem it;
+  if (!item_ids<NW>(a, it)) return;
+  const int Hq = a.Hkv * G;
 
-  float qr[G][CPL][X];
+  // the length decides whether the item is empty (most of the grid when the
+  // batch is ragged); then the partition's table slice and the queries load together
+  const int L = a.context_lens[it.s];
+  if (!item_extent<D, B, G>(a, it, L)) return;
+  TableWindow tw;
+  tw.load(a.block_tables + (size_t)it.s * a.max_blocks, it.start / B, a.max_blocks);
+  u32x4 qv[G][CPL];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(
-          q + ((size_t)s * Hq + g * G + gi) * D + (cg + NCG * j) * X);
-#pragma unroll
-      for (int e = 0; e < X; ++e) qr[gi][j][e] = vec_elem<E>(v, e);
-    }
+    for (int j = 0; j < CPL; ++j)
+      qv[gi][j] = *reinterpret_cast<const u32x4*>(
+          q + ((size_t)it.s * Hq + it.g * G + gi) * D + (cg + NCG * j) * X);
 
   float m[G], ls[G], acc[G][ND];
 #pragma unroll
@@ -162,25 +214,32 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
     for (int k = 0; k < ND; ++k) acc[gi][k] = 0.f;
   }
 
-  const int* table = a.block_tables + (size_t)s * a.max_blocks;
-  const int lb_end = (end + B - 1) / B;
-  for (int lb = start / B + w; lb < lb_end; lb += NW) {
-    const int pb = min(max(table[lb], 0), a.num_blocks - 1);
-    const size_t base = ((size_t)pb * a.Hkv + g) * (size_t)(D * B);
-    const E* kb = k_pool + base;
-    const E* vb = v_pool + base;
-    u32x4 kr[CPL];
+  struct Tile {
+    u32x4 k[CPL];
+    u32x4 v[NVT][ND];
+  };
+  const int lb_first = it.start / B;
+  const int n = (it.end + B - 1) / B - lb_first;
+  const size_t head_off = (size_t)it.g * (D * B);
+  const size_t blk_stride = (size_t)a.Hkv * (D * B);
+
+  auto load = [&](int k, Tile& tl) {
+    const int pb = tw.at(lb_first + k, a.num_blocks);
+    const E* kb = k_pool + pb * blk_stride + head_off;
+    const E* vb = v_pool + pb * blk_stride + head_off;
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
-      kr[j] = *reinterpret_cast<const u32x4*>(kb + ((cg + NCG * j) * B + t) * X);
-    u32x4 vr[NVT][ND];
+      tl.k[j] = *reinterpret_cast<const u32x4*>(kb + ((cg + NCG * j) * B + t) * X);
 #pragma unroll
     for (int tc = 0; tc < NVT; ++tc)
 #pragma unroll
-      for (int k = 0; k < ND; ++k)
-        vr[tc][k] = *reinterpret_cast<const u32x4*>(vb + (lane + kWave * k) * B + tc * X);
+      for (int k2 = 0; k2 < ND; ++k2)
+        tl.v[tc][k2] = *reinterpret_cast<const u32x4*>(vb + (lane + kWave * k2) * B + tc * X);
+  };
 
-    const bool valid = lb * B + t < end;
+  auto compute = [&](int k, const Tile& tl) {
+    const int tok0 = (lb_first + k) * B;
+    const bool valid = tok0 + t < it.end;
     float pr[G];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
@@ -188,7 +247,8 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
 #pragma unroll
       for (int j = 0; j < CPL; ++j)
 #pragma unroll
-        for (int e = 0; e < X; ++e) sc = fmaf(qr[gi][j][e], vec_elem<E>(kr[j], e), sc);
+        for (int e = 0; e < X; ++e)
+          sc = fmaf(vec_elem<E>(qv[gi][j], e), vec_elem<E>(tl.k[j], e), sc);
       if (NCG >= 4) sc += shfl_xor_f(sc, 16);
       if (NCG >= 2) sc += shfl_xor_f(sc, 32);
       sc = valid ? sc * a.scale_log2e : -INFINITY;
@@ -200,154 +260,161 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
       pr[gi] = fast_exp2(sc - mn);
       ls[gi] = ls[gi] * alpha + (cg == 0 ? pr[gi] : 0.f);
 #pragma unroll
-      for (int k = 0; k < ND; ++k) acc[gi][k] *= alpha;
+      for (int k2 = 0; k2 < ND; ++k2) acc[gi][k2] *= alpha;
       m[gi] = mn;
     }
-    const int tok0 = lb * B;
 #pragma unroll
     for (int tc = 0; tc < NVT; ++tc)
 #pragma unroll
       for (int e = 0; e < X; ++e) {
         const int tt = tc * X + e;
-        if (tok0 + tt < end) {
+        if (tok0 + tt < it.end) {
 #pragma unroll
           for (int gi = 0; gi < G; ++gi) {
             const float pt = read_lane(pr[gi], tt);
 #pragma unroll
-            for (int k = 0; k < ND; ++k) acc[gi][k] = fmaf(pt, vec_elem<E>(vr[tc][k], e), acc[gi][k]);
+            for (int k2 = 0; k2 < ND; ++k2)
+              acc[gi][k2] = fmaf(pt, vec_elem<E>(tl.v[tc][k2], e), acc[gi][k2]);
           }
         }
       }
-  }
+  };
+
+  pipelined<Tile>(n, load, compute);
 
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     const float l = wave_sum(ls[gi]);
-    if (lane == 0) {
-      sm_m[w][gi] = m[gi];
-      sm_l[w][gi] = l;
-    }
+    const RowSink dst = row_sink<D, G>(a, it, gi);
+    const float scl = dst.ml ? 1.f : 1.f / l;
 #pragma unroll
-    for (int k = 0; k < ND; ++k) sm_acc[w][gi][lane + kWave * k] = acc[gi][k];
+    for (int k = 0; k < ND; ++k) dst.acc[lane + kWave * k] = acc[gi][k] * scl;
+    if (dst.ml && lane == 0) {
+      dst.ml[0] = m[gi];
+      dst.ml[1] = l;
+    }
   }
-  __syncthreads();
-  merge_and_store<D, G, NW>(a, s, g, p, nps, sm_m, sm_l, sm_acc);
 }
 
 // ---------------------------------------------------------------------------
-// MFMA main kernel (bf16, G <= 16).  Tile = 32 tokens.
+// MFMA main kernel (bf16, G <= 16).  Tile = 32 tokens, as two 16-token halves
+// th = 0, 1 (for B = 16, one KV block each).
 // v_mfma_f32_16x16x32_bf16 operand layout (lane l, c = l / 16, r = l % 16):
 //   A[16 x 32]: lane holds row r, k = 8c .. 8c+7;  B[32 x 16]: col r, k = 8c .. 8c+7;
 //   C[16 x 16]: lane holds col r, rows 4c .. 4c+3.
-// q.k:  C_th[m][n] = sum_d K[tok_th(m)][d] Q[n][d], tok_th(m) = 8(m/4) + 4th + m%4,
-//       so lane (c, r) ends with scores of head r for tile tokens 8c + 4th + i:
-//       eight consecutive tokens 8c .. 8c+7 over th = 0, 1.
-// p.v:  C_dt[m][n] = sum_t V[t][16dt + m] P[n][t] with the k index = tile token
-//       8c + i, which is exactly the eight scores the lane already holds, and
-//       exactly the 16 bytes V stores for dim 16dt + r at tokens 8c .. 8c+7.
+// q.k:  C_th[m][n] = sum_d K[16th + m][d] Q[n][d]: the A operand of lane (c, r)
+//       is token 16th + r, dims 32j + 8c .. +7 -- one 16-byte K vector; for a
+//       fixed c the 16 lanes r read 16 consecutive tokens, 256 contiguous bytes.
+//       Lane (c, r) ends with the scores of head r at tokens 16th + 4c + i.
+// p.v:  O^T = V^T P^T with the MFMA k index 8c + 4th + i standing for tile token
+//       16th + 4c + i -- exactly the eight scores lane (c, r) holds, so P needs
+//       no shuffle.  The A operand of lane (c, r) is dim 16dt + r at those
+//       tokens: two 8-byte runs of the V row (tokens 4c .. 4c+3 of each half).
 // ---------------------------------------------------------------------------
 template <int D, int B, int G, int NW>
-__global__ __launch_bounds__(NW* kWave) void pa_mfma_kernel(DecodeArgs a,
-                                                             const uint16_t* __restrict__ q,
-                                                             const uint16_t* __restrict__ k_pool,
-                                                             const uint16_t* __restrict__ v_pool) {
+__global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
+                                                                const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ k_pool,
+                                                                const uint16_t* __restrict__ v_pool) {
   constexpr int TILE = 32;
   constexpr int NJ = D / 32;   // q.k k-steps
   constexpr int NDT = D / 16;  // p.v output dim tiles
   static_assert(G >= 1 && G <= 16 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-  __shared__ float sm_m[NW][16], sm_l[NW][16];
-  __shared__ float sm_acc[NW][G][D];
-
-  int s, g, p, start, end, nps;
-  if (!decode_setup<D, B, G, NW>(a, s, g, p, start, end, nps)) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = uniform(threadIdx.x / kWave);
-  const int Hq = a.Hkv * G;
   const int c = lane >> 4, r = lane & 15;
+  WorkItem it;
+  if (!item_ids<NW>(a, it)) return;
+  const int Hq = a.Hkv * G;
 
+  // the length decides whether the item is empty (most of the grid when the
+  // batch is ragged); then the partition's table slice and the queries load together
+  const int L = a.context_lens[it.s];
+  if (!item_extent<D, B, G>(a, it, L)) return;
+  TableWindow tw;
+  tw.load(a.block_tables + (size_t)it.s * a.max_blocks, it.start / B, a.max_blocks);
   bf16x8 qb[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < G)
-      v = *reinterpret_cast<const u32x4*>(q + ((size_t)s * Hq + g * G + r) * D + 8 * (4 * j + c));
+      v = *reinterpret_cast<const u32x4*>(q + ((size_t)it.s * Hq + it.g * G + r) * D +
+                                          8 * (4 * j + c));
     qb[j] = __builtin_bit_cast(bf16x8, v);
   }
-  // tile tokens this lane loads: K rows for th = 0, 1 and its V run 8c .. 8c+7
-  int ktok[2];
-#pragma unroll
-  for (int th = 0; th < 2; ++th) ktok[th] = 8 * (r >> 2) + 4 * th + (r & 3);
-  const int vtok = 8 * c;
 
   float m = -INFINITY, ls = 0.f;
   f32x4 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int* table = a.block_tables + (size_t)s * a.max_blocks;
-  const int t_end = (end + TILE - 1) / TILE;
-  const int nb_end = (end + B - 1) / B;
-  const size_t head_off = (size_t)g * (D * B);
+  struct Tile {
+    u32x4 k[2][NJ];
+    u32x2 v[2][NDT];
+  };
+  const int t_first = it.start / TILE;
+  const int n = (it.end + TILE - 1) / TILE - t_first;
+  const int nb_last = (it.end + B - 1) / B - 1;  // last logical block of the partition
+  const size_t head_off = (size_t)it.g * (D * B);
   const size_t blk_stride = (size_t)a.Hkv * (D * B);
-  for (int ti = start / TILE + w; ti < t_end; ti += NW) {
-    const int T0 = ti * TILE;
-    const int lb0 = T0 / B;
-    const int pb0 = min(max(table[lb0], 0), a.num_blocks - 1);
-    int pb1 = pb0;
-    if (B == 16 && lb0 + 1 < nb_end) pb1 = min(max(table[lb0 + 1], 0), a.num_blocks - 1);
-    const uint16_t* kb0 = k_pool + pb0 * blk_stride + head_off;
-    const uint16_t* kb1 = k_pool + pb1 * blk_stride + head_off;
-    const uint16_t* vb0 = v_pool + pb0 * blk_stride + head_off;
-    const uint16_t* vb1 = v_pool + pb1 * blk_stride + head_off;
 
-    u32x4 ka[2][NJ];
+  auto load = [&](int k, Tile& tl) {
+    const int lb0 = (t_first + k) * TILE / B;
+    const int pb0 = tw.at(lb0, a.num_blocks);
+    // B = 16: the tile's second block; past the partition end it repeats the
+    // first (those tokens are masked)
+    const int pb1 = B == 16 ? tw.at(min(lb0 + 1, nb_last), a.num_blocks) : pb0;
 #pragma unroll
     for (int th = 0; th < 2; ++th) {
-      const uint16_t* kb = (B == 16 && ktok[th] >= 16) ? kb1 : kb0;
-      const int off = ktok[th] % B;
+      const size_t blk = (B == 16 && th == 1) ? pb1 : pb0;
+      const int tok = (B == 16 ? 0 : 16 * th);  // token offset of this half in its block
+      const uint16_t* kb = k_pool + blk * blk_stride + head_off;
+      const uint16_t* vb = v_pool + blk * blk_stride + head_off;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        ka[th][j] = *reinterpret_cast<const u32x4*>(kb + ((size_t)(4 * j + c) * B + off) * 8);
-    }
-    u32x4 va[NDT];
-    {
-      const uint16_t* vb = (B == 16 && vtok >= 16) ? vb1 : vb0;
-      const int off = vtok % B;
+        tl.k[th][j] =
+            *reinterpret_cast<const u32x4*>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        va[dt] = *reinterpret_cast<const u32x4*>(vb + (size_t)(16 * dt + r) * B + off);
+        tl.v[th][dt] = *reinterpret_cast<const u32x2*>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
     }
+  };
 
+  auto compute = [&](int k, Tile& tl) {
+    const int T0 = (t_first + k) * TILE;
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int th = 0; th < 2; ++th)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[th][j]),
+        sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tl.k[th][j]),
                                                            qb[j], sacc[th], 0, 0, 0);
-
+    // sv[4th + i]: token T0 + 16th + 4c + i
     float sv[8];
 #pragma unroll
     for (int th = 0; th < 2; ++th)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * a.scale_log2e;
-    const bool partial = T0 + TILE > end;
-    if (partial) {
+    if (T0 + TILE > it.end) {  // the partition's last, partial tile
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (T0 + vtok + k >= end) sv[k] = -INFINITY;
-      const int nv = min(max(end - (T0 + vtok), 0), 8);
+      for (int th = 0; th < 2; ++th) {
+        const int nv = min(max(it.end - (T0 + 16 * th + 4 * c), 0), 4);
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const uint32_t mk = (2 * wd < nv ? 0x0000ffffu : 0u) | (2 * wd + 1 < nv ? 0xffff0000u : 0u);
+        for (int i = 0; i < 4; ++i)
+          if (i >= nv) sv[4 * th + i] = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) va[dt][wd] &= mk;
+        for (int wd = 0; wd < 2; ++wd) {
+          const uint32_t mk =
+              (2 * wd < nv ? 0x0000ffffu : 0u) | (2 * wd + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt][wd] &= mk;
+        }
       }
     }
     float mx = sv[0];
 #pragma unroll
-    for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
     const float mn = fmaxf(m, mx);  // finite: tile token T0 is valid
@@ -372,65 +439,113 @@ __global__ __launch_bounds__(NW* kWave) void pa_mfma_kernel(DecodeArgs a,
     const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
+      const u32x4 va = {tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
       acc[dt] *= alpha;
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[dt]), ph,
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), ph,
                                                         acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[dt]), pl,
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pl,
                                                         acc[dt], 0, 0, 0);
     }
-  }
+  };
+
+  pipelined<Tile>(n, load, compute);
 
   ls += shfl_xor_f(ls, 16);
   ls += shfl_xor_f(ls, 32);
-  if (c == 0 && r < G) {
-    sm_m[w][r] = m;
-    sm_l[w][r] = ls;
-  }
   if (r < G) {
+    const RowSink dst = row_sink<D, G>(a, it, r);
+    const float scl = dst.ml ? 1.f : 1.f / ls;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<f32x4*>(&sm_acc[w][r][16 * dt + 4 * c]) = acc[dt];
+      *reinterpret_cast<f32x4*>(dst.acc + 16 * dt + 4 * c) = acc[dt] * scl;
+    if (dst.ml && c == 0) {
+      dst.ml[0] = m;
+      dst.ml[1] = ls;
+    }
   }
-  __syncthreads();
-  merge_and_store<D, G, NW>(a, s, g, p, nps, sm_m, sm_l, sm_acc);
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of partition partials: one wave per (sequence, query head).
+// Log-sum-exp merge of partition partials: one 256-thread workgroup per
+// (sequence, query head) row.  Thread (pg, col) folds partitions pg, pg + PG, ...
+// of float4 column col into a local (max, sum, acc) state; U partitions per
+// thread are loaded at once (indices past the end re-read the last partition
+// with weight 0), so one round trip covers U * PG partitions.  The PG local
+// states are then merged through LDS.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kWave) void pa_reduce_kernel(float* __restrict__ out,
-                                                          const float* __restrict__ part_acc,
-                                                          const float* __restrict__ part_ml,
-                                                          const int* __restrict__ context_lens,
-                                                          int Hq, int max_blocks, int B, int nparts,
-                                                          int P) {
-  constexpr int ND = D / kWave;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void pa_reduce_kernel(float* __restrict__ out,
+                                                        const float* __restrict__ part_acc,
+                                                        const float* __restrict__ part_ml,
+                                                        const int* __restrict__ context_lens,
+                                                        int Hq, int max_blocks, int B, int nparts,
+                                                        int P) {
+  constexpr int C4 = D / 4;      // float4 columns of a row
+  constexpr int PG = 256 / C4;   // partition groups
+  constexpr int U = 64 / PG;     // partitions per thread per round
+  __shared__ float sm_m[PG], sm_l[PG];
+  __shared__ f32x4 sm_acc[PG][C4];
+
   const int row = blockIdx.x;  // s * Hq + h
   const int s = row / Hq;
   const int L = min(context_lens[s], max_blocks * B);
   const int n = L <= 0 ? 0 : min((L + P - 1) / P, nparts);
   if (n <= 1) return;  // the main kernel wrote this row
+  const int col = threadIdx.x % C4, pg = threadIdx.x / C4;
   const float* ml = part_ml + (size_t)row * nparts * 2;
-  const float* pa = part_acc + (size_t)row * nparts * D;
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += kWave) M = fmaxf(M, ml[2 * i]);
-  M = wave_max(M);
-  float den = 0.f;
-  for (int i = lane; i < n; i += kWave) den += fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
-  den = wave_sum(den);
-  float num[ND];
+  const f32x4* pa = reinterpret_cast<const f32x4*>(part_acc + (size_t)row * nparts * D);
+
+  float M = -INFINITY, den = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = pg; i0 < n; i0 += PG * U) {
+    float mi[U], li[U];
+    f32x4 ai[U];
 #pragma unroll
-  for (int k = 0; k < ND; ++k) num[k] = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float f = fast_exp2(ml[2 * i] - M);
+    for (int u = 0; u < U; ++u) {
+      const int i = min(i0 + u * PG, n - 1);
+      mi[u] = ml[2 * i];
+      li[u] = ml[2 * i + 1];
+      ai[u] = pa[(size_t)i * C4 + col];
+    }
+    float mn = M;
 #pragma unroll
-    for (int k = 0; k < ND; ++k) num[k] = fmaf(f, pa[(size_t)i * D + lane + kWave * k], num[k]);
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u * PG >= n) mi[u] = -INFINITY;
+      mn = fmaxf(mn, mi[u]);
+    }
+    const float fo = fast_exp2(M - mn);  // M = -inf gives 0
+    den *= fo;
+    acc *= fo;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = fast_exp2(mi[u] - mn);  // -inf (past the end) gives 0
+      den = fmaf(f, li[u], den);
+      acc += f * ai[u];
+    }
+    M = mn;
   }
-  const float inv = 1.f / den;
+  if (col == 0) {
+    sm_m[pg] = M;
+    sm_l[pg] = den;
+  }
+  sm_acc[pg][col] = acc;
+  __syncthreads();
+  if (threadIdx.x < C4) {
+    float Mg = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < ND; ++k) out[(size_t)row * D + lane + kWave * k] = num[k] * inv;
+    for (int j = 0; j < PG; ++j) Mg = fmaxf(Mg, sm_m[j]);
+    float dg = 0.f;
+    f32x4 ag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < PG; ++j) {
+      const float mj = sm_m[j];
+      const float f = (mj == -INFINITY) ? 0.f : fast_exp2(mj - Mg);
+      dg = fmaf(f, sm_l[j], dg);
+      ag += f * sm_acc[j][threadIdx.x];
+    }
+    const float inv = 1.f / dg;
+    reinterpret_cast<f32x4*>(out + (size_t)row * D)[threadIdx.x] = ag * inv;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -517,19 +632,21 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   const int G = Hq / Hkv;
   if (!shape_supported(D, B, G)) return PKV_EUNSUPPORTED;
   const int P = partition_size > 0 ? partition_size : kDefaultPartition;
-  if (P % 32 != 0 || P % B != 0) return PKV_EINVAL;
+  if (P % 32 != 0 || P % B != 0 || P / B > kMaxPartitionBlocks) return PKV_EINVAL;
   if (S == 0) return PKV_OK;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !block_tables || !context_lens)
     return PKV_EINVAL;
   const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
   const int64_t nparts = num_partitions(mcl, P);
-  const int64_t g = (int64_t)S * Hkv * nparts;
-  if (g > 0x7fffffffLL || (int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
+  const int64_t items = (int64_t)S * Hkv * nparts;
+  if (items > 0x7fffffffLL || (int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
   *a = DecodeArgs{};
   a->out = out;
   a->block_tables = block_tables;
   a->context_lens = context_lens;
+  a->SG = S * Hkv;
+  a->items = (int)items;
   a->Hkv = Hkv;
   a->max_blocks = max_blocks;
   a->num_blocks = num_blocks;
@@ -542,7 +659,7 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
     a->part_acc = (float*)workspace;
     a->part_ml = a->part_acc + (size_t)S * Hq * nparts * D;
   }
-  *groups = g;
+  *groups = (items + kWavesPerGroup - 1) / kWavesPerGroup;
   return PKV_OK;
 }
 
@@ -560,10 +677,10 @@ static pkv_status launch_reduce_kernel(const DecodeArgs& a, int S, int Hq, int D
                                        hipStream_t st) {
   if (a.nparts <= 1) return PKV_OK;
   if (D == 64)
-    pa_reduce_kernel<64><<<(unsigned)(S * Hq), kWave, 0, st>>>(
+    pa_reduce_kernel<64><<<(unsigned)(S * Hq), 256, 0, st>>>(
         a.out, a.part_acc, a.part_ml, a.context_lens, Hq, a.max_blocks, B, a.nparts, a.P);
   else
-    pa_reduce_kernel<128><<<(unsigned)(S * Hq), kWave, 0, st>>>(
+    pa_reduce_kernel<128><<<(unsigned)(S * Hq), 256, 0, st>>>(
         a.out, a.part_acc, a.part_ml, a.context_lens, Hq, a.max_blocks, B, a.nparts, a.P);
   return launch_status();
 }
@@ -612,7 +729,7 @@ extern "C" pkv_status pkv_paged_attention_reduce(
     return PKV_EINVAL;
   if (!(D == 64 || D == 128) || !(B == 16 || B == 32)) return PKV_EUNSUPPORTED;
   const int P = partition_size > 0 ? partition_size : kDefaultPartition;
-  if (P % 32 != 0 || P % B != 0) return PKV_EINVAL;
+  if (P % 32 != 0 || P % B != 0 || P / B > kMaxPartitionBlocks) return PKV_EINVAL;
   if (S == 0) return PKV_OK;
   if (!aligned16(out) || !context_lens) return PKV_EINVAL;
   const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
