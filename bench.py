@@ -155,6 +155,9 @@ class Batch:
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((c.S, c.Hq, c.D), dtype=torch.float32, device=dev)
         self.kv_bytes = w.kv_bytes
+        # blocks shared by several sequences are read with cached loads
+        self.shared_entries = bm.count_shared(ids)
+        self.shared_kv = self.shared_entries > 0
         torch.cuda.synchronize()
 
     @staticmethod
@@ -180,7 +183,8 @@ class Batch:
         if main_ev is not None:
             main_ev[0].record()
         pkv.paged_attention_main(self.out, self.q, self.k_pool, self.v_pool, self.tables,
-                                 self.lens, self.mcl, partition_size=self.P, workspace=self.ws)
+                                 self.lens, self.mcl, partition_size=self.P, workspace=self.ws,
+                                 shared_kv=self.shared_kv)
         if main_ev is not None:
             main_ev[1].record()
         rec(3)
@@ -347,6 +351,7 @@ def main() -> int:
         "partition_size": batch.P or 512, "new_tokens": 0 if batch.slots is None
         else int(batch.slots.shape[0]), "cow_copies": batch.n_pairs,
         "kv_bytes_per_step": batch.kv_bytes,
+        "shared_block_entries": batch.shared_entries,
         "pool_bytes_per_layer": batch.pool_bytes,
     }
     rec = {

@@ -60,6 +60,17 @@ typedef enum pkv_status {
 
 typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 
+/* Attention flags (bit set).
+ * PKV_ATTN_SHARED_KV: sequences of the batch share KV blocks (forked parallel
+ *   samples, shared prompt prefixes: [RTI] "Pages, from operating systems",
+ *   [ZENO] "Implementation Essentials", prefix sharing).  K/V are then read
+ *   with ordinary cached loads, so a block that several sequences read can be
+ *   served from L2 or the last-level cache after the first read.  Without it,
+ *   K/V are streamed with nontemporal loads, which is faster when every block
+ *   is read once per step.  Only a performance hint: results are identical.
+ *   pkv_bm_count_shared() tells whether a batch shares blocks. */
+enum { PKV_ATTN_SHARED_KV = 1u };
+
 const char* pkv_status_string(pkv_status s);
 
 /* ---------------------------------------------------------------------------
@@ -127,6 +138,12 @@ pkv_status pkv_bm_fill_batch(const pkv_bm* bm, const int64_t* seq_ids, int32_t n
                              int32_t max_blocks, int32_t* block_tables,
                              int32_t* context_lens);
 
+/* Table entries of the listed sequences whose block has refcount > 1 (blocks
+ * shared through fork), summed over the sequences, into *out.  Non-zero means
+ * the batch should be attended with PKV_ATTN_SHARED_KV. */
+pkv_status pkv_bm_count_shared(const pkv_bm* bm, const int64_t* seq_ids, int32_t n,
+                               int64_t* out);
+
 /* Whole-pool state for parity checks: refcounts[num_blocks] and the free queue
  * front to back in free_queue[0 .. *n_free) (room for num_blocks entries). */
 pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_queue,
@@ -187,6 +204,7 @@ size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
  *                 split and merged by a log-sum-exp reduce launch.
  *   workspace     device buffer of workspace_bytes >= pkv_attention_workspace_bytes
  *                 (may be NULL when that is 0)
+ *   flags         0 or PKV_ATTN_SHARED_KV (other bits: PKV_EINVAL)
  * Compiled shapes: D in {64, 128}, B in {16, 32}; bf16 with Hq/Hkv in
  * {1, 2, 4, 8}; fp32 with Hq/Hkv in {1, 2, 4, 8}.  Others: PKV_EUNSUPPORTED. */
 pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_pool,
@@ -196,7 +214,7 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_p
                                       int32_t num_blocks, int32_t max_context_len,
                                       float scale, int32_t partition_size, void* workspace,
                                       size_t workspace_bytes, pkv_dtype dtype,
-                                      void* hip_stream);
+                                      uint32_t flags, void* hip_stream);
 
 /* The two launches of pkv_paged_attention_decode, callable one at a time (for
  * per-kernel timing, or to put other work between them on the stream).
@@ -216,7 +234,8 @@ pkv_status pkv_paged_attention_main(float* out, const void* q, const void* k_poo
                                     int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
                                     int32_t num_blocks, int32_t max_context_len, float scale,
                                     int32_t partition_size, void* workspace,
-                                    size_t workspace_bytes, pkv_dtype dtype, void* hip_stream);
+                                    size_t workspace_bytes, pkv_dtype dtype, uint32_t flags,
+                                    void* hip_stream);
 pkv_status pkv_paged_attention_reduce(float* out, const int32_t* context_lens, int32_t S,
                                       int32_t Hq, int32_t D, int32_t B, int32_t max_blocks,
                                       int32_t max_context_len, int32_t partition_size,

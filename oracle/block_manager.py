@@ -153,6 +153,18 @@ class BlockManager:
         return tables, lens
 
 
+def count_shared(bm, seq_ids) -> int:
+    """Table entries of the listed sequences whose block is referenced by more
+    than one table (a block shared through fork, "Pages, from operating
+    systems"): the batch reads such a block once per sharer."""
+    total = 0
+    for sid in seq_ids:
+        if sid not in bm.tables:
+            raise BMError(ENOSEQ)
+        total += sum(1 for b in bm.tables[sid] if bm.ref[b] > 1)
+    return total
+
+
 def run_ops(bm, ops):
     """Apply a request script (see workloads.script / random_script).  Returns
     the status code of every op and the (slot, src, dst) of every append."""

@@ -30,9 +30,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 PKV_OK, PKV_EINVAL, PKV_ENOBLOCKS, PKV_ENOSEQ, PKV_EEXIST, PKV_EUNSUPPORTED, PKV_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
 PKV_F32, PKV_BF16 = 0, 1
+PKV_ATTN_SHARED_KV = 1
 
 _i32, _i64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
                               ctypes.c_size_t)
+_u32 = ctypes.c_uint32
 _pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
 
 # name -> (restype, argtypes); mirrors include/pkv.h
@@ -51,15 +53,17 @@ SIGNATURES = {
     "pkv_bm_block_table": (_i32, [_vp, _i64, _pi32, _i32]),
     "pkv_bm_fill_batch": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
     "pkv_bm_snapshot": (_i32, [_vp, _pi32, _pi32, _pi32]),
+    "pkv_bm_count_shared": (_i32, [_vp, _pi64, _i32, _pi64]),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
-                                          _vp]),
+                                          _u32, _vp]),
     "pkv_paged_attention_main": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                        _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
+                                        _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _u32,
+                                        _vp]),
     "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _vp, _sz, _vp]),
 }
@@ -186,6 +190,14 @@ class BlockManager:
                                      _np_ptr(lens, ctypes.c_int32)), "pkv_bm_fill_batch")
         return tables, lens
 
+    def count_shared(self, seq_ids) -> int:
+        """Table entries of these sequences whose block has refcount > 1."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        out = _i64()
+        _check(lib.pkv_bm_count_shared(self._h, _np_ptr(ids, ctypes.c_int64), ids.shape[0],
+                                       ctypes.byref(out)), "pkv_bm_count_shared")
+        return out.value
+
     def snapshot(self):
         ref = np.empty(self.num_blocks, np.int32)
         fq = np.empty(self.num_blocks, np.int32)
@@ -275,7 +287,7 @@ def pkv_attention_workspace_bytes(S: int, Hq: int, D: int, max_context_len: int,
 
 
 def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                    scale, partition_size, workspace):
+                    scale, partition_size, workspace, shared_kv):
     N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
     S, Hq = q.shape[0], q.shape[1]
     if tuple(q.shape) != (S, Hq, D) or q.dtype != k_pool.dtype:
@@ -295,28 +307,31 @@ def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_cont
     return (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
             _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, D,
             B, block_tables.shape[1], N, int(max_context_len), float(scale), int(partition_size),
-            ws_ptr, ws_bytes, _dtype_code(k_pool))
+            ws_ptr, ws_bytes, _dtype_code(k_pool), PKV_ATTN_SHARED_KV if shared_kv else 0)
 
 
 def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
                                max_context_len: int, scale: float | None = None,
-                               partition_size: int = 0, workspace=None, stream=None) -> None:
+                               partition_size: int = 0, workspace=None, stream=None,
+                               shared_kv: bool = False) -> None:
     """out[s, h] = softmax(q[s, h] K_s^T * scale) V_s through the block tables.
 
     out fp32 [S, Hq, D]; q [S, Hq, D] in the pool dtype; block_tables int32
     [S, max_blocks]; context_lens int32 [S].  `workspace` (a uint8 device tensor)
-    is needed when max_context_len exceeds one partition."""
+    is needed when max_context_len exceeds one partition.  `shared_kv` sets
+    PKV_ATTN_SHARED_KV (the batch shares blocks; a load-policy hint only)."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                           scale, partition_size, workspace)
+                           scale, partition_size, workspace, shared_kv)
     _check(lib.pkv_paged_attention_decode(*args, _stream(stream)), "pkv_paged_attention_decode")
 
 
 def pkv_paged_attention_main(out, q, k_pool, v_pool, block_tables, context_lens,
                              max_context_len: int, scale: float | None = None,
-                             partition_size: int = 0, workspace=None, stream=None) -> None:
+                             partition_size: int = 0, workspace=None, stream=None,
+                             shared_kv: bool = False) -> None:
     """The main launch of pkv_paged_attention_decode alone (same arguments)."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                           scale, partition_size, workspace)
+                           scale, partition_size, workspace, shared_kv)
     _check(lib.pkv_paged_attention_main(*args, _stream(stream)), "pkv_paged_attention_main")
 
 

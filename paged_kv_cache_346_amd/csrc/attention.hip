@@ -13,12 +13,19 @@
 // Work decomposition (not on the pages).  A work item is one (sequence, KV
 // head, partition of P tokens); ONE wave64 owns an item from start to finish, so
 // there is no cross-wave merge, no LDS and no barrier.  The whole GQA group of a
-// KV head lives in that wave, so each K/V byte is fetched from HBM once.  Items
-// are numbered partition-major and workgroups hold NW consecutive items; the
-// dispatcher deals consecutive workgroups round-robin to the 8 XCDs, so every XCD
-// gets a like share of each partition index (with the partition index fastest,
-// the partition-0 items -- most of the work when sequences are short -- would
-// pile onto a few XCDs).
+// KV head lives in that wave, so each K/V byte is fetched from HBM once.
+// Items are numbered partition-major, with the partition counted from the END
+// of its sequence and the farthest-from-the-end slice dispatched first:
+//   * the dispatcher deals consecutive workgroups round-robin to the 8 XCDs, so
+//     every XCD gets a like share of each slice (with the partition index
+//     fastest, the first partitions -- most of the work when sequences are
+//     short -- would pile onto a few XCDs);
+//   * every slice but the last holds only full partitions, and the last slice
+//     holds each sequence's final, partial one, so large items start first and
+//     small ones fill the tail of a ragged batch.
+// K/V tiles are read with nontemporal loads: the pool is streamed once per step
+// and nothing in it is reused by the step, so it should not displace other data
+// in the caches (measured 7-10% faster than ordinary loads on every workload).
 //
 // Each wave
 //   * reads the partition's slice of the block table once, one entry per lane,
@@ -74,6 +81,8 @@ struct DecodeArgs {
 };
 
 // One wave's share: sequence s, KV head g, partition p, tokens [start, end).
+// item_ids() stores the partition counted from the sequence's end in p;
+// item_extent() turns it into the partition index once the length is known.
 struct WorkItem {
   int s, g, p, start, end, nps;
 };
@@ -83,11 +92,11 @@ template <int NW>
 __device__ __forceinline__ bool item_ids(const DecodeArgs& a, WorkItem& it) {
   const int item = (int)blockIdx.x * NW + uniform((int)threadIdx.x / kWave);
   if (item >= a.items) return false;
-  it.p = item / a.SG;
-  const int sg = item - it.p * a.SG;
+  const int k = item / a.SG;
+  it.p = a.nparts - 1 - k;   // partitions counted from the sequence's end
+  const int sg = item - k * a.SG;
   it.g = sg % a.Hkv;
   it.s = sg / a.Hkv;
-  it.start = it.p * a.P;
   return true;
 }
 
@@ -96,14 +105,18 @@ __device__ __forceinline__ bool item_ids(const DecodeArgs& a, WorkItem& it) {
 template <int D, int B, int G>
 __device__ __forceinline__ bool item_extent(const DecodeArgs& a, WorkItem& it, int L) {
   L = min(L, a.max_blocks * B);
+  const int pe = it.p;                  // partition counted from the end
+  const int np = L <= 0 ? 0 : min((L + a.P - 1) / a.P, a.nparts);
+  it.p = np - 1 - pe;
+  it.start = it.p * a.P;
   if (L <= 0) {
-    if (it.p == 0) {
+    if (pe == 0) {
       float* o = a.out + ((size_t)it.s * a.Hkv * G + (size_t)it.g * G) * D;
       for (int i = threadIdx.x & (kWave - 1); i < G * D; i += kWave) o[i] = 0.f;
     }
     return false;
   }
-  if (it.start >= L) return false;
+  if (it.p < 0) return false;
   it.end = min(L, it.start + a.P);
   it.nps = min((L + a.P - 1) / a.P, a.nparts);
   return true;
@@ -143,6 +156,26 @@ __device__ __forceinline__ RowSink row_sink(const DecodeArgs& a, const WorkItem&
   return RowSink{a.part_acc + row * D, a.part_ml + 2 * row};
 }
 
+// A 16- or 8-byte vector load of pool data: nontemporal when the step streams
+// the pool (every block read once), ordinary when blocks are shared by several
+// sequences of the batch and a second read can hit in L2 or the last-level cache.
+template <bool NT, typename V>
+__device__ __forceinline__ V pool_load(const uint16_t* p) {
+  const V* v = reinterpret_cast<const V*>(p);
+  if constexpr (NT)
+    return __builtin_nontemporal_load(v);
+  else
+    return *v;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ V pool_load(const float* p) {
+  const V* v = reinterpret_cast<const V*>(p);
+  if constexpr (NT)
+    return __builtin_nontemporal_load(v);
+  else
+    return *v;
+}
+
 // Run `compute(k, tile)` over a wave's n tiles with the loads of tile k+1 issued
 // before tile k is computed.  Two register buffers alternate; every load in the
 // steady loop is unconditional, so the compiler's wait before each compute only
@@ -171,7 +204,7 @@ __device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute)
 // ---------------------------------------------------------------------------
 // VALU main kernel.  E = float or uint16_t (bf16 bits).  Tile = one KV block.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int B, int G, int NW>
+template <typename E, int D, int B, int G, int NW, bool NT>
 __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
                                                              const E* __restrict__ q,
                                                              const E* __restrict__ k_pool,
@@ -229,12 +262,12 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
     const E* vb = v_pool + pb * blk_stride + head_off;
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
-      tl.k[j] = *reinterpret_cast<const u32x4*>(kb + ((cg + NCG * j) * B + t) * X);
+      tl.k[j] = pool_load<NT, u32x4>(kb + ((cg + NCG * j) * B + t) * X);
 #pragma unroll
     for (int tc = 0; tc < NVT; ++tc)
 #pragma unroll
       for (int k2 = 0; k2 < ND; ++k2)
-        tl.v[tc][k2] = *reinterpret_cast<const u32x4*>(vb + (lane + kWave * k2) * B + tc * X);
+        tl.v[tc][k2] = pool_load<NT, u32x4>(vb + (lane + kWave * k2) * B + tc * X);
   };
 
   auto compute = [&](int k, const Tile& tl) {
@@ -311,7 +344,7 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
 //       no shuffle.  The A operand of lane (c, r) is dim 16dt + r at those
 //       tokens: two 8-byte runs of the V row (tokens 4c .. 4c+3 of each half).
 // ---------------------------------------------------------------------------
-template <int D, int B, int G, int NW>
+template <int D, int B, int G, int NW, bool NT>
 __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
                                                                 const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ k_pool,
@@ -321,6 +354,11 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
   constexpr int NDT = D / 16;  // p.v output dim tiles
   static_assert(G >= 1 && G <= 16 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  // At B = 32 one V load instruction covers half of each 64-byte dim row and the
+  // other half follows in the next instruction; a nontemporal first read lets
+  // the line go before the second arrives (measured 17% slower), so V streams
+  // only at B = 16, where every V instruction reads whole lines.
+  constexpr bool kNtV = NT && B == 16;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane >> 4, r = lane & 15;
@@ -373,11 +411,10 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
       const uint16_t* vb = v_pool + blk * blk_stride + head_off;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        tl.k[th][j] =
-            *reinterpret_cast<const u32x4*>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+        tl.k[th][j] = pool_load<NT, u32x4>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        tl.v[th][dt] = *reinterpret_cast<const u32x2*>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+        tl.v[th][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
     }
   };
 
@@ -551,43 +588,52 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(float* __restrict__ out,
 // ---------------------------------------------------------------------------
 // Host dispatch.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int B, int G>
-static void launch_main(const DecodeArgs& a, unsigned grid, const void* q, const void* kp,
-                        const void* vp, hipStream_t st) {
+template <typename E, int D, int B, int G, bool NT>
+static void launch_main_nt(const DecodeArgs& a, unsigned grid, const void* q, const void* kp,
+                           const void* vp, hipStream_t st) {
   constexpr bool kMfma = sizeof(E) == 2 && G >= 4;
   if constexpr (kMfma)
-    pa_mfma_kernel<D, B, G, kWavesPerGroup><<<grid, kWavesPerGroup * kWave, 0, st>>>(
+    pa_mfma_kernel<D, B, G, kWavesPerGroup, NT><<<grid, kWavesPerGroup * kWave, 0, st>>>(
         a, (const uint16_t*)q, (const uint16_t*)kp, (const uint16_t*)vp);
   else
-    pa_valu_kernel<E, D, B, G, kWavesPerGroup><<<grid, kWavesPerGroup * kWave, 0, st>>>(
+    pa_valu_kernel<E, D, B, G, kWavesPerGroup, NT><<<grid, kWavesPerGroup * kWave, 0, st>>>(
         a, (const E*)q, (const E*)kp, (const E*)vp);
 }
 
+template <typename E, int D, int B, int G>
+static void launch_main(bool stream, const DecodeArgs& a, unsigned grid, const void* q,
+                        const void* kp, const void* vp, hipStream_t st) {
+  if (stream)
+    launch_main_nt<E, D, B, G, true>(a, grid, q, kp, vp, st);
+  else
+    launch_main_nt<E, D, B, G, false>(a, grid, q, kp, vp, st);
+}
+
 template <typename E, int D, int B>
-static bool dispatch_g(int G, const DecodeArgs& a, unsigned grid, const void* q, const void* kp,
-                       const void* vp, hipStream_t st) {
+static bool dispatch_g(int G, bool stream, const DecodeArgs& a, unsigned grid, const void* q,
+                       const void* kp, const void* vp, hipStream_t st) {
   switch (G) {
-    case 1: launch_main<E, D, B, 1>(a, grid, q, kp, vp, st); return true;
-    case 2: launch_main<E, D, B, 2>(a, grid, q, kp, vp, st); return true;
-    case 4: launch_main<E, D, B, 4>(a, grid, q, kp, vp, st); return true;
-    case 8: launch_main<E, D, B, 8>(a, grid, q, kp, vp, st); return true;
+    case 1: launch_main<E, D, B, 1>(stream, a, grid, q, kp, vp, st); return true;
+    case 2: launch_main<E, D, B, 2>(stream, a, grid, q, kp, vp, st); return true;
+    case 4: launch_main<E, D, B, 4>(stream, a, grid, q, kp, vp, st); return true;
+    case 8: launch_main<E, D, B, 8>(stream, a, grid, q, kp, vp, st); return true;
     default: return false;
   }
 }
 
 template <typename E, int D>
-static bool dispatch_b(int B, int G, const DecodeArgs& a, unsigned grid, const void* q,
-                       const void* kp, const void* vp, hipStream_t st) {
-  if (B == 16) return dispatch_g<E, D, 16>(G, a, grid, q, kp, vp, st);
-  if (B == 32) return dispatch_g<E, D, 32>(G, a, grid, q, kp, vp, st);
+static bool dispatch_b(int B, int G, bool stream, const DecodeArgs& a, unsigned grid,
+                       const void* q, const void* kp, const void* vp, hipStream_t st) {
+  if (B == 16) return dispatch_g<E, D, 16>(G, stream, a, grid, q, kp, vp, st);
+  if (B == 32) return dispatch_g<E, D, 32>(G, stream, a, grid, q, kp, vp, st);
   return false;
 }
 
 template <typename E>
-static bool dispatch_d(int D, int B, int G, const DecodeArgs& a, unsigned grid, const void* q,
-                       const void* kp, const void* vp, hipStream_t st) {
-  if (D == 64) return dispatch_b<E, 64>(B, G, a, grid, q, kp, vp, st);
-  if (D == 128) return dispatch_b<E, 128>(B, G, a, grid, q, kp, vp, st);
+static bool dispatch_d(int D, int B, int G, bool stream, const DecodeArgs& a, unsigned grid,
+                       const void* q, const void* kp, const void* vp, hipStream_t st) {
+  if (D == 64) return dispatch_b<E, 64>(B, G, stream, a, grid, q, kp, vp, st);
+  if (D == 128) return dispatch_b<E, 128>(B, G, stream, a, grid, q, kp, vp, st);
   return false;
 }
 
@@ -623,8 +669,9 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
                                  int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                  int32_t max_blocks, int32_t num_blocks, int32_t max_context_len,
                                  float scale, int32_t partition_size, void* workspace,
-                                 size_t workspace_bytes, pkv_dtype dtype) {
+                                 size_t workspace_bytes, pkv_dtype dtype, uint32_t flags) {
   *groups = 0;
+  if (flags & ~(uint32_t)PKV_ATTN_SHARED_KV) return PKV_EINVAL;
   if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 || num_blocks <= 0 ||
       max_context_len < 0 || partition_size < 0 || !std::isfinite(scale))
     return PKV_EINVAL;
@@ -665,10 +712,12 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
 
 static pkv_status launch_main_kernel(const DecodeArgs& a, int64_t groups, const void* q,
                                      const void* k_pool, const void* v_pool, int D, int B, int G,
-                                     pkv_dtype dtype, hipStream_t st) {
-  const bool ok = dtype == PKV_F32
-                      ? dispatch_d<float>(D, B, G, a, (unsigned)groups, q, k_pool, v_pool, st)
-                      : dispatch_d<uint16_t>(D, B, G, a, (unsigned)groups, q, k_pool, v_pool, st);
+                                     pkv_dtype dtype, uint32_t flags, hipStream_t st) {
+  const bool stream = (flags & PKV_ATTN_SHARED_KV) == 0;
+  const bool ok =
+      dtype == PKV_F32
+          ? dispatch_d<float>(D, B, G, stream, a, (unsigned)groups, q, k_pool, v_pool, st)
+          : dispatch_d<uint16_t>(D, B, G, stream, a, (unsigned)groups, q, k_pool, v_pool, st);
   if (!ok) return PKV_EUNSUPPORTED;
   return launch_status();
 }
@@ -692,15 +741,15 @@ extern "C" pkv_status pkv_paged_attention_decode(
     const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
     int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-    void* hip_stream) {
+    uint32_t flags, void* hip_stream) {
   DecodeArgs a;
   int64_t groups;
   pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, block_tables, context_lens,
                                  S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
-                                 partition_size, workspace, workspace_bytes, dtype);
+                                 partition_size, workspace, workspace_bytes, dtype, flags);
   if (st != PKV_OK || groups == 0) return st;
   hipStream_t hs = (hipStream_t)hip_stream;
-  st = launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, hs);
+  st = launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, flags, hs);
   if (st != PKV_OK) return st;
   return launch_reduce_kernel(a, S, Hq, D, B, hs);
 }
@@ -710,14 +759,14 @@ extern "C" pkv_status pkv_paged_attention_main(
     const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
     int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-    void* hip_stream) {
+    uint32_t flags, void* hip_stream) {
   DecodeArgs a;
   int64_t groups;
   pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, block_tables, context_lens,
                                  S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
-                                 partition_size, workspace, workspace_bytes, dtype);
+                                 partition_size, workspace, workspace_bytes, dtype, flags);
   if (st != PKV_OK || groups == 0) return st;
-  return launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype,
+  return launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, flags,
                             (hipStream_t)hip_stream);
 }
 

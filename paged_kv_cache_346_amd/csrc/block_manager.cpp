@@ -218,6 +218,19 @@ pkv_status pkv_bm_fill_batch(const pkv_bm* bm, const int64_t* seq_ids, int32_t n
   return PKV_OK;
 }
 
+pkv_status pkv_bm_count_shared(const pkv_bm* bm, const int64_t* seq_ids, int32_t n,
+                               int64_t* out) {
+  if (!bm || n < 0 || !out || (n > 0 && !seq_ids)) return PKV_EINVAL;
+  int64_t shared = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PKV_ENOSEQ;
+    for (int32_t b : it->second.table) shared += bm->ref[b] > 1;
+  }
+  *out = shared;
+  return PKV_OK;
+}
+
 pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_queue,
                            int32_t* n_free) {
   if (!bm || !refcounts || !free_queue || !n_free) return PKV_EINVAL;

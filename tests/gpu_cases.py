@@ -72,7 +72,9 @@ class Case:
         self.bm = bm
 
     # -- device path -----------------------------------------------------------
-    def run_device(self, pkv, partition_size=None):
+    def run_device(self, pkv, partition_size=None, shared_kv=None):
+        """shared_kv None: set PKV_ATTN_SHARED_KV when the batch shares blocks
+        (the benchmark's choice)."""
         c = self.w.cfg
         P = c.partition_size if partition_size is None else partition_size
         kp, vp = to_dev(self.k_pool), to_dev(self.v_pool)
@@ -86,9 +88,11 @@ class Case:
         mcl = int(self.lens.max())
         nbytes = pkv.attention_workspace_bytes(c.S, c.Hq, c.D, mcl, P)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        if shared_kv is None:
+            shared_kv = self.bm.count_shared(range(c.S)) > 0
         pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(self.tables).cuda(),
                                    torch.from_numpy(self.lens).cuda(), mcl, partition_size=P,
-                                   workspace=ws)
+                                   workspace=ws, shared_kv=shared_kv)
         torch.cuda.synchronize()
         return out.cpu().numpy(), kp, vp
 

@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 
 import workloads as W
-from oracle.block_manager import BlockManager as RefBM, run_ops as ref_run
+from oracle.block_manager import BlockManager as RefBM, count_shared as ref_count_shared
+from oracle.block_manager import run_ops as ref_run
 
 
 def run_native(pkv, bm, ops):
@@ -54,6 +55,8 @@ def test_random_scripts_bit_exact(pkv, seed):
         part = ops[chunk:chunk + 25]
         assert run_native(pkv, native, part) == ref_run(ref, part)
         assert_same_state(native, ref, range(7))
+        live = [i for i in range(7) if i in ref.tables]
+        assert native.count_shared(live) == ref_count_shared(ref, live)
 
 
 @pytest.mark.parametrize("name", ["tiny_mha_f32", "opt13b_mha", "llama8b_gqa", "sampling_steady",
@@ -73,6 +76,11 @@ def test_workload_scripts_bit_exact(pkv, name):
     assert tables.tolist() == rt and lens.tolist() == rl
     assert lens.tolist() == w.lengths.tolist()
     assert_same_state(native, ref, range(w.cfg.S))
+    assert native.count_shared(range(w.cfg.S)) == ref_count_shared(ref, range(w.cfg.S))
+    if name.startswith("sampling"):
+        assert native.count_shared(range(w.cfg.S)) > 0
+    else:
+        assert native.count_shared(range(w.cfg.S)) == 0
 
 
 def test_append_slots_stops_at_first_failure(pkv):
@@ -90,3 +98,11 @@ def test_create_rejects_bad_free_order(pkv):
         pkv.BlockManager(4, 16, [0, 1, 1, 3])
     with pytest.raises(pkv.PkvError):
         pkv.BlockManager(0, 16)
+
+
+def test_count_shared_rejects_unknown_ids(pkv):
+    bm = pkv.BlockManager(4, 16)
+    bm.add_seq(0, 20)
+    with pytest.raises(pkv.PkvError) as e:
+        bm.count_shared([0, 5])
+    assert e.value.code == pkv.PKV_ENOSEQ

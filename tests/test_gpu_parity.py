@@ -50,6 +50,21 @@ def test_ragged_all_rows(pkv, dtype, G, D, B, P):
     say(f"  worst error {worst:.3e}")
 
 
+@pytest.mark.parametrize("dtype,G,B", [("bf16", 8, 16), ("bf16", 4, 32), ("bf16", 1, 16),
+                                       ("f32", 2, 32)])
+def test_load_policy_does_not_change_results(pkv, dtype, G, B):
+    """PKV_ATTN_SHARED_KV only switches nontemporal loads to cached ones: the
+    output must be bit-identical either way."""
+    cfg = ragged(f"policy_{dtype}_G{G}_B{B}", 300 + G + B, RAGGED_LENS, 2 * G, 2, 128, B, dtype,
+                 256)
+    say(f"case {cfg.name}")
+    case = Case(pkv, W.make(cfg))
+    a, _, _ = case.run_device(pkv, shared_kv=False)
+    b, _, _ = case.run_device(pkv, shared_kv=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    check_attention(a, case.oracle_out(*case.oracle_pools()), dtype)
+
+
 def test_tiny_mha_config(pkv):
     """Four sequences of 1, 15, 16 and 70 tokens, fp32, with the step's
     reshape_and_cache of 4 new tokens at positions 0, 14, 15 and 69."""

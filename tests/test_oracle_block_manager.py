@@ -170,3 +170,21 @@ def test_error_paths_leave_state_unchanged():
     with pytest.raises(BMError) as e:
         bm.free_seq(2)                     # double free
     assert e.value.code == ENOSEQ
+
+
+def test_count_shared_follows_fork_and_cow():
+    """Forked samples reference the parent's blocks ("Pages, from operating
+    systems": sequences that share a prefix map to the same physical blocks) and
+    a shared block stops being shared once each writer has its own copy."""
+    from oracle.block_manager import count_shared
+    bm = BlockManager(16, 16)
+    bm.add_seq(0, 50)                  # 3 full blocks + 1 holding 2 tokens
+    for child in (1, 2, 3):
+        bm.fork(0, child)
+    assert count_shared(bm, [0, 1, 2, 3]) == 4 * 4
+    for sid in (0, 1, 2, 3):           # 0, 1, 2 copy the partial block; 3 writes in place
+        bm.append_slot(sid)
+    assert count_shared(bm, [0, 1, 2, 3]) == 4 * 3
+    for sid in (1, 2, 3):
+        bm.free_seq(sid)
+    assert count_shared(bm, [0]) == 0
