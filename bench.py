@@ -90,7 +90,8 @@ class Batch:
     """One decode batch, built through the product's block manager and resident
     on the device."""
 
-    def __init__(self, pkv, torch, W, name: str, partition_size=None, layers=0):
+    def __init__(self, pkv, torch, W, name: str, partition_size=None, layers=0, use_plan=True):
+        import numpy as np
         self.cfg = c = W.CONFIGS[name]
         self.w = w = W.make(name, pools=False)
         t0 = time.perf_counter()
@@ -158,6 +159,15 @@ class Batch:
         # blocks shared by several sequences are read with cached loads
         self.shared_entries = bm.count_shared(ids)
         self.shared_kv = self.shared_entries > 0
+        # host work plan: exactly the batch's work items, largest first
+        self.plan = None
+        if use_plan:
+            t0 = time.perf_counter()
+            words, n_items, n_merge = pkv.attention_plan(lens, c.Hkv, c.B, self.max_blocks,
+                                                         self.mcl, self.P)
+            self.host_plan_us = (time.perf_counter() - t0) * 1e6
+            dev_words = torch.from_numpy(words if words.size else np.zeros(4, np.int32)).to(dev)
+            self.plan = pkv.Plan(dev_words, n_items, n_merge)
         torch.cuda.synchronize()
 
     @staticmethod
@@ -184,12 +194,13 @@ class Batch:
             main_ev[0].record()
         pkv.paged_attention_main(self.out, self.q, self.k_pool, self.v_pool, self.tables,
                                  self.lens, self.mcl, partition_size=self.P, workspace=self.ws,
-                                 shared_kv=self.shared_kv)
+                                 shared_kv=self.shared_kv, plan=self.plan)
         if main_ev is not None:
             main_ev[1].record()
         rec(3)
-        pkv.paged_attention_reduce(self.out, self.lens, self.cfg.B, self.max_blocks, self.mcl,
-                                   partition_size=self.P, workspace=self.ws)
+        pkv.paged_attention_reduce(self.out, self.lens, self.cfg.Hkv, self.cfg.B, self.max_blocks,
+                                   self.mcl, partition_size=self.P, workspace=self.ws,
+                                   plan=self.plan)
         rec(4)
 
     def launches(self):
@@ -251,6 +262,8 @@ def main() -> int:
     ap.add_argument("--config", default="llama8b_gqa", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition size (tokens per workgroup)")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="launch without the host work plan (one wave per possible partition)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--layers", type=int, default=0,
@@ -283,7 +296,7 @@ def main() -> int:
 
     name = args.config
     log(f"bench: building workload {name}")
-    batch = Batch(pkv, torch, W, name, args.partition_size, args.layers)
+    batch = Batch(pkv, torch, W, name, args.partition_size, args.layers, not args.no_plan)
     c = batch.cfg
     log(f"bench: N={batch.w.num_blocks} blocks, KV {batch.kv_bytes / 1e6:.1f} MB, "
         f"{batch.n_pairs} CoW pairs, max L {batch.mcl}")
@@ -352,6 +365,8 @@ def main() -> int:
         else int(batch.slots.shape[0]), "cow_copies": batch.n_pairs,
         "kv_bytes_per_step": batch.kv_bytes,
         "shared_block_entries": batch.shared_entries,
+        "host_plan": batch.plan is not None,
+        "work_items": None if batch.plan is None else batch.plan.n_items,
         "pool_bytes_per_layer": batch.pool_bytes,
     }
     rec = {
@@ -373,6 +388,7 @@ def main() -> int:
         "kernel_us": kernel_us,
         "layers": batch.layers,
         "host_bookkeeping_us": round(batch.host_bookkeeping_us, 1),
+        "host_plan_us": None if batch.plan is None else round(batch.host_plan_us, 1),
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -183,6 +183,30 @@ pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int
 size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
                                      int32_t max_context_len, int32_t partition_size);
 
+/* Host-side work plan for one decode batch (optional).  The caller's block
+ * manager already holds every length on the host (the batch tables are built
+ * there, [ZENO] "Implementation Essentials": block manager), so the host can
+ * list exactly the batch's work items -- one per (sequence, KV head, partition)
+ * that holds tokens -- instead of the device launching one per possible
+ * partition.  Items are ordered largest first; a zero-length sequence keeps one
+ * empty item (it writes the zero rows).  After the items come the (sequence, KV
+ * head) rows whose partitions the reduce launch merges.
+ *   context_lens  HOST int32 [S], the same lengths the device copy holds
+ *   plan          HOST int32 buffer of plan_words entries, filled with
+ *                 *n_items records {s, g, p, L} (4 int32 each) followed by
+ *                 *n_merge entries s*Hkv + g
+ *   B, max_blocks, max_context_len, partition_size: as for the attention call
+ * *n_items and *n_merge are set even when plan_words is too small (then
+ * PKV_EINVAL and the plan is not written); pkv_attention_plan_words gives an
+ * upper bound.  The caller copies the plan to the device and passes it, with
+ * the two counts, to the attention calls below. */
+size_t pkv_attention_plan_words(int32_t S, int32_t Hkv, int32_t B, int32_t max_blocks,
+                                int32_t max_context_len, int32_t partition_size);
+pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hkv, int32_t B,
+                              int32_t max_blocks, int32_t max_context_len,
+                              int32_t partition_size, int32_t* plan, size_t plan_words,
+                              int32_t* n_items, int32_t* n_merge);
+
 /* Decode attention through the block table ([LLMS] "Direct answer":
  * PagedAttention follows the logical-to-physical block mapping while computing
  * attention; [ZENO] "The Core Idea": attention computed through block-table
@@ -198,10 +222,17 @@ size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
  *   Query head h reads KV head h / (Hq/Hkv).
  *   max_context_len  host-known bound on context_lens; sizes the grid (no sync)
  *   scale         score scale, usually 1/sqrt(D)
- *   partition_size   tokens per workgroup partition: 0 = default (512), else a
- *                 positive multiple of 32 and of B spanning at most 64 blocks
- *                 (<= 64*B tokens).  Sequences longer than one partition are
- *                 split and merged by a log-sum-exp reduce launch.
+ *   partition_size   tokens per work item: 0 = default (512), else a positive
+ *                 multiple of 32 and of B spanning at most 64 blocks (<= 64*B
+ *                 tokens).  Sequences longer than one partition are split and
+ *                 merged by a log-sum-exp reduce launch.
+ *   plan, plan_items, plan_merge   NULL, or a DEVICE copy of the plan that
+ *                 pkv_attention_plan built for this batch (16-byte aligned) and
+ *                 its two counts.  With a plan the main launch runs exactly the
+ *                 listed items (taking each partition's length from the plan)
+ *                 and the reduce merges exactly the listed rows; results are
+ *                 bit-identical to the unplanned call.  A record naming a
+ *                 sequence or head outside the batch is skipped.
  *   workspace     device buffer of workspace_bytes >= pkv_attention_workspace_bytes
  *                 (may be NULL when that is 0)
  *   flags         0 or PKV_ATTN_SHARED_KV (other bits: PKV_EINVAL)
@@ -212,7 +243,9 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_p
                                       const int32_t* context_lens, int32_t S, int32_t Hq,
                                       int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
                                       int32_t num_blocks, int32_t max_context_len,
-                                      float scale, int32_t partition_size, void* workspace,
+                                      float scale, int32_t partition_size,
+                                      const int32_t* plan, int32_t plan_items,
+                                      int32_t plan_merge, void* workspace,
                                       size_t workspace_bytes, pkv_dtype dtype,
                                       uint32_t flags, void* hip_stream);
 
@@ -225,20 +258,23 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_p
  * pkv_paged_attention_reduce then merges those partials into `out` (log-sum-exp
  * combine of the partitions; the split itself is not on the pages, which only
  * note that long contexts are hard: [ZENO] "Limitations").  Its arguments must
- * repeat the values given to the main call (same S, Hq, D, B, max_blocks,
- * max_context_len, partition_size, context_lens, workspace); it reads nothing
- * else and is a no-op when every sequence fits one partition. */
+ * repeat the values given to the main call (same S, Hq, Hkv, D, B, max_blocks,
+ * max_context_len, partition_size, plan, context_lens, workspace); it reads
+ * nothing else and is a no-op when every sequence fits one partition. */
 pkv_status pkv_paged_attention_main(float* out, const void* q, const void* k_pool,
                                     const void* v_pool, const int32_t* block_tables,
                                     const int32_t* context_lens, int32_t S, int32_t Hq,
                                     int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
                                     int32_t num_blocks, int32_t max_context_len, float scale,
-                                    int32_t partition_size, void* workspace,
+                                    int32_t partition_size, const int32_t* plan,
+                                    int32_t plan_items, int32_t plan_merge, void* workspace,
                                     size_t workspace_bytes, pkv_dtype dtype, uint32_t flags,
                                     void* hip_stream);
 pkv_status pkv_paged_attention_reduce(float* out, const int32_t* context_lens, int32_t S,
-                                      int32_t Hq, int32_t D, int32_t B, int32_t max_blocks,
-                                      int32_t max_context_len, int32_t partition_size,
+                                      int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                      int32_t max_blocks, int32_t max_context_len,
+                                      int32_t partition_size, const int32_t* plan,
+                                      int32_t plan_items, int32_t plan_merge,
                                       const void* workspace, size_t workspace_bytes,
                                       void* hip_stream);
 

@@ -21,6 +21,8 @@ __all__ = [
     "PkvError", "BlockManager", "pkv_reshape_and_cache", "pkv_copy_blocks",
     "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pkv_paged_attention_main",
     "pkv_paged_attention_reduce", "pool_shapes", "paged_attention_main", "paged_attention_reduce",
+    "pkv_attention_plan", "pkv_attention_plan_words", "attention_plan", "attention_plan_words",
+    "Plan", "make_plan",
     "reshape_and_cache", "copy_blocks", "attention_workspace_bytes", "paged_attention_decode",
     "LIB_PATH", "lib",
 ]
@@ -58,14 +60,17 @@ SIGNATURES = {
                                      _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_attention_plan_words": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_attention_plan": (_i32, [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _sz, _pi32,
+                                  _pi32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
-                                          _u32, _vp]),
+                                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32,
+                                          _vp, _sz, _i32, _u32, _vp]),
     "pkv_paged_attention_main": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                        _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _u32,
-                                        _vp]),
+                                        _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32, _vp,
+                                        _sz, _i32, _u32, _vp]),
     "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                          _vp, _sz, _vp]),
+                                          _i32, _vp, _i32, _i32, _vp, _sz, _vp]),
 }
 
 
@@ -286,8 +291,56 @@ def pkv_attention_workspace_bytes(S: int, Hq: int, D: int, max_context_len: int,
     return int(lib.pkv_attention_workspace_bytes(S, Hq, D, max_context_len, partition_size))
 
 
+class Plan:
+    """A device copy of a host work plan (pkv_attention_plan) and its counts."""
+
+    def __init__(self, words: torch.Tensor, n_items: int, n_merge: int):
+        if words.dtype != torch.int32 or not words.is_cuda:
+            raise ValueError("plan words must be an int32 device tensor")
+        self.words, self.n_items, self.n_merge = words, int(n_items), int(n_merge)
+
+
+def pkv_attention_plan_words(S: int, Hkv: int, B: int, max_blocks: int, max_context_len: int,
+                             partition_size: int = 0) -> int:
+    return int(lib.pkv_attention_plan_words(S, Hkv, B, max_blocks, max_context_len,
+                                            partition_size))
+
+
+def pkv_attention_plan(context_lens, Hkv: int, B: int, max_blocks: int, max_context_len: int,
+                       partition_size: int = 0):
+    """Host plan for a batch from its HOST lengths: (int32 words, n_items, n_merge)."""
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = lens.shape[0]
+    cap = pkv_attention_plan_words(S, Hkv, B, max_blocks, max_context_len, partition_size)
+    words = np.zeros(max(cap, 4), np.int32)
+    n_items, n_merge = _i32(), _i32()
+    _check(lib.pkv_attention_plan(_np_ptr(lens, ctypes.c_int32), S, Hkv, B, max_blocks,
+                                  max_context_len, partition_size, _np_ptr(words, ctypes.c_int32),
+                                  words.shape[0], ctypes.byref(n_items), ctypes.byref(n_merge)),
+           "pkv_attention_plan")
+    used = 4 * n_items.value + n_merge.value
+    return words[:used].copy(), n_items.value, n_merge.value
+
+
+def make_plan(context_lens, Hkv: int, B: int, max_blocks: int, max_context_len: int,
+              partition_size: int = 0, device="cuda") -> Plan:
+    """pkv_attention_plan, then the copy to the device."""
+    words, n_items, n_merge = pkv_attention_plan(context_lens, Hkv, B, max_blocks,
+                                                 max_context_len, partition_size)
+    dev = torch.from_numpy(words if words.size else np.zeros(4, np.int32)).to(device)
+    return Plan(dev, n_items, n_merge)
+
+
+def _plan_args(plan):
+    if plan is None:
+        return None, 0, 0
+    if not isinstance(plan, Plan):
+        raise TypeError("plan must be a Plan (see make_plan)")
+    return _dev(plan.words, "plan"), plan.n_items, plan.n_merge
+
+
 def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                    scale, partition_size, workspace, shared_kv):
+                    scale, partition_size, plan, workspace, shared_kv):
     N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
     S, Hq = q.shape[0], q.shape[1]
     if tuple(q.shape) != (S, Hq, D) or q.dtype != k_pool.dtype:
@@ -307,36 +360,39 @@ def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_cont
     return (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
             _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, D,
             B, block_tables.shape[1], N, int(max_context_len), float(scale), int(partition_size),
-            ws_ptr, ws_bytes, _dtype_code(k_pool), PKV_ATTN_SHARED_KV if shared_kv else 0)
+            *_plan_args(plan), ws_ptr, ws_bytes, _dtype_code(k_pool),
+            PKV_ATTN_SHARED_KV if shared_kv else 0)
 
 
 def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
                                max_context_len: int, scale: float | None = None,
                                partition_size: int = 0, workspace=None, stream=None,
-                               shared_kv: bool = False) -> None:
+                               shared_kv: bool = False, plan: Plan | None = None) -> None:
     """out[s, h] = softmax(q[s, h] K_s^T * scale) V_s through the block tables.
 
     out fp32 [S, Hq, D]; q [S, Hq, D] in the pool dtype; block_tables int32
     [S, max_blocks]; context_lens int32 [S].  `workspace` (a uint8 device tensor)
     is needed when max_context_len exceeds one partition.  `shared_kv` sets
-    PKV_ATTN_SHARED_KV (the batch shares blocks; a load-policy hint only)."""
+    PKV_ATTN_SHARED_KV (the batch shares blocks; a load-policy hint only).
+    `plan` (make_plan) runs exactly the batch's work items."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                           scale, partition_size, workspace, shared_kv)
+                           scale, partition_size, plan, workspace, shared_kv)
     _check(lib.pkv_paged_attention_decode(*args, _stream(stream)), "pkv_paged_attention_decode")
 
 
 def pkv_paged_attention_main(out, q, k_pool, v_pool, block_tables, context_lens,
                              max_context_len: int, scale: float | None = None,
                              partition_size: int = 0, workspace=None, stream=None,
-                             shared_kv: bool = False) -> None:
+                             shared_kv: bool = False, plan: Plan | None = None) -> None:
     """The main launch of pkv_paged_attention_decode alone (same arguments)."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                           scale, partition_size, workspace, shared_kv)
+                           scale, partition_size, plan, workspace, shared_kv)
     _check(lib.pkv_paged_attention_main(*args, _stream(stream)), "pkv_paged_attention_main")
 
 
-def pkv_paged_attention_reduce(out, context_lens, B: int, max_blocks: int, max_context_len: int,
-                               partition_size: int = 0, workspace=None, stream=None) -> None:
+def pkv_paged_attention_reduce(out, context_lens, Hkv: int, B: int, max_blocks: int,
+                               max_context_len: int, partition_size: int = 0, workspace=None,
+                               stream=None, plan: Plan | None = None) -> None:
     """The partition merge of pkv_paged_attention_decode alone; the arguments
     repeat those of the preceding pkv_paged_attention_main call."""
     S, Hq, D = out.shape
@@ -349,8 +405,9 @@ def pkv_paged_attention_reduce(out, context_lens, B: int, max_blocks: int, max_c
         ws_ptr = _dev(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.pkv_paged_attention_reduce(_dev(out, "out"), _dev(context_lens, "context_lens"),
-                                          S, Hq, D, int(B), int(max_blocks), int(max_context_len),
-                                          int(partition_size), ws_ptr, ws_bytes, _stream(stream)),
+                                          S, Hq, int(Hkv), D, int(B), int(max_blocks),
+                                          int(max_context_len), int(partition_size),
+                                          *_plan_args(plan), ws_ptr, ws_bytes, _stream(stream)),
            "pkv_paged_attention_reduce")
 
 
@@ -360,3 +417,5 @@ attention_workspace_bytes = pkv_attention_workspace_bytes
 paged_attention_decode = pkv_paged_attention_decode
 paged_attention_main = pkv_paged_attention_main
 paged_attention_reduce = pkv_paged_attention_reduce
+attention_plan = pkv_attention_plan
+attention_plan_words = pkv_attention_plan_words

@@ -57,16 +57,16 @@
 #include <cmath>
 
 #include "../../include/pkv.h"
+#include "decode_config.h"
 #include "device_common.h"
 #include "launch_check.h"
 
 namespace pkv {
 
-constexpr int kDefaultPartition = 512;
 // One wave per workgroup: the dispatcher then balances the ragged items wave by
 // wave (measured faster than four-item workgroups on ragged batches).
 constexpr int kWavesPerGroup = 1;           // items per workgroup
-constexpr int kMaxPartitionBlocks = kWave;  // one table entry per lane
+static_assert(kMaxPartitionBlocks == kWave, "one table entry per lane");
 
 struct DecodeArgs {
   float* out;
@@ -74,8 +74,10 @@ struct DecodeArgs {
   float* part_ml;    // [S, Hq, nparts, 2]
   const int* block_tables;
   const int* context_lens;
+  const int4* plan;  // host-built work list {s, g, p, L} per item, or nullptr
+  int S;
   int SG;            // S * Hkv: items per partition index
-  int items;         // SG * nparts
+  int items;         // work items in the grid
   int Hkv, max_blocks, num_blocks, nparts, P;
   float scale_log2e;
 };
@@ -87,16 +89,33 @@ struct WorkItem {
   int s, g, p, start, end, nps;
 };
 
-// Item of this wave (partition-major numbering); false past the last item.
+// Item of this wave and its sequence length; false past the last item.
+// Without a plan: partition-major numbering of every (sequence, KV head,
+// partition), the partition counted from the sequence's end (item_extent turns
+// it into the index).  With a plan: item i is the plan's record i, whose
+// partition index and length come from the host (no length load here), and a
+// record naming a sequence or head outside the batch is skipped.
 template <int NW>
-__device__ __forceinline__ bool item_ids(const DecodeArgs& a, WorkItem& it) {
+__device__ __forceinline__ bool item_ids(const DecodeArgs& a, WorkItem& it, int& L) {
   const int item = (int)blockIdx.x * NW + uniform((int)threadIdx.x / kWave);
   if (item >= a.items) return false;
+  if (a.plan) {
+    const int4 rec = a.plan[item];
+    it.s = rec.x;
+    it.g = rec.y;
+    const int p = rec.z;
+    L = rec.w;
+    if (it.s < 0 || it.s >= a.S || it.g < 0 || it.g >= a.Hkv || p < 0 || p >= a.nparts)
+      return false;
+    it.p = p;
+    return true;
+  }
   const int k = item / a.SG;
   it.p = a.nparts - 1 - k;   // partitions counted from the sequence's end
   const int sg = item - k * a.SG;
   it.g = sg % a.Hkv;
   it.s = sg / a.Hkv;
+  L = a.context_lens[it.s];
   return true;
 }
 
@@ -105,20 +124,22 @@ __device__ __forceinline__ bool item_ids(const DecodeArgs& a, WorkItem& it) {
 template <int D, int B, int G>
 __device__ __forceinline__ bool item_extent(const DecodeArgs& a, WorkItem& it, int L) {
   L = min(L, a.max_blocks * B);
-  const int pe = it.p;                  // partition counted from the end
   const int np = L <= 0 ? 0 : min((L + a.P - 1) / a.P, a.nparts);
-  it.p = np - 1 - pe;
-  it.start = it.p * a.P;
+  int p = it.p;
+  if (!a.plan) p = np - 1 - p;  // unplanned ids count the partition from the sequence's end
   if (L <= 0) {
-    if (pe == 0) {
+    // a sequence with no tokens gets zero rows, written by its first item only
+    if (a.plan ? p == 0 : p == -1) {
       float* o = a.out + ((size_t)it.s * a.Hkv * G + (size_t)it.g * G) * D;
       for (int i = threadIdx.x & (kWave - 1); i < G * D; i += kWave) o[i] = 0.f;
     }
     return false;
   }
-  if (it.p < 0) return false;
+  if (p < 0 || p >= np) return false;
+  it.p = p;
+  it.start = p * a.P;
   it.end = min(L, it.start + a.P);
-  it.nps = min((L + a.P - 1) / a.P, a.nparts);
+  it.nps = np;
   return true;
 }
 
@@ -221,12 +242,13 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
   const int t = lane % B;   // token of this lane in q.k
   const int cg = lane / B;  // its chunk group
   WorkItem it;
-  if (!item_ids<NW>(a, it)) return;
+  int L;
+  if (!item_ids<NW>(a, it, L)) return;
   const int Hq = a.Hkv * G;
 
-  // the length decides whether the item is empty (most of the grid when the
-  // batch is ragged); then the partition's table slice and the queries load together
-  const int L = a.context_lens[it.s];
+  // the length decides whether the item is empty (most of an unplanned grid when
+  // the batch is ragged); then the partition's table slice and the queries load
+  // together
   if (!item_extent<D, B, G>(a, it, L)) return;
   TableWindow tw;
   tw.load(a.block_tables + (size_t)it.s * a.max_blocks, it.start / B, a.max_blocks);
@@ -363,12 +385,13 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane >> 4, r = lane & 15;
   WorkItem it;
-  if (!item_ids<NW>(a, it)) return;
+  int L;
+  if (!item_ids<NW>(a, it, L)) return;
   const int Hq = a.Hkv * G;
 
-  // the length decides whether the item is empty (most of the grid when the
-  // batch is ragged); then the partition's table slice and the queries load together
-  const int L = a.context_lens[it.s];
+  // the length decides whether the item is empty (most of an unplanned grid when
+  // the batch is ragged); then the partition's table slice and the queries load
+  // together
   if (!item_extent<D, B, G>(a, it, L)) return;
   TableWindow tw;
   tw.load(a.block_tables + (size_t)it.s * a.max_blocks, it.start / B, a.max_blocks);
@@ -515,15 +538,23 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(float* __restrict__ out,
                                                         const float* __restrict__ part_acc,
                                                         const float* __restrict__ part_ml,
                                                         const int* __restrict__ context_lens,
-                                                        int Hq, int max_blocks, int B, int nparts,
-                                                        int P) {
+                                                        const int* __restrict__ merge_rows, int S,
+                                                        int Hq, int G, int max_blocks, int B,
+                                                        int nparts, int P) {
   constexpr int C4 = D / 4;      // float4 columns of a row
   constexpr int PG = 256 / C4;   // partition groups
   constexpr int U = 64 / PG;     // partitions per thread per round
   __shared__ float sm_m[PG], sm_l[PG];
   __shared__ f32x4 sm_acc[PG][C4];
 
-  const int row = blockIdx.x;  // s * Hq + h
+  // row = s * Hq + h: every row of the batch, or (planned) the G query heads of
+  // each listed (sequence, KV head) = s * Hkv + g, whose rows are (s*Hkv + g)*G + gi
+  int row = blockIdx.x;
+  if (merge_rows) {
+    const int sg = merge_rows[blockIdx.x / G];
+    if (sg < 0 || sg >= S * (Hq / G)) return;
+    row = sg * G + (int)(blockIdx.x % G);
+  }
   const int s = row / Hq;
   const int L = min(context_lens[s], max_blocks * B);
   const int n = L <= 0 ? 0 : min((L + P - 1) / P, nparts);
@@ -645,53 +676,52 @@ static int64_t num_partitions(int64_t max_context_len, int P) {
   return max_context_len <= 0 ? 1 : (max_context_len + P - 1) / P;
 }
 
-}  // namespace pkv
+// The optional host-built plan: n_items records of 4 int32, then n_merge rows.
+struct PlanArg {
+  const int32_t* ptr;
+  int32_t n_items, n_merge;
+};
 
-using namespace pkv;
-
-extern "C" size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
-                                                int32_t max_context_len, int32_t partition_size) {
-  if (S <= 0 || Hq <= 0 || D <= 0 || partition_size < 0) return 0;
-  const int P = partition_size > 0 ? partition_size : kDefaultPartition;
-  const int64_t np = num_partitions(max_context_len, P);
-  if (np <= 1) return 0;
-  return (size_t)S * Hq * np * (D + 2) * sizeof(float);
+static bool plan_ok(const PlanArg& pl) {
+  if (!pl.ptr) return true;
+  return aligned16(pl.ptr) && pl.n_items >= 0 && pl.n_merge >= 0;
 }
 
-namespace pkv {
-
-// Host validation and argument set-up shared by the three attention entry
-// points.  On PKV_OK, *a and *groups describe the main launch (groups == 0 when
-// S == 0: nothing to launch).
+// Host validation and argument set-up shared by the attention entry points.
+// On PKV_OK, *a and *groups describe the main launch (groups == 0: nothing to
+// launch).
 static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, const void* q,
                                  const void* k_pool, const void* v_pool,
                                  const int32_t* block_tables, const int32_t* context_lens,
                                  int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                  int32_t max_blocks, int32_t num_blocks, int32_t max_context_len,
-                                 float scale, int32_t partition_size, void* workspace,
-                                 size_t workspace_bytes, pkv_dtype dtype, uint32_t flags) {
+                                 float scale, int32_t partition_size, const PlanArg& plan,
+                                 void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                 uint32_t flags) {
   *groups = 0;
   if (flags & ~(uint32_t)PKV_ATTN_SHARED_KV) return PKV_EINVAL;
   if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 || num_blocks <= 0 ||
-      max_context_len < 0 || partition_size < 0 || !std::isfinite(scale))
+      max_context_len < 0 || partition_size < 0 || !std::isfinite(scale) || !plan_ok(plan))
     return PKV_EINVAL;
   if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_EINVAL;
   const int G = Hq / Hkv;
   if (!shape_supported(D, B, G)) return PKV_EUNSUPPORTED;
-  const int P = partition_size > 0 ? partition_size : kDefaultPartition;
-  if (P % 32 != 0 || P % B != 0 || P / B > kMaxPartitionBlocks) return PKV_EINVAL;
+  const int P = resolve_partition(partition_size, B);
+  if (P == 0) return PKV_EINVAL;
   if (S == 0) return PKV_OK;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !block_tables || !context_lens)
     return PKV_EINVAL;
   const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
   const int64_t nparts = num_partitions(mcl, P);
-  const int64_t items = (int64_t)S * Hkv * nparts;
+  const int64_t items = plan.ptr ? (int64_t)plan.n_items : (int64_t)S * Hkv * nparts;
   if (items > 0x7fffffffLL || (int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
   *a = DecodeArgs{};
   a->out = out;
   a->block_tables = block_tables;
   a->context_lens = context_lens;
+  a->plan = reinterpret_cast<const int4*>(plan.ptr);
+  a->S = S;
   a->SG = S * Hkv;
   a->items = (int)items;
   a->Hkv = Hkv;
@@ -722,63 +752,86 @@ static pkv_status launch_main_kernel(const DecodeArgs& a, int64_t groups, const 
   return launch_status();
 }
 
-static pkv_status launch_reduce_kernel(const DecodeArgs& a, int S, int Hq, int D, int B,
-                                       hipStream_t st) {
+// The merge launch: every row of the batch, or only the plan's merge rows.
+static pkv_status launch_reduce_kernel(const DecodeArgs& a, const PlanArg& plan, int S, int Hq,
+                                       int G, int D, int B, hipStream_t st) {
   if (a.nparts <= 1) return PKV_OK;
+  const int* rows = plan.ptr ? plan.ptr + 4 * (size_t)plan.n_items : nullptr;
+  const int64_t grid = plan.ptr ? (int64_t)plan.n_merge * G : (int64_t)S * Hq;
+  if (grid == 0) return PKV_OK;
+  if (grid > 0x7fffffffLL) return PKV_EINVAL;
   if (D == 64)
-    pa_reduce_kernel<64><<<(unsigned)(S * Hq), 256, 0, st>>>(
-        a.out, a.part_acc, a.part_ml, a.context_lens, Hq, a.max_blocks, B, a.nparts, a.P);
+    pa_reduce_kernel<64><<<(unsigned)grid, 256, 0, st>>>(a.out, a.part_acc, a.part_ml,
+                                                         a.context_lens, rows, S, Hq, G,
+                                                         a.max_blocks, B, a.nparts, a.P);
   else
-    pa_reduce_kernel<128><<<(unsigned)(S * Hq), 256, 0, st>>>(
-        a.out, a.part_acc, a.part_ml, a.context_lens, Hq, a.max_blocks, B, a.nparts, a.P);
+    pa_reduce_kernel<128><<<(unsigned)grid, 256, 0, st>>>(a.out, a.part_acc, a.part_ml,
+                                                          a.context_lens, rows, S, Hq, G,
+                                                          a.max_blocks, B, a.nparts, a.P);
   return launch_status();
 }
 
 }  // namespace pkv
 
+using namespace pkv;
+
+extern "C" size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
+                                                int32_t max_context_len, int32_t partition_size) {
+  if (S <= 0 || Hq <= 0 || D <= 0 || partition_size < 0) return 0;
+  const int P = partition_size > 0 ? partition_size : kDefaultPartition;
+  const int64_t np = num_partitions(max_context_len, P);
+  if (np <= 1) return 0;
+  return (size_t)S * Hq * np * (D + 2) * sizeof(float);
+}
+
 extern "C" pkv_status pkv_paged_attention_decode(
     float* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
     const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-    uint32_t flags, void* hip_stream) {
+    int32_t partition_size, const int32_t* plan, int32_t plan_items, int32_t plan_merge,
+    void* workspace, size_t workspace_bytes, pkv_dtype dtype, uint32_t flags, void* hip_stream) {
   DecodeArgs a;
   int64_t groups;
+  const PlanArg pl{plan, plan_items, plan_merge};
   pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, block_tables, context_lens,
                                  S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
-                                 partition_size, workspace, workspace_bytes, dtype, flags);
+                                 partition_size, pl, workspace, workspace_bytes, dtype, flags);
   if (st != PKV_OK || groups == 0) return st;
   hipStream_t hs = (hipStream_t)hip_stream;
   st = launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, flags, hs);
   if (st != PKV_OK) return st;
-  return launch_reduce_kernel(a, S, Hq, D, B, hs);
+  return launch_reduce_kernel(a, pl, S, Hq, Hq / Hkv, D, B, hs);
 }
 
 extern "C" pkv_status pkv_paged_attention_main(
     float* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
     const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-    uint32_t flags, void* hip_stream) {
+    int32_t partition_size, const int32_t* plan, int32_t plan_items, int32_t plan_merge,
+    void* workspace, size_t workspace_bytes, pkv_dtype dtype, uint32_t flags, void* hip_stream) {
   DecodeArgs a;
   int64_t groups;
+  const PlanArg pl{plan, plan_items, plan_merge};
   pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, block_tables, context_lens,
                                  S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
-                                 partition_size, workspace, workspace_bytes, dtype, flags);
+                                 partition_size, pl, workspace, workspace_bytes, dtype, flags);
   if (st != PKV_OK || groups == 0) return st;
   return launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, flags,
                             (hipStream_t)hip_stream);
 }
 
 extern "C" pkv_status pkv_paged_attention_reduce(
-    float* out, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t D, int32_t B,
-    int32_t max_blocks, int32_t max_context_len, int32_t partition_size, const void* workspace,
+    float* out, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+    int32_t B, int32_t max_blocks, int32_t max_context_len, int32_t partition_size,
+    const int32_t* plan, int32_t plan_items, int32_t plan_merge, const void* workspace,
     size_t workspace_bytes, void* hip_stream) {
-  if (S < 0 || Hq <= 0 || max_blocks <= 0 || max_context_len < 0 || partition_size < 0)
+  const PlanArg pl{plan, plan_items, plan_merge};
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 || max_context_len < 0 ||
+      partition_size < 0 || !plan_ok(pl))
     return PKV_EINVAL;
   if (!(D == 64 || D == 128) || !(B == 16 || B == 32)) return PKV_EUNSUPPORTED;
-  const int P = partition_size > 0 ? partition_size : kDefaultPartition;
-  if (P % 32 != 0 || P % B != 0 || P / B > kMaxPartitionBlocks) return PKV_EINVAL;
+  const int P = resolve_partition(partition_size, B);
+  if (P == 0) return PKV_EINVAL;
   if (S == 0) return PKV_OK;
   if (!aligned16(out) || !context_lens) return PKV_EINVAL;
   const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
@@ -795,5 +848,5 @@ extern "C" pkv_status pkv_paged_attention_reduce(
   a.P = P;
   a.part_acc = (float*)workspace;
   a.part_ml = a.part_acc + (size_t)S * Hq * nparts * D;
-  return launch_reduce_kernel(a, S, Hq, D, B, (hipStream_t)hip_stream);
+  return launch_reduce_kernel(a, pl, S, Hq, Hq / Hkv, D, B, (hipStream_t)hip_stream);
 }

@@ -72,9 +72,9 @@ class Case:
         self.bm = bm
 
     # -- device path -----------------------------------------------------------
-    def run_device(self, pkv, partition_size=None, shared_kv=None):
+    def run_device(self, pkv, partition_size=None, shared_kv=None, plan=False):
         """shared_kv None: set PKV_ATTN_SHARED_KV when the batch shares blocks
-        (the benchmark's choice)."""
+        (the benchmark's choice); plan: run from a host work plan."""
         c = self.w.cfg
         P = c.partition_size if partition_size is None else partition_size
         kp, vp = to_dev(self.k_pool), to_dev(self.v_pool)
@@ -90,9 +90,12 @@ class Case:
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
         if shared_kv is None:
             shared_kv = self.bm.count_shared(range(c.S)) > 0
+        pl = None
+        if plan:
+            pl = pkv.make_plan(self.lens, c.Hkv, c.B, self.max_blocks, mcl, P)
         pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(self.tables).cuda(),
                                    torch.from_numpy(self.lens).cuda(), mcl, partition_size=P,
-                                   workspace=ws, shared_kv=shared_kv)
+                                   workspace=ws, shared_kv=shared_kv, plan=pl)
         torch.cuda.synchronize()
         return out.cpu().numpy(), kp, vp
 

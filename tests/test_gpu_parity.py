@@ -65,6 +65,23 @@ def test_load_policy_does_not_change_results(pkv, dtype, G, B):
     check_attention(a, case.oracle_out(*case.oracle_pools()), dtype)
 
 
+@pytest.mark.parametrize("dtype,G,D,B,P", KERNEL_CASES[::2])
+def test_plan_matches_unplanned(pkv, dtype, G, D, B, P):
+    """A host work plan changes which waves run, not what they compute: the
+    output is bit-identical to the unplanned launch (zero-length rows included)."""
+    lens = RAGGED_LENS + (0, 3)
+    cfg = ragged(f"plan_{dtype}_G{G}_D{D}_B{B}_P{P}", 400 + G + D + B, lens, 2 * G, 2, D, B,
+                 dtype, P, kind="decode")
+    say(f"case {cfg.name}")
+    case = Case(pkv, W.make(cfg))
+    a, _, _ = case.run_device(pkv, plan=False)
+    b, _, _ = case.run_device(pkv, plan=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.all(b[len(RAGGED_LENS)] == 0.0)
+    rows = [(s, h) for s in range(len(lens)) if lens[s] > 0 for h in range(2 * G)]
+    check_attention(b, case.oracle_out(case.k_pool, case.v_pool, rows), dtype, rows)
+
+
 def test_tiny_mha_config(pkv):
     """Four sequences of 1, 15, 16 and 70 tokens, fp32, with the step's
     reshape_and_cache of 4 new tokens at positions 0, 14, 15 and 69."""
@@ -133,12 +150,13 @@ def _sample_rows(case, n, seed):
 @pytest.mark.parametrize("name", ["llama8b_gqa", "sampling_fork", "sampling_steady",
                                   "opt13b_mha", "long70b_b16", "long70b_b32"])
 def test_full_config(pkv, name):
-    """Full-size workload in the benchmark's launch configuration: whole pools
-    compared bit for bit after the step's cache writes, attention compared on
-    sampled rows (the longest and shortest sequences included)."""
+    """Full-size workload in the benchmark's launch configuration (host work
+    plan, load policy from the batch's sharing): whole pools compared bit for bit
+    after the step's cache writes, attention compared on sampled rows (the
+    longest and shortest sequences included)."""
     say(f"case {name} (full size)")
     case = Case(pkv, W.make(name))
-    got, kp, vp = case.run_device(pkv)
+    got, kp, vp = case.run_device(pkv, plan=True)
     say("  device done")
     assert np.isfinite(got).all()
     if len(case.slots) or len(case.pairs):
