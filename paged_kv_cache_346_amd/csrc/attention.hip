@@ -526,24 +526,26 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of partition partials: one 256-thread workgroup per
-// (sequence, query head) row.  Thread (pg, col) folds partitions pg, pg + PG, ...
-// of float4 column col into a local (max, sum, acc) state; U partitions per
-// thread are loaded at once (indices past the end re-read the last partition
-// with weight 0), so one round trip covers U * PG partitions.  The PG local
-// states are then merged through LDS.
+// Log-sum-exp merge of partition partials: one TPR-thread workgroup per
+// (sequence, query head) row (TPR = 64 when a row has at most 16 partitions,
+// 256 for long contexts).  Thread (pg, col) folds partitions pg, pg + PG, ... of
+// float4 column col into a local (max, sum, acc) state; U partitions per thread
+// are loaded at once (indices past the end re-read the last partition with
+// weight 0), so one round trip covers U * PG partitions (16 or 64).  The PG
+// local states are then merged through LDS.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void pa_reduce_kernel(float* __restrict__ out,
+template <int D, int TPR>
+__global__ __launch_bounds__(TPR) void pa_reduce_kernel(float* __restrict__ out,
                                                         const float* __restrict__ part_acc,
                                                         const float* __restrict__ part_ml,
                                                         const int* __restrict__ context_lens,
                                                         const int* __restrict__ merge_rows, int S,
                                                         int Hq, int G, int max_blocks, int B,
                                                         int nparts, int P) {
-  constexpr int C4 = D / 4;      // float4 columns of a row
-  constexpr int PG = 256 / C4;   // partition groups
-  constexpr int U = 64 / PG;     // partitions per thread per round
+  constexpr int C4 = D / 4;                       // float4 columns of a row
+  constexpr int PG = TPR / C4;                    // partition groups
+  constexpr int U = (TPR == 64 ? 16 : 64) / PG;   // partitions per thread per round
+  static_assert(PG >= 1 && U >= 1, "unsupported reduce shape");
   __shared__ float sm_m[PG], sm_l[PG];
   __shared__ f32x4 sm_acc[PG][C4];
 
@@ -760,14 +762,17 @@ static pkv_status launch_reduce_kernel(const DecodeArgs& a, const PlanArg& plan,
   const int64_t grid = plan.ptr ? (int64_t)plan.n_merge * G : (int64_t)S * Hq;
   if (grid == 0) return PKV_OK;
   if (grid > 0x7fffffffLL) return PKV_EINVAL;
-  if (D == 64)
-    pa_reduce_kernel<64><<<(unsigned)grid, 256, 0, st>>>(a.out, a.part_acc, a.part_ml,
-                                                         a.context_lens, rows, S, Hq, G,
-                                                         a.max_blocks, B, a.nparts, a.P);
-  else
-    pa_reduce_kernel<128><<<(unsigned)grid, 256, 0, st>>>(a.out, a.part_acc, a.part_ml,
-                                                          a.context_lens, rows, S, Hq, G,
-                                                          a.max_blocks, B, a.nparts, a.P);
+  const bool small = a.nparts <= 16;  // one round of a 64-thread row covers it
+#define PKV_REDUCE(DD, TT)                                                                \
+  pa_reduce_kernel<DD, TT><<<(unsigned)grid, TT, 0, st>>>(a.out, a.part_acc, a.part_ml,   \
+                                                          a.context_lens, rows, S, Hq, G, \
+                                                          a.max_blocks, B, a.nparts, a.P)
+  if (D == 64) {
+    if (small) PKV_REDUCE(64, 64); else PKV_REDUCE(64, 256);
+  } else {
+    if (small) PKV_REDUCE(128, 64); else PKV_REDUCE(128, 256);
+  }
+#undef PKV_REDUCE
   return launch_status();
 }
 

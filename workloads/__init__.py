@@ -62,7 +62,7 @@ CONFIGS = {
     "opt13b_mha": Config("opt13b_mha", 2, S=64, Hq=40, Hkv=40, D=128, B=16, dtype="bf16",
                          kind="decode"),
     "llama8b_gqa": Config("llama8b_gqa", 3, S=256, Hq=32, Hkv=8, D=128, B=16, dtype="bf16",
-                          kind="step"),
+                          kind="step", partition_size=1024),
     "sampling_steady": Config("sampling_steady", 4, S=256, Hq=32, Hkv=8, D=128, B=16,
                               dtype="bf16", kind="steady"),
     "sampling_fork": Config("sampling_fork", 4, S=256, Hq=32, Hkv=8, D=128, B=16,
