@@ -127,6 +127,8 @@ pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent_id, int64_t child_id);
 pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id);
 
 pkv_status pkv_bm_num_free(const pkv_bm* bm, int32_t* out);
+/* Pool geometry given at creation: blocks and tokens per block. */
+pkv_status pkv_bm_geometry(const pkv_bm* bm, int32_t* num_blocks, int32_t* block_size);
 pkv_status pkv_bm_refcount(const pkv_bm* bm, int32_t block, int32_t* out);
 pkv_status pkv_bm_seq_info(const pkv_bm* bm, int64_t seq_id, int32_t* len, int32_t* nblocks);
 /* Copy the sequence's table into out[cap]; PKV_EINVAL if cap is too small. */
@@ -148,6 +150,73 @@ pkv_status pkv_bm_count_shared(const pkv_bm* bm, const int64_t* seq_ids, int32_t
  * front to back in free_queue[0 .. *n_free) (room for num_blocks entries). */
 pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_queue,
                            int32_t* n_free);
+
+/* ---------------------------------------------------------------------------
+ * Continuous batching scheduler ([RTI] "Batch by step, not by request": the
+ * batch is rebuilt after every decode step, finished sequences leave and
+ * waiting ones join, and with paging a newcomer needs only free blocks;
+ * [ZENO] "Continuous Batching" figure: A finishes, A dequeues, D enqueues, the
+ * batch becomes {B, C, D}; [ZENO] "Implementation Essentials": under memory
+ * pressure a request's blocks are dropped and its KV recomputed later).
+ *
+ * A host-side driver over one block manager (which it does not own; the
+ * manager must outlive it and take no other sequence ids meanwhile).  Policy
+ * (readings where the pages are silent):
+ *   - requests are admitted first come first served; admission stops at the
+ *     first waiting request that does not fit; at most max_running run;
+ *   - paged policy: admission allocates blocks for the request's context (its
+ *     prompt plus tokens generated before any preemption), whose KV the caller
+ *     then writes (prefill);
+ *   - reserve policy (reserve_max != 0): a simulation of the max-length
+ *     reservation of the systems before paging ([ZENO] "Background and
+ *     Motivation"): a request is admitted only if the blocks not yet reserved
+ *     cover ceil((prompt + max_new) / B); they stay reserved until it finishes;
+ *   - every running request produces one token per step; slots are appended
+ *     in admission order;
+ *   - when an append finds no free block, the most recently admitted running
+ *     request is preempted: its blocks are freed, it returns to the front of
+ *     the waiting queue keeping its generated tokens, and the append is retried;
+ *   - a request finishes in the step that produces its max_new-th token and is
+ *     freed by pkv_sched_end_step, after the caller has read the step's tables.
+ * Not thread-safe; one scheduler thread owns a handle.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_sched pkv_sched;
+
+/* Caller-owned host arrays one step fills; each holds `capacity` entries
+ * (>= max_running), cow_pairs 2*capacity. */
+typedef struct pkv_sched_step {
+  int32_t capacity;
+  int64_t* batch_ids;      /* running requests after the step, admission order */
+  int64_t* slots;          /* slot of each one's new token (block*B + offset) */
+  int32_t n_batch;
+  int32_t* cow_pairs;      /* (src, dst) block copies to run before the writes */
+  int32_t n_cow;
+  int64_t* admitted_ids;   /* admitted this step: prefill tokens [0, ctx) ... */
+  int32_t* admitted_ctx;   /* ... whose KV the caller writes before attention */
+  int32_t n_admitted;
+  int64_t* preempted_ids;  /* preempted this step (back in the waiting queue) */
+  int32_t n_preempted;
+  int64_t* finished_ids;   /* produced their last token this step */
+  int32_t n_finished;
+} pkv_sched_step;
+
+pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t reserve_max,
+                            pkv_sched** out);
+void pkv_sched_destroy(pkv_sched* sched);
+/* Queue a request; PKV_EEXIST for a known id, PKV_EINVAL when prompt_len < 0,
+ * max_new_tokens < 1 or its maximum length can never fit the pool. */
+pkv_status pkv_sched_add_request(pkv_sched* sched, int64_t req_id, int32_t prompt_len,
+                                 int32_t max_new_tokens);
+/* One iteration (admissions, then one slot per running request).  Steps
+ * alternate with pkv_sched_end_step; either one out of turn is PKV_EINVAL. */
+pkv_status pkv_sched_begin_step(pkv_sched* sched, pkv_sched_step* out);
+/* Free the requests that finished in the step. */
+pkv_status pkv_sched_end_step(pkv_sched* sched);
+/* Tokens the running requests hold, slots the policy keeps for them (allocated
+ * blocks, or reserved blocks under the reserve policy, times B), queue sizes. */
+pkv_status pkv_sched_stats(const pkv_sched* sched, int64_t* tokens_held,
+                           int64_t* slots_committed, int32_t* n_waiting,
+                           int32_t* n_running);
 
 /* ---------------------------------------------------------------------------
  * Device operations.

@@ -1,0 +1,176 @@
+"""Reference iteration-level (continuous) batching scheduler -- TEST
+INFRASTRUCTURE ONLY (plain Python over the reference block manager; the product
+never imports it).
+
+From the pages:
+  * scheduling works at the level of single decoding iterations: after every
+    step, finished sequences leave the batch and waiting ones join ("PagedAttention
+    and Continuous Batching", "Batch by step, not by request"; "PagedAttention:
+    The vLLM Paper", "Continuous Batching: Request-Level vs. Iteration-Level
+    Scheduling", whose figure has A finish, A dequeue and D enqueue, giving the
+    batch {B, C, D});
+  * with paging a new request only needs free blocks, not a large contiguous
+    region (same section of the first page);
+  * under memory pressure a running request is preempted: its blocks are dropped
+    and its KV recomputed later ("Implementation Essentials", block manager;
+    OS-paging analogy table, "Swapping");
+  * the systems before paging reserved a region per request for its maximum
+    length ("Background and Motivation").
+
+Readings where the pages are silent:
+  * requests are admitted first-come first-served: admission stops at the first
+    waiting request that does not fit (no skipping ahead) and at most
+    `max_running` requests run at once;
+  * paged policy: admitting a request allocates blocks for its current context
+    (its prompt plus the tokens it generated before any preemption);
+  * reserve policy (the max-length reservation of the earlier systems,
+    simulated over the same pool): a request is admitted only if the blocks not
+    yet reserved cover its maximum length ceil((prompt + max_new) / B); they stay
+    reserved until it finishes, so its appends can never run out of blocks;
+  * every running request (one admitted this step included) produces one token
+    per step, and the running requests append their slots in admission order;
+  * when an append finds no free block (paged policy), the most recently
+    admitted running request is preempted: its blocks are freed, it returns to
+    the FRONT of the waiting queue keeping the tokens it generated (they are
+    rebuilt with its prompt on re-admission), and the append is retried;
+  * a request finishes in the step that produces its max_new-th token and is
+    freed by end_step(), after the step's batch tables have been read;
+  * a request whose maximum length can never fit the pool is rejected when it
+    is submitted;
+  * begin_step() and end_step() alternate; calling either out of turn is an
+    error.
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass
+
+from oracle.block_manager import BMError, EEXIST, EINVAL, ENOBLOCKS
+
+
+@dataclass
+class Request:
+    rid: int
+    prompt: int
+    max_new: int
+    generated: int = 0
+    reserved: int = 0   # blocks held by a reservation (reserve policy)
+
+    @property
+    def ctx(self) -> int:
+        """Tokens whose KV the request holds (or must rebuild) right now."""
+        return self.prompt + self.generated
+
+
+class Scheduler:
+    def __init__(self, bm, max_running: int, reserve_max: bool = False):
+        if max_running <= 0:
+            raise BMError(EINVAL, "max_running must be positive")
+        self.bm = bm
+        self.max_running = max_running
+        self.reserve_max = reserve_max
+        self.waiting: deque[Request] = deque()
+        self.running: list[Request] = []
+        self.known: set[int] = set()
+        self.reserved = 0
+        self.finishing: list[Request] = []
+        self.in_step = False
+
+    def _blocks(self, tokens: int) -> int:
+        return -(-tokens // self.bm.B)
+
+    def add_request(self, rid: int, prompt: int, max_new: int) -> None:
+        if prompt < 0 or max_new < 1:
+            raise BMError(EINVAL, "prompt must be >= 0 and max_new >= 1")
+        if rid in self.known:
+            raise BMError(EEXIST)
+        if self._blocks(prompt + max_new) > self.bm.N:
+            raise BMError(EINVAL, "request can never fit the pool")
+        self.known.add(rid)
+        self.waiting.append(Request(rid, prompt, max_new))
+
+    def begin_step(self):
+        """One iteration: admissions, then one slot per running request.
+        Returns dict(batch, slots, cow, admitted=[(rid, ctx)], preempted,
+        finished)."""
+        if self.in_step:
+            raise BMError(EINVAL, "end_step() was not called")
+        self.in_step = True
+        admitted: list[tuple[Request, int]] = []   # (request, context it was admitted with)
+        while self.waiting and len(self.running) < self.max_running:
+            r = self.waiting[0]
+            need_max = self._blocks(r.prompt + r.max_new)
+            if self.reserve_max and self.reserved + need_max > self.bm.N:
+                break
+            try:
+                self.bm.add_seq(r.rid, r.ctx)
+            except BMError as e:
+                if e.code == ENOBLOCKS:
+                    break
+                raise
+            if self.reserve_max:
+                r.reserved = need_max
+                self.reserved += need_max
+            self.waiting.popleft()
+            self.running.append(r)
+            admitted.append((r, r.ctx))
+
+        slots, cow, preempted = [], [], []
+        i = 0
+        while i < len(self.running):
+            r = self.running[i]
+            try:
+                slot, src, dst = self.bm.append_slot(r.rid)
+            except BMError as e:
+                if e.code != ENOBLOCKS:
+                    raise
+                victim = self.running.pop()
+                self.bm.free_seq(victim.rid)
+                admitted = [(a, n) for a, n in admitted if a is not victim]
+                preempted.append(victim.rid)
+                self.waiting.appendleft(victim)
+                continue
+            slots.append(slot)
+            if src >= 0:
+                cow.append((src, dst))
+            i += 1
+
+        finished = []
+        for r in self.running:
+            r.generated += 1
+            if r.generated == r.max_new:
+                finished.append(r.rid)
+                self.finishing.append(r)
+        return {
+            "batch": [r.rid for r in self.running],
+            "slots": slots,
+            "cow": cow,
+            "admitted": [(r.rid, n) for r, n in admitted],
+            "preempted": preempted,
+            "finished": finished,
+        }
+
+    def end_step(self) -> None:
+        """Free the requests that finished in the step."""
+        if not self.in_step:
+            raise BMError(EINVAL, "no step in progress")
+        self.in_step = False
+        for r in self.finishing:
+            self.bm.free_seq(r.rid)
+            self.running.remove(r)
+            self.reserved -= r.reserved
+        self.finishing = []
+
+    # -- accounting ------------------------------------------------------------
+    def tokens_held(self) -> int:
+        return sum(r.ctx for r in self.running)
+
+    def slots_committed(self) -> int:
+        """Slots the policy keeps for the running requests: allocated blocks
+        (paged) or reserved blocks (reserve policy), times B."""
+        if self.reserve_max:
+            return self.reserved * self.bm.B
+        return (self.bm.N - self.bm.num_free()) * self.bm.B
+
+    def idle(self) -> bool:
+        return not self.waiting and not self.running

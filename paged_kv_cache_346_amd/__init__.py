@@ -18,7 +18,7 @@ import numpy as np
 import torch  # imported before the library so both share torch's HIP runtime
 
 __all__ = [
-    "PkvError", "BlockManager", "pkv_reshape_and_cache", "pkv_copy_blocks",
+    "PkvError", "BlockManager", "Scheduler", "pkv_reshape_and_cache", "pkv_copy_blocks",
     "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pkv_paged_attention_main",
     "pkv_paged_attention_reduce", "pool_shapes", "paged_attention_main", "paged_attention_reduce",
     "pkv_attention_plan", "pkv_attention_plan_words", "attention_plan", "attention_plan_words",
@@ -39,6 +39,23 @@ _i32, _i64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ct
 _u32 = ctypes.c_uint32
 _pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
 
+class _SchedStep(ctypes.Structure):
+    """pkv_sched_step (include/pkv.h)."""
+    _fields_ = [("capacity", ctypes.c_int32),
+                ("batch_ids", ctypes.POINTER(ctypes.c_int64)),
+                ("slots", ctypes.POINTER(ctypes.c_int64)),
+                ("n_batch", ctypes.c_int32),
+                ("cow_pairs", ctypes.POINTER(ctypes.c_int32)),
+                ("n_cow", ctypes.c_int32),
+                ("admitted_ids", ctypes.POINTER(ctypes.c_int64)),
+                ("admitted_ctx", ctypes.POINTER(ctypes.c_int32)),
+                ("n_admitted", ctypes.c_int32),
+                ("preempted_ids", ctypes.POINTER(ctypes.c_int64)),
+                ("n_preempted", ctypes.c_int32),
+                ("finished_ids", ctypes.POINTER(ctypes.c_int64)),
+                ("n_finished", ctypes.c_int32)]
+
+
 # name -> (restype, argtypes); mirrors include/pkv.h
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -50,6 +67,13 @@ SIGNATURES = {
     "pkv_bm_fork": (_i32, [_vp, _i64, _i64]),
     "pkv_bm_free_seq": (_i32, [_vp, _i64]),
     "pkv_bm_num_free": (_i32, [_vp, _pi32]),
+    "pkv_bm_geometry": (_i32, [_vp, _pi32, _pi32]),
+    "pkv_sched_create": (_i32, [_vp, _i32, _i32, ctypes.POINTER(_vp)]),
+    "pkv_sched_destroy": (None, [_vp]),
+    "pkv_sched_add_request": (_i32, [_vp, _i64, _i32, _i32]),
+    "pkv_sched_begin_step": (_i32, [_vp, ctypes.POINTER(_SchedStep)]),
+    "pkv_sched_end_step": (_i32, [_vp]),
+    "pkv_sched_stats": (_i32, [_vp, _pi64, _pi64, _pi32, _pi32]),
     "pkv_bm_refcount": (_i32, [_vp, _i32, _pi32]),
     "pkv_bm_seq_info": (_i32, [_vp, _i64, _pi32, _pi32]),
     "pkv_bm_block_table": (_i32, [_vp, _i64, _pi32, _i32]),
@@ -162,6 +186,12 @@ class BlockManager:
     def free_seq(self, seq_id: int) -> None:
         _check(lib.pkv_bm_free_seq(self._h, seq_id), "pkv_bm_free_seq")
 
+    def geometry(self):
+        """(num_blocks, block_size)."""
+        n, b = _i32(), _i32()
+        _check(lib.pkv_bm_geometry(self._h, ctypes.byref(n), ctypes.byref(b)), "pkv_bm_geometry")
+        return n.value, b.value
+
     def num_free(self) -> int:
         out = _i32()
         _check(lib.pkv_bm_num_free(self._h, ctypes.byref(out)), "pkv_bm_num_free")
@@ -211,6 +241,73 @@ class BlockManager:
                                    _np_ptr(fq, ctypes.c_int32), ctypes.byref(nf)),
                "pkv_bm_snapshot")
         return ref.tolist(), fq[:nf.value].tolist()
+
+
+class Scheduler:
+    """Owner of a pkv_sched handle: continuous batching over a BlockManager
+    (which must outlive it).  begin_step() returns the step as a dict with the
+    same keys as the reference scheduler: batch, slots, cow, admitted
+    [(id, ctx)], preempted, finished."""
+
+    def __init__(self, bm: BlockManager, max_running: int, reserve_max: bool = False):
+        h = _vp()
+        _check(lib.pkv_sched_create(bm._h, max_running, 1 if reserve_max else 0,
+                                    ctypes.byref(h)), "pkv_sched_create")
+        self._h, self.bm, self.max_running = h, bm, int(max_running)
+        n = self.max_running
+        self._ids = np.zeros(n, np.int64)
+        self._slots = np.zeros(n, np.int64)
+        self._cow = np.zeros(2 * n, np.int32)
+        self._adm = np.zeros(n, np.int64)
+        self._adm_ctx = np.zeros(n, np.int32)
+        self._pre = np.zeros(n, np.int64)
+        self._fin = np.zeros(n, np.int64)
+        self._step = _SchedStep(n, _np_ptr(self._ids, ctypes.c_int64),
+                                _np_ptr(self._slots, ctypes.c_int64), 0,
+                                _np_ptr(self._cow, ctypes.c_int32), 0,
+                                _np_ptr(self._adm, ctypes.c_int64),
+                                _np_ptr(self._adm_ctx, ctypes.c_int32), 0,
+                                _np_ptr(self._pre, ctypes.c_int64), 0,
+                                _np_ptr(self._fin, ctypes.c_int64), 0)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib.pkv_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
+        _check(lib.pkv_sched_add_request(self._h, req_id, prompt_len, max_new_tokens),
+               "pkv_sched_add_request")
+
+    def begin_step(self):
+        st = self._step
+        _check(lib.pkv_sched_begin_step(self._h, ctypes.byref(st)), "pkv_sched_begin_step")
+        nb, nc = st.n_batch, st.n_cow
+        return {
+            "batch": self._ids[:nb].tolist(),
+            "slots": self._slots[:nb].tolist(),
+            "cow": [tuple(x) for x in self._cow[:2 * nc].reshape(-1, 2).tolist()],
+            "admitted": list(zip(self._adm[:st.n_admitted].tolist(),
+                                 self._adm_ctx[:st.n_admitted].tolist())),
+            "preempted": self._pre[:st.n_preempted].tolist(),
+            "finished": self._fin[:st.n_finished].tolist(),
+        }
+
+    def end_step(self) -> None:
+        _check(lib.pkv_sched_end_step(self._h), "pkv_sched_end_step")
+
+    def stats(self):
+        """(tokens held, slots committed, waiting, running)."""
+        held, committed, nw, nr = _i64(), _i64(), _i32(), _i32()
+        _check(lib.pkv_sched_stats(self._h, ctypes.byref(held), ctypes.byref(committed),
+                                   ctypes.byref(nw), ctypes.byref(nr)), "pkv_sched_stats")
+        return held.value, committed.value, nw.value, nr.value
 
 
 # ---------------------------------------------------------------------------

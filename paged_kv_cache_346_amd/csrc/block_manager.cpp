@@ -165,6 +165,13 @@ pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id) {
   return PKV_OK;
 }
 
+pkv_status pkv_bm_geometry(const pkv_bm* bm, int32_t* num_blocks, int32_t* block_size) {
+  if (!bm || !num_blocks || !block_size) return PKV_EINVAL;
+  *num_blocks = bm->N;
+  *block_size = bm->B;
+  return PKV_OK;
+}
+
 pkv_status pkv_bm_num_free(const pkv_bm* bm, int32_t* out) {
   if (!bm || !out) return PKV_EINVAL;
   *out = bm->nfree;

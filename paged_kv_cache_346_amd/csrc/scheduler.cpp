@@ -1,0 +1,187 @@
+// Iteration-level (continuous) batching scheduler behind the pkv_sched_* entry
+// points: a host-side loop driver over one block manager.
+//
+// PagedAttention and Continuous Batching, "Batch by step, not by request": the
+// batch is rebuilt after every decode step -- finished sequences leave, waiting
+// ones join -- and with paging a newcomer needs only free blocks.
+// PagedAttention: The vLLM Paper, "Continuous Batching" (A finishes, A dequeues,
+// D enqueues, giving {B, C, D}) and "Implementation Essentials" (preemption
+// drops a request's blocks for later recomputation under memory pressure).
+//
+// Policy (readings of the pages, stated in include/pkv.h): first-come
+// first-served admission with no skipping ahead; at most max_running requests;
+// one token per running request per step, appended in admission order; the
+// most recently admitted request is preempted when an append finds no free
+// block.  The reserve policy simulates the max-length reservation of the
+// systems before paging over the same pool.  Integer bookkeeping only.
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/pkv.h"
+
+struct pkv_sched {
+  struct Req {
+    int64_t id;
+    int32_t prompt, max_new, generated, reserved;
+    int32_t ctx() const { return prompt + generated; }
+  };
+  pkv_bm* bm = nullptr;
+  int32_t N = 0, B = 0, max_running = 0;
+  bool reserve = false;
+  int64_t reserved_total = 0;
+  bool in_step = false;
+  std::unordered_map<int64_t, Req> reqs;  // every submitted, unfinished request
+  std::deque<Req*> waiting;
+  std::vector<Req*> running;
+  std::vector<Req*> finishing;
+
+  int32_t blocks(int64_t tokens) const { return (int32_t)((tokens + B - 1) / B); }
+};
+
+extern "C" {
+
+pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t reserve_max,
+                            pkv_sched** out) {
+  if (!out) return PKV_EINVAL;
+  *out = nullptr;
+  if (!bm || max_running <= 0) return PKV_EINVAL;
+  int32_t N = 0, B = 0;
+  if (pkv_bm_geometry(bm, &N, &B) != PKV_OK) return PKV_EINVAL;
+  pkv_sched* s = new (std::nothrow) pkv_sched();
+  if (!s) return PKV_EINVAL;
+  s->bm = bm;
+  s->N = N;
+  s->B = B;
+  s->max_running = max_running;
+  s->reserve = reserve_max != 0;
+  *out = s;
+  return PKV_OK;
+}
+
+void pkv_sched_destroy(pkv_sched* s) { delete s; }
+
+pkv_status pkv_sched_add_request(pkv_sched* s, int64_t req_id, int32_t prompt_len,
+                                 int32_t max_new_tokens) {
+  if (!s || prompt_len < 0 || max_new_tokens < 1) return PKV_EINVAL;
+  if (s->reqs.count(req_id)) return PKV_EEXIST;
+  if (s->blocks((int64_t)prompt_len + max_new_tokens) > s->N) return PKV_EINVAL;
+  auto it = s->reqs.emplace(req_id, pkv_sched::Req{req_id, prompt_len, max_new_tokens, 0, 0});
+  s->waiting.push_back(&it.first->second);
+  return PKV_OK;
+}
+
+pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
+  if (!s || !o || o->capacity < s->max_running) return PKV_EINVAL;
+  if (!o->batch_ids || !o->slots || !o->cow_pairs || !o->admitted_ids || !o->admitted_ctx ||
+      !o->preempted_ids || !o->finished_ids)
+    return PKV_EINVAL;
+  if (s->in_step) return PKV_EINVAL;  // end_step() of the last step is due
+  o->n_batch = o->n_cow = o->n_admitted = o->n_preempted = o->n_finished = 0;
+  s->in_step = true;
+
+  // admissions, first come first served
+  std::vector<std::pair<pkv_sched::Req*, int32_t>> admitted;
+  while (!s->waiting.empty() && (int32_t)s->running.size() < s->max_running) {
+    pkv_sched::Req* r = s->waiting.front();
+    const int32_t need_max = s->blocks((int64_t)r->prompt + r->max_new);
+    if (s->reserve && s->reserved_total + need_max > s->N) break;
+    const pkv_status st = pkv_bm_add_seq(s->bm, r->id, r->ctx());
+    if (st == PKV_ENOBLOCKS) break;
+    if (st != PKV_OK) return st;
+    if (s->reserve) {
+      r->reserved = need_max;
+      s->reserved_total += need_max;
+    }
+    s->waiting.pop_front();
+    s->running.push_back(r);
+    admitted.emplace_back(r, r->ctx());
+  }
+
+  // one slot per running request; preempt the youngest when the pool is dry
+  size_t i = 0;
+  while (i < s->running.size()) {
+    pkv_sched::Req* r = s->running[i];
+    int64_t slot;
+    int32_t src, dst;
+    const pkv_status st = pkv_bm_append_slot(s->bm, r->id, &slot, &src, &dst);
+    if (st == PKV_ENOBLOCKS) {
+      pkv_sched::Req* victim = s->running.back();
+      s->running.pop_back();
+      const pkv_status fs = pkv_bm_free_seq(s->bm, victim->id);
+      if (fs != PKV_OK) return fs;
+      for (size_t k = 0; k < admitted.size(); ++k)
+        if (admitted[k].first == victim) {
+          admitted.erase(admitted.begin() + k);
+          break;
+        }
+      o->preempted_ids[o->n_preempted++] = victim->id;
+      s->waiting.push_front(victim);
+      continue;
+    }
+    if (st != PKV_OK) return st;
+    o->slots[i] = slot;
+    if (src >= 0) {
+      o->cow_pairs[2 * o->n_cow] = src;
+      o->cow_pairs[2 * o->n_cow + 1] = dst;
+      ++o->n_cow;
+    }
+    ++i;
+  }
+
+  for (size_t k = 0; k < s->running.size(); ++k) {
+    pkv_sched::Req* r = s->running[k];
+    o->batch_ids[k] = r->id;
+    r->generated += 1;
+    if (r->generated == r->max_new) {
+      o->finished_ids[o->n_finished++] = r->id;
+      s->finishing.push_back(r);
+    }
+  }
+  o->n_batch = (int32_t)s->running.size();
+  for (const auto& a : admitted) {
+    o->admitted_ids[o->n_admitted] = a.first->id;
+    o->admitted_ctx[o->n_admitted] = a.second;
+    ++o->n_admitted;
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_sched_end_step(pkv_sched* s) {
+  if (!s || !s->in_step) return PKV_EINVAL;
+  s->in_step = false;
+  for (pkv_sched::Req* r : s->finishing) {
+    const pkv_status st = pkv_bm_free_seq(s->bm, r->id);
+    if (st != PKV_OK) return st;
+    for (size_t k = 0; k < s->running.size(); ++k)
+      if (s->running[k] == r) {
+        s->running.erase(s->running.begin() + k);
+        break;
+      }
+    s->reserved_total -= r->reserved;
+    s->reqs.erase(r->id);
+  }
+  s->finishing.clear();
+  return PKV_OK;
+}
+
+pkv_status pkv_sched_stats(const pkv_sched* s, int64_t* tokens_held, int64_t* slots_committed,
+                           int32_t* n_waiting, int32_t* n_running) {
+  if (!s || !tokens_held || !slots_committed || !n_waiting || !n_running) return PKV_EINVAL;
+  int64_t held = 0;
+  for (const pkv_sched::Req* r : s->running) held += r->ctx();
+  *tokens_held = held;
+  if (s->reserve) {
+    *slots_committed = s->reserved_total * s->B;
+  } else {
+    int32_t nfree = 0;
+    pkv_bm_num_free(s->bm, &nfree);
+    *slots_committed = (int64_t)(s->N - nfree) * s->B;
+  }
+  *n_waiting = (int32_t)s->waiting.size();
+  *n_running = (int32_t)s->running.size();
+  return PKV_OK;
+}
+
+}  // extern "C"

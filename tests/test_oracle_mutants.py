@@ -103,3 +103,55 @@ def test_block_manager_mutants_fail_pins(monkeypatch, cls):
         except AssertionError:
             failed += 1
     assert failed > 0
+
+
+# --- continuous-batching scheduler -------------------------------------------
+import oracle.scheduler as osched
+from tests import test_oracle_scheduler as tsched
+
+
+class _SkipAheadSched(osched.Scheduler):
+    """Admits a later request when the head of the queue does not fit."""
+
+    def begin_step(self):
+        if self.waiting and len(self.waiting) > 1:
+            head = self.waiting[0]
+            need = -(-head.ctx // self.bm.B)
+            if need > self.bm.num_free():
+                self.waiting.rotate(-1)
+        return super().begin_step()
+
+
+class _PreemptOldestSched(osched.Scheduler):
+    """Preempts the oldest running request instead of the youngest."""
+
+    def begin_step(self):
+        self.running.reverse()
+        out = super().begin_step()
+        return out
+
+
+class _NoRejoinSched(osched.Scheduler):
+    """Frees finished requests only every other step (slow to let others join)."""
+
+    def end_step(self):
+        self._flip = not getattr(self, "_flip", False)
+        if self._flip:
+            self.in_step = False
+            return
+        super().end_step()
+
+
+@pytest.mark.parametrize("cls", [_SkipAheadSched, _PreemptOldestSched, _NoRejoinSched])
+def test_scheduler_mutants_fail_pins(monkeypatch, cls):
+    monkeypatch.setattr(tsched, "Scheduler", cls)
+    tests = [tsched.test_iteration_level_figure, tsched.test_preemption_drops_the_youngest_and_recomputes_it]
+    tests += [lambda s=s, r=r: tsched.test_invariants_on_random_traces(s, r)
+              for s in range(6) for r in (False, True)]
+    failed = 0
+    for t in tests:
+        try:
+            t()
+        except (AssertionError, osched.BMError, IndexError, ValueError, KeyError):
+            failed += 1
+    assert failed > 0

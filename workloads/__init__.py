@@ -231,3 +231,17 @@ def random_script(rng: np.random.Generator, n_ops: int, max_seqs: int = 8, max_a
         else:
             ops.append(("free", sid))
     return ops
+
+
+def request_trace(rng: np.random.Generator, n: int, prompt_median: float = 256.0,
+                  prompt_sigma: float = 1.0, out_median: float = 256.0, out_sigma: float = 0.8,
+                  max_prompt: int = 2048, max_out: int = 1024):
+    """A synthetic request trace for the continuous-batching loop: n requests
+    (id, prompt_len, max_new_tokens) with log-normal prompt and output lengths
+    (a long-tailed mix like chat serving traffic; not drawn from any dataset),
+    all submitted at the start."""
+    p = np.clip(np.rint(np.exp(rng.normal(math.log(prompt_median), prompt_sigma, n))), 1,
+                max_prompt).astype(np.int64)
+    o = np.clip(np.rint(np.exp(rng.normal(math.log(out_median), out_sigma, n))), 1,
+                max_out).astype(np.int64)
+    return [(i, int(p[i]), int(o[i])) for i in range(n)]
