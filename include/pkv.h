@@ -134,6 +134,13 @@ pkv_status pkv_bm_seq_info(const pkv_bm* bm, int64_t seq_id, int32_t* len, int32
 /* Copy the sequence's table into out[cap]; PKV_EINVAL if cap is too small. */
 pkv_status pkv_bm_block_table(const pkv_bm* bm, int64_t seq_id, int32_t* out, int32_t cap);
 
+/* Slot numbers (block*B + offset) of the sequence's tokens [start,
+ * start+count) into slots[count] -- where a prefill writes its KV
+ * ([RTI] "Pages, from operating systems": token t of a request lives in its
+ * logical block t/B, mapped by the block table).  PKV_EINVAL past its length. */
+pkv_status pkv_bm_slots(const pkv_bm* bm, int64_t seq_id, int32_t start, int32_t count,
+                        int64_t* slots);
+
 /* Host arrays for a decode batch: block_tables[n*max_blocks] (row i = seq_ids[i],
  * padded with -1) and context_lens[n]. */
 pkv_status pkv_bm_fill_batch(const pkv_bm* bm, const int64_t* seq_ids, int32_t n,

@@ -153,6 +153,17 @@ class BlockManager:
         return tables, lens
 
 
+def slots(bm, sid, start: int, count: int):
+    """Slots of tokens [start, start+count) of a sequence: token t lives in
+    logical block t // B at offset t % B ("Pages, from operating systems")."""
+    if sid not in bm.tables:
+        raise BMError(ENOSEQ)
+    if start < 0 or count < 0 or start + count > bm.lens[sid]:
+        raise BMError(EINVAL, "tokens past the sequence's length")
+    t = bm.tables[sid]
+    return [t[i // bm.B] * bm.B + i % bm.B for i in range(start, start + count)]
+
+
 def count_shared(bm, seq_ids) -> int:
     """Table entries of the listed sequences whose block is referenced by more
     than one table (a block shared through fork, "Pages, from operating

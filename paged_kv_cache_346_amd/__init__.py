@@ -80,6 +80,7 @@ SIGNATURES = {
     "pkv_bm_fill_batch": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
     "pkv_bm_snapshot": (_i32, [_vp, _pi32, _pi32, _pi32]),
     "pkv_bm_count_shared": (_i32, [_vp, _pi64, _i32, _pi64]),
+    "pkv_bm_slots": (_i32, [_vp, _i64, _i32, _i32, _pi64]),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -224,6 +225,13 @@ class BlockManager:
                                      _np_ptr(tables, ctypes.c_int32),
                                      _np_ptr(lens, ctypes.c_int32)), "pkv_bm_fill_batch")
         return tables, lens
+
+    def slots(self, seq_id: int, start: int, count: int) -> np.ndarray:
+        """int64 slots of tokens [start, start+count) of a sequence."""
+        out = np.empty(max(count, 1), np.int64)
+        _check(lib.pkv_bm_slots(self._h, seq_id, start, count, _np_ptr(out, ctypes.c_int64)),
+               "pkv_bm_slots")
+        return out[:count]
 
     def count_shared(self, seq_ids) -> int:
         """Table entries of these sequences whose block has refcount > 1."""

@@ -203,6 +203,21 @@ pkv_status pkv_bm_block_table(const pkv_bm* bm, int64_t seq_id, int32_t* out, in
   return PKV_OK;
 }
 
+pkv_status pkv_bm_slots(const pkv_bm* bm, int64_t seq_id, int32_t start, int32_t count,
+                        int64_t* slots) {
+  if (!bm || start < 0 || count < 0 || (count > 0 && !slots)) return PKV_EINVAL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  const auto& s = it->second;
+  if ((int64_t)start + count > s.len) return PKV_EINVAL;
+  const int32_t B = bm->B;
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t t = start + i;
+    slots[i] = (int64_t)s.table[t / B] * B + t % B;
+  }
+  return PKV_OK;
+}
+
 pkv_status pkv_bm_fill_batch(const pkv_bm* bm, const int64_t* seq_ids, int32_t n,
                              int32_t max_blocks, int32_t* block_tables, int32_t* context_lens) {
   if (!bm || n < 0 || max_blocks < 0) return PKV_EINVAL;

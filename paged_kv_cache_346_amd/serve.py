@@ -1,0 +1,150 @@
+"""Continuous-batching decode loop for one attention layer on one GPU.
+
+Drives the native scheduler (pkv_sched_*) and the device kernels step by step
+(PagedAttention and Continuous Batching, "Batch by step, not by request";
+PagedAttention: The vLLM Paper, "Continuous Batching" and "Implementation
+Essentials"): every step
+
+  1. the scheduler admits waiting requests into free blocks, appends one slot
+     per running request (preempting the youngest when the pool runs dry) and
+     names the requests that finish;
+  2. copy-on-write block copies run, then one reshape_and_cache writes the
+     prompt KV of the admitted requests and the new token of every running one;
+  3. paged attention runs over the batch's block tables (host work plan);
+  4. the finished requests give their blocks back.
+
+The step's metadata (slots, block tables, lengths, work plan) is packed into
+one pinned host buffer and sent with a single asynchronous copy; two buffers
+alternate so the host fills one while the previous step's copy may still run.
+
+K/V and query values come from caller-supplied sources (the loop computes no
+model): kv_source(pairs) returns the K and V rows [T, Hkv, D] for an int64
+array of (request id, token position) pairs, and q_source(ids) the queries
+[n, Hq, D] of the batch.  Everything the method computes runs in libpkv.so.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import (BlockManager, Plan, Scheduler, attention_plan, attention_workspace_bytes,
+               copy_blocks, paged_attention_decode, pool_shapes, reshape_and_cache)
+
+
+def _pad4(n: int) -> int:
+    return (n + 3) // 4 * 4   # int32 words to the next 16-byte boundary
+
+
+class DecodeLoop:
+    def __init__(self, *, num_blocks: int, block_size: int, q_heads: int, kv_heads: int,
+                 head_dim: int, max_running: int, max_len: int, dtype=torch.bfloat16,
+                 partition_size: int = 0, reserve_max: bool = False, free_order=None,
+                 device="cuda"):
+        self.B, self.Hq, self.Hkv, self.D = block_size, q_heads, kv_heads, head_dim
+        self.P = partition_size
+        self.max_len = max_len
+        self.max_blocks = max(1, math.ceil(max_len / block_size))
+        self.device = torch.device(device)
+        self.bm = BlockManager(num_blocks, block_size, free_order)
+        self.sched = Scheduler(self.bm, max_running, reserve_max)
+        ks, vs = pool_shapes(num_blocks, kv_heads, head_dim, block_size, dtype)
+        self.k_pool = torch.empty(ks, dtype=dtype, device=self.device)
+        self.v_pool = torch.empty(vs, dtype=dtype, device=self.device)
+        nbytes = attention_workspace_bytes(max_running, q_heads, head_dim, max_len,
+                                           partition_size)
+        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        self.out = torch.empty((max_running, q_heads, head_dim), dtype=torch.float32,
+                               device=self.device)
+        self._host = [None, None]      # pinned int32 staging buffers, used alternately
+        self._done = [None, None]      # event after each buffer's last copy
+        self._dev = None
+        self._turn = 0
+
+    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
+        if prompt_len + max_new_tokens > self.max_len:
+            raise ValueError("request longer than the loop's max_len")
+        self.sched.add_request(req_id, prompt_len, max_new_tokens)
+
+    def _stage(self, parts):
+        """Copy the int32 arrays `parts` to the device in one transfer; returns
+        device views of them (each starting on a 16-byte boundary)."""
+        total = sum(_pad4(p.size) for p in parts)
+        i = self._turn
+        self._turn ^= 1
+        if self._done[i] is not None:
+            self._done[i].synchronize()    # its previous copy has left the buffer
+        if self._host[i] is None or self._host[i].numel() < total:
+            cap = max(total, 1 << 16) * 2
+            self._host[i] = torch.empty(cap, dtype=torch.int32, pin_memory=True)
+            if self._dev is None or self._dev.numel() < cap:
+                self._dev = torch.empty(cap, dtype=torch.int32, device=self.device)
+        host = self._host[i].numpy()
+        off, spans = 0, []
+        for p in parts:
+            host[off:off + p.size] = p.reshape(-1)
+            spans.append((off, p.size))
+            off += _pad4(p.size)
+        self._dev[:total].copy_(self._host[i][:total], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._done[i] = ev
+        return [self._dev[o:o + n] for o, n in spans]
+
+    def step(self, kv_source, q_source):
+        """One iteration.  Returns (the scheduler's step dict -- plus "stats",
+        the scheduler's (tokens held, slots committed, waiting, running) taken
+        before the finished requests leave --, the attention output [n_batch,
+        Hq, D] -- a view valid until the next step -- and the host context
+        lengths of the batch)."""
+        st = self.sched.begin_step()
+        ids, slots = st["batch"], st["slots"]
+        n = len(ids)
+        # token writes: the admitted requests' prompts, then one token per request
+        pairs, write_slots = [], []
+        for rid, ctx in st["admitted"]:
+            if ctx:
+                write_slots.append(self.bm.slots(rid, 0, ctx))
+                pairs.append(np.stack([np.full(ctx, rid, np.int64),
+                                       np.arange(ctx, dtype=np.int64)], 1))
+        lens = np.empty(0, np.int32)
+        if n:
+            tables, lens = self.bm.fill_batch(ids, self.max_blocks)
+            mcl = int(lens.max())
+            width = max(1, -(-mcl // self.B))          # the batch's widest table
+            tables = np.ascontiguousarray(tables[:, :width])
+            words, n_items, n_merge = attention_plan(lens, self.Hkv, self.B, width, mcl,
+                                                     self.P)
+            write_slots.append(np.asarray(slots, np.int64))
+            pairs.append(np.stack([np.asarray(ids, np.int64), lens.astype(np.int64) - 1], 1))
+        parts = []
+        if write_slots:
+            parts.append(np.concatenate(write_slots).view(np.int32))
+        if n:
+            parts += [tables.reshape(-1), lens, words]
+        dev = self._stage(parts) if parts else []
+        if st["cow"]:
+            copy_blocks(self.k_pool, self.v_pool,
+                        torch.tensor(st["cow"], dtype=torch.int32, device=self.device))
+        if write_slots:
+            pairs = np.concatenate(pairs)
+            k, v = kv_source(pairs)
+            reshape_and_cache(k, v, self.k_pool, self.v_pool, dev[0].view(torch.int64))
+        out = self.out[:n]
+        if n:
+            d_tables, d_lens, d_plan = dev[-3:]
+            paged_attention_decode(out, q_source(ids), self.k_pool, self.v_pool,
+                                   d_tables.view(n, -1), d_lens, mcl, partition_size=self.P,
+                                   workspace=self.ws, plan=Plan(d_plan, n_items, n_merge))
+        st["stats"] = self.sched.stats()   # before the finished requests leave
+        self.sched.end_step()
+        return st, out, lens
+
+    def stats(self):
+        """(tokens held, slots committed, waiting, running)."""
+        return self.sched.stats()
+
+    def idle(self) -> bool:
+        _, _, nw, nr = self.sched.stats()
+        return nw == 0 and nr == 0

@@ -7,6 +7,7 @@ import pytest
 
 import workloads as W
 from oracle.block_manager import BlockManager as RefBM, count_shared as ref_count_shared
+from oracle.block_manager import slots as ref_slots
 from oracle.block_manager import run_ops as ref_run
 
 
@@ -57,6 +58,10 @@ def test_random_scripts_bit_exact(pkv, seed):
         assert_same_state(native, ref, range(7))
         live = [i for i in range(7) if i in ref.tables]
         assert native.count_shared(live) == ref_count_shared(ref, live)
+        for sid in live:
+            L = ref.lens[sid]
+            a = int(rng.integers(0, L + 1))
+            assert native.slots(sid, a, L - a).tolist() == ref_slots(ref, sid, a, L - a)
 
 
 @pytest.mark.parametrize("name", ["tiny_mha_f32", "opt13b_mha", "llama8b_gqa", "sampling_steady",
@@ -106,3 +111,13 @@ def test_count_shared_rejects_unknown_ids(pkv):
     with pytest.raises(pkv.PkvError) as e:
         bm.count_shared([0, 5])
     assert e.value.code == pkv.PKV_ENOSEQ
+
+
+def test_slots_rejects_tokens_past_the_length(pkv):
+    bm = pkv.BlockManager(4, 16)
+    bm.add_seq(0, 20)
+    assert bm.slots(0, 0, 20).tolist() == [i for i in range(16)] + [16 + i for i in range(4)]
+    with pytest.raises(pkv.PkvError):
+        bm.slots(0, 10, 11)
+    with pytest.raises(pkv.PkvError):
+        bm.slots(3, 0, 1)
