@@ -4,9 +4,12 @@
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
 
 One step is one pass of the whole device path over one batch that already sits
-in HBM: copy-on-write block copies (when the batch has any), reshape_and_cache
-of the step's new tokens (when it has any), the paged-attention main kernel and
-the log-sum-exp reduce, for one attention layer.  The host block manager builds
+in HBM: copy-on-write block copies (when the batch has any), the write of the
+step's new tokens into their slots, the paged-attention main kernel and the
+log-sum-exp reduce, for one attention layer.  When every sequence appends one
+token at its last position (a decode step) the main kernel writes the tokens
+itself; otherwise, or with --separate-cache-write, reshape_and_cache runs
+first.  The host block manager builds
 the batch (slots, copy pairs, block tables) once before timing; its cost is
 reported separately.
 
@@ -46,16 +49,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 DESCRIPTIONS = {
     "tiny_mha_f32": "tiny MHA decode: 4 seqs, 4 heads, D 64, B 16, fp32, L {1,15,16,70}, "
-                    "+ reshape_and_cache of 4 tokens",
+                    "+ 4 new tokens, one per sequence",
     "opt13b_mha": "OPT-13B-shaped layer decode: 64 seqs, 40 heads (MHA), D 128, B 16, bf16 KV, "
                   "L uniform [128,2048]",
     "llama8b_gqa": "Llama-3-8B-shaped GQA decode: 256 seqs, 32 q heads / 8 KV heads, D 128, "
                    "B 16, bf16 KV, L log-normal (median 600, sigma 0.8) clipped [16,4096], "
-                   "+ reshape_and_cache of 256 new tokens",
+                   "+ 256 new tokens, one per sequence",
     "sampling_steady": "parallel sampling, steady step: 32 prompts x 8 samples, 1024-token "
                        "shared prompt blocks (refcount 8), 32/8 heads, D 128, B 16, bf16",
     "sampling_fork": "parallel sampling, fork step: 32 prompts x 8 samples, 224 copy-on-write "
-                     "block copies before the cache write, 32/8 heads, D 128, B 16, bf16",
+                     "block copies before the token writes, 32/8 heads, D 128, B 16, bf16",
     "long70b_b16": "70B-shaped long-context decode: 16 seqs x 32768 tokens, 64 q heads / 8 KV "
                    "heads, D 128, B 16, bf16, 512-token partitions + log-sum-exp reduce",
     "long70b_b32": "70B-shaped long-context decode: 16 seqs x 32768 tokens, 64 q heads / 8 KV "
@@ -90,7 +93,8 @@ class Batch:
     """One decode batch, built through the product's block manager and resident
     on the device."""
 
-    def __init__(self, pkv, torch, W, name: str, partition_size=None, layers=0, use_plan=True):
+    def __init__(self, pkv, torch, W, name: str, partition_size=None, layers=0, use_plan=True,
+                 append=True):
         import numpy as np
         self.cfg = c = W.CONFIGS[name]
         self.w = w = W.make(name, pools=False)
@@ -143,6 +147,9 @@ class Batch:
         self.k_pool, self.v_pool = self.pools[0]
         self.q = self._to_dev(torch, w.q)
         self.slots = None if slots is None else torch.from_numpy(slots).to(dev)
+        # a decode step appends one token per sequence, in batch order: the
+        # attention launch can write them itself
+        self.append = bool(append and slots is not None and list(w.step_ids) == ids)
         self.k_new = self._to_dev(torch, w.k_new) if slots is not None else None
         self.v_new = self._to_dev(torch, w.v_new) if slots is not None else None
         self.pairs = (torch.from_numpy(pairs).to(dev)
@@ -187,14 +194,16 @@ class Batch:
         if self.pairs is not None:
             pkv.copy_blocks(self.k_pool, self.v_pool, self.pairs)
         rec(1)
-        if self.slots is not None:
+        if self.slots is not None and not self.append:
             pkv.reshape_and_cache(self.k_new, self.v_new, self.k_pool, self.v_pool, self.slots)
         rec(2)
         if main_ev is not None:
             main_ev[0].record()
+        nk, nv = (self.k_new, self.v_new) if self.append else (None, None)
         pkv.paged_attention_main(self.out, self.q, self.k_pool, self.v_pool, self.tables,
                                  self.lens, self.mcl, partition_size=self.P, workspace=self.ws,
-                                 shared_kv=self.shared_kv, plan=self.plan)
+                                 shared_kv=self.shared_kv, plan=self.plan, new_key=nk,
+                                 new_value=nv)
         if main_ev is not None:
             main_ev[1].record()
         rec(3)
@@ -205,7 +214,8 @@ class Batch:
 
     def launches(self):
         """Which of the four step kernels this batch launches."""
-        return (self.pairs is not None, self.slots is not None, True, self.mcl > (self.P or 512))
+        return (self.pairs is not None, self.slots is not None and not self.append, True,
+                self.mcl > (self.P or 512))
 
 
 def cpu_baseline(batch, torch, budget_s: float):
@@ -363,6 +373,9 @@ def main() -> int:
     ap.add_argument("--config", default="llama8b_gqa", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition size (tokens per workgroup)")
+    ap.add_argument("--separate-cache-write", action="store_true",
+                    help="write the step's tokens with reshape_and_cache instead of the "
+                         "attention launch")
     ap.add_argument("--no-plan", action="store_true",
                     help="launch without the host work plan (one wave per possible partition)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -403,7 +416,8 @@ def main() -> int:
 
     name = args.config
     log(f"bench: building workload {name}")
-    batch = Batch(pkv, torch, W, name, args.partition_size, args.layers, not args.no_plan)
+    batch = Batch(pkv, torch, W, name, args.partition_size, args.layers, not args.no_plan,
+                  not args.separate_cache_write)
     c = batch.cfg
     log(f"bench: N={batch.w.num_blocks} blocks, KV {batch.kv_bytes / 1e6:.1f} MB, "
         f"{batch.n_pairs} CoW pairs, max L {batch.mcl}")
@@ -473,6 +487,8 @@ def main() -> int:
         "kv_bytes_per_step": batch.kv_bytes,
         "shared_block_entries": batch.shared_entries,
         "host_plan": batch.plan is not None,
+        "cache_write": ("none" if batch.slots is None else
+                        "in the attention launch" if batch.append else "reshape_and_cache"),
         "work_items": None if batch.plan is None else batch.plan.n_items,
         "pool_bytes_per_layer": batch.pool_bytes,
     }

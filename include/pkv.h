@@ -290,6 +290,19 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  * each new token attends over all previous tokens).
  *   out           device fp32 [S, Hq, D]: softmax(q K^T * scale) V per (s, h)
  *   q             device [S, Hq, D], pool dtype
+ *   k_pool/v_pool device pools; written only when new_key is given
+ *   new_key, new_value   NULL, or device [S, Hkv, D] in the pool dtype: the
+ *                 token each sequence appends this step (a decode step).  The
+ *                 token is the sequence's last, at position context_lens[s]-1;
+ *                 it is written into that position's slot (block
+ *                 block_tables[s][(L-1)/B], offset (L-1)%B) and attended to in
+ *                 the same launch.  Pools and output are bit-identical to
+ *                 pkv_reshape_and_cache with those slots followed by the call
+ *                 without new_key.  Copy-on-write copies must run before, so
+ *                 that no other sequence of the batch reads the written block.
+ *                 A zero-length sequence appends nothing, and so does one whose
+ *                 context_lens[s] exceeds max_context_len or max_blocks*B (its
+ *                 last position is not in the launch).
  *   block_tables  device int32 [S, max_blocks]
  *   context_lens  device int32 [S]: tokens of sequence s (the one written this
  *                 step included); 0 gives a zero row; at most
@@ -314,8 +327,9 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *   flags         0 or PKV_ATTN_SHARED_KV (other bits: PKV_EINVAL)
  * Compiled shapes: D in {64, 128}, B in {16, 32}; bf16 with Hq/Hkv in
  * {1, 2, 4, 8}; fp32 with Hq/Hkv in {1, 2, 4, 8}.  Others: PKV_EUNSUPPORTED. */
-pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_pool,
-                                      const void* v_pool, const int32_t* block_tables,
+pkv_status pkv_paged_attention_decode(float* out, const void* q, void* k_pool, void* v_pool,
+                                      const void* new_key, const void* new_value,
+                                      const int32_t* block_tables,
                                       const int32_t* context_lens, int32_t S, int32_t Hq,
                                       int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
                                       int32_t num_blocks, int32_t max_context_len,
@@ -337,8 +351,9 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_p
  * repeat the values given to the main call (same S, Hq, Hkv, D, B, max_blocks,
  * max_context_len, partition_size, plan, context_lens, workspace); it reads
  * nothing else and is a no-op when every sequence fits one partition. */
-pkv_status pkv_paged_attention_main(float* out, const void* q, const void* k_pool,
-                                    const void* v_pool, const int32_t* block_tables,
+pkv_status pkv_paged_attention_main(float* out, const void* q, void* k_pool, void* v_pool,
+                                    const void* new_key, const void* new_value,
+                                    const int32_t* block_tables,
                                     const int32_t* context_lens, int32_t S, int32_t Hq,
                                     int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
                                     int32_t num_blocks, int32_t max_context_len, float scale,

@@ -88,12 +88,12 @@ SIGNATURES = {
     "pkv_attention_plan_words": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_attention_plan": (_i32, [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _sz, _pi32,
                                   _pi32]),
-    "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                          _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32,
-                                          _vp, _sz, _i32, _u32, _vp]),
-    "pkv_paged_attention_main": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                        _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32, _i32, _vp,
-                                        _sz, _i32, _u32, _vp]),
+    "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
+                                          _i32, _i32, _vp, _sz, _i32, _u32, _vp]),
+    "pkv_paged_attention_main": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32,
+                                        _i32, _vp, _sz, _i32, _u32, _vp]),
     "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _i32, _i32, _vp, _sz, _vp]),
 }
@@ -445,9 +445,17 @@ def _plan_args(plan):
 
 
 def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                    scale, partition_size, plan, workspace, shared_kv):
+                    scale, partition_size, plan, workspace, shared_kv, new_key, new_value):
     N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
     S, Hq = q.shape[0], q.shape[1]
+    nk = nv = None
+    if (new_key is None) != (new_value is None):
+        raise ValueError("new_key and new_value go together")
+    if new_key is not None:
+        for t, name in ((new_key, "new_key"), (new_value, "new_value")):
+            if tuple(t.shape) != (S, Hkv, D) or t.dtype != k_pool.dtype:
+                raise ValueError(f"{name} must be [S, Hkv, D] in the pool dtype")
+        nk, nv = _dev(new_key, "new_key"), _dev(new_value, "new_value")
     if tuple(q.shape) != (S, Hq, D) or q.dtype != k_pool.dtype:
         raise ValueError("q must be [S, Hq, D] in the pool dtype")
     if out.dtype != torch.float32 or tuple(out.shape) != (S, Hq, D):
@@ -463,7 +471,8 @@ def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_cont
         ws_ptr = _dev(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
     return (_dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
-            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, D,
+            nk, nv, _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq,
+            Hkv, D,
             B, block_tables.shape[1], N, int(max_context_len), float(scale), int(partition_size),
             *_plan_args(plan), ws_ptr, ws_bytes, _dtype_code(k_pool),
             PKV_ATTN_SHARED_KV if shared_kv else 0)
@@ -472,26 +481,30 @@ def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_cont
 def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
                                max_context_len: int, scale: float | None = None,
                                partition_size: int = 0, workspace=None, stream=None,
-                               shared_kv: bool = False, plan: Plan | None = None) -> None:
+                               shared_kv: bool = False, plan: Plan | None = None,
+                               new_key=None, new_value=None) -> None:
     """out[s, h] = softmax(q[s, h] K_s^T * scale) V_s through the block tables.
 
     out fp32 [S, Hq, D]; q [S, Hq, D] in the pool dtype; block_tables int32
     [S, max_blocks]; context_lens int32 [S].  `workspace` (a uint8 device tensor)
     is needed when max_context_len exceeds one partition.  `shared_kv` sets
     PKV_ATTN_SHARED_KV (the batch shares blocks; a load-policy hint only).
-    `plan` (make_plan) runs exactly the batch's work items."""
+    `plan` (make_plan) runs exactly the batch's work items.  `new_key` /
+    `new_value` ([S, Hkv, D]) append each sequence's token of this step (its
+    position context_lens[s]-1) into the pools in the same launch."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                           scale, partition_size, plan, workspace, shared_kv)
+                           scale, partition_size, plan, workspace, shared_kv, new_key, new_value)
     _check(lib.pkv_paged_attention_decode(*args, _stream(stream)), "pkv_paged_attention_decode")
 
 
 def pkv_paged_attention_main(out, q, k_pool, v_pool, block_tables, context_lens,
                              max_context_len: int, scale: float | None = None,
                              partition_size: int = 0, workspace=None, stream=None,
-                             shared_kv: bool = False, plan: Plan | None = None) -> None:
+                             shared_kv: bool = False, plan: Plan | None = None,
+                             new_key=None, new_value=None) -> None:
     """The main launch of pkv_paged_attention_decode alone (same arguments)."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                           scale, partition_size, plan, workspace, shared_kv)
+                           scale, partition_size, plan, workspace, shared_kv, new_key, new_value)
     _check(lib.pkv_paged_attention_main(*args, _stream(stream)), "pkv_paged_attention_main")
 
 

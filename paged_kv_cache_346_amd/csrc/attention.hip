@@ -55,6 +55,7 @@
 // reaches the output.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "../../include/pkv.h"
 #include "decode_config.h"
@@ -74,6 +75,8 @@ struct DecodeArgs {
   float* part_ml;    // [S, Hq, nparts, 2]
   const int* block_tables;
   const int* context_lens;
+  const void* new_k;  // [S, Hkv, D]: each sequence's token of this step, or nullptr
+  const void* new_v;
   const int4* plan;  // host-built work list {s, g, p, L} per item, or nullptr
   int S;
   int SG;            // S * Hkv: items per partition index
@@ -87,6 +90,7 @@ struct DecodeArgs {
 // item_extent() turns it into the partition index once the length is known.
 struct WorkItem {
   int s, g, p, start, end, nps;
+  bool tail;  // the item ends at the sequence's own last token (no clamping cut it)
 };
 
 // Item of this wave and its sequence length; false past the last item.
@@ -123,6 +127,7 @@ __device__ __forceinline__ bool item_ids(const DecodeArgs& a, WorkItem& it, int&
 // nothing to do (a zero-length sequence gets zero output rows).
 template <int D, int B, int G>
 __device__ __forceinline__ bool item_extent(const DecodeArgs& a, WorkItem& it, int L) {
+  const int L0 = L;
   L = min(L, a.max_blocks * B);
   const int np = L <= 0 ? 0 : min((L + a.P - 1) / a.P, a.nparts);
   int p = it.p;
@@ -140,6 +145,7 @@ __device__ __forceinline__ bool item_extent(const DecodeArgs& a, WorkItem& it, i
   it.start = p * a.P;
   it.end = min(L, it.start + a.P);
   it.nps = np;
+  it.tail = it.end == L0;
   return true;
 }
 
@@ -200,12 +206,19 @@ __device__ __forceinline__ V pool_load(const float* p) {
 // Run `compute(k, tile)` over a wave's n tiles with the loads of tile k+1 issued
 // before tile k is computed.  Two register buffers alternate; every load in the
 // steady loop is unconditional, so the compiler's wait before each compute only
-// covers the tile it needs.
-template <typename Tile, typename Load, typename Compute>
-__device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute) {
+// covers the tile it needs.  Two hooks that the steady loop never runs (so they
+// add no code to it): `first()` once the first tile's loads are issued, and
+// `last(k, tile)` in place of compute for the final tile.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <typename Tile, typename Load, typename Compute, typename First, typename Last>
+__device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute, First&& first,
+                                          Last&& last) {
   if (n <= 0) return;
   Tile ta, tb;
   load(0, ta);
+  first();
   int k = 0;
   for (; k + 2 < n; k += 2) {
     load(k + 1, tb);
@@ -216,20 +229,24 @@ __device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute)
   if (k + 1 < n) {
     load(k + 1, tb);
     compute(k, ta);
-    compute(k + 1, tb);
+    last(k + 1, tb);
   } else {
-    compute(k, ta);
+    last(k, ta);
   }
+}
+template <typename Tile, typename Load, typename Compute>
+__device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute) {
+  pipelined<Tile>(n, load, compute, NoHook{}, compute);
 }
 
 // ---------------------------------------------------------------------------
 // VALU main kernel.  E = float or uint16_t (bf16 bits).  Tile = one KV block.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int B, int G, int NW, bool NT>
+template <typename E, int D, int B, int G, int NW, bool NT, bool AP>
 __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
                                                              const E* __restrict__ q,
-                                                             const E* __restrict__ k_pool,
-                                                             const E* __restrict__ v_pool) {
+                                                             E* __restrict__ k_pool,
+                                                             E* __restrict__ v_pool) {
   constexpr int X = 16 / sizeof(E);  // elements per 16-byte vector
   constexpr int NCG = kWave / B;     // lanes sharing one token in q.k
   constexpr int NCH = D / X;         // 16-byte chunks per token
@@ -278,6 +295,41 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
   const size_t head_off = (size_t)it.g * (D * B);
   const size_t blk_stride = (size_t)a.Hkv * (D * B);
 
+  // Append (decode step with new_k/new_v): the sequence's token of this step is
+  // its last, at position L-1 in this item's final block.  The wave owning that
+  // partition loads it before its first tile, puts it into the final tile's
+  // registers in place of what the pool held there, and writes it into its slot
+  // after the tile loop (gfx9 counts stores with loads, so a store inside the
+  // loop would make every later load wait for it; nothing reads the slot back).
+  const bool appends = AP && it.tail;
+  const int tnew = it.end - 1;
+  u32x4 nk[CPL];
+  E nv[ND];
+  if (appends) {
+    const size_t row = ((size_t)it.s * a.Hkv + it.g) * D;
+    const E* kn = reinterpret_cast<const E*>(a.new_k) + row;
+    const E* vn = reinterpret_cast<const E*>(a.new_v) + row;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+      nk[j] = *reinterpret_cast<const u32x4*>(kn + (cg + NCG * j) * X);
+#pragma unroll
+    for (int k2 = 0; k2 < ND; ++k2) nv[k2] = vn[lane + kWave * k2];
+  }
+  auto write_new = [&]() {
+    if (!appends) return;
+    const int pb = tw.at(tnew / B, a.num_blocks);
+    const int off = tnew % B;
+    E* kb = k_pool + pb * blk_stride + head_off;
+    E* vb = v_pool + pb * blk_stride + head_off;
+    if (t == 0) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+        *reinterpret_cast<u32x4*>(kb + ((cg + NCG * j) * B + off) * X) = nk[j];
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < ND; ++k2) vb[(lane + kWave * k2) * B + off] = nv[k2];
+  };
+
   auto load = [&](int k, Tile& tl) {
     const int pb = tw.at(lb_first + k, a.num_blocks);
     const E* kb = k_pool + pb * blk_stride + head_off;
@@ -292,7 +344,25 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
         tl.v[tc][k2] = pool_load<NT, u32x4>(vb + (lane + kWave * k2) * B + tc * X);
   };
 
-  auto compute = [&](int k, const Tile& tl) {
+  // the final block: the appended token (its place tn in the block is
+  // wave-uniform) replaces what the pool held there
+  auto substitute = [&](int k, Tile& tl) {
+    const int tn = tnew - (lb_first + k) * B;
+    if (t == tn) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) tl.k[j] = nk[j];
+    }
+#pragma unroll
+    for (int tc = 0; tc < NVT; ++tc)
+#pragma unroll
+      for (int e = 0; e < X; ++e)
+        if (tc * X + e == tn) {
+#pragma unroll
+          for (int k2 = 0; k2 < ND; ++k2) vec_set<E>(tl.v[tc][k2], e, nv[k2]);
+        }
+  };
+
+  auto compute = [&](int k, Tile& tl) {
     const int tok0 = (lb_first + k) * B;
     const bool valid = tok0 + t < it.end;
     float pr[G];
@@ -335,7 +405,15 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
       }
   };
 
-  pipelined<Tile>(n, load, compute);
+  if constexpr (AP) {
+    pipelined<Tile>(n, load, compute, NoHook{}, [&](int k, Tile& tl) {
+      if (appends) substitute(k, tl);
+      compute(k, tl);
+    });
+    write_new();
+  } else {
+    pipelined<Tile>(n, load, compute);
+  }
 
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
@@ -366,11 +444,11 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
 //       no shuffle.  The A operand of lane (c, r) is dim 16dt + r at those
 //       tokens: two 8-byte runs of the V row (tokens 4c .. 4c+3 of each half).
 // ---------------------------------------------------------------------------
-template <int D, int B, int G, int NW, bool NT>
+template <int D, int B, int G, int NW, bool NT, bool AP>
 __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
                                                                 const uint16_t* __restrict__ q,
-                                                                const uint16_t* __restrict__ k_pool,
-                                                                const uint16_t* __restrict__ v_pool) {
+                                                                uint16_t* __restrict__ k_pool,
+                                                                uint16_t* __restrict__ v_pool) {
   constexpr int TILE = 32;
   constexpr int NJ = D / 32;   // q.k k-steps
   constexpr int NDT = D / 16;  // p.v output dim tiles
@@ -420,6 +498,48 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
   const size_t head_off = (size_t)it.g * (D * B);
   const size_t blk_stride = (size_t)a.Hkv * (D * B);
 
+  // Append (decode step with new_k/new_v): the sequence's token of this step is
+  // its last, at position L-1 in this item's final tile.  The wave owning that
+  // partition loads it before its first tile and stages it in LDS once that
+  // tile's loads are out; when the final tile arrives the staged values replace
+  // what the pool held there, and only after the tile loop does the wave write
+  // the token into its slot (gfx9 counts stores with loads, so a store inside
+  // the loop would make every later load wait for it; nothing reads the slot
+  // back).
+  __shared__ __align__(16) uint16_t s_new[kWavesPerGroup][2][D];
+  uint16_t* lds_k = s_new[threadIdx.x / kWave][0];
+  uint16_t* lds_v = s_new[threadIdx.x / kWave][1];
+  const bool appends = AP && it.tail;
+  const int tnew = it.end - 1;
+  // lanes < D/8 hold K dims 8*lane .. +7 (one chunk of the K layout); every
+  // lane holds V dims lane + 64i, so four lanes share each V line it writes
+  constexpr int NVD = D / kWave;
+  u32x4 nk = {0u, 0u, 0u, 0u};
+  uint16_t nv[NVD];
+  if (appends) {
+    const size_t row = ((size_t)it.s * a.Hkv + it.g) * D;
+    if (lane < D / 8)
+      nk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.new_k) + row +
+                                           8 * lane);
+#pragma unroll
+    for (int i = 0; i < NVD; ++i)
+      nv[i] = reinterpret_cast<const uint16_t*>(a.new_v)[row + lane + kWave * i];
+  }
+  auto stage_new = [&]() {
+    if constexpr (AP) {
+      if (appends) {
+        if (lane < D / 8) *reinterpret_cast<u32x4*>(lds_k + 8 * lane) = nk;
+#pragma unroll
+        for (int i = 0; i < NVD; ++i) lds_v[lane + kWave * i] = nv[i];
+      }
+      // other lanes of the wave read the staged token back: order the LDS
+      // writes before those reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  };
+
   auto load = [&](int k, Tile& tl) {
     const int lb0 = (t_first + k) * TILE / B;
     const int pb0 = tw.at(lb0, a.num_blocks);
@@ -438,6 +558,31 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         tl.v[th][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+    }
+  };
+
+  // put the appended token (tile-relative index tn, wave-uniform) into half TH
+  // of the final tile:
+  // lane (c, r) holds K chunks 4j + c of token 16TH + r and V dims 16dt + r of
+  // tokens 16TH + 4c .. +3
+  auto substitute = [&](Tile& tl, auto half, int tn) {
+    constexpr int TH = decltype(half)::value;
+    if (r == (tn & 15)) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) tl.k[TH][j] = *reinterpret_cast<const u32x4*>(lds_k + 8 * (4 * j + c));
+    }
+    if (c == ((tn & 15) >> 2)) {
+      const int e = tn & 3;  // element of this lane's 4-token V run
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t nv = lds_v[16 * dt + r];
+        uint32_t w = e < 2 ? tl.v[TH][dt][0] : tl.v[TH][dt][1];
+        w = (e & 1) ? ((w & 0x0000ffffu) | (nv << 16)) : ((w & 0xffff0000u) | nv);
+        if (e < 2)
+          tl.v[TH][dt][0] = w;
+        else
+          tl.v[TH][dt][1] = w;
+      }
     }
   };
 
@@ -508,7 +653,36 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
     }
   };
 
-  pipelined<Tile>(n, load, compute);
+  auto write_new = [&]() {
+    if constexpr (AP) {
+      if (appends) {
+        const int pb = tw.at(tnew / B, a.num_blocks);
+        const int off = tnew % B;
+        if (lane < D / 8)
+          *reinterpret_cast<u32x4*>(k_pool + pb * blk_stride + head_off +
+                                    ((size_t)lane * B + off) * 8) = nk;
+        uint16_t* vb = v_pool + pb * blk_stride + head_off;
+#pragma unroll
+        for (int i = 0; i < NVD; ++i) vb[(size_t)(lane + kWave * i) * B + off] = nv[i];
+      }
+    }
+  };
+
+  if constexpr (AP) {
+    pipelined<Tile>(n, load, compute, stage_new, [&](int k, Tile& tl) {
+      const int tn = tnew - (t_first + k) * TILE;  // in this tile when appending
+      if (appends) {
+        if (tn < 16)
+          substitute(tl, std::integral_constant<int, 0>{}, tn);
+        else
+          substitute(tl, std::integral_constant<int, 1>{}, tn);
+      }
+      compute(k, tl);
+    });
+    write_new();
+  } else {
+    pipelined<Tile>(n, load, compute);
+  }
 
   ls += shfl_xor_f(ls, 16);
   ls += shfl_xor_f(ls, 32);
@@ -622,20 +796,31 @@ __global__ __launch_bounds__(TPR) void pa_reduce_kernel(float* __restrict__ out,
 // Host dispatch.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int B, int G, bool NT>
-static void launch_main_nt(const DecodeArgs& a, unsigned grid, const void* q, const void* kp,
-                           const void* vp, hipStream_t st) {
+static void launch_main_nt(const DecodeArgs& a, unsigned grid, const void* q, void* kp, void* vp,
+                           hipStream_t st) {
   constexpr bool kMfma = sizeof(E) == 2 && G >= 4;
-  if constexpr (kMfma)
-    pa_mfma_kernel<D, B, G, kWavesPerGroup, NT><<<grid, kWavesPerGroup * kWave, 0, st>>>(
-        a, (const uint16_t*)q, (const uint16_t*)kp, (const uint16_t*)vp);
-  else
-    pa_valu_kernel<E, D, B, G, kWavesPerGroup, NT><<<grid, kWavesPerGroup * kWave, 0, st>>>(
-        a, (const E*)q, (const E*)kp, (const E*)vp);
+  // the append variants hold more registers and a longer epilogue; plain
+  // launches compile without them
+  if constexpr (kMfma) {
+    if (a.new_k)
+      pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, true><<<grid, kWavesPerGroup * kWave, 0, st>>>(
+          a, (const uint16_t*)q, (uint16_t*)kp, (uint16_t*)vp);
+    else
+      pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, false><<<grid, kWavesPerGroup * kWave, 0, st>>>(
+          a, (const uint16_t*)q, (uint16_t*)kp, (uint16_t*)vp);
+  } else {
+    if (a.new_k)
+      pa_valu_kernel<E, D, B, G, kWavesPerGroup, NT, true><<<grid, kWavesPerGroup * kWave, 0, st>>>(
+          a, (const E*)q, (E*)kp, (E*)vp);
+    else
+      pa_valu_kernel<E, D, B, G, kWavesPerGroup, NT, false><<<grid, kWavesPerGroup * kWave, 0, st>>>(
+          a, (const E*)q, (E*)kp, (E*)vp);
+  }
 }
 
 template <typename E, int D, int B, int G>
 static void launch_main(bool stream, const DecodeArgs& a, unsigned grid, const void* q,
-                        const void* kp, const void* vp, hipStream_t st) {
+                        void* kp, void* vp, hipStream_t st) {
   if (stream)
     launch_main_nt<E, D, B, G, true>(a, grid, q, kp, vp, st);
   else
@@ -644,7 +829,7 @@ static void launch_main(bool stream, const DecodeArgs& a, unsigned grid, const v
 
 template <typename E, int D, int B>
 static bool dispatch_g(int G, bool stream, const DecodeArgs& a, unsigned grid, const void* q,
-                       const void* kp, const void* vp, hipStream_t st) {
+                       void* kp, void* vp, hipStream_t st) {
   switch (G) {
     case 1: launch_main<E, D, B, 1>(stream, a, grid, q, kp, vp, st); return true;
     case 2: launch_main<E, D, B, 2>(stream, a, grid, q, kp, vp, st); return true;
@@ -656,7 +841,7 @@ static bool dispatch_g(int G, bool stream, const DecodeArgs& a, unsigned grid, c
 
 template <typename E, int D>
 static bool dispatch_b(int B, int G, bool stream, const DecodeArgs& a, unsigned grid,
-                       const void* q, const void* kp, const void* vp, hipStream_t st) {
+                       const void* q, void* kp, void* vp, hipStream_t st) {
   if (B == 16) return dispatch_g<E, D, 16>(G, stream, a, grid, q, kp, vp, st);
   if (B == 32) return dispatch_g<E, D, 32>(G, stream, a, grid, q, kp, vp, st);
   return false;
@@ -664,7 +849,7 @@ static bool dispatch_b(int B, int G, bool stream, const DecodeArgs& a, unsigned 
 
 template <typename E>
 static bool dispatch_d(int D, int B, int G, bool stream, const DecodeArgs& a, unsigned grid,
-                       const void* q, const void* kp, const void* vp, hipStream_t st) {
+                       const void* q, void* kp, void* vp, hipStream_t st) {
   if (D == 64) return dispatch_b<E, 64>(B, G, stream, a, grid, q, kp, vp, st);
   if (D == 128) return dispatch_b<E, 128>(B, G, stream, a, grid, q, kp, vp, st);
   return false;
@@ -693,8 +878,9 @@ static bool plan_ok(const PlanArg& pl) {
 // On PKV_OK, *a and *groups describe the main launch (groups == 0: nothing to
 // launch).
 static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, const void* q,
-                                 const void* k_pool, const void* v_pool,
-                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const void* k_pool, const void* v_pool, const void* new_key,
+                                 const void* new_value, const int32_t* block_tables,
+                                 const int32_t* context_lens,
                                  int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
                                  int32_t max_blocks, int32_t num_blocks, int32_t max_context_len,
                                  float scale, int32_t partition_size, const PlanArg& plan,
@@ -714,6 +900,8 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !block_tables || !context_lens)
     return PKV_EINVAL;
+  if ((new_key == nullptr) != (new_value == nullptr)) return PKV_EINVAL;
+  if (new_key && (!aligned16(new_key) || !aligned16(new_value))) return PKV_EINVAL;
   const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
   const int64_t nparts = num_partitions(mcl, P);
   const int64_t items = plan.ptr ? (int64_t)plan.n_items : (int64_t)S * Hkv * nparts;
@@ -722,6 +910,8 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   a->out = out;
   a->block_tables = block_tables;
   a->context_lens = context_lens;
+  a->new_k = new_key;
+  a->new_v = new_value;
   a->plan = reinterpret_cast<const int4*>(plan.ptr);
   a->S = S;
   a->SG = S * Hkv;
@@ -743,7 +933,7 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
 }
 
 static pkv_status launch_main_kernel(const DecodeArgs& a, int64_t groups, const void* q,
-                                     const void* k_pool, const void* v_pool, int D, int B, int G,
+                                     void* k_pool, void* v_pool, int D, int B, int G,
                                      pkv_dtype dtype, uint32_t flags, hipStream_t st) {
   const bool stream = (flags & PKV_ATTN_SHARED_KV) == 0;
   const bool ok =
@@ -790,15 +980,16 @@ extern "C" size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D
 }
 
 extern "C" pkv_status pkv_paged_attention_decode(
-    float* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
-    const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+    float* out, const void* q, void* k_pool, void* v_pool, const void* new_key,
+    const void* new_value, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
     int32_t partition_size, const int32_t* plan, int32_t plan_items, int32_t plan_merge,
     void* workspace, size_t workspace_bytes, pkv_dtype dtype, uint32_t flags, void* hip_stream) {
   DecodeArgs a;
   int64_t groups;
   const PlanArg pl{plan, plan_items, plan_merge};
-  pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, block_tables, context_lens,
+  pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, new_key, new_value,
+                                 block_tables, context_lens,
                                  S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
                                  partition_size, pl, workspace, workspace_bytes, dtype, flags);
   if (st != PKV_OK || groups == 0) return st;
@@ -809,15 +1000,16 @@ extern "C" pkv_status pkv_paged_attention_decode(
 }
 
 extern "C" pkv_status pkv_paged_attention_main(
-    float* out, const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
-    const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+    float* out, const void* q, void* k_pool, void* v_pool, const void* new_key,
+    const void* new_value, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
     int32_t partition_size, const int32_t* plan, int32_t plan_items, int32_t plan_merge,
     void* workspace, size_t workspace_bytes, pkv_dtype dtype, uint32_t flags, void* hip_stream) {
   DecodeArgs a;
   int64_t groups;
   const PlanArg pl{plan, plan_items, plan_merge};
-  pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, block_tables, context_lens,
+  pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, new_key, new_value,
+                                 block_tables, context_lens,
                                  S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
                                  partition_size, pl, workspace, workspace_bytes, dtype, flags);
   if (st != PKV_OK || groups == 0) return st;

@@ -31,6 +31,19 @@ __device__ __forceinline__ float vec_elem<float>(const u32x4& v, int e) {
   return __uint_as_float(v[e]);
 }
 
+// Replace element e of a 16-byte vector with the raw value x (a bit copy).
+template <typename E>
+__device__ __forceinline__ void vec_set(u32x4& v, int e, E x);
+template <>
+__device__ __forceinline__ void vec_set<uint16_t>(u32x4& v, int e, uint16_t x) {
+  const uint32_t w = v[e >> 1];
+  v[e >> 1] = (e & 1) ? ((w & 0x0000ffffu) | ((uint32_t)x << 16)) : ((w & 0xffff0000u) | x);
+}
+template <>
+__device__ __forceinline__ void vec_set<float>(u32x4& v, int e, float x) {
+  v[e] = __float_as_uint(x);
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -78,7 +78,7 @@ extern "C" pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S,
         r[0] = s;
         r[1] = g;
         r[2] = p;
-        r[3] = L[s];
+        r[3] = context_lens[s];  // as given: the kernel clamps it the same way
       }
     }
   }

@@ -9,8 +9,9 @@ Essentials"): every step
      per running request (preempting the youngest when the pool runs dry) and
      names the requests that finish;
   2. copy-on-write block copies run, then one reshape_and_cache writes the
-     prompt KV of the admitted requests and the new token of every running one;
-  3. paged attention runs over the batch's block tables (host work plan);
+     prompt KV of the admitted requests;
+  3. paged attention runs over the batch's block tables (host work plan) and
+     writes the new token of every running request into its slot as it goes;
   4. the finished requests give their blocks back.
 
 The step's metadata (slots, block tables, lengths, work plan) is packed into
@@ -99,9 +100,10 @@ class DecodeLoop:
         Hq, D] -- a view valid until the next step -- and the host context
         lengths of the batch)."""
         st = self.sched.begin_step()
-        ids, slots = st["batch"], st["slots"]
+        ids = st["batch"]
         n = len(ids)
-        # token writes: the admitted requests' prompts, then one token per request
+        # token rows: the admitted requests' prompts (written by reshape_and_cache),
+        # then one token per running request (written by the attention launch)
         pairs, write_slots = [], []
         for rid, ctx in st["admitted"]:
             if ctx:
@@ -116,7 +118,6 @@ class DecodeLoop:
             tables = np.ascontiguousarray(tables[:, :width])
             words, n_items, n_merge = attention_plan(lens, self.Hkv, self.B, width, mcl,
                                                      self.P)
-            write_slots.append(np.asarray(slots, np.int64))
             pairs.append(np.stack([np.asarray(ids, np.int64), lens.astype(np.int64) - 1], 1))
         parts = []
         if write_slots:
@@ -127,16 +128,18 @@ class DecodeLoop:
         if st["cow"]:
             copy_blocks(self.k_pool, self.v_pool,
                         torch.tensor(st["cow"], dtype=torch.int32, device=self.device))
-        if write_slots:
-            pairs = np.concatenate(pairs)
-            k, v = kv_source(pairs)
-            reshape_and_cache(k, v, self.k_pool, self.v_pool, dev[0].view(torch.int64))
         out = self.out[:n]
+        if pairs:
+            k, v = kv_source(np.concatenate(pairs))
+            if write_slots:
+                reshape_and_cache(k[:-n] if n else k, v[:-n] if n else v, self.k_pool,
+                                  self.v_pool, dev[0].view(torch.int64))
         if n:
             d_tables, d_lens, d_plan = dev[-3:]
             paged_attention_decode(out, q_source(ids), self.k_pool, self.v_pool,
                                    d_tables.view(n, -1), d_lens, mcl, partition_size=self.P,
-                                   workspace=self.ws, plan=Plan(d_plan, n_items, n_merge))
+                                   workspace=self.ws, plan=Plan(d_plan, n_items, n_merge),
+                                   new_key=k[-n:], new_value=v[-n:])
         st["stats"] = self.sched.stats()   # before the finished requests leave
         self.sched.end_step()
         return st, out, lens

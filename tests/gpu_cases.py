@@ -72,17 +72,24 @@ class Case:
         self.bm = bm
 
     # -- device path -----------------------------------------------------------
-    def run_device(self, pkv, partition_size=None, shared_kv=None, plan=False):
+    def run_device(self, pkv, partition_size=None, shared_kv=None, plan=False, append=False):
         """shared_kv None: set PKV_ATTN_SHARED_KV when the batch shares blocks
-        (the benchmark's choice); plan: run from a host work plan."""
+        (the benchmark's choice); plan: run from a host work plan; append: let
+        the attention launch write the step's tokens (one per sequence, at its
+        last position) instead of a separate reshape_and_cache."""
         c = self.w.cfg
         P = c.partition_size if partition_size is None else partition_size
         kp, vp = to_dev(self.k_pool), to_dev(self.v_pool)
         if len(self.pairs):
             pkv.copy_blocks(kp, vp, torch.from_numpy(self.pairs).cuda())
+        new_k = new_v = None
         if len(self.slots):
-            pkv.reshape_and_cache(to_dev(self.w.k_new), to_dev(self.w.v_new), kp, vp,
-                                  torch.from_numpy(self.slots).cuda())
+            if append:
+                assert list(self.w.step_ids) == list(range(c.S))
+                new_k, new_v = to_dev(self.w.k_new), to_dev(self.w.v_new)
+            else:
+                pkv.reshape_and_cache(to_dev(self.w.k_new), to_dev(self.w.v_new), kp, vp,
+                                      torch.from_numpy(self.slots).cuda())
         q = to_dev(self.w.q)
         out = torch.full((c.S, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
         mcl = int(self.lens.max())
@@ -95,7 +102,8 @@ class Case:
             pl = pkv.make_plan(self.lens, c.Hkv, c.B, self.max_blocks, mcl, P)
         pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(self.tables).cuda(),
                                    torch.from_numpy(self.lens).cuda(), mcl, partition_size=P,
-                                   workspace=ws, shared_kv=shared_kv, plan=pl)
+                                   workspace=ws, shared_kv=shared_kv, plan=pl,
+                                   new_key=new_k, new_value=new_v)
         torch.cuda.synchronize()
         return out.cpu().numpy(), kp, vp
 

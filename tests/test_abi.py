@@ -42,33 +42,38 @@ def test_single_hip_runtime_in_process(pkv):
 def test_host_validation_rejects_before_launch(pkv):
     lib = pkv.lib
     fake = ctypes.c_void_p(4096)            # never dereferenced: every call below fails validation
+    odd = ctypes.c_void_p(4098)
     tbl = ctypes.c_void_p(4096)
     # unsupported head dim / block size / group size
     for D, B, Hq, Hkv in ((96, 16, 8, 8), (128, 8, 8, 8), (128, 16, 24, 8)):
-        st = lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, Hq, Hkv, D, B, 4,
+        st = lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, Hq, Hkv, D, B, 4,
                                             8, 16, 0.1, 0, None, 0, 0, None, 0, pkv.PKV_BF16, 0, None)
         assert st == pkv.PKV_EUNSUPPORTED
     # Hq not a multiple of Hkv, bad partition size, misaligned pointer, bad dtype
-    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 6, 4, 128, 16, 4,
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 6, 4, 128, 16, 4,
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
-    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 4,
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 48, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
     # a partition may span at most 64 blocks (2048 tokens = 128 blocks of 16)
-    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 4,
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 2048, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
-    odd = ctypes.c_void_p(4098)
-    assert lib.pkv_paged_attention_decode(odd, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 4,
+    assert lib.pkv_paged_attention_decode(odd, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
-    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 4,
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 7, 0, None) == pkv.PKV_EINVAL
     # unknown flag bits
-    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 4,
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 2, None) == pkv.PKV_EINVAL
+    # the step's new token needs both rows, 16-byte aligned
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, fake, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, fake, odd, tbl, tbl, 1, 8, 8, 128, 16, 4,
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
     # long contexts need a workspace
-    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, tbl, tbl, 1, 8, 8, 128, 16, 64,
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 64,
                                           128, 1024, 0.1, 512, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
     # empty batches are a no-op success
-    assert lib.pkv_paged_attention_decode(None, None, None, None, None, None, 0, 8, 8, 128, 16, 4,
+    assert lib.pkv_paged_attention_decode(None, None, None, None, None, None, None, None, 0, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_OK
     assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 8, 1,
                                      None) == pkv.PKV_OK

@@ -82,6 +82,25 @@ def test_plan_matches_unplanned(pkv, dtype, G, D, B, P):
     check_attention(b, case.oracle_out(case.k_pool, case.v_pool, rows), dtype, rows)
 
 
+@pytest.mark.parametrize("dtype,G,D,B,P", KERNEL_CASES)
+def test_append_matches_separate_cache_write(pkv, dtype, G, D, B, P):
+    """A decode step that lets the attention launch write each sequence's new
+    token gives the same pools and the same output, bit for bit, as
+    reshape_and_cache followed by attention."""
+    Hkv = 2
+    cfg = ragged(f"append_{dtype}_G{G}_D{D}_B{B}_P{P}", 500 + G + D + B, RAGGED_LENS, Hkv * G,
+                 Hkv, D, B, dtype, P)
+    say(f"case {cfg.name}")
+    case = Case(pkv, W.make(cfg))
+    a, ka, va = case.run_device(pkv, plan=True)
+    b, kb, vb = case.run_device(pkv, plan=True, append=True)
+    assert np.array_equal(to_host_bits(ka).view(np.uint8), to_host_bits(kb).view(np.uint8))
+    assert np.array_equal(to_host_bits(va).view(np.uint8), to_host_bits(vb).view(np.uint8))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c, _, _ = case.run_device(pkv, plan=False, append=True)
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
 def test_tiny_mha_config(pkv):
     """Four sequences of 1, 15, 16 and 70 tokens, fp32, with the step's
     reshape_and_cache of 4 new tokens at positions 0, 14, 15 and 69."""
@@ -151,12 +170,13 @@ def _sample_rows(case, n, seed):
                                   "opt13b_mha", "long70b_b16", "long70b_b32"])
 def test_full_config(pkv, name):
     """Full-size workload in the benchmark's launch configuration (host work
-    plan, load policy from the batch's sharing): whole pools compared bit for bit
-    after the step's cache writes, attention compared on sampled rows (the
-    longest and shortest sequences included)."""
+    plan, load policy from the batch's sharing, the step's tokens written by the
+    attention launch): whole pools compared bit for bit after the step's cache
+    writes, attention compared on sampled rows (the longest and shortest
+    sequences included)."""
     say(f"case {name} (full size)")
     case = Case(pkv, W.make(name))
-    got, kp, vp = case.run_device(pkv, plan=True)
+    got, kp, vp = case.run_device(pkv, plan=True, append=len(case.slots) > 0)
     say("  device done")
     assert np.isfinite(got).all()
     if len(case.slots) or len(case.pairs):

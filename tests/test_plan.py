@@ -10,13 +10,13 @@ def expected_items(lens, Hkv, B, max_blocks, mcl, P):
     cap = max_blocks * B
     nparts = max(1, -(-min(mcl, cap) // P))
     items, merge = {}, []
-    for s, L in enumerate(lens):
-        L = min(int(L), cap)
+    for s, L0 in enumerate(lens):
+        L = min(int(L0), cap)
         n = 0 if L <= 0 else min(-(-L // P), nparts)
         for p in range(max(n, 1)):
             size = 0 if L <= 0 else min(P, L - p * P)
             for g in range(Hkv):
-                items[(s, g, p)] = (L, size)
+                items[(s, g, p)] = (int(L0), size)   # the length as given
         if n > 1:
             merge += [s * Hkv + g for g in range(Hkv)]
     return items, merge
