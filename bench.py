@@ -321,7 +321,7 @@ def run_serve(args, torch, np):
             batch_sum += n
             preempted += len(st["preempted"])
             prefill += sum(c for _, c in st["admitted"])
-            held, committed, _, _ = st["stats"]
+            held, committed = st["stats"][:2]
             if n:
                 util_sum += held / max(committed, 1)
         torch.cuda.synchronize()

@@ -158,13 +158,52 @@ pkv_status pkv_bm_count_shared(const pkv_bm* bm, const int64_t* seq_ids, int32_t
 pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_queue,
                            int32_t* n_free);
 
+/* Swapping ([ZENO] "The Core Idea", OS-paging analogy table, "Swapping": KV
+ * blocks go to CPU memory; [ZENO] "Implementation Essentials": preemption
+ * swaps a request's blocks to the CPU).  Semantics fixed by this library where
+ * the pages are silent:
+ *   - a host pool of num_host_blocks blocks with the device pool's geometry,
+ *     set once (PKV_EINVAL on a second call or a size <= 0); its free blocks
+ *     form a FIFO queue, initially ascending;
+ *   - swap_out moves a resident sequence to the host: walking its table from
+ *     logical block 0 it takes one host block per entry and writes the pair
+ *     (device block, host block) into pairs[2i], pairs[2i+1]; then it releases
+ *     its device blocks as free_seq does.  A block it shares keeps its other
+ *     references on the device; the host copy is private;
+ *   - swap_in brings a swapped sequence back: one new device block per host
+ *     block, in table order, pairs (host block, device block); then the host
+ *     blocks return to the host free queue in table order;
+ *   - both are all-or-nothing: PKV_ENOBLOCKS when the destination side has
+ *     fewer free blocks than the table has entries, PKV_EINVAL when `cap`
+ *     (pairs, i.e. 2*cap int32 entries) is too small, PKV_ENOSEQ for an unknown
+ *     id, PKV_EINVAL for the wrong side (swap_out of a swapped sequence, swap_in
+ *     of a resident one); a failing call changes nothing;
+ *   - a swapped sequence keeps its id and length (pkv_bm_seq_info works) and
+ *     can be freed (its host blocks return to the host queue); append_slot(s),
+ *     fork (as parent), block_table, slots, fill_batch and count_shared give
+ *     PKV_EINVAL for it.
+ * The caller copies the data (pkv_swap_blocks): swap-out pairs before any
+ * write to the released device blocks, swap-in pairs before the sequence's
+ * blocks are read or written on the device. */
+pkv_status pkv_bm_set_host_pool(pkv_bm* bm, int32_t num_host_blocks);
+pkv_status pkv_bm_num_free_host(const pkv_bm* bm, int32_t* out);
+pkv_status pkv_bm_is_swapped(const pkv_bm* bm, int64_t seq_id, int32_t* out);
+pkv_status pkv_bm_swap_out(pkv_bm* bm, int64_t seq_id, int32_t* pairs, int32_t cap,
+                           int32_t* n_pairs);
+pkv_status pkv_bm_swap_in(pkv_bm* bm, int64_t seq_id, int32_t* pairs, int32_t cap,
+                          int32_t* n_pairs);
+/* The host free queue front to back in free_queue[0 .. *n_free) (room for
+ * num_host_blocks entries; free_queue may be NULL before a host pool is set). */
+pkv_status pkv_bm_host_snapshot(const pkv_bm* bm, int32_t* free_queue, int32_t* n_free);
+
 /* ---------------------------------------------------------------------------
  * Continuous batching scheduler ([RTI] "Batch by step, not by request": the
  * batch is rebuilt after every decode step, finished sequences leave and
  * waiting ones join, and with paging a newcomer needs only free blocks;
  * [ZENO] "Continuous Batching" figure: A finishes, A dequeues, D enqueues, the
  * batch becomes {B, C, D}; [ZENO] "Implementation Essentials": under memory
- * pressure a request's blocks are dropped and its KV recomputed later).
+ * pressure a request's blocks are swapped to CPU memory, or dropped and its KV
+ * recomputed later).
  *
  * A host-side driver over one block manager (which it does not own; the
  * manager must outlive it and take no other sequence ids meanwhile).  Policy
@@ -174,7 +213,7 @@ pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_q
  *   - paged policy: admission allocates blocks for the request's context (its
  *     prompt plus tokens generated before any preemption), whose KV the caller
  *     then writes (prefill);
- *   - reserve policy (reserve_max != 0): a simulation of the max-length
+ *   - reserve policy (PKV_SCHED_RESERVE_MAX): a simulation of the max-length
  *     reservation of the systems before paging ([ZENO] "Background and
  *     Motivation"): a request is admitted only if the blocks not yet reserved
  *     cover ceil((prompt + max_new) / B); they stay reserved until it finishes;
@@ -183,14 +222,32 @@ pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_q
  *   - when an append finds no free block, the most recently admitted running
  *     request is preempted: its blocks are freed, it returns to the front of
  *     the waiting queue keeping its generated tokens, and the append is retried;
+ *   - swap policy (PKV_SCHED_SWAP; the block manager needs a host pool): a
+ *     preempted request that holds KV (not admitted in this same step, whose
+ *     prefill is not written yet) is swapped out (pkv_bm_swap_out) when the
+ *     host has a block for each of its blocks, and goes to the front of a
+ *     swapped queue; otherwise it is dropped as above.  Each step first swaps
+ *     requests back in from the front of that queue (pkv_bm_swap_in) while
+ *     fewer than max_running run and the device has room, no skipping ahead;
+ *     a resumed request rejoins the running list at its end.  No waiting
+ *     request is admitted while any request is swapped out.  The caller runs a
+ *     step's copies in this order: swap_in_pairs (host to device), then
+ *     swap_out_pairs (device to host; they may reuse host blocks the swap-ins
+ *     released), then cow_pairs, then the prefill writes, then the token
+ *     writes and attention;
  *   - a request finishes in the step that produces its max_new-th token and is
  *     freed by pkv_sched_end_step, after the caller has read the step's tables.
  * Not thread-safe; one scheduler thread owns a handle.
  * ------------------------------------------------------------------------- */
 typedef struct pkv_sched pkv_sched;
 
+enum { PKV_SCHED_RESERVE_MAX = 1, PKV_SCHED_SWAP = 2 };
+
 /* Caller-owned host arrays one step fills; each holds `capacity` entries
- * (>= max_running), cow_pairs 2*capacity. */
+ * (>= max_running), cow_pairs 2*capacity.  Under the swap policy the two pair
+ * arrays hold 2*pair_capacity entries (pair_capacity >= the pool's
+ * num_blocks) and the id arrays `capacity`; otherwise they may be NULL and
+ * their counts are 0. */
 typedef struct pkv_sched_step {
   int32_t capacity;
   int64_t* batch_ids;      /* running requests after the step, admission order */
@@ -205,9 +262,20 @@ typedef struct pkv_sched_step {
   int32_t n_preempted;
   int64_t* finished_ids;   /* produced their last token this step */
   int32_t n_finished;
+  int32_t pair_capacity;
+  int32_t* swap_in_pairs;   /* (host block, device block) copies, run first */
+  int32_t n_swap_in;
+  int32_t* swap_out_pairs;  /* (device block, host block) copies, run second */
+  int32_t n_swap_out;
+  int64_t* swapped_in_ids;  /* resumed from the host this step */
+  int32_t n_swapped_in;
+  int64_t* swapped_out_ids; /* swapped out this step (not in preempted_ids) */
+  int32_t n_swapped_out;
 } pkv_sched_step;
 
-pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t reserve_max,
+/* policy: 0 (paged, preempt by dropping), PKV_SCHED_RESERVE_MAX, or
+ * PKV_SCHED_SWAP; PKV_EINVAL for unknown bits or both. */
+pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t policy,
                             pkv_sched** out);
 void pkv_sched_destroy(pkv_sched* sched);
 /* Queue a request; PKV_EEXIST for a known id, PKV_EINVAL when prompt_len < 0,
@@ -220,10 +288,11 @@ pkv_status pkv_sched_begin_step(pkv_sched* sched, pkv_sched_step* out);
 /* Free the requests that finished in the step. */
 pkv_status pkv_sched_end_step(pkv_sched* sched);
 /* Tokens the running requests hold, slots the policy keeps for them (allocated
- * blocks, or reserved blocks under the reserve policy, times B), queue sizes. */
+ * device blocks, or reserved blocks under the reserve policy, times B), and the
+ * sizes of the waiting, running and swapped-out sets. */
 pkv_status pkv_sched_stats(const pkv_sched* sched, int64_t* tokens_held,
                            int64_t* slots_committed, int32_t* n_waiting,
-                           int32_t* n_running);
+                           int32_t* n_running, int32_t* n_swapped);
 
 /* ---------------------------------------------------------------------------
  * Device operations.
@@ -252,6 +321,27 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_poo
 pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n,
                            int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
                            pkv_dtype dtype, void* hip_stream);
+
+/* Block copies between two pools of the same geometry, one of which is usually
+ * a host pool ([ZENO] "The Core Idea", OS-paging analogy table, "Swapping": KV
+ * blocks moved to CPU memory and back; [ZENO] "Implementation Essentials").
+ * For each pair k, dst block pairs[2k+1] := src block pairs[2k], K and V, all
+ * heads and slots; a bit copy.
+ *   dst_k, dst_v, dst_blocks   destination pools and their block count
+ *   src_k, src_v, src_blocks   source pools and their block count
+ *     Each pool is device memory or pinned host memory (hipHostMalloc, or a
+ *     pinned torch tensor) that the GPU reaches through its device mapping; the
+ *     GPU reads or writes host pools over the host link.  Pageable host memory
+ *     is rejected with PKV_EINVAL before any launch.  16-byte aligned.
+ *   pairs  device int32 [n, 2] (src block, dst block); a pair with an id
+ *          outside its pool is skipped; dst ids must be distinct.
+ * Stream-ordered like every device call: a swap-out (device to host) must be
+ * enqueued before any write to its released device blocks, a swap-in before
+ * the blocks are read; a host pool read by the CPU needs the stream synced. */
+pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_blocks, const void* src_k,
+                           const void* src_v, int32_t src_blocks, const int32_t* pairs,
+                           int32_t n, int32_t Hkv, int32_t D, int32_t B, pkv_dtype dtype,
+                           void* hip_stream);
 
 /* Bytes of workspace pkv_paged_attention_decode needs: 0 when every sequence
  * fits one partition, else S*Hq*nparts*(D+2)*4 with

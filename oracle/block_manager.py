@@ -29,6 +29,23 @@ Readings where the pages are silent:
     written in place;
   * add_seq(n) is all-or-nothing: it fails with no change when fewer than
     ceil(n/B) blocks are free; every failing call leaves the state unchanged.
+
+Swapping ("The Core Idea", OS-paging analogy table, "Swapping": KV blocks go
+to CPU memory; "Implementation Essentials": preemption swaps a request's
+blocks to the CPU).  Readings where the pages are silent:
+  * a host pool of blocks with the device pool's geometry, set once; its free
+    blocks form a FIFO queue, initially ascending;
+  * swap_out(s) moves a resident sequence to the host: walking its table from
+    logical block 0 it takes one host block per table entry (pairs (device
+    block, host block) for the copy), then releases its device blocks as
+    free_seq does.  A block the sequence shares keeps its other references on
+    the device; the host copy is private to the swapped sequence;
+  * swap_in(s) brings it back: one new device block per host block, in table
+    order (pairs (host block, device block)), then the host blocks return to
+    the host free queue in table order;
+  * both are all-or-nothing (too few free blocks on the destination side:
+    ENOBLOCKS, no change); a swapped sequence cannot be appended to, forked or
+    batched (EINVAL) but can be freed, and keeps its length.
 """
 from __future__ import annotations
 
@@ -56,6 +73,9 @@ class BlockManager:
         self.free = deque(order)
         self.tables = {}   # seq id -> list of physical block ids
         self.lens = {}     # seq id -> tokens held
+        self.NH = 0                  # host pool blocks
+        self.host_free = deque()
+        self.host_tables = {}        # swapped seq id -> list of host block ids
 
     # -- queries -------------------------------------------------------------
     def num_free(self) -> int:
@@ -67,14 +87,31 @@ class BlockManager:
         return self.ref[block]
 
     def seq_info(self, sid: int):
-        if sid not in self.tables:
+        if not self._known(sid):
             raise BMError(ENOSEQ)
-        return self.lens[sid], len(self.tables[sid])
+        t = self.tables[sid] if sid in self.tables else self.host_tables[sid]
+        return self.lens[sid], len(t)
 
     def block_table(self, sid: int):
+        self._resident(sid)
+        return list(self.tables[sid])
+
+    def _resident(self, sid: int) -> None:
+        if sid in self.host_tables:
+            raise BMError(EINVAL, "sequence is swapped out")
         if sid not in self.tables:
             raise BMError(ENOSEQ)
-        return list(self.tables[sid])
+
+    def _known(self, sid: int) -> bool:
+        return sid in self.tables or sid in self.host_tables
+
+    def is_swapped(self, sid: int) -> bool:
+        if not self._known(sid):
+            raise BMError(ENOSEQ)
+        return sid in self.host_tables
+
+    def num_free_host(self) -> int:
+        return len(self.host_free)
 
     def snapshot(self):
         return list(self.ref), list(self.free)
@@ -88,7 +125,7 @@ class BlockManager:
     def add_seq(self, sid: int, num_tokens: int) -> None:
         if num_tokens < 0:
             raise BMError(EINVAL, "negative length")
-        if sid in self.tables:
+        if self._known(sid):
             raise BMError(EEXIST)
         need = -(-num_tokens // self.B)
         if need > len(self.free):
@@ -99,8 +136,7 @@ class BlockManager:
     def append_slot(self, sid: int):
         """Reserve the slot for the sequence's next token.  Returns
         (slot, cow_src, cow_dst); cow_src = cow_dst = -1 when no copy is due."""
-        if sid not in self.tables:
-            raise BMError(ENOSEQ)
+        self._resident(sid)
         table, L, B = self.tables[sid], self.lens[sid], self.B
         src = dst = -1
         if L % B == 0:
@@ -121,9 +157,8 @@ class BlockManager:
         return slot, src, dst
 
     def fork(self, parent: int, child: int) -> None:
-        if parent not in self.tables:
-            raise BMError(ENOSEQ)
-        if child in self.tables:
+        self._resident(parent)
+        if self._known(child):
             raise BMError(EEXIST)
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
@@ -131,20 +166,61 @@ class BlockManager:
             self.ref[b] += 1
 
     def free_seq(self, sid: int) -> None:
+        if sid in self.host_tables:
+            self.host_free.extend(self.host_tables.pop(sid))
+            del self.lens[sid]
+            return
         if sid not in self.tables:
             raise BMError(ENOSEQ)
-        for b in self.tables.pop(sid):
+        self._release(self.tables.pop(sid))
+        del self.lens[sid]
+
+    def _release(self, table) -> None:
+        for b in table:
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
-        del self.lens[sid]
+
+    # -- swapping ------------------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int) -> None:
+        if num_host_blocks <= 0 or self.NH:
+            raise BMError(EINVAL, "host pool is set once, with a positive size")
+        self.NH = num_host_blocks
+        self.host_free = deque(range(num_host_blocks))
+
+    def swap_out(self, sid: int):
+        """Move a resident sequence to host blocks; returns the (device block,
+        host block) copies, in table order, to run before any write to the
+        released device blocks."""
+        self._resident(sid)
+        table = self.tables[sid]
+        if len(table) > len(self.host_free):
+            raise BMError(ENOBLOCKS)
+        host = [self.host_free.popleft() for _ in table]
+        self._release(table)
+        del self.tables[sid]
+        self.host_tables[sid] = host
+        return list(zip(table, host))
+
+    def swap_in(self, sid: int):
+        """Bring a swapped sequence back into new device blocks; returns the
+        (host block, device block) copies, in table order."""
+        if sid not in self.host_tables:
+            raise BMError(EINVAL if sid in self.tables else ENOSEQ)
+        host = self.host_tables[sid]
+        if len(host) > len(self.free):
+            raise BMError(ENOBLOCKS)
+        table = [self._take() for _ in host]
+        self.host_free.extend(host)
+        del self.host_tables[sid]
+        self.tables[sid] = table
+        return list(zip(host, table))
 
     def fill_batch(self, sids, max_blocks: int):
         """Block tables [n, max_blocks] (padded with -1) and context lengths."""
         tables, lens = [], []
         for sid in sids:
-            if sid not in self.tables:
-                raise BMError(ENOSEQ)
+            self._resident(sid)
             t = self.tables[sid]
             if len(t) > max_blocks:
                 raise BMError(EINVAL, "table longer than max_blocks")
@@ -156,8 +232,7 @@ class BlockManager:
 def slots(bm, sid, start: int, count: int):
     """Slots of tokens [start, start+count) of a sequence: token t lives in
     logical block t // B at offset t % B ("Pages, from operating systems")."""
-    if sid not in bm.tables:
-        raise BMError(ENOSEQ)
+    bm._resident(sid)
     if start < 0 or count < 0 or start + count > bm.lens[sid]:
         raise BMError(EINVAL, "tokens past the sequence's length")
     t = bm.tables[sid]
@@ -170,15 +245,15 @@ def count_shared(bm, seq_ids) -> int:
     systems"): the batch reads such a block once per sharer."""
     total = 0
     for sid in seq_ids:
-        if sid not in bm.tables:
-            raise BMError(ENOSEQ)
+        bm._resident(sid)
         total += sum(1 for b in bm.tables[sid] if bm.ref[b] > 1)
     return total
 
 
 def run_ops(bm, ops):
     """Apply a request script (see workloads.script / random_script).  Returns
-    the status code of every op and the (slot, src, dst) of every append."""
+    the status code of every op, and the (slot, src, dst) of every append and
+    the tuple of copy pairs of every swap, in op order."""
     codes, appends = [], []
     for op in ops:
         kind = op[0]
@@ -194,6 +269,10 @@ def run_ops(bm, ops):
                     appends.append(bm.append_slot(op[1]))
             elif kind == "free":
                 bm.free_seq(op[1])
+            elif kind == "swap_out":
+                appends.append(tuple(bm.swap_out(op[1])))
+            elif kind == "swap_in":
+                appends.append(tuple(bm.swap_in(op[1])))
             else:
                 raise ValueError(kind)
             codes.append(OK)

@@ -11,9 +11,9 @@ From the pages:
     batch {B, C, D});
   * with paging a new request only needs free blocks, not a large contiguous
     region (same section of the first page);
-  * under memory pressure a running request is preempted: its blocks are dropped
-    and its KV recomputed later ("Implementation Essentials", block manager;
-    OS-paging analogy table, "Swapping");
+  * under memory pressure a running request is preempted: its blocks are swapped
+    to CPU memory, or dropped and its KV recomputed later ("Implementation
+    Essentials", block manager; OS-paging analogy table, "Swapping");
   * the systems before paging reserved a region per request for its maximum
     length ("Background and Motivation").
 
@@ -39,6 +39,23 @@ Readings where the pages are silent:
     is submitted;
   * begin_step() and end_step() alternate; calling either out of turn is an
     error.
+
+Swap policy (swap=True, over a block manager with a host pool):
+  * the preempted request's blocks move to the host (block manager swap_out)
+    when the host has a block for each of them; otherwise it is dropped and
+    recomputed as above.  A request admitted in the same step holds no KV yet
+    (its prefill is written after scheduling), so it is always dropped;
+  * swapped requests wait in their own queue, the most recently preempted
+    behind the others as for dropped ones (each victim goes to the front);
+  * each step first swaps requests back in from the front of that queue while
+    fewer than max_running run and the device has a block for each of their
+    blocks (no skipping ahead); a resumed request rejoins the running list at
+    its end, keeping its tokens;
+  * no waiting request is admitted while any request is still swapped out;
+  * the caller runs a step's copies in this order: swap-ins (host to device),
+    swap-outs (device to host: they may reuse host blocks the swap-ins just
+    released), copy-on-write copies, prefill writes, then the token writes and
+    attention.
 """
 from __future__ import annotations
 
@@ -63,12 +80,16 @@ class Request:
 
 
 class Scheduler:
-    def __init__(self, bm, max_running: int, reserve_max: bool = False):
+    def __init__(self, bm, max_running: int, reserve_max: bool = False, swap: bool = False):
         if max_running <= 0:
             raise BMError(EINVAL, "max_running must be positive")
+        if reserve_max and swap:
+            raise BMError(EINVAL, "the reserve policy never preempts")
         self.bm = bm
         self.max_running = max_running
         self.reserve_max = reserve_max
+        self.swap = swap
+        self.swapped: deque[Request] = deque()
         self.waiting: deque[Request] = deque()
         self.running: list[Request] = []
         self.known: set[int] = set()
@@ -90,14 +111,28 @@ class Scheduler:
         self.waiting.append(Request(rid, prompt, max_new))
 
     def begin_step(self):
-        """One iteration: admissions, then one slot per running request.
-        Returns dict(batch, slots, cow, admitted=[(rid, ctx)], preempted,
-        finished)."""
+        """One iteration: swap-ins, admissions, then one slot per running
+        request.  Returns dict(batch, slots, cow, admitted=[(rid, ctx)],
+        preempted (dropped), finished, swap_in=[(host, device)],
+        swap_out=[(device, host)], swapped_in, swapped_out)."""
         if self.in_step:
             raise BMError(EINVAL, "end_step() was not called")
         self.in_step = True
+        swap_in, swapped_in = [], []
+        while self.swapped and len(self.running) < self.max_running:
+            r = self.swapped[0]
+            try:
+                swap_in += self.bm.swap_in(r.rid)
+            except BMError as e:
+                if e.code == ENOBLOCKS:
+                    break
+                raise
+            self.swapped.popleft()
+            self.running.append(r)
+            swapped_in.append(r.rid)
+
         admitted: list[tuple[Request, int]] = []   # (request, context it was admitted with)
-        while self.waiting and len(self.running) < self.max_running:
+        while self._may_admit() and self.waiting and len(self.running) < self.max_running:
             r = self.waiting[0]
             need_max = self._blocks(r.prompt + r.max_new)
             if self.reserve_max and self.reserved + need_max > self.bm.N:
@@ -115,7 +150,7 @@ class Scheduler:
             self.running.append(r)
             admitted.append((r, r.ctx))
 
-        slots, cow, preempted = [], [], []
+        slots, cow, preempted, swap_out, swapped_out = [], [], [], [], []
         i = 0
         while i < len(self.running):
             r = self.running[i]
@@ -124,7 +159,13 @@ class Scheduler:
             except BMError as e:
                 if e.code != ENOBLOCKS:
                     raise
-                victim = self.running.pop()
+                victim = self._victim()
+                fresh = any(a is victim for a, _ in admitted)
+                if self._swap_victim(victim, fresh):
+                    swap_out += self.bm.swap_out(victim.rid)
+                    swapped_out.append(victim.rid)
+                    self.swapped.appendleft(victim)
+                    continue
                 self.bm.free_seq(victim.rid)
                 admitted = [(a, n) for a, n in admitted if a is not victim]
                 preempted.append(victim.rid)
@@ -148,7 +189,26 @@ class Scheduler:
             "admitted": [(r.rid, n) for r, n in admitted],
             "preempted": preempted,
             "finished": finished,
+            "swap_in": swap_in,
+            "swap_out": swap_out,
+            "swapped_in": swapped_in,
+            "swapped_out": swapped_out,
         }
+
+    # -- policy decisions ----------------------------------------------------------
+    def _victim(self) -> Request:
+        """The preempted request: the most recently admitted one."""
+        return self.running.pop()
+
+    def _may_admit(self) -> bool:
+        """New requests wait while any preempted one is still swapped out."""
+        return not self.swapped
+
+    def _swap_victim(self, victim: Request, fresh: bool) -> bool:
+        """Swap (rather than drop) a victim that holds KV, when the host has a
+        block for each of its blocks."""
+        return self.swap and not fresh and \
+            self.bm.seq_info(victim.rid)[1] <= self.bm.num_free_host()
 
     def end_step(self) -> None:
         """Free the requests that finished in the step."""
@@ -173,4 +233,4 @@ class Scheduler:
         return (self.bm.N - self.bm.num_free()) * self.bm.B
 
     def idle(self) -> bool:
-        return not self.waiting and not self.running
+        return not self.waiting and not self.running and not self.swapped

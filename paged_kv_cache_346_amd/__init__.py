@@ -19,6 +19,7 @@ import torch  # imported before the library so both share torch's HIP runtime
 
 __all__ = [
     "PkvError", "BlockManager", "Scheduler", "pkv_reshape_and_cache", "pkv_copy_blocks",
+    "pkv_swap_blocks", "swap_blocks",
     "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pkv_paged_attention_main",
     "pkv_paged_attention_reduce", "pool_shapes", "paged_attention_main", "paged_attention_reduce",
     "pkv_attention_plan", "pkv_attention_plan_words", "attention_plan", "attention_plan_words",
@@ -33,6 +34,7 @@ PKV_OK, PKV_EINVAL, PKV_ENOBLOCKS, PKV_ENOSEQ, PKV_EEXIST, PKV_EUNSUPPORTED, PKV
     0, -1, -2, -3, -4, -5, -6)
 PKV_F32, PKV_BF16 = 0, 1
 PKV_ATTN_SHARED_KV = 1
+PKV_SCHED_RESERVE_MAX, PKV_SCHED_SWAP = 1, 2
 
 _i32, _i64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
                               ctypes.c_size_t)
@@ -53,7 +55,16 @@ class _SchedStep(ctypes.Structure):
                 ("preempted_ids", ctypes.POINTER(ctypes.c_int64)),
                 ("n_preempted", ctypes.c_int32),
                 ("finished_ids", ctypes.POINTER(ctypes.c_int64)),
-                ("n_finished", ctypes.c_int32)]
+                ("n_finished", ctypes.c_int32),
+                ("pair_capacity", ctypes.c_int32),
+                ("swap_in_pairs", ctypes.POINTER(ctypes.c_int32)),
+                ("n_swap_in", ctypes.c_int32),
+                ("swap_out_pairs", ctypes.POINTER(ctypes.c_int32)),
+                ("n_swap_out", ctypes.c_int32),
+                ("swapped_in_ids", ctypes.POINTER(ctypes.c_int64)),
+                ("n_swapped_in", ctypes.c_int32),
+                ("swapped_out_ids", ctypes.POINTER(ctypes.c_int64)),
+                ("n_swapped_out", ctypes.c_int32)]
 
 
 # name -> (restype, argtypes); mirrors include/pkv.h
@@ -73,17 +84,25 @@ SIGNATURES = {
     "pkv_sched_add_request": (_i32, [_vp, _i64, _i32, _i32]),
     "pkv_sched_begin_step": (_i32, [_vp, ctypes.POINTER(_SchedStep)]),
     "pkv_sched_end_step": (_i32, [_vp]),
-    "pkv_sched_stats": (_i32, [_vp, _pi64, _pi64, _pi32, _pi32]),
+    "pkv_sched_stats": (_i32, [_vp, _pi64, _pi64, _pi32, _pi32, _pi32]),
     "pkv_bm_refcount": (_i32, [_vp, _i32, _pi32]),
     "pkv_bm_seq_info": (_i32, [_vp, _i64, _pi32, _pi32]),
     "pkv_bm_block_table": (_i32, [_vp, _i64, _pi32, _i32]),
     "pkv_bm_fill_batch": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
     "pkv_bm_snapshot": (_i32, [_vp, _pi32, _pi32, _pi32]),
+    "pkv_bm_set_host_pool": (_i32, [_vp, _i32]),
+    "pkv_bm_num_free_host": (_i32, [_vp, _pi32]),
+    "pkv_bm_is_swapped": (_i32, [_vp, _i64, _pi32]),
+    "pkv_bm_swap_out": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pkv_bm_swap_in": (_i32, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pkv_bm_host_snapshot": (_i32, [_vp, _pi32, _pi32]),
     "pkv_bm_count_shared": (_i32, [_vp, _pi64, _i32, _pi64]),
     "pkv_bm_slots": (_i32, [_vp, _i64, _i32, _i32, _pi64]),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_swap_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                               _i32, _vp]),
     "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_attention_plan_words": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_attention_plan": (_i32, [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _sz, _pi32,
@@ -250,19 +269,65 @@ class BlockManager:
                "pkv_bm_snapshot")
         return ref.tolist(), fq[:nf.value].tolist()
 
+    # -- swapping (host pool) ------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int) -> None:
+        _check(lib.pkv_bm_set_host_pool(self._h, num_host_blocks), "pkv_bm_set_host_pool")
+        self.num_host_blocks = int(num_host_blocks)
+
+    def num_free_host(self) -> int:
+        out = _i32()
+        _check(lib.pkv_bm_num_free_host(self._h, ctypes.byref(out)), "pkv_bm_num_free_host")
+        return out.value
+
+    def is_swapped(self, seq_id: int) -> bool:
+        out = _i32()
+        _check(lib.pkv_bm_is_swapped(self._h, seq_id, ctypes.byref(out)), "pkv_bm_is_swapped")
+        return bool(out.value)
+
+    def _swap(self, fn, name, seq_id):
+        _, nb = self.seq_info(seq_id)
+        pairs = np.empty((max(nb, 1), 2), np.int32)
+        n = _i32()
+        _check(fn(self._h, seq_id, _np_ptr(pairs, ctypes.c_int32), nb, ctypes.byref(n)), name)
+        return pairs[:n.value].copy()
+
+    def swap_out(self, seq_id: int) -> np.ndarray:
+        """(device block, host block) pairs int32 [n, 2], table order."""
+        return self._swap(lib.pkv_bm_swap_out, "pkv_bm_swap_out", seq_id)
+
+    def swap_in(self, seq_id: int) -> np.ndarray:
+        """(host block, device block) pairs int32 [n, 2], table order."""
+        return self._swap(lib.pkv_bm_swap_in, "pkv_bm_swap_in", seq_id)
+
+    def host_free_queue(self):
+        cap = getattr(self, "num_host_blocks", 0)
+        fq = np.empty(max(cap, 1), np.int32)
+        nf = _i32()
+        _check(lib.pkv_bm_host_snapshot(self._h, _np_ptr(fq, ctypes.c_int32), ctypes.byref(nf)),
+               "pkv_bm_host_snapshot")
+        return fq[:nf.value].tolist()
+
 
 class Scheduler:
     """Owner of a pkv_sched handle: continuous batching over a BlockManager
     (which must outlive it).  begin_step() returns the step as a dict with the
     same keys as the reference scheduler: batch, slots, cow, admitted
-    [(id, ctx)], preempted, finished."""
+    [(id, ctx)], preempted, finished, swap_in [(host, device)], swap_out
+    [(device, host)], swapped_in, swapped_out."""
 
-    def __init__(self, bm: BlockManager, max_running: int, reserve_max: bool = False):
+    def __init__(self, bm: BlockManager, max_running: int, reserve_max: bool = False,
+                 swap: bool = False):
         h = _vp()
-        _check(lib.pkv_sched_create(bm._h, max_running, 1 if reserve_max else 0,
-                                    ctypes.byref(h)), "pkv_sched_create")
+        policy = (PKV_SCHED_RESERVE_MAX if reserve_max else 0) | (PKV_SCHED_SWAP if swap else 0)
+        _check(lib.pkv_sched_create(bm._h, max_running, policy, ctypes.byref(h)),
+               "pkv_sched_create")
         self._h, self.bm, self.max_running = h, bm, int(max_running)
         n = self.max_running
+        npairs = bm.num_blocks
+        self._swin = np.zeros(2 * npairs, np.int32)
+        self._swout = np.zeros(2 * npairs, np.int32)
+        self._swin_ids = np.zeros(n, np.int64)
+        self._swout_ids = np.zeros(n, np.int64)
         self._ids = np.zeros(n, np.int64)
         self._slots = np.zeros(n, np.int64)
         self._cow = np.zeros(2 * n, np.int32)
@@ -276,7 +341,11 @@ class Scheduler:
                                 _np_ptr(self._adm, ctypes.c_int64),
                                 _np_ptr(self._adm_ctx, ctypes.c_int32), 0,
                                 _np_ptr(self._pre, ctypes.c_int64), 0,
-                                _np_ptr(self._fin, ctypes.c_int64), 0)
+                                _np_ptr(self._fin, ctypes.c_int64), 0, npairs,
+                                _np_ptr(self._swin, ctypes.c_int32), 0,
+                                _np_ptr(self._swout, ctypes.c_int32), 0,
+                                _np_ptr(self._swin_ids, ctypes.c_int64), 0,
+                                _np_ptr(self._swout_ids, ctypes.c_int64), 0)
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
@@ -305,17 +374,22 @@ class Scheduler:
                                  self._adm_ctx[:st.n_admitted].tolist())),
             "preempted": self._pre[:st.n_preempted].tolist(),
             "finished": self._fin[:st.n_finished].tolist(),
+            "swap_in": [tuple(x) for x in self._swin[:2 * st.n_swap_in].reshape(-1, 2).tolist()],
+            "swap_out": [tuple(x) for x in self._swout[:2 * st.n_swap_out].reshape(-1, 2).tolist()],
+            "swapped_in": self._swin_ids[:st.n_swapped_in].tolist(),
+            "swapped_out": self._swout_ids[:st.n_swapped_out].tolist(),
         }
 
     def end_step(self) -> None:
         _check(lib.pkv_sched_end_step(self._h), "pkv_sched_end_step")
 
     def stats(self):
-        """(tokens held, slots committed, waiting, running)."""
-        held, committed, nw, nr = _i64(), _i64(), _i32(), _i32()
+        """(tokens held, slots committed, waiting, running, swapped out)."""
+        held, committed, nw, nr, ns = _i64(), _i64(), _i32(), _i32(), _i32()
         _check(lib.pkv_sched_stats(self._h, ctypes.byref(held), ctypes.byref(committed),
-                                   ctypes.byref(nw), ctypes.byref(nr)), "pkv_sched_stats")
-        return held.value, committed.value, nw.value, nr.value
+                                   ctypes.byref(nw), ctypes.byref(nr), ctypes.byref(ns)),
+               "pkv_sched_stats")
+        return held.value, committed.value, nw.value, nr.value, ns.value
 
 
 # ---------------------------------------------------------------------------
@@ -389,6 +463,34 @@ def pkv_copy_blocks(k_pool, v_pool, pairs, stream=None) -> None:
     _check(lib.pkv_copy_blocks(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                                _dev(pairs, "pairs"), n, Hkv, D, B, N, _dtype_code(k_pool),
                                _stream(stream)), "pkv_copy_blocks")
+
+
+def _pool_ptr(t: torch.Tensor, name: str) -> int:
+    """Device tensor, or pinned host tensor (the library maps it for the GPU)."""
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or a pinned host tensor")
+    return t.data_ptr()
+
+
+def pkv_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
+    """dst block pairs[k, 1] := src block pairs[k, 0] (K and V), between two pools
+    of the same geometry, each on the device or in pinned host memory; pairs is
+    int32 [n, 2] on the device."""
+    N_dst, Hkv, D, B = _pool_geometry(dst_k, dst_v)
+    N_src, *geo = _pool_geometry(src_k, src_v)
+    if tuple(geo) != (Hkv, D, B) or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools differ in geometry or dtype")
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [n, 2]")
+    n = pairs.shape[0]
+    if n == 0:
+        return
+    _check(lib.pkv_swap_blocks(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), N_dst,
+                               _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"), N_src,
+                               _dev(pairs, "pairs"), n, Hkv, D, B, _dtype_code(dst_k),
+                               _stream(stream)), "pkv_swap_blocks")
 
 
 def pkv_attention_workspace_bytes(S: int, Hq: int, D: int, max_context_len: int,
@@ -531,6 +633,7 @@ def pkv_paged_attention_reduce(out, context_lens, Hkv: int, B: int, max_blocks: 
 
 reshape_and_cache = pkv_reshape_and_cache
 copy_blocks = pkv_copy_blocks
+swap_blocks = pkv_swap_blocks
 attention_workspace_bytes = pkv_attention_workspace_bytes
 paged_attention_decode = pkv_paged_attention_decode
 paged_attention_main = pkv_paged_attention_main

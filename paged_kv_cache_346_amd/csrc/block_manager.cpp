@@ -7,9 +7,15 @@
 // Batching, "Pages, from operating systems": block tables, allocation as tokens
 // arrive, copy-on-write of shared blocks).
 //
-// All integer work, O(1) per token except fork/free (O(blocks of the sequence)).
-// The free queue is a ring buffer of capacity num_blocks: a block id is in it
-// exactly when its refcount is zero, so it can never overflow.
+// All integer work, O(1) per token except fork/free/swap (O(blocks of the
+// sequence)).  The free queue is a ring buffer of capacity num_blocks: a block
+// id is in it exactly when its refcount is zero, so it can never overflow.
+//
+// Swapping (PagedAttention: The vLLM Paper, "The Core Idea", OS-paging analogy
+// table, "Swapping"; "Implementation Essentials": preemption moves a request's
+// blocks to CPU memory): an optional host pool with the device pool's geometry
+// and its own FIFO free ring.  A swapped sequence keeps its length and holds
+// host block ids in its table until it is swapped back in or freed.
 #include <cstring>
 #include <new>
 #include <unordered_map>
@@ -19,13 +25,17 @@
 
 struct pkv_bm {
   struct Seq {
-    std::vector<int32_t> table;
+    std::vector<int32_t> table;  // device blocks, or host blocks while swapped
     int32_t len = 0;
+    bool swapped = false;
   };
   int32_t N = 0, B = 0;
   std::vector<int32_t> ref;
   std::vector<int32_t> ring;  // free queue: ring[(head + i) % N], i < nfree
   int32_t head = 0, nfree = 0;
+  int32_t NH = 0;             // host pool: FIFO ring of its free blocks
+  std::vector<int32_t> hring;
+  int32_t hhead = 0, hnfree = 0;
   std::unordered_map<int64_t, Seq> seqs;
 
   int32_t pop_free() {
@@ -40,6 +50,37 @@ struct pkv_bm {
     if (tail >= N) tail -= N;
     ring[tail] = b;
     ++nfree;
+  }
+  int32_t pop_host() {
+    int32_t h = hring[hhead];
+    hhead = (hhead + 1 == NH) ? 0 : hhead + 1;
+    --hnfree;
+    return h;
+  }
+  void push_host(int32_t h) {
+    int32_t tail = hhead + hnfree;
+    if (tail >= NH) tail -= NH;
+    hring[tail] = h;
+    ++hnfree;
+  }
+  void release(const std::vector<int32_t>& table) {
+    for (int32_t b : table)
+      if (--ref[b] == 0) push_free(b);
+  }
+  // a sequence on the device: PKV_ENOSEQ if unknown, PKV_EINVAL if swapped out
+  pkv_status resident(int64_t id, Seq** out) {
+    auto it = seqs.find(id);
+    if (it == seqs.end()) return PKV_ENOSEQ;
+    if (it->second.swapped) return PKV_EINVAL;
+    *out = &it->second;
+    return PKV_OK;
+  }
+  pkv_status resident(int64_t id, const Seq** out) const {
+    auto it = seqs.find(id);
+    if (it == seqs.end()) return PKV_ENOSEQ;
+    if (it->second.swapped) return PKV_EINVAL;
+    *out = &it->second;
+    return PKV_OK;
   }
 };
 
@@ -116,9 +157,9 @@ static pkv_status append_one(pkv_bm* bm, pkv_bm::Seq& s, int64_t* slot, int32_t*
 pkv_status pkv_bm_append_slot(pkv_bm* bm, int64_t seq_id, int64_t* slot, int32_t* cow_src,
                               int32_t* cow_dst) {
   if (!bm || !slot || !cow_src || !cow_dst) return PKV_EINVAL;
-  auto it = bm->seqs.find(seq_id);
-  if (it == bm->seqs.end()) return PKV_ENOSEQ;
-  return append_one(bm, it->second, slot, cow_src, cow_dst);
+  pkv_bm::Seq* s;
+  if (pkv_status st = bm->resident(seq_id, &s)) return st;
+  return append_one(bm, *s, slot, cow_src, cow_dst);
 }
 
 pkv_status pkv_bm_append_slots(pkv_bm* bm, const int64_t* seq_ids, int32_t n, int64_t* slots,
@@ -128,10 +169,10 @@ pkv_status pkv_bm_append_slots(pkv_bm* bm, const int64_t* seq_ids, int32_t n, in
   *n_cow = 0;
   *n_done = 0;
   for (int32_t i = 0; i < n; ++i) {
-    auto it = bm->seqs.find(seq_ids[i]);
-    if (it == bm->seqs.end()) return PKV_ENOSEQ;
+    pkv_bm::Seq* s;
+    if (pkv_status st = bm->resident(seq_ids[i], &s)) return st;
     int32_t src, dst;
-    pkv_status st = append_one(bm, it->second, &slots[i], &src, &dst);
+    pkv_status st = append_one(bm, *s, &slots[i], &src, &dst);
     if (st != PKV_OK) return st;
     if (src >= 0) {
       cow_pairs[2 * *n_cow] = src;
@@ -145,10 +186,10 @@ pkv_status pkv_bm_append_slots(pkv_bm* bm, const int64_t* seq_ids, int32_t n, in
 
 pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent_id, int64_t child_id) {
   if (!bm) return PKV_EINVAL;
-  auto it = bm->seqs.find(parent_id);
-  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  pkv_bm::Seq* parent;
+  if (pkv_status st = bm->resident(parent_id, &parent)) return st;
   if (bm->seqs.count(child_id)) return PKV_EEXIST;
-  pkv_bm::Seq child = it->second;  // copy before emplace may rehash
+  pkv_bm::Seq child = *parent;  // copy before emplace may rehash
   for (int32_t b : child.table) bm->ref[b] += 1;
   bm->seqs.emplace(child_id, std::move(child));
   return PKV_OK;
@@ -158,10 +199,80 @@ pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id) {
   if (!bm) return PKV_EINVAL;
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PKV_ENOSEQ;
-  for (int32_t b : it->second.table) {
-    if (--bm->ref[b] == 0) bm->push_free(b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.table) bm->push_host(h);
+  } else {
+    bm->release(it->second.table);
   }
   bm->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_set_host_pool(pkv_bm* bm, int32_t num_host_blocks) {
+  if (!bm || num_host_blocks <= 0 || bm->NH) return PKV_EINVAL;
+  bm->hring.resize(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i) bm->hring[i] = i;
+  bm->NH = num_host_blocks;
+  bm->hnfree = num_host_blocks;
+  bm->hhead = 0;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_num_free_host(const pkv_bm* bm, int32_t* out) {
+  if (!bm || !out) return PKV_EINVAL;
+  *out = bm->hnfree;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_is_swapped(const pkv_bm* bm, int64_t seq_id, int32_t* out) {
+  if (!bm || !out) return PKV_EINVAL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  *out = it->second.swapped ? 1 : 0;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_out(pkv_bm* bm, int64_t seq_id, int32_t* pairs, int32_t cap,
+                           int32_t* n_pairs) {
+  if (!bm || !n_pairs || cap < 0 || (cap > 0 && !pairs)) return PKV_EINVAL;
+  pkv_bm::Seq* s;
+  if (pkv_status st = bm->resident(seq_id, &s)) return st;
+  const int32_t n = (int32_t)s->table.size();
+  if (n > cap) return PKV_EINVAL;
+  if (n > bm->hnfree) return PKV_ENOBLOCKS;
+  std::vector<int32_t> host(n);
+  for (int32_t i = 0; i < n; ++i) {
+    host[i] = bm->pop_host();
+    pairs[2 * i] = s->table[i];
+    pairs[2 * i + 1] = host[i];
+  }
+  bm->release(s->table);
+  s->table.swap(host);
+  s->swapped = true;
+  *n_pairs = n;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_in(pkv_bm* bm, int64_t seq_id, int32_t* pairs, int32_t cap,
+                          int32_t* n_pairs) {
+  if (!bm || !n_pairs || cap < 0 || (cap > 0 && !pairs)) return PKV_EINVAL;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return PKV_ENOSEQ;
+  pkv_bm::Seq& s = it->second;
+  if (!s.swapped) return PKV_EINVAL;
+  const int32_t n = (int32_t)s.table.size();
+  if (n > cap) return PKV_EINVAL;
+  if (n > bm->nfree) return PKV_ENOBLOCKS;
+  std::vector<int32_t> dev(n);
+  for (int32_t i = 0; i < n; ++i) {
+    dev[i] = bm->pop_free();
+    pairs[2 * i] = s.table[i];
+    pairs[2 * i + 1] = dev[i];
+  }
+  for (int32_t h : s.table) bm->push_host(h);
+  s.table.swap(dev);
+  s.swapped = false;
+  *n_pairs = n;
   return PKV_OK;
 }
 
@@ -195,9 +306,9 @@ pkv_status pkv_bm_seq_info(const pkv_bm* bm, int64_t seq_id, int32_t* len, int32
 
 pkv_status pkv_bm_block_table(const pkv_bm* bm, int64_t seq_id, int32_t* out, int32_t cap) {
   if (!bm || cap < 0 || (cap > 0 && !out)) return PKV_EINVAL;
-  auto it = bm->seqs.find(seq_id);
-  if (it == bm->seqs.end()) return PKV_ENOSEQ;
-  const auto& t = it->second.table;
+  const pkv_bm::Seq* s;
+  if (pkv_status st = bm->resident(seq_id, &s)) return st;
+  const auto& t = s->table;
   if ((int32_t)t.size() > cap) return PKV_EINVAL;
   if (!t.empty()) std::memcpy(out, t.data(), t.size() * sizeof(int32_t));
   return PKV_OK;
@@ -206,9 +317,9 @@ pkv_status pkv_bm_block_table(const pkv_bm* bm, int64_t seq_id, int32_t* out, in
 pkv_status pkv_bm_slots(const pkv_bm* bm, int64_t seq_id, int32_t start, int32_t count,
                         int64_t* slots) {
   if (!bm || start < 0 || count < 0 || (count > 0 && !slots)) return PKV_EINVAL;
-  auto it = bm->seqs.find(seq_id);
-  if (it == bm->seqs.end()) return PKV_ENOSEQ;
-  const auto& s = it->second;
+  const pkv_bm::Seq* sp;
+  if (pkv_status st = bm->resident(seq_id, &sp)) return st;
+  const auto& s = *sp;
   if ((int64_t)start + count > s.len) return PKV_EINVAL;
   const int32_t B = bm->B;
   for (int32_t i = 0; i < count; ++i) {
@@ -225,9 +336,9 @@ pkv_status pkv_bm_fill_batch(const pkv_bm* bm, const int64_t* seq_ids, int32_t n
     return PKV_EINVAL;
   // validate everything first so a failing call writes nothing
   for (int32_t i = 0; i < n; ++i) {
-    auto it = bm->seqs.find(seq_ids[i]);
-    if (it == bm->seqs.end()) return PKV_ENOSEQ;
-    if ((int32_t)it->second.table.size() > max_blocks) return PKV_EINVAL;
+    const pkv_bm::Seq* s;
+    if (pkv_status st = bm->resident(seq_ids[i], &s)) return st;
+    if ((int32_t)s->table.size() > max_blocks) return PKV_EINVAL;
   }
   for (int32_t i = 0; i < n; ++i) {
     const auto& s = bm->seqs.find(seq_ids[i])->second;
@@ -245,9 +356,9 @@ pkv_status pkv_bm_count_shared(const pkv_bm* bm, const int64_t* seq_ids, int32_t
   if (!bm || n < 0 || !out || (n > 0 && !seq_ids)) return PKV_EINVAL;
   int64_t shared = 0;
   for (int32_t i = 0; i < n; ++i) {
-    auto it = bm->seqs.find(seq_ids[i]);
-    if (it == bm->seqs.end()) return PKV_ENOSEQ;
-    for (int32_t b : it->second.table) shared += bm->ref[b] > 1;
+    const pkv_bm::Seq* s;
+    if (pkv_status st = bm->resident(seq_ids[i], &s)) return st;
+    for (int32_t b : s->table) shared += bm->ref[b] > 1;
   }
   *out = shared;
   return PKV_OK;
@@ -263,6 +374,17 @@ pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_q
     free_queue[i] = bm->ring[k];
   }
   *n_free = bm->nfree;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_host_snapshot(const pkv_bm* bm, int32_t* free_queue, int32_t* n_free) {
+  if (!bm || !n_free || (bm->NH > 0 && !free_queue)) return PKV_EINVAL;
+  for (int32_t i = 0; i < bm->hnfree; ++i) {
+    int32_t k = bm->hhead + i;
+    if (k >= bm->NH) k -= bm->NH;
+    free_queue[i] = bm->hring[k];
+  }
+  *n_free = bm->hnfree;
   return PKV_OK;
 }
 

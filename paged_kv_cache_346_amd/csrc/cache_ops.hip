@@ -11,6 +11,10 @@
 //     Batching, "Pages, from operating systems": a shared block is copied only
 //     when one sequence needs to modify it).  A (block, all heads) run is
 //     contiguous in both pools, so a pair is two straight 16-byte-vector copies.
+//   swap_blocks: the same copy between two pools, one of them in pinned host
+//     memory that the GPU reads or writes over the host link (PagedAttention:
+//     The vLLM Paper, "The Core Idea", analogy table, "Swapping": KV blocks
+//     moved to CPU memory and back).
 #include "../../include/pkv.h"
 #include "device_common.h"
 #include "launch_check.h"
@@ -52,22 +56,24 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ k_pool,
-                                                          u32x4* __restrict__ v_pool,
-                                                          const int32_t* __restrict__ pairs,
-                                                          int64_t total, int64_t units,
-                                                          int num_blocks) {
+// dst_pool[dst] = src_pool[src] for each pair (src, dst), K and V; `units`
+// 16-byte vectors per block.  A pair naming a block outside its pool is
+// skipped.  src and dst may be the same pool (copy-on-write: within one call
+// no block is both a source and a destination).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    const u32x4* src_k, const u32x4* src_v, int src_blocks, u32x4* dst_k, u32x4* dst_v,
+    int dst_blocks, const int32_t* __restrict__ pairs, int64_t total, int64_t units) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
   const int64_t k = gid / units;
   const int64_t u = gid % units;
   const int src = pairs[2 * k];
   const int dst = pairs[2 * k + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const u32x4 a = k_pool[(int64_t)src * units + u];
-  const u32x4 b = v_pool[(int64_t)src * units + u];
-  k_pool[(int64_t)dst * units + u] = a;
-  v_pool[(int64_t)dst * units + u] = b;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const u32x4 a = src_k[(int64_t)src * units + u];
+  const u32x4 b = src_v[(int64_t)src * units + u];
+  dst_k[(int64_t)dst * units + u] = a;
+  dst_v[(int64_t)dst * units + u] = b;
 }
 
 }  // namespace pkv
@@ -116,6 +122,48 @@ extern "C" pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t*
   const int64_t total = units * n;
   const dim3 grid((unsigned)((total + 255) / 256));
   copy_blocks_kernel<<<grid, 256, 0, (hipStream_t)hip_stream>>>(
-      (u32x4*)k_pool, (u32x4*)v_pool, pairs, total, units, num_blocks);
+      (const u32x4*)k_pool, (const u32x4*)v_pool, num_blocks, (u32x4*)k_pool, (u32x4*)v_pool,
+      num_blocks, pairs, total, units);
+  return launch_status();
+}
+
+// The address at which the GPU reaches `p`: device memory as is, pinned host
+// memory through its device mapping; nullptr for memory the GPU cannot reach
+// (pageable host memory), so such a pool is rejected before any launch.
+static void* device_view(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // the query leaves its error behind for pageable memory
+    return nullptr;
+  }
+  if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeHost) return nullptr;
+  return at.devicePointer;
+}
+
+extern "C" pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_blocks,
+                                      const void* src_k, const void* src_v, int32_t src_blocks,
+                                      const int32_t* pairs, int32_t n, int32_t Hkv, int32_t D,
+                                      int32_t B, pkv_dtype dtype, void* hip_stream) {
+  if (n < 0 || Hkv <= 0 || D <= 0 || B <= 0 || dst_blocks <= 0 || src_blocks <= 0)
+    return PKV_EINVAL;
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_EINVAL;
+  const int es = dtype == PKV_F32 ? 4 : 2;
+  const int64_t block_bytes = (int64_t)Hkv * D * B * es;
+  if (block_bytes % 16 != 0) return PKV_EINVAL;
+  if (n == 0) return PKV_OK;
+  if (!pairs || !aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v))
+    return PKV_EINVAL;
+  void* dk = device_view(dst_k);
+  void* dv = device_view(dst_v);
+  void* sk = device_view(src_k);
+  void* sv = device_view(src_v);
+  if (!dk || !dv || !sk || !sv) return PKV_EINVAL;
+  if (!aligned16(dk) || !aligned16(dv) || !aligned16(sk) || !aligned16(sv)) return PKV_EINVAL;
+  const int64_t units = block_bytes / 16;
+  const int64_t total = units * n;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  copy_blocks_kernel<<<grid, 256, 0, (hipStream_t)hip_stream>>>(
+      (const u32x4*)sk, (const u32x4*)sv, src_blocks, (u32x4*)dk, (u32x4*)dv, dst_blocks, pairs,
+      total, units);
   return launch_status();
 }

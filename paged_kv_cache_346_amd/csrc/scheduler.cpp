@@ -6,14 +6,17 @@
 // ones join -- and with paging a newcomer needs only free blocks.
 // PagedAttention: The vLLM Paper, "Continuous Batching" (A finishes, A dequeues,
 // D enqueues, giving {B, C, D}) and "Implementation Essentials" (preemption
-// drops a request's blocks for later recomputation under memory pressure).
+// swaps a request's blocks to CPU memory, or drops them for later
+// recomputation, under memory pressure).
 //
 // Policy (readings of the pages, stated in include/pkv.h): first-come
 // first-served admission with no skipping ahead; at most max_running requests;
 // one token per running request per step, appended in admission order; the
 // most recently admitted request is preempted when an append finds no free
-// block.  The reserve policy simulates the max-length reservation of the
-// systems before paging over the same pool.  Integer bookkeeping only.
+// block -- swapped to the host pool under the swap policy when it holds KV and
+// the host has room, else dropped.  The reserve policy simulates the
+// max-length reservation of the systems before paging over the same pool.
+// Integer bookkeeping only.
 #include <deque>
 #include <new>
 #include <unordered_map>
@@ -29,11 +32,12 @@ struct pkv_sched {
   };
   pkv_bm* bm = nullptr;
   int32_t N = 0, B = 0, max_running = 0;
-  bool reserve = false;
+  bool reserve = false, swap = false;
   int64_t reserved_total = 0;
   bool in_step = false;
   std::unordered_map<int64_t, Req> reqs;  // every submitted, unfinished request
   std::deque<Req*> waiting;
+  std::deque<Req*> swapped;  // preempted to the host, front resumes first
   std::vector<Req*> running;
   std::vector<Req*> finishing;
 
@@ -42,11 +46,13 @@ struct pkv_sched {
 
 extern "C" {
 
-pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t reserve_max,
+pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t policy,
                             pkv_sched** out) {
   if (!out) return PKV_EINVAL;
   *out = nullptr;
   if (!bm || max_running <= 0) return PKV_EINVAL;
+  if (policy & ~(PKV_SCHED_RESERVE_MAX | PKV_SCHED_SWAP)) return PKV_EINVAL;
+  if ((policy & PKV_SCHED_RESERVE_MAX) && (policy & PKV_SCHED_SWAP)) return PKV_EINVAL;
   int32_t N = 0, B = 0;
   if (pkv_bm_geometry(bm, &N, &B) != PKV_OK) return PKV_EINVAL;
   pkv_sched* s = new (std::nothrow) pkv_sched();
@@ -55,7 +61,8 @@ pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t reserve_max
   s->N = N;
   s->B = B;
   s->max_running = max_running;
-  s->reserve = reserve_max != 0;
+  s->reserve = (policy & PKV_SCHED_RESERVE_MAX) != 0;
+  s->swap = (policy & PKV_SCHED_SWAP) != 0;
   *out = s;
   return PKV_OK;
 }
@@ -77,13 +84,33 @@ pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
   if (!o->batch_ids || !o->slots || !o->cow_pairs || !o->admitted_ids || !o->admitted_ctx ||
       !o->preempted_ids || !o->finished_ids)
     return PKV_EINVAL;
+  if (s->swap && (o->pair_capacity < s->N || !o->swap_in_pairs || !o->swap_out_pairs ||
+                  !o->swapped_in_ids || !o->swapped_out_ids))
+    return PKV_EINVAL;
   if (s->in_step) return PKV_EINVAL;  // end_step() of the last step is due
   o->n_batch = o->n_cow = o->n_admitted = o->n_preempted = o->n_finished = 0;
+  o->n_swap_in = o->n_swap_out = o->n_swapped_in = o->n_swapped_out = 0;
   s->in_step = true;
 
-  // admissions, first come first served
+  // swapped requests come back first, in queue order, while the device has room
+  while (!s->swapped.empty() && (int32_t)s->running.size() < s->max_running) {
+    pkv_sched::Req* r = s->swapped.front();
+    int32_t n = 0;
+    // at most N device blocks are free, so the pairs fit pair_capacity
+    const pkv_status st = pkv_bm_swap_in(s->bm, r->id, o->swap_in_pairs + 2 * o->n_swap_in,
+                                         o->pair_capacity - o->n_swap_in, &n);
+    if (st == PKV_ENOBLOCKS) break;
+    if (st != PKV_OK) return st;
+    o->n_swap_in += n;
+    s->swapped.pop_front();
+    s->running.push_back(r);
+    o->swapped_in_ids[o->n_swapped_in++] = r->id;
+  }
+
+  // admissions, first come first served, none while a request is swapped out
   std::vector<std::pair<pkv_sched::Req*, int32_t>> admitted;
-  while (!s->waiting.empty() && (int32_t)s->running.size() < s->max_running) {
+  while (s->swapped.empty() && !s->waiting.empty() &&
+         (int32_t)s->running.size() < s->max_running) {
     pkv_sched::Req* r = s->waiting.front();
     const int32_t need_max = s->blocks((int64_t)r->prompt + r->max_new);
     if (s->reserve && s->reserved_total + need_max > s->N) break;
@@ -109,13 +136,29 @@ pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
     if (st == PKV_ENOBLOCKS) {
       pkv_sched::Req* victim = s->running.back();
       s->running.pop_back();
+      size_t fresh = admitted.size();  // admitted this step: no KV written yet
+      for (size_t k = 0; k < admitted.size(); ++k)
+        if (admitted[k].first == victim) fresh = k;
+      if (s->swap && fresh == admitted.size()) {
+        int32_t len = 0, nb = 0, host_free = 0;
+        pkv_bm_seq_info(s->bm, victim->id, &len, &nb);
+        pkv_bm_num_free_host(s->bm, &host_free);
+        // the step's swap-outs never hold more blocks than the device has
+        if (nb <= host_free && o->n_swap_out + nb <= o->pair_capacity) {
+          int32_t n = 0;
+          const pkv_status ss =
+              pkv_bm_swap_out(s->bm, victim->id, o->swap_out_pairs + 2 * o->n_swap_out,
+                              o->pair_capacity - o->n_swap_out, &n);
+          if (ss != PKV_OK) return ss;
+          o->n_swap_out += n;
+          o->swapped_out_ids[o->n_swapped_out++] = victim->id;
+          s->swapped.push_front(victim);
+          continue;
+        }
+      }
       const pkv_status fs = pkv_bm_free_seq(s->bm, victim->id);
       if (fs != PKV_OK) return fs;
-      for (size_t k = 0; k < admitted.size(); ++k)
-        if (admitted[k].first == victim) {
-          admitted.erase(admitted.begin() + k);
-          break;
-        }
+      if (fresh < admitted.size()) admitted.erase(admitted.begin() + fresh);
       o->preempted_ids[o->n_preempted++] = victim->id;
       s->waiting.push_front(victim);
       continue;
@@ -167,8 +210,9 @@ pkv_status pkv_sched_end_step(pkv_sched* s) {
 }
 
 pkv_status pkv_sched_stats(const pkv_sched* s, int64_t* tokens_held, int64_t* slots_committed,
-                           int32_t* n_waiting, int32_t* n_running) {
-  if (!s || !tokens_held || !slots_committed || !n_waiting || !n_running) return PKV_EINVAL;
+                           int32_t* n_waiting, int32_t* n_running, int32_t* n_swapped) {
+  if (!s || !tokens_held || !slots_committed || !n_waiting || !n_running || !n_swapped)
+    return PKV_EINVAL;
   int64_t held = 0;
   for (const pkv_sched::Req* r : s->running) held += r->ctx();
   *tokens_held = held;
@@ -181,6 +225,7 @@ pkv_status pkv_sched_stats(const pkv_sched* s, int64_t* tokens_held, int64_t* sl
   }
   *n_waiting = (int32_t)s->waiting.size();
   *n_running = (int32_t)s->running.size();
+  *n_swapped = (int32_t)s->swapped.size();
   return PKV_OK;
 }
 

@@ -5,18 +5,23 @@ Drives the native scheduler (pkv_sched_*) and the device kernels step by step
 PagedAttention: The vLLM Paper, "Continuous Batching" and "Implementation
 Essentials"): every step
 
-  1. the scheduler admits waiting requests into free blocks, appends one slot
-     per running request (preempting the youngest when the pool runs dry) and
-     names the requests that finish;
-  2. copy-on-write block copies run, then one reshape_and_cache writes the
+  1. the scheduler swaps preempted requests back in, admits waiting requests
+     into free blocks, appends one slot per running request (preempting the
+     youngest when the pool runs dry: swapped to the host pool when the loop
+     has one, else dropped for recomputation) and names the requests that
+     finish;
+  2. the swap-in copies (host to device), the swap-out copies (device to host)
+     and the copy-on-write copies run, then one reshape_and_cache writes the
      prompt KV of the admitted requests;
   3. paged attention runs over the batch's block tables (host work plan) and
      writes the new token of every running request into its slot as it goes;
   4. the finished requests give their blocks back.
 
-The step's metadata (slots, block tables, lengths, work plan) is packed into
-one pinned host buffer and sent with a single asynchronous copy; two buffers
-alternate so the host fills one while the previous step's copy may still run.
+The step's metadata (slots, block copy pairs, block tables, lengths, work plan)
+is packed into one pinned host buffer and sent with a single asynchronous copy;
+two buffers alternate so the host fills one while the previous step's copy may
+still run.  The host pool, when there is one, is pinned host memory that the
+swap kernel reads and writes over the host link.
 
 K/V and query values come from caller-supplied sources (the loop computes no
 model): kv_source(pairs) returns the K and V rows [T, Hkv, D] for an int64
@@ -31,7 +36,7 @@ import numpy as np
 import torch
 
 from . import (BlockManager, Plan, Scheduler, attention_plan, attention_workspace_bytes,
-               copy_blocks, paged_attention_decode, pool_shapes, reshape_and_cache)
+               copy_blocks, paged_attention_decode, pool_shapes, reshape_and_cache, swap_blocks)
 
 
 def _pad4(n: int) -> int:
@@ -42,17 +47,24 @@ class DecodeLoop:
     def __init__(self, *, num_blocks: int, block_size: int, q_heads: int, kv_heads: int,
                  head_dim: int, max_running: int, max_len: int, dtype=torch.bfloat16,
                  partition_size: int = 0, reserve_max: bool = False, free_order=None,
-                 device="cuda"):
+                 host_blocks: int = 0, device="cuda"):
         self.B, self.Hq, self.Hkv, self.D = block_size, q_heads, kv_heads, head_dim
         self.P = partition_size
         self.max_len = max_len
         self.max_blocks = max(1, math.ceil(max_len / block_size))
         self.device = torch.device(device)
         self.bm = BlockManager(num_blocks, block_size, free_order)
-        self.sched = Scheduler(self.bm, max_running, reserve_max)
+        if host_blocks:
+            self.bm.set_host_pool(host_blocks)
+        self.sched = Scheduler(self.bm, max_running, reserve_max, swap=host_blocks > 0)
         ks, vs = pool_shapes(num_blocks, kv_heads, head_dim, block_size, dtype)
         self.k_pool = torch.empty(ks, dtype=dtype, device=self.device)
         self.v_pool = torch.empty(vs, dtype=dtype, device=self.device)
+        self.host_k = self.host_v = None
+        if host_blocks:
+            hks, hvs = pool_shapes(host_blocks, kv_heads, head_dim, block_size, dtype)
+            self.host_k = torch.empty(hks, dtype=dtype, pin_memory=True)
+            self.host_v = torch.empty(hvs, dtype=dtype, pin_memory=True)
         nbytes = attention_workspace_bytes(max_running, q_heads, head_dim, max_len,
                                            partition_size)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
@@ -69,9 +81,9 @@ class DecodeLoop:
         self.sched.add_request(req_id, prompt_len, max_new_tokens)
 
     def _stage(self, parts):
-        """Copy the int32 arrays `parts` to the device in one transfer; returns
-        device views of them (each starting on a 16-byte boundary)."""
-        total = sum(_pad4(p.size) for p in parts)
+        """Copy the int32 arrays `parts` (a dict) to the device in one transfer;
+        returns device views of them by name (each on a 16-byte boundary)."""
+        total = sum(_pad4(p.size) for p in parts.values())
         i = self._turn
         self._turn ^= 1
         if self._done[i] is not None:
@@ -82,16 +94,16 @@ class DecodeLoop:
             if self._dev is None or self._dev.numel() < cap:
                 self._dev = torch.empty(cap, dtype=torch.int32, device=self.device)
         host = self._host[i].numpy()
-        off, spans = 0, []
-        for p in parts:
+        off, spans = 0, {}
+        for name, p in parts.items():
             host[off:off + p.size] = p.reshape(-1)
-            spans.append((off, p.size))
+            spans[name] = (off, p.size)
             off += _pad4(p.size)
         self._dev[:total].copy_(self._host[i][:total], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
         self._done[i] = ev
-        return [self._dev[o:o + n] for o, n in spans]
+        return {name: self._dev[o:o + n] for name, (o, n) in spans.items()}
 
     def step(self, kv_source, q_source):
         """One iteration.  Returns (the scheduler's step dict -- plus "stats",
@@ -119,35 +131,44 @@ class DecodeLoop:
             words, n_items, n_merge = attention_plan(lens, self.Hkv, self.B, width, mcl,
                                                      self.P)
             pairs.append(np.stack([np.asarray(ids, np.int64), lens.astype(np.int64) - 1], 1))
-        parts = []
+        parts = {}
         if write_slots:
-            parts.append(np.concatenate(write_slots).view(np.int32))
+            parts["slots"] = np.concatenate(write_slots).view(np.int32)
+        for key in ("swap_in", "swap_out", "cow"):
+            if st[key]:
+                parts[key] = np.asarray(st[key], np.int32)
         if n:
-            parts += [tables.reshape(-1), lens, words]
-        dev = self._stage(parts) if parts else []
-        if st["cow"]:
-            copy_blocks(self.k_pool, self.v_pool,
-                        torch.tensor(st["cow"], dtype=torch.int32, device=self.device))
+            parts.update(tables=tables.reshape(-1), lens=lens, plan=words)
+        dev = self._stage(parts) if parts else {}
+        # block copies in the scheduler's order: swap-ins, swap-outs, copy-on-write
+        if "swap_in" in dev:
+            swap_blocks(self.k_pool, self.v_pool, self.host_k, self.host_v,
+                        dev["swap_in"].view(-1, 2))
+        if "swap_out" in dev:
+            swap_blocks(self.host_k, self.host_v, self.k_pool, self.v_pool,
+                        dev["swap_out"].view(-1, 2))
+        if "cow" in dev:
+            copy_blocks(self.k_pool, self.v_pool, dev["cow"].view(-1, 2))
         out = self.out[:n]
         if pairs:
             k, v = kv_source(np.concatenate(pairs))
             if write_slots:
                 reshape_and_cache(k[:-n] if n else k, v[:-n] if n else v, self.k_pool,
-                                  self.v_pool, dev[0].view(torch.int64))
+                                  self.v_pool, dev["slots"].view(torch.int64))
         if n:
-            d_tables, d_lens, d_plan = dev[-3:]
             paged_attention_decode(out, q_source(ids), self.k_pool, self.v_pool,
-                                   d_tables.view(n, -1), d_lens, mcl, partition_size=self.P,
-                                   workspace=self.ws, plan=Plan(d_plan, n_items, n_merge),
+                                   dev["tables"].view(n, -1), dev["lens"], mcl,
+                                   partition_size=self.P, workspace=self.ws,
+                                   plan=Plan(dev["plan"], n_items, n_merge),
                                    new_key=k[-n:], new_value=v[-n:])
         st["stats"] = self.sched.stats()   # before the finished requests leave
         self.sched.end_step()
         return st, out, lens
 
     def stats(self):
-        """(tokens held, slots committed, waiting, running)."""
+        """(tokens held, slots committed, waiting, running, swapped out)."""
         return self.sched.stats()
 
     def idle(self) -> bool:
-        _, _, nw, nr = self.sched.stats()
-        return nw == 0 and nr == 0
+        _, _, nw, nr, ns = self.sched.stats()
+        return nw == 0 and nr == 0 and ns == 0

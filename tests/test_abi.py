@@ -83,6 +83,22 @@ def test_host_validation_rejects_before_launch(pkv):
     assert lib.pkv_copy_blocks(fake, odd, tbl, 3, 8, 128, 16, 8, 1, None) == pkv.PKV_EINVAL
 
 
+def test_swap_blocks_validation(pkv):
+    """Host-side checks only: nothing here can launch (a pointer the HIP runtime
+    does not know, or no GPU at all, is rejected before any launch)."""
+    lib = pkv.lib
+    fake, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4098)
+    args = lambda dk, n, dtype=1, nb=8: (dk, fake, nb, fake, fake, nb, fake, n, 8, 128, 16,
+                                         dtype, None)
+    assert lib.pkv_swap_blocks(*args(fake, 0)) == pkv.PKV_OK          # empty: no-op
+    assert lib.pkv_swap_blocks(*args(fake, -1)) == pkv.PKV_EINVAL
+    assert lib.pkv_swap_blocks(*args(fake, 1, dtype=7)) == pkv.PKV_EINVAL
+    assert lib.pkv_swap_blocks(*args(fake, 1, nb=0)) == pkv.PKV_EINVAL
+    assert lib.pkv_swap_blocks(*args(odd, 1)) == pkv.PKV_EINVAL         # misaligned
+    # memory the runtime cannot map for the GPU (here: an address it never gave out)
+    assert lib.pkv_swap_blocks(*args(fake, 1)) == pkv.PKV_EINVAL
+
+
 def test_workspace_size_formula(pkv):
     f = pkv.pkv_attention_workspace_bytes
     assert f(256, 32, 128, 512, 0) == 0                 # one partition: no workspace

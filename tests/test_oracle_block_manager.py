@@ -188,3 +188,4 @@ def test_count_shared_follows_fork_and_cow():
     for sid in (1, 2, 3):
         bm.free_seq(sid)
     assert count_shared(bm, [0]) == 0
+

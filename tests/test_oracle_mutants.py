@@ -105,6 +105,59 @@ def test_block_manager_mutants_fail_pins(monkeypatch, cls):
     assert failed > 0
 
 
+# --- swapping -------------------------------------------------------------------
+import tests.test_oracle_swap as tswap
+
+
+class _SwapKeepsDeviceBlocksBM(obm.BlockManager):
+    """swap_out copies to the host but never releases the device blocks."""
+
+    def _release(self, table):
+        if getattr(self, "_in_swap", False):
+            return
+        super()._release(table)
+
+    def swap_out(self, sid):
+        self._in_swap = True
+        try:
+            return super().swap_out(sid)
+        finally:
+            self._in_swap = False
+
+
+class _SwapInReversedBM(obm.BlockManager):
+    """swap_in pairs the host blocks with the new device blocks in reverse."""
+
+    def swap_in(self, sid):
+        pairs = super().swap_in(sid)
+        return [(h, d) for (h, _), (_, d) in zip(pairs, reversed(pairs))]
+
+
+class _LifoHostBM(obm.BlockManager):
+    """Host blocks come back to the front of the host free queue."""
+
+    def swap_in(self, sid):
+        host = list(self.host_tables.get(sid, []))
+        pairs = super().swap_in(sid)
+        for _ in host:
+            self.host_free.pop()
+        self.host_free.extendleft(reversed(host))
+        return pairs
+
+
+@pytest.mark.parametrize("cls", [_SwapKeepsDeviceBlocksBM, _SwapInReversedBM, _LifoHostBM])
+def test_swap_mutants_fail_pins(monkeypatch, cls):
+    monkeypatch.setattr(tswap, "BlockManager", cls)
+    failed = 0
+    for pin in [tswap.test_swap_worked_example, tswap.test_swap_of_a_shared_block_keeps_the_other_owner]\
+            + [lambda s=s: tswap._run_swap_script(s) for s in range(4)]:
+        try:
+            pin()
+        except (AssertionError, obm.BMError):
+            failed += 1
+    assert failed > 0
+
+
 # --- continuous-batching scheduler -------------------------------------------
 import oracle.scheduler as osched
 from tests import test_oracle_scheduler as tsched
@@ -153,5 +206,45 @@ def test_scheduler_mutants_fail_pins(monkeypatch, cls):
         try:
             t()
         except (AssertionError, osched.BMError, IndexError, ValueError, KeyError):
+            failed += 1
+    assert failed > 0
+
+
+
+# --- swap policy of the scheduler ---------------------------------------------
+from tests import test_oracle_scheduler_swap as tss
+
+
+class _SwapFreshVictimSched(osched.Scheduler):
+    """Swaps out a victim admitted in the same step, whose KV is not written."""
+
+    def _swap_victim(self, victim, fresh):
+        return super()._swap_victim(victim, False)
+
+
+class _AdmitWhileSwappedSched(osched.Scheduler):
+    """Admits waiting requests while preempted ones are still swapped out."""
+
+    def _may_admit(self):
+        return True
+
+
+class _SwapOldestSched(osched.Scheduler):
+    """Preempts the oldest running request instead of the youngest."""
+
+    def _victim(self):
+        return self.running.pop(0)
+
+
+@pytest.mark.parametrize("cls", [_SwapFreshVictimSched, _AdmitWhileSwappedSched,
+                                 _SwapOldestSched])
+def test_scheduler_swap_mutants_fail_pins(monkeypatch, cls):
+    monkeypatch.setattr(tss, "Scheduler", cls)
+    failed = 0
+    for t in [tss.test_swap_trace_worked_by_hand, tss.test_a_victim_without_kv_is_dropped_not_swapped] + \
+            [lambda s=s: tss.swap_trace_run(s, cls) for s in range(8)]:
+        try:
+            t()
+        except (AssertionError, osched.BMError, IndexError, KeyError, ValueError):
             failed += 1
     assert failed > 0

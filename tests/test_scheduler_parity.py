@@ -1,7 +1,10 @@
 """The C++ continuous-batching scheduler (through the C ABI) against the
 reference scheduler: identical steps (batch, slots, copy pairs, admissions with
-their contexts, preemptions, finishes), identical accounting and identical
-block-manager state after every step, under both policies (CPU only)."""
+their contexts, preemptions, finishes, swap pairs), identical accounting and
+identical block-manager state after every step, under all three policies
+(CPU only)."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -10,9 +13,8 @@ from oracle.scheduler import Scheduler as RefSched
 from workloads import request_trace
 
 
-@pytest.mark.parametrize("reserve", [False, True])
-@pytest.mark.parametrize("seed", range(10))
-def test_random_traces_bit_exact(pkv, seed, reserve):
+def run_parity(pkv, seed, policy):
+    reserve, swap = policy == "reserve", policy == "swap"
     rng = np.random.default_rng(1500 + seed)
     B = int(rng.choice([1, 4, 16, 32]))
     trace = request_trace(rng, int(rng.integers(1, 60)), prompt_median=50, out_median=30,
@@ -21,19 +23,23 @@ def test_random_traces_bit_exact(pkv, seed, reserve):
     order = rng.permutation(N)
     max_running = int(rng.integers(1, 16))
     nbm, rbm = pkv.BlockManager(N, B, order), RefBM(N, B, order)
-    nat = pkv.Scheduler(nbm, max_running, reserve)
-    ref = RefSched(rbm, max_running, reserve)
+    if swap:
+        NH = int(rng.integers(1, 2 * N))
+        nbm.set_host_pool(NH)
+        rbm.set_host_pool(NH)
+    nat = pkv.Scheduler(nbm, max_running, reserve, swap)
+    ref = RefSched(rbm, max_running, reserve, swap)
     for rid, p, m in trace:
         nat.add_request(rid, p, m)
         ref.add_request(rid, p, m)
-    steps = 0
+    steps = swaps = 0
     while not ref.idle():
         a, b = nat.begin_step(), ref.begin_step()
         assert a == {k: (list(v) if k != "admitted" else [tuple(x) for x in v])
                      for k, v in b.items()}
-        held, committed, nw, nr = nat.stats()
+        held, committed, nw, nr, ns = nat.stats()
         assert (held, committed) == (ref.tokens_held(), ref.slots_committed())
-        assert (nw, nr) == (len(ref.waiting), len(ref.running))
+        assert (nw, nr, ns) == (len(ref.waiting), len(ref.running), len(ref.swapped))
         ids = a["batch"]
         if ids:
             maxb = max(len(rbm.tables[i]) for i in ids)
@@ -44,9 +50,30 @@ def test_random_traces_bit_exact(pkv, seed, reserve):
         ref.end_step()
         refc, free = nbm.snapshot()
         assert refc == rbm.ref and free == list(rbm.free)
+        if swap:
+            assert nbm.host_free_queue() == list(rbm.host_free)
+            swaps += len(a["swapped_out"])
         steps += 1
-    assert nat.stats() == (0, 0, 0, 0)
+    assert nat.stats() == (0, 0, 0, 0, 0)
     assert steps > 0
+    return swaps
+
+
+@pytest.mark.parametrize("policy", ["paged", "reserve", "swap"])
+@pytest.mark.parametrize("seed", range(10))
+def test_random_traces_bit_exact(pkv, seed, policy):
+    run_parity(pkv, seed, policy)
+
+
+def test_swap_parity_traces_do_swap(pkv):
+    assert sum(run_parity(pkv, s, "swap") > 0 for s in range(10)) >= 5
+
+
+def test_policy_word_is_validated(pkv):
+    bm = pkv.BlockManager(4, 16)
+    h = ctypes.c_void_p()
+    for bad in (pkv.PKV_SCHED_RESERVE_MAX | pkv.PKV_SCHED_SWAP, 4, -1):
+        assert pkv.lib.pkv_sched_create(bm._h, 2, bad, ctypes.byref(h)) == pkv.PKV_EINVAL
 
 
 def test_native_error_paths(pkv):

@@ -215,11 +215,17 @@ def make(name_or_cfg, *, extra_free: float = 0.2, extra_blocks: int = 0,
     return Workload(cfg, lengths, N, free_order, q, k_pool, v_pool, k_new, v_new, ops, step_ids)
 
 
-def random_script(rng: np.random.Generator, n_ops: int, max_seqs: int = 8, max_add: int = 80):
+def random_script(rng: np.random.Generator, n_ops: int, max_seqs: int = 8, max_add: int = 80,
+                  swap: bool = False):
     """A random block-manager op script (for state-parity tests): admissions,
-    forks, single-token appends and frees over a small id space."""
+    forks, single-token appends and frees over a small id space; with swap,
+    also swap-outs and swap-ins (one op in five)."""
     ops = []
     for _ in range(n_ops):
+        if swap and rng.random() < 0.2:
+            ops.append(("swap_out" if rng.random() < 0.5 else "swap_in",
+                        int(rng.integers(0, max_seqs))))
+            continue
         r = rng.random()
         sid = int(rng.integers(0, max_seqs))
         if r < 0.2:
