@@ -44,6 +44,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged-attn decode KV-read GB/s (% of HBM peak) and decode tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
+HOST_LINK_PEAK_GBS = 64.0      # PCIe 5.0 x16 host link, per direction, before protocol overhead
 MAIN_KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_346_amd", "csrc", "attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -264,11 +265,47 @@ def cpu_baseline(batch, torch, budget_s: float):
     }
 
 
+def _swap_probe(torch, pkv, Hkv, D, B, N, n_blocks=2048, reps=5):
+    """swap_blocks bandwidth over the host link: n_blocks random device blocks
+    to a pinned host pool and back, timed with HIP events on the launch
+    stream, best of `reps`."""
+    dev = torch.device("cuda")
+    ks, vs = pkv.pool_shapes(N, Hkv, D, B, torch.bfloat16)
+    hks, hvs = pkv.pool_shapes(n_blocks, Hkv, D, B, torch.bfloat16)
+    k = torch.zeros(ks, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros(vs, dtype=torch.bfloat16, device=dev)
+    hk = torch.zeros(hks, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.zeros(hvs, dtype=torch.bfloat16, pin_memory=True)
+    g = torch.Generator().manual_seed(5)
+    src = torch.randperm(N, generator=g)[:n_blocks].to(torch.int32)
+    out_pairs = torch.stack([src, torch.arange(n_blocks, dtype=torch.int32)], 1).to(dev)
+    in_pairs = torch.stack([torch.arange(n_blocks, dtype=torch.int32), src], 1).to(dev)
+    nbytes = 2 * n_blocks * Hkv * D * B * 2
+    res = {}
+    for name, call in (("device_to_host", lambda: pkv.swap_blocks(hk, hv, k, v, out_pairs)),
+                       ("host_to_device", lambda: pkv.swap_blocks(k, v, hk, hv, in_pairs))):
+        call()
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            b.synchronize()
+            best = min(best, a.elapsed_time(b) * 1e-3)
+        res[name + "_GBps"] = round(nbytes / best / 1e9, 1)
+    res.update(bytes_per_call=nbytes, blocks=n_blocks,
+               link_peak_GBps_per_direction=HOST_LINK_PEAK_GBS)
+    return res
+
+
 def run_serve(args, torch, np):
-    """Continuous-batching loop over a synthetic request trace, under the paged
-    policy and under the simulated max-length reservation of the earlier
-    systems, on the same pool (the Llama-3-8B-shaped layer's 16,162 blocks).
-    Prints one JSON line (not the headline metric)."""
+    """Continuous-batching loop over a synthetic request trace on the same pool
+    (the Llama-3-8B-shaped layer's 16,162 blocks) under three policies: paged
+    with preemption by dropping and recomputing, paged with preemption by
+    swapping to a host pool of as many blocks, and the simulated max-length
+    reservation of the earlier systems.  Also times swap_blocks over the host
+    link.  Prints one JSON line (not the headline metric)."""
     import paged_kv_cache_346_amd as pkv
     from paged_kv_cache_346_amd.serve import DecodeLoop
     import workloads as W
@@ -302,14 +339,20 @@ def run_serve(args, torch, np):
     torch.cuda.synchronize()
     del warm
 
+    block_bytes = 2 * Hkv * D * B * 2          # K and V of one block, bf16
+    swap_probe = _swap_probe(torch, pkv, Hkv, D, B, N)
+    log(f"bench: swap_blocks probe: {swap_probe}")
+
     result = {}
-    for policy in ("paged", "reserve"):
+    prompts = sum(p_ for _, p_, _ in trace)
+    for policy in ("paged", "swap", "reserve"):
         loop = DecodeLoop(num_blocks=N, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
                           max_running=args.serve_running, max_len=max_len,
-                          reserve_max=(policy == "reserve"), free_order=order)
+                          reserve_max=(policy == "reserve"), free_order=order,
+                          host_blocks=N if policy == "swap" else 0)
         for rid, p_, m_ in trace:
             loop.add_request(rid, p_, m_)
-        steps = tokens = preempted = prefill = 0
+        steps = tokens = preempted = prefill = swapped = blocks_out = blocks_in = 0
         util_sum, batch_sum = 0.0, 0
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -321,6 +364,9 @@ def run_serve(args, torch, np):
             batch_sum += n
             preempted += len(st["preempted"])
             prefill += sum(c for _, c in st["admitted"])
+            swapped += len(st["swapped_out"])
+            blocks_out += len(st["swap_out"])
+            blocks_in += len(st["swap_in"])
             held, committed = st["stats"][:2]
             if n:
                 util_sum += held / max(committed, 1)
@@ -328,7 +374,11 @@ def run_serve(args, torch, np):
         wall = time.perf_counter() - t0
         result[policy] = {
             "decode_tokens": tokens, "steps": steps, "mean_batch": round(batch_sum / steps, 1),
-            "preemptions": preempted, "prefill_tokens_written": prefill,
+            "preemptions": preempted + swapped, "dropped": preempted, "swapped_out": swapped,
+            "blocks_swapped_out": blocks_out, "blocks_swapped_in": blocks_in,
+            "swap_bytes": (blocks_out + blocks_in) * block_bytes,
+            "prefill_tokens_written": prefill,
+            "prefill_tokens_recomputed": prefill - prompts,
             "kv_utilization": round(util_sum / steps, 4),
             "wall_s": round(wall, 3),
             "decode_tokens_per_s": round(tokens / wall, 1),
@@ -351,7 +401,9 @@ def run_serve(args, torch, np):
                    "requests": len(trace), "pool_blocks": N,
                    "max_running": args.serve_running},
         "paged": result["paged"],
+        "paged_swap": result["swap"],
         "reserve_max_len": result["reserve"],
+        "swap_blocks_probe": swap_probe,
         "paged_vs_reserve_steps": round(result["reserve"]["steps"] / result["paged"]["steps"],
                                         3),
         "paged_vs_reserve_mean_batch": round(result["paged"]["mean_batch"] /
