@@ -90,6 +90,62 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale=
     return out
 
 
+def query_starts(query_lens) -> np.ndarray:
+    """Offsets of each sequence's first query row in the packed query array."""
+    starts = np.zeros(len(query_lens) + 1, dtype=np.int64)
+    np.cumsum(np.asarray(query_lens, dtype=np.int64), out=starts[1:])
+    return starts
+
+
+def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, query_lens,
+                            scale=None, rows=None):
+    """Attention of several new tokens per sequence over the paged cache
+    (chunked prefill, and the uncached rest of a prompt after a prefix-cache
+    hit: PagedAttention: The vLLM Paper, "Impact and Follow-Ups").
+
+    Sequence s holds L_s = context_lens[s] cached tokens, the last Q_s =
+    query_lens[s] of which are this call's queries (their K/V are already in
+    the cache).  The query at position p = L_s - Q_s + i attends to tokens
+    0..p: each token attends over itself and every earlier token ("Background
+    and Motivation").  q packs the sequences' query rows [T, Hq, D], T = sum
+    Q_s, sequence by sequence in batch order.  Returns fp64 [T, Hq, D]; with
+    `rows` (a list of (packed row, head) pairs) only those are computed and the
+    rest are NaN."""
+    T, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    starts = query_starts(query_lens)
+    if starts[-1] != T:
+        raise ValueError("query rows must total sum(query_lens)")
+    out = np.full((T, Hq, D), np.nan)
+    want = None
+    if rows is not None:
+        want = {}
+        for t, h in rows:
+            want.setdefault(int(t), set()).add(int(h))
+    qf = to_f64(q)
+    for s in range(len(query_lens)):
+        L, Q = int(context_lens[s]), int(query_lens[s])
+        if not 0 <= Q <= L:
+            raise ValueError("each sequence needs 0 <= query_lens <= context_lens")
+        for g in range(Hkv):
+            K = V = None
+            for i in range(Q):
+                t = int(starts[s]) + i
+                heads = [h for h in range(g * G, (g + 1) * G)
+                         if want is None or h in want.get(t, ())]
+                if not heads:
+                    continue
+                if K is None:
+                    K, V = gather_kv(k_pool, v_pool, block_tables[s], L, g)
+                p = L - Q + i
+                for h in heads:
+                    out[t, h] = attention(qf[t, h], K[:p + 1], V[:p + 1], scale)
+    return out
+
+
 def partition_partials(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, P: int):
     """Split the context into partitions of P tokens and return, per partition,
     (m, l, acc): the max score, the sum of exp(score - m) and the unnormalised

@@ -248,3 +248,45 @@ def test_scheduler_swap_mutants_fail_pins(monkeypatch, cls):
         except (AssertionError, osched.BMError, IndexError, KeyError, ValueError):
             failed += 1
     assert failed > 0
+
+
+# --- multi-token (prefill) reference -------------------------------------------
+from tests import test_oracle_prefill as tp
+
+
+def _mutant_prefill(shift=0, top_left=False):
+    def prefill(q, k_pool, v_pool, block_tables, context_lens, query_lens, scale=None,
+                rows=None):
+        T, Hq, D = q.shape
+        Hkv = k_pool.shape[1]
+        G = Hq // Hkv
+        scale = 1.0 / np.sqrt(D) if scale is None else scale
+        out = np.full((T, Hq, D), np.nan)
+        starts = oa.query_starts(query_lens)
+        qf = oa.to_f64(q)
+        for s in range(len(query_lens)):
+            L, Q = int(context_lens[s]), int(query_lens[s])
+            for g in range(Hkv):
+                K, V = oa.gather_kv(k_pool, v_pool, block_tables[s], L, g)
+                for i in range(Q):
+                    p = (i if top_left else L - Q + i) + shift
+                    p = max(0, min(p, L - 1))
+                    for h in range(g * G, (g + 1) * G):
+                        out[starts[s] + i, h] = oa.attention(qf[starts[s] + i, h], K[:p + 1],
+                                                             V[:p + 1], scale)
+        return out
+    return prefill
+
+
+@pytest.mark.parametrize("mutant", ["minus_one", "top_left"])
+def test_prefill_mutants_fail_pins(monkeypatch, mutant):
+    fn = _mutant_prefill(shift=-1) if mutant == "minus_one" else _mutant_prefill(top_left=True)
+    monkeypatch.setattr(tp, "paged_attention_prefill", fn)
+    failed = 0
+    for t in (lambda: tp.test_prefill_equals_masked_sdpa("bf16", 16, 4),
+              tp.test_brute_force_scalar_loops, tp.test_one_query_per_sequence_is_decode):
+        try:
+            t()
+        except AssertionError:
+            failed += 1
+    assert failed > 0
