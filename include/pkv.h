@@ -322,6 +322,36 @@ pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int
                            int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
                            pkv_dtype dtype, void* hip_stream);
 
+/* Multi-token queries over the paged cache: chunked prefill, and the
+ * uncached rest of a prompt after a prefix-cache hit ([ZENO] "Impact and
+ * Follow-Ups": prefix caching reuses a cached prompt prefix so only the rest
+ * is prefilled; chunked prefill splits long prompts into chunks interleaved
+ * with decode).  Sequence s holds L_s = context_lens[s] cached tokens; the
+ * last Q_s = query_start[s+1] - query_start[s] of them are this call's queries
+ * (their K/V already written, e.g. by pkv_reshape_and_cache).  The query at
+ * position p = L_s - Q_s + i attends causally to tokens 0..p ([ZENO]
+ * "Background and Motivation"):
+ *   out[row, h] = softmax(q[row, h] . K_s[0..p]^T * scale) V_s[0..p]
+ *   out           device fp32 [T, Hq, D]; rows of sequence s are
+ *                 query_start[s] .. query_start[s+1]-1
+ *   q             device bf16 [T, Hq, D], same row packing
+ *   query_start   device int32 [S+1], non-decreasing, query_start[S] <= T; a
+ *                 sequence whose rows fall outside [0, T) gets none written
+ *   context_lens  device int32 [S]; Q_s is clamped to L_s (a sequence with
+ *                 more rows than tokens gets only its last L_s rows written)
+ *   max_query_len host bound on Q_s (sizes the grid)
+ *   block_tables, max_blocks, num_blocks, Hq, Hkv, scale as for decode.
+ * bf16 pools only, D in {64, 128}, B in {16, 32}, Hq/Hkv in {1, 2, 4, 8};
+ * others PKV_EUNSUPPORTED.  A query of one token per sequence is decode (the
+ * result matches pkv_paged_attention_decode's rows). */
+pkv_status pkv_paged_attention_prefill(float* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* query_start,
+                                       int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t B, int32_t max_blocks, int32_t num_blocks,
+                                       int32_t max_query_len, float scale, pkv_dtype dtype,
+                                       void* hip_stream);
+
 /* Block copies between two pools of the same geometry, one of which is usually
  * a host pool ([ZENO] "The Core Idea", OS-paging analogy table, "Swapping": KV
  * blocks moved to CPU memory and back; [ZENO] "Implementation Essentials").

@@ -19,7 +19,7 @@ import torch  # imported before the library so both share torch's HIP runtime
 
 __all__ = [
     "PkvError", "BlockManager", "Scheduler", "pkv_reshape_and_cache", "pkv_copy_blocks",
-    "pkv_swap_blocks", "swap_blocks",
+    "pkv_swap_blocks", "swap_blocks", "pkv_paged_attention_prefill", "paged_attention_prefill",
     "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pkv_paged_attention_main",
     "pkv_paged_attention_reduce", "pool_shapes", "paged_attention_main", "paged_attention_reduce",
     "pkv_attention_plan", "pkv_attention_plan_words", "attention_plan", "attention_plan_words",
@@ -101,6 +101,8 @@ SIGNATURES = {
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "pkv_swap_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                _i32, _vp]),
     "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -493,6 +495,35 @@ def pkv_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
                                _stream(stream)), "pkv_swap_blocks")
 
 
+def pkv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                                max_query_len: int, scale=None, stream=None) -> None:
+    """Causal attention of each sequence's last Q_s tokens over the paged cache:
+    q and out [T, Hq, D] packed by query_start (int32 [S+1]); Q_s =
+    query_start[s+1] - query_start[s]."""
+    N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
+    T, Hq = q.shape[0], q.shape[1]
+    S = context_lens.shape[0]
+    if tuple(q.shape) != (T, Hq, D) or tuple(out.shape) != (T, Hq, D):
+        raise ValueError("q and out must be [T, Hq, D]")
+    if out.dtype != torch.float32 or q.dtype != k_pool.dtype:
+        raise ValueError("out must be fp32 and q in the pool dtype")
+    if query_start.dtype != torch.int32 or tuple(query_start.shape) != (S + 1,):
+        raise ValueError("query_start must be int32 [S + 1]")
+    if context_lens.dtype != torch.int32 or block_tables.dtype != torch.int32 or \
+            block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S, max_blocks], context_lens int32 [S]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if S == 0 or T == 0:
+        return
+    _check(lib.pkv_paged_attention_prefill(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        _dev(query_start, "query_start"), S, T, Hq, Hkv, D, B, block_tables.shape[1], N,
+        int(max_query_len), float(scale), _dtype_code(k_pool), _stream(stream)),
+        "pkv_paged_attention_prefill")
+
+
 def pkv_attention_workspace_bytes(S: int, Hq: int, D: int, max_context_len: int,
                                   partition_size: int = 0) -> int:
     return int(lib.pkv_attention_workspace_bytes(S, Hq, D, max_context_len, partition_size))
@@ -634,6 +665,7 @@ def pkv_paged_attention_reduce(out, context_lens, Hkv: int, B: int, max_blocks: 
 reshape_and_cache = pkv_reshape_and_cache
 copy_blocks = pkv_copy_blocks
 swap_blocks = pkv_swap_blocks
+paged_attention_prefill = pkv_paged_attention_prefill
 attention_workspace_bytes = pkv_attention_workspace_bytes
 paged_attention_decode = pkv_paged_attention_decode
 paged_attention_main = pkv_paged_attention_main

@@ -60,6 +60,7 @@
 #include "../../include/pkv.h"
 #include "decode_config.h"
 #include "device_common.h"
+#include "kv_tiles.h"
 #include "launch_check.h"
 
 namespace pkv {
@@ -149,24 +150,6 @@ __device__ __forceinline__ bool item_extent(const DecodeArgs& a, WorkItem& it, i
   return true;
 }
 
-// Physical block ids of up to 64 consecutive logical blocks, one per lane: each
-// table entry is read from memory once per wave and taken as a scalar with
-// readlane when its block is loaded.  A partition spans at most 64 blocks.
-struct TableWindow {
-  int base, v;
-  __device__ __forceinline__ void load(const int* row, int b, int limit) {
-    base = b;
-    const int i = b + (int)(threadIdx.x & (kWave - 1));
-    v = i < limit ? row[i] : 0;
-  }
-  // Block of logical block lb (wave-uniform, base <= lb < base + 64), clamped
-  // into the pool so a corrupt entry can never address outside it.
-  __device__ __forceinline__ int at(int lb, int num_blocks) const {
-    const int pb = __builtin_amdgcn_readlane(v, lb - base);
-    return min(max(pb, 0), num_blocks - 1);
-  }
-};
-
 // Where an item's result row for query head h goes: the output (the item covers
 // the whole sequence) or its partition's partial slot.
 struct RowSink {
@@ -181,62 +164,6 @@ __device__ __forceinline__ RowSink row_sink(const DecodeArgs& a, const WorkItem&
   if (it.nps == 1) return RowSink{a.out + h * D, nullptr};
   const size_t row = h * a.nparts + it.p;
   return RowSink{a.part_acc + row * D, a.part_ml + 2 * row};
-}
-
-// A 16- or 8-byte vector load of pool data: nontemporal when the step streams
-// the pool (every block read once), ordinary when blocks are shared by several
-// sequences of the batch and a second read can hit in L2 or the last-level cache.
-template <bool NT, typename V>
-__device__ __forceinline__ V pool_load(const uint16_t* p) {
-  const V* v = reinterpret_cast<const V*>(p);
-  if constexpr (NT)
-    return __builtin_nontemporal_load(v);
-  else
-    return *v;
-}
-template <bool NT, typename V>
-__device__ __forceinline__ V pool_load(const float* p) {
-  const V* v = reinterpret_cast<const V*>(p);
-  if constexpr (NT)
-    return __builtin_nontemporal_load(v);
-  else
-    return *v;
-}
-
-// Run `compute(k, tile)` over a wave's n tiles with the loads of tile k+1 issued
-// before tile k is computed.  Two register buffers alternate; every load in the
-// steady loop is unconditional, so the compiler's wait before each compute only
-// covers the tile it needs.  Two hooks that the steady loop never runs (so they
-// add no code to it): `first()` once the first tile's loads are issued, and
-// `last(k, tile)` in place of compute for the final tile.
-struct NoHook {
-  __device__ void operator()() const {}
-};
-template <typename Tile, typename Load, typename Compute, typename First, typename Last>
-__device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute, First&& first,
-                                          Last&& last) {
-  if (n <= 0) return;
-  Tile ta, tb;
-  load(0, ta);
-  first();
-  int k = 0;
-  for (; k + 2 < n; k += 2) {
-    load(k + 1, tb);
-    compute(k, ta);
-    load(k + 2, ta);
-    compute(k + 1, tb);
-  }
-  if (k + 1 < n) {
-    load(k + 1, tb);
-    compute(k, ta);
-    last(k + 1, tb);
-  } else {
-    last(k, ta);
-  }
-}
-template <typename Tile, typename Load, typename Compute>
-__device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute) {
-  pipelined<Tile>(n, load, compute, NoHook{}, compute);
 }
 
 // ---------------------------------------------------------------------------

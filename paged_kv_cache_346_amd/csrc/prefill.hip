@@ -1,0 +1,286 @@
+// Multi-token queries over the paged KV cache for gfx950 (CDNA4): chunked
+// prefill, and the uncached rest of a prompt after a prefix-cache hit
+// (PagedAttention: The vLLM Paper, "Impact and Follow-Ups": prefix caching
+// reuses the KV of a shared prompt prefix so only the rest is prefilled;
+// chunked prefill splits a long prompt into chunks interleaved with decode).
+//
+// What is computed: sequence s holds L_s cached tokens, the last Q_s of which
+// are this call's queries (their K/V are already in the cache).  The query at
+// position p = L_s - Q_s + i attends causally to tokens 0..p ("Background and
+// Motivation": each token attends over itself and every earlier token):
+//   out[row, h] = softmax(q[row, h] . K_s[0..p]^T * scale) V_s[0..p]
+// with query head h reading KV head h / G.  Rows are packed sequence by
+// sequence: sequence s owns rows query_start[s] .. query_start[s+1]-1.
+//
+// Work decomposition (not on the pages).  One wave64 owns a (sequence, KV head,
+// query group) item, where a query group is 16/G consecutive query tokens: the
+// 16 columns of v_mfma_f32_16x16x32_bf16 hold (token, head) pairs, 16/G tokens
+// times the G heads of the KV head, so the matrix core is full for every G.
+// The wave walks the sequence's KV from token 0 to its last query's position in
+// 32-token tiles, exactly as the decode kernel's tile loop does (same operand
+// layouts, same base-2 online softmax, same bf16 hi + lo split of P); each
+// column masks the tokens after its own position (causal), and the block table
+// is read in windows of 64 entries, one per lane.  Query groups are numbered
+// from the end of each sequence's chunk, so the items with the longest KV range
+// are dispatched first.  Every group of a sequence reads the same prefix, so
+// K/V use ordinary cached loads: the re-reads are served from L2 or the
+// last-level cache.
+#include <cmath>
+#include <type_traits>
+
+#include "../../include/pkv.h"
+#include "device_common.h"
+#include "kv_tiles.h"
+#include "launch_check.h"
+
+namespace pkv {
+
+struct PrefillArgs {
+  float* out;                 // [T, Hq, D]
+  const int* block_tables;    // [S, max_blocks]
+  const int* context_lens;    // [S]
+  const int* query_start;     // [S + 1]
+  int S, Hkv, T, max_blocks, num_blocks, groups;
+  float scale_log2e;
+};
+
+template <int D, int B, int G>
+__global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(PrefillArgs a,
+                                                              const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k_pool,
+                                                              const uint16_t* __restrict__ v_pool) {
+  constexpr int TILE = 32;
+  constexpr int NJ = D / 32;   // q.k k-steps
+  constexpr int NDT = D / 16;  // p.v output dim tiles
+  constexpr int QT = 16 / G;   // query tokens per item
+  static_assert(16 % G == 0 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane >> 4, r = lane & 15;
+  const int SG = a.S * a.Hkv;
+  const int k_end = (int)blockIdx.x / SG;  // query group counted from the chunk's end
+  const int sg = (int)blockIdx.x - k_end * SG;
+  const int s = sg / a.Hkv, g = sg - s * a.Hkv;
+  const int Hq = a.Hkv * G;
+
+  const int row0 = a.query_start[s];
+  const int row1 = a.query_start[s + 1];
+  const int L = min(a.context_lens[s], a.max_blocks * B);
+  if (row0 < 0 || row1 > a.T || row1 < row0) return;  // a malformed offset: no rows
+  const int Q = min(row1 - row0, L);
+  if (Q <= 0) return;
+  const int rbase = row1 - Q;  // row of query 0 (rows past L_s leave the first ones out)
+  const int qg = (Q + QT - 1) / QT - 1 - k_end;
+  if (qg < 0) return;
+
+  // column r: query token qi (the last valid one stands in past the chunk's
+  // end; those columns are computed but not written) and head gi
+  const int qi_raw = qg * QT + r / G;
+  const bool col_valid = qi_raw < Q;
+  const int qi = min(qi_raw, Q - 1);
+  const int gi = r % G;
+  const int pos = L - Q + qi;                       // this column's last visible token
+  const int end = L - Q + min(qg * QT + QT, Q);     // one past the group's last position
+  const int first_pos = L - Q + qg * QT;            // smallest position of the group
+
+  bf16x8 qb[NJ];
+  {
+    const uint16_t* qrow = q + ((size_t)(rbase + qi) * Hq + g * G + gi) * D;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      qb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * j + c)));
+  }
+
+  float m = -INFINITY, ls = 0.f;
+  f32x4 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Tile {
+    u32x4 k[2][NJ];
+    u32x2 v[2][NDT];
+  };
+  const size_t head_off = (size_t)g * (D * B);
+  const size_t blk_stride = (size_t)a.Hkv * (D * B);
+  const int* table = a.block_tables + (size_t)s * a.max_blocks;
+  TableWindow tw;
+
+  // windows of 64 table entries (64 * B tokens, a whole number of tiles)
+  for (int w0 = 0; w0 * B < end; w0 += kWave) {
+    tw.load(table, w0, a.max_blocks);
+    const int tok0 = w0 * B;
+    const int wend = min(end, (w0 + kWave) * B);
+    const int n = (wend - tok0 + TILE - 1) / TILE;
+    const int nb_last = (wend + B - 1) / B - 1;  // last logical block of the window's range
+
+    auto load = [&](int k, Tile& tl) {
+      const int lb0 = (tok0 + k * TILE) / B;
+      const int pb0 = tw.at(lb0, a.num_blocks);
+      // B = 16: the tile's second block; past the range end it repeats the
+      // first (those tokens are masked)
+      const int pb1 = B == 16 ? tw.at(min(lb0 + 1, nb_last), a.num_blocks) : pb0;
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        const size_t blk = (B == 16 && th == 1) ? pb1 : pb0;
+        const int tok = (B == 16 ? 0 : 16 * th);
+        const uint16_t* kb = k_pool + blk * blk_stride + head_off;
+        const uint16_t* vb = v_pool + blk * blk_stride + head_off;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          tl.k[th][j] = *reinterpret_cast<const u32x4*>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          tl.v[th][dt] = *reinterpret_cast<const u32x2*>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+      }
+    };
+
+    auto compute = [&](int k, Tile& tl) {
+      const int T0 = tok0 + k * TILE;
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, tl.k[th][j]), qb[j], sacc[th], 0, 0, 0);
+      // sv[4th + i]: token T0 + 16th + 4c + i of column r
+      float sv[8];
+#pragma unroll
+      for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * a.scale_log2e;
+      if (T0 + TILE > first_pos + 1) {  // a tile some column cannot see all of
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+          // tokens this lane's column may see, and tokens that exist at all
+          const int base = T0 + 16 * th + 4 * c;
+          const int nv = min(max(pos + 1 - base, 0), 4);
+          const int ne = min(max(end - base, 0), 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i >= nv) sv[4 * th + i] = -INFINITY;
+          // V rows past the range end may hold anything (NaN): zero them so a
+          // zero weight cannot turn into NaN in the product
+#pragma unroll
+          for (int wd = 0; wd < 2; ++wd) {
+            const uint32_t mk =
+                (2 * wd < ne ? 0x0000ffffu : 0u) | (2 * wd + 1 < ne ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt][wd] &= mk;
+          }
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      // finite: token 0 is visible to every column, so the first tile sets a
+      // finite max and a later fully masked tile keeps it
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      u32x4 phw, plw;
+      float psum = 0.f;
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const float p0 = fast_exp2(sv[2 * wd] - mn);
+        const float p1 = fast_exp2(sv[2 * wd + 1] - mn);
+        psum += p0 + p1;
+        const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
+        const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
+        const uint32_t l0 = f32_to_bf16_rne(p0 - __uint_as_float(h0));
+        const uint32_t l1 = f32_to_bf16_rne(p1 - __uint_as_float(h1));
+        phw[wd] = (h0 >> 16) | h1;
+        plw[wd] = l0 | (l1 << 16);
+      }
+      ls = ls * alpha + psum;
+      const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const u32x4 va = {tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
+        acc[dt] *= alpha;
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), ph,
+                                                          acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pl,
+                                                          acc[dt], 0, 0, 0);
+      }
+    };
+
+    pipelined<Tile>(n, load, compute);
+  }
+
+  ls += shfl_xor_f(ls, 16);
+  ls += shfl_xor_f(ls, 32);
+  if (col_valid) {
+    float* dst = a.out + ((size_t)(rbase + qi) * Hq + g * G + gi) * D;
+    const float scl = 1.f / ls;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * c) = acc[dt] * scl;
+  }
+}
+
+template <int D, int B>
+static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, const void* q,
+                             const void* kp, const void* vp, hipStream_t st) {
+  const uint16_t* qq = (const uint16_t*)q;
+  const uint16_t* kk = (const uint16_t*)kp;
+  const uint16_t* vv = (const uint16_t*)vp;
+  switch (G) {
+    case 1: pa_prefill_kernel<D, B, 1><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    case 2: pa_prefill_kernel<D, B, 2><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    case 4: pa_prefill_kernel<D, B, 4><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    case 8: pa_prefill_kernel<D, B, 8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    default: return false;
+  }
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status pkv_paged_attention_prefill(
+    float* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+    int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
+    int32_t num_blocks, int32_t max_query_len, float scale, pkv_dtype dtype, void* hip_stream) {
+  if (S < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || max_blocks <= 0 ||
+      num_blocks <= 0 || max_query_len < 0 || !(scale > 0.f) || Hq % Hkv != 0)
+    return PKV_EINVAL;
+  if (dtype != PKV_BF16 && dtype != PKV_F32) return PKV_EINVAL;
+  const int G = Hq / Hkv;
+  if (dtype != PKV_BF16 || (D != 64 && D != 128) || (B != 16 && B != 32) ||
+      (G != 1 && G != 2 && G != 4 && G != 8))
+    return PKV_EUNSUPPORTED;
+  if (S == 0 || T == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start ||
+      !aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_EINVAL;
+  const int QT = 16 / G;
+  const int64_t groups = (max_query_len + QT - 1) / QT;
+  const int64_t items = groups * S * Hkv;
+  if (items > 0x7fffffffLL) return PKV_EINVAL;
+  PrefillArgs a;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.S = S;
+  a.Hkv = Hkv;
+  a.T = T;
+  a.max_blocks = max_blocks;
+  a.num_blocks = num_blocks;
+  a.groups = (int)groups;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const unsigned grid = (unsigned)items;
+  const bool ok = D == 64 ? (B == 16 ? launch_prefill_g<64, 16>(G, a, grid, q, k_pool, v_pool, st)
+                                     : launch_prefill_g<64, 32>(G, a, grid, q, k_pool, v_pool, st))
+                          : (B == 16 ? launch_prefill_g<128, 16>(G, a, grid, q, k_pool, v_pool, st)
+                                     : launch_prefill_g<128, 32>(G, a, grid, q, k_pool, v_pool, st));
+  if (!ok) return PKV_EUNSUPPORTED;
+  return launch_status();
+}

@@ -99,6 +99,27 @@ def test_swap_blocks_validation(pkv):
     assert lib.pkv_swap_blocks(*args(fake, 1)) == pkv.PKV_EINVAL
 
 
+def test_prefill_validation(pkv):
+    """Host-side checks of pkv_paged_attention_prefill (nothing here launches)."""
+    lib = pkv.lib
+    fake = ctypes.c_void_p(4096)
+
+    def call(S=2, T=8, Hq=8, Hkv=2, D=128, B=16, mq=4, scale=0.1, dtype=1, odd=False):
+        out = ctypes.c_void_p(4098) if odd else fake
+        return lib.pkv_paged_attention_prefill(out, fake, fake, fake, fake, fake, fake, S, T, Hq,
+                                               Hkv, D, B, 4, 16, mq, scale, dtype, None)
+    assert call(dtype=0) == pkv.PKV_EUNSUPPORTED          # fp32 pools
+    assert call(Hq=48, Hkv=3) == pkv.PKV_EUNSUPPORTED     # G = 16
+    assert call(D=96) == pkv.PKV_EUNSUPPORTED
+    assert call(B=8) == pkv.PKV_EUNSUPPORTED
+    assert call(Hq=6, Hkv=4) == pkv.PKV_EINVAL           # Hq not a multiple of Hkv
+    assert call(scale=0.0) == pkv.PKV_EINVAL
+    assert call(dtype=5) == pkv.PKV_EINVAL
+    assert call(odd=True) == pkv.PKV_EINVAL               # misaligned output
+    assert call(S=0) == pkv.PKV_OK and call(T=0) == pkv.PKV_OK and call(mq=0) == pkv.PKV_OK
+    assert call(mq=-1) == pkv.PKV_EINVAL
+
+
 def test_workspace_size_formula(pkv):
     f = pkv.pkv_attention_workspace_bytes
     assert f(256, 32, 128, 512, 0) == 0                 # one partition: no workspace
