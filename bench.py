@@ -417,6 +417,74 @@ def run_serve(args, torch, np):
     return 0
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, AMD's published figure
+
+
+def run_prefill(args, torch, np):
+    """Multi-token queries (chunked prefill) over the paged cache: S sequences of
+    the Llama-3-8B-shaped layer, each with a cached prefix and a chunk of new
+    tokens attending causally over prefix + chunk.  One JSON line (not the
+    headline metric); the kernel is timed with HIP events on its launch stream."""
+    import paged_kv_cache_346_amd as pkv
+
+    Hq, Hkv, D, B = 32, 8, 128, 16
+    S, prefix, chunk = args.prefill_seqs, args.prefill_prefix, args.prefill_chunk
+    L = prefix + chunk
+    nb = -(-L // B)
+    N = S * nb
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2027)
+    ks, vs = pkv.pool_shapes(N, Hkv, D, B, torch.bfloat16)
+    k = torch.randn(ks, generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn(vs, generator=gen, device=dev).to(torch.bfloat16)
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(3)).to(torch.int32)
+    tables = perm.view(S, nb).to(dev)
+    lens = torch.full((S,), L, dtype=torch.int32, device=dev)
+    starts = (torch.arange(S + 1, dtype=torch.int32) * chunk).to(dev)
+    T = S * chunk
+    q = torch.randn((T, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    call = lambda: pkv.paged_attention_prefill(out, q, k, v, tables, lens, starts, chunk)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    # two contractions (q.K and p.V) of D multiply-adds per (row, head, visible token)
+    visible = sum(prefix + i + 1 for i in range(chunk))
+    flops = 4.0 * D * Hq * S * visible
+    tflops = flops / (us * 1e-6) / 1e12
+    kv_bytes = S * L * Hkv * D * 2 * 2
+    rec = {
+        "metric": "multi-token query (chunked prefill) attention TFLOP/s",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "higher_is_better": True,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{S} sequences x ({prefix} cached + {chunk} new tokens), Llama-3-"
+                               f"8B-shaped layer (32/8 heads, D 128, B 16, bf16), causal over "
+                               f"prefix + chunk", "seqs": S, "prefix": prefix, "chunk": chunk},
+        "kernel_us": round(us, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "pa_prefill_kernel", "algorithmic_flops_per_launch": flops},
+        "kv_bytes_per_launch": kv_bytes,
+    }
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,6 +505,11 @@ def main() -> int:
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--serve", action="store_true",
                     help="run the continuous-batching loop over a request trace instead")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time multi-token queries (chunked prefill) instead")
+    ap.add_argument("--prefill-seqs", type=int, default=16)
+    ap.add_argument("--prefill-prefix", type=int, default=1536)
+    ap.add_argument("--prefill-chunk", type=int, default=512)
     ap.add_argument("--serve-requests", type=int, default=1024)
     ap.add_argument("--serve-running", type=int, default=1024)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -463,6 +536,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.serve:
         return run_serve(args, torch, np)
+    if args.prefill:
+        return run_prefill(args, torch, np)
     import paged_kv_cache_346_amd as pkv
     import workloads as W
 
