@@ -158,6 +158,33 @@ pkv_status pkv_bm_count_shared(const pkv_bm* bm, const int64_t* seq_ids, int32_t
 pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_queue,
                            int32_t* n_free);
 
+/* Prefix caching ([ZENO] "Impact and Follow-Ups": the KV of a shared prompt
+ * prefix is cached and reused across requests, so on a hit that part of the
+ * prefill is free; [ZENO] "Implementation Essentials": prefix sharing through
+ * block refcounts).  Semantics fixed by this library where the pages are
+ * silent:
+ *   - a full block is identified by the token ids of the whole prefix up to
+ *     its end (exact match, no hash collisions);
+ *   - pkv_bm_add_seq_prefix admits seq_id with num_tokens tokens whose first
+ *     n_ids ids are tokens[0..n_ids).  Walking its full blocks from logical
+ *     block 0 it reuses the cached block of each prefix while one exists
+ *     (refcount + 1; a cached block with refcount 0 leaves the free queue), at
+ *     most (num_tokens - 1) / B blocks so at least one token is left to
+ *     compute; the remaining blocks are taken as add_seq takes them.  Every
+ *     full block the ids cover that no block holds yet is then registered: the
+ *     caller must write tokens [*cached, num_tokens) before anything reads
+ *     them.  *cached = reused tokens (a multiple of B).  All-or-nothing:
+ *     PKV_ENOBLOCKS when the free queue, less the hits taken out of it, is too
+ *     short; PKV_EEXIST for a known id; PKV_EINVAL when num_tokens < n_ids;
+ *   - a cached block stays cached while in use and after it is freed, until
+ *     the free queue hands it out for other content (the least recently freed
+ *     cached block goes first).
+ * Token ids are only compared, never interpreted. */
+pkv_status pkv_bm_add_seq_prefix(pkv_bm* bm, int64_t seq_id, const int32_t* tokens,
+                                 int32_t n_ids, int32_t num_tokens, int32_t* cached);
+/* Number of blocks currently registered in the prefix cache. */
+pkv_status pkv_bm_cached_blocks(const pkv_bm* bm, int32_t* out);
+
 /* Swapping ([ZENO] "The Core Idea", OS-paging analogy table, "Swapping": KV
  * blocks go to CPU memory; [ZENO] "Implementation Essentials": preemption
  * swaps a request's blocks to the CPU).  Semantics fixed by this library where

@@ -46,6 +46,26 @@ blocks to the CPU).  Readings where the pages are silent:
   * both are all-or-nothing (too few free blocks on the destination side:
     ENOBLOCKS, no change); a swapped sequence cannot be appended to, forked or
     batched (EINVAL) but can be freed, and keeps its length.
+
+Prefix caching ("Impact and Follow-Ups": the KV of a shared prompt prefix is
+cached and reused across requests, so a hit makes that part of the prefill
+free; "Implementation Essentials": prefix sharing through block refcounts).
+Readings where the pages are silent:
+  * a full block's content is identified by the token ids of the whole prefix
+    up to its end (exact: no hash collisions can merge different prefixes);
+  * add_seq_prefix(s, tokens, n) admits a sequence of n tokens whose first
+    len(tokens) ids are known: walking its full blocks from logical block 0 it
+    reuses the cached block of each prefix while one exists (refcount + 1; a
+    cached block with refcount 0 is taken back out of the free queue), at most
+    (n - 1) // B blocks, so at least one token is always left to compute; the
+    rest are fresh blocks as in add_seq.  Every full block the known ids cover
+    is then registered as holding its prefix (the caller writes the new ones
+    before anything reads them).  Returns the number of cached tokens;
+  * a block stays cached while it is in use and after it is freed, until it is
+    taken from the free queue for other content (the queue order then makes
+    the least recently freed cached block the first to go);
+  * all-or-nothing: ENOBLOCKS when the free queue, after the hits are taken out
+    of it, holds fewer blocks than the rest needs.
 """
 from __future__ import annotations
 
@@ -73,6 +93,8 @@ class BlockManager:
         self.free = deque(order)
         self.tables = {}   # seq id -> list of physical block ids
         self.lens = {}     # seq id -> tokens held
+        self.cache = {}              # prefix token ids (tuple) -> block holding them
+        self.cached_key = {}         # block -> its prefix key, while cached
         self.NH = 0                  # host pool blocks
         self.host_free = deque()
         self.host_tables = {}        # swapped seq id -> list of host block ids
@@ -120,7 +142,49 @@ class BlockManager:
     def _take(self) -> int:
         b = self.free.popleft()
         self.ref[b] = 1
+        key = self.cached_key.pop(b, None)      # reused for other content
+        if key is not None:
+            del self.cache[key]
         return b
+
+    def add_seq_prefix(self, sid: int, tokens, num_tokens: int) -> int:
+        """Admit a sequence whose first len(tokens) token ids are known,
+        reusing cached full blocks of its prefix.  Returns the number of tokens
+        whose KV is already cached (a multiple of B)."""
+        tokens = [int(t) for t in tokens]
+        if num_tokens < len(tokens) or num_tokens < 0:
+            raise BMError(EINVAL, "num_tokens below the known ids")
+        if self._known(sid):
+            raise BMError(EEXIST)
+        B = self.B
+        full = len(tokens) // B                 # full blocks the ids cover
+        hits = []
+        for j in range(min(full, max(num_tokens - 1, 0) // B)):
+            b = self.cache.get(tuple(tokens[:(j + 1) * B]))
+            if b is None:
+                break
+            hits.append(b)
+        need = -(-num_tokens // B) - len(hits)
+        from_free = sum(1 for b in hits if self.ref[b] == 0)
+        if need > len(self.free) - from_free:
+            raise BMError(ENOBLOCKS)
+        for b in hits:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+        table = hits + [self._take() for _ in range(need)]
+        for j in range(len(hits), full):
+            key = tuple(tokens[:(j + 1) * B])
+            old = self.cache.get(key)
+            if old is None:
+                self.cache[key] = table[j]
+                self.cached_key[table[j]] = key
+        self.tables[sid] = table
+        self.lens[sid] = num_tokens
+        return len(hits) * B
+
+    def cached_blocks(self) -> int:
+        return len(self.cache)
 
     def add_seq(self, sid: int, num_tokens: int) -> None:
         if num_tokens < 0:

@@ -90,6 +90,8 @@ SIGNATURES = {
     "pkv_bm_block_table": (_i32, [_vp, _i64, _pi32, _i32]),
     "pkv_bm_fill_batch": (_i32, [_vp, _pi64, _i32, _i32, _pi32, _pi32]),
     "pkv_bm_snapshot": (_i32, [_vp, _pi32, _pi32, _pi32]),
+    "pkv_bm_add_seq_prefix": (_i32, [_vp, _i64, _pi32, _i32, _i32, _pi32]),
+    "pkv_bm_cached_blocks": (_i32, [_vp, _pi32]),
     "pkv_bm_set_host_pool": (_i32, [_vp, _i32]),
     "pkv_bm_num_free_host": (_i32, [_vp, _pi32]),
     "pkv_bm_is_swapped": (_i32, [_vp, _i64, _pi32]),
@@ -270,6 +272,22 @@ class BlockManager:
                                    _np_ptr(fq, ctypes.c_int32), ctypes.byref(nf)),
                "pkv_bm_snapshot")
         return ref.tolist(), fq[:nf.value].tolist()
+
+    # -- prefix cache ----------------------------------------------------------
+    def add_seq_prefix(self, seq_id: int, tokens, num_tokens: int) -> int:
+        """Admit a sequence whose first len(tokens) ids are known, reusing cached
+        full blocks of its prefix; returns the tokens already cached."""
+        ids = np.ascontiguousarray(tokens, dtype=np.int32)
+        out = _i32()
+        _check(lib.pkv_bm_add_seq_prefix(self._h, seq_id, _np_ptr(ids, ctypes.c_int32),
+                                         ids.shape[0], num_tokens, ctypes.byref(out)),
+               "pkv_bm_add_seq_prefix")
+        return out.value
+
+    def cached_blocks(self) -> int:
+        out = _i32()
+        _check(lib.pkv_bm_cached_blocks(self._h, ctypes.byref(out)), "pkv_bm_cached_blocks")
+        return out.value
 
     # -- swapping (host pool) ------------------------------------------------
     def set_host_pool(self, num_host_blocks: int) -> None:

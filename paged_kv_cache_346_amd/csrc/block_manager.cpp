@@ -8,16 +8,24 @@
 // arrive, copy-on-write of shared blocks).
 //
 // All integer work, O(1) per token except fork/free/swap (O(blocks of the
-// sequence)).  The free queue is a ring buffer of capacity num_blocks: a block
-// id is in it exactly when its refcount is zero, so it can never overflow.
+// sequence)).  The free queue is a doubly linked list threaded through two
+// arrays of num_blocks entries: a block id is in it exactly when its refcount
+// is zero, and a prefix-cache hit can take a block out of the middle in O(1).
 //
 // Swapping (PagedAttention: The vLLM Paper, "The Core Idea", OS-paging analogy
 // table, "Swapping"; "Implementation Essentials": preemption moves a request's
 // blocks to CPU memory): an optional host pool with the device pool's geometry
 // and its own FIFO free ring.  A swapped sequence keeps its length and holds
 // host block ids in its table until it is swapped back in or freed.
+//
+// Prefix caching (PagedAttention: The vLLM Paper, "Impact and Follow-Ups": the
+// KV of a shared prompt prefix is cached and reused across requests): a full
+// block is registered under the exact token ids of the whole prefix up to its
+// end, stays cached while in use and after it is freed, and loses its entry
+// when the free queue hands it out for other content.
 #include <cstring>
 #include <new>
+#include <string>
 #include <unordered_map>
 #include <vector>
 
@@ -31,24 +39,37 @@ struct pkv_bm {
   };
   int32_t N = 0, B = 0;
   std::vector<int32_t> ref;
-  std::vector<int32_t> ring;  // free queue: ring[(head + i) % N], i < nfree
-  int32_t head = 0, nfree = 0;
+  std::vector<int32_t> nxt, prv;  // free queue links (-1 = none), front at head
+  int32_t head = -1, tail = -1, nfree = 0;
+  std::unordered_map<std::string, int32_t> cache;  // prefix token ids -> block
+  std::vector<std::string> cached_key;             // block -> its key ("" = none)
   int32_t NH = 0;             // host pool: FIFO ring of its free blocks
   std::vector<int32_t> hring;
   int32_t hhead = 0, hnfree = 0;
   std::unordered_map<int64_t, Seq> seqs;
 
-  int32_t pop_free() {
-    int32_t b = ring[head];
-    head = (head + 1 == N) ? 0 : head + 1;
+  void unlink(int32_t b) {
+    if (prv[b] >= 0) nxt[prv[b]] = nxt[b]; else head = nxt[b];
+    if (nxt[b] >= 0) prv[nxt[b]] = prv[b]; else tail = prv[b];
+    nxt[b] = prv[b] = -1;
     --nfree;
+  }
+  // the front block, for new content: its cached prefix (if any) is dropped
+  int32_t pop_free() {
+    const int32_t b = head;
+    unlink(b);
     ref[b] = 1;
+    if (!cached_key[b].empty()) {
+      cache.erase(cached_key[b]);
+      cached_key[b].clear();
+    }
     return b;
   }
   void push_free(int32_t b) {
-    int32_t tail = head + nfree;
-    if (tail >= N) tail -= N;
-    ring[tail] = b;
+    prv[b] = tail;
+    nxt[b] = -1;
+    if (tail >= 0) nxt[tail] = b; else head = b;
+    tail = b;
     ++nfree;
   }
   int32_t pop_host() {
@@ -58,9 +79,9 @@ struct pkv_bm {
     return h;
   }
   void push_host(int32_t h) {
-    int32_t tail = hhead + hnfree;
-    if (tail >= NH) tail -= NH;
-    hring[tail] = h;
+    int32_t t = hhead + hnfree;
+    if (t >= NH) t -= NH;
+    hring[t] = h;
     ++hnfree;
   }
   void release(const std::vector<int32_t>& table) {
@@ -95,7 +116,9 @@ pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* 
   bm->N = num_blocks;
   bm->B = block_size;
   bm->ref.assign(num_blocks, 0);
-  bm->ring.resize(num_blocks);
+  bm->nxt.assign(num_blocks, -1);
+  bm->prv.assign(num_blocks, -1);
+  bm->cached_key.resize(num_blocks);
   if (init_free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -105,12 +128,11 @@ pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* 
         return PKV_EINVAL;
       }
       seen[b] = 1;
-      bm->ring[i] = b;
     }
+    for (int32_t i = 0; i < num_blocks; ++i) bm->push_free(init_free_order[i]);
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) bm->ring[i] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) bm->push_free(i);
   }
-  bm->nfree = num_blocks;
   *out = bm;
   return PKV_OK;
 }
@@ -127,6 +149,53 @@ pkv_status pkv_bm_add_seq(pkv_bm* bm, int64_t seq_id, int32_t num_tokens) {
   for (int32_t i = 0; i < need; ++i) s.table.push_back(bm->pop_free());
   s.len = num_tokens;
   bm->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_add_seq_prefix(pkv_bm* bm, int64_t seq_id, const int32_t* tokens,
+                                 int32_t n_ids, int32_t num_tokens, int32_t* cached) {
+  if (!bm || !cached || n_ids < 0 || num_tokens < n_ids || (n_ids > 0 && !tokens))
+    return PKV_EINVAL;
+  if (bm->seqs.count(seq_id)) return PKV_EEXIST;
+  const int32_t B = bm->B;
+  const int32_t full = n_ids / B;                      // full blocks the ids cover
+  const int32_t cap = (num_tokens > 0 ? num_tokens - 1 : 0) / B;  // leave a token to compute
+  const char* bytes = reinterpret_cast<const char*>(tokens);
+  auto key_of = [&](int32_t j) { return std::string(bytes, (size_t)(j + 1) * B * sizeof(int32_t)); };
+  std::vector<int32_t> hits;
+  for (int32_t j = 0; j < full && j < cap; ++j) {
+    auto it = bm->cache.find(key_of(j));
+    if (it == bm->cache.end()) break;
+    hits.push_back(it->second);
+  }
+  const int32_t need = num_tokens / B + (num_tokens % B != 0) - (int32_t)hits.size();
+  int32_t from_free = 0;
+  for (int32_t b : hits) from_free += bm->ref[b] == 0;
+  if (need > bm->nfree - from_free) return PKV_ENOBLOCKS;
+  for (int32_t b : hits) {
+    if (bm->ref[b] == 0) bm->unlink(b);
+    bm->ref[b] += 1;
+  }
+  pkv_bm::Seq s;
+  s.table = hits;
+  s.table.reserve(hits.size() + need + 1);
+  for (int32_t i = 0; i < need; ++i) s.table.push_back(bm->pop_free());
+  for (int32_t j = (int32_t)hits.size(); j < full; ++j) {
+    std::string key = key_of(j);
+    if (bm->cache.count(key)) continue;  // another block already holds this prefix
+    const int32_t b = s.table[j];
+    bm->cached_key[b] = key;
+    bm->cache.emplace(std::move(key), b);
+  }
+  s.len = num_tokens;
+  bm->seqs.emplace(seq_id, std::move(s));
+  *cached = (int32_t)hits.size() * B;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_cached_blocks(const pkv_bm* bm, int32_t* out) {
+  if (!bm || !out) return PKV_EINVAL;
+  *out = (int32_t)bm->cache.size();
   return PKV_OK;
 }
 
@@ -368,11 +437,8 @@ pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_q
                            int32_t* n_free) {
   if (!bm || !refcounts || !free_queue || !n_free) return PKV_EINVAL;
   std::memcpy(refcounts, bm->ref.data(), (size_t)bm->N * sizeof(int32_t));
-  for (int32_t i = 0; i < bm->nfree; ++i) {
-    int32_t k = bm->head + i;
-    if (k >= bm->N) k -= bm->N;
-    free_queue[i] = bm->ring[k];
-  }
+  int32_t i = 0;
+  for (int32_t b = bm->head; b >= 0; b = bm->nxt[b]) free_queue[i++] = b;
   *n_free = bm->nfree;
   return PKV_OK;
 }

@@ -193,3 +193,61 @@ def test_slots_rejects_tokens_past_the_length(pkv):
         bm.slots(0, 10, 11)
     with pytest.raises(pkv.PkvError):
         bm.slots(3, 0, 1)
+
+
+def _prefix_ops(rng, B, n_ops=300):
+    prompts = [list(map(int, rng.integers(0, 3, size=int(rng.integers(1, 6 * B)))))
+               for _ in range(4)]
+    ops = []
+    for _ in range(n_ops):
+        sid = int(rng.integers(0, 6))
+        r = rng.random()
+        if r < 0.3:
+            base = prompts[int(rng.integers(0, 4))]
+            tokens = base[:int(rng.integers(0, len(base) + 1))] + \
+                list(map(int, rng.integers(0, 3, size=int(rng.integers(0, 2 * B)))))
+            ops.append(("prefix", sid, tokens, len(tokens) + int(rng.integers(0, B + 1))))
+        elif r < 0.4:
+            ops.append(("add", sid, int(rng.integers(0, 3 * B))))
+        elif r < 0.8:
+            ops.append(("append", sid))
+        elif r < 0.88:
+            ops.append(("fork", sid, int(rng.integers(0, 6))))
+        else:
+            ops.append(("free", sid))
+    return ops
+
+
+def _apply(bm, op, err):
+    try:
+        if op[0] == "prefix":
+            return bm.add_seq_prefix(op[1], op[2], op[3])
+        if op[0] == "add":
+            return bm.add_seq(op[1], op[2])
+        if op[0] == "append":
+            return bm.append_slot(op[1])
+        if op[0] == "fork":
+            return bm.fork(op[1], op[2])
+        return bm.free_seq(op[1])
+    except err as e:
+        return ("error", e.code)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_prefix_cache_scripts_bit_exact(pkv, seed):
+    """Reused tokens, tables, refcounts, free-queue order and the number of
+    cached blocks against the reference after every op."""
+    from oracle.block_manager import BMError
+    rng = np.random.default_rng(5600 + seed)
+    B = int(rng.choice([1, 2, 4, 16]))
+    N = int(rng.integers(6, 60))
+    order = rng.permutation(N)
+    native, ref = pkv.BlockManager(N, B, order), RefBM(N, B, order)
+    for op in _prefix_ops(rng, B):
+        a = _apply(native, op, pkv.PkvError)
+        b = _apply(ref, op, BMError)
+        if isinstance(a, tuple) and len(a) == 3:
+            a = tuple(int(x) for x in a)
+        assert a == b, op
+        assert native.cached_blocks() == ref.cached_blocks()
+        assert_same_state(native, ref, range(6))

@@ -290,3 +290,74 @@ def test_prefill_mutants_fail_pins(monkeypatch, mutant):
         except AssertionError:
             failed += 1
     assert failed > 0
+
+
+# --- prefix cache ----------------------------------------------------------------
+from tests import test_oracle_prefix_cache as tpc
+
+
+class _NoCapBM(obm.BlockManager):
+    """Lets a hit cover the whole prompt, leaving no token to compute."""
+
+    def add_seq_prefix(self, sid, tokens, num_tokens):
+        tokens = [int(t) for t in tokens]
+        if self._known(sid):
+            raise obm.BMError(obm.EEXIST)
+        B = self.B
+        hits = []
+        for j in range(len(tokens) // B):
+            b = self.cache.get(tuple(tokens[:(j + 1) * B]))
+            if b is None:
+                break
+            hits.append(b)
+        need = -(-num_tokens // B) - len(hits)
+        if need > len(self.free) - sum(1 for b in hits if self.ref[b] == 0):
+            raise obm.BMError(obm.ENOBLOCKS)
+        for b in hits:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+        table = hits + [self._take() for _ in range(need)]
+        for j in range(len(hits), len(tokens) // B):
+            key = tuple(tokens[:(j + 1) * B])
+            if key not in self.cache:
+                self.cache[key] = table[j]
+                self.cached_key[table[j]] = key
+        self.tables[sid] = table
+        self.lens[sid] = num_tokens
+        return len(hits) * B
+
+
+class _HitStaysFreeBM(obm.BlockManager):
+    """Takes a cached block with refcount 0 without removing it from the free queue."""
+
+    def add_seq_prefix(self, sid, tokens, num_tokens):
+        free_before = list(self.free)
+        cached = super().add_seq_prefix(sid, tokens, num_tokens)
+        taken = [b for b in free_before if b not in self.free]
+        hits = self.tables[sid][:cached // self.B]
+        back = [b for b in taken if b in hits]
+        self.free.extendleft(reversed(back))        # the hits stay queued
+        return cached
+
+
+class _StaleCacheBM(obm.BlockManager):
+    """Reallocating a cached block keeps its old cache entry."""
+
+    def _take(self):
+        b = self.free.popleft()
+        self.ref[b] = 1
+        return b
+
+
+@pytest.mark.parametrize("cls", [_NoCapBM, _HitStaysFreeBM, _StaleCacheBM])
+def test_prefix_cache_mutants_fail_pins(monkeypatch, cls):
+    monkeypatch.setattr(tpc, "BlockManager", cls)
+    failed = 0
+    for t in [tpc.test_prefix_cache_worked_example] + \
+            [lambda s=s: tpc.run_prefix_script(s, cls) for s in range(6)]:
+        try:
+            t()
+        except (AssertionError, obm.BMError, KeyError, ValueError):
+            failed += 1
+    assert failed > 0
