@@ -170,18 +170,27 @@ pkv_status pkv_bm_snapshot(const pkv_bm* bm, int32_t* refcounts, int32_t* free_q
  *     block 0 it reuses the cached block of each prefix while one exists
  *     (refcount + 1; a cached block with refcount 0 leaves the free queue), at
  *     most (num_tokens - 1) / B blocks so at least one token is left to
- *     compute; the remaining blocks are taken as add_seq takes them.  Every
- *     full block the ids cover that no block holds yet is then registered: the
- *     caller must write tokens [*cached, num_tokens) before anything reads
- *     them.  *cached = reused tokens (a multiple of B).  All-or-nothing:
+ *     compute; the remaining blocks are taken as add_seq takes them.
+ *     *cached = reused tokens (a multiple of B).  All-or-nothing:
  *     PKV_ENOBLOCKS when the free queue, less the hits taken out of it, is too
  *     short; PKV_EEXIST for a known id; PKV_EINVAL when num_tokens < n_ids;
+ *   - pkv_bm_register_prefix registers each full block of the sequence that
+ *     the ids cover and that ends at or before token `upto`, unless another
+ *     block holds that prefix already.  Call it once that KV is written, or
+ *     will be written before anything reads it (a prefill chunk of the same
+ *     step); PKV_EINVAL when upto or n_ids exceeds the sequence's length;
+ *   - pkv_bm_unregister_prefix withdraws the sequence's own entries (blocks it
+ *     alone holds) for blocks ending after token `start`: KV that will not be
+ *     written after all (a prefill chunk withdrawn by preemption);
  *   - a cached block stays cached while in use and after it is freed, until
  *     the free queue hands it out for other content (the least recently freed
  *     cached block goes first).
  * Token ids are only compared, never interpreted. */
 pkv_status pkv_bm_add_seq_prefix(pkv_bm* bm, int64_t seq_id, const int32_t* tokens,
                                  int32_t n_ids, int32_t num_tokens, int32_t* cached);
+pkv_status pkv_bm_register_prefix(pkv_bm* bm, int64_t seq_id, const int32_t* tokens,
+                                  int32_t n_ids, int32_t upto);
+pkv_status pkv_bm_unregister_prefix(pkv_bm* bm, int64_t seq_id, int32_t start);
 /* Number of blocks currently registered in the prefix cache. */
 pkv_status pkv_bm_cached_blocks(const pkv_bm* bm, int32_t* out);
 
@@ -201,8 +210,8 @@ pkv_status pkv_bm_cached_blocks(const pkv_bm* bm, int32_t* out);
  *     block, in table order, pairs (host block, device block); then the host
  *     blocks return to the host free queue in table order;
  *   - both are all-or-nothing: PKV_ENOBLOCKS when the destination side has
- *     fewer free blocks than the table has entries, PKV_EINVAL when `cap`
- *     (pairs, i.e. 2*cap int32 entries) is too small, PKV_ENOSEQ for an unknown
+ *     fewer free blocks than the table has entries (checked first), else
+ *     PKV_EINVAL when `cap` (pairs, i.e. 2*cap int32 entries) is too small, PKV_ENOSEQ for an unknown
  *     id, PKV_EINVAL for the wrong side (swap_out of a swapped sequence, swap_in
  *     of a resident one); a failing call changes nothing;
  *   - a swapped sequence keeps its id and length (pkv_bm_seq_info works) and
@@ -262,6 +271,17 @@ pkv_status pkv_bm_host_snapshot(const pkv_bm* bm, int32_t* free_queue, int32_t* 
  *     swap_out_pairs (device to host; they may reuse host blocks the swap-ins
  *     released), then cow_pairs, then the prefill writes, then the token
  *     writes and attention;
+ *   - prefix caching and chunked prefill ([ZENO] "Impact and Follow-Ups"): a
+ *     request submitted with its prompt's token ids is admitted with
+ *     pkv_bm_add_seq_prefix and its cached tokens are not prefilled again (a
+ *     dropped request admitted again finds its prompt blocks the same way;
+ *     generated tokens are always recomputed).  With max_prefill_tokens > 0
+ *     each step first continues the prefills of admitted requests in admission
+ *     order, then admits new requests while budget is left, each getting a
+ *     chunk of at most the budget left; 0 means no limit (every prefill
+ *     completes in its admission step).  A request produces a token only in
+ *     steps where its prefill is complete, including the step of its last
+ *     chunk.  A preempted request's chunk of that step is withdrawn;
  *   - a request finishes in the step that produces its max_new-th token and is
  *     freed by pkv_sched_end_step, after the caller has read the step's tables.
  * Not thread-safe; one scheduler thread owns a handle.
@@ -277,14 +297,19 @@ enum { PKV_SCHED_RESERVE_MAX = 1, PKV_SCHED_SWAP = 2 };
  * their counts are 0. */
 typedef struct pkv_sched_step {
   int32_t capacity;
-  int64_t* batch_ids;      /* running requests after the step, admission order */
+  int64_t* batch_ids;      /* requests that produced a token, admission order */
   int64_t* slots;          /* slot of each one's new token (block*B + offset) */
   int32_t n_batch;
   int32_t* cow_pairs;      /* (src, dst) block copies to run before the writes */
   int32_t n_cow;
-  int64_t* admitted_ids;   /* admitted this step: prefill tokens [0, ctx) ... */
-  int32_t* admitted_ctx;   /* ... whose KV the caller writes before attention */
+  int64_t* admitted_ids;   /* admitted this step with context ctx, of which ... */
+  int32_t* admitted_ctx;
+  int32_t* admitted_cached;/* ... the first `cached` tokens are in the prefix cache */
   int32_t n_admitted;
+  int64_t* prefill_ids;    /* prefill chunks: tokens [start, start + len) of the */
+  int32_t* prefill_start;  /* request, whose KV the caller writes (and whose rows */
+  int32_t* prefill_len;    /* it attends) before the step's token writes */
+  int32_t n_prefill;
   int64_t* preempted_ids;  /* preempted this step (back in the waiting queue) */
   int32_t n_preempted;
   int64_t* finished_ids;   /* produced their last token this step */
@@ -301,14 +326,17 @@ typedef struct pkv_sched_step {
 } pkv_sched_step;
 
 /* policy: 0 (paged, preempt by dropping), PKV_SCHED_RESERVE_MAX, or
- * PKV_SCHED_SWAP; PKV_EINVAL for unknown bits or both. */
+ * PKV_SCHED_SWAP; PKV_EINVAL for unknown bits or both.  max_prefill_tokens:
+ * prefill budget per step, 0 = no limit. */
 pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t policy,
-                            pkv_sched** out);
+                            int32_t max_prefill_tokens, pkv_sched** out);
 void pkv_sched_destroy(pkv_sched* sched);
-/* Queue a request; PKV_EEXIST for a known id, PKV_EINVAL when prompt_len < 0,
- * max_new_tokens < 1 or its maximum length can never fit the pool. */
+/* Queue a request; tokens: NULL or its prompt's prompt_len token ids (copied;
+ * enables the prefix cache).  PKV_EEXIST for a known id, PKV_EINVAL when
+ * prompt_len < 0, max_new_tokens < 1 or its maximum length can never fit the
+ * pool. */
 pkv_status pkv_sched_add_request(pkv_sched* sched, int64_t req_id, int32_t prompt_len,
-                                 int32_t max_new_tokens);
+                                 int32_t max_new_tokens, const int32_t* tokens);
 /* One iteration (admissions, then one slot per running request).  Steps
  * alternate with pkv_sched_end_step; either one out of turn is PKV_EINVAL. */
 pkv_status pkv_sched_begin_step(pkv_sched* sched, pkv_sched_step* out);

@@ -58,9 +58,14 @@ Readings where the pages are silent:
     reuses the cached block of each prefix while one exists (refcount + 1; a
     cached block with refcount 0 is taken back out of the free queue), at most
     (n - 1) // B blocks, so at least one token is always left to compute; the
-    rest are fresh blocks as in add_seq.  Every full block the known ids cover
-    is then registered as holding its prefix (the caller writes the new ones
-    before anything reads them).  Returns the number of cached tokens;
+    rest are fresh blocks as in add_seq.  Returns the number of cached tokens;
+  * register_prefix(s, tokens, upto) registers each full block of the
+    sequence that the known ids cover and that ends at or before token `upto`,
+    unless another block already holds that prefix: the caller calls it once
+    that KV is written or about to be written before anything reads it (a
+    prefill chunk); unregister_prefix(s, start) withdraws the sequence's own
+    entries for blocks that end after token `start` (KV that will not be
+    written after all);
   * a block stays cached while it is in use and after it is freed, until it is
     taken from the free queue for other content (the queue order then makes
     the least recently freed cached block the first to go);
@@ -173,15 +178,32 @@ class BlockManager:
                 self.free.remove(b)
             self.ref[b] += 1
         table = hits + [self._take() for _ in range(need)]
-        for j in range(len(hits), full):
-            key = tuple(tokens[:(j + 1) * B])
-            old = self.cache.get(key)
-            if old is None:
-                self.cache[key] = table[j]
-                self.cached_key[table[j]] = key
         self.tables[sid] = table
         self.lens[sid] = num_tokens
         return len(hits) * B
+
+    def register_prefix(self, sid: int, tokens, upto: int) -> None:
+        self._resident(sid)
+        tokens = [int(t) for t in tokens]
+        if upto < 0 or upto > self.lens[sid] or len(tokens) > self.lens[sid]:
+            raise BMError(EINVAL, "tokens past the sequence's length")
+        table, B = self.tables[sid], self.B
+        for j in range(min(upto, len(tokens)) // B):
+            key = tuple(tokens[:(j + 1) * B])
+            if key not in self.cache and table[j] not in self.cached_key:
+                self.cache[key] = table[j]
+                self.cached_key[table[j]] = key
+
+    def unregister_prefix(self, sid: int, start: int) -> None:
+        self._resident(sid)
+        if start < 0:
+            raise BMError(EINVAL, "negative token index")
+        table = self.tables[sid]
+        for j in range(start // self.B, len(table)):
+            key = self.cached_key.get(table[j])
+            if key is not None and self.ref[table[j]] == 1:
+                del self.cache[key]
+                del self.cached_key[table[j]]
 
     def cached_blocks(self) -> int:
         return len(self.cache)

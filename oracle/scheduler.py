@@ -56,6 +56,29 @@ Swap policy (swap=True, over a block manager with a host pool):
     swap-outs (device to host: they may reuse host blocks the swap-ins just
     released), copy-on-write copies, prefill writes, then the token writes and
     attention.
+
+Prefix caching and chunked prefill ("Impact and Follow-Ups": a cached prompt
+prefix makes that part of the prefill free; long prompts are split into chunks
+interleaved with decode):
+  * a request may carry its prompt's token ids; it is then admitted with the
+    block manager's add_seq_prefix, and the tokens already cached are not
+    prefilled again (a request admitted again after being dropped finds its
+    prompt blocks the same way; its generated tokens are always recomputed);
+  * with a prefill budget of C tokens per step, each step first continues the
+    prefills of admitted requests in admission order, then admits new requests
+    while budget is left; each gets a chunk of at most the budget left.  No
+    budget (None) means every prefill completes in its admission step;
+  * a request produces a token only in steps where its prefill is complete,
+    including the step its last chunk runs in; the batch lists the requests
+    that produced a token;
+  * a chunk's full prompt blocks join the prefix cache when the chunk is
+    issued (the caller writes every chunk of a step before anything reads
+    them; a request admitted later in the same step may already reuse them);
+  * a preempted request's chunk of the same step is undone (its KV for that
+    chunk is never written) and its cache entries for it are withdrawn, so a
+    swapped request resumes its prefill where its written KV ends.  The
+    youngest request is preempted first, so any request that reused those
+    blocks in the same step is preempted before them.
 """
 from __future__ import annotations
 
@@ -72,6 +95,9 @@ class Request:
     max_new: int
     generated: int = 0
     reserved: int = 0   # blocks held by a reservation (reserve policy)
+    tokens: list | None = None   # prompt token ids, when known
+    target: int = 0     # context to prefill since the last admission
+    prefilled: int = 0  # tokens of it whose KV is written (or cached)
 
     @property
     def ctx(self) -> int:
@@ -80,15 +106,19 @@ class Request:
 
 
 class Scheduler:
-    def __init__(self, bm, max_running: int, reserve_max: bool = False, swap: bool = False):
+    def __init__(self, bm, max_running: int, reserve_max: bool = False, swap: bool = False,
+                 max_prefill_tokens: int | None = None):
         if max_running <= 0:
             raise BMError(EINVAL, "max_running must be positive")
+        if max_prefill_tokens is not None and max_prefill_tokens <= 0:
+            raise BMError(EINVAL, "the prefill budget must be positive")
         if reserve_max and swap:
             raise BMError(EINVAL, "the reserve policy never preempts")
         self.bm = bm
         self.max_running = max_running
         self.reserve_max = reserve_max
         self.swap = swap
+        self.max_prefill = max_prefill_tokens
         self.swapped: deque[Request] = deque()
         self.waiting: deque[Request] = deque()
         self.running: list[Request] = []
@@ -100,21 +130,26 @@ class Scheduler:
     def _blocks(self, tokens: int) -> int:
         return -(-tokens // self.bm.B)
 
-    def add_request(self, rid: int, prompt: int, max_new: int) -> None:
+    def add_request(self, rid: int, prompt: int, max_new: int, tokens=None) -> None:
         if prompt < 0 or max_new < 1:
             raise BMError(EINVAL, "prompt must be >= 0 and max_new >= 1")
+        if tokens is not None and len(tokens) != prompt:
+            raise BMError(EINVAL, "token ids must cover the prompt")
         if rid in self.known:
             raise BMError(EEXIST)
         if self._blocks(prompt + max_new) > self.bm.N:
             raise BMError(EINVAL, "request can never fit the pool")
         self.known.add(rid)
-        self.waiting.append(Request(rid, prompt, max_new))
+        self.waiting.append(Request(rid, prompt, max_new,
+                                    tokens=None if tokens is None else [int(t) for t in tokens]))
 
     def begin_step(self):
-        """One iteration: swap-ins, admissions, then one slot per running
-        request.  Returns dict(batch, slots, cow, admitted=[(rid, ctx)],
-        preempted (dropped), finished, swap_in=[(host, device)],
-        swap_out=[(device, host)], swapped_in, swapped_out)."""
+        """One iteration: swap-ins, prefill chunks and admissions, then one
+        slot per request whose prefill is complete.  Returns dict(batch (the
+        requests that produced a token), slots, cow, admitted=[(rid, ctx,
+        cached)], prefill=[(rid, start, n)], preempted (dropped), finished,
+        swap_in=[(host, device)], swap_out=[(device, host)], swapped_in,
+        swapped_out)."""
         if self.in_step:
             raise BMError(EINVAL, "end_step() was not called")
         self.in_step = True
@@ -131,14 +166,37 @@ class Scheduler:
             self.running.append(r)
             swapped_in.append(r.rid)
 
-        admitted: list[tuple[Request, int]] = []   # (request, context it was admitted with)
-        while self._may_admit() and self.waiting and len(self.running) < self.max_running:
+        # prefill chunks: admitted requests first, in admission order
+        budget = float("inf") if self.max_prefill is None else self.max_prefill
+        chunks: list[list] = []                     # [request, start, n]
+
+        def give_chunk(r):
+            nonlocal budget
+            n = int(min(r.target - r.prefilled, budget))
+            if n > 0:
+                chunks.append([r, r.prefilled, n])
+                r.prefilled += n
+                budget -= n
+                if r.tokens is not None:        # the chunk's full blocks join the cache
+                    self.bm.register_prefix(r.rid, r.tokens, r.prefilled)
+
+        for r in self.running:
+            if r.prefilled < r.target and budget > 0:
+                give_chunk(r)
+
+        admitted: list[tuple[Request, int, int]] = []   # (request, context, cached)
+        while self._may_admit() and self.waiting and len(self.running) < self.max_running \
+                and budget > 0:
             r = self.waiting[0]
             need_max = self._blocks(r.prompt + r.max_new)
             if self.reserve_max and self.reserved + need_max > self.bm.N:
                 break
             try:
-                self.bm.add_seq(r.rid, r.ctx)
+                if r.tokens is not None:
+                    cached = self.bm.add_seq_prefix(r.rid, r.tokens, r.ctx)
+                else:
+                    self.bm.add_seq(r.rid, r.ctx)
+                    cached = 0
             except BMError as e:
                 if e.code == ENOBLOCKS:
                     break
@@ -148,45 +206,59 @@ class Scheduler:
                 self.reserved += need_max
             self.waiting.popleft()
             self.running.append(r)
-            admitted.append((r, r.ctx))
+            r.target, r.prefilled = r.ctx, cached
+            admitted.append((r, r.ctx, cached))
+            give_chunk(r)
 
         slots, cow, preempted, swap_out, swapped_out = [], [], [], [], []
+        decoding: list[Request] = []
         i = 0
         while i < len(self.running):
             r = self.running[i]
+            if r.prefilled < r.target:              # still prefilling: no token this step
+                i += 1
+                continue
             try:
                 slot, src, dst = self.bm.append_slot(r.rid)
             except BMError as e:
                 if e.code != ENOBLOCKS:
                     raise
                 victim = self._victim()
-                fresh = any(a is victim for a, _ in admitted)
+                fresh = any(a is victim for a, _, _ in admitted)
+                for ch in chunks:                   # its chunk of this step is not written
+                    if ch[0] is victim:
+                        victim.prefilled -= ch[2]
+                        chunks.remove(ch)
+                        self.bm.unregister_prefix(victim.rid, victim.prefilled)
+                        break
                 if self._swap_victim(victim, fresh):
                     swap_out += self.bm.swap_out(victim.rid)
                     swapped_out.append(victim.rid)
                     self.swapped.appendleft(victim)
                     continue
                 self.bm.free_seq(victim.rid)
-                admitted = [(a, n) for a, n in admitted if a is not victim]
+                admitted = [a for a in admitted if a[0] is not victim]
                 preempted.append(victim.rid)
                 self.waiting.appendleft(victim)
                 continue
             slots.append(slot)
             if src >= 0:
                 cow.append((src, dst))
+            decoding.append(r)
             i += 1
 
         finished = []
-        for r in self.running:
+        for r in decoding:
             r.generated += 1
             if r.generated == r.max_new:
                 finished.append(r.rid)
                 self.finishing.append(r)
         return {
-            "batch": [r.rid for r in self.running],
+            "batch": [r.rid for r in decoding],
             "slots": slots,
             "cow": cow,
-            "admitted": [(r.rid, n) for r, n in admitted],
+            "admitted": [(r.rid, n, c) for r, n, c in admitted],
+            "prefill": [(r.rid, start, n) for r, start, n in chunks],
             "preempted": preempted,
             "finished": finished,
             "swap_in": swap_in,

@@ -51,7 +51,12 @@ class _SchedStep(ctypes.Structure):
                 ("n_cow", ctypes.c_int32),
                 ("admitted_ids", ctypes.POINTER(ctypes.c_int64)),
                 ("admitted_ctx", ctypes.POINTER(ctypes.c_int32)),
+                ("admitted_cached", ctypes.POINTER(ctypes.c_int32)),
                 ("n_admitted", ctypes.c_int32),
+                ("prefill_ids", ctypes.POINTER(ctypes.c_int64)),
+                ("prefill_start", ctypes.POINTER(ctypes.c_int32)),
+                ("prefill_len", ctypes.POINTER(ctypes.c_int32)),
+                ("n_prefill", ctypes.c_int32),
                 ("preempted_ids", ctypes.POINTER(ctypes.c_int64)),
                 ("n_preempted", ctypes.c_int32),
                 ("finished_ids", ctypes.POINTER(ctypes.c_int64)),
@@ -79,9 +84,9 @@ SIGNATURES = {
     "pkv_bm_free_seq": (_i32, [_vp, _i64]),
     "pkv_bm_num_free": (_i32, [_vp, _pi32]),
     "pkv_bm_geometry": (_i32, [_vp, _pi32, _pi32]),
-    "pkv_sched_create": (_i32, [_vp, _i32, _i32, ctypes.POINTER(_vp)]),
+    "pkv_sched_create": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_vp)]),
     "pkv_sched_destroy": (None, [_vp]),
-    "pkv_sched_add_request": (_i32, [_vp, _i64, _i32, _i32]),
+    "pkv_sched_add_request": (_i32, [_vp, _i64, _i32, _i32, _pi32]),
     "pkv_sched_begin_step": (_i32, [_vp, ctypes.POINTER(_SchedStep)]),
     "pkv_sched_end_step": (_i32, [_vp]),
     "pkv_sched_stats": (_i32, [_vp, _pi64, _pi64, _pi32, _pi32, _pi32]),
@@ -92,6 +97,8 @@ SIGNATURES = {
     "pkv_bm_snapshot": (_i32, [_vp, _pi32, _pi32, _pi32]),
     "pkv_bm_add_seq_prefix": (_i32, [_vp, _i64, _pi32, _i32, _i32, _pi32]),
     "pkv_bm_cached_blocks": (_i32, [_vp, _pi32]),
+    "pkv_bm_register_prefix": (_i32, [_vp, _i64, _pi32, _i32, _i32]),
+    "pkv_bm_unregister_prefix": (_i32, [_vp, _i64, _i32]),
     "pkv_bm_set_host_pool": (_i32, [_vp, _i32]),
     "pkv_bm_num_free_host": (_i32, [_vp, _pi32]),
     "pkv_bm_is_swapped": (_i32, [_vp, _i64, _pi32]),
@@ -284,6 +291,15 @@ class BlockManager:
                "pkv_bm_add_seq_prefix")
         return out.value
 
+    def register_prefix(self, seq_id: int, tokens, upto: int) -> None:
+        """Register the sequence's full blocks that the ids cover, up to token upto."""
+        ids = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(lib.pkv_bm_register_prefix(self._h, seq_id, _np_ptr(ids, ctypes.c_int32),
+                                          ids.shape[0], upto), "pkv_bm_register_prefix")
+
+    def unregister_prefix(self, seq_id: int, start: int) -> None:
+        _check(lib.pkv_bm_unregister_prefix(self._h, seq_id, start), "pkv_bm_unregister_prefix")
+
     def cached_blocks(self) -> int:
         out = _i32()
         _check(lib.pkv_bm_cached_blocks(self._h, ctypes.byref(out)), "pkv_bm_cached_blocks")
@@ -336,11 +352,11 @@ class Scheduler:
     [(device, host)], swapped_in, swapped_out."""
 
     def __init__(self, bm: BlockManager, max_running: int, reserve_max: bool = False,
-                 swap: bool = False):
+                 swap: bool = False, max_prefill_tokens=None):
         h = _vp()
         policy = (PKV_SCHED_RESERVE_MAX if reserve_max else 0) | (PKV_SCHED_SWAP if swap else 0)
-        _check(lib.pkv_sched_create(bm._h, max_running, policy, ctypes.byref(h)),
-               "pkv_sched_create")
+        _check(lib.pkv_sched_create(bm._h, max_running, policy, int(max_prefill_tokens or 0),
+                                    ctypes.byref(h)), "pkv_sched_create")
         self._h, self.bm, self.max_running = h, bm, int(max_running)
         n = self.max_running
         npairs = bm.num_blocks
@@ -353,13 +369,21 @@ class Scheduler:
         self._cow = np.zeros(2 * n, np.int32)
         self._adm = np.zeros(n, np.int64)
         self._adm_ctx = np.zeros(n, np.int32)
+        self._adm_cached = np.zeros(n, np.int32)
+        self._pf_ids = np.zeros(n, np.int64)
+        self._pf_start = np.zeros(n, np.int32)
+        self._pf_len = np.zeros(n, np.int32)
         self._pre = np.zeros(n, np.int64)
         self._fin = np.zeros(n, np.int64)
         self._step = _SchedStep(n, _np_ptr(self._ids, ctypes.c_int64),
                                 _np_ptr(self._slots, ctypes.c_int64), 0,
                                 _np_ptr(self._cow, ctypes.c_int32), 0,
                                 _np_ptr(self._adm, ctypes.c_int64),
-                                _np_ptr(self._adm_ctx, ctypes.c_int32), 0,
+                                _np_ptr(self._adm_ctx, ctypes.c_int32),
+                                _np_ptr(self._adm_cached, ctypes.c_int32), 0,
+                                _np_ptr(self._pf_ids, ctypes.c_int64),
+                                _np_ptr(self._pf_start, ctypes.c_int32),
+                                _np_ptr(self._pf_len, ctypes.c_int32), 0,
                                 _np_ptr(self._pre, ctypes.c_int64), 0,
                                 _np_ptr(self._fin, ctypes.c_int64), 0, npairs,
                                 _np_ptr(self._swin, ctypes.c_int32), 0,
@@ -378,8 +402,15 @@ class Scheduler:
         except Exception:
             pass
 
-    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
-        _check(lib.pkv_sched_add_request(self._h, req_id, prompt_len, max_new_tokens),
+    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int,
+                    tokens=None) -> None:
+        ids = None
+        if tokens is not None:
+            ids = np.ascontiguousarray(tokens, dtype=np.int32)
+            if ids.shape != (prompt_len,):
+                raise ValueError("token ids must cover the prompt")
+        _check(lib.pkv_sched_add_request(self._h, req_id, prompt_len, max_new_tokens,
+                                         None if ids is None else _np_ptr(ids, ctypes.c_int32)),
                "pkv_sched_add_request")
 
     def begin_step(self):
@@ -391,7 +422,11 @@ class Scheduler:
             "slots": self._slots[:nb].tolist(),
             "cow": [tuple(x) for x in self._cow[:2 * nc].reshape(-1, 2).tolist()],
             "admitted": list(zip(self._adm[:st.n_admitted].tolist(),
-                                 self._adm_ctx[:st.n_admitted].tolist())),
+                                 self._adm_ctx[:st.n_admitted].tolist(),
+                                 self._adm_cached[:st.n_admitted].tolist())),
+            "prefill": list(zip(self._pf_ids[:st.n_prefill].tolist(),
+                                self._pf_start[:st.n_prefill].tolist(),
+                                self._pf_len[:st.n_prefill].tolist())),
             "preempted": self._pre[:st.n_preempted].tolist(),
             "finished": self._fin[:st.n_finished].tolist(),
             "swap_in": [tuple(x) for x in self._swin[:2 * st.n_swap_in].reshape(-1, 2).tolist()],

@@ -23,6 +23,7 @@
 // block is registered under the exact token ids of the whole prefix up to its
 // end, stays cached while in use and after it is freed, and loses its entry
 // when the free queue hands it out for other content.
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -180,16 +181,41 @@ pkv_status pkv_bm_add_seq_prefix(pkv_bm* bm, int64_t seq_id, const int32_t* toke
   s.table = hits;
   s.table.reserve(hits.size() + need + 1);
   for (int32_t i = 0; i < need; ++i) s.table.push_back(bm->pop_free());
-  for (int32_t j = (int32_t)hits.size(); j < full; ++j) {
-    std::string key = key_of(j);
-    if (bm->cache.count(key)) continue;  // another block already holds this prefix
-    const int32_t b = s.table[j];
-    bm->cached_key[b] = key;
-    bm->cache.emplace(std::move(key), b);
-  }
   s.len = num_tokens;
   bm->seqs.emplace(seq_id, std::move(s));
   *cached = (int32_t)hits.size() * B;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_register_prefix(pkv_bm* bm, int64_t seq_id, const int32_t* tokens,
+                                  int32_t n_ids, int32_t upto) {
+  if (!bm || n_ids < 0 || (n_ids > 0 && !tokens)) return PKV_EINVAL;
+  pkv_bm::Seq* s;
+  if (pkv_status st = bm->resident(seq_id, &s)) return st;
+  if (upto < 0 || upto > s->len || n_ids > s->len) return PKV_EINVAL;
+  const int32_t B = bm->B;
+  const int32_t nfull = std::min(upto, n_ids) / B;
+  const char* bytes = reinterpret_cast<const char*>(tokens);
+  for (int32_t j = 0; j < nfull; ++j) {
+    std::string key(bytes, (size_t)(j + 1) * B * sizeof(int32_t));
+    const int32_t b = s->table[j];
+    if (bm->cache.count(key) || !bm->cached_key[b].empty()) continue;
+    bm->cached_key[b] = key;
+    bm->cache.emplace(std::move(key), b);
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_unregister_prefix(pkv_bm* bm, int64_t seq_id, int32_t start) {
+  if (!bm || start < 0) return PKV_EINVAL;
+  pkv_bm::Seq* s;
+  if (pkv_status st = bm->resident(seq_id, &s)) return st;
+  for (size_t j = (size_t)(start / bm->B); j < s->table.size(); ++j) {
+    const int32_t b = s->table[j];
+    if (bm->cached_key[b].empty() || bm->ref[b] != 1) continue;  // not cached, or shared
+    bm->cache.erase(bm->cached_key[b]);
+    bm->cached_key[b].clear();
+  }
   return PKV_OK;
 }
 
@@ -307,8 +333,8 @@ pkv_status pkv_bm_swap_out(pkv_bm* bm, int64_t seq_id, int32_t* pairs, int32_t c
   pkv_bm::Seq* s;
   if (pkv_status st = bm->resident(seq_id, &s)) return st;
   const int32_t n = (int32_t)s->table.size();
-  if (n > cap) return PKV_EINVAL;
-  if (n > bm->hnfree) return PKV_ENOBLOCKS;
+  if (n > bm->hnfree) return PKV_ENOBLOCKS;  // before the buffer check: a caller
+  if (n > cap) return PKV_EINVAL;            // sizing pairs by free blocks sees ENOBLOCKS
   std::vector<int32_t> host(n);
   for (int32_t i = 0; i < n; ++i) {
     host[i] = bm->pop_host();
@@ -330,8 +356,8 @@ pkv_status pkv_bm_swap_in(pkv_bm* bm, int64_t seq_id, int32_t* pairs, int32_t ca
   pkv_bm::Seq& s = it->second;
   if (!s.swapped) return PKV_EINVAL;
   const int32_t n = (int32_t)s.table.size();
-  if (n > cap) return PKV_EINVAL;
   if (n > bm->nfree) return PKV_ENOBLOCKS;
+  if (n > cap) return PKV_EINVAL;
   std::vector<int32_t> dev(n);
   for (int32_t i = 0; i < n; ++i) {
     dev[i] = bm->pop_free();

@@ -16,7 +16,12 @@
 // block -- swapped to the host pool under the swap policy when it holds KV and
 // the host has room, else dropped.  The reserve policy simulates the
 // max-length reservation of the systems before paging over the same pool.
-// Integer bookkeeping only.
+// Prefix caching and chunked prefill ("Impact and Follow-Ups"): requests may
+// carry prompt token ids (admission then reuses cached prefix blocks), and a
+// per-step prefill budget splits long prompts into chunks, continuing
+// admitted requests first.  Integer bookkeeping only.
+#include <algorithm>
+#include <cstdint>
 #include <deque>
 #include <new>
 #include <unordered_map>
@@ -28,10 +33,14 @@ struct pkv_sched {
   struct Req {
     int64_t id;
     int32_t prompt, max_new, generated, reserved;
+    std::vector<int32_t> tokens;  // prompt token ids, when known
+    bool has_tokens;
+    int32_t target, prefilled;    // context to prefill since admission, and done so far
     int32_t ctx() const { return prompt + generated; }
   };
   pkv_bm* bm = nullptr;
   int32_t N = 0, B = 0, max_running = 0;
+  int64_t max_prefill = 0;  // tokens per step, 0 = no limit
   bool reserve = false, swap = false;
   int64_t reserved_total = 0;
   bool in_step = false;
@@ -47,10 +56,10 @@ struct pkv_sched {
 extern "C" {
 
 pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t policy,
-                            pkv_sched** out) {
+                            int32_t max_prefill_tokens, pkv_sched** out) {
   if (!out) return PKV_EINVAL;
   *out = nullptr;
-  if (!bm || max_running <= 0) return PKV_EINVAL;
+  if (!bm || max_running <= 0 || max_prefill_tokens < 0) return PKV_EINVAL;
   if (policy & ~(PKV_SCHED_RESERVE_MAX | PKV_SCHED_SWAP)) return PKV_EINVAL;
   if ((policy & PKV_SCHED_RESERVE_MAX) && (policy & PKV_SCHED_SWAP)) return PKV_EINVAL;
   int32_t N = 0, B = 0;
@@ -63,6 +72,7 @@ pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t policy,
   s->max_running = max_running;
   s->reserve = (policy & PKV_SCHED_RESERVE_MAX) != 0;
   s->swap = (policy & PKV_SCHED_SWAP) != 0;
+  s->max_prefill = max_prefill_tokens;
   *out = s;
   return PKV_OK;
 }
@@ -70,11 +80,13 @@ pkv_status pkv_sched_create(pkv_bm* bm, int32_t max_running, int32_t policy,
 void pkv_sched_destroy(pkv_sched* s) { delete s; }
 
 pkv_status pkv_sched_add_request(pkv_sched* s, int64_t req_id, int32_t prompt_len,
-                                 int32_t max_new_tokens) {
+                                 int32_t max_new_tokens, const int32_t* tokens) {
   if (!s || prompt_len < 0 || max_new_tokens < 1) return PKV_EINVAL;
   if (s->reqs.count(req_id)) return PKV_EEXIST;
   if (s->blocks((int64_t)prompt_len + max_new_tokens) > s->N) return PKV_EINVAL;
-  auto it = s->reqs.emplace(req_id, pkv_sched::Req{req_id, prompt_len, max_new_tokens, 0, 0});
+  pkv_sched::Req r{req_id, prompt_len, max_new_tokens, 0, 0, {}, tokens != nullptr, 0, 0};
+  if (tokens) r.tokens.assign(tokens, tokens + prompt_len);
+  auto it = s->reqs.emplace(req_id, std::move(r));
   s->waiting.push_back(&it.first->second);
   return PKV_OK;
 }
@@ -82,6 +94,7 @@ pkv_status pkv_sched_add_request(pkv_sched* s, int64_t req_id, int32_t prompt_le
 pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
   if (!s || !o || o->capacity < s->max_running) return PKV_EINVAL;
   if (!o->batch_ids || !o->slots || !o->cow_pairs || !o->admitted_ids || !o->admitted_ctx ||
+      !o->admitted_cached || !o->prefill_ids || !o->prefill_start || !o->prefill_len ||
       !o->preempted_ids || !o->finished_ids)
     return PKV_EINVAL;
   if (s->swap && (o->pair_capacity < s->N || !o->swap_in_pairs || !o->swap_out_pairs ||
@@ -89,7 +102,7 @@ pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
     return PKV_EINVAL;
   if (s->in_step) return PKV_EINVAL;  // end_step() of the last step is due
   o->n_batch = o->n_cow = o->n_admitted = o->n_preempted = o->n_finished = 0;
-  o->n_swap_in = o->n_swap_out = o->n_swapped_in = o->n_swapped_out = 0;
+  o->n_swap_in = o->n_swap_out = o->n_swapped_in = o->n_swapped_out = o->n_prefill = 0;
   s->in_step = true;
 
   // swapped requests come back first, in queue order, while the device has room
@@ -107,14 +120,43 @@ pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
     o->swapped_in_ids[o->n_swapped_in++] = r->id;
   }
 
+  // prefill chunks: admitted requests first, in admission order, within the budget
+  int64_t budget = s->max_prefill > 0 ? s->max_prefill : INT64_MAX;
+  struct Chunk {
+    pkv_sched::Req* r;
+    int32_t start, n;
+  };
+  std::vector<Chunk> chunks;
+  auto give_chunk = [&](pkv_sched::Req* r) {
+    const int32_t n = (int32_t)std::min<int64_t>(r->target - r->prefilled, budget);
+    if (n > 0) {
+      chunks.push_back({r, r->prefilled, n});
+      r->prefilled += n;
+      budget -= n;
+      if (r->has_tokens)  // the chunk's full prompt blocks join the prefix cache
+        pkv_bm_register_prefix(s->bm, r->id, r->tokens.data(), (int32_t)r->tokens.size(),
+                               r->prefilled);
+    }
+  };
+  for (pkv_sched::Req* r : s->running)
+    if (r->prefilled < r->target && budget > 0) give_chunk(r);
+
   // admissions, first come first served, none while a request is swapped out
-  std::vector<std::pair<pkv_sched::Req*, int32_t>> admitted;
+  struct Adm {
+    pkv_sched::Req* r;
+    int32_t ctx, cached;
+  };
+  std::vector<Adm> admitted;
   while (s->swapped.empty() && !s->waiting.empty() &&
-         (int32_t)s->running.size() < s->max_running) {
+         (int32_t)s->running.size() < s->max_running && budget > 0) {
     pkv_sched::Req* r = s->waiting.front();
     const int32_t need_max = s->blocks((int64_t)r->prompt + r->max_new);
     if (s->reserve && s->reserved_total + need_max > s->N) break;
-    const pkv_status st = pkv_bm_add_seq(s->bm, r->id, r->ctx());
+    int32_t cached = 0;
+    const pkv_status st =
+        r->has_tokens ? pkv_bm_add_seq_prefix(s->bm, r->id, r->tokens.data(),
+                                              (int32_t)r->tokens.size(), r->ctx(), &cached)
+                      : pkv_bm_add_seq(s->bm, r->id, r->ctx());
     if (st == PKV_ENOBLOCKS) break;
     if (st != PKV_OK) return st;
     if (s->reserve) {
@@ -123,13 +165,22 @@ pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
     }
     s->waiting.pop_front();
     s->running.push_back(r);
-    admitted.emplace_back(r, r->ctx());
+    r->target = r->ctx();
+    r->prefilled = cached;
+    admitted.push_back({r, r->ctx(), cached});
+    give_chunk(r);
   }
 
-  // one slot per running request; preempt the youngest when the pool is dry
+  // one slot per request whose prefill is complete; preempt the youngest when
+  // the pool is dry
+  std::vector<pkv_sched::Req*> decoding;
   size_t i = 0;
   while (i < s->running.size()) {
     pkv_sched::Req* r = s->running[i];
+    if (r->prefilled < r->target) {  // still prefilling: no token this step
+      ++i;
+      continue;
+    }
     int64_t slot;
     int32_t src, dst;
     const pkv_status st = pkv_bm_append_slot(s->bm, r->id, &slot, &src, &dst);
@@ -138,7 +189,14 @@ pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
       s->running.pop_back();
       size_t fresh = admitted.size();  // admitted this step: no KV written yet
       for (size_t k = 0; k < admitted.size(); ++k)
-        if (admitted[k].first == victim) fresh = k;
+        if (admitted[k].r == victim) fresh = k;
+      for (size_t k = 0; k < chunks.size(); ++k)  // its chunk of this step is not written
+        if (chunks[k].r == victim) {
+          victim->prefilled -= chunks[k].n;
+          chunks.erase(chunks.begin() + k);
+          pkv_bm_unregister_prefix(s->bm, victim->id, victim->prefilled);
+          break;
+        }
       if (s->swap && fresh == admitted.size()) {
         int32_t len = 0, nb = 0, host_free = 0;
         pkv_bm_seq_info(s->bm, victim->id, &len, &nb);
@@ -164,17 +222,18 @@ pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
       continue;
     }
     if (st != PKV_OK) return st;
-    o->slots[i] = slot;
+    o->slots[decoding.size()] = slot;
     if (src >= 0) {
       o->cow_pairs[2 * o->n_cow] = src;
       o->cow_pairs[2 * o->n_cow + 1] = dst;
       ++o->n_cow;
     }
+    decoding.push_back(r);
     ++i;
   }
 
-  for (size_t k = 0; k < s->running.size(); ++k) {
-    pkv_sched::Req* r = s->running[k];
+  for (size_t k = 0; k < decoding.size(); ++k) {
+    pkv_sched::Req* r = decoding[k];
     o->batch_ids[k] = r->id;
     r->generated += 1;
     if (r->generated == r->max_new) {
@@ -182,11 +241,18 @@ pkv_status pkv_sched_begin_step(pkv_sched* s, pkv_sched_step* o) {
       s->finishing.push_back(r);
     }
   }
-  o->n_batch = (int32_t)s->running.size();
-  for (const auto& a : admitted) {
-    o->admitted_ids[o->n_admitted] = a.first->id;
-    o->admitted_ctx[o->n_admitted] = a.second;
+  o->n_batch = (int32_t)decoding.size();
+  for (const Adm& a : admitted) {
+    o->admitted_ids[o->n_admitted] = a.r->id;
+    o->admitted_ctx[o->n_admitted] = a.ctx;
+    o->admitted_cached[o->n_admitted] = a.cached;
     ++o->n_admitted;
+  }
+  for (const Chunk& c : chunks) {
+    o->prefill_ids[o->n_prefill] = c.r->id;
+    o->prefill_start[o->n_prefill] = c.start;
+    o->prefill_len[o->n_prefill] = c.n;
+    ++o->n_prefill;
   }
   return PKV_OK;
 }

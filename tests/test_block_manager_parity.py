@@ -211,8 +211,10 @@ def _prefix_ops(rng, B, n_ops=300):
             ops.append(("add", sid, int(rng.integers(0, 3 * B))))
         elif r < 0.8:
             ops.append(("append", sid))
-        elif r < 0.88:
+        elif r < 0.85:
             ops.append(("fork", sid, int(rng.integers(0, 6))))
+        elif r < 0.9:
+            ops.append(("unregister", sid, int(rng.integers(0, 4 * B))))
         else:
             ops.append(("free", sid))
     return ops
@@ -221,7 +223,11 @@ def _prefix_ops(rng, B, n_ops=300):
 def _apply(bm, op, err):
     try:
         if op[0] == "prefix":
-            return bm.add_seq_prefix(op[1], op[2], op[3])
+            cached = bm.add_seq_prefix(op[1], op[2], op[3])
+            bm.register_prefix(op[1], op[2], op[3])
+            return cached
+        if op[0] == "unregister":
+            return bm.unregister_prefix(op[1], op[2])
         if op[0] == "add":
             return bm.add_seq(op[1], op[2])
         if op[0] == "append":

@@ -318,11 +318,6 @@ class _NoCapBM(obm.BlockManager):
                 self.free.remove(b)
             self.ref[b] += 1
         table = hits + [self._take() for _ in range(need)]
-        for j in range(len(hits), len(tokens) // B):
-            key = tuple(tokens[:(j + 1) * B])
-            if key not in self.cache:
-                self.cache[key] = table[j]
-                self.cached_key[table[j]] = key
         self.tables[sid] = table
         self.lens[sid] = num_tokens
         return len(hits) * B

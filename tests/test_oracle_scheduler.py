@@ -33,7 +33,7 @@ def test_iteration_level_figure():
     # the very next iteration: A has left and D has joined
     nxt = steps[a_done + 1]
     assert label(nxt["batch"]) == g["batch_after"]
-    assert label([r for r, _ in nxt["admitted"]]) == [g["joins"]]
+    assert label([a[0] for a in nxt["admitted"]]) == [g["joins"]]
     # D waited only because of the batch limit, not for B and C to finish
     b_done = next(k for k, o in enumerate(steps) if 1 in o["finished"])
     assert a_done + 1 < b_done
@@ -54,7 +54,7 @@ def test_admission_needs_free_blocks_not_a_contiguous_region():
     sc = Scheduler(bm, max_running=4)
     sc.add_request(0, 31, 1)        # 32 tokens after its step: exactly 2 blocks
     out = sc.begin_step()
-    assert out["admitted"] == [(0, 31)] and bm.tables[0] == [3, 5]
+    assert out["admitted"] == [(0, 31, 0)] and bm.tables[0] == [3, 5]
 
 
 def test_reserve_policy_holds_the_maximum_length():
@@ -106,7 +106,7 @@ def test_invariants_on_random_traces(seed, reserve):
         assert 0 < len(out["batch"]) <= max_running
         for rid in out["batch"]:
             produced[rid] += 1
-        admitted_order += [r for r, _ in out["admitted"]]
+        admitted_order += [a[0] for a in out["admitted"]]
         finished += out["finished"]
         assert held <= committed
         if reserve:
@@ -143,7 +143,7 @@ def test_preemption_drops_the_youngest_and_recomputes_it():
     pre = [k for k, o in enumerate(seen) if o["preempted"]]
     assert pre and seen[pre[0]]["preempted"] == [1]          # the younger request
     back = next(o for o in seen[pre[0]:] if o["admitted"])
-    rid, ctx = back["admitted"][0]
+    rid, ctx, _ = back["admitted"][0]
     assert rid == 1 and ctx > 8                                # prompt + kept tokens
 
 

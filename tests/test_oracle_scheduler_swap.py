@@ -45,7 +45,7 @@ def test_swap_trace_worked_by_hand():
     sc.add_request(1, 8, 9)
     steps = _run(sc)
     assert len(steps) == 14
-    assert steps[0]["admitted"] == [(0, 8), (1, 8)] and steps[0]["slots"] == [16, 20]
+    assert steps[0]["admitted"] == [(0, 8, 0), (1, 8, 0)] and steps[0]["slots"] == [16, 20]
     assert all(not s["admitted"] for s in steps[1:])             # no recomputation
     assert all(not s["preempted"] for s in steps)
     s5 = steps[4]
@@ -71,7 +71,7 @@ def test_a_victim_without_kv_is_dropped_not_swapped():
     sc.add_request(1, 4, 3)
     out = sc.begin_step()
     assert out["preempted"] == [1] and out["swap_out"] == []
-    assert out["admitted"] == [(0, 8)] and out["batch"] == [0]
+    assert out["admitted"] == [(0, 8, 0)] and out["batch"] == [0]
 
 
 def test_swap_and_reserve_do_not_combine():
@@ -101,8 +101,8 @@ class Pools:
             self.host[h] = list(self.dev[d])
         for src, dst in out["cow"]:
             self.dev[dst] = list(self.dev[src])
-        for rid, ctx in out["admitted"]:
-            for t in range(ctx):
+        for rid, start, n in out["prefill"]:
+            for t in range(start, start + n):
                 b, o = self._slot(rid, t)
                 self.dev[b][o] = (rid, t)
         B = self.bm.B
@@ -154,7 +154,7 @@ def swap_trace_run(seed, sched_cls=Scheduler):
         assert 0 < len(out["batch"]) <= max_running
         for rid in out["batch"]:
             produced[rid] += 1
-        admitted_order += [r for r, _ in out["admitted"]]
+        admitted_order += [a[0] for a in out["admitted"]]
         swaps += len(out["swapped_out"])
         # a swapped request resumes with the tokens it held
         for rid in out["swapped_in"]:

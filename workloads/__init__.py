@@ -251,3 +251,23 @@ def request_trace(rng: np.random.Generator, n: int, prompt_median: float = 256.0
     o = np.clip(np.rint(np.exp(rng.normal(math.log(out_median), out_sigma, n))), 1,
                 max_out).astype(np.int64)
     return [(i, int(p[i]), int(o[i])) for i in range(n)]
+
+
+def prefix_trace(rng: np.random.Generator, n: int, n_prefixes: int = 4,
+                 prefix_median: float = 64.0, suffix_median: float = 24.0,
+                 out_median: float = 16.0, max_prefix: int = 400, max_suffix: int = 200,
+                 max_out: int = 100, vocab: int = 1000):
+    """Requests whose prompts start with one of a few shared prefixes (system
+    prompts, few-shot templates) followed by a request-specific part; token ids
+    are random and carry no meaning.  Returns [(id, prompt_len, max_new,
+    token ids)], all submitted at the start."""
+    lognorm = lambda med, cap: int(np.clip(np.rint(np.exp(rng.normal(math.log(med), 0.6))),
+                                           1, cap))
+    prefixes = [rng.integers(0, vocab, size=lognorm(prefix_median, max_prefix)).tolist()
+                for _ in range(n_prefixes)]
+    out = []
+    for i in range(n):
+        base = prefixes[int(rng.integers(0, n_prefixes))] if rng.random() < 0.85 else []
+        tokens = base + rng.integers(0, vocab, size=lognorm(suffix_median, max_suffix)).tolist()
+        out.append((i, len(tokens), lognorm(out_median, max_out), [int(t) for t in tokens]))
+    return out
