@@ -320,14 +320,15 @@ def run_serve(args, torch, np):
     gen.manual_seed(1011)
     rows = 1 << 16
     kv_rows = torch.randn((2, rows, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
-    q_all = torch.randn((args.serve_running, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    q_rows = torch.randn((rows, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
 
     def kv_source(pairs):
         idx = torch.from_numpy((pairs[:, 0] * 7919 + pairs[:, 1]) % rows).to(dev)
         return kv_rows[0].index_select(0, idx), kv_rows[1].index_select(0, idx)
 
-    def q_source(ids):
-        return q_all[:len(ids)]
+    def q_source(pairs):
+        idx = torch.from_numpy((pairs[:, 0] * 104729 + pairs[:, 1]) % rows).to(dev)
+        return q_rows.index_select(0, idx)
 
     # untimed warm-up: first launches, pinned staging buffers, allocator
     warm = DecodeLoop(num_blocks=N, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
@@ -357,13 +358,13 @@ def run_serve(args, torch, np):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         while not loop.idle():
-            st, _, lens = loop.step(kv_source, q_source)
+            st, _, _, lens = loop.step(kv_source, q_source)
             n = len(st["batch"])
             steps += 1
             tokens += n
             batch_sum += n
             preempted += len(st["preempted"])
-            prefill += sum(c for _, c in st["admitted"])
+            prefill += sum(c for _, _, c in st["prefill"])
             swapped += len(st["swapped_out"])
             blocks_out += len(st["swap_out"])
             blocks_in += len(st["swap_in"])

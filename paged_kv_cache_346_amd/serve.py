@@ -5,16 +5,21 @@ Drives the native scheduler (pkv_sched_*) and the device kernels step by step
 PagedAttention: The vLLM Paper, "Continuous Batching" and "Implementation
 Essentials"): every step
 
-  1. the scheduler swaps preempted requests back in, admits waiting requests
-     into free blocks, appends one slot per running request (preempting the
+  1. the scheduler swaps preempted requests back in, hands out prefill chunks
+     (continuing admitted requests first, within the optional per-step prefill
+     budget), admits waiting requests into free blocks -- reusing cached blocks
+     of their prompt's prefix when the request carries its token ids --,
+     appends one slot per request whose prefill is complete (preempting the
      youngest when the pool runs dry: swapped to the host pool when the loop
      has one, else dropped for recomputation) and names the requests that
      finish;
   2. the swap-in copies (host to device), the swap-out copies (device to host)
      and the copy-on-write copies run, then one reshape_and_cache writes the
-     prompt KV of the admitted requests;
-  3. paged attention runs over the batch's block tables (host work plan) and
-     writes the new token of every running request into its slot as it goes;
+     KV of every prefill chunk;
+  3. the multi-token attention kernel attends each chunk's rows causally over
+     its sequence's cache, then paged decode attention runs over the batch's
+     block tables (host work plan) and writes the new token of every decoding
+     request into its slot as it goes;
   4. the finished requests give their blocks back.
 
 The step's metadata (slots, block copy pairs, block tables, lengths, work plan)
@@ -24,9 +29,9 @@ still run.  The host pool, when there is one, is pinned host memory that the
 swap kernel reads and writes over the host link.
 
 K/V and query values come from caller-supplied sources (the loop computes no
-model): kv_source(pairs) returns the K and V rows [T, Hkv, D] for an int64
-array of (request id, token position) pairs, and q_source(ids) the queries
-[n, Hq, D] of the batch.  Everything the method computes runs in libpkv.so.
+model): kv_source(pairs) returns the K and V rows [T, Hkv, D] and
+q_source(pairs) the query rows [T, Hq, D] for an int64 array of (request id,
+token position) pairs.  Everything the method computes runs in libpkv.so.
 """
 from __future__ import annotations
 
@@ -36,7 +41,8 @@ import numpy as np
 import torch
 
 from . import (BlockManager, Plan, Scheduler, attention_plan, attention_workspace_bytes,
-               copy_blocks, paged_attention_decode, pool_shapes, reshape_and_cache, swap_blocks)
+               copy_blocks, paged_attention_decode, paged_attention_prefill, pool_shapes,
+               reshape_and_cache, swap_blocks)
 
 
 def _pad4(n: int) -> int:
@@ -47,7 +53,7 @@ class DecodeLoop:
     def __init__(self, *, num_blocks: int, block_size: int, q_heads: int, kv_heads: int,
                  head_dim: int, max_running: int, max_len: int, dtype=torch.bfloat16,
                  partition_size: int = 0, reserve_max: bool = False, free_order=None,
-                 host_blocks: int = 0, device="cuda"):
+                 host_blocks: int = 0, max_prefill_tokens=None, device="cuda"):
         self.B, self.Hq, self.Hkv, self.D = block_size, q_heads, kv_heads, head_dim
         self.P = partition_size
         self.max_len = max_len
@@ -56,7 +62,8 @@ class DecodeLoop:
         self.bm = BlockManager(num_blocks, block_size, free_order)
         if host_blocks:
             self.bm.set_host_pool(host_blocks)
-        self.sched = Scheduler(self.bm, max_running, reserve_max, swap=host_blocks > 0)
+        self.sched = Scheduler(self.bm, max_running, reserve_max, swap=host_blocks > 0,
+                               max_prefill_tokens=max_prefill_tokens)
         ks, vs = pool_shapes(num_blocks, kv_heads, head_dim, block_size, dtype)
         self.k_pool = torch.empty(ks, dtype=dtype, device=self.device)
         self.v_pool = torch.empty(vs, dtype=dtype, device=self.device)
@@ -75,10 +82,12 @@ class DecodeLoop:
         self._dev = None
         self._turn = 0
 
-    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
+    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int,
+                    tokens=None) -> None:
+        """tokens: the prompt's token ids, or None (no prefix caching for it)."""
         if prompt_len + max_new_tokens > self.max_len:
             raise ValueError("request longer than the loop's max_len")
-        self.sched.add_request(req_id, prompt_len, max_new_tokens)
+        self.sched.add_request(req_id, prompt_len, max_new_tokens, tokens=tokens)
 
     def _stage(self, parts):
         """Copy the int32 arrays `parts` (a dict) to the device in one transfer;
@@ -107,21 +116,34 @@ class DecodeLoop:
 
     def step(self, kv_source, q_source):
         """One iteration.  Returns (the scheduler's step dict -- plus "stats",
-        the scheduler's (tokens held, slots committed, waiting, running) taken
-        before the finished requests leave --, the attention output [n_batch,
-        Hq, D] -- a view valid until the next step -- and the host context
-        lengths of the batch)."""
+        the scheduler's (tokens held, slots committed, waiting, running,
+        swapped) taken before the finished requests leave --, the decode
+        attention output [n_batch, Hq, D], the prefill attention output
+        [prefill rows, Hq, D] for the step's chunks in order -- views valid
+        until the next step -- and the host context lengths of the batch)."""
         st = self.sched.begin_step()
         ids = st["batch"]
         n = len(ids)
-        # token rows: the admitted requests' prompts (written by reshape_and_cache),
-        # then one token per running request (written by the attention launch)
+        chunks = st["prefill"]
+        # token rows: the prefill chunks (written by reshape_and_cache), then one
+        # token per decoding request (written by the attention launch)
         pairs, write_slots = [], []
-        for rid, ctx in st["admitted"]:
-            if ctx:
-                write_slots.append(self.bm.slots(rid, 0, ctx))
-                pairs.append(np.stack([np.full(ctx, rid, np.int64),
-                                       np.arange(ctx, dtype=np.int64)], 1))
+        for rid, start, cnt in chunks:
+            write_slots.append(self.bm.slots(rid, start, cnt))
+            pairs.append(np.stack([np.full(cnt, rid, np.int64),
+                                   np.arange(start, start + cnt, dtype=np.int64)], 1))
+        n_pf = sum(c for _, _, c in chunks)
+        parts = {}
+        if write_slots:
+            parts["slots"] = np.concatenate(write_slots).view(np.int32)
+            pf_ids = [rid for rid, _, _ in chunks]
+            pf_tables, _ = self.bm.fill_batch(pf_ids, self.max_blocks)
+            pf_lens = np.array([start + cnt for _, start, cnt in chunks], np.int32)
+            pf_width = max(1, -(-int(pf_lens.max()) // self.B))
+            parts.update(pf_tables=np.ascontiguousarray(pf_tables[:, :pf_width]).reshape(-1),
+                         pf_lens=pf_lens,
+                         pf_start=np.concatenate([[0], np.cumsum([c for _, _, c in chunks])])
+                         .astype(np.int32))
         lens = np.empty(0, np.int32)
         if n:
             tables, lens = self.bm.fill_batch(ids, self.max_blocks)
@@ -131,14 +153,10 @@ class DecodeLoop:
             words, n_items, n_merge = attention_plan(lens, self.Hkv, self.B, width, mcl,
                                                      self.P)
             pairs.append(np.stack([np.asarray(ids, np.int64), lens.astype(np.int64) - 1], 1))
-        parts = {}
-        if write_slots:
-            parts["slots"] = np.concatenate(write_slots).view(np.int32)
+            parts.update(tables=tables.reshape(-1), lens=lens, plan=words)
         for key in ("swap_in", "swap_out", "cow"):
             if st[key]:
                 parts[key] = np.asarray(st[key], np.int32)
-        if n:
-            parts.update(tables=tables.reshape(-1), lens=lens, plan=words)
         dev = self._stage(parts) if parts else {}
         # block copies in the scheduler's order: swap-ins, swap-outs, copy-on-write
         if "swap_in" in dev:
@@ -150,20 +168,33 @@ class DecodeLoop:
         if "cow" in dev:
             copy_blocks(self.k_pool, self.v_pool, dev["cow"].view(-1, 2))
         out = self.out[:n]
+        out_pf = None
         if pairs:
-            k, v = kv_source(np.concatenate(pairs))
-            if write_slots:
-                reshape_and_cache(k[:-n] if n else k, v[:-n] if n else v, self.k_pool,
-                                  self.v_pool, dev["slots"].view(torch.int64))
+            all_pairs = np.concatenate(pairs)
+            k, v = kv_source(all_pairs)
+            q = q_source(all_pairs)
+            if n_pf:
+                reshape_and_cache(k[:n_pf], v[:n_pf], self.k_pool, self.v_pool,
+                                  dev["slots"].view(torch.int64))
+                out_pf = self._prefill_out(n_pf)
+                paged_attention_prefill(out_pf, q[:n_pf], self.k_pool, self.v_pool,
+                                        dev["pf_tables"].view(len(chunks), -1), dev["pf_lens"],
+                                        dev["pf_start"], max(c for _, _, c in chunks))
         if n:
-            paged_attention_decode(out, q_source(ids), self.k_pool, self.v_pool,
+            paged_attention_decode(out, q[n_pf:], self.k_pool, self.v_pool,
                                    dev["tables"].view(n, -1), dev["lens"], mcl,
                                    partition_size=self.P, workspace=self.ws,
                                    plan=Plan(dev["plan"], n_items, n_merge),
-                                   new_key=k[-n:], new_value=v[-n:])
+                                   new_key=k[n_pf:], new_value=v[n_pf:])
         st["stats"] = self.sched.stats()   # before the finished requests leave
         self.sched.end_step()
-        return st, out, lens
+        return st, out, out_pf, lens
+
+    def _prefill_out(self, rows: int) -> torch.Tensor:
+        if getattr(self, "_pf_out", None) is None or self._pf_out.shape[0] < rows:
+            self._pf_out = torch.empty((max(rows, 1024), self.Hq, self.D), dtype=torch.float32,
+                                       device=self.device)
+        return self._pf_out[:rows]
 
     def stats(self):
         """(tokens held, slots committed, waiting, running, swapped out)."""
