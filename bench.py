@@ -386,6 +386,37 @@ def run_serve(args, torch, np):
         }
         log(f"bench: serve {policy}: {result[policy]}")
         del loop
+    # prefix caching and chunked prefill: prompts drawn from 8 shared system
+    # prompts plus a request-specific part, with a prefill budget per step
+    ptrace = W.prefix_trace(np.random.default_rng(12), args.serve_requests, n_prefixes=8,
+                            prefix_median=512, suffix_median=96, out_median=128,
+                            max_prefix=1024, max_suffix=512, max_out=512, vocab=32000)
+    p_max_len = max(p_ + m_ for _, p_, m_, _ in ptrace)
+    prefix_result = {}
+    for mode in ("cache_off", "cache_on"):
+        loop = DecodeLoop(num_blocks=N, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
+                          max_running=args.serve_running, max_len=p_max_len, free_order=order,
+                          max_prefill_tokens=args.serve_prefill_budget)
+        for rid, p_, m_, toks in ptrace:
+            loop.add_request(rid, p_, m_, tokens=toks if mode == "cache_on" else None)
+        steps = tokens = prefill = cached = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while not loop.idle():
+            st, _, _, _ = loop.step(kv_source, q_source)
+            steps += 1
+            tokens += len(st["batch"])
+            prefill += sum(c for _, _, c in st["prefill"])
+            cached += sum(c for _, _, c in st["admitted"])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        prefix_result[mode] = {"steps": steps, "decode_tokens": tokens,
+                               "prefill_tokens_computed": prefill,
+                               "prompt_tokens_from_cache": cached, "wall_s": round(wall, 3),
+                               "decode_tokens_per_s": round(tokens / wall, 1)}
+        log(f"bench: serve prefix {mode}: {prefix_result[mode]}")
+        del loop
+
     rec = {
         "metric": "continuous-batching decode tokens/s, one attention layer (wall clock, "
                   "host scheduling included)",
@@ -405,6 +436,11 @@ def run_serve(args, torch, np):
         "paged_swap": result["swap"],
         "reserve_max_len": result["reserve"],
         "swap_blocks_probe": swap_probe,
+        "prefix_cache": {"workload": f"{len(ptrace)} requests: one of 8 shared prompts "
+                                     f"(log-normal median 512 tokens, <= 1024) + a private "
+                                     f"part (median 96, <= 512), output median 128; prefill "
+                                     f"budget {args.serve_prefill_budget} tokens per step",
+                         **prefix_result},
         "paged_vs_reserve_steps": round(result["reserve"]["steps"] / result["paged"]["steps"],
                                         3),
         "paged_vs_reserve_mean_batch": round(result["paged"]["mean_batch"] /
@@ -513,6 +549,8 @@ def main() -> int:
     ap.add_argument("--prefill-chunk", type=int, default=512)
     ap.add_argument("--serve-requests", type=int, default=1024)
     ap.add_argument("--serve-running", type=int, default=1024)
+    ap.add_argument("--serve-prefill-budget", type=int, default=2048,
+                    help="prefill tokens per step in the prefix-cache scenario")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for hardware byte counters)")
