@@ -15,11 +15,16 @@ Readings where the pages are silent:
     sequence lives in physical block table[t // B], slot t % B;
   * L_s counts every cached token including the one written this step;
   * query head h reads KV head h // (Hq / Hkv) (consecutive heads share);
-  * bf16 values are held as raw uint16 bit patterns and widened exactly.
+  * bf16 values are held as raw uint16 bit patterns and widened exactly;
+  * an fp8 pool (uint8 E4M3 codes, oracle/fp8.py) holds K and V divided by a
+    per-KV-head scale: the value of a code times its head's scale, exact in
+    fp64, is what attention uses.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from oracle import fp8
 
 
 def to_f64(a: np.ndarray) -> np.ndarray:
@@ -31,8 +36,15 @@ def to_f64(a: np.ndarray) -> np.ndarray:
     raise TypeError(f"unsupported element type {a.dtype}")
 
 
-def gather_kv(k_pool, v_pool, table, L: int, g: int):
-    """Contiguous K, V [L, D] (fp64) of one sequence and KV head `g`.
+def _widen(a: np.ndarray, scale) -> np.ndarray:
+    if a.dtype == np.uint8:
+        return fp8.DECODE[a] * float(scale)
+    return to_f64(a)
+
+
+def gather_kv(k_pool, v_pool, table, L: int, g: int, k_scale=None, v_scale=None):
+    """Contiguous K, V [L, D] (fp64) of one sequence and KV head `g` (fp8 pools
+    are dequantized with the head's scales).
 
     Logical block j of the sequence is physical block table[j]; it holds
     tokens j*B .. j*B+B-1, of which only the first L - j*B are valid when it is
@@ -47,9 +59,11 @@ def gather_kv(k_pool, v_pool, table, L: int, g: int):
         n = min(B, L - j * B)
         # K block [D/x, B, x] -> tokens x dims
         kb = k_pool[pb, g, :, :n, :]                 # [D/x, n, x]
-        K[j * B:j * B + n] = to_f64(np.transpose(kb, (1, 0, 2)).reshape(n, D))
+        ks = None if k_scale is None else k_scale[g]
+        vs = None if v_scale is None else v_scale[g]
+        K[j * B:j * B + n] = _widen(np.transpose(kb, (1, 0, 2)).reshape(n, D), ks)
         vb = v_pool[pb, g, :, :n]                    # [D, n]
-        V[j * B:j * B + n] = to_f64(vb.T)
+        V[j * B:j * B + n] = _widen(vb.T, vs)
     return K, V
 
 
@@ -62,7 +76,7 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.n
 
 
 def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale=None,
-                           rows=None):
+                           rows=None, k_scale=None, v_scale=None):
     """Decode attention for every (sequence, query head), or only `rows`
     (a list of (s, h) pairs).  Returns fp64 [S, Hq, D] (unsampled rows are NaN)."""
     S, Hq, D = q.shape
@@ -84,7 +98,7 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale=
             heads = [h for h in range(g * G, (g + 1) * G) if want is None or h in want[s]]
             if not heads:
                 continue
-            K, V = gather_kv(k_pool, v_pool, block_tables[s], L, g)
+            K, V = gather_kv(k_pool, v_pool, block_tables[s], L, g, k_scale, v_scale)
             for h in heads:
                 out[s, h] = attention(qf[s, h], K, V, scale)
     return out
@@ -98,7 +112,7 @@ def query_starts(query_lens) -> np.ndarray:
 
 
 def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, query_lens,
-                            scale=None, rows=None):
+                            scale=None, rows=None, k_scale=None, v_scale=None):
     """Attention of several new tokens per sequence over the paged cache
     (chunked prefill, and the uncached rest of a prompt after a prefix-cache
     hit: PagedAttention: The vLLM Paper, "Impact and Follow-Ups").
@@ -139,7 +153,7 @@ def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, query
                 if not heads:
                     continue
                 if K is None:
-                    K, V = gather_kv(k_pool, v_pool, block_tables[s], L, g)
+                    K, V = gather_kv(k_pool, v_pool, block_tables[s], L, g, k_scale, v_scale)
                 p = L - Q + i
                 for h in heads:
                     out[t, h] = attention(qf[t, h], K[:p + 1], V[:p + 1], scale)

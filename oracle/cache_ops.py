@@ -19,12 +19,27 @@ from __future__ import annotations
 
 import numpy as np
 
+from oracle import fp8
 
-def reshape_and_cache(k_pool, v_pool, key, value, slot_mapping):
+
+def _f32(a):
+    """bf16 bit patterns (uint16) or fp32 -> fp32, exactly."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32)
+    return a.astype(np.float32)
+
+
+def reshape_and_cache(k_pool, v_pool, key, value, slot_mapping, k_scale=None, v_scale=None):
     """Return new (k_pool, v_pool) with token i written to slot_mapping[i].
 
-    key/value: [T, Hkv, D]; k_pool [N, Hkv, D/x, B, x]; v_pool [N, Hkv, D, B]."""
+    key/value: [T, Hkv, D]; k_pool [N, Hkv, D/x, B, x]; v_pool [N, Hkv, D, B].
+    fp8 pools (uint8): key/value (bf16 bits or fp32) are quantized to E4M3
+    with the per-KV-head scales first (oracle/fp8.py)."""
     N, Hkv, Dx, B, x = k_pool.shape
+    if k_pool.dtype == np.uint8:
+        key = fp8.quantize(_f32(key), k_scale, head_axis=1)
+        value = fp8.quantize(_f32(value), v_scale, head_axis=1)
     k_out = k_pool.copy()
     v_out = v_pool.copy()
     for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):

@@ -32,7 +32,7 @@ def _mutant_decode(head_of=None, drop_scale=False, short=False):
     return decode
 
 
-def _gather_transposed(k_pool, v_pool, table, L, g):
+def _gather_transposed(k_pool, v_pool, table, L, g, k_scale=None, v_scale=None):
     N, Hkv, Dx, B, x = k_pool.shape
     D = Dx * x
     K = np.empty((L, D))
@@ -354,5 +354,45 @@ def test_prefix_cache_mutants_fail_pins(monkeypatch, cls):
         try:
             t()
         except (AssertionError, obm.BMError, KeyError, ValueError):
+            failed += 1
+    assert failed > 0
+
+
+# --- fp8 codec -------------------------------------------------------------------
+from oracle import fp8 as ofp8
+from tests import test_oracle_fp8 as tf8
+
+
+def _encode_half_up(y):
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(ofp8._POS_VALS, a, side="left"), 1, len(ofp8._POS_VALS) - 1)
+    lo = hi - 1
+    pick_hi = (ofp8._POS_VALS[hi] - a) <= (a - ofp8._POS_VALS[lo])       # ties go up
+    code = np.where(pick_hi, ofp8._POS_CODES[hi], ofp8._POS_CODES[lo]).astype(np.uint8)
+    code = np.where(a >= 448.0, np.uint8(0x7E), code)
+    return np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def _decode_bias8(code):
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 0:
+        return (-1.0 if code & 0x80 else 1.0) * m * 2.0 ** -10
+    return (-1.0 if code & 0x80 else 1.0) * (1 + m / 8) * 2.0 ** (e - 8)
+
+
+@pytest.mark.parametrize("mutant", ["half_up", "bias8"])
+def test_fp8_mutants_fail_pins(monkeypatch, mutant):
+    if mutant == "half_up":
+        monkeypatch.setattr(ofp8, "encode", _encode_half_up)
+        pins = [tf8.test_array_encoder_equals_the_definition]
+    else:
+        monkeypatch.setattr(ofp8, "e4m3_to_f64", _decode_bias8)
+        pins = [lambda: tf8.test_code_points(0x38, 1.0), lambda: tf8.test_code_points(0x7E, 448.0)]
+    failed = 0
+    for t in pins:
+        try:
+            t()
+        except AssertionError:
             failed += 1
     assert failed > 0

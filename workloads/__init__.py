@@ -79,7 +79,7 @@ PROMPTS, SAMPLES, PROMPT_LEN = 32, 8, 1024
 def pool_shapes(N: int, Hkv: int, D: int, B: int, dtype: str):
     """Array shapes of the K and V pools in the library's documented layout:
     K [N, Hkv, D/x, B, x] with x elements per 16 bytes, V [N, Hkv, D, B]."""
-    x = 16 // (4 if dtype == "f32" else 2)
+    x = 16 // {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
     return (N, Hkv, D // x, B, x), (N, Hkv, D, B)
 
 
