@@ -58,7 +58,16 @@ typedef enum pkv_status {
   PKV_EHIP = -6           /* a HIP runtime call or kernel launch failed */
 } pkv_status;
 
-typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/* Pool element type.  PKV_FP8_E4M3: an fp8 KV cache ([ZENO] "Impact and
+ * Follow-Ups" and "Limitations": KV-cache quantization shrinks KV bytes
+ * further).  Reading of the format, which the pages leave open: OCP E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN
+ * 0x7F/0xFF, largest finite 448), stored as the value divided by a per-KV-head
+ * fp32 scale (separate scales for K and V; K chunks hold 16 dims, x = 16).
+ * Writes encode x / scale (fp32, correctly rounded) to the nearest E4M3 value,
+ * ties to an even mantissa, saturating at 448; reads use code value * scale.
+ * With fp8 pools the queries and the K/V rows written are bf16. */
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
 /* Attention flags (bit set).
  * PKV_ATTN_SHARED_KV: sequences of the batch share KV blocks (forked parallel
@@ -360,11 +369,15 @@ pkv_status pkv_sched_stats(const pkv_sched* sched, int64_t* tokens_held,
  *   k_pool/v_pool device pools (layout above), updated in place
  *   slot_mapping  device int64 [T]; slot < 0 = skip; slot >= num_blocks*B skipped
  * A bit copy: no conversion, NaN payloads kept.  Two tokens with the same slot
- * in one call race (caller's responsibility). */
+ * in one call race (caller's responsibility).
+ *   k_scale, v_scale  fp8 pools: device fp32 [Hkv], the per-KV-head scales
+ *                 (key/value are then bf16 and are encoded, see pkv_dtype);
+ *                 ignored (may be NULL) otherwise. */
 pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
                                  void* v_pool, const int64_t* slot_mapping, int32_t T,
                                  int32_t Hkv, int32_t D, int32_t B, int32_t num_blocks,
-                                 pkv_dtype dtype, void* hip_stream);
+                                 pkv_dtype dtype, const float* k_scale, const float* v_scale,
+                                 void* hip_stream);
 
 /* Copy-on-write block copies ([RTI] "Pages, from operating systems": shared
  * blocks are copied only when one sequence needs to modify them; [ZENO] OS-paging
@@ -500,8 +513,11 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *   workspace     device buffer of workspace_bytes >= pkv_attention_workspace_bytes
  *                 (may be NULL when that is 0)
  *   flags         0 or PKV_ATTN_SHARED_KV (other bits: PKV_EINVAL)
+ *   k_scale, v_scale  fp8 pools: device fp32 [Hkv] per-KV-head scales (the
+ *                 values read are code * scale); NULL otherwise
  * Compiled shapes: D in {64, 128}, B in {16, 32}; bf16 with Hq/Hkv in
- * {1, 2, 4, 8}; fp32 with Hq/Hkv in {1, 2, 4, 8}.  Others: PKV_EUNSUPPORTED. */
+ * {1, 2, 4, 8}; fp32 with Hq/Hkv in {1, 2, 4, 8}; fp8 pools (bf16 queries)
+ * with Hq/Hkv in {4, 8} and no new_key.  Others: PKV_EUNSUPPORTED. */
 pkv_status pkv_paged_attention_decode(float* out, const void* q, void* k_pool, void* v_pool,
                                       const void* new_key, const void* new_value,
                                       const int32_t* block_tables,
@@ -512,7 +528,8 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, void* k_pool, v
                                       const int32_t* plan, int32_t plan_items,
                                       int32_t plan_merge, void* workspace,
                                       size_t workspace_bytes, pkv_dtype dtype,
-                                      uint32_t flags, void* hip_stream);
+                                      uint32_t flags, const float* k_scale,
+                                      const float* v_scale, void* hip_stream);
 
 /* The two launches of pkv_paged_attention_decode, callable one at a time (for
  * per-kernel timing, or to put other work between them on the stream).
@@ -535,6 +552,7 @@ pkv_status pkv_paged_attention_main(float* out, const void* q, void* k_pool, voi
                                     int32_t partition_size, const int32_t* plan,
                                     int32_t plan_items, int32_t plan_merge, void* workspace,
                                     size_t workspace_bytes, pkv_dtype dtype, uint32_t flags,
+                                    const float* k_scale, const float* v_scale,
                                     void* hip_stream);
 pkv_status pkv_paged_attention_reduce(float* out, const int32_t* context_lens, int32_t S,
                                       int32_t Hq, int32_t Hkv, int32_t D, int32_t B,

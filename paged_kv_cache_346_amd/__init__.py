@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOBLOCKS, PKV_ENOSEQ, PKV_EEXIST, PKV_EUNSUPPORTED, PKV_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_ATTN_SHARED_KV = 1
 PKV_SCHED_RESERVE_MAX, PKV_SCHED_SWAP = 1, 2
 
@@ -108,7 +108,7 @@ SIGNATURES = {
     "pkv_bm_count_shared": (_i32, [_vp, _pi64, _i32, _pi64]),
     "pkv_bm_slots": (_i32, [_vp, _i64, _i32, _i32, _pi64]),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
-                                     _vp]),
+                                     _vp, _vp, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
@@ -120,10 +120,10 @@ SIGNATURES = {
                                   _pi32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
-                                          _i32, _i32, _vp, _sz, _i32, _u32, _vp]),
+                                          _i32, _i32, _vp, _sz, _i32, _u32, _vp, _vp, _vp]),
     "pkv_paged_attention_main": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _i32,
-                                        _i32, _vp, _sz, _i32, _u32, _vp]),
+                                        _i32, _vp, _sz, _i32, _u32, _vp, _vp, _vp]),
     "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _i32, _i32, _vp, _sz, _vp]),
 }
@@ -450,12 +450,33 @@ class Scheduler:
 # ---------------------------------------------------------------------------
 # device operations
 # ---------------------------------------------------------------------------
+_FP8_DTYPES = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return PKV_F32
     if t.dtype == torch.bfloat16:
         return PKV_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype in _FP8_DTYPES:
+        return PKV_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or uint8 / "
+                    f"float8_e4m3fn for fp8 E4M3)")
+
+
+def _row_dtype(pool: torch.Tensor) -> torch.dtype:
+    """dtype of the q / K / V rows that go with a pool (bf16 for fp8 pools)."""
+    return torch.bfloat16 if pool.dtype in _FP8_DTYPES else pool.dtype
+
+
+def _scales(k_pool, k_scale, v_scale, Hkv):
+    """Device pointers of the per-head fp8 scales (None for other pools)."""
+    if k_pool.dtype not in _FP8_DTYPES:
+        return None, None
+    for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t is None or t.dtype != torch.float32 or tuple(t.shape) != (Hkv,):
+            raise ValueError(f"fp8 pools need {name}: float32 [Hkv] on the device")
+    return _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale")
 
 
 def _dev(t: torch.Tensor, name: str) -> int:
@@ -474,7 +495,7 @@ def _stream(stream) -> int:
 
 def pool_shapes(num_blocks: int, Hkv: int, D: int, B: int, dtype: torch.dtype):
     """Tensor shapes of the K and V pools (K [N, Hkv, D/x, B, x], V [N, Hkv, D, B])."""
-    x = 16 // (4 if dtype == torch.float32 else 2)
+    x = 16 // (4 if dtype == torch.float32 else 1 if dtype in _FP8_DTYPES else 2)
     return (num_blocks, Hkv, D // x, B, x), (num_blocks, Hkv, D, B)
 
 
@@ -490,20 +511,24 @@ def _pool_geometry(k_pool: torch.Tensor, v_pool: torch.Tensor):
     return N, Hkv, D, B
 
 
-def pkv_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, stream=None) -> None:
-    """Write token i's K/V ([T, Hkv, D]) into slot slot_mapping[i] (int64; <0 skips)."""
+def pkv_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, stream=None,
+                          k_scale=None, v_scale=None) -> None:
+    """Write token i's K/V ([T, Hkv, D]) into slot slot_mapping[i] (int64; <0 skips).
+    fp8 pools: key/value are bf16 and are encoded with the per-head scales
+    (float32 [Hkv] device tensors)."""
     N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
     T = key.shape[0]
     if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
         raise ValueError("key/value must be [T, Hkv, D]")
-    if key.dtype != k_pool.dtype or value.dtype != k_pool.dtype:
-        raise ValueError("key/value dtype must match the pools")
+    if key.dtype != _row_dtype(k_pool) or value.dtype != _row_dtype(k_pool):
+        raise ValueError("key/value dtype must match the pools (bf16 for fp8 pools)")
     if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (T,):
         raise ValueError("slot_mapping must be int64 [T]")
+    ks, vs = _scales(k_pool, k_scale, v_scale, Hkv)
     _check(lib.pkv_reshape_and_cache(_dev(key, "key"), _dev(value, "value"),
                                      _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                                      _dev(slot_mapping, "slot_mapping"), T, Hkv, D, B, N,
-                                     _dtype_code(k_pool), _stream(stream)),
+                                     _dtype_code(k_pool), ks, vs, _stream(stream)),
            "pkv_reshape_and_cache")
 
 
@@ -631,7 +656,8 @@ def _plan_args(plan):
 
 
 def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                    scale, partition_size, plan, workspace, shared_kv, new_key, new_value):
+                    scale, partition_size, plan, workspace, shared_kv, new_key, new_value,
+                    k_scale=None, v_scale=None):
     N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
     S, Hq = q.shape[0], q.shape[1]
     nk = nv = None
@@ -642,8 +668,8 @@ def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_cont
             if tuple(t.shape) != (S, Hkv, D) or t.dtype != k_pool.dtype:
                 raise ValueError(f"{name} must be [S, Hkv, D] in the pool dtype")
         nk, nv = _dev(new_key, "new_key"), _dev(new_value, "new_value")
-    if tuple(q.shape) != (S, Hq, D) or q.dtype != k_pool.dtype:
-        raise ValueError("q must be [S, Hq, D] in the pool dtype")
+    if tuple(q.shape) != (S, Hq, D) or q.dtype != _row_dtype(k_pool):
+        raise ValueError("q must be [S, Hq, D] in the pool dtype (bf16 for fp8 pools)")
     if out.dtype != torch.float32 or tuple(out.shape) != (S, Hq, D):
         raise ValueError("out must be float32 [S, Hq, D]")
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
@@ -661,14 +687,15 @@ def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_cont
             Hkv, D,
             B, block_tables.shape[1], N, int(max_context_len), float(scale), int(partition_size),
             *_plan_args(plan), ws_ptr, ws_bytes, _dtype_code(k_pool),
-            PKV_ATTN_SHARED_KV if shared_kv else 0)
+            PKV_ATTN_SHARED_KV if shared_kv else 0, *_scales(k_pool, k_scale, v_scale, Hkv))
 
 
 def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
                                max_context_len: int, scale: float | None = None,
                                partition_size: int = 0, workspace=None, stream=None,
                                shared_kv: bool = False, plan: Plan | None = None,
-                               new_key=None, new_value=None) -> None:
+                               new_key=None, new_value=None, k_scale=None,
+                               v_scale=None) -> None:
     """out[s, h] = softmax(q[s, h] K_s^T * scale) V_s through the block tables.
 
     out fp32 [S, Hq, D]; q [S, Hq, D] in the pool dtype; block_tables int32
@@ -677,9 +704,12 @@ def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_len
     PKV_ATTN_SHARED_KV (the batch shares blocks; a load-policy hint only).
     `plan` (make_plan) runs exactly the batch's work items.  `new_key` /
     `new_value` ([S, Hkv, D]) append each sequence's token of this step (its
-    position context_lens[s]-1) into the pools in the same launch."""
+    position context_lens[s]-1) into the pools in the same launch.  fp8 pools
+    (uint8 / float8_e4m3fn) take bf16 q and the per-head k_scale / v_scale
+    (float32 [Hkv] device tensors)."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                           scale, partition_size, plan, workspace, shared_kv, new_key, new_value)
+                           scale, partition_size, plan, workspace, shared_kv, new_key, new_value,
+                           k_scale, v_scale)
     _check(lib.pkv_paged_attention_decode(*args, _stream(stream)), "pkv_paged_attention_decode")
 
 
@@ -687,10 +717,12 @@ def pkv_paged_attention_main(out, q, k_pool, v_pool, block_tables, context_lens,
                              max_context_len: int, scale: float | None = None,
                              partition_size: int = 0, workspace=None, stream=None,
                              shared_kv: bool = False, plan: Plan | None = None,
-                             new_key=None, new_value=None) -> None:
+                             new_key=None, new_value=None, k_scale=None,
+                             v_scale=None) -> None:
     """The main launch of pkv_paged_attention_decode alone (same arguments)."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                           scale, partition_size, plan, workspace, shared_kv, new_key, new_value)
+                           scale, partition_size, plan, workspace, shared_kv, new_key, new_value,
+                           k_scale, v_scale)
     _check(lib.pkv_paged_attention_main(*args, _stream(stream)), "pkv_paged_attention_main")
 
 

@@ -79,6 +79,8 @@ struct DecodeArgs {
   const void* new_k;  // [S, Hkv, D]: each sequence's token of this step, or nullptr
   const void* new_v;
   const int4* plan;  // host-built work list {s, g, p, L} per item, or nullptr
+  const float* k_scale;  // fp8 pools: per-KV-head scales of K and V, else nullptr
+  const float* v_scale;
   int S;
   int SG;            // S * Hkv: items per partition index
   int items;         // work items in the grid
@@ -371,11 +373,12 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
 //       no shuffle.  The A operand of lane (c, r) is dim 16dt + r at those
 //       tokens: two 8-byte runs of the V row (tokens 4c .. 4c+3 of each half).
 // ---------------------------------------------------------------------------
-template <int D, int B, int G, int NW, bool NT, bool AP>
-__global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
-                                                                const uint16_t* __restrict__ q,
-                                                                uint16_t* __restrict__ k_pool,
-                                                                uint16_t* __restrict__ v_pool) {
+template <int D, int B, int G, int NW, bool NT, bool AP, bool F8>
+__global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
+    DecodeArgs a, const uint16_t* __restrict__ q,
+    std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ k_pool,
+    std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ v_pool) {
+  static_assert(!(AP && F8), "the appending variant is bf16 only");
   constexpr int TILE = 32;
   constexpr int NJ = D / 32;   // q.k k-steps
   constexpr int NDT = D / 16;  // p.v output dim tiles
@@ -415,10 +418,14 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // fp8 tiles hold the raw codes (half the registers); compute() widens them
   struct Tile {
-    u32x4 k[2][NJ];
-    u32x2 v[2][NDT];
+    std::conditional_t<F8, u32x2, u32x4> k[2][NJ];
+    std::conditional_t<F8, uint32_t, u32x2> v[2][NDT];
   };
+  // fp8: the K scale joins the score scale, the V scale the output
+  const float score_scale = F8 ? a.scale_log2e * a.k_scale[it.g] : a.scale_log2e;
+  const float out_scale = F8 ? a.v_scale[it.g] : 1.f;
   const int t_first = it.start / TILE;
   const int n = (it.end + TILE - 1) / TILE - t_first;
   const int nb_last = (it.end + B - 1) / B - 1;  // last logical block of the partition
@@ -477,14 +484,26 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
     for (int th = 0; th < 2; ++th) {
       const size_t blk = (B == 16 && th == 1) ? pb1 : pb0;
       const int tok = (B == 16 ? 0 : 16 * th);  // token offset of this half in its block
-      const uint16_t* kb = k_pool + blk * blk_stride + head_off;
-      const uint16_t* vb = v_pool + blk * blk_stride + head_off;
+      const auto* kb = k_pool + blk * blk_stride + head_off;
+      const auto* vb = v_pool + blk * blk_stride + head_off;
+      if constexpr (F8) {
+        // K chunks hold 16 dims: lanes c = 0, 1 read the two halves of chunk 2j,
+        // lanes c = 2, 3 those of chunk 2j + 1 (512 contiguous bytes per load)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        tl.k[th][j] = pool_load<NT, u32x4>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+        for (int j = 0; j < NJ; ++j)
+          tl.k[th][j] = pool_load<NT, u32x2>(
+              kb + ((size_t)(2 * j + (c >> 1)) * B + tok + r) * 16 + (c & 1) * 8);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        tl.v[th][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+        for (int dt = 0; dt < NDT; ++dt)
+          tl.v[th][dt] = pool_load<kNtV, uint32_t>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          tl.k[th][j] = pool_load<NT, u32x4>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          tl.v[th][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+      }
     }
   };
 
@@ -492,7 +511,7 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
   // of the final tile:
   // lane (c, r) holds K chunks 4j + c of token 16TH + r and V dims 16dt + r of
   // tokens 16TH + 4c .. +3
-  auto substitute = [&](Tile& tl, auto half, int tn) {
+  auto substitute = [&](auto& tl, auto half, int tn) {  // appending (bf16) tiles only
     constexpr int TH = decltype(half)::value;
     if (r == (tn & 15)) {
 #pragma unroll
@@ -513,21 +532,21 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
     }
   };
 
-  auto compute = [&](int k, Tile& tl) {
+  auto compute_bf16 = [&](int k, u32x4 (&tk)[2][NJ], u32x2 (&tv)[2][NDT]) {
     const int T0 = (t_first + k) * TILE;
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int th = 0; th < 2; ++th)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tl.k[th][j]),
+        sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tk[th][j]),
                                                            qb[j], sacc[th], 0, 0, 0);
     // sv[4th + i]: token T0 + 16th + 4c + i
     float sv[8];
 #pragma unroll
     for (int th = 0; th < 2; ++th)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * a.scale_log2e;
+      for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * score_scale;
     if (T0 + TILE > it.end) {  // the partition's last, partial tile
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
@@ -540,7 +559,7 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
           const uint32_t mk =
               (2 * wd < nv ? 0x0000ffffu : 0u) | (2 * wd + 1 < nv ? 0xffff0000u : 0u);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt][wd] &= mk;
+          for (int dt = 0; dt < NDT; ++dt) tv[th][dt][wd] &= mk;
         }
       }
     }
@@ -571,12 +590,28 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
     const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const u32x4 va = {tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
+      const u32x4 va = {tv[0][dt][0], tv[0][dt][1], tv[1][dt][0], tv[1][dt][1]};
       acc[dt] *= alpha;
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), ph,
                                                         acc[dt], 0, 0, 0);
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pl,
                                                         acc[dt], 0, 0, 0);
+    }
+  };
+  auto compute = [&](int k, Tile& tl) {
+    if constexpr (F8) {
+      u32x4 tk[2][NJ];
+      u32x2 tv[2][NDT];
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) tk[th][j] = fp8x8_to_bf16(tl.k[th][j]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) tv[th][dt] = fp8x4_to_bf16(tl.v[th][dt]);
+      }
+      compute_bf16(k, tk, tv);
+    } else {
+      compute_bf16(k, tl.k, tl.v);
     }
   };
 
@@ -615,7 +650,7 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(DecodeArgs a,
   ls += shfl_xor_f(ls, 32);
   if (r < G) {
     const RowSink dst = row_sink<D, G>(a, it, r);
-    const float scl = dst.ml ? 1.f : 1.f / ls;
+    const float scl = (dst.ml ? 1.f : 1.f / ls) * out_scale;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<f32x4*>(dst.acc + 16 * dt + 4 * c) = acc[dt] * scl;
@@ -722,19 +757,28 @@ __global__ __launch_bounds__(TPR) void pa_reduce_kernel(float* __restrict__ out,
 // ---------------------------------------------------------------------------
 // Host dispatch.
 // ---------------------------------------------------------------------------
+// E is the pool element: float, uint16_t (bf16) or uint8_t (fp8 E4M3, whose
+// queries are bf16).  fp8 runs only on the MFMA kernel (G >= 4), never appending.
 template <typename E, int D, int B, int G, bool NT>
 static void launch_main_nt(const DecodeArgs& a, unsigned grid, const void* q, void* kp, void* vp,
                            hipStream_t st) {
-  constexpr bool kMfma = sizeof(E) == 2 && G >= 4;
+  constexpr bool kMfma = sizeof(E) <= 2 && G >= 4;
   // the append variants hold more registers and a longer epilogue; plain
   // launches compile without them
-  if constexpr (kMfma) {
+  if constexpr (sizeof(E) == 1) {
+    if constexpr (kMfma)
+      pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, false, true>
+          <<<grid, kWavesPerGroup * kWave, 0, st>>>(a, (const uint16_t*)q, (uint8_t*)kp,
+                                                     (uint8_t*)vp);
+  } else if constexpr (kMfma) {
     if (a.new_k)
-      pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, true><<<grid, kWavesPerGroup * kWave, 0, st>>>(
-          a, (const uint16_t*)q, (uint16_t*)kp, (uint16_t*)vp);
+      pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, true, false>
+          <<<grid, kWavesPerGroup * kWave, 0, st>>>(a, (const uint16_t*)q, (uint16_t*)kp,
+                                                     (uint16_t*)vp);
     else
-      pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, false><<<grid, kWavesPerGroup * kWave, 0, st>>>(
-          a, (const uint16_t*)q, (uint16_t*)kp, (uint16_t*)vp);
+      pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, false, false>
+          <<<grid, kWavesPerGroup * kWave, 0, st>>>(a, (const uint16_t*)q, (uint16_t*)kp,
+                                                     (uint16_t*)vp);
   } else {
     if (a.new_k)
       pa_valu_kernel<E, D, B, G, kWavesPerGroup, NT, true><<<grid, kWavesPerGroup * kWave, 0, st>>>(
@@ -757,6 +801,7 @@ static void launch_main(bool stream, const DecodeArgs& a, unsigned grid, const v
 template <typename E, int D, int B>
 static bool dispatch_g(int G, bool stream, const DecodeArgs& a, unsigned grid, const void* q,
                        void* kp, void* vp, hipStream_t st) {
+  if (sizeof(E) == 1 && G < 4) return false;
   switch (G) {
     case 1: launch_main<E, D, B, 1>(stream, a, grid, q, kp, vp, st); return true;
     case 2: launch_main<E, D, B, 2>(stream, a, grid, q, kp, vp, st); return true;
@@ -812,15 +857,19 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
                                  int32_t max_blocks, int32_t num_blocks, int32_t max_context_len,
                                  float scale, int32_t partition_size, const PlanArg& plan,
                                  void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-                                 uint32_t flags) {
+                                 uint32_t flags, const float* k_scale, const float* v_scale) {
   *groups = 0;
   if (flags & ~(uint32_t)PKV_ATTN_SHARED_KV) return PKV_EINVAL;
   if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 || num_blocks <= 0 ||
       max_context_len < 0 || partition_size < 0 || !std::isfinite(scale) || !plan_ok(plan))
     return PKV_EINVAL;
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_EINVAL;
+  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3) return PKV_EINVAL;
   const int G = Hq / Hkv;
   if (!shape_supported(D, B, G)) return PKV_EUNSUPPORTED;
+  if (dtype == PKV_FP8_E4M3) {
+    if (!k_scale || !v_scale) return PKV_EINVAL;
+    if (G < 4 || new_key) return PKV_EUNSUPPORTED;
+  }
   const int P = resolve_partition(partition_size, B);
   if (P == 0) return PKV_EINVAL;
   if (S == 0) return PKV_OK;
@@ -840,6 +889,8 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   a->new_k = new_key;
   a->new_v = new_value;
   a->plan = reinterpret_cast<const int4*>(plan.ptr);
+  a->k_scale = k_scale;
+  a->v_scale = v_scale;
   a->S = S;
   a->SG = S * Hkv;
   a->items = (int)items;
@@ -863,10 +914,11 @@ static pkv_status launch_main_kernel(const DecodeArgs& a, int64_t groups, const 
                                      void* k_pool, void* v_pool, int D, int B, int G,
                                      pkv_dtype dtype, uint32_t flags, hipStream_t st) {
   const bool stream = (flags & PKV_ATTN_SHARED_KV) == 0;
+  const unsigned g = (unsigned)groups;
   const bool ok =
-      dtype == PKV_F32
-          ? dispatch_d<float>(D, B, G, stream, a, (unsigned)groups, q, k_pool, v_pool, st)
-          : dispatch_d<uint16_t>(D, B, G, stream, a, (unsigned)groups, q, k_pool, v_pool, st);
+      dtype == PKV_F32    ? dispatch_d<float>(D, B, G, stream, a, g, q, k_pool, v_pool, st)
+      : dtype == PKV_BF16 ? dispatch_d<uint16_t>(D, B, G, stream, a, g, q, k_pool, v_pool, st)
+                          : dispatch_d<uint8_t>(D, B, G, stream, a, g, q, k_pool, v_pool, st);
   if (!ok) return PKV_EUNSUPPORTED;
   return launch_status();
 }
@@ -911,14 +963,16 @@ extern "C" pkv_status pkv_paged_attention_decode(
     const void* new_value, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
     int32_t partition_size, const int32_t* plan, int32_t plan_items, int32_t plan_merge,
-    void* workspace, size_t workspace_bytes, pkv_dtype dtype, uint32_t flags, void* hip_stream) {
+    void* workspace, size_t workspace_bytes, pkv_dtype dtype, uint32_t flags,
+    const float* k_scale, const float* v_scale, void* hip_stream) {
   DecodeArgs a;
   int64_t groups;
   const PlanArg pl{plan, plan_items, plan_merge};
   pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, new_key, new_value,
                                  block_tables, context_lens,
                                  S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
-                                 partition_size, pl, workspace, workspace_bytes, dtype, flags);
+                                 partition_size, pl, workspace, workspace_bytes, dtype, flags,
+                                 k_scale, v_scale);
   if (st != PKV_OK || groups == 0) return st;
   hipStream_t hs = (hipStream_t)hip_stream;
   st = launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, flags, hs);
@@ -931,14 +985,16 @@ extern "C" pkv_status pkv_paged_attention_main(
     const void* new_value, const int32_t* block_tables, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
     int32_t max_blocks, int32_t num_blocks, int32_t max_context_len, float scale,
     int32_t partition_size, const int32_t* plan, int32_t plan_items, int32_t plan_merge,
-    void* workspace, size_t workspace_bytes, pkv_dtype dtype, uint32_t flags, void* hip_stream) {
+    void* workspace, size_t workspace_bytes, pkv_dtype dtype, uint32_t flags,
+    const float* k_scale, const float* v_scale, void* hip_stream) {
   DecodeArgs a;
   int64_t groups;
   const PlanArg pl{plan, plan_items, plan_merge};
   pkv_status st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, new_key, new_value,
                                  block_tables, context_lens,
                                  S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len, scale,
-                                 partition_size, pl, workspace, workspace_bytes, dtype, flags);
+                                 partition_size, pl, workspace, workspace_bytes, dtype, flags,
+                                 k_scale, v_scale);
   if (st != PKV_OK || groups == 0) return st;
   return launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, flags,
                             (hipStream_t)hip_stream);

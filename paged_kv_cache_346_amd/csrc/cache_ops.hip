@@ -60,6 +60,49 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 // 16-byte vectors per block.  A pair naming a block outside its pool is
 // skipped.  src and dst may be the same pool (copy-on-write: within one call
 // no block is both a source and a destination).
+// fp8 pools: token i's K/V (bf16) divided by its KV head's scale and encoded
+// as E4M3 (f32_to_e4m3).  One thread per 16-dim chunk: K is one 16-byte store
+// (a K chunk holds 16 dims), V 16 byte stores into the chunk's dim rows.
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    const int64_t* __restrict__ slot_mapping, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, int64_t total, int Hkv, int D, int B, int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int nch = D / 16;
+  const int c = (int)(gid % nch);
+  const int64_t ih = gid / nch;  // token * Hkv + head
+  const int h = (int)(ih % Hkv);
+  const int64_t i = ih / Hkv;
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t pb = slot / B;
+  const int off = (int)(slot % B);
+  const int64_t src = ih * D + (int64_t)c * 16;
+  const float ks = k_scale[h], vs = v_scale[h];
+  uint32_t kw[4] = {0u, 0u, 0u, 0u};
+  uint8_t vb[16];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(key + src + 8 * half);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(value + src + 8 * half);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t kbits = (e & 1) ? (kx[e >> 1] & 0xffff0000u) : (kx[e >> 1] << 16);
+      const uint32_t vbits = (e & 1) ? (vx[e >> 1] & 0xffff0000u) : (vx[e >> 1] << 16);
+      const int d = 8 * half + e;
+      kw[d >> 2] |= f32_to_e4m3(__uint_as_float(kbits) / ks) << (8 * (d & 3));
+      vb[d] = (uint8_t)f32_to_e4m3(__uint_as_float(vbits) / vs);
+    }
+  }
+  const int64_t kb = ((pb * Hkv + h) * nch + c) * B * 16 + (int64_t)off * 16;
+  *reinterpret_cast<u32x4*>(k_pool + kb) = u32x4{kw[0], kw[1], kw[2], kw[3]};
+  uint8_t* vrow = v_pool + ((pb * Hkv + h) * D + (int64_t)c * 16) * B + off;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) vrow[(int64_t)d * B] = vb[d];
+}
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
     const u32x4* src_k, const u32x4* src_v, int src_blocks, u32x4* dst_k, u32x4* dst_v,
     int dst_blocks, const int32_t* __restrict__ pairs, int64_t total, int64_t units) {
@@ -80,15 +123,22 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 
 using namespace pkv;
 
+// bytes per pool element
+static int elem_size(pkv_dtype dtype) {
+  return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : dtype == PKV_FP8_E4M3 ? 1 : 0;
+}
+
 extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_pool,
                                             void* v_pool, const int64_t* slot_mapping,
                                             int32_t T, int32_t Hkv, int32_t D, int32_t B,
                                             int32_t num_blocks, pkv_dtype dtype,
+                                            const float* k_scale, const float* v_scale,
                                             void* hip_stream) {
   if (T < 0 || Hkv <= 0 || D <= 0 || B <= 0 || num_blocks <= 0) return PKV_EINVAL;
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_EINVAL;
-  const int es = dtype == PKV_F32 ? 4 : 2;
+  const int es = elem_size(dtype);
+  if (es == 0) return PKV_EINVAL;
   if ((D * es) % 16 != 0) return PKV_EINVAL;
+  if (dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_EINVAL;
   if (T == 0) return PKV_OK;
   if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !slot_mapping)
@@ -97,7 +147,11 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
   const dim3 grid((unsigned)((total + 255) / 256));
   hipStream_t st = (hipStream_t)hip_stream;
   const int64_t slots = (int64_t)num_blocks * B;
-  if (dtype == PKV_F32)
+  if (dtype == PKV_FP8_E4M3)
+    reshape_and_cache_fp8_kernel<<<grid, 256, 0, st>>>(
+        (const uint16_t*)key, (const uint16_t*)value, (uint8_t*)k_pool, (uint8_t*)v_pool,
+        slot_mapping, k_scale, v_scale, total, Hkv, D, B, slots);
+  else if (dtype == PKV_F32)
     reshape_and_cache_kernel<float><<<grid, 256, 0, st>>>(
         (const float*)key, (const float*)value, (float*)k_pool, (float*)v_pool, slot_mapping,
         total, Hkv, D, B, slots);
@@ -112,8 +166,8 @@ extern "C" pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t*
                                       int32_t n, int32_t Hkv, int32_t D, int32_t B,
                                       int32_t num_blocks, pkv_dtype dtype, void* hip_stream) {
   if (n < 0 || Hkv <= 0 || D <= 0 || B <= 0 || num_blocks <= 0) return PKV_EINVAL;
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_EINVAL;
-  const int es = dtype == PKV_F32 ? 4 : 2;
+  const int es = elem_size(dtype);
+  if (es == 0) return PKV_EINVAL;
   const int64_t block_bytes = (int64_t)Hkv * D * B * es;
   if (block_bytes % 16 != 0) return PKV_EINVAL;
   if (n == 0) return PKV_OK;
@@ -146,8 +200,8 @@ extern "C" pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_bloc
                                       int32_t B, pkv_dtype dtype, void* hip_stream) {
   if (n < 0 || Hkv <= 0 || D <= 0 || B <= 0 || dst_blocks <= 0 || src_blocks <= 0)
     return PKV_EINVAL;
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_EINVAL;
-  const int es = dtype == PKV_F32 ? 4 : 2;
+  const int es = elem_size(dtype);
+  if (es == 0) return PKV_EINVAL;
   const int64_t block_bytes = (int64_t)Hkv * D * B * es;
   if (block_bytes % 16 != 0) return PKV_EINVAL;
   if (n == 0) return PKV_OK;

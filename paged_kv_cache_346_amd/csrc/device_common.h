@@ -74,4 +74,44 @@ __device__ __forceinline__ float read_lane(float v, int src) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// fp8 E4M3 (OCP, gfx950's fp8) to bf16.  Every E4M3 value has at most four
+// significant bits, so its fp32 conversion has a zero low half and the top 16
+// bits are the bf16 value exactly.  Two codes from one half of a dword (hi
+// selects the upper half), first code in the low bf16.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+}
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2_t w) {
+  return u32x4{fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+               fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
+}
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t w) {
+  return u32x2_t{fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w)};
+}
+
+// fp32 to fp8 E4M3 code: nearest value, ties to an even mantissa, magnitudes
+// at or above 448 (the largest finite value) saturate to 448, NaN gives 0x7F.
+// Written from the format: 1 sign, 4 exponent (bias 7), 3 mantissa bits;
+// exponent field 0 holds m * 2^-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                      // NaN
+  const float af = __uint_as_float(a);
+  if (af >= 448.f) return sign | 0x7eu;
+  if (af < 0.015625f) {                                   // below 2^-6: steps of 2^-9
+    const uint32_t q = (uint32_t)__builtin_rintf(af * 512.f);  // exact scaling; 8 = 2^-6
+    return sign | q;
+  }
+  // keep 3 of the 23 mantissa bits, rounding the 20 dropped ones to nearest even;
+  // a carry moves into the exponent field
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+  const int e = (int)(r >> 23) - 127;                     // -6 .. 8
+  return sign | ((uint32_t)(e + 7) << 3) | ((r >> 20) & 7u);
+}
+
 }  // namespace pkv

@@ -39,6 +39,14 @@ __device__ __forceinline__ V pool_load(const uint16_t* p) {
     return *v;
 }
 template <bool NT, typename V>
+__device__ __forceinline__ V pool_load(const uint8_t* p) {
+  const V* v = reinterpret_cast<const V*>(p);
+  if constexpr (NT)
+    return __builtin_nontemporal_load(v);
+  else
+    return *v;
+}
+template <bool NT, typename V>
 __device__ __forceinline__ V pool_load(const float* p) {
   const V* v = reinterpret_cast<const V*>(p);
   if constexpr (NT)

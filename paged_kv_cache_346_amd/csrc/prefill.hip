@@ -250,7 +250,7 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   if (S < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || max_blocks <= 0 ||
       num_blocks <= 0 || max_query_len < 0 || !(scale > 0.f) || Hq % Hkv != 0)
     return PKV_EINVAL;
-  if (dtype != PKV_BF16 && dtype != PKV_F32) return PKV_EINVAL;
+  if (dtype != PKV_BF16 && dtype != PKV_F32 && dtype != PKV_FP8_E4M3) return PKV_EINVAL;
   const int G = Hq / Hkv;
   if (dtype != PKV_BF16 || (D != 64 && D != 128) || (B != 16 && B != 32) ||
       (G != 1 && G != 2 && G != 4 && G != 8))

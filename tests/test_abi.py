@@ -47,39 +47,55 @@ def test_host_validation_rejects_before_launch(pkv):
     # unsupported head dim / block size / group size
     for D, B, Hq, Hkv in ((96, 16, 8, 8), (128, 8, 8, 8), (128, 16, 24, 8)):
         st = lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, Hq, Hkv, D, B, 4,
-                                            8, 16, 0.1, 0, None, 0, 0, None, 0, pkv.PKV_BF16, 0, None)
+                                            8, 16, 0.1, 0, None, 0, 0, None, 0, pkv.PKV_BF16, 0, None,
+                                            None, None)
         assert st == pkv.PKV_EUNSUPPORTED
     # Hq not a multiple of Hkv, bad partition size, misaligned pointer, bad dtype
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 6, 4, 128, 16, 4,
-                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 48, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 48, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     # a partition may span at most 64 blocks (2048 tokens = 128 blocks of 16)
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 2048, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 2048, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_paged_attention_decode(odd, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 7, 0, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 7, 0, None, None, None) == pkv.PKV_EINVAL
     # unknown flag bits
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 2, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 2, None, None, None) == pkv.PKV_EINVAL
     # the step's new token needs both rows, 16-byte aligned
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, fake, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, fake, odd, tbl, tbl, 1, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     # long contexts need a workspace
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 64,
-                                          128, 1024, 0.1, 512, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_EINVAL
+                                          128, 1024, 0.1, 512, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     # empty batches are a no-op success
     assert lib.pkv_paged_attention_decode(None, None, None, None, None, None, None, None, 0, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None) == pkv.PKV_OK
+                                          8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_OK
     assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 8, 1,
-                                     None) == pkv.PKV_OK
+                                     None, None, None) == pkv.PKV_OK
     assert lib.pkv_copy_blocks(None, None, None, 0, 8, 128, 16, 8, 1, None) == pkv.PKV_OK
     assert lib.pkv_reshape_and_cache(odd, fake, fake, fake, tbl, 4, 8, 128, 16, 8, 1,
-                                     None) == pkv.PKV_EINVAL
+                                     None, None, None) == pkv.PKV_EINVAL
+    # fp8 pools need both scales; fp8 attention needs G >= 4, scales, no append
+    assert lib.pkv_reshape_and_cache(fake, fake, fake, fake, tbl, 4, 8, 128, 16, 8, 2,
+                                     None, None, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8,
+                                          128, 16, 4, 8, 16, 0.1, 0, None, 0, 0, None, 0, 2, 0,
+                                          fake, fake, None) == pkv.PKV_EUNSUPPORTED     # G = 1
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 32,
+                                          8, 128, 16, 4, 8, 16, 0.1, 0, None, 0, 0, None, 0, 2,
+                                          0, None, None, None) == pkv.PKV_EINVAL         # no scales
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, fake, fake, tbl, tbl, 1, 32,
+                                          8, 128, 16, 4, 8, 16, 0.1, 0, None, 0, 0, None, 0, 2,
+                                          0, fake, fake, None) == pkv.PKV_EUNSUPPORTED   # append
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 32,
+                                          8, 128, 16, 4, 8, 16, 0.1, 0, None, 0, 0, None, 0, 3,
+                                          0, fake, fake, None) == pkv.PKV_EINVAL         # dtype 3
     assert lib.pkv_copy_blocks(fake, odd, tbl, 3, 8, 128, 16, 8, 1, None) == pkv.PKV_EINVAL
 
 
