@@ -46,7 +46,7 @@ def test_fp8_cache_write_bit_exact(pkv):
     # at power-of-two scales), saturation, the subnormal range, +-0, NaN
     vals = sorted(v for v in fp8.DECODE if not np.isnan(v) and v >= 0)
     mids = [(a + b) / 2 for a, b in zip(vals, vals[1:])]
-    edge = np.array(mids + [-m for m in mids] + [500.0, -1e4, 2 ** -12, 3 * 2 ** -10, 0.0,
+    edge = np.array(mids + [-m for m in mids] + [500.0, -16384.0, 2 ** -12, 3 * 2 ** -10, 0.0,
                                                  -0.0], np.float32)
     edge_bits = _bits_of(edge)
     assert np.array_equal(((edge_bits.astype(np.uint32) << 16).view(np.float32)), edge)
