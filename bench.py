@@ -95,9 +95,14 @@ class Batch:
     on the device."""
 
     def __init__(self, pkv, torch, W, name: str, partition_size=None, layers=0, use_plan=True,
-                 append=True):
+                 append=True, kv_dtype=None):
         import numpy as np
         self.cfg = c = W.CONFIGS[name]
+        self.kv_dtype = kv_dtype or c.dtype
+        self.fp8 = self.kv_dtype == "fp8"
+        if self.kv_dtype not in (c.dtype, "fp8") or (self.fp8 and c.dtype != "bf16"):
+            raise ValueError(f"{name} is a {c.dtype} workload; fp8 KV goes with bf16 "
+                             f"workloads only")
         self.w = w = W.make(name, pools=False)
         t0 = time.perf_counter()
         bm = pkv.BlockManager(w.num_blocks, c.B, w.free_order)
@@ -140,10 +145,25 @@ class Batch:
                                           dtype=torch.float32).to(tdt)
             return x
 
-        esize = 4 if c.dtype == "f32" else 2
+        def codes(shape):
+            # finite E4M3 codes of magnitude below 4 (exponent field < 10), random sign
+            mag = torch.randint(0, 0x50, shape, generator=gen, device=dev, dtype=torch.uint8)
+            sign = torch.randint(0, 2, shape, generator=gen, device=dev, dtype=torch.uint8)
+            return mag | (sign << 7)
+
+        esize = 4 if c.dtype == "f32" else 1 if self.fp8 else 2
         pool_bytes = 2 * w.num_blocks * c.Hkv * c.D * c.B * esize
         self.layers = layers or max(2, min(16, -(-(4 << 30) // pool_bytes)))
-        self.pools = [(normal(ks), normal(vs)) for _ in range(self.layers)]
+        if self.fp8:
+            ks, vs = pkv.pool_shapes(w.num_blocks, c.Hkv, c.D, c.B, torch.uint8)
+            self.pools = [(codes(ks), codes(vs)) for _ in range(self.layers)]
+            # per-KV-head scales in the range a calibration would give for unit-variance K/V
+            self.k_scale = torch.linspace(0.02, 0.03, c.Hkv, device=dev, dtype=torch.float32)
+            self.v_scale = torch.linspace(0.03, 0.02, c.Hkv, device=dev, dtype=torch.float32)
+            append = False          # the fused append takes bf16 pools only
+        else:
+            self.pools = [(normal(ks), normal(vs)) for _ in range(self.layers)]
+            self.k_scale = self.v_scale = None
         self.pool_bytes = pool_bytes
         self.k_pool, self.v_pool = self.pools[0]
         self.q = self._to_dev(torch, w.q)
@@ -163,7 +183,8 @@ class Batch:
         nbytes = pkv.attention_workspace_bytes(c.S, c.Hq, c.D, self.mcl, self.P)
         self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         self.out = torch.empty((c.S, c.Hq, c.D), dtype=torch.float32, device=dev)
-        self.kv_bytes = w.kv_bytes
+        self.kv_bytes = w.kv_bytes // 2 if self.fp8 else w.kv_bytes
+        self.kv_elem_bytes = esize
         # blocks shared by several sequences are read with cached loads
         self.shared_entries = bm.count_shared(ids)
         self.shared_kv = self.shared_entries > 0
@@ -196,7 +217,8 @@ class Batch:
             pkv.copy_blocks(self.k_pool, self.v_pool, self.pairs)
         rec(1)
         if self.slots is not None and not self.append:
-            pkv.reshape_and_cache(self.k_new, self.v_new, self.k_pool, self.v_pool, self.slots)
+            pkv.reshape_and_cache(self.k_new, self.v_new, self.k_pool, self.v_pool, self.slots,
+                                  k_scale=self.k_scale, v_scale=self.v_scale)
         rec(2)
         if main_ev is not None:
             main_ev[0].record()
@@ -204,7 +226,7 @@ class Batch:
         pkv.paged_attention_main(self.out, self.q, self.k_pool, self.v_pool, self.tables,
                                  self.lens, self.mcl, partition_size=self.P, workspace=self.ws,
                                  shared_kv=self.shared_kv, plan=self.plan, new_key=nk,
-                                 new_value=nv)
+                                 new_value=nv, k_scale=self.k_scale, v_scale=self.v_scale)
         if main_ev is not None:
             main_ev[1].record()
         rec(3)
@@ -234,9 +256,12 @@ def cpu_baseline(batch, torch, budget_s: float):
         return t.cpu().numpy()
 
     kp, vp, q = host(batch.k_pool), host(batch.v_pool), host(batch.q)
+    scales = {}
+    if batch.fp8:
+        scales = {"k_scale": batch.k_scale.cpu().numpy(), "v_scale": batch.v_scale.cpu().numpy()}
     order = np.random.default_rng(7).permutation(c.S)
     done_bytes, done_seqs, elapsed = 0, 0, 0.0
-    per_tok = c.Hkv * c.D * 2 * c.elem_bytes
+    per_tok = c.Hkv * c.D * 2 * batch.kv_elem_bytes
     passes = 0
     with threadpool_limits(limits=1):
         while elapsed < budget_s and passes < 100:
@@ -244,7 +269,7 @@ def cpu_baseline(batch, torch, budget_s: float):
                 s = int(s)
                 rows = [(s, h) for h in range(c.Hq)]
                 t0 = time.perf_counter()
-                oracle_decode(q, kp, vp, batch.tables_host, batch.lens_host, rows=rows)
+                oracle_decode(q, kp, vp, batch.tables_host, batch.lens_host, rows=rows, **scales)
                 elapsed += time.perf_counter() - t0
                 done_bytes += int(batch.lens_host[s]) * per_tok
                 done_seqs += 1
@@ -528,6 +553,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama8b_gqa", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default=None,
+                    help="fp8: the same workload over fp8 E4M3 pools with per-head scales "
+                         "(bf16 workloads only; the cache write runs as reshape_and_cache)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition size (tokens per workgroup)")
     ap.add_argument("--separate-cache-write", action="store_true",
@@ -583,7 +611,7 @@ def main() -> int:
     name = args.config
     log(f"bench: building workload {name}")
     batch = Batch(pkv, torch, W, name, args.partition_size, args.layers, not args.no_plan,
-                  not args.separate_cache_write)
+                  not args.separate_cache_write, args.kv_dtype)
     c = batch.cfg
     log(f"bench: N={batch.w.num_blocks} blocks, KV {batch.kv_bytes / 1e6:.1f} MB, "
         f"{batch.n_pairs} CoW pairs, max L {batch.mcl}")
@@ -631,7 +659,8 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     value = batch.kv_bytes * args.steps / wall / 1e9
     k1_gbs = batch.kv_bytes / (k1_ms * 1e-3) / 1e9
-    traffic = load_traffic(name, 1)
+    traffic_key = name + (":fp8" if batch.fp8 else "")
+    traffic = load_traffic(traffic_key, 1)
     roofline = {
         "bound": "hbm",
         "achieved": round(k1_gbs, 1),
@@ -640,13 +669,17 @@ def main() -> int:
         "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
         "traffic": traffic,
         "kernel": "pa_mfma_kernel" if (c.dtype == "bf16" and c.G >= 4) else "pa_valu_kernel",
+        "traffic_key": traffic_key,
         "launch_us": round(k1_ms * 1e3, 2),
         "algorithmic_bytes_per_launch": batch.kv_bytes,
     }
     cfg_obj = {
-        "workload": f"{name}: {DESCRIPTIONS[name]}",
+        "workload": f"{name}: {DESCRIPTIONS[name]}" + (
+            "; KV pools in fp8 E4M3 with per-KV-head scales (finite codes below 4 in "
+            "magnitude), bf16 queries and new tokens" if batch.fp8 else ""),
         "seqs": c.S, "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D, "block_size": c.B,
-        "kv_dtype": c.dtype, "context_tokens": int(batch.lens_host.sum()),
+        "kv_dtype": "fp8_e4m3" if batch.fp8 else c.dtype,
+        "context_tokens": int(batch.lens_host.sum()),
         "max_context": batch.mcl, "pool_blocks": batch.w.num_blocks,
         "partition_size": batch.P or 512, "new_tokens": 0 if batch.slots is None
         else int(batch.slots.shape[0]), "cow_copies": batch.n_pairs,

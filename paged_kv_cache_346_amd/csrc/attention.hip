@@ -372,6 +372,17 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
 //       16th + 4c + i -- exactly the eight scores lane (c, r) holds, so P needs
 //       no shuffle.  The A operand of lane (c, r) is dim 16dt + r at those
 //       tokens: two 8-byte runs of the V row (tokens 4c .. 4c+3 of each half).
+// fp8 tiles are 64 tokens, two 32-token steps s of two quarters th each, and
+// take the same number of load instructions per byte as bf16 (gfx9 lets a wave
+// have at most 63 vector loads outstanding, so narrower loads would cap the
+// bytes in flight):
+//   K: one 16-byte load per lane is one whole 16-dim chunk of the layout and
+//      feeds two q.k k-steps: k-step j of lane c takes dims 16(4(j/2) + c) +
+//      8(j%2) .. +7 (q is read with the same mapping);
+//   V: one 8-byte load per lane: tokens 8c .. 8c+7 of step s, dim 16dt + r.
+//      For that, row r of quarter th stands for step token 8(r/4) + 4th + r%4,
+//      so the scores lane (c, r) holds -- rows 4c .. 4c+3 of both quarters --
+//      are exactly tokens 8c .. 8c+7, the p.v k index 8c + e is token 8c + e.
 // ---------------------------------------------------------------------------
 template <int D, int B, int G, int NW, bool NT, bool AP, bool F8>
 __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
@@ -379,16 +390,23 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
     std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ k_pool,
     std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ v_pool) {
   static_assert(!(AP && F8), "the appending variant is bf16 only");
-  constexpr int TILE = 32;
+  // bf16 tiles are 32 tokens (two 16-token quarters); fp8 tiles are 64 (four
+  // quarters, two MFMA steps) so that one tile's loads move the same 16 KiB
+  // per wave and keep as many bytes in flight
+  constexpr int NQ = F8 ? 4 : 2;
+  constexpr int TILE = 16 * NQ;
   constexpr int NJ = D / 32;   // q.k k-steps
   constexpr int NDT = D / 16;  // p.v output dim tiles
   static_assert(G >= 1 && G <= 16 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  // At B = 32 one V load instruction covers half of each 64-byte dim row and the
-  // other half follows in the next instruction; a nontemporal first read lets
-  // the line go before the second arrives (measured 17% slower), so V streams
-  // only at B = 16, where every V instruction reads whole lines.
-  constexpr bool kNtV = NT && B == 16;
+  // bf16 at B = 32: one V load instruction covers half of each 64-byte dim row
+  // and the other half follows in the next instruction; a nontemporal first
+  // read lets the line go before the second arrives (measured 17% slower), so
+  // bf16 V streams only at B = 16, where every V instruction reads whole lines.
+  // fp8 V instructions read whole lines at both block sizes; fp8 K loads read
+  // 64-byte runs whose other halves come with the next quarter's load.
+  constexpr bool kNtV = NT && (B == 16 || F8);
+  constexpr bool kNtK = NT && !F8;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane >> 4, r = lane & 15;
@@ -406,10 +424,11 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   bf16x8 qb[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
+    // the dims of k-step j in lane c (bf16: 32j + 8c; fp8: see above)
+    const int d0 = F8 ? 16 * (4 * (j >> 1) + c) + 8 * (j & 1) : 8 * (4 * j + c);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < G)
-      v = *reinterpret_cast<const u32x4*>(q + ((size_t)it.s * Hq + it.g * G + r) * D +
-                                          8 * (4 * j + c));
+      v = *reinterpret_cast<const u32x4*>(q + ((size_t)it.s * Hq + it.g * G + r) * D + d0);
     qb[j] = __builtin_bit_cast(bf16x8, v);
   }
 
@@ -418,16 +437,24 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fp8 tiles hold the raw codes (half the registers); compute() widens them
-  struct Tile {
-    std::conditional_t<F8, u32x2, u32x4> k[2][NJ];
-    std::conditional_t<F8, uint32_t, u32x2> v[2][NDT];
+  // bf16: K of quarter th, k-step j; V runs of quarter th, dim tile dt.
+  // fp8 (raw codes; the MFMA operands are widened to bf16 where they are used):
+  // K of quarter 2s + th, chunk 4i + c; V runs of step s, dim tile dt
+  struct Tile16 {
+    u32x4 k[NQ][NJ];
+    u32x2 v[NQ][NDT];
   };
+  struct Tile8 {
+    u32x4 k[NQ][NJ / 2];
+    u32x2 v[NQ / 2][NDT];
+  };
+  using Tile = std::conditional_t<F8, Tile8, Tile16>;
   // fp8: the K scale joins the score scale, the V scale the output
   const float score_scale = F8 ? a.scale_log2e * a.k_scale[it.g] : a.scale_log2e;
   const float out_scale = F8 ? a.v_scale[it.g] : 1.f;
-  const int t_first = it.start / TILE;
-  const int n = (it.end + TILE - 1) / TILE - t_first;
+  // tile k covers tokens it.start + TILE*k .. +TILE-1 (partitions start at
+  // multiples of 32 and of B)
+  const int n = (it.end - it.start + TILE - 1) / TILE;
   const int nb_last = (it.end + B - 1) / B - 1;  // last logical block of the partition
   const size_t head_off = (size_t)it.g * (D * B);
   const size_t blk_stride = (size_t)a.Hkv * (D * B);
@@ -475,31 +502,45 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   };
 
   auto load = [&](int k, Tile& tl) {
-    const int lb0 = (t_first + k) * TILE / B;
-    const int pb0 = tw.at(lb0, a.num_blocks);
-    // B = 16: the tile's second block; past the partition end it repeats the
-    // first (those tokens are masked)
-    const int pb1 = B == 16 ? tw.at(min(lb0 + 1, nb_last), a.num_blocks) : pb0;
+    const int lb0 = (it.start + k * TILE) / B;
+    // the tile's blocks (B / 16 quarters each); a block past the partition end
+    // repeats the last one (its tokens are masked)
+    constexpr int NBT = TILE / B;
+    int pbs[NBT];
 #pragma unroll
-    for (int th = 0; th < 2; ++th) {
-      const size_t blk = (B == 16 && th == 1) ? pb1 : pb0;
-      const int tok = (B == 16 ? 0 : 16 * th);  // token offset of this half in its block
-      const auto* kb = k_pool + blk * blk_stride + head_off;
-      const auto* vb = v_pool + blk * blk_stride + head_off;
-      if constexpr (F8) {
-        // K chunks hold 16 dims: lanes c = 0, 1 read the two halves of chunk 2j,
-        // lanes c = 2, 3 those of chunk 2j + 1 (512 contiguous bytes per load)
+    for (int i = 0; i < NBT; ++i) pbs[i] = tw.at(min(lb0 + i, nb_last), a.num_blocks);
+    if constexpr (F8) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          tl.k[th][j] = pool_load<NT, u32x2>(
-              kb + ((size_t)(2 * j + (c >> 1)) * B + tok + r) * 16 + (c & 1) * 8);
+      for (int st = 0; st < 2; ++st) {
+        // K row r of quarter th: step token 8(r/4) + 4th + r%4; V lane c: step
+        // tokens 8c .. 8c+7.  At B = 16 a step spans two blocks, so the block
+        // depends on the lane: K rows r >= 8 and V lanes c >= 2 are in the second
+        const size_t bk = B == 16 ? (r >= 8 ? pbs[2 * st + 1] : pbs[2 * st]) : pbs[st];
+        const size_t bv = B == 16 ? (c >= 2 ? pbs[2 * st + 1] : pbs[2 * st]) : pbs[st];
+        const int ktok = (8 * (r >> 2) + (r & 3)) % B;  // + 4th
+        const int vtok = (8 * c) % B;
+        const auto* kb = k_pool + bk * blk_stride + head_off;
+        const auto* vb = v_pool + bv * blk_stride + head_off;
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+          for (int i = 0; i < NJ / 2; ++i)
+            tl.k[2 * st + th][i] =
+                pool_load<kNtK, u32x4>(kb + ((size_t)(4 * i + c) * B + ktok + 4 * th) * 16);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-          tl.v[th][dt] = pool_load<kNtV, uint32_t>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
-      } else {
+          tl.v[st][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + vtok);
+      }
+    } else {
+#pragma unroll
+      for (int th = 0; th < NQ; ++th) {
+        const size_t blk = pbs[th * 16 / B];
+        const int tok = (16 * th) % B;  // token offset of this quarter in its block
+        const auto* kb = k_pool + blk * blk_stride + head_off;
+        const auto* vb = v_pool + blk * blk_stride + head_off;
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          tl.k[th][j] = pool_load<NT, u32x4>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+          tl.k[th][j] = pool_load<kNtK, u32x4>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
           tl.v[th][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
@@ -532,34 +573,83 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
     }
   };
 
-  auto compute_bf16 = [&](int k, u32x4 (&tk)[2][NJ], u32x2 (&tv)[2][NDT]) {
-    const int T0 = (t_first + k) * TILE;
+  // MFMA operands: the K vector of quarter th at k-step j, and the V runs of dim
+  // tile dt over quarters q0, q0 + 1.  fp8 codes are widened to bf16 here, one
+  // operand at a time, so no widened tile is ever held in registers
+  auto k_operand = [&](Tile& tl, int th, int j) {
+    if constexpr (F8) {
+      const u32x4 w = tl.k[th][j >> 1];
+      return __builtin_bit_cast(bf16x8, fp8x8_to_bf16((j & 1) ? u32x2{w[2], w[3]}
+                                                              : u32x2{w[0], w[1]}));
+    } else {
+      return __builtin_bit_cast(bf16x8, tl.k[th][j]);
+    }
+  };
+  auto v_operand = [&](Tile& tl, int q0, int dt) {
+    if constexpr (F8) {
+      return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(tl.v[q0 / 2][dt]));
+    } else {
+      return __builtin_bit_cast(bf16x8, u32x4{tl.v[q0][dt][0], tl.v[q0][dt][1],
+                                              tl.v[q0 + 1][dt][0], tl.v[q0 + 1][dt][1]});
+    }
+  };
+  // Tokens past the partition end: their scores become -inf and their V
+  // elements zero (the pool may hold anything there, NaN included, and a zero
+  // weight times NaN would still reach the output).  bf16: this lane's 4-token
+  // run in quarter th keeps its first nv elements; fp8: its 8-token run of
+  // step q0 / 2 keeps its first nv.
+  auto mask_v = [&](Tile& tl, int th, int nv) {
+    if constexpr (F8) {
+      const uint32_t m0 = nv >= 4 ? 0xffffffffu : (1u << (8 * nv)) - 1u;
+      const uint32_t m1 = nv >= 8 ? 0xffffffffu : nv <= 4 ? 0u : (1u << (8 * (nv - 4))) - 1u;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        tl.v[th / 2][dt][0] &= m0;
+        tl.v[th / 2][dt][1] &= m1;
+      }
+    } else {
+#pragma unroll
+      for (int wd = 0; wd < 2; ++wd) {
+        const uint32_t mk =
+            (2 * wd < nv ? 0x0000ffffu : 0u) | (2 * wd + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt][wd] &= mk;
+      }
+    }
+  };
+
+  // one 32-token MFMA step over quarters q0, q0 + 1 of a tile: tokens T0 ..
+  // T0 + 31, of which T0 is valid
+  auto step32 = [&](Tile& tl, auto q0c, int T0) {
+    constexpr int q0 = decltype(q0c)::value;
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int th = 0; th < 2; ++th)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tk[th][j]),
-                                                           qb[j], sacc[th], 0, 0, 0);
-    // sv[4th + i]: token T0 + 16th + 4c + i
+        sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tl, q0 + th, j), qb[j],
+                                                           sacc[th], 0, 0, 0);
+    // sv[4th + i]: token T0 + 16th + 4c + i (bf16), T0 + 8c + 4th + i (fp8)
     float sv[8];
 #pragma unroll
     for (int th = 0; th < 2; ++th)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * score_scale;
-    if (T0 + TILE > it.end) {  // the partition's last, partial tile
+    if (T0 + 32 > it.end) {  // the partition's last, partial step
+      if constexpr (F8) {
+        const int nv = min(max(it.end - (T0 + 8 * c), 0), 8);
 #pragma unroll
-      for (int th = 0; th < 2; ++th) {
-        const int nv = min(max(it.end - (T0 + 16 * th + 4 * c), 0), 4);
+        for (int e = 0; e < 8; ++e)
+          if (e >= nv) sv[e] = -INFINITY;
+        mask_v(tl, q0, nv);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i >= nv) sv[4 * th + i] = -INFINITY;
+        for (int th = 0; th < 2; ++th) {
+          const int nv = min(max(it.end - (T0 + 16 * th + 4 * c), 0), 4);
 #pragma unroll
-        for (int wd = 0; wd < 2; ++wd) {
-          const uint32_t mk =
-              (2 * wd < nv ? 0x0000ffffu : 0u) | (2 * wd + 1 < nv ? 0xffff0000u : 0u);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) tv[th][dt][wd] &= mk;
+          for (int i = 0; i < 4; ++i)
+            if (i >= nv) sv[4 * th + i] = -INFINITY;
+          mask_v(tl, q0 + th, nv);
         }
       }
     }
@@ -568,7 +658,7 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float mn = fmaxf(m, mx);  // finite: tile token T0 is valid
+    const float mn = fmaxf(m, mx);  // finite: token T0 is valid
     const float alpha = fast_exp2(m - mn);
     m = mn;
     u32x4 phw, plw;
@@ -590,28 +680,17 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
     const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const u32x4 va = {tv[0][dt][0], tv[0][dt][1], tv[1][dt][0], tv[1][dt][1]};
+      const bf16x8 va = v_operand(tl, q0, dt);
       acc[dt] *= alpha;
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), ph,
-                                                        acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pl,
-                                                        acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[dt], 0, 0, 0);
     }
   };
   auto compute = [&](int k, Tile& tl) {
+    const int T0 = it.start + k * TILE;
+    step32(tl, std::integral_constant<int, 0>{}, T0);
     if constexpr (F8) {
-      u32x4 tk[2][NJ];
-      u32x2 tv[2][NDT];
-#pragma unroll
-      for (int th = 0; th < 2; ++th) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) tk[th][j] = fp8x8_to_bf16(tl.k[th][j]);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) tv[th][dt] = fp8x4_to_bf16(tl.v[th][dt]);
-      }
-      compute_bf16(k, tk, tv);
-    } else {
-      compute_bf16(k, tl.k, tl.v);
+      if (T0 + 32 < it.end) step32(tl, std::integral_constant<int, 2>{}, T0 + 32);
     }
   };
 
@@ -632,7 +711,7 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
 
   if constexpr (AP) {
     pipelined<Tile>(n, load, compute, stage_new, [&](int k, Tile& tl) {
-      const int tn = tnew - (t_first + k) * TILE;  // in this tile when appending
+      const int tn = tnew - (it.start + k * TILE);  // in this tile when appending
       if (appends) {
         if (tn < 16)
           substitute(tl, std::integral_constant<int, 0>{}, tn);

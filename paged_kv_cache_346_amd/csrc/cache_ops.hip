@@ -56,13 +56,11 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
-// dst_pool[dst] = src_pool[src] for each pair (src, dst), K and V; `units`
-// 16-byte vectors per block.  A pair naming a block outside its pool is
-// skipped.  src and dst may be the same pool (copy-on-write: within one call
-// no block is both a source and a destination).
 // fp8 pools: token i's K/V (bf16) divided by its KV head's scale and encoded
-// as E4M3 (f32_to_e4m3).  One thread per 16-dim chunk: K is one 16-byte store
-// (a K chunk holds 16 dims), V 16 byte stores into the chunk's dim rows.
+// as E4M3 (f32_to_e4m3).  One thread per 4 dims, so a decode step's few
+// tokens still spread over the whole chip: K is one 4-byte store into the
+// token's 16-byte vector of its 16-dim chunk, V 4 byte stores into the dims'
+// rows.
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
@@ -70,39 +68,41 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const float* __restrict__ v_scale, int64_t total, int Hkv, int D, int B, int64_t num_slots) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
-  const int nch = D / 16;
-  const int c = (int)(gid % nch);
-  const int64_t ih = gid / nch;  // token * Hkv + head
+  const int nq = D / 4;
+  const int q = (int)(gid % nq);  // dims 4q .. 4q+3
+  const int64_t ih = gid / nq;    // token * Hkv + head
   const int h = (int)(ih % Hkv);
   const int64_t i = ih / Hkv;
   const int64_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t pb = slot / B;
   const int off = (int)(slot % B);
-  const int64_t src = ih * D + (int64_t)c * 16;
+  const int64_t src = ih * D + (int64_t)q * 4;
   const float ks = k_scale[h], vs = v_scale[h];
-  uint32_t kw[4] = {0u, 0u, 0u, 0u};
-  uint8_t vb[16];
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 kx = *reinterpret_cast<const u32x2*>(key + src);
+  const u32x2 vx = *reinterpret_cast<const u32x2*>(value + src);
+  uint32_t kw = 0u;
+  uint8_t vb[4];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const u32x4 kx = *reinterpret_cast<const u32x4*>(key + src + 8 * half);
-    const u32x4 vx = *reinterpret_cast<const u32x4*>(value + src + 8 * half);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t kbits = (e & 1) ? (kx[e >> 1] & 0xffff0000u) : (kx[e >> 1] << 16);
-      const uint32_t vbits = (e & 1) ? (vx[e >> 1] & 0xffff0000u) : (vx[e >> 1] << 16);
-      const int d = 8 * half + e;
-      kw[d >> 2] |= f32_to_e4m3(__uint_as_float(kbits) / ks) << (8 * (d & 3));
-      vb[d] = (uint8_t)f32_to_e4m3(__uint_as_float(vbits) / vs);
-    }
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t kbits = (e & 1) ? (kx[e >> 1] & 0xffff0000u) : (kx[e >> 1] << 16);
+    const uint32_t vbits = (e & 1) ? (vx[e >> 1] & 0xffff0000u) : (vx[e >> 1] << 16);
+    kw |= f32_to_e4m3(__uint_as_float(kbits) / ks) << (8 * e);
+    vb[e] = (uint8_t)f32_to_e4m3(__uint_as_float(vbits) / vs);
   }
-  const int64_t kb = ((pb * Hkv + h) * nch + c) * B * 16 + (int64_t)off * 16;
-  *reinterpret_cast<u32x4*>(k_pool + kb) = u32x4{kw[0], kw[1], kw[2], kw[3]};
-  uint8_t* vrow = v_pool + ((pb * Hkv + h) * D + (int64_t)c * 16) * B + off;
+  const int nch = D / 16;
+  const int64_t kb = ((pb * Hkv + h) * nch + q / 4) * B * 16 + (int64_t)off * 16 + (q & 3) * 4;
+  *reinterpret_cast<uint32_t*>(k_pool + kb) = kw;
+  uint8_t* vrow = v_pool + ((pb * Hkv + h) * D + (int64_t)q * 4) * B + off;
 #pragma unroll
-  for (int d = 0; d < 16; ++d) vrow[(int64_t)d * B] = vb[d];
+  for (int e = 0; e < 4; ++e) vrow[(int64_t)e * B] = vb[e];
 }
 
+// dst_pool[dst] = src_pool[src] for each pair (src, dst), K and V; `units`
+// 16-byte vectors per block.  A pair naming a block outside its pool is
+// skipped.  src and dst may be the same pool (copy-on-write: within one call
+// no block is both a source and a destination).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
     const u32x4* src_k, const u32x4* src_v, int src_blocks, u32x4* dst_k, u32x4* dst_v,
     int dst_blocks, const int32_t* __restrict__ pairs, int64_t total, int64_t units) {
@@ -143,7 +143,8 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
   if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !slot_mapping)
     return PKV_EINVAL;
-  const int64_t total = (int64_t)T * Hkv * (D * es / 16);
+  // threads: one per 16-byte vector of a token's row; fp8, one per 4 dims
+  const int64_t total = (int64_t)T * Hkv * (dtype == PKV_FP8_E4M3 ? D / 4 : D * es / 16);
   const dim3 grid((unsigned)((total + 255) / 256));
   hipStream_t st = (hipStream_t)hip_stream;
   const int64_t slots = (int64_t)num_blocks * B;

@@ -94,12 +94,15 @@ def _fp8_pools(rng, lens, Hkv, D, B, k_scale, v_scale, extra=4):
 LENS = (1, 2, 15, 16, 17, 33, 100, 511, 512, 513, 1030, 1300)
 
 
-@pytest.mark.parametrize("G,D,B,P,plan", [(4, 128, 16, 512, True), (8, 128, 16, 256, False),
-                                          (8, 128, 32, 512, True), (4, 64, 32, 128, False),
-                                          (8, 64, 16, 1024, True)])
-def test_fp8_attention_matches_reference(pkv, G, D, B, P, plan):
+# partitions of 96 tokens end inside a 64-token fp8 tile; shared: cached loads
+@pytest.mark.parametrize("G,D,B,P,plan,shared", [
+    (4, 128, 16, 512, True, False), (8, 128, 16, 256, False, False),
+    (8, 128, 32, 512, True, False), (4, 64, 32, 128, False, False),
+    (8, 64, 16, 1024, True, False), (4, 128, 32, 96, False, False),
+    (8, 128, 16, 96, True, True), (4, 128, 16, 512, False, True)])
+def test_fp8_attention_matches_reference(pkv, G, D, B, P, plan, shared):
     import torch
-    say(f"case fp8 attention G={G} D={D} B={B} P={P} plan={plan}")
+    say(f"case fp8 attention G={G} D={D} B={B} P={P} plan={plan} shared={shared}")
     rng = np.random.default_rng(70 + G + D + B + P)
     Hkv = 2
     k_scale = rng.uniform(0.004, 0.03, Hkv).astype(np.float32)
@@ -114,7 +117,7 @@ def test_fp8_attention_matches_reference(pkv, G, D, B, P, plan):
     pl = pkv.make_plan(clens, Hkv, B, tables.shape[1], mcl, P) if plan else None
     pkv.paged_attention_decode(out, to_dev(q), _u8(kp), _u8(vp), torch.from_numpy(tables).cuda(),
                                torch.from_numpy(clens).cuda(), mcl, partition_size=P,
-                               workspace=ws, plan=pl,
+                               workspace=ws, plan=pl, shared_kv=shared,
                                k_scale=torch.from_numpy(k_scale).cuda(),
                                v_scale=torch.from_numpy(v_scale).cuda())
     torch.cuda.synchronize()
