@@ -160,7 +160,6 @@ class Batch:
             # per-KV-head scales in the range a calibration would give for unit-variance K/V
             self.k_scale = torch.linspace(0.02, 0.03, c.Hkv, device=dev, dtype=torch.float32)
             self.v_scale = torch.linspace(0.03, 0.02, c.Hkv, device=dev, dtype=torch.float32)
-            append = False          # the fused append takes bf16 pools only
         else:
             self.pools = [(normal(ks), normal(vs)) for _ in range(self.layers)]
             self.k_scale = self.v_scale = None
@@ -555,7 +554,7 @@ def main() -> int:
     ap.add_argument("--config", default="llama8b_gqa", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default=None,
                     help="fp8: the same workload over fp8 E4M3 pools with per-head scales "
-                         "(bf16 workloads only; the cache write runs as reshape_and_cache)")
+                         "(bf16 workloads only; queries and new tokens stay bf16)")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition size (tokens per workgroup)")
     ap.add_argument("--separate-cache-write", action="store_true",

@@ -479,7 +479,8 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *   out           device fp32 [S, Hq, D]: softmax(q K^T * scale) V per (s, h)
  *   q             device [S, Hq, D], pool dtype
  *   k_pool/v_pool device pools; written only when new_key is given
- *   new_key, new_value   NULL, or device [S, Hkv, D] in the pool dtype: the
+ *   new_key, new_value   NULL, or device [S, Hkv, D] in the pool dtype (bf16
+ *                 for fp8 pools, encoded as pkv_reshape_and_cache does): the
  *                 token each sequence appends this step (a decode step).  The
  *                 token is the sequence's last, at position context_lens[s]-1;
  *                 it is written into that position's slot (block
@@ -517,7 +518,7 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *                 values read are code * scale); NULL otherwise
  * Compiled shapes: D in {64, 128}, B in {16, 32}; bf16 with Hq/Hkv in
  * {1, 2, 4, 8}; fp32 with Hq/Hkv in {1, 2, 4, 8}; fp8 pools (bf16 queries)
- * with Hq/Hkv in {4, 8} and no new_key.  Others: PKV_EUNSUPPORTED. */
+ * with Hq/Hkv in {4, 8}.  Others: PKV_EUNSUPPORTED. */
 pkv_status pkv_paged_attention_decode(float* out, const void* q, void* k_pool, void* v_pool,
                                       const void* new_key, const void* new_value,
                                       const int32_t* block_tables,

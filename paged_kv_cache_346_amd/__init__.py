@@ -665,8 +665,9 @@ def _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_cont
         raise ValueError("new_key and new_value go together")
     if new_key is not None:
         for t, name in ((new_key, "new_key"), (new_value, "new_value")):
-            if tuple(t.shape) != (S, Hkv, D) or t.dtype != k_pool.dtype:
-                raise ValueError(f"{name} must be [S, Hkv, D] in the pool dtype")
+            if tuple(t.shape) != (S, Hkv, D) or t.dtype != _row_dtype(k_pool):
+                raise ValueError(f"{name} must be [S, Hkv, D] in the pool dtype "
+                                 f"(bf16 for fp8 pools)")
         nk, nv = _dev(new_key, "new_key"), _dev(new_value, "new_value")
     if tuple(q.shape) != (S, Hq, D) or q.dtype != _row_dtype(k_pool):
         raise ValueError("q must be [S, Hq, D] in the pool dtype (bf16 for fp8 pools)")
@@ -703,8 +704,9 @@ def pkv_paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_len
     is needed when max_context_len exceeds one partition.  `shared_kv` sets
     PKV_ATTN_SHARED_KV (the batch shares blocks; a load-policy hint only).
     `plan` (make_plan) runs exactly the batch's work items.  `new_key` /
-    `new_value` ([S, Hkv, D]) append each sequence's token of this step (its
-    position context_lens[s]-1) into the pools in the same launch.  fp8 pools
+    `new_value` ([S, Hkv, D]; bf16 for fp8 pools, encoded with the scales) append
+    each sequence's token of this step (its position context_lens[s]-1) into the
+    pools in the same launch.  fp8 pools
     (uint8 / float8_e4m3fn) take bf16 q and the per-head k_scale / v_scale
     (float32 [Hkv] device tensors)."""
     args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,

@@ -389,7 +389,6 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
     DecodeArgs a, const uint16_t* __restrict__ q,
     std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ k_pool,
     std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ v_pool) {
-  static_assert(!(AP && F8), "the appending variant is bf16 only");
   // bf16 tiles are 32 tokens (two 16-token quarters); fp8 tiles are 64 (four
   // quarters, two MFMA steps) so that one tile's loads move the same 16 KiB
   // per wave and keep as many bytes in flight
@@ -466,17 +465,23 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   // what the pool held there, and only after the tile loop does the wave write
   // the token into its slot (gfx9 counts stores with loads, so a store inside
   // the loop would make every later load wait for it; nothing reads the slot
-  // back).
+  // back).  fp8 pools: the token (bf16) is encoded with its head's scales as
+  // the cache write does, and its codes are staged, substituted and stored.
   __shared__ __align__(16) uint16_t s_new[kWavesPerGroup][2][D];
   uint16_t* lds_k = s_new[threadIdx.x / kWave][0];
   uint16_t* lds_v = s_new[threadIdx.x / kWave][1];
+  uint8_t* lds_k8 = reinterpret_cast<uint8_t*>(lds_k);
+  uint8_t* lds_v8 = reinterpret_cast<uint8_t*>(lds_v);
   const bool appends = AP && it.tail;
   const int tnew = it.end - 1;
-  // lanes < D/8 hold K dims 8*lane .. +7 (one chunk of the K layout); every
-  // lane holds V dims lane + 64i, so four lanes share each V line it writes
+  // lanes < D/8 hold K dims 8*lane .. +7 (bf16: one chunk of the K layout;
+  // fp8: half of one); every lane holds V dims lane + 64i, so four lanes share
+  // each V line it writes
   constexpr int NVD = D / kWave;
   u32x4 nk = {0u, 0u, 0u, 0u};
   uint16_t nv[NVD];
+  u32x2 nk8 = {0u, 0u};
+  uint8_t nv8[NVD];
   if (appends) {
     const size_t row = ((size_t)it.s * a.Hkv + it.g) * D;
     if (lane < D / 8)
@@ -485,13 +490,31 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < NVD; ++i)
       nv[i] = reinterpret_cast<const uint16_t*>(a.new_v)[row + lane + kWave * i];
+    if constexpr (F8) {
+      const float ks = a.k_scale[it.g], vs = a.v_scale[it.g];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = nk[e >> 1];
+        const uint32_t bits = (e & 1) ? (w & 0xffff0000u) : (w << 16);
+        nk8[e >> 2] |= f32_to_e4m3(__uint_as_float(bits) / ks) << (8 * (e & 3));
+      }
+#pragma unroll
+      for (int i = 0; i < NVD; ++i)
+        nv8[i] = (uint8_t)f32_to_e4m3(__uint_as_float((uint32_t)nv[i] << 16) / vs);
+    }
   }
   auto stage_new = [&]() {
     if constexpr (AP) {
       if (appends) {
-        if (lane < D / 8) *reinterpret_cast<u32x4*>(lds_k + 8 * lane) = nk;
+        if constexpr (F8) {
+          if (lane < D / 8) *reinterpret_cast<u32x2*>(lds_k8 + 8 * lane) = nk8;
 #pragma unroll
-        for (int i = 0; i < NVD; ++i) lds_v[lane + kWave * i] = nv[i];
+          for (int i = 0; i < NVD; ++i) lds_v8[lane + kWave * i] = nv8[i];
+        } else {
+          if (lane < D / 8) *reinterpret_cast<u32x4*>(lds_k + 8 * lane) = nk;
+#pragma unroll
+          for (int i = 0; i < NVD; ++i) lds_v[lane + kWave * i] = nv[i];
+        }
       }
       // other lanes of the wave read the staged token back: order the LDS
       // writes before those reads
@@ -552,7 +575,7 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   // of the final tile:
   // lane (c, r) holds K chunks 4j + c of token 16TH + r and V dims 16dt + r of
   // tokens 16TH + 4c .. +3
-  auto substitute = [&](auto& tl, auto half, int tn) {  // appending (bf16) tiles only
+  auto substitute = [&](auto& tl, auto half, int tn) {  // bf16 tiles
     constexpr int TH = decltype(half)::value;
     if (r == (tn & 15)) {
 #pragma unroll
@@ -569,6 +592,30 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
           tl.v[TH][dt][0] = w;
         else
           tl.v[TH][dt][1] = w;
+      }
+    }
+  };
+
+  // fp8: put the appended token's codes (tile token tn = 32 ST + t) into step
+  // ST of the final tile.  Row 4(t/8) + t%4 of quarter (t/4) % 2 holds its K
+  // chunks; lanes c = t/8 hold its V codes at byte t%8 of their 8-token runs
+  auto substitute8 = [&](auto& tl, auto stc, auto thc, int t) {
+    constexpr int ST = decltype(stc)::value, TH = decltype(thc)::value;
+    if (r == 4 * (t >> 3) + (t & 3)) {
+#pragma unroll
+      for (int i = 0; i < NJ / 2; ++i)
+        tl.k[2 * ST + TH][i] = *reinterpret_cast<const u32x4*>(lds_k8 + 16 * (4 * i + c));
+    }
+    if (c == (t >> 3)) {
+      const int e = t & 7;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t code = lds_v8[16 * dt + r];
+        const uint32_t sh = 8 * (e & 3), keep = ~(0xffu << sh);
+        if (e < 4)
+          tl.v[ST][dt][0] = (tl.v[ST][dt][0] & keep) | (code << sh);
+        else
+          tl.v[ST][dt][1] = (tl.v[ST][dt][1] & keep) | (code << sh);
       }
     }
   };
@@ -699,12 +746,21 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
       if (appends) {
         const int pb = tw.at(tnew / B, a.num_blocks);
         const int off = tnew % B;
-        if (lane < D / 8)
-          *reinterpret_cast<u32x4*>(k_pool + pb * blk_stride + head_off +
-                                    ((size_t)lane * B + off) * 8) = nk;
-        uint16_t* vb = v_pool + pb * blk_stride + head_off;
+        auto* vb = v_pool + pb * blk_stride + head_off;
+        if constexpr (F8) {
+          // lane holds half (lane % 2) of K chunk lane / 2
+          if (lane < D / 8)
+            *reinterpret_cast<u32x2*>(k_pool + pb * blk_stride + head_off +
+                                      ((size_t)(lane >> 1) * B + off) * 16 + 8 * (lane & 1)) = nk8;
 #pragma unroll
-        for (int i = 0; i < NVD; ++i) vb[(size_t)(lane + kWave * i) * B + off] = nv[i];
+          for (int i = 0; i < NVD; ++i) vb[(size_t)(lane + kWave * i) * B + off] = nv8[i];
+        } else {
+          if (lane < D / 8)
+            *reinterpret_cast<u32x4*>(k_pool + pb * blk_stride + head_off +
+                                      ((size_t)lane * B + off) * 8) = nk;
+#pragma unroll
+          for (int i = 0; i < NVD; ++i) vb[(size_t)(lane + kWave * i) * B + off] = nv[i];
+        }
       }
     }
   };
@@ -712,11 +768,22 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   if constexpr (AP) {
     pipelined<Tile>(n, load, compute, stage_new, [&](int k, Tile& tl) {
       const int tn = tnew - (it.start + k * TILE);  // in this tile when appending
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
       if (appends) {
-        if (tn < 16)
-          substitute(tl, std::integral_constant<int, 0>{}, tn);
-        else
-          substitute(tl, std::integral_constant<int, 1>{}, tn);
+        if constexpr (F8) {
+          const int t = tn & 31, th = (t >> 2) & 1;
+          if (tn < 32) {
+            if (th == 0) substitute8(tl, I0{}, I0{}, t); else substitute8(tl, I0{}, I1{}, t);
+          } else {
+            if (th == 0) substitute8(tl, I1{}, I0{}, t); else substitute8(tl, I1{}, I1{}, t);
+          }
+        } else {
+          if (tn < 16)
+            substitute(tl, I0{}, tn);
+          else
+            substitute(tl, I1{}, tn);
+        }
       }
       compute(k, tl);
     });
@@ -837,7 +904,7 @@ __global__ __launch_bounds__(TPR) void pa_reduce_kernel(float* __restrict__ out,
 // Host dispatch.
 // ---------------------------------------------------------------------------
 // E is the pool element: float, uint16_t (bf16) or uint8_t (fp8 E4M3, whose
-// queries are bf16).  fp8 runs only on the MFMA kernel (G >= 4), never appending.
+// queries and appended tokens are bf16).  fp8 runs only on the MFMA kernel (G >= 4).
 template <typename E, int D, int B, int G, bool NT>
 static void launch_main_nt(const DecodeArgs& a, unsigned grid, const void* q, void* kp, void* vp,
                            hipStream_t st) {
@@ -845,10 +912,16 @@ static void launch_main_nt(const DecodeArgs& a, unsigned grid, const void* q, vo
   // the append variants hold more registers and a longer epilogue; plain
   // launches compile without them
   if constexpr (sizeof(E) == 1) {
-    if constexpr (kMfma)
-      pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, false, true>
-          <<<grid, kWavesPerGroup * kWave, 0, st>>>(a, (const uint16_t*)q, (uint8_t*)kp,
-                                                     (uint8_t*)vp);
+    if constexpr (G >= 4) {
+      if (a.new_k)
+        pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, true, true>
+            <<<grid, kWavesPerGroup * kWave, 0, st>>>(a, (const uint16_t*)q, (uint8_t*)kp,
+                                                       (uint8_t*)vp);
+      else
+        pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, false, true>
+            <<<grid, kWavesPerGroup * kWave, 0, st>>>(a, (const uint16_t*)q, (uint8_t*)kp,
+                                                       (uint8_t*)vp);
+    }
   } else if constexpr (kMfma) {
     if (a.new_k)
       pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, true, false>
@@ -947,7 +1020,7 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   if (!shape_supported(D, B, G)) return PKV_EUNSUPPORTED;
   if (dtype == PKV_FP8_E4M3) {
     if (!k_scale || !v_scale) return PKV_EINVAL;
-    if (G < 4 || new_key) return PKV_EUNSUPPORTED;
+    if (G < 4) return PKV_EUNSUPPORTED;
   }
   const int P = resolve_partition(partition_size, B);
   if (P == 0) return PKV_EINVAL;

@@ -140,3 +140,58 @@ def test_fp8_block_copies_bit_exact(pkv):
     for s_, d_ in pairs:
         kp0[d_], vp0[d_] = kp0[s_], vp0[s_]
     assert np.array_equal(kp.cpu().numpy(), kp0) and np.array_equal(vp.cpu().numpy(), vp0)
+
+
+@pytest.mark.parametrize("G,D,B,P,plan", [(4, 128, 16, 512, True), (8, 128, 32, 256, False),
+                                          (4, 64, 16, 96, True), (8, 64, 32, 1024, False)])
+def test_fp8_append_in_the_attention_launch(pkv, G, D, B, P, plan):
+    """new_key / new_value (bf16) are encoded, written into each sequence's last
+    slot and attended to in the same launch: pools bit-identical to the cache
+    write, output within the bf16 bound of the reference over those pools."""
+    import torch
+    say(f"case fp8 append G={G} D={D} B={B} P={P} plan={plan}")
+    rng = np.random.default_rng(90 + G + D + B + P)
+    Hkv = 2
+    lens = (1, 2, 16, 17, 32, 33, 63, 64, 65, 96, 97, 511, 512, 513, 1025)
+    k_scale = rng.uniform(0.004, 0.03, Hkv).astype(np.float32)
+    v_scale = rng.uniform(0.004, 0.03, Hkv).astype(np.float32)
+    N = sum(-(-L // B) for L in lens) + 3
+    bm = BlockManager(N, B, rng.permutation(N))
+    ks, vs = W.pool_shapes(N, Hkv, D, B, "fp8")
+    kp, vp = np.full(ks, NAN8, np.uint8), np.full(vs, NAN8, np.uint8)
+    slots, Ks, Vs, new_slots = [], [], [], []
+    for s, L in enumerate(lens):
+        bm.add_seq(s, L - 1)
+        t = bm.tables[s]
+        slots += [t[i // B] * B + i % B for i in range(L - 1)]
+        Ks.append(W.normal(rng, (L - 1, Hkv, D), "bf16"))
+        Vs.append(W.normal(rng, (L - 1, Hkv, D), "bf16"))
+        new_slots.append(bm.append_slot(s)[0])
+    kp, vp = ref_cache(kp, vp, np.concatenate(Ks), np.concatenate(Vs), np.asarray(slots),
+                       k_scale, v_scale)
+    S = len(lens)
+    tables, clens = bm.fill_batch(range(S), max(-(-L // B) for L in lens))
+    tables, clens = np.asarray(tables, np.int32), np.asarray(clens, np.int32)
+    assert clens.tolist() == list(lens)
+    k_new = W.normal(rng, (S, Hkv, D), "bf16")
+    v_new = W.normal(rng, (S, Hkv, D), "bf16")
+    q = W.normal(rng, (S, Hkv * G, D), "bf16")
+    mcl = int(clens.max())
+    dk, dv = _u8(kp), _u8(vp)
+    out = torch.full((S, Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(pkv.attention_workspace_bytes(S, Hkv * G, D, mcl, P), 16),
+                     dtype=torch.uint8, device="cuda")
+    pl = pkv.make_plan(clens, Hkv, B, tables.shape[1], mcl, P) if plan else None
+    pkv.paged_attention_decode(out, to_dev(q), dk, dv, torch.from_numpy(tables).cuda(),
+                               torch.from_numpy(clens).cuda(), mcl, partition_size=P,
+                               workspace=ws, plan=pl, new_key=to_dev(k_new),
+                               new_value=to_dev(v_new),
+                               k_scale=torch.from_numpy(k_scale).cuda(),
+                               v_scale=torch.from_numpy(v_scale).cuda())
+    torch.cuda.synchronize()
+    rk, rv = ref_cache(kp, vp, k_new, v_new, np.asarray(new_slots), k_scale, v_scale)
+    assert np.array_equal(dk.cpu().numpy(), rk)
+    assert np.array_equal(dv.cpu().numpy(), rv)
+    want = ref_decode(q, rk, rv, tables, clens, k_scale=k_scale, v_scale=v_scale)
+    worst = check_attention(out.cpu().numpy(), want, "bf16")
+    say(f"  worst error {worst:.3e}")
