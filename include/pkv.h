@@ -409,15 +409,19 @@ pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int
  *                 more rows than tokens gets only its last L_s rows written)
  *   max_query_len host bound on Q_s (sizes the grid)
  *   block_tables, max_blocks, num_blocks, Hq, Hkv, scale as for decode.
- * bf16 pools only, D in {64, 128}, B in {16, 32}, Hq/Hkv in {1, 2, 4, 8};
- * others PKV_EUNSUPPORTED.  A query of one token per sequence is decode (the
- * result matches pkv_paged_attention_decode's rows). */
+ *   k_scale, v_scale  fp8 pools: device fp32 [Hkv] per-KV-head scales (q stays
+ *                 bf16); NULL otherwise
+ * bf16 or fp8 E4M3 pools, D in {64, 128}, B in {16, 32}, Hq/Hkv in
+ * {1, 2, 4, 8}; others PKV_EUNSUPPORTED.  A query of one token per sequence is
+ * decode (with bf16 pools the result matches pkv_paged_attention_decode's rows
+ * bit for bit). */
 pkv_status pkv_paged_attention_prefill(float* out, const void* q, const void* k_pool,
                                        const void* v_pool, const int32_t* block_tables,
                                        const int32_t* context_lens, const int32_t* query_start,
                                        int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
                                        int32_t B, int32_t max_blocks, int32_t num_blocks,
                                        int32_t max_query_len, float scale, pkv_dtype dtype,
+                                       const float* k_scale, const float* v_scale,
                                        void* hip_stream);
 
 /* Block copies between two pools of the same geometry, one of which is usually

@@ -111,7 +111,8 @@ SIGNATURES = {
                                      _vp, _vp, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
-                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
+                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
+                                           _vp, _vp]),
     "pkv_swap_blocks": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                _i32, _vp]),
     "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -574,17 +575,19 @@ def pkv_swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
 
 
 def pkv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
-                                max_query_len: int, scale=None, stream=None) -> None:
+                                max_query_len: int, scale=None, stream=None, k_scale=None,
+                                v_scale=None) -> None:
     """Causal attention of each sequence's last Q_s tokens over the paged cache:
     q and out [T, Hq, D] packed by query_start (int32 [S+1]); Q_s =
-    query_start[s+1] - query_start[s]."""
+    query_start[s+1] - query_start[s].  fp8 pools take bf16 q and the per-head
+    k_scale / v_scale (float32 [Hkv] device tensors)."""
     N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
     T, Hq = q.shape[0], q.shape[1]
     S = context_lens.shape[0]
     if tuple(q.shape) != (T, Hq, D) or tuple(out.shape) != (T, Hq, D):
         raise ValueError("q and out must be [T, Hq, D]")
-    if out.dtype != torch.float32 or q.dtype != k_pool.dtype:
-        raise ValueError("out must be fp32 and q in the pool dtype")
+    if out.dtype != torch.float32 or q.dtype != _row_dtype(k_pool):
+        raise ValueError("out must be fp32 and q in the pool dtype (bf16 for fp8 pools)")
     if query_start.dtype != torch.int32 or tuple(query_start.shape) != (S + 1,):
         raise ValueError("query_start must be int32 [S + 1]")
     if context_lens.dtype != torch.int32 or block_tables.dtype != torch.int32 or \
@@ -598,7 +601,8 @@ def pkv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_le
         _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
         _dev(query_start, "query_start"), S, T, Hq, Hkv, D, B, block_tables.shape[1], N,
-        int(max_query_len), float(scale), _dtype_code(k_pool), _stream(stream)),
+        int(max_query_len), float(scale), _dtype_code(k_pool),
+        *_scales(k_pool, k_scale, v_scale, Hkv), _stream(stream)),
         "pkv_paged_attention_prefill")
 
 

@@ -25,6 +25,10 @@
 // are dispatched first.  Every group of a sequence reads the same prefix, so
 // K/V use ordinary cached loads: the re-reads are served from L2 or the
 // last-level cache.
+// fp8 E4M3 pools: the tiles hold the raw codes (8-byte K and 4-byte V runs in
+// the same token order) and each MFMA operand is widened to bf16 where it is
+// used (exact: an E4M3 value has 4 significant bits); the K scale joins the
+// score scale and the V scale the output.
 #include <cmath>
 #include <type_traits>
 
@@ -40,15 +44,17 @@ struct PrefillArgs {
   const int* block_tables;    // [S, max_blocks]
   const int* context_lens;    // [S]
   const int* query_start;     // [S + 1]
+  const float* k_scale;       // fp8 pools: per-KV-head scales, else nullptr
+  const float* v_scale;
   int S, Hkv, T, max_blocks, num_blocks, groups;
   float scale_log2e;
 };
 
-template <int D, int B, int G>
-__global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(PrefillArgs a,
-                                                              const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k_pool,
-                                                              const uint16_t* __restrict__ v_pool) {
+template <int D, int B, int G, bool F8>
+__global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
+    PrefillArgs a, const uint16_t* __restrict__ q,
+    const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ k_pool,
+    const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ v_pool) {
   constexpr int TILE = 32;
   constexpr int NJ = D / 32;   // q.k k-steps
   constexpr int NDT = D / 16;  // p.v output dim tiles
@@ -98,9 +104,17 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(PrefillArgs a,
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   struct Tile {
-    u32x4 k[2][NJ];
-    u32x2 v[2][NDT];
+    std::conditional_t<F8, u32x2, u32x4> k[2][NJ];
+    std::conditional_t<F8, uint32_t, u32x2> v[2][NDT];
   };
+  const float score_scale = F8 ? a.scale_log2e * a.k_scale[g] : a.scale_log2e;
+  auto k_operand = [](const auto& w) {
+    if constexpr (F8)
+      return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(w));
+    else
+      return __builtin_bit_cast(bf16x8, w);
+  };
+  const float out_scale = F8 ? a.v_scale[g] : 1.f;
   const size_t head_off = (size_t)g * (D * B);
   const size_t blk_stride = (size_t)a.Hkv * (D * B);
   const int* table = a.block_tables + (size_t)s * a.max_blocks;
@@ -124,14 +138,28 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(PrefillArgs a,
       for (int th = 0; th < 2; ++th) {
         const size_t blk = (B == 16 && th == 1) ? pb1 : pb0;
         const int tok = (B == 16 ? 0 : 16 * th);
-        const uint16_t* kb = k_pool + blk * blk_stride + head_off;
-        const uint16_t* vb = v_pool + blk * blk_stride + head_off;
+        const auto* kb = k_pool + blk * blk_stride + head_off;
+        const auto* vb = v_pool + blk * blk_stride + head_off;
+        if constexpr (F8) {
+          // dims 8(4j + c) .. +7: half c % 2 of the 16-dim chunk 2j + c / 2
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          tl.k[th][j] = *reinterpret_cast<const u32x4*>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+          for (int j = 0; j < NJ; ++j)
+            tl.k[th][j] = *reinterpret_cast<const u32x2*>(
+                kb + ((size_t)(2 * j + (c >> 1)) * B + tok + r) * 16 + 8 * (c & 1));
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          tl.v[th][dt] = *reinterpret_cast<const u32x2*>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+          for (int dt = 0; dt < NDT; ++dt)
+            tl.v[th][dt] =
+                *reinterpret_cast<const uint32_t*>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            tl.k[th][j] =
+                *reinterpret_cast<const u32x4*>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            tl.v[th][dt] =
+                *reinterpret_cast<const u32x2*>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+        }
       }
     };
 
@@ -142,14 +170,14 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(PrefillArgs a,
       for (int th = 0; th < 2; ++th)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, tl.k[th][j]), qb[j], sacc[th], 0, 0, 0);
+          sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tl.k[th][j]), qb[j],
+                                                             sacc[th], 0, 0, 0);
       // sv[4th + i]: token T0 + 16th + 4c + i of column r
       float sv[8];
 #pragma unroll
       for (int th = 0; th < 2; ++th)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * a.scale_log2e;
+        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * score_scale;
       if (T0 + TILE > first_pos + 1) {  // a tile some column cannot see all of
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
@@ -162,12 +190,18 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(PrefillArgs a,
             if (i >= nv) sv[4 * th + i] = -INFINITY;
           // V rows past the range end may hold anything (NaN): zero them so a
           // zero weight cannot turn into NaN in the product
+          if constexpr (F8) {
+            const uint32_t mk = ne >= 4 ? 0xffffffffu : (1u << (8 * ne)) - 1u;
 #pragma unroll
-          for (int wd = 0; wd < 2; ++wd) {
-            const uint32_t mk =
-                (2 * wd < ne ? 0x0000ffffu : 0u) | (2 * wd + 1 < ne ? 0xffff0000u : 0u);
+            for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt] &= mk;
+          } else {
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt][wd] &= mk;
+            for (int wd = 0; wd < 2; ++wd) {
+              const uint32_t mk =
+                  (2 * wd < ne ? 0x0000ffffu : 0u) | (2 * wd + 1 < ne ? 0xffff0000u : 0u);
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt][wd] &= mk;
+            }
           }
         }
       }
@@ -200,7 +234,13 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(PrefillArgs a,
       const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const u32x4 va = {tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
+        u32x4 va;
+        if constexpr (F8) {
+          const u32x2 lo = fp8x4_to_bf16(tl.v[0][dt]), hi = fp8x4_to_bf16(tl.v[1][dt]);
+          va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          va = u32x4{tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
+        }
         acc[dt] *= alpha;
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), ph,
                                                           acc[dt], 0, 0, 0);
@@ -216,26 +256,37 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(PrefillArgs a,
   ls += shfl_xor_f(ls, 32);
   if (col_valid) {
     float* dst = a.out + ((size_t)(rbase + qi) * Hq + g * G + gi) * D;
-    const float scl = 1.f / ls;
+    const float scl = out_scale / ls;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * c) = acc[dt] * scl;
   }
 }
 
-template <int D, int B>
+template <int D, int B, bool F8>
 static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, const void* q,
                              const void* kp, const void* vp, hipStream_t st) {
+  using E = std::conditional_t<F8, uint8_t, uint16_t>;
   const uint16_t* qq = (const uint16_t*)q;
-  const uint16_t* kk = (const uint16_t*)kp;
-  const uint16_t* vv = (const uint16_t*)vp;
+  const E* kk = (const E*)kp;
+  const E* vv = (const E*)vp;
   switch (G) {
-    case 1: pa_prefill_kernel<D, B, 1><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
-    case 2: pa_prefill_kernel<D, B, 2><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
-    case 4: pa_prefill_kernel<D, B, 4><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
-    case 8: pa_prefill_kernel<D, B, 8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    case 1: pa_prefill_kernel<D, B, 1, F8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    case 2: pa_prefill_kernel<D, B, 2, F8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    case 4: pa_prefill_kernel<D, B, 4, F8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    case 8: pa_prefill_kernel<D, B, 8, F8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
     default: return false;
   }
+}
+
+template <bool F8>
+static bool launch_prefill(int D, int B, int G, const PrefillArgs& a, unsigned grid,
+                           const void* q, const void* kp, const void* vp, hipStream_t st) {
+  if (D == 64)
+    return B == 16 ? launch_prefill_g<64, 16, F8>(G, a, grid, q, kp, vp, st)
+                   : launch_prefill_g<64, 32, F8>(G, a, grid, q, kp, vp, st);
+  return B == 16 ? launch_prefill_g<128, 16, F8>(G, a, grid, q, kp, vp, st)
+                 : launch_prefill_g<128, 32, F8>(G, a, grid, q, kp, vp, st);
 }
 
 }  // namespace pkv
@@ -246,13 +297,15 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     float* out, const void* q, const void* k_pool, const void* v_pool,
     const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
     int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks,
-    int32_t num_blocks, int32_t max_query_len, float scale, pkv_dtype dtype, void* hip_stream) {
+    int32_t num_blocks, int32_t max_query_len, float scale, pkv_dtype dtype,
+    const float* k_scale, const float* v_scale, void* hip_stream) {
   if (S < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || max_blocks <= 0 ||
       num_blocks <= 0 || max_query_len < 0 || !(scale > 0.f) || Hq % Hkv != 0)
     return PKV_EINVAL;
   if (dtype != PKV_BF16 && dtype != PKV_F32 && dtype != PKV_FP8_E4M3) return PKV_EINVAL;
   const int G = Hq / Hkv;
-  if (dtype != PKV_BF16 || (D != 64 && D != 128) || (B != 16 && B != 32) ||
+  if (dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (dtype == PKV_F32 || (D != 64 && D != 128) || (B != 16 && B != 32) ||
       (G != 1 && G != 2 && G != 4 && G != 8))
     return PKV_EUNSUPPORTED;
   if (S == 0 || T == 0 || max_query_len == 0) return PKV_OK;
@@ -268,6 +321,8 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start = query_start;
+  a.k_scale = dtype == PKV_FP8_E4M3 ? k_scale : nullptr;
+  a.v_scale = dtype == PKV_FP8_E4M3 ? v_scale : nullptr;
   a.S = S;
   a.Hkv = Hkv;
   a.T = T;
@@ -277,10 +332,9 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.scale_log2e = scale * 1.4426950408889634f;
   hipStream_t st = (hipStream_t)hip_stream;
   const unsigned grid = (unsigned)items;
-  const bool ok = D == 64 ? (B == 16 ? launch_prefill_g<64, 16>(G, a, grid, q, k_pool, v_pool, st)
-                                     : launch_prefill_g<64, 32>(G, a, grid, q, k_pool, v_pool, st))
-                          : (B == 16 ? launch_prefill_g<128, 16>(G, a, grid, q, k_pool, v_pool, st)
-                                     : launch_prefill_g<128, 32>(G, a, grid, q, k_pool, v_pool, st));
+  const bool ok = dtype == PKV_FP8_E4M3
+                      ? launch_prefill<true>(D, B, G, a, grid, q, k_pool, v_pool, st)
+                      : launch_prefill<false>(D, B, G, a, grid, q, k_pool, v_pool, st);
   if (!ok) return PKV_EUNSUPPORTED;
   return launch_status();
 }

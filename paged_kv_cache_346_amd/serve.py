@@ -32,6 +32,8 @@ K/V and query values come from caller-supplied sources (the loop computes no
 model): kv_source(pairs) returns the K and V rows [T, Hkv, D] and
 q_source(pairs) the query rows [T, Hq, D] for an int64 array of (request id,
 token position) pairs.  Everything the method computes runs in libpkv.so.
+With fp8 E4M3 pools (dtype torch.uint8) the rows stay bf16 and every call
+takes the per-KV-head scales (kv_scales).
 """
 from __future__ import annotations
 
@@ -53,12 +55,17 @@ class DecodeLoop:
     def __init__(self, *, num_blocks: int, block_size: int, q_heads: int, kv_heads: int,
                  head_dim: int, max_running: int, max_len: int, dtype=torch.bfloat16,
                  partition_size: int = 0, reserve_max: bool = False, free_order=None,
-                 host_blocks: int = 0, max_prefill_tokens=None, device="cuda"):
+                 host_blocks: int = 0, max_prefill_tokens=None, kv_scales=None,
+                 device="cuda"):
         self.B, self.Hq, self.Hkv, self.D = block_size, q_heads, kv_heads, head_dim
         self.P = partition_size
         self.max_len = max_len
         self.max_blocks = max(1, math.ceil(max_len / block_size))
         self.device = torch.device(device)
+        self.fp8 = dtype == torch.uint8
+        if self.fp8 != (kv_scales is not None):
+            raise ValueError("fp8 pools (torch.uint8) go with kv_scales=(k_scale, v_scale)")
+        self.k_scale, self.v_scale = kv_scales if self.fp8 else (None, None)
         self.bm = BlockManager(num_blocks, block_size, free_order)
         if host_blocks:
             self.bm.set_host_pool(host_blocks)
@@ -175,17 +182,20 @@ class DecodeLoop:
             q = q_source(all_pairs)
             if n_pf:
                 reshape_and_cache(k[:n_pf], v[:n_pf], self.k_pool, self.v_pool,
-                                  dev["slots"].view(torch.int64))
+                                  dev["slots"].view(torch.int64), k_scale=self.k_scale,
+                                  v_scale=self.v_scale)
                 out_pf = self._prefill_out(n_pf)
                 paged_attention_prefill(out_pf, q[:n_pf], self.k_pool, self.v_pool,
                                         dev["pf_tables"].view(len(chunks), -1), dev["pf_lens"],
-                                        dev["pf_start"], max(c for _, _, c in chunks))
+                                        dev["pf_start"], max(c for _, _, c in chunks),
+                                        k_scale=self.k_scale, v_scale=self.v_scale)
         if n:
             paged_attention_decode(out, q[n_pf:], self.k_pool, self.v_pool,
                                    dev["tables"].view(n, -1), dev["lens"], mcl,
                                    partition_size=self.P, workspace=self.ws,
                                    plan=Plan(dev["plan"], n_items, n_merge),
-                                   new_key=k[n_pf:], new_value=v[n_pf:])
+                                   new_key=k[n_pf:], new_value=v[n_pf:],
+                                   k_scale=self.k_scale, v_scale=self.v_scale)
         st["stats"] = self.sched.stats()   # before the finished requests leave
         self.sched.end_step()
         return st, out, out_pf, lens

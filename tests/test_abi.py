@@ -120,11 +120,16 @@ def test_prefill_validation(pkv):
     lib = pkv.lib
     fake = ctypes.c_void_p(4096)
 
-    def call(S=2, T=8, Hq=8, Hkv=2, D=128, B=16, mq=4, scale=0.1, dtype=1, odd=False):
+    def call(S=2, T=8, Hq=8, Hkv=2, D=128, B=16, mq=4, scale=0.1, dtype=1, odd=False,
+             scales=None):
         out = ctypes.c_void_p(4098) if odd else fake
+        ks = vs = scales
         return lib.pkv_paged_attention_prefill(out, fake, fake, fake, fake, fake, fake, S, T, Hq,
-                                               Hkv, D, B, 4, 16, mq, scale, dtype, None)
+                                               Hkv, D, B, 4, 16, mq, scale, dtype, ks, vs, None)
     assert call(dtype=0) == pkv.PKV_EUNSUPPORTED          # fp32 pools
+    assert call(dtype=2) == pkv.PKV_EINVAL                # fp8 pools without scales
+    assert call(dtype=2, scales=fake, D=96) == pkv.PKV_EUNSUPPORTED
+    assert call(dtype=2, scales=fake, S=0) == pkv.PKV_OK
     assert call(Hq=48, Hkv=3) == pkv.PKV_EUNSUPPORTED     # G = 16
     assert call(D=96) == pkv.PKV_EUNSUPPORTED
     assert call(B=8) == pkv.PKV_EUNSUPPORTED

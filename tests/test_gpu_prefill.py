@@ -128,3 +128,44 @@ def test_rows_outside_the_batch_are_not_written(pkv):
     check_attention(got[3:8], want0, "bf16")
     want1 = ref_prefill(q[8:18], kp, vp, tables[1:2], clens[1:2], [10])
     check_attention(got[8:18], want1, "bf16")
+
+
+@pytest.mark.parametrize("G,D,B", [(4, 128, 16), (1, 64, 32), (8, 128, 32), (2, 128, 16)])
+def test_prefill_fp8_matches_reference(pkv, G, D, B):
+    """fp8 E4M3 pools (codes of the bf16 K/V at per-head scales; NaN codes in
+    every unused slot): within the bf16 bound of the fp64 reference over the
+    dequantized pools."""
+    import torch
+    from oracle.cache_ops import reshape_and_cache as ref_cache
+    say(f"case prefill fp8 G={G} D={D} B={B}")
+    rng = np.random.default_rng(950 + G * 7 + D + B)
+    Hkv = 2
+    k_scale = rng.uniform(0.004, 0.03, Hkv).astype(np.float32)
+    v_scale = rng.uniform(0.004, 0.03, Hkv).astype(np.float32)
+    N = sum(-(-L // B) for L in LENS) + 5
+    bm = BlockManager(N, B, rng.permutation(N))
+    ks, vs = W.pool_shapes(N, Hkv, D, B, "fp8")
+    kp, vp = np.full(ks, 0x7F, np.uint8), np.full(vs, 0x7F, np.uint8)
+    slots, Ks, Vs = [], [], []
+    for s, L in enumerate(LENS):
+        bm.add_seq(s, L)
+        t = bm.tables[s]
+        slots += [t[i // B] * B + i % B for i in range(L)]
+        Ks.append(W.normal(rng, (L, Hkv, D), "bf16"))
+        Vs.append(W.normal(rng, (L, Hkv, D), "bf16"))
+    kp, vp = ref_cache(kp, vp, np.concatenate(Ks), np.concatenate(Vs), np.asarray(slots),
+                       k_scale, v_scale)
+    tables, clens = bm.fill_batch(range(len(LENS)), max(-(-L // B) for L in LENS))
+    tables, clens = np.asarray(tables, np.int32), np.asarray(clens, np.int32)
+    q = W.normal(rng, (sum(QLENS), Hkv * G, D), "bf16")
+    starts = np.concatenate([[0], np.cumsum(QLENS)]).astype(np.int32)
+    out = torch.full((q.shape[0], Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_prefill(out, to_dev(q), to_dev(kp), to_dev(vp),
+                                torch.from_numpy(tables).cuda(), torch.from_numpy(clens).cuda(),
+                                torch.from_numpy(starts).cuda(), max(QLENS),
+                                k_scale=torch.from_numpy(k_scale).cuda(),
+                                v_scale=torch.from_numpy(v_scale).cuda())
+    torch.cuda.synchronize()
+    want = ref_prefill(q, kp, vp, tables, clens, QLENS, k_scale=k_scale, v_scale=v_scale)
+    worst = check_attention(out.cpu().numpy(), want, "bf16")
+    say(f"  worst error {worst:.3e}")
