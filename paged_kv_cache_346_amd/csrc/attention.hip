@@ -169,13 +169,18 @@ __device__ __forceinline__ RowSink row_sink(const DecodeArgs& a, const WorkItem&
 }
 
 // ---------------------------------------------------------------------------
-// VALU main kernel.  E = float or uint16_t (bf16 bits).  Tile = one KV block.
+// VALU main kernel.  E = float, uint16_t (bf16 bits) or uint8_t (fp8 E4M3 codes,
+// bf16 queries: each 16-dim K chunk pairs with two 16-byte q vectors, codes are
+// widened to fp32 exactly, the K scale joins the score scale and the V scale
+// the output).  Tile = one KV block.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int B, int G, int NW, bool NT, bool AP>
-__global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
-                                                             const E* __restrict__ q,
-                                                             E* __restrict__ k_pool,
-                                                             E* __restrict__ v_pool) {
+__global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(
+    DecodeArgs a, const std::conditional_t<sizeof(E) == 1, uint16_t, E>* __restrict__ q,
+    E* __restrict__ k_pool, E* __restrict__ v_pool) {
+  constexpr bool F8 = sizeof(E) == 1;
+  using QE = std::conditional_t<F8, uint16_t, E>;
+  constexpr int QV = F8 ? 2 : 1;     // 16-byte q vectors per K chunk
   constexpr int X = 16 / sizeof(E);  // elements per 16-byte vector
   constexpr int NCG = kWave / B;     // lanes sharing one token in q.k
   constexpr int NCH = D / X;         // 16-byte chunks per token
@@ -198,13 +203,17 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
   if (!item_extent<D, B, G>(a, it, L)) return;
   TableWindow tw;
   tw.load(a.block_tables + (size_t)it.s * a.max_blocks, it.start / B, a.max_blocks);
-  u32x4 qv[G][CPL];
+  u32x4 qv[G][CPL][QV];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi)
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
-      qv[gi][j] = *reinterpret_cast<const u32x4*>(
-          q + ((size_t)it.s * Hq + it.g * G + gi) * D + (cg + NCG * j) * X);
+#pragma unroll
+      for (int h = 0; h < QV; ++h)
+        qv[gi][j][h] = *reinterpret_cast<const u32x4*>(
+            q + ((size_t)it.s * Hq + it.g * G + gi) * D + (cg + NCG * j) * X + 8 * h);
+  const float score_scale = F8 ? a.scale_log2e * a.k_scale[it.g] : a.scale_log2e;
+  const float out_scale = F8 ? a.v_scale[it.g] : 1.f;
 
   float m[G], ls[G], acc[G][ND];
 #pragma unroll
@@ -236,13 +245,35 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
   E nv[ND];
   if (appends) {
     const size_t row = ((size_t)it.s * a.Hkv + it.g) * D;
-    const E* kn = reinterpret_cast<const E*>(a.new_k) + row;
-    const E* vn = reinterpret_cast<const E*>(a.new_v) + row;
+    const QE* kn = reinterpret_cast<const QE*>(a.new_k) + row;
+    const QE* vn = reinterpret_cast<const QE*>(a.new_v) + row;
+    if constexpr (F8) {
+      // the token's bf16 rows encoded with the head's scales, as the cache write does
+      const float ks = a.k_scale[it.g], vs = a.v_scale[it.g];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j)
-      nk[j] = *reinterpret_cast<const u32x4*>(kn + (cg + NCG * j) * X);
+      for (int j = 0; j < CPL; ++j) {
+        nk[j] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k2 = 0; k2 < ND; ++k2) nv[k2] = vn[lane + kWave * k2];
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(kn + (cg + NCG * j) * X + 8 * h);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+            const int d = 8 * h + e;
+            nk[j][d >> 2] |= f32_to_e4m3(__uint_as_float(bits) / ks) << (8 * (d & 3));
+          }
+        }
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < ND; ++k2)
+        nv[k2] = (E)f32_to_e4m3(__uint_as_float((uint32_t)vn[lane + kWave * k2] << 16) / vs);
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+        nk[j] = *reinterpret_cast<const u32x4*>(kn + (cg + NCG * j) * X);
+#pragma unroll
+      for (int k2 = 0; k2 < ND; ++k2) nv[k2] = vn[lane + kWave * k2];
+    }
   }
   auto write_new = [&]() {
     if (!appends) return;
@@ -295,17 +326,27 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
     const int tok0 = (lb_first + k) * B;
     const bool valid = tok0 + t < it.end;
     float pr[G];
+    // fp8: the K codes widened once for all heads of the group
+    float kf[F8 ? CPL : 1][16];
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) fp8x16_to_f32(tl.k[j], kf[j]);
+    }
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       float sc = 0.f;
 #pragma unroll
       for (int j = 0; j < CPL; ++j)
 #pragma unroll
-        for (int e = 0; e < X; ++e)
-          sc = fmaf(vec_elem<E>(qv[gi][j], e), vec_elem<E>(tl.k[j], e), sc);
+        for (int e = 0; e < X; ++e) {
+          if constexpr (F8)
+            sc = fmaf(vec_elem<uint16_t>(qv[gi][j][e >> 3], e & 7), kf[j][e], sc);
+          else
+            sc = fmaf(vec_elem<E>(qv[gi][j][0], e), vec_elem<E>(tl.k[j], e), sc);
+        }
       if (NCG >= 4) sc += shfl_xor_f(sc, 16);
       if (NCG >= 2) sc += shfl_xor_f(sc, 32);
-      sc = valid ? sc * a.scale_log2e : -INFINITY;
+      sc = valid ? sc * score_scale : -INFINITY;
       float mx = sc;
 #pragma unroll
       for (int o = 1; o < B; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
@@ -318,7 +359,12 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
       m[gi] = mn;
     }
 #pragma unroll
-    for (int tc = 0; tc < NVT; ++tc)
+    for (int tc = 0; tc < NVT; ++tc) {
+      float vf[F8 ? ND : 1][16];
+      if constexpr (F8) {
+#pragma unroll
+        for (int k2 = 0; k2 < ND; ++k2) fp8x16_to_f32(tl.v[tc][k2], vf[k2]);
+      }
 #pragma unroll
       for (int e = 0; e < X; ++e) {
         const int tt = tc * X + e;
@@ -327,11 +373,16 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
           for (int gi = 0; gi < G; ++gi) {
             const float pt = read_lane(pr[gi], tt);
 #pragma unroll
-            for (int k2 = 0; k2 < ND; ++k2)
-              acc[gi][k2] = fmaf(pt, vec_elem<E>(tl.v[tc][k2], e), acc[gi][k2]);
+            for (int k2 = 0; k2 < ND; ++k2) {
+              if constexpr (F8)
+                acc[gi][k2] = fmaf(pt, vf[k2][e], acc[gi][k2]);
+              else
+                acc[gi][k2] = fmaf(pt, vec_elem<E>(tl.v[tc][k2], e), acc[gi][k2]);
+            }
           }
         }
       }
+    }
   };
 
   if constexpr (AP) {
@@ -348,7 +399,7 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(DecodeArgs a,
   for (int gi = 0; gi < G; ++gi) {
     const float l = wave_sum(ls[gi]);
     const RowSink dst = row_sink<D, G>(a, it, gi);
-    const float scl = dst.ml ? 1.f : 1.f / l;
+    const float scl = (dst.ml ? 1.f : 1.f / l) * out_scale;
 #pragma unroll
     for (int k = 0; k < ND; ++k) dst.acc[lane + kWave * k] = acc[gi][k] * scl;
     if (dst.ml && lane == 0) {
@@ -904,15 +955,16 @@ __global__ __launch_bounds__(TPR) void pa_reduce_kernel(float* __restrict__ out,
 // Host dispatch.
 // ---------------------------------------------------------------------------
 // E is the pool element: float, uint16_t (bf16) or uint8_t (fp8 E4M3, whose
-// queries and appended tokens are bf16).  fp8 runs only on the MFMA kernel (G >= 4).
+// queries and appended tokens are bf16): the MFMA kernel for G >= 4, else VALU.
 template <typename E, int D, int B, int G, bool NT>
 static void launch_main_nt(const DecodeArgs& a, unsigned grid, const void* q, void* kp, void* vp,
                            hipStream_t st) {
   constexpr bool kMfma = sizeof(E) <= 2 && G >= 4;
   // the append variants hold more registers and a longer epilogue; plain
   // launches compile without them
-  if constexpr (sizeof(E) == 1) {
-    if constexpr (G >= 4) {
+  using QE = std::conditional_t<sizeof(E) == 1, uint16_t, E>;
+  if constexpr (sizeof(E) == 1 && G >= 4) {
+    {
       if (a.new_k)
         pa_mfma_kernel<D, B, G, kWavesPerGroup, NT, true, true>
             <<<grid, kWavesPerGroup * kWave, 0, st>>>(a, (const uint16_t*)q, (uint8_t*)kp,
@@ -934,10 +986,10 @@ static void launch_main_nt(const DecodeArgs& a, unsigned grid, const void* q, vo
   } else {
     if (a.new_k)
       pa_valu_kernel<E, D, B, G, kWavesPerGroup, NT, true><<<grid, kWavesPerGroup * kWave, 0, st>>>(
-          a, (const E*)q, (E*)kp, (E*)vp);
+          a, (const QE*)q, (E*)kp, (E*)vp);
     else
       pa_valu_kernel<E, D, B, G, kWavesPerGroup, NT, false><<<grid, kWavesPerGroup * kWave, 0, st>>>(
-          a, (const E*)q, (E*)kp, (E*)vp);
+          a, (const QE*)q, (E*)kp, (E*)vp);
   }
 }
 
@@ -953,7 +1005,6 @@ static void launch_main(bool stream, const DecodeArgs& a, unsigned grid, const v
 template <typename E, int D, int B>
 static bool dispatch_g(int G, bool stream, const DecodeArgs& a, unsigned grid, const void* q,
                        void* kp, void* vp, hipStream_t st) {
-  if (sizeof(E) == 1 && G < 4) return false;
   switch (G) {
     case 1: launch_main<E, D, B, 1>(stream, a, grid, q, kp, vp, st); return true;
     case 2: launch_main<E, D, B, 2>(stream, a, grid, q, kp, vp, st); return true;
@@ -1020,7 +1071,6 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   if (!shape_supported(D, B, G)) return PKV_EUNSUPPORTED;
   if (dtype == PKV_FP8_E4M3) {
     if (!k_scale || !v_scale) return PKV_EINVAL;
-    if (G < 4) return PKV_EUNSUPPORTED;
   }
   const int P = resolve_partition(partition_size, B);
   if (P == 0) return PKV_EINVAL;

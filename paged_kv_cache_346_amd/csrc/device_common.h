@@ -43,6 +43,11 @@ template <>
 __device__ __forceinline__ void vec_set<float>(u32x4& v, int e, float x) {
   v[e] = __float_as_uint(x);
 }
+template <>
+__device__ __forceinline__ void vec_set<uint8_t>(u32x4& v, int e, uint8_t x) {
+  const uint32_t sh = 8 * (e & 3);
+  v[e >> 2] = (v[e >> 2] & ~(0xffu << sh)) | ((uint32_t)x << sh);
+}
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -87,6 +92,18 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2_t w) {
   return u32x4{fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
                fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
+}
+// The 16 E4M3 codes of a 16-byte vector as fp32 values (exact), code e in f[e].
+__device__ __forceinline__ void fp8x16_to_f32(const u32x4& w, float (&f)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    f[4 * i] = lo[0];
+    f[4 * i + 1] = lo[1];
+    f[4 * i + 2] = hi[0];
+    f[4 * i + 3] = hi[1];
+  }
 }
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16(uint32_t w) {
   return u32x2_t{fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w)};

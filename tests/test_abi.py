@@ -81,12 +81,12 @@ def test_host_validation_rejects_before_launch(pkv):
     assert lib.pkv_copy_blocks(None, None, None, 0, 8, 128, 16, 8, 1, None) == pkv.PKV_OK
     assert lib.pkv_reshape_and_cache(odd, fake, fake, fake, tbl, 4, 8, 128, 16, 8, 1,
                                      None, None, None) == pkv.PKV_EINVAL
-    # fp8 pools need both scales; fp8 attention needs G >= 4 and scales
+    # fp8 pools need both scales; fp8 attention needs scales and a compiled G
     assert lib.pkv_reshape_and_cache(fake, fake, fake, fake, tbl, 4, 8, 128, 16, 8, 2,
                                      None, None, None) == pkv.PKV_EINVAL
-    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8,
-                                          128, 16, 4, 8, 16, 0.1, 0, None, 0, 0, None, 0, 2, 0,
-                                          fake, fake, None) == pkv.PKV_EUNSUPPORTED     # G = 1
+    assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 48,
+                                          3, 128, 16, 4, 8, 16, 0.1, 0, None, 0, 0, None, 0, 2,
+                                          0, fake, fake, None) == pkv.PKV_EUNSUPPORTED   # G = 16
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 32,
                                           8, 128, 16, 4, 8, 16, 0.1, 0, None, 0, 0, None, 0, 2,
                                           0, None, None, None) == pkv.PKV_EINVAL         # no scales

@@ -99,7 +99,9 @@ LENS = (1, 2, 15, 16, 17, 33, 100, 511, 512, 513, 1030, 1300)
     (4, 128, 16, 512, True, False), (8, 128, 16, 256, False, False),
     (8, 128, 32, 512, True, False), (4, 64, 32, 128, False, False),
     (8, 64, 16, 1024, True, False), (4, 128, 32, 96, False, False),
-    (8, 128, 16, 96, True, True), (4, 128, 16, 512, False, True)])
+    (8, 128, 16, 96, True, True), (4, 128, 16, 512, False, True),
+    (1, 128, 16, 512, True, False), (2, 128, 32, 256, False, False),
+    (1, 64, 32, 96, False, True), (2, 64, 16, 1024, True, False)])
 def test_fp8_attention_matches_reference(pkv, G, D, B, P, plan, shared):
     import torch
     say(f"case fp8 attention G={G} D={D} B={B} P={P} plan={plan} shared={shared}")
@@ -143,7 +145,8 @@ def test_fp8_block_copies_bit_exact(pkv):
 
 
 @pytest.mark.parametrize("G,D,B,P,plan", [(4, 128, 16, 512, True), (8, 128, 32, 256, False),
-                                          (4, 64, 16, 96, True), (8, 64, 32, 1024, False)])
+                                          (4, 64, 16, 96, True), (8, 64, 32, 1024, False),
+                                          (1, 128, 16, 512, True), (2, 64, 32, 96, False)])
 def test_fp8_append_in_the_attention_launch(pkv, G, D, B, P, plan):
     """new_key / new_value (bf16) are encoded, written into each sequence's last
     slot and attended to in the same launch: pools bit-identical to the cache
