@@ -549,8 +549,8 @@ def run_prefill(args, torch, np):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama8b_gqa", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default=None,
                     help="fp8: the same workload over fp8 E4M3 pools with per-head scales "
