@@ -80,13 +80,12 @@ __device__ __forceinline__ float read_lane(float v, int src) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // fp8 E4M3 (OCP, gfx950's fp8) to bf16.  Every E4M3 value has at most four
-// significant bits, so its fp32 conversion has a zero low half and the top 16
-// bits are the bf16 value exactly.  Two codes from one half of a dword (hi
-// selects the upper half), first code in the low bf16.
+// significant bits and an exponent inside bf16's range, so bf16 holds it
+// exactly.  Two codes from one half of a dword (hi selects the upper half),
+// first code in the low bf16, in one gfx950 conversion with unit scale.
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2_t w) {

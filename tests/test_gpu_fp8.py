@@ -198,3 +198,37 @@ def test_fp8_append_in_the_attention_launch(pkv, G, D, B, P, plan):
     want = ref_decode(q, rk, rv, tables, clens, k_scale=k_scale, v_scale=v_scale)
     worst = check_attention(out.cpu().numpy(), want, "bf16")
     say(f"  worst error {worst:.3e}")
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_fp8_subnormal_codes_decode_exactly(pkv, G):
+    """A KV head whose scale is large stores mostly subnormal codes (exponent
+    field 0): the widening must keep them (no flush to zero) in both kernels."""
+    import torch
+    say(f"case fp8 subnormal codes G={G}")
+    rng = np.random.default_rng(130 + G)
+    Hkv, D, B, P = 2, 128, 16, 512
+    k_scale = np.array([0.02, 60.0], np.float32)
+    v_scale = np.array([0.02, 60.0], np.float32)
+    lens = (5, 40, 700)
+    kp, vp, tables, clens, N = _fp8_pools(rng, lens, Hkv, D, B, k_scale, v_scale)
+    used = np.zeros(N, bool)
+    for s, L in enumerate(lens):
+        used[tables[s, :-(-L // B)]] = True
+    codes = kp[used][:, 1]
+    sub = ((codes & 0x78) == 0) & ((codes & 7) != 0)
+    assert sub.mean() > 0.3, sub.mean()        # head 1 is mostly subnormal codes
+    S = len(lens)
+    q = W.normal(rng, (S, Hkv * G, D), "bf16")
+    mcl = int(clens.max())
+    out = torch.full((S, Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(pkv.attention_workspace_bytes(S, Hkv * G, D, mcl, P), 16),
+                     dtype=torch.uint8, device="cuda")
+    pkv.paged_attention_decode(out, to_dev(q), _u8(kp), _u8(vp), torch.from_numpy(tables).cuda(),
+                               torch.from_numpy(clens).cuda(), mcl, partition_size=P,
+                               workspace=ws, k_scale=torch.from_numpy(k_scale).cuda(),
+                               v_scale=torch.from_numpy(v_scale).cuda())
+    torch.cuda.synchronize()
+    want = ref_decode(q, kp, vp, tables, clens, k_scale=k_scale, v_scale=v_scale)
+    worst = check_attention(out.cpu().numpy(), want, "bf16")
+    say(f"  worst error {worst:.3e}")
