@@ -45,7 +45,9 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode KV-read GB/s (% of HBM peak) and decode tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published figure
 HOST_LINK_PEAK_GBS = 64.0      # PCIe 5.0 x16 host link, per direction, before protocol overhead
-MAIN_KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_346_amd", "csrc", "attention.hip")
+# the main kernel's source and the device headers it includes
+MAIN_KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_346_amd", "csrc", n)
+                    for n in ("attention.hip", "device_common.h", "kv_tiles.h", "decode_config.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 DESCRIPTIONS = {
@@ -72,8 +74,11 @@ def log(msg: str) -> None:
 
 
 def source_digest() -> str:
-    with open(MAIN_KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in MAIN_KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, launches_per_step: int):
