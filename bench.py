@@ -340,6 +340,8 @@ def run_serve(args, torch, np):
     import workloads as W
 
     Hq, Hkv, D, B, N = 32, 8, 128, 16, 16162
+    if args.kv_dtype == "fp8":
+        return run_serve_fp8(args, torch, np, pkv, DecodeLoop, W, Hq, Hkv, D, B, N)
     rng = np.random.default_rng(11)
     trace = W.request_trace(rng, args.serve_requests)
     max_len = max(p + m for _, p, m in trace)
@@ -483,6 +485,82 @@ def run_serve(args, torch, np):
     return 0
 
 
+def run_serve_fp8(args, torch, np, pkv, DecodeLoop, W, Hq, Hkv, D, B, N):
+    """The continuous-batching loop over fp8 E4M3 pools (the same request trace
+    as the bf16 run) at the bf16 pool's block count and at its byte budget
+    (twice the blocks), against bf16 at the same byte budget.  Paged policy,
+    preemption by dropping and recomputing.  One JSON line."""
+    rng = np.random.default_rng(11)
+    trace = W.request_trace(rng, args.serve_requests)
+    max_len = max(p + m for _, p, m in trace)
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1011)
+    rows = 1 << 16
+    kv_rows = torch.randn((2, rows, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    q_rows = torch.randn((rows, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    scales = (torch.full((Hkv,), 0.025, device=dev), torch.full((Hkv,), 0.025, device=dev))
+
+    def kv_source(pairs):
+        idx = torch.from_numpy((pairs[:, 0] * 7919 + pairs[:, 1]) % rows).to(dev)
+        return kv_rows[0].index_select(0, idx), kv_rows[1].index_select(0, idx)
+
+    def q_source(pairs):
+        idx = torch.from_numpy((pairs[:, 0] * 104729 + pairs[:, 1]) % rows).to(dev)
+        return q_rows.index_select(0, idx)
+
+    def run(kv, blocks, warm=False):
+        kw = {"dtype": torch.uint8, "kv_scales": scales} if kv == "fp8" else {}
+        order = np.random.default_rng(13).permutation(blocks).astype(np.int32)
+        loop = DecodeLoop(num_blocks=blocks, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
+                          max_running=args.serve_running, max_len=max_len, free_order=order,
+                          **kw)
+        for rid, p_, m_ in (trace[:64] if warm else trace):
+            loop.add_request(rid, p_, min(m_, 8) if warm else m_)
+        steps = tokens = preempted = 0
+        batch_sum = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while not loop.idle():
+            st, _, _, _ = loop.step(kv_source, q_source)
+            steps += 1
+            tokens += len(st["batch"])
+            batch_sum += len(st["batch"])
+            preempted += len(st["preempted"])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del loop
+        return {"kv_dtype": kv, "pool_blocks": blocks,
+                "pool_bytes": 2 * blocks * Hkv * D * B * (1 if kv == "fp8" else 2),
+                "decode_tokens": tokens, "steps": steps,
+                "mean_batch": round(batch_sum / steps, 1), "preemptions": preempted,
+                "wall_s": round(wall, 3), "decode_tokens_per_s": round(tokens / wall, 1)}
+
+    run("fp8", N, warm=True)
+    run("bf16", N, warm=True)
+    res = {"bf16": run("bf16", N), "fp8_same_blocks": run("fp8", N),
+           "fp8_same_bytes": run("fp8", 2 * N)}
+    for k_, v_ in res.items():
+        log(f"bench: serve fp8 {k_}: {v_}")
+    rec = {
+        "metric": "continuous-batching decode tokens/s over fp8 KV, one attention layer "
+                  "(wall clock, host scheduling included)",
+        "value": res["fp8_same_bytes"]["decode_tokens_per_s"], "unit": "tokens/s",
+        "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": f"the bf16 serve trace ({len(trace)} requests); Llama-3-8B-shaped "
+                               f"layer (32/8 heads, D 128, B 16); paged, drop + recompute; fp8 "
+                               f"E4M3 pools with per-head scales, bf16 rows",
+                   "requests": len(trace), "max_running": args.serve_running},
+        **res,
+    }
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, AMD's published figure
 
 
@@ -501,9 +579,22 @@ def run_prefill(args, torch, np):
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     gen.manual_seed(2027)
-    ks, vs = pkv.pool_shapes(N, Hkv, D, B, torch.bfloat16)
-    k = torch.randn(ks, generator=gen, device=dev).to(torch.bfloat16)
-    v = torch.randn(vs, generator=gen, device=dev).to(torch.bfloat16)
+    fp8 = args.kv_dtype == "fp8"
+    pdt = torch.uint8 if fp8 else torch.bfloat16
+    ks, vs = pkv.pool_shapes(N, Hkv, D, B, pdt)
+    if fp8:
+        # finite E4M3 codes of magnitude below 4, random sign; per-head scales
+        def codes(shape):
+            mag = torch.randint(0, 0x50, shape, generator=gen, device=dev, dtype=torch.uint8)
+            return mag | (torch.randint(0, 2, shape, generator=gen, device=dev,
+                                        dtype=torch.uint8) << 7)
+        k, v = codes(ks), codes(vs)
+        scales = {"k_scale": torch.full((Hkv,), 0.025, device=dev),
+                  "v_scale": torch.full((Hkv,), 0.025, device=dev)}
+    else:
+        k = torch.randn(ks, generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn(vs, generator=gen, device=dev).to(torch.bfloat16)
+        scales = {}
     perm = torch.randperm(N, generator=torch.Generator().manual_seed(3)).to(torch.int32)
     tables = perm.view(S, nb).to(dev)
     lens = torch.full((S,), L, dtype=torch.int32, device=dev)
@@ -511,7 +602,8 @@ def run_prefill(args, torch, np):
     T = S * chunk
     q = torch.randn((T, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
     out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
-    call = lambda: pkv.paged_attention_prefill(out, q, k, v, tables, lens, starts, chunk)
+    call = lambda: pkv.paged_attention_prefill(out, q, k, v, tables, lens, starts, chunk,
+                                               **scales)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -527,15 +619,17 @@ def run_prefill(args, torch, np):
     visible = sum(prefix + i + 1 for i in range(chunk))
     flops = 4.0 * D * Hq * S * visible
     tflops = flops / (us * 1e-6) / 1e12
-    kv_bytes = S * L * Hkv * D * 2 * 2
+    kv_bytes = S * L * Hkv * D * 2 * (1 if fp8 else 2)
+    kv_desc = "fp8 E4M3 KV with per-head scales, bf16 queries" if fp8 else "bf16"
     rec = {
         "metric": "multi-token query (chunked prefill) attention TFLOP/s",
         "value": round(tflops, 1), "unit": "TFLOP/s", "higher_is_better": True,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{S} sequences x ({prefix} cached + {chunk} new tokens), Llama-3-"
-                               f"8B-shaped layer (32/8 heads, D 128, B 16, bf16), causal over "
-                               f"prefix + chunk", "seqs": S, "prefix": prefix, "chunk": chunk},
+                               f"8B-shaped layer (32/8 heads, D 128, B 16, {kv_desc}), causal "
+                               f"over prefix + chunk", "seqs": S, "prefix": prefix, "chunk": chunk,
+                   "kv_dtype": "fp8_e4m3" if fp8 else "bf16"},
         "kernel_us": round(us, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

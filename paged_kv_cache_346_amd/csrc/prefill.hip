@@ -25,10 +25,14 @@
 // are dispatched first.  Every group of a sequence reads the same prefix, so
 // K/V use ordinary cached loads: the re-reads are served from L2 or the
 // last-level cache.
-// fp8 E4M3 pools: the tiles hold the raw codes (8-byte K and 4-byte V runs in
-// the same token order) and each MFMA operand is widened to bf16 where it is
-// used (exact: an E4M3 value has 4 significant bits); the K scale joins the
-// score scale and the V scale the output.
+// fp8 E4M3 pools: the tiles hold the raw codes and each MFMA operand is widened
+// to bf16 where it is used (exact: an E4M3 value fits bf16); the K scale joins
+// the score scale and the V scale the output.  The kernel re-reads K/V from L2
+// for every query group, so it is bound by load instructions per token: fp8
+// tiles take the decode kernel's wide-load token order -- one 16-byte K load
+// is a whole 16-dim chunk feeding two k-steps (q read with the same dim
+// mapping), row r of quarter th stands for tile token 8(r/4) + 4th + r%4, and
+// one 8-byte V load holds the lane's tokens 8c .. 8c+7 -- 12 loads per tile.
 #include <cmath>
 #include <type_traits>
 
@@ -94,8 +98,10 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
   {
     const uint16_t* qrow = q + ((size_t)(rbase + qi) * Hq + g * G + gi) * D;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      qb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * j + c)));
+    for (int j = 0; j < NJ; ++j) {
+      const int d0 = F8 ? 16 * (4 * (j >> 1) + c) + 8 * (j & 1) : 8 * (4 * j + c);
+      qb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + d0));
+    }
   }
 
   float m = -INFINITY, ls = 0.f;
@@ -103,16 +109,26 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  struct Tile {
-    std::conditional_t<F8, u32x2, u32x4> k[2][NJ];
-    std::conditional_t<F8, uint32_t, u32x2> v[2][NDT];
+  // bf16: K of quarter th, k-step j, and V runs of quarter th; fp8: K of quarter
+  // th, 16-byte load i (k-steps 2i, 2i + 1), and the lane's 8-token V run
+  struct Tile16 {
+    u32x4 k[2][NJ];
+    u32x2 v[2][NDT];
   };
+  struct Tile8 {
+    u32x4 k[2][NJ / 2];
+    u32x2 v[NDT];
+  };
+  using Tile = std::conditional_t<F8, Tile8, Tile16>;
   const float score_scale = F8 ? a.scale_log2e * a.k_scale[g] : a.scale_log2e;
-  auto k_operand = [](const auto& w) {
-    if constexpr (F8)
-      return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(w));
-    else
-      return __builtin_bit_cast(bf16x8, w);
+  auto k_operand = [](const Tile& tl, int th, int j) {
+    if constexpr (F8) {
+      const u32x4 w = tl.k[th][j >> 1];
+      return __builtin_bit_cast(bf16x8, fp8x8_to_bf16((j & 1) ? u32x2{w[2], w[3]}
+                                                              : u32x2{w[0], w[1]}));
+    } else {
+      return __builtin_bit_cast(bf16x8, tl.k[th][j]);
+    }
   };
   const float out_scale = F8 ? a.v_scale[g] : 1.f;
   const size_t head_off = (size_t)g * (D * B);
@@ -134,23 +150,32 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
       // B = 16: the tile's second block; past the range end it repeats the
       // first (those tokens are masked)
       const int pb1 = B == 16 ? tw.at(min(lb0 + 1, nb_last), a.num_blocks) : pb0;
+      if constexpr (F8) {
+        // K row r of quarter th: tile token 8(r/4) + 4th + r%4; V lane c: tile
+        // tokens 8c .. 8c+7 (at B = 16, K rows r >= 8 and V lanes c >= 2 are in
+        // the tile's second block)
+        const size_t bk = (B == 16 && r >= 8) ? pb1 : pb0;
+        const size_t bv = (B == 16 && c >= 2) ? pb1 : pb0;
+        const int ktok = (8 * (r >> 2) + (r & 3)) % B;
+        const int vtok = (8 * c) % B;
+        const auto* kb = k_pool + bk * blk_stride + head_off;
+        const auto* vb = v_pool + bv * blk_stride + head_off;
 #pragma unroll
-      for (int th = 0; th < 2; ++th) {
-        const size_t blk = (B == 16 && th == 1) ? pb1 : pb0;
-        const int tok = (B == 16 ? 0 : 16 * th);
-        const auto* kb = k_pool + blk * blk_stride + head_off;
-        const auto* vb = v_pool + blk * blk_stride + head_off;
-        if constexpr (F8) {
-          // dims 8(4j + c) .. +7: half c % 2 of the 16-dim chunk 2j + c / 2
+        for (int th = 0; th < 2; ++th)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            tl.k[th][j] = *reinterpret_cast<const u32x2*>(
-                kb + ((size_t)(2 * j + (c >> 1)) * B + tok + r) * 16 + 8 * (c & 1));
+          for (int i = 0; i < NJ / 2; ++i)
+            tl.k[th][i] = *reinterpret_cast<const u32x4*>(
+                kb + ((size_t)(4 * i + c) * B + ktok + 4 * th) * 16);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-            tl.v[th][dt] =
-                *reinterpret_cast<const uint32_t*>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
-        } else {
+        for (int dt = 0; dt < NDT; ++dt)
+          tl.v[dt] = *reinterpret_cast<const u32x2*>(vb + (size_t)(16 * dt + r) * B + vtok);
+      } else {
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+          const size_t blk = (B == 16 && th == 1) ? pb1 : pb0;
+          const int tok = (B == 16 ? 0 : 16 * th);
+          const auto* kb = k_pool + blk * blk_stride + head_off;
+          const auto* vb = v_pool + blk * blk_stride + head_off;
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             tl.k[th][j] =
@@ -170,31 +195,45 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
       for (int th = 0; th < 2; ++th)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tl.k[th][j]), qb[j],
+          sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tl, th, j), qb[j],
                                                              sacc[th], 0, 0, 0);
-      // sv[4th + i]: token T0 + 16th + 4c + i of column r
+      // sv[4th + i]: token T0 + 16th + 4c + i of column r (bf16), T0 + 8c + 4th + i
+      // (fp8)
       float sv[8];
 #pragma unroll
       for (int th = 0; th < 2; ++th)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * score_scale;
       if (T0 + TILE > first_pos + 1) {  // a tile some column cannot see all of
-#pragma unroll
-        for (int th = 0; th < 2; ++th) {
+        if constexpr (F8) {
           // tokens this lane's column may see, and tokens that exist at all
-          const int base = T0 + 16 * th + 4 * c;
-          const int nv = min(max(pos + 1 - base, 0), 4);
-          const int ne = min(max(end - base, 0), 4);
+          const int base = T0 + 8 * c;
+          const int nv = min(max(pos + 1 - base, 0), 8);
+          const int ne = min(max(end - base, 0), 8);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (i >= nv) sv[4 * th + i] = -INFINITY;
-          // V rows past the range end may hold anything (NaN): zero them so a
-          // zero weight cannot turn into NaN in the product
-          if constexpr (F8) {
-            const uint32_t mk = ne >= 4 ? 0xffffffffu : (1u << (8 * ne)) - 1u;
+          for (int e = 0; e < 8; ++e)
+            if (e >= nv) sv[e] = -INFINITY;
+          // V past the range end may hold anything (NaN): zero it so a zero
+          // weight cannot turn into NaN in the product
+          const uint32_t m0 = ne >= 4 ? 0xffffffffu : (1u << (8 * ne)) - 1u;
+          const uint32_t m1 = ne >= 8 ? 0xffffffffu : ne <= 4 ? 0u : (1u << (8 * (ne - 4))) - 1u;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt] &= mk;
-          } else {
+          for (int dt = 0; dt < NDT; ++dt) {
+            tl.v[dt][0] &= m0;
+            tl.v[dt][1] &= m1;
+          }
+        } else {
+#pragma unroll
+          for (int th = 0; th < 2; ++th) {
+            // tokens this lane's column may see, and tokens that exist at all
+            const int base = T0 + 16 * th + 4 * c;
+            const int nv = min(max(pos + 1 - base, 0), 4);
+            const int ne = min(max(end - base, 0), 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i >= nv) sv[4 * th + i] = -INFINITY;
+            // V rows past the range end may hold anything (NaN): zero them so a
+            // zero weight cannot turn into NaN in the product
 #pragma unroll
             for (int wd = 0; wd < 2; ++wd) {
               const uint32_t mk =
@@ -236,8 +275,7 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
       for (int dt = 0; dt < NDT; ++dt) {
         u32x4 va;
         if constexpr (F8) {
-          const u32x2 lo = fp8x4_to_bf16(tl.v[0][dt]), hi = fp8x4_to_bf16(tl.v[1][dt]);
-          va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          va = fp8x8_to_bf16(tl.v[dt]);
         } else {
           va = u32x4{tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
         }
