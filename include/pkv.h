@@ -494,13 +494,15 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *                 without new_key.  Copy-on-write copies must run before, so
  *                 that no other sequence of the batch reads the written block.
  *                 A zero-length sequence appends nothing, and so does one whose
- *                 context_lens[s] exceeds max_context_len or max_blocks*B (its
- *                 last position is not in the launch).
+ *                 last position is not in the launch (see context_lens).
  *   block_tables  device int32 [S, max_blocks]
  *   context_lens  device int32 [S]: tokens of sequence s (the one written this
  *                 step included); 0 gives a zero row; at most
- *                 min(max_context_len, max_blocks*B) (larger values are clamped
- *                 to max_blocks*B and tokens past max_context_len are not read)
+ *                 min(max_context_len, max_blocks*B).  A larger value is not
+ *                 an error the device reports: the launch covers the first
+ *                 min(L, max_blocks*B, nparts*P) tokens, with P the partition
+ *                 size and nparts = ceil(min(max_context_len, max_blocks*B) / P),
+ *                 and appends only when that is all L tokens
  *   Query head h reads KV head h / (Hq/Hkv).
  *   max_context_len  host-known bound on context_lens; sizes the grid (no sync)
  *   scale         score scale, usually 1/sqrt(D)

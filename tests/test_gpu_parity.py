@@ -191,3 +191,49 @@ def test_full_config(pkv, name):
     say(f"  {len(rows)} rows, worst error {worst:.3e}")
     if name == "sampling_fork":
         assert len(case.pairs) == 224
+
+
+@pytest.mark.parametrize("dtype,G,D", [("bf16", 4, 128), ("bf16", 1, 64), ("f32", 2, 128),
+                                       ("bf16", 8, 64)])
+def test_reduce_more_partitions_than_one_round(pkv, dtype, G, D):
+    """Rows split into up to 125 partitions of 32 tokens: more than one round of
+    the 256-thread reduce (64 partitions a round), planned and unplanned."""
+    lens = (4000, 2100, 64, 1, 3333, 2049)
+    cfg = ragged(f"manyparts_{dtype}_G{G}_D{D}", 900 + G + D, lens, 2 * G, 2, D, 16, dtype, 32)
+    say(f"case {cfg.name}")
+    case = Case(pkv, W.make(cfg))
+    rkp, rvp = case.oracle_pools()
+    ref = case.oracle_out(rkp, rvp)
+    for plan in (False, True):
+        got, _, _ = case.run_device(pkv, plan=plan)
+        worst = check_attention(got, ref, dtype)
+        say(f"  plan={plan}: worst error {worst:.3e}")
+
+
+def test_context_beyond_table_row_is_clamped(pkv):
+    """A length beyond the table row (max_blocks * B tokens) is read as the row's
+    capacity: the output covers the first max_blocks * B tokens."""
+    import torch
+    lens = (1024, 100, 700)
+    cfg = ragged("clamp", 950, lens, 8, 2, 128, 16, "bf16", 512, kind="decode")
+    say("case clamp")
+    case = Case(pkv, W.make(cfg))
+    cap_blocks = 40                                    # 640 tokens per row
+    tables = np.ascontiguousarray(case.tables[:, :cap_blocks])
+    kp, vp = to_dev(case.k_pool), to_dev(case.v_pool)
+    q = to_dev(case.w.q)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    from oracle.attention import paged_attention_decode as ref_decode
+    ref = ref_decode(case.w.q, case.k_pool, case.v_pool, tables,
+                     np.minimum(np.asarray(lens, np.int32), cap_blocks * 16))
+    for plan in (False, True):
+        out = torch.full((3, 8, 128), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.empty(pkv.attention_workspace_bytes(3, 8, 128, 1024, 512), dtype=torch.uint8,
+                         device="cuda")
+        pl = pkv.make_plan(np.asarray(lens, np.int32), 2, 16, cap_blocks, 1024, 512) if plan \
+            else None
+        pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(tables).cuda(), lens_dev,
+                                   1024, partition_size=512, workspace=ws, plan=pl)
+        torch.cuda.synchronize()
+        worst = check_attention(out.cpu().numpy(), ref, "bf16")
+        say(f"  plan={plan}: worst error {worst:.3e}")
