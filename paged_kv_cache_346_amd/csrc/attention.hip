@@ -83,7 +83,8 @@ struct DecodeArgs {
   const float* v_scale;
   int S;
   int SG;            // S * Hkv: items per partition index
-  int items;         // work items in the grid
+  int items;         // attention work items in the grid
+  int store_items;   // appending launch: S store items after them, else 0
   int Hkv, max_blocks, num_blocks, nparts, P;
   float scale_log2e;
 };
@@ -168,6 +169,75 @@ __device__ __forceinline__ RowSink row_sink(const DecodeArgs& a, const WorkItem&
   return RowSink{a.part_acc + row * D, a.part_ml + 2 * row};
 }
 
+// Store item of an appending launch: sequence s's token of this step (row s of
+// new_k / new_v, every KV head) written into its slot at position L-1, when
+// the launch covers that position (the rule that gives the sequence an
+// attention item ending there).  The attention wave that ends at L-1 takes the
+// token from new_k / new_v, never from the pool, so these stores need no
+// ordering with it; the store items follow every attention item in the grid
+// and run in the launch's tail, so no attention wave waits for a store to be
+// acknowledged.  fp8 pools: each bf16 value is encoded with its head's scale,
+// as the cache write does.
+template <typename E, int D, int B>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, int s, E* __restrict__ k_pool,
+                                                E* __restrict__ v_pool) {
+  constexpr bool F8 = sizeof(E) == 1;
+  using RE = std::conditional_t<F8, uint16_t, E>;  // element of the new rows
+  constexpr int X = 16 / sizeof(E);                // elements per 16-byte K vector
+  constexpr int NCH = D / X;                       // K vectors per head
+  const int L0 = a.context_lens[s];
+  if (L0 <= 0 || L0 > a.max_blocks * B || L0 > a.nparts * a.P) return;
+  const int t = L0 - 1, off = t % B;
+  const int pb =
+      min(max(a.block_tables[(size_t)s * a.max_blocks + t / B], 0), a.num_blocks - 1);
+  const int lane = threadIdx.x & (kWave - 1);
+  const RE* kn = reinterpret_cast<const RE*>(a.new_k) + (size_t)s * a.Hkv * D;
+  const RE* vn = reinterpret_cast<const RE*>(a.new_v) + (size_t)s * a.Hkv * D;
+  E* kb = k_pool + (size_t)pb * a.Hkv * (D * B);
+  E* vb = v_pool + (size_t)pb * a.Hkv * (D * B);
+  for (int i = lane; i < a.Hkv * NCH; i += kWave) {
+    const int g = i / NCH, ch = i - g * NCH;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if constexpr (F8) {
+      const float ks = a.k_scale[g];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 src = *reinterpret_cast<const u32x4*>(kn + (size_t)g * D + ch * X + 8 * h);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (e & 1) ? (src[e >> 1] & 0xffff0000u) : (src[e >> 1] << 16);
+          const int d = 8 * h + e;
+          w[d >> 2] |= f32_to_e4m3(__uint_as_float(bits) / ks) << (8 * (d & 3));
+        }
+      }
+    } else {
+      w = *reinterpret_cast<const u32x4*>(kn + (size_t)g * D + ch * X);
+    }
+    *reinterpret_cast<u32x4*>(kb + (size_t)g * (D * B) + ((size_t)ch * B + off) * X) = w;
+  }
+  for (int i = lane; i < a.Hkv * D; i += kWave) {
+    const int g = i / D, d = i - g * D;
+    E v;
+    if constexpr (F8)
+      v = (E)f32_to_e4m3(__uint_as_float((uint32_t)vn[i] << 16) / a.v_scale[g]);
+    else
+      v = vn[i];
+    vb[(size_t)g * (D * B) + (size_t)d * B + off] = v;
+  }
+}
+
+// Grid position of this wave: a store item of an appending launch is handled
+// here (true: the wave is done); attention items return false.
+template <typename E, int D, int B, int NW, bool AP>
+__device__ __forceinline__ bool store_item(const DecodeArgs& a, E* k_pool, E* v_pool) {
+  if constexpr (!AP) return false;
+  const int item = (int)blockIdx.x * NW + uniform((int)threadIdx.x / kWave);
+  if (item < a.items) return false;
+  const int s = item - a.items;
+  if (s < a.store_items) store_new_token<E, D, B>(a, s, k_pool, v_pool);
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // VALU main kernel.  E = float, uint16_t (bf16 bits) or uint8_t (fp8 E4M3 codes,
 // bf16 queries: each 16-dim K chunk pairs with two 16-byte q vectors, codes are
@@ -192,6 +262,7 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int t = lane % B;   // token of this lane in q.k
   const int cg = lane / B;  // its chunk group
+  if (store_item<E, D, B, NW, AP>(a, k_pool, v_pool)) return;
   WorkItem it;
   int L;
   if (!item_ids<NW>(a, it, L)) return;
@@ -235,10 +306,9 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(
 
   // Append (decode step with new_k/new_v): the sequence's token of this step is
   // its last, at position L-1 in this item's final block.  The wave owning that
-  // partition loads it before its first tile, puts it into the final tile's
-  // registers in place of what the pool held there, and writes it into its slot
-  // after the tile loop (gfx9 counts stores with loads, so a store inside the
-  // loop would make every later load wait for it; nothing reads the slot back).
+  // partition loads it before its first tile and puts it into the final tile's
+  // registers in place of what the pool held there; a store item at the end of
+  // the grid writes it into its slot (store_new_token).
   const bool appends = AP && it.tail;
   const int tnew = it.end - 1;
   u32x4 nk[CPL];
@@ -275,21 +345,6 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(
       for (int k2 = 0; k2 < ND; ++k2) nv[k2] = vn[lane + kWave * k2];
     }
   }
-  auto write_new = [&]() {
-    if (!appends) return;
-    const int pb = tw.at(tnew / B, a.num_blocks);
-    const int off = tnew % B;
-    E* kb = k_pool + pb * blk_stride + head_off;
-    E* vb = v_pool + pb * blk_stride + head_off;
-    if (t == 0) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j)
-        *reinterpret_cast<u32x4*>(kb + ((cg + NCG * j) * B + off) * X) = nk[j];
-    }
-#pragma unroll
-    for (int k2 = 0; k2 < ND; ++k2) vb[(lane + kWave * k2) * B + off] = nv[k2];
-  };
-
   auto load = [&](int k, Tile& tl) {
     const int pb = tw.at(lb_first + k, a.num_blocks);
     const E* kb = k_pool + pb * blk_stride + head_off;
@@ -390,7 +445,6 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(
       if (appends) substitute(k, tl);
       compute(k, tl);
     });
-    write_new();
   } else {
     pipelined<Tile>(n, load, compute);
   }
@@ -460,6 +514,8 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane >> 4, r = lane & 15;
+  if (store_item<std::conditional_t<F8, uint8_t, uint16_t>, D, B, NW, AP>(a, k_pool, v_pool))
+    return;
   WorkItem it;
   int L;
   if (!item_ids<NW>(a, it, L)) return;
@@ -513,11 +569,10 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   // its last, at position L-1 in this item's final tile.  The wave owning that
   // partition loads it before its first tile and stages it in LDS once that
   // tile's loads are out; when the final tile arrives the staged values replace
-  // what the pool held there, and only after the tile loop does the wave write
-  // the token into its slot (gfx9 counts stores with loads, so a store inside
-  // the loop would make every later load wait for it; nothing reads the slot
-  // back).  fp8 pools: the token (bf16) is encoded with its head's scales as
-  // the cache write does, and its codes are staged, substituted and stored.
+  // what the pool held there.  A store item at the end of the grid writes the
+  // token into its slot (store_new_token).  fp8 pools: the token (bf16) is
+  // encoded with its head's scales as the cache write does, and its codes are
+  // staged and substituted.
   __shared__ __align__(16) uint16_t s_new[kWavesPerGroup][2][D];
   uint16_t* lds_k = s_new[threadIdx.x / kWave][0];
   uint16_t* lds_v = s_new[threadIdx.x / kWave][1];
@@ -792,30 +847,6 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
     }
   };
 
-  auto write_new = [&]() {
-    if constexpr (AP) {
-      if (appends) {
-        const int pb = tw.at(tnew / B, a.num_blocks);
-        const int off = tnew % B;
-        auto* vb = v_pool + pb * blk_stride + head_off;
-        if constexpr (F8) {
-          // lane holds half (lane % 2) of K chunk lane / 2
-          if (lane < D / 8)
-            *reinterpret_cast<u32x2*>(k_pool + pb * blk_stride + head_off +
-                                      ((size_t)(lane >> 1) * B + off) * 16 + 8 * (lane & 1)) = nk8;
-#pragma unroll
-          for (int i = 0; i < NVD; ++i) vb[(size_t)(lane + kWave * i) * B + off] = nv8[i];
-        } else {
-          if (lane < D / 8)
-            *reinterpret_cast<u32x4*>(k_pool + pb * blk_stride + head_off +
-                                      ((size_t)lane * B + off) * 8) = nk;
-#pragma unroll
-          for (int i = 0; i < NVD; ++i) vb[(size_t)(lane + kWave * i) * B + off] = nv[i];
-        }
-      }
-    }
-  };
-
   if constexpr (AP) {
     pipelined<Tile>(n, load, compute, stage_new, [&](int k, Tile& tl) {
       const int tn = tnew - (it.start + k * TILE);  // in this tile when appending
@@ -838,7 +869,6 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
       }
       compute(k, tl);
     });
-    write_new();
   } else {
     pipelined<Tile>(n, load, compute);
   }
@@ -1083,7 +1113,8 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
   const int64_t nparts = num_partitions(mcl, P);
   const int64_t items = plan.ptr ? (int64_t)plan.n_items : (int64_t)S * Hkv * nparts;
-  if (items > 0x7fffffffLL || (int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
+  const int64_t store_items = new_key ? S : 0;
+  if (items + store_items > 0x7fffffffLL || (int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
   *a = DecodeArgs{};
   a->out = out;
   a->block_tables = block_tables;
@@ -1096,6 +1127,7 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   a->S = S;
   a->SG = S * Hkv;
   a->items = (int)items;
+  a->store_items = (int)store_items;
   a->Hkv = Hkv;
   a->max_blocks = max_blocks;
   a->num_blocks = num_blocks;
@@ -1108,7 +1140,8 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
     a->part_acc = (float*)workspace;
     a->part_ml = a->part_acc + (size_t)S * Hq * nparts * D;
   }
-  *groups = (items + kWavesPerGroup - 1) / kWavesPerGroup;
+  // attention items, then (appending) one store item per sequence
+  *groups = (items + store_items + kWavesPerGroup - 1) / kWavesPerGroup;
   return PKV_OK;
 }
 
