@@ -165,15 +165,17 @@ class DecodeLoop:
             if st[key]:
                 parts[key] = np.asarray(st[key], np.int32)
         dev = self._stage(parts) if parts else {}
+        # every launch of the step goes to the current stream, looked up once
+        stream = torch.cuda.current_stream().cuda_stream
         # block copies in the scheduler's order: swap-ins, swap-outs, copy-on-write
         if "swap_in" in dev:
             swap_blocks(self.k_pool, self.v_pool, self.host_k, self.host_v,
-                        dev["swap_in"].view(-1, 2))
+                        dev["swap_in"].view(-1, 2), stream=stream)
         if "swap_out" in dev:
             swap_blocks(self.host_k, self.host_v, self.k_pool, self.v_pool,
-                        dev["swap_out"].view(-1, 2))
+                        dev["swap_out"].view(-1, 2), stream=stream)
         if "cow" in dev:
-            copy_blocks(self.k_pool, self.v_pool, dev["cow"].view(-1, 2))
+            copy_blocks(self.k_pool, self.v_pool, dev["cow"].view(-1, 2), stream=stream)
         out = self.out[:n]
         out_pf = None
         if pairs:
@@ -182,18 +184,19 @@ class DecodeLoop:
             q = q_source(all_pairs)
             if n_pf:
                 reshape_and_cache(k[:n_pf], v[:n_pf], self.k_pool, self.v_pool,
-                                  dev["slots"].view(torch.int64), k_scale=self.k_scale,
-                                  v_scale=self.v_scale)
+                                  dev["slots"].view(torch.int64), stream=stream,
+                                  k_scale=self.k_scale, v_scale=self.v_scale)
                 out_pf = self._prefill_out(n_pf)
                 paged_attention_prefill(out_pf, q[:n_pf], self.k_pool, self.v_pool,
                                         dev["pf_tables"].view(len(chunks), -1), dev["pf_lens"],
                                         dev["pf_start"], max(c for _, _, c in chunks),
-                                        k_scale=self.k_scale, v_scale=self.v_scale)
+                                        stream=stream, k_scale=self.k_scale,
+                                        v_scale=self.v_scale)
         if n:
             paged_attention_decode(out, q[n_pf:], self.k_pool, self.v_pool,
                                    dev["tables"].view(n, -1), dev["lens"], mcl,
                                    partition_size=self.P, workspace=self.ws,
-                                   plan=Plan(dev["plan"], n_items, n_merge),
+                                   plan=Plan(dev["plan"], n_items, n_merge), stream=stream,
                                    new_key=k[n_pf:], new_value=v[n_pf:],
                                    k_scale=self.k_scale, v_scale=self.v_scale)
         st["stats"] = self.sched.stats()   # before the finished requests leave
