@@ -358,6 +358,49 @@ pkv_status pkv_sched_stats(const pkv_sched* sched, int64_t* tokens_held,
                            int64_t* slots_committed, int32_t* n_waiting,
                            int32_t* n_running, int32_t* n_swapped);
 
+/* One step's device metadata, packed by pkv_pack_step into one host int32
+ * buffer so that a single copy takes it to the device.  Offsets count int32
+ * words from the buffer's start and are multiples of 4 (16 bytes); int64
+ * arrays take two words per entry.  n_prefill_rows = sum of the step's prefill
+ * chunk lengths; n_prefill = step->n_prefill; n_batch = step->n_batch. */
+typedef struct pkv_step_pack {
+  int32_t total_words;     /* words used (set also when buf_words is too small) */
+  int32_t n_prefill_rows;
+  int32_t slots_off;       /* int64 [n_prefill_rows]: slot of every chunk token */
+  int32_t pf_tables_off;   /* int32 [n_prefill, pf_width]: chunk requests' tables */
+  int32_t pf_width;        /* blocks of the longest chunk's end position */
+  int32_t pf_lens_off;     /* int32 [n_prefill]: start + len of each chunk */
+  int32_t pf_start_off;    /* int32 [n_prefill + 1]: first row of each chunk */
+  int32_t pf_max_rows;     /* longest chunk */
+  int32_t tables_off;      /* int32 [n_batch, width]: decode batch tables */
+  int32_t width;           /* blocks of the batch's longest context */
+  int32_t lens_off;        /* int32 [n_batch]: context lengths (token of the step included) */
+  int32_t max_context;
+  int32_t plan_off;        /* the batch's pkv_attention_plan, built from lens_off */
+  int32_t n_items, n_merge;
+  int32_t pairs_off;       /* int64 [n_prefill_rows + n_batch, 2]: (request id,
+                              position) of every K/V row the step writes: the
+                              chunks' tokens in order, then each batch request's
+                              new token */
+  int32_t swap_in_off, swap_out_off, cow_off; /* int32 pairs, step->n_* of each */
+} pkv_step_pack;
+
+/* Pack the device metadata of the step pkv_sched_begin_step just returned in
+ * `step` (before pkv_sched_end_step): the chunks' slots and tables, the decode
+ * batch's tables, lengths and work plan, the K/V row list and the block copy
+ * pairs ([ZENO] "Implementation Essentials": the block manager hands the
+ * kernels block tables; [RTI] "Batch by step, not by request").
+ *   bm            the scheduler's block manager
+ *   max_blocks    table row capacity of the loop (blocks of its longest request)
+ *   Hkv, partition_size   as for the attention call (for the plan)
+ *   buf           HOST int32 buffer of buf_words words (pinned, for an
+ *                 asynchronous copy)
+ * PKV_EINVAL with out->total_words set when buf_words is too small (nothing
+ * useful written); the caller grows the buffer and calls again. */
+pkv_status pkv_pack_step(const pkv_bm* bm, const pkv_sched_step* step, int32_t max_blocks,
+                         int32_t Hkv, int32_t partition_size, int32_t* buf, size_t buf_words,
+                         pkv_step_pack* out);
+
 /* ---------------------------------------------------------------------------
  * Device operations.
  * ------------------------------------------------------------------------- */

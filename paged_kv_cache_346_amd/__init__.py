@@ -23,7 +23,7 @@ __all__ = [
     "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pkv_paged_attention_main",
     "pkv_paged_attention_reduce", "pool_shapes", "paged_attention_main", "paged_attention_reduce",
     "pkv_attention_plan", "pkv_attention_plan_words", "attention_plan", "attention_plan_words",
-    "Plan", "make_plan",
+    "Plan", "make_plan", "StepPack",
     "reshape_and_cache", "copy_blocks", "attention_workspace_bytes", "paged_attention_decode",
     "LIB_PATH", "lib",
 ]
@@ -72,6 +72,16 @@ class _SchedStep(ctypes.Structure):
                 ("n_swapped_out", ctypes.c_int32)]
 
 
+class StepPack(ctypes.Structure):
+    """pkv_step_pack (include/pkv.h): where pkv_pack_step put each array, in
+    int32 words from the buffer's start."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "total_words", "n_prefill_rows", "slots_off", "pf_tables_off", "pf_width",
+        "pf_lens_off", "pf_start_off", "pf_max_rows", "tables_off", "width", "lens_off",
+        "max_context", "plan_off", "n_items", "n_merge", "pairs_off", "swap_in_off",
+        "swap_out_off", "cow_off")]
+
+
 # name -> (restype, argtypes); mirrors include/pkv.h
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -90,6 +100,8 @@ SIGNATURES = {
     "pkv_sched_begin_step": (_i32, [_vp, ctypes.POINTER(_SchedStep)]),
     "pkv_sched_end_step": (_i32, [_vp]),
     "pkv_sched_stats": (_i32, [_vp, _pi64, _pi64, _pi32, _pi32, _pi32]),
+    "pkv_pack_step": (_i32, [_vp, ctypes.POINTER(_SchedStep), _i32, _i32, _i32, _pi32, _sz,
+                             ctypes.POINTER(StepPack)]),
     "pkv_bm_refcount": (_i32, [_vp, _i32, _pi32]),
     "pkv_bm_seq_info": (_i32, [_vp, _i64, _pi32, _pi32]),
     "pkv_bm_block_table": (_i32, [_vp, _i64, _pi32, _i32]),
@@ -438,6 +450,18 @@ class Scheduler:
 
     def end_step(self) -> None:
         _check(lib.pkv_sched_end_step(self._h), "pkv_sched_end_step")
+
+    def pack_step(self, max_blocks: int, Hkv: int, partition_size: int, buf: np.ndarray,
+                  out: StepPack) -> bool:
+        """pkv_pack_step for the step begin_step just returned, into the int32
+        array `buf`; False (with out.total_words set) when buf is too small."""
+        st = lib.pkv_pack_step(self.bm._h, ctypes.byref(self._step), max_blocks, Hkv,
+                               partition_size, _np_ptr(buf, ctypes.c_int32), buf.shape[0],
+                               ctypes.byref(out))
+        if st == PKV_EINVAL and out.total_words > buf.shape[0]:
+            return False
+        _check(st, "pkv_pack_step")
+        return True
 
     def stats(self):
         """(tokens held, slots committed, waiting, running, swapped out)."""

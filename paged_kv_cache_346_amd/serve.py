@@ -22,10 +22,10 @@ Essentials"): every step
      request into its slot as it goes;
   4. the finished requests give their blocks back.
 
-The step's metadata (slots, block copy pairs, block tables, lengths, work plan)
-is packed into one pinned host buffer and sent with a single asynchronous copy;
-two buffers alternate so the host fills one while the previous step's copy may
-still run.  The host pool, when there is one, is pinned host memory that the
+The step's metadata (slots, block copy pairs, block tables, lengths, work plan,
+the K/V row list) is packed by the library (pkv_pack_step) into one pinned host
+buffer and sent with a single asynchronous copy; two buffers alternate so the
+host fills one while the previous step's copy may still run.  The host pool, when there is one, is pinned host memory that the
 swap kernel reads and writes over the host link.
 
 K/V and query values come from caller-supplied sources (the loop computes no
@@ -42,13 +42,9 @@ import math
 import numpy as np
 import torch
 
-from . import (BlockManager, Plan, Scheduler, attention_plan, attention_workspace_bytes,
-               copy_blocks, paged_attention_decode, paged_attention_prefill, pool_shapes,
-               reshape_and_cache, swap_blocks)
-
-
-def _pad4(n: int) -> int:
-    return (n + 3) // 4 * 4   # int32 words to the next 16-byte boundary
+from . import (BlockManager, Plan, Scheduler, StepPack, attention_workspace_bytes, copy_blocks,
+               paged_attention_decode, paged_attention_prefill, pool_shapes, reshape_and_cache,
+               swap_blocks)
 
 
 class DecodeLoop:
@@ -96,30 +92,32 @@ class DecodeLoop:
             raise ValueError("request longer than the loop's max_len")
         self.sched.add_request(req_id, prompt_len, max_new_tokens, tokens=tokens)
 
-    def _stage(self, parts):
-        """Copy the int32 arrays `parts` (a dict) to the device in one transfer;
-        returns device views of them by name (each on a 16-byte boundary)."""
-        total = sum(_pad4(p.size) for p in parts.values())
+    def _pack(self):
+        """pkv_pack_step of the step begun into a pinned buffer (two alternate,
+        so the host fills one while the previous step's copy may still run),
+        then one asynchronous copy to the device.  Returns (layout, host
+        int32 view, device int32 buffer)."""
         i = self._turn
         self._turn ^= 1
         if self._done[i] is not None:
             self._done[i].synchronize()    # its previous copy has left the buffer
-        if self._host[i] is None or self._host[i].numel() < total:
-            cap = max(total, 1 << 16) * 2
+        lay = StepPack()
+        while True:
+            buf = self._host[i]
+            if buf is not None and self.sched.pack_step(self.max_blocks, self.Hkv, self.P,
+                                                        buf.numpy(), lay):
+                break
+            cap = max(lay.total_words, 1 << 16) * 2
             self._host[i] = torch.empty(cap, dtype=torch.int32, pin_memory=True)
             if self._dev is None or self._dev.numel() < cap:
                 self._dev = torch.empty(cap, dtype=torch.int32, device=self.device)
-        host = self._host[i].numpy()
-        off, spans = 0, {}
-        for name, p in parts.items():
-            host[off:off + p.size] = p.reshape(-1)
-            spans[name] = (off, p.size)
-            off += _pad4(p.size)
-        self._dev[:total].copy_(self._host[i][:total], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self._done[i] = ev
-        return {name: self._dev[o:o + n] for name, (o, n) in spans.items()}
+        total = lay.total_words
+        if total:
+            self._dev[:total].copy_(self._host[i][:total], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record()
+            self._done[i] = ev
+        return lay, self._host[i].numpy(), self._dev
 
     def step(self, kv_source, q_source):
         """One iteration.  Returns (the scheduler's step dict -- plus "stats",
@@ -129,75 +127,53 @@ class DecodeLoop:
         [prefill rows, Hq, D] for the step's chunks in order -- views valid
         until the next step -- and the host context lengths of the batch)."""
         st = self.sched.begin_step()
-        ids = st["batch"]
-        n = len(ids)
-        chunks = st["prefill"]
-        # token rows: the prefill chunks (written by reshape_and_cache), then one
-        # token per decoding request (written by the attention launch)
-        pairs, write_slots = [], []
-        for rid, start, cnt in chunks:
-            write_slots.append(self.bm.slots(rid, start, cnt))
-            pairs.append(np.stack([np.full(cnt, rid, np.int64),
-                                   np.arange(start, start + cnt, dtype=np.int64)], 1))
-        n_pf = sum(c for _, _, c in chunks)
-        parts = {}
-        if write_slots:
-            parts["slots"] = np.concatenate(write_slots).view(np.int32)
-            pf_ids = [rid for rid, _, _ in chunks]
-            pf_tables, _ = self.bm.fill_batch(pf_ids, self.max_blocks)
-            pf_lens = np.array([start + cnt for _, start, cnt in chunks], np.int32)
-            pf_width = max(1, -(-int(pf_lens.max()) // self.B))
-            parts.update(pf_tables=np.ascontiguousarray(pf_tables[:, :pf_width]).reshape(-1),
-                         pf_lens=pf_lens,
-                         pf_start=np.concatenate([[0], np.cumsum([c for _, _, c in chunks])])
-                         .astype(np.int32))
-        lens = np.empty(0, np.int32)
-        if n:
-            tables, lens = self.bm.fill_batch(ids, self.max_blocks)
-            mcl = int(lens.max())
-            width = max(1, -(-mcl // self.B))          # the batch's widest table
-            tables = np.ascontiguousarray(tables[:, :width])
-            words, n_items, n_merge = attention_plan(lens, self.Hkv, self.B, width, mcl,
-                                                     self.P)
-            pairs.append(np.stack([np.asarray(ids, np.int64), lens.astype(np.int64) - 1], 1))
-            parts.update(tables=tables.reshape(-1), lens=lens, plan=words)
-        for key in ("swap_in", "swap_out", "cow"):
-            if st[key]:
-                parts[key] = np.asarray(st[key], np.int32)
-        dev = self._stage(parts) if parts else {}
+        n = len(st["batch"])
+        nc = len(st["prefill"])
+        lay, host, dev = self._pack()
+        n_pf = lay.n_prefill_rows
+
+        def d(off, words):
+            return dev[off:off + words]
+
         # every launch of the step goes to the current stream, looked up once
         stream = torch.cuda.current_stream().cuda_stream
         # block copies in the scheduler's order: swap-ins, swap-outs, copy-on-write
-        if "swap_in" in dev:
+        if st["swap_in"]:
             swap_blocks(self.k_pool, self.v_pool, self.host_k, self.host_v,
-                        dev["swap_in"].view(-1, 2), stream=stream)
-        if "swap_out" in dev:
+                        d(lay.swap_in_off, 2 * len(st["swap_in"])).view(-1, 2), stream=stream)
+        if st["swap_out"]:
             swap_blocks(self.host_k, self.host_v, self.k_pool, self.v_pool,
-                        dev["swap_out"].view(-1, 2), stream=stream)
-        if "cow" in dev:
-            copy_blocks(self.k_pool, self.v_pool, dev["cow"].view(-1, 2), stream=stream)
+                        d(lay.swap_out_off, 2 * len(st["swap_out"])).view(-1, 2), stream=stream)
+        if st["cow"]:
+            copy_blocks(self.k_pool, self.v_pool, d(lay.cow_off, 2 * len(st["cow"])).view(-1, 2),
+                        stream=stream)
         out = self.out[:n]
         out_pf = None
-        if pairs:
-            all_pairs = np.concatenate(pairs)
-            k, v = kv_source(all_pairs)
-            q = q_source(all_pairs)
+        lens = host[lay.lens_off:lay.lens_off + n].copy()
+        # token rows: the prefill chunks (written by reshape_and_cache), then one
+        # token per decoding request (written by the attention launch)
+        if n_pf + n:
+            pairs = host[lay.pairs_off:lay.pairs_off + 4 * (n_pf + n)].view(np.int64)
+            pairs = pairs.reshape(-1, 2).copy()
+            k, v = kv_source(pairs)
+            q = q_source(pairs)
             if n_pf:
                 reshape_and_cache(k[:n_pf], v[:n_pf], self.k_pool, self.v_pool,
-                                  dev["slots"].view(torch.int64), stream=stream,
+                                  d(lay.slots_off, 2 * n_pf).view(torch.int64), stream=stream,
                                   k_scale=self.k_scale, v_scale=self.v_scale)
                 out_pf = self._prefill_out(n_pf)
                 paged_attention_prefill(out_pf, q[:n_pf], self.k_pool, self.v_pool,
-                                        dev["pf_tables"].view(len(chunks), -1), dev["pf_lens"],
-                                        dev["pf_start"], max(c for _, _, c in chunks),
-                                        stream=stream, k_scale=self.k_scale,
+                                        d(lay.pf_tables_off, nc * lay.pf_width).view(nc, -1),
+                                        d(lay.pf_lens_off, nc), d(lay.pf_start_off, nc + 1),
+                                        lay.pf_max_rows, stream=stream, k_scale=self.k_scale,
                                         v_scale=self.v_scale)
         if n:
+            plan = Plan(d(lay.plan_off, 4 * lay.n_items + lay.n_merge), lay.n_items, lay.n_merge)
             paged_attention_decode(out, q[n_pf:], self.k_pool, self.v_pool,
-                                   dev["tables"].view(n, -1), dev["lens"], mcl,
-                                   partition_size=self.P, workspace=self.ws,
-                                   plan=Plan(dev["plan"], n_items, n_merge), stream=stream,
-                                   new_key=k[n_pf:], new_value=v[n_pf:],
+                                   d(lay.tables_off, n * lay.width).view(n, -1),
+                                   d(lay.lens_off, n), lay.max_context,
+                                   partition_size=self.P, workspace=self.ws, plan=plan,
+                                   stream=stream, new_key=k[n_pf:], new_value=v[n_pf:],
                                    k_scale=self.k_scale, v_scale=self.v_scale)
         st["stats"] = self.sched.stats()   # before the finished requests leave
         self.sched.end_step()
