@@ -630,7 +630,8 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
     }
   };
 
-  auto load = [&](int k, Tile& tl) {
+  // the K and/or V half of tile k (WK, WV: std::bool_constant)
+  auto load_part = [&](int k, Tile& tl, auto WK, auto WV) {
     const int lb0 = (it.start + k * TILE) / B;
     // the tile's blocks (B / 16 quarters each); a block past the partition end
     // repeats the last one (its tokens are masked)
@@ -650,15 +651,19 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
         const int vtok = (8 * c) % B;
         const auto* kb = k_pool + bk * blk_stride + head_off;
         const auto* vb = v_pool + bv * blk_stride + head_off;
+        if constexpr (decltype(WK)::value) {
 #pragma unroll
-        for (int th = 0; th < 2; ++th)
+          for (int th = 0; th < 2; ++th)
 #pragma unroll
-          for (int i = 0; i < NJ / 2; ++i)
-            tl.k[2 * st + th][i] =
-                pool_load<kNtK, u32x4>(kb + ((size_t)(4 * i + c) * B + ktok + 4 * th) * 16);
+            for (int i = 0; i < NJ / 2; ++i)
+              tl.k[2 * st + th][i] =
+                  pool_load<kNtK, u32x4>(kb + ((size_t)(4 * i + c) * B + ktok + 4 * th) * 16);
+        }
+        if constexpr (decltype(WV)::value) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          tl.v[st][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + vtok);
+          for (int dt = 0; dt < NDT; ++dt)
+            tl.v[st][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + vtok);
+        }
       }
     } else {
 #pragma unroll
@@ -667,15 +672,24 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
         const int tok = (16 * th) % B;  // token offset of this quarter in its block
         const auto* kb = k_pool + blk * blk_stride + head_off;
         const auto* vb = v_pool + blk * blk_stride + head_off;
+        if constexpr (decltype(WK)::value) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          tl.k[th][j] = pool_load<kNtK, u32x4>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+          for (int j = 0; j < NJ; ++j)
+            tl.k[th][j] = pool_load<kNtK, u32x4>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
+        }
+        if constexpr (decltype(WV)::value) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          tl.v[th][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+          for (int dt = 0; dt < NDT; ++dt)
+            tl.v[th][dt] = pool_load<kNtV, u32x2>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
+        }
       }
     }
   };
+  using Yes = std::true_type;
+  using No = std::false_type;
+  auto load = [&](int k, Tile& tl) { load_part(k, tl, Yes{}, Yes{}); };
+  auto load_k = [&](int k, Tile& tl) { load_part(k, tl, Yes{}, No{}); };
+  auto load_v = [&](int k, Tile& tl) { load_part(k, tl, No{}, Yes{}); };
 
   // put the appended token (tile-relative index tn, wave-uniform) into half TH
   // of the final tile:
@@ -773,7 +787,8 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
 
   // one 32-token MFMA step over quarters q0, q0 + 1 of a tile: tokens T0 ..
   // T0 + 31, of which T0 is valid
-  auto step32 = [&](Tile& tl, auto q0c, int T0) {
+  // `mid()` runs once the step's q.k products have taken their K operands
+  auto step32 = [&](Tile& tl, auto q0c, int T0, auto&& mid) {
     constexpr int q0 = decltype(q0c)::value;
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -782,6 +797,12 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
       for (int j = 0; j < NJ; ++j)
         sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tl, q0 + th, j), qb[j],
                                                            sacc[th], 0, 0, 0);
+    if constexpr (!std::is_same_v<std::decay_t<decltype(mid)>, NoHook>) {
+      // keep the next loads after the products that read these K registers
+      // (hoisted above them, old and new K would both be live and spill)
+      __builtin_amdgcn_sched_barrier(0);
+      mid();
+    }
     // sv[4th + i]: token T0 + 16th + 4c + i (bf16), T0 + 8c + 4th + i (fp8)
     float sv[8];
 #pragma unroll
@@ -839,16 +860,24 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[dt], 0, 0, 0);
     }
   };
-  auto compute = [&](int k, Tile& tl) {
+  // tile k; `mid()` runs once the tile's K registers are free (after the last
+  // q.k products), so the next loads into them can be issued before the p.v half
+  auto compute_mid = [&](int k, Tile& tl, auto&& mid) {
     const int T0 = it.start + k * TILE;
-    step32(tl, std::integral_constant<int, 0>{}, T0);
     if constexpr (F8) {
-      if (T0 + 32 < it.end) step32(tl, std::integral_constant<int, 2>{}, T0 + 32);
+      step32(tl, std::integral_constant<int, 0>{}, T0, NoHook{});
+      if (T0 + 32 < it.end)
+        step32(tl, std::integral_constant<int, 2>{}, T0 + 32, mid);
+      else
+        mid();
+    } else {
+      step32(tl, std::integral_constant<int, 0>{}, T0, mid);
     }
   };
+  auto compute = [&](int k, Tile& tl) { compute_mid(k, tl, NoHook{}); };
 
   if constexpr (AP) {
-    pipelined<Tile>(n, load, compute, stage_new, [&](int k, Tile& tl) {
+    pipelined_split<Tile>(n, load, load_k, load_v, compute_mid, stage_new, [&](int k, Tile& tl) {
       const int tn = tnew - (it.start + k * TILE);  // in this tile when appending
       using I0 = std::integral_constant<int, 0>;
       using I1 = std::integral_constant<int, 1>;
@@ -870,7 +899,7 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
       compute(k, tl);
     });
   } else {
-    pipelined<Tile>(n, load, compute);
+    pipelined_split<Tile>(n, load, load_k, load_v, compute_mid, NoHook{}, compute);
   }
 
   ls += shfl_xor_f(ls, 16);

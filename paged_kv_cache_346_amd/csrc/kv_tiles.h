@@ -91,4 +91,36 @@ __device__ __forceinline__ void pipelined(int n, Load&& load, Compute&& compute)
   pipelined<Tile>(n, load, compute, NoHook{}, compute);
 }
 
+// The same two-buffer pipeline, but the K half of tile k+2 is issued inside
+// compute(k) for every other tile, through compute's `mid` hook, as soon as
+// tile k's K registers have been consumed, and the V half after compute(k):
+// more bytes are in flight while the rest of tile k is computed.  `load(k,
+// tile)` loads both halves, `load_k` and `load_v` one each; `compute(k, tile,
+// mid)` calls mid() exactly once.  Every load in the steady loop is
+// unconditional.
+template <typename Tile, typename Load, typename LoadK, typename LoadV, typename Compute,
+          typename First, typename Last>
+__device__ __forceinline__ void pipelined_split(int n, Load&& load, LoadK&& load_k,
+                                                LoadV&& load_v, Compute&& compute,
+                                                First&& first, Last&& last) {
+  if (n <= 0) return;
+  Tile ta, tb;
+  load(0, ta);
+  first();
+  int k = 0;
+  for (; k + 2 < n; k += 2) {
+    load(k + 1, tb);
+    compute(k, ta, [&] { load_k(k + 2, ta); });
+    load_v(k + 2, ta);
+    compute(k + 1, tb, NoHook{});
+  }
+  if (k + 1 < n) {
+    load(k + 1, tb);
+    compute(k, ta, NoHook{});
+    last(k + 1, tb);
+  } else {
+    last(k, ta);
+  }
+}
+
 }  // namespace pkv
