@@ -237,3 +237,41 @@ def test_context_beyond_table_row_is_clamped(pkv):
         torch.cuda.synchronize()
         worst = check_attention(out.cpu().numpy(), ref, "bf16")
         say(f"  plan={plan}: worst error {worst:.3e}")
+
+
+@pytest.mark.parametrize("plan", [False, True])
+def test_append_only_where_the_launch_covers_the_last_position(pkv, plan):
+    """A step's token is written only when the launch covers the sequence's
+    last position: not beyond the table row (max_blocks * B tokens), not beyond
+    the partitions max_context_len sizes.  The other sequences' tokens land as
+    reshape_and_cache would write them; nothing else in the pools changes."""
+    import torch
+    from oracle.cache_ops import reshape_and_cache as ref_cache
+    lens = (100, 700, 40)
+    cfg = ragged("append_cover", 960, lens, 8, 2, 128, 16, "bf16", 256)
+    say(f"case append_cover plan={plan}")
+    case = Case(pkv, W.make(cfg))
+    assert list(case.w.step_ids) == [0, 1, 2]
+    q = to_dev(case.w.q)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    # (table row width in blocks, max_context_len): 32 blocks hold 512 tokens, so
+    # the 700-token sequence is clamped; max_context_len 200 gives one 256-token
+    # partition, which does not reach position 699 either
+    for width, mcl in ((32, 700), (case.tables.shape[1], 200)):
+        tables = np.ascontiguousarray(case.tables[:, :width])
+        kp, vp = to_dev(case.k_pool), to_dev(case.v_pool)
+        out = torch.empty((3, 8, 128), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(pkv.attention_workspace_bytes(3, 8, 128, mcl, 256), 16),
+                         dtype=torch.uint8, device="cuda")
+        pl = pkv.make_plan(np.asarray(lens, np.int32), 2, 16, width, mcl, 256) if plan else None
+        pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(tables).cuda(), lens_dev, mcl,
+                                   partition_size=256, workspace=ws, plan=pl,
+                                   new_key=to_dev(case.w.k_new), new_value=to_dev(case.w.v_new))
+        torch.cuda.synchronize()
+        keep = [0, 2]
+        rk, rv = ref_cache(case.k_pool, case.v_pool, case.w.k_new[keep], case.w.v_new[keep],
+                           case.slots[keep])
+        assert np.array_equal(to_host_bits(kp).view(np.uint8), rk.view(np.uint8)), (width, mcl)
+        assert np.array_equal(to_host_bits(vp).view(np.uint8), rv.view(np.uint8)), (width, mcl)
+        rows = [(s, h) for s in keep for h in range(8)]
+        check_attention(out.cpu().numpy(), case.oracle_out(rk, rv, rows), "bf16", rows)
