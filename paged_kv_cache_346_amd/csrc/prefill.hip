@@ -12,19 +12,21 @@
 // with query head h reading KV head h / G.  Rows are packed sequence by
 // sequence: sequence s owns rows query_start[s] .. query_start[s+1]-1.
 //
-// Work decomposition (not on the pages).  One wave64 owns a (sequence, KV head,
-// query group) item, where a query group is 16/G consecutive query tokens: the
-// 16 columns of v_mfma_f32_16x16x32_bf16 hold (token, head) pairs, 16/G tokens
-// times the G heads of the KV head, so the matrix core is full for every G.
+// Work decomposition (not on the pages).  A query group is 16/G consecutive
+// query tokens: the 16 columns of v_mfma_f32_16x16x32_bf16 hold (token, head)
+// pairs, 16/G tokens times the G heads of the KV head, so the matrix core is
+// full for every G.  One wave64 owns a (sequence, KV head, NGQ consecutive
+// query groups) item: every K/V tile it loads feeds the products of all NGQ
+// groups, so the tiles are read from L2 once per NGQ * 16 query columns.
 // The wave walks the sequence's KV from token 0 to its last query's position in
 // 32-token tiles, exactly as the decode kernel's tile loop does (same operand
-// layouts, same base-2 online softmax, same bf16 hi + lo split of P); each
-// column masks the tokens after its own position (causal), and the block table
-// is read in windows of 64 entries, one per lane.  Query groups are numbered
-// from the end of each sequence's chunk, so the items with the longest KV range
-// are dispatched first.  Every group of a sequence reads the same prefix, so
-// K/V use ordinary cached loads: the re-reads are served from L2 or the
-// last-level cache.
+// layouts, same base-2 online softmax, same bf16 hi + lo split of P), with one
+// softmax state and accumulator per group; each column masks the tokens after
+// its own position (causal), and the block table is read in windows of 64
+// entries, one per lane.  Items are numbered from the end of each sequence's
+// chunk, so the items with the longest KV range are dispatched first.  Every
+// item of a sequence reads the same prefix, so K/V use ordinary cached loads:
+// the re-reads are served from L2 or the last-level cache.
 // fp8 E4M3 pools: the tiles hold the raw codes and each MFMA operand is widened
 // to bf16 where it is used (exact: an E4M3 value fits bf16); the K scale joins
 // the score scale and the V scale the output.  The kernel re-reads K/V from L2
@@ -54,22 +56,34 @@ struct PrefillArgs {
   float scale_log2e;
 };
 
+// Query groups per wave: two over bf16 pools (each tile feeds 32 query columns;
+// at D = 128 the two groups' state takes one wave per SIMD), one over fp8
+// pools, whose tiles are half the bytes and whose waves keep two per SIMD
+// (measured on 16 x (1,536 cached + 512 new) tokens: bf16 375 against 361
+// TFLOP/s, fp8 388 against 498 with two groups).
+template <bool F8>
+constexpr int prefill_groups_per_wave() {
+  return F8 ? 1 : 2;
+}
+
 template <int D, int B, int G, bool F8>
-__global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
+__global__ __launch_bounds__(kWave, (D == 128 && prefill_groups_per_wave<F8>() > 1) ? 1 : 2)
+void pa_prefill_kernel(
     PrefillArgs a, const uint16_t* __restrict__ q,
     const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ k_pool,
     const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ v_pool) {
   constexpr int TILE = 32;
   constexpr int NJ = D / 32;   // q.k k-steps
   constexpr int NDT = D / 16;  // p.v output dim tiles
-  constexpr int QT = 16 / G;   // query tokens per item
+  constexpr int QT = 16 / G;   // query tokens per group
+  constexpr int NGQ = prefill_groups_per_wave<F8>();
   static_assert(16 % G == 0 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane >> 4, r = lane & 15;
   const int SG = a.S * a.Hkv;
-  const int k_end = (int)blockIdx.x / SG;  // query group counted from the chunk's end
+  const int k_end = (int)blockIdx.x / SG;  // group set counted from the chunk's end
   const int sg = (int)blockIdx.x - k_end * SG;
   const int s = sg / a.Hkv, g = sg - s * a.Hkv;
   const int Hq = a.Hkv * G;
@@ -81,33 +95,46 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
   const int Q = min(row1 - row0, L);
   if (Q <= 0) return;
   const int rbase = row1 - Q;  // row of query 0 (rows past L_s leave the first ones out)
-  const int qg = (Q + QT - 1) / QT - 1 - k_end;
-  if (qg < 0) return;
+  const int nsets = ((Q + QT - 1) / QT + NGQ - 1) / NGQ;  // group sets of the chunk
+  const int set = nsets - 1 - k_end;
+  if (set < 0) return;
+  const int qg0 = set * NGQ;  // the set's first query group
 
-  // column r: query token qi (the last valid one stands in past the chunk's
-  // end; those columns are computed but not written) and head gi
-  const int qi_raw = qg * QT + r / G;
-  const bool col_valid = qi_raw < Q;
-  const int qi = min(qi_raw, Q - 1);
+  // column r of group u: query token qi (the last valid one stands in past the
+  // chunk's end; those columns are computed but not written) and head gi
   const int gi = r % G;
-  const int pos = L - Q + qi;                       // this column's last visible token
-  const int end = L - Q + min(qg * QT + QT, Q);     // one past the group's last position
-  const int first_pos = L - Q + qg * QT;            // smallest position of the group
+  int qi[NGQ], pos[NGQ];
+  bool col_valid[NGQ];
+#pragma unroll
+  for (int u = 0; u < NGQ; ++u) {
+    const int qi_raw = (qg0 + u) * QT + r / G;
+    col_valid[u] = qi_raw < Q;
+    qi[u] = min(qi_raw, Q - 1);
+    pos[u] = L - Q + qi[u];                         // this column's last visible token
+  }
+  const int end = L - Q + min((qg0 + NGQ) * QT, Q);  // one past the set's last position
+  const int first_pos = L - Q + qg0 * QT;           // smallest position of the set
 
-  bf16x8 qb[NJ];
-  {
-    const uint16_t* qrow = q + ((size_t)(rbase + qi) * Hq + g * G + gi) * D;
+  bf16x8 qb[NGQ][NJ];
+#pragma unroll
+  for (int u = 0; u < NGQ; ++u) {
+    const uint16_t* qrow = q + ((size_t)(rbase + qi[u]) * Hq + g * G + gi) * D;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int d0 = F8 ? 16 * (4 * (j >> 1) + c) + 8 * (j & 1) : 8 * (4 * j + c);
-      qb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + d0));
+      qb[u][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + d0));
     }
   }
 
-  float m = -INFINITY, ls = 0.f;
-  f32x4 acc[NDT];
+  float m[NGQ], ls[NGQ];
+  f32x4 acc[NGQ][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < NGQ; ++u) {
+    m[u] = -INFINITY;
+    ls[u] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // bf16: K of quarter th, k-step j, and V runs of quarter th; fp8: K of quarter
   // th, 16-byte load i (k-steps 2i, 2i + 1), and the lane's 8-token V run
@@ -190,31 +217,11 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
 
     auto compute = [&](int k, Tile& tl) {
       const int T0 = tok0 + k * TILE;
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int th = 0; th < 2; ++th)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tl, th, j), qb[j],
-                                                             sacc[th], 0, 0, 0);
-      // sv[4th + i]: token T0 + 16th + 4c + i of column r (bf16), T0 + 8c + 4th + i
-      // (fp8)
-      float sv[8];
-#pragma unroll
-      for (int th = 0; th < 2; ++th)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * score_scale;
-      if (T0 + TILE > first_pos + 1) {  // a tile some column cannot see all of
+      // V past the range end may hold anything (NaN): zero it so a zero weight
+      // cannot turn into NaN in the products
+      if (T0 + TILE > end) {
         if constexpr (F8) {
-          // tokens this lane's column may see, and tokens that exist at all
-          const int base = T0 + 8 * c;
-          const int nv = min(max(pos + 1 - base, 0), 8);
-          const int ne = min(max(end - base, 0), 8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= nv) sv[e] = -INFINITY;
-          // V past the range end may hold anything (NaN): zero it so a zero
-          // weight cannot turn into NaN in the product
+          const int ne = min(max(end - (T0 + 8 * c), 0), 8);
           const uint32_t m0 = ne >= 4 ? 0xffffffffu : (1u << (8 * ne)) - 1u;
           const uint32_t m1 = ne >= 8 ? 0xffffffffu : ne <= 4 ? 0u : (1u << (8 * (ne - 4))) - 1u;
 #pragma unroll
@@ -225,15 +232,7 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
         } else {
 #pragma unroll
           for (int th = 0; th < 2; ++th) {
-            // tokens this lane's column may see, and tokens that exist at all
-            const int base = T0 + 16 * th + 4 * c;
-            const int nv = min(max(pos + 1 - base, 0), 4);
-            const int ne = min(max(end - base, 0), 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (i >= nv) sv[4 * th + i] = -INFINITY;
-            // V rows past the range end may hold anything (NaN): zero them so a
-            // zero weight cannot turn into NaN in the product
+            const int ne = min(max(end - (T0 + 16 * th + 4 * c), 0), 4);
 #pragma unroll
             for (int wd = 0; wd < 2; ++wd) {
               const uint32_t mk =
@@ -244,60 +243,97 @@ __global__ __launch_bounds__(kWave, 2) void pa_prefill_kernel(
           }
         }
       }
-      float mx = sv[0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      // finite: token 0 is visible to every column, so the first tile sets a
-      // finite max and a later fully masked tile keeps it
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      u32x4 phw, plw;
-      float psum = 0.f;
+      for (int u = 0; u < NGQ; ++u) {
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const float p0 = fast_exp2(sv[2 * wd] - mn);
-        const float p1 = fast_exp2(sv[2 * wd + 1] - mn);
-        psum += p0 + p1;
-        const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
-        const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
-        const uint32_t l0 = f32_to_bf16_rne(p0 - __uint_as_float(h0));
-        const uint32_t l1 = f32_to_bf16_rne(p1 - __uint_as_float(h1));
-        phw[wd] = (h0 >> 16) | h1;
-        plw[wd] = l0 | (l1 << 16);
-      }
-      ls = ls * alpha + psum;
-      const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
-      const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
+        for (int th = 0; th < 2; ++th)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        u32x4 va;
-        if constexpr (F8) {
-          va = fp8x8_to_bf16(tl.v[dt]);
-        } else {
-          va = u32x4{tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
+          for (int j = 0; j < NJ; ++j)
+            sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tl, th, j), qb[u][j],
+                                                               sacc[th], 0, 0, 0);
+        // sv[4th + i]: token T0 + 16th + 4c + i of column r (bf16), T0 + 8c + 4th
+        // + i (fp8)
+        float sv[8];
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * score_scale;
+        if (T0 + TILE > first_pos + u * QT + 1) {  // a tile some column cannot see all of
+          if constexpr (F8) {
+            const int nv = min(max(pos[u] + 1 - (T0 + 8 * c), 0), 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e >= nv) sv[e] = -INFINITY;
+          } else {
+#pragma unroll
+            for (int th = 0; th < 2; ++th) {
+              const int nv = min(max(pos[u] + 1 - (T0 + 16 * th + 4 * c), 0), 4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (i >= nv) sv[4 * th + i] = -INFINITY;
+            }
+          }
         }
-        acc[dt] *= alpha;
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), ph,
-                                                          acc[dt], 0, 0, 0);
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pl,
-                                                          acc[dt], 0, 0, 0);
+        float mx = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, shfl_xor_f(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        // finite: token 0 is visible to every column, so the first tile sets a
+        // finite max and a later fully masked tile keeps it
+        const float mn = fmaxf(m[u], mx);
+        const float alpha = fast_exp2(m[u] - mn);
+        m[u] = mn;
+        u32x4 phw, plw;
+        float psum = 0.f;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const float p0 = fast_exp2(sv[2 * wd] - mn);
+          const float p1 = fast_exp2(sv[2 * wd + 1] - mn);
+          psum += p0 + p1;
+          const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
+          const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
+          const uint32_t l0 = f32_to_bf16_rne(p0 - __uint_as_float(h0));
+          const uint32_t l1 = f32_to_bf16_rne(p1 - __uint_as_float(h1));
+          phw[wd] = (h0 >> 16) | h1;
+          plw[wd] = l0 | (l1 << 16);
+        }
+        ls[u] = ls[u] * alpha + psum;
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          u32x4 va;
+          if constexpr (F8) {
+            va = fp8x8_to_bf16(tl.v[dt]);
+          } else {
+            va = u32x4{tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
+          }
+          acc[u][dt] *= alpha;
+          acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                               ph, acc[u][dt], 0, 0, 0);
+          acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                               pl, acc[u][dt], 0, 0, 0);
+        }
       }
     };
 
     pipelined<Tile>(n, load, compute);
   }
 
-  ls += shfl_xor_f(ls, 16);
-  ls += shfl_xor_f(ls, 32);
-  if (col_valid) {
-    float* dst = a.out + ((size_t)(rbase + qi) * Hq + g * G + gi) * D;
-    const float scl = out_scale / ls;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * c) = acc[dt] * scl;
+  for (int u = 0; u < NGQ; ++u) {
+    float l = ls[u];
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    if (col_valid[u]) {
+      float* dst = a.out + ((size_t)(rbase + qi[u]) * Hq + g * G + gi) * D;
+      const float scl = out_scale / l;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * c) = acc[u][dt] * scl;
+    }
   }
 }
 
@@ -352,7 +388,10 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     return PKV_EINVAL;
   const int QT = 16 / G;
   const int64_t groups = (max_query_len + QT - 1) / QT;
-  const int64_t items = groups * S * Hkv;
+  const int ngq = dtype == PKV_FP8_E4M3 ? prefill_groups_per_wave<true>()
+                                        : prefill_groups_per_wave<false>();
+  const int64_t sets = (groups + ngq - 1) / ngq;
+  const int64_t items = sets * S * Hkv;
   if (items > 0x7fffffffLL) return PKV_EINVAL;
   PrefillArgs a;
   a.out = out;
