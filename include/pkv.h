@@ -135,6 +135,17 @@ pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent_id, int64_t child_id);
  * the back of the free queue in logical order. */
 pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id);
 
+/* Give back a resident sequence's tokens past new_len, e.g. speculative draft
+ * tokens a verification rejected ([ZENO] "Impact and Follow-Ups": multi-token
+ * queries over paged KV also serve speculative decoding; drafts take their
+ * slots through pkv_bm_append_slot like any token).  Blocks past
+ * ceil(new_len/B) lose one reference each, in logical order, as in
+ * pkv_bm_free_seq; if the kept last block becomes partial and is not shared,
+ * its prefix-cache entry is withdrawn (its later slots will be rewritten).
+ * PKV_EINVAL for new_len outside [0, length] or a swapped-out sequence,
+ * PKV_ENOSEQ for an unknown one; no change on error. */
+pkv_status pkv_bm_truncate(pkv_bm* bm, int64_t seq_id, int32_t new_len);
+
 pkv_status pkv_bm_num_free(const pkv_bm* bm, int32_t* out);
 /* Pool geometry given at creation: blocks and tokens per block. */
 pkv_status pkv_bm_geometry(const pkv_bm* bm, int32_t* num_blocks, int32_t* block_size);

@@ -47,6 +47,15 @@ blocks to the CPU).  Readings where the pages are silent:
     ENOBLOCKS, no change); a swapped sequence cannot be appended to, forked or
     batched (EINVAL) but can be freed, and keeps its length.
 
+Speculative drafts ("Impact and Follow-Ups": multi-token queries over paged
+KV also serve speculative decoding): draft tokens take slots through
+append_slot like any token, and truncate(s, n) gives back those a verification
+rejects.  Readings where the pages are silent: the blocks past ceil(n/B) are
+released in logical order as free_seq releases them; the kept last block, when
+it becomes partial and is not shared, loses its prefix-cache entry (its slots
+past n will be rewritten); truncating to a length the sequence already has
+changes nothing.
+
 Prefix caching ("Impact and Follow-Ups": the KV of a shared prompt prefix is
 cached and reused across requests, so a hit makes that part of the prefill
 free; "Implementation Essentials": prefix sharing through block refcounts).
@@ -261,6 +270,26 @@ class BlockManager:
         self._release(self.tables.pop(sid))
         del self.lens[sid]
 
+    def truncate(self, sid: int, new_len: int) -> None:
+        """Give back the tokens of a resident sequence past new_len (rejected
+        speculative draft tokens).  Blocks past ceil(new_len / B) are released
+        as free_seq releases them, in logical order; if the kept last block
+        becomes partial, later appends will overwrite it in place, so a prefix
+        cache entry it holds is withdrawn when no other sequence shares it."""
+        self._resident(sid)
+        L = self.lens[sid]
+        if new_len < 0 or new_len > L:
+            raise BMError(EINVAL, "new length outside [0, length]")
+        table, B = self.tables[sid], self.B
+        keep = -(-new_len // B)
+        if new_len % B and self.ref[table[keep - 1]] == 1:
+            key = self.cached_key.pop(table[keep - 1], None)
+            if key is not None:
+                del self.cache[key]
+        self._release(table[keep:])
+        del table[keep:]
+        self.lens[sid] = new_len
+
     def _release(self, table) -> None:
         for b in table:
             self.ref[b] -= 1
@@ -359,6 +388,10 @@ def run_ops(bm, ops):
                 appends.append(tuple(bm.swap_out(op[1])))
             elif kind == "swap_in":
                 appends.append(tuple(bm.swap_in(op[1])))
+            elif kind == "truncate_by":
+                # cut op[2] tokens (more than the length is an invalid call)
+                L = bm.lens.get(op[1], 0)
+                bm.truncate(op[1], L - op[2])
             else:
                 raise ValueError(kind)
             codes.append(OK)

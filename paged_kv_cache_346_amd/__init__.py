@@ -92,6 +92,7 @@ SIGNATURES = {
     "pkv_bm_append_slots": (_i32, [_vp, _pi64, _i32, _pi64, _pi32, _pi32, _pi32]),
     "pkv_bm_fork": (_i32, [_vp, _i64, _i64]),
     "pkv_bm_free_seq": (_i32, [_vp, _i64]),
+    "pkv_bm_truncate": (_i32, [_vp, _i64, _i32]),
     "pkv_bm_num_free": (_i32, [_vp, _pi32]),
     "pkv_bm_geometry": (_i32, [_vp, _pi32, _pi32]),
     "pkv_sched_create": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(_vp)]),
@@ -229,6 +230,10 @@ class BlockManager:
 
     def free_seq(self, seq_id: int) -> None:
         _check(lib.pkv_bm_free_seq(self._h, seq_id), "pkv_bm_free_seq")
+
+    def truncate(self, seq_id: int, new_len: int) -> None:
+        """pkv_bm_truncate: give back the sequence's tokens past new_len."""
+        _check(lib.pkv_bm_truncate(self._h, seq_id, new_len), "pkv_bm_truncate")
 
     def geometry(self):
         """(num_blocks, block_size)."""

@@ -290,6 +290,28 @@ pkv_status pkv_bm_fork(pkv_bm* bm, int64_t parent_id, int64_t child_id) {
   return PKV_OK;
 }
 
+pkv_status pkv_bm_truncate(pkv_bm* bm, int64_t seq_id, int32_t new_len) {
+  if (!bm) return PKV_EINVAL;
+  pkv_bm::Seq* s;
+  if (pkv_status st = bm->resident(seq_id, &s)) return st;
+  if (new_len < 0 || new_len > s->len) return PKV_EINVAL;
+  const size_t keep = (size_t)((new_len + bm->B - 1) / bm->B);
+  if (new_len % bm->B) {
+    // the kept last block becomes partial: appends will rewrite it in place
+    // unless it is shared, so its prefix-cache entry goes
+    const int32_t b = s->table[keep - 1];
+    if (bm->ref[b] == 1 && !bm->cached_key[b].empty()) {
+      bm->cache.erase(bm->cached_key[b]);
+      bm->cached_key[b].clear();
+    }
+  }
+  for (size_t j = keep; j < s->table.size(); ++j)
+    if (--bm->ref[s->table[j]] == 0) bm->push_free(s->table[j]);
+  s->table.resize(keep);
+  s->len = new_len;
+  return PKV_OK;
+}
+
 pkv_status pkv_bm_free_seq(pkv_bm* bm, int64_t seq_id) {
   if (!bm) return PKV_EINVAL;
   auto it = bm->seqs.find(seq_id);

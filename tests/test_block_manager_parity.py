@@ -31,6 +31,12 @@ def run_native(pkv, bm, ops):
             elif op[0] in ("swap_out", "swap_in"):
                 fn = bm.swap_out if op[0] == "swap_out" else bm.swap_in
                 appends.append(tuple(map(tuple, fn(op[1]).tolist())))
+            elif op[0] == "truncate_by":
+                try:
+                    L = bm.seq_info(op[1])[0]
+                except pkv.PkvError:
+                    L = 0
+                bm.truncate(op[1], L - op[2])
             codes.append(0)
         except pkv.PkvError as e:
             codes.append(e.code)
@@ -257,3 +263,63 @@ def test_prefix_cache_scripts_bit_exact(pkv, seed):
         assert a == b, op
         assert native.cached_blocks() == ref.cached_blocks()
         assert_same_state(native, ref, range(6))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_scripts_with_truncation_bit_exact(pkv, seed):
+    rng = np.random.default_rng(1700 + seed)
+    N, B = int(rng.integers(3, 48)), int(rng.choice([1, 3, 16, 32]))
+    order = rng.permutation(N)
+    native, ref = pkv.BlockManager(N, B, order), RefBM(N, B, order)
+    swap = seed % 2 == 1
+    if swap:
+        native.set_host_pool(N // 2 + 1)
+        ref.set_host_pool(N // 2 + 1)
+    ops = W.random_script(rng, 400, max_seqs=7, max_add=4 * B, swap=swap, truncate=True)
+    assert any(op[0] == "truncate_by" for op in ops)
+    for chunk in range(0, len(ops), 25):
+        part = ops[chunk:chunk + 25]
+        assert run_native(pkv, native, part) == ref_run(ref, part)
+        assert_same_state(native, ref, range(7))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_speculative_trace_bit_exact(pkv, seed):
+    """The reference's speculative-decoding content simulation (drafts kept in
+    part, rollbacks into cached prompt blocks, prefix hits, copy-on-write)
+    replayed on the native block manager: the same results, state and
+    prefix-cache size after every call."""
+    from tests.test_oracle_truncate import simulate_speculative
+    log = []
+    simulate_speculative(1600 + seed, log=log)
+    B = int(np.random.default_rng(1600 + seed).choice([2, 4]))
+    order = np.random.default_rng(1600 + seed)
+    order.choice([2, 4])
+    order = order.permutation(40)
+    native, ref = pkv.BlockManager(40, B, order), RefBM(40, B, order)
+    for op in log:
+        got = want = None
+        try:
+            want = getattr(ref, {"add_prefix": "add_seq_prefix", "register": "register_prefix",
+                                 "append": "append_slot", "truncate": "truncate",
+                                 "free": "free_seq"}[op[0]])(*op[1:])
+        except Exception as e:       # noqa: BLE001 -- the status must match below
+            want = ("error", getattr(e, "code", None))
+        try:
+            if op[0] == "add_prefix":
+                got = native.add_seq_prefix(op[1], np.asarray(op[2], np.int32), op[3])
+            elif op[0] == "register":
+                got = native.register_prefix(op[1], np.asarray(op[2], np.int32), op[3])
+            elif op[0] == "append":
+                got = native.append_slot(op[1])
+            elif op[0] == "truncate":
+                got = native.truncate(op[1], op[2])
+            else:
+                got = native.free_seq(op[1])
+        except pkv.PkvError as e:
+            got = ("error", e.code)
+        assert got == want, op
+        ref_counts, free = native.snapshot()
+        assert ref_counts == ref.ref and free == list(ref.free), op
+        assert native.cached_blocks() == ref.cached_blocks(), op
+    assert any(op[0] == "truncate" for op in log)

@@ -396,3 +396,52 @@ def test_fp8_mutants_fail_pins(monkeypatch, mutant):
         except AssertionError:
             failed += 1
     assert failed > 0
+
+
+# --- truncate (speculative drafts) --------------------------------------------
+from tests import test_oracle_truncate as ttr
+
+
+class _TruncateKeepsCacheBM(obm.BlockManager):
+    """Truncation into a cached block leaves its prefix-cache entry in place."""
+
+    def truncate(self, sid, new_len):
+        self._resident(sid)
+        if new_len < 0 or new_len > self.lens[sid]:
+            raise obm.BMError(obm.EINVAL)
+        keep = -(-new_len // self.B)
+        table = self.tables[sid]
+        self._release(table[keep:])
+        del table[keep:]
+        self.lens[sid] = new_len
+
+
+class _TruncateReversedBM(obm.BlockManager):
+    """Truncation releases the cut blocks from the last one down."""
+
+    def truncate(self, sid, new_len):
+        self._resident(sid)
+        if new_len < 0 or new_len > self.lens[sid]:
+            raise obm.BMError(obm.EINVAL)
+        table, B = self.tables[sid], self.B
+        keep = -(-new_len // B)
+        if new_len % B and self.ref[table[keep - 1]] == 1:
+            key = self.cached_key.pop(table[keep - 1], None)
+            if key is not None:
+                del self.cache[key]
+        self._release(list(reversed(table[keep:])))
+        del table[keep:]
+        self.lens[sid] = new_len
+
+
+@pytest.mark.parametrize("cls", [_TruncateKeepsCacheBM, _TruncateReversedBM])
+def test_truncate_mutants_fail_pins(monkeypatch, cls):
+    monkeypatch.setattr(ttr, "BlockManager", cls)
+    failed = 0
+    for t in [ttr.test_truncate_worked_example] + \
+            [lambda s=s: ttr.simulate_speculative(1600 + s, cls) for s in range(12)]:
+        try:
+            t()
+        except (AssertionError, obm.BMError, KeyError, ValueError):
+            failed += 1
+    assert failed > 0

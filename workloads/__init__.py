@@ -216,15 +216,21 @@ def make(name_or_cfg, *, extra_free: float = 0.2, extra_blocks: int = 0,
 
 
 def random_script(rng: np.random.Generator, n_ops: int, max_seqs: int = 8, max_add: int = 80,
-                  swap: bool = False):
+                  swap: bool = False, truncate: bool = False):
     """A random block-manager op script (for state-parity tests): admissions,
     forks, single-token appends and frees over a small id space; with swap,
-    also swap-outs and swap-ins (one op in five)."""
+    also swap-outs and swap-ins (one op in five); with truncate, also
+    truncations by 0 to 2*max_add/10 tokens (one op in six; the length to cut
+    is drawn here, the new length is the sequence's length minus it)."""
     ops = []
     for _ in range(n_ops):
         if swap and rng.random() < 0.2:
             ops.append(("swap_out" if rng.random() < 0.5 else "swap_in",
                         int(rng.integers(0, max_seqs))))
+            continue
+        if truncate and rng.random() < 1 / 6:
+            ops.append(("truncate_by", int(rng.integers(0, max_seqs)),
+                        int(rng.integers(0, max(2, max_add // 5) + 1))))
             continue
         r = rng.random()
         sid = int(rng.integers(0, max_seqs))
