@@ -232,3 +232,76 @@ def test_fp8_subnormal_codes_decode_exactly(pkv, G):
     want = ref_decode(q, kp, vp, tables, clens, k_scale=k_scale, v_scale=v_scale)
     worst = check_attention(out.cpu().numpy(), want, "bf16")
     say(f"  worst error {worst:.3e}")
+
+
+@pytest.mark.parametrize("name", ["llama8b_gqa", "long70b_b16"])
+def test_fp8_full_config(pkv, name):
+    """Full-size workloads over fp8 pools in the benchmark's launch configuration
+    (host plan; the step's tokens encoded and written by the attention launch):
+    whole pools bit-exact against the reference fp8 cache write, sampled rows
+    (longest and shortest sequences included) within the bf16 bound of the fp64
+    reference over the dequantized pools.  Pools hold random finite codes, NaN
+    codes in every slot that holds no token."""
+    import torch
+    from oracle.attention import valid_slot_mask
+    say(f"case fp8 {name} (full size)")
+    w = W.make(name, pools=False)
+    c = w.cfg
+    bm = pkv.BlockManager(w.num_blocks, c.B, w.free_order)
+    for op in w.ops:
+        if op[0] == "add":
+            bm.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            bm.fork(op[1], op[2])
+        elif op[0] == "extend":
+            for _ in range(op[2]):
+                bm.append_slot(op[1])
+    ids = list(range(c.S))
+    max_blocks = max(1, max(-(-int(L) // c.B) for L in w.lengths))
+    pre_tables, pre_lens = bm.fill_batch(ids, max_blocks)
+    slots = np.zeros(0, np.int64)
+    if w.step_ids:
+        slots, pairs = bm.append_slots(w.step_ids)
+        assert len(pairs) == 0
+    tables, lens = bm.fill_batch(ids, max_blocks)
+    rng = np.random.default_rng(2000 + c.seed)
+    ks, vs = W.pool_shapes(w.num_blocks, c.Hkv, c.D, c.B, "fp8")
+
+    def codes(shape):   # finite E4M3 codes below 4 in magnitude, random sign
+        return (rng.integers(0, 0x50, shape, dtype=np.uint8)
+                | (rng.integers(0, 2, shape, dtype=np.uint8) << 7))
+
+    kp, vp = codes(ks), codes(vs)
+    bi, oi = np.nonzero(~valid_slot_mask(pre_tables, pre_lens, w.num_blocks, c.B))
+    kp[bi, :, :, oi, :] = NAN8
+    vp[bi, :, :, oi] = NAN8
+    k_scale = np.linspace(0.02, 0.03, c.Hkv).astype(np.float32)
+    v_scale = np.linspace(0.03, 0.02, c.Hkv).astype(np.float32)
+    append = len(w.step_ids) > 0
+    assert not append or list(w.step_ids) == ids
+    mcl = int(lens.max())
+    P = c.partition_size
+    dk, dv = _u8(kp), _u8(vp)
+    out = torch.full((c.S, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(pkv.attention_workspace_bytes(c.S, c.Hq, c.D, mcl, P), 16),
+                     dtype=torch.uint8, device="cuda")
+    pl = pkv.make_plan(lens, c.Hkv, c.B, max_blocks, mcl, P)
+    pkv.paged_attention_decode(out, to_dev(w.q), dk, dv, torch.from_numpy(tables).cuda(),
+                               torch.from_numpy(lens).cuda(), mcl, partition_size=P,
+                               workspace=ws, plan=pl,
+                               new_key=to_dev(w.k_new) if append else None,
+                               new_value=to_dev(w.v_new) if append else None,
+                               k_scale=torch.from_numpy(k_scale).cuda(),
+                               v_scale=torch.from_numpy(v_scale).cuda())
+    torch.cuda.synchronize()
+    say("  device done")
+    if append:
+        kp, vp = ref_cache(kp, vp, w.k_new, w.v_new, slots, k_scale, v_scale)
+    assert np.array_equal(dk.cpu().numpy(), kp)
+    assert np.array_equal(dv.cpu().numpy(), vp)
+    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
+    pick |= set(rng.choice(c.S, size=min(c.S, 10), replace=False).tolist())
+    rows = [(s, h) for s in sorted(pick) for h in (0, c.Hq // 2 + 1, c.Hq - 1)]
+    want = ref_decode(w.q, kp, vp, tables, lens, rows=rows, k_scale=k_scale, v_scale=v_scale)
+    worst = check_attention(out.cpu().numpy(), want, "bf16", rows)
+    say(f"  {len(rows)} rows, worst error {worst:.3e}")
