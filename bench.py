@@ -339,6 +339,7 @@ class _PinnedIndex:
         self.bufs = [torch.empty(cap, dtype=torch.int64, pin_memory=True) for _ in range(slots)]
         self.done = [None] * slots
         self.i = 0
+        self.stream = torch.cuda.current_stream()
 
     def __call__(self, idx):
         torch = self.torch
@@ -352,7 +353,7 @@ class _PinnedIndex:
         self.bufs[i][:n].numpy()[:] = idx
         out = self.bufs[i][:n].to(self.dev, non_blocking=True)
         ev = torch.cuda.Event()
-        ev.record()
+        ev.record(self.stream)
         self.done[i] = ev
         return out
 

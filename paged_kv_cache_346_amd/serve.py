@@ -92,7 +92,7 @@ class DecodeLoop:
             raise ValueError("request longer than the loop's max_len")
         self.sched.add_request(req_id, prompt_len, max_new_tokens, tokens=tokens)
 
-    def _pack(self):
+    def _pack(self, stream):
         """pkv_pack_step of the step begun into a pinned buffer (two alternate,
         so the host fills one while the previous step's copy may still run),
         then one asynchronous copy to the device.  Returns (layout, host
@@ -115,7 +115,7 @@ class DecodeLoop:
         if total:
             self._dev[:total].copy_(self._host[i][:total], non_blocking=True)
             ev = torch.cuda.Event()
-            ev.record()
+            ev.record(stream)
             self._done[i] = ev
         return lay, self._host[i].numpy(), self._dev
 
@@ -126,17 +126,18 @@ class DecodeLoop:
         attention output [n_batch, Hq, D], the prefill attention output
         [prefill rows, Hq, D] for the step's chunks in order -- views valid
         until the next step -- and the host context lengths of the batch)."""
+        # every copy and launch of the step goes to the current stream, looked up once
+        ts = torch.cuda.current_stream()
+        stream = ts.cuda_stream
         st = self.sched.begin_step()
         n = len(st["batch"])
         nc = len(st["prefill"])
-        lay, host, dev = self._pack()
+        lay, host, dev = self._pack(ts)
         n_pf = lay.n_prefill_rows
 
         def d(off, words):
             return dev[off:off + words]
 
-        # every launch of the step goes to the current stream, looked up once
-        stream = torch.cuda.current_stream().cuda_stream
         # block copies in the scheduler's order: swap-ins, swap-outs, copy-on-write
         if st["swap_in"]:
             swap_blocks(self.k_pool, self.v_pool, self.host_k, self.host_v,
