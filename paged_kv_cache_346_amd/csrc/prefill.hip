@@ -15,10 +15,11 @@
 // Work decomposition (not on the pages).  A query group is 16/G consecutive
 // query tokens: the 16 columns of v_mfma_f32_16x16x32_bf16 hold (token, head)
 // pairs, 16/G tokens times the G heads of the KV head, so the matrix core is
-// full for every G.  One wave64 owns a (sequence, KV head, NGQ consecutive
-// query groups) item: every K/V tile it loads feeds the products of all NGQ
-// groups, so the tiles are read from L2 once per NGQ * 16 query columns.
-// The wave walks the sequence's KV from token 0 to its last query's position in
+// full for every G.  Over fp8 pools one wave64 owns a (sequence, KV head, NGQ
+// consecutive query groups) item: every K/V tile it loads feeds the products of
+// all NGQ groups, so the tiles are read from L2 once per NGQ * 16 query columns.
+// Over bf16 pools a workgroup of waves shares each tile through LDS
+// (pa_prefill_shared_kernel below).  The wave walks the sequence's KV from token 0 to its last query's position in
 // 32-token tiles, exactly as the decode kernel's tile loop does (same operand
 // layouts, same base-2 online softmax, same bf16 hi + lo split of P), with one
 // softmax state and accumulator per group; each column masks the tokens after
@@ -56,11 +57,11 @@ struct PrefillArgs {
   float scale_log2e;
 };
 
-// Query groups per wave: two over bf16 pools (each tile feeds 32 query columns;
-// at D = 128 the two groups' state takes one wave per SIMD), one over fp8
-// pools, whose tiles are half the bytes and whose waves keep two per SIMD
-// (measured on 16 x (1,536 cached + 512 new) tokens: bf16 375 against 361
-// TFLOP/s, fp8 388 against 498 with two groups).
+// Query groups per wave of the per-wave kernel: one over fp8 pools, whose
+// waves then keep two per SIMD (measured on 16 x (1,536 cached + 512 new)
+// tokens: 498 TFLOP/s against 388 with two groups).  The bf16 setting (two;
+// at D = 128 their state takes one wave per SIMD) is what bf16 pools ran at
+// before the shared kernel: 375 TFLOP/s on the same workload.
 template <bool F8>
 constexpr int prefill_groups_per_wave() {
   return F8 ? 1 : 2;
@@ -337,6 +338,289 @@ void pa_prefill_kernel(
   }
 }
 
+// The same computation over bf16 pools with K/V tiles shared through LDS (not
+// on the pages).  A workgroup of PW waves owns a (sequence, KV head, PW * NGQ
+// consecutive query groups) item; each 32-token tile is fetched from memory once
+// per workgroup -- every thread moves a few 16-byte vectors of it into one of
+// two LDS buffers -- and each wave reads its MFMA operands from there, so a tile
+// feeds PW * NGQ * 16 query columns instead of NGQ * 16.  The LDS tile is a byte
+// copy of the tile's pool regions (K of its blocks, then V of its blocks), so the
+// operand reads have the pool's layout: a K operand is 1 KiB read contiguously
+// by the wave.  One barrier per tile: the buffer a tile is written into was last
+// read two tiles earlier, before every wave passed the previous barrier.  The
+// loads of tile k + 1 are issued after the barrier and land while tile k is
+// computed.  The tile count and every early exit depend only on the
+// workgroup's item, so all its waves reach every barrier.  Each wave computes
+// the tiles up to its own last position with exactly the per-wave kernel's
+// arithmetic for its groups (V past that position is zeroed), so the two
+// kernels give the same bits.
+constexpr int kPrefillSharedWaves = 4;
+constexpr int kPrefillSharedGroups = 2;
+
+template <int D, int B, int G, int PW, int NGQ>
+__global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
+    PrefillArgs a, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool) {
+  constexpr int TILE = 32;
+  constexpr int NJ = D / 32;   // q.k k-steps
+  constexpr int NDT = D / 16;  // p.v output dim tiles
+  constexpr int QT = 16 / G;   // query tokens per group
+  constexpr int GPS = PW * NGQ;     // query groups per workgroup item
+  constexpr int KB = TILE * D * 2;  // bytes of a tile's K (and of its V)
+  constexpr int RB = B * D * 2;     // bytes of one (block, head) K or V region
+  constexpr int NTH = PW * kWave;
+  constexpr int VPT = 2 * KB / (16 * NTH);  // 16-byte vectors per thread per tile
+  static_assert(16 % G == 0 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
+  static_assert(VPT >= 1 && VPT * 16 * NTH == 2 * KB, "a tile splits evenly over the threads");
+  static_assert(RB % (16 * kWave) == 0, "a wave's run of a tile lies in one pool region");
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  __shared__ __align__(16) uint8_t smem[2][2 * KB];
+
+  const int wave = (int)threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane >> 4, r = lane & 15;
+  const int SG = a.S * a.Hkv;
+  const int k_end = (int)blockIdx.x / SG;  // item counted from the chunk's end
+  const int sg = (int)blockIdx.x - k_end * SG;
+  const int s = sg / a.Hkv, g = sg - s * a.Hkv;
+  const int Hq = a.Hkv * G;
+
+  // workgroup-uniform exits only (before the first barrier)
+  const int row0 = a.query_start[s];
+  const int row1 = a.query_start[s + 1];
+  const int L = min(a.context_lens[s], a.max_blocks * B);
+  if (row0 < 0 || row1 > a.T || row1 < row0) return;  // a malformed offset: no rows
+  const int Q = min(row1 - row0, L);
+  if (Q <= 0) return;
+  const int rbase = row1 - Q;  // row of query 0 (rows past L_s leave the first ones out)
+  const int nsets = ((Q + QT - 1) / QT + GPS - 1) / GPS;
+  const int set = nsets - 1 - k_end;
+  if (set < 0) return;
+  // one past the item's last position: the tiles the workgroup loads
+  const int end = L - Q + min((set + 1) * GPS * QT, Q);
+
+  // this wave's groups; a wave whose groups all lie past the chunk still loads
+  // its share of every tile and takes every barrier
+  const int qg0 = set * GPS + wave * NGQ;
+  const bool active = qg0 * QT < Q;
+  const int gi = r % G;
+  int qi[NGQ], pos[NGQ];
+  bool col_valid[NGQ];
+#pragma unroll
+  for (int u = 0; u < NGQ; ++u) {
+    const int qi_raw = (qg0 + u) * QT + r / G;
+    col_valid[u] = qi_raw < Q;
+    qi[u] = min(qi_raw, Q - 1);
+    pos[u] = L - Q + qi[u];
+  }
+  const int wend = L - Q + min((qg0 + NGQ) * QT, Q);  // one past the wave's last position
+  const int first_pos = L - Q + qg0 * QT;
+
+  bf16x8 qb[NGQ][NJ];
+#pragma unroll
+  for (int u = 0; u < NGQ; ++u) {
+    const uint16_t* qrow = q + ((size_t)(rbase + qi[u]) * Hq + g * G + gi) * D;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      qb[u][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * j + c)));
+  }
+  float m[NGQ], ls[NGQ];
+  f32x4 acc[NGQ][NDT];
+#pragma unroll
+  for (int u = 0; u < NGQ; ++u) {
+    m[u] = -INFINITY;
+    ls[u] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int n = (end + TILE - 1) / TILE;
+  const int nb_last = (end + B - 1) / B - 1;  // a block past it repeats it (masked tokens)
+  const int* table = a.block_tables + (size_t)s * a.max_blocks;
+  const size_t head_off = (size_t)g * (D * B);
+  const size_t blk_stride = (size_t)a.Hkv * (D * B);
+
+  // thread t moves bytes 16(t + NTH i) of the tile's pool regions (K of its
+  // blocks, then V of its blocks); a wave's 1 KiB run lies in one region, so its
+  // block id is wave-uniform and read once per wave.  K lands in LDS in the pool
+  // layout.  V lands in MFMA operand order: 16 bytes per (dim tile dt, lane (c,
+  // r)) at (64 dt + lane) * 16 -- dim 16dt + r, tokens 4c .. 4c+3 of quarter 0
+  // and then of quarter 1 -- so each V operand is one contiguous 16-byte read;
+  // a staged V vector (dim d, tokens T .. T+7 of the tile) splits into two
+  // 8-byte runs of lanes (c0, d % 16) and (c0 + 1, d % 16), c0 = (T % 16) / 4
+  u32x4 stg[VPT];
+  auto sstore = [&](uint8_t* t) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int byte = 16 * ((int)threadIdx.x + NTH * i);
+      if (byte < KB) {
+        *reinterpret_cast<u32x4*>(t + byte) = stg[i];
+      } else {
+        const int o = byte - KB;
+        const int bt = o / RB;
+        const int e = (o - bt * RB) / 2;  // element of the (block, head) V region
+        const int d = e / B, tt = bt * B + e % B;
+        const int at = KB + ((d / 16) * kWave + ((tt % 16) / 4) * 16 + d % 16) * 16 + (tt / 16) * 8;
+        *reinterpret_cast<u32x2*>(t + at) = u32x2{stg[i][0], stg[i][1]};
+        *reinterpret_cast<u32x2*>(t + at + 256) = u32x2{stg[i][2], stg[i][3]};
+      }
+    }
+  };
+  auto gload = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int byte = 16 * ((int)threadIdx.x + NTH * i);
+      const int part = byte / KB;  // 0: K, 1: V
+      const int o = byte - part * KB;
+      const int bt = o / RB;       // block of the tile
+      const int lb = __builtin_amdgcn_readfirstlane(min(k * (TILE / B) + bt, nb_last));
+      const int pb = min(max(table[lb], 0), a.num_blocks - 1);
+      const uint16_t* base = (part ? v_pool : k_pool) + (size_t)pb * blk_stride + head_off;
+      stg[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(base) +
+                                               (o - bt * RB));
+    }
+  };
+
+  // tile k from LDS: K of quarter th at k-step j (lane (c, r): chunk 4j + c of
+  // token 16th + r, the pool layout) and the V operand of dim tile dt
+  auto compute = [&](int k, const uint8_t* t) {
+    const int T0 = k * TILE;
+    u32x4 v[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      v[dt] = *reinterpret_cast<const u32x4*>(t + KB + (dt * kWave + lane) * 16);
+    // V past the wave's last position may hold anything (NaN): zero it (words
+    // 2th + wd: tokens 16th + 4c + 2wd, +1)
+    if (T0 + TILE > wend) {
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        const int ne = min(max(wend - (T0 + 16 * th + 4 * c), 0), 4);
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd) {
+          const uint32_t mk =
+              (2 * wd < ne ? 0x0000ffffu : 0u) | (2 * wd + 1 < ne ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) v[dt][2 * th + wd] &= mk;
+        }
+      }
+    }
+    f32x4 sacc[NGQ][2];
+#pragma unroll
+    for (int u = 0; u < NGQ; ++u) sacc[u][0] = sacc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      const int rq = (16 * th) / B * RB, tq = (16 * th) % B;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x8 kop = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(t + rq + ((4 * j + c) * B + tq + r) * 16));
+#pragma unroll
+        for (int u = 0; u < NGQ; ++u)
+          sacc[u][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qb[u][j], sacc[u][th], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NGQ; ++u) {
+      // sv[4th + i]: token T0 + 16th + 4c + i of column r
+      float sv[8];
+#pragma unroll
+      for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[u][th][i] * a.scale_log2e;
+      if (T0 + TILE > first_pos + u * QT + 1) {  // a tile some column cannot see all of
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+          const int nv = min(max(pos[u] + 1 - (T0 + 16 * th + 4 * c), 0), 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i >= nv) sv[4 * th + i] = -INFINITY;
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      // finite: token 0 is visible to every column
+      const float mn = fmaxf(m[u], mx);
+      const float alpha = fast_exp2(m[u] - mn);
+      // no column's max moved: alpha is exactly 1 everywhere, skip the rescale
+      const bool rescale = __builtin_amdgcn_ballot_w64(mn != m[u]) != 0;
+      m[u] = mn;
+      u32x4 phw, plw;
+      float psum = 0.f;
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const float p0 = fast_exp2(sv[2 * wd] - mn);
+        const float p1 = fast_exp2(sv[2 * wd + 1] - mn);
+        psum += p0 + p1;
+        // hi: truncated to bf16; lo: the exact remainder rounded to nearest even
+        const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
+        const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
+        phw[wd] = (h0 >> 16) | h1;
+        plw[wd] = __builtin_bit_cast(
+            uint32_t, __builtin_convertvector(
+                          f32x2{p0 - __uint_as_float(h0), p1 - __uint_as_float(h1)}, bf16x2));
+      }
+      ls[u] = ls[u] * alpha + psum;
+      const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
+      if (rescale) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[u][dt] *= alpha;
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 va = __builtin_bit_cast(bf16x8, v[dt]);
+        acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[u][dt], 0, 0, 0);
+        acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[u][dt], 0, 0, 0);
+      }
+    }
+  };
+
+  gload(0);
+  for (int k = 0; k < n; ++k) {
+    uint8_t* t = smem[k & 1];
+    sstore(t);
+    __syncthreads();
+    if (k + 1 < n) gload(k + 1);
+    if (active && k * TILE < wend) compute(k, t);
+  }
+
+#pragma unroll
+  for (int u = 0; u < NGQ; ++u) {
+    float l = ls[u];
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    if (col_valid[u]) {
+      float* dst = a.out + ((size_t)(rbase + qi[u]) * Hq + g * G + gi) * D;
+      const float scl = 1.f / l;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * c) = acc[u][dt] * scl;
+    }
+  }
+}
+
+template <int D, int B>
+static bool launch_prefill_shared(int G, const PrefillArgs& a, unsigned grid, const void* q,
+                                  const void* kp, const void* vp, hipStream_t st) {
+  constexpr int PW = kPrefillSharedWaves, NGQ = kPrefillSharedGroups;
+  const uint16_t* qq = (const uint16_t*)q;
+  const uint16_t* kk = (const uint16_t*)kp;
+  const uint16_t* vv = (const uint16_t*)vp;
+  const dim3 blk(PW * kWave);
+  switch (G) {
+    case 1: pa_prefill_shared_kernel<D, B, 1, PW, NGQ><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
+    case 2: pa_prefill_shared_kernel<D, B, 2, PW, NGQ><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
+    case 4: pa_prefill_shared_kernel<D, B, 4, PW, NGQ><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
+    case 8: pa_prefill_shared_kernel<D, B, 8, PW, NGQ><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
+    default: return false;
+  }
+}
+
 template <int D, int B, bool F8>
 static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, const void* q,
                              const void* kp, const void* vp, hipStream_t st) {
@@ -388,8 +672,10 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     return PKV_EINVAL;
   const int QT = 16 / G;
   const int64_t groups = (max_query_len + QT - 1) / QT;
-  const int ngq = dtype == PKV_FP8_E4M3 ? prefill_groups_per_wave<true>()
-                                        : prefill_groups_per_wave<false>();
+  // query groups per item: per wave over fp8 pools, per workgroup over bf16
+  const bool f8 = dtype == PKV_FP8_E4M3;
+  const int ngq = f8 ? prefill_groups_per_wave<true>()
+                     : kPrefillSharedWaves * kPrefillSharedGroups;
   const int64_t sets = (groups + ngq - 1) / ngq;
   const int64_t items = sets * S * Hkv;
   if (items > 0x7fffffffLL) return PKV_EINVAL;
@@ -409,9 +695,15 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.scale_log2e = scale * 1.4426950408889634f;
   hipStream_t st = (hipStream_t)hip_stream;
   const unsigned grid = (unsigned)items;
-  const bool ok = dtype == PKV_FP8_E4M3
-                      ? launch_prefill<true>(D, B, G, a, grid, q, k_pool, v_pool, st)
-                      : launch_prefill<false>(D, B, G, a, grid, q, k_pool, v_pool, st);
+  bool ok;
+  if (f8)
+    ok = launch_prefill<true>(D, B, G, a, grid, q, k_pool, v_pool, st);
+  else if (D == 64)
+    ok = B == 16 ? launch_prefill_shared<64, 16>(G, a, grid, q, k_pool, v_pool, st)
+                 : launch_prefill_shared<64, 32>(G, a, grid, q, k_pool, v_pool, st);
+  else
+    ok = B == 16 ? launch_prefill_shared<128, 16>(G, a, grid, q, k_pool, v_pool, st)
+                 : launch_prefill_shared<128, 32>(G, a, grid, q, k_pool, v_pool, st);
   if (!ok) return PKV_EUNSUPPORTED;
   return launch_status();
 }
