@@ -670,7 +670,7 @@ def run_prefill(args, torch, np):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "pa_prefill_kernel" if fp8 else "pa_prefill_shared_kernel",
+                     "kernel": "pa_prefill_shared_kernel",
                      "algorithmic_flops_per_launch": flops},
         "kv_bytes_per_launch": kv_bytes,
     }

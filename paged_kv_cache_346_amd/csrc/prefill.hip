@@ -15,33 +15,26 @@
 // Work decomposition (not on the pages).  A query group is 16/G consecutive
 // query tokens: the 16 columns of v_mfma_f32_16x16x32_bf16 hold (token, head)
 // pairs, 16/G tokens times the G heads of the KV head, so the matrix core is
-// full for every G.  Over fp8 pools one wave64 owns a (sequence, KV head, NGQ
-// consecutive query groups) item: every K/V tile it loads feeds the products of
-// all NGQ groups, so the tiles are read from L2 once per NGQ * 16 query columns.
-// Over bf16 pools a workgroup of waves shares each tile through LDS
-// (pa_prefill_shared_kernel below).  The wave walks the sequence's KV from token 0 to its last query's position in
-// 32-token tiles, exactly as the decode kernel's tile loop does (same operand
-// layouts, same base-2 online softmax, same bf16 hi + lo split of P), with one
-// softmax state and accumulator per group; each column masks the tokens after
-// its own position (causal), and the block table is read in windows of 64
-// entries, one per lane.  Items are numbered from the end of each sequence's
-// chunk, so the items with the longest KV range are dispatched first.  Every
-// item of a sequence reads the same prefix, so K/V use ordinary cached loads:
-// the re-reads are served from L2 or the last-level cache.
-// fp8 E4M3 pools: the tiles hold the raw codes and each MFMA operand is widened
-// to bf16 where it is used (exact: an E4M3 value fits bf16); the K scale joins
-// the score scale and the V scale the output.  The kernel re-reads K/V from L2
-// for every query group, so it is bound by load instructions per token: fp8
-// tiles take the decode kernel's wide-load token order -- one 16-byte K load
-// is a whole 16-dim chunk feeding two k-steps (q read with the same dim
-// mapping), row r of quarter th stands for tile token 8(r/4) + 4th + r%4, and
-// one 8-byte V load holds the lane's tokens 8c .. 8c+7 -- 12 loads per tile.
+// full for every G.  A workgroup of PW waves owns a (sequence, KV head, PW * NGQ
+// consecutive query groups) item, NGQ groups per wave, and walks the sequence's
+// KV from token 0 to the item's last position in 32-token tiles.  Each tile is
+// fetched once per workgroup -- every thread moves a few 16-byte vectors of it
+// into one of two LDS buffers -- and each wave reads its MFMA operands from
+// there, so a tile feeds PW * NGQ * 16 query columns.  The products are the
+// decode kernel's (same operand layouts, same base-2 online softmax, same bf16
+// hi + lo split of P), with one softmax state and accumulator per group; each
+// column masks the tokens after its own position (causal).  Items are numbered
+// from the end of each sequence's chunk, so the items with the longest KV range
+// are dispatched first; every item of a sequence reads the same prefix, so the
+// pool loads are ordinary cached loads.
+// fp8 E4M3 pools: the tiles hold the raw codes (half the bytes) and each MFMA
+// operand is widened to bf16 where it is used (exact: an E4M3 value fits bf16);
+// the K scale joins the score scale and the V scale the output.
 #include <cmath>
 #include <type_traits>
 
 #include "../../include/pkv.h"
 #include "device_common.h"
-#include "kv_tiles.h"
 #include "launch_check.h"
 
 namespace pkv {
@@ -57,317 +50,35 @@ struct PrefillArgs {
   float scale_log2e;
 };
 
-// Query groups per wave of the per-wave kernel: one over fp8 pools, whose
-// waves then keep two per SIMD (measured on 16 x (1,536 cached + 512 new)
-// tokens: 498 TFLOP/s against 388 with two groups).  The bf16 setting (two;
-// at D = 128 their state takes one wave per SIMD) is what bf16 pools ran at
-// before the shared kernel: 375 TFLOP/s on the same workload.
-template <bool F8>
-constexpr int prefill_groups_per_wave() {
-  return F8 ? 1 : 2;
-}
-
-template <int D, int B, int G, bool F8>
-__global__ __launch_bounds__(kWave, (D == 128 && prefill_groups_per_wave<F8>() > 1) ? 1 : 2)
-void pa_prefill_kernel(
-    PrefillArgs a, const uint16_t* __restrict__ q,
-    const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ k_pool,
-    const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ v_pool) {
-  constexpr int TILE = 32;
-  constexpr int NJ = D / 32;   // q.k k-steps
-  constexpr int NDT = D / 16;  // p.v output dim tiles
-  constexpr int QT = 16 / G;   // query tokens per group
-  constexpr int NGQ = prefill_groups_per_wave<F8>();
-  static_assert(16 % G == 0 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int c = lane >> 4, r = lane & 15;
-  const int SG = a.S * a.Hkv;
-  const int k_end = (int)blockIdx.x / SG;  // group set counted from the chunk's end
-  const int sg = (int)blockIdx.x - k_end * SG;
-  const int s = sg / a.Hkv, g = sg - s * a.Hkv;
-  const int Hq = a.Hkv * G;
-
-  const int row0 = a.query_start[s];
-  const int row1 = a.query_start[s + 1];
-  const int L = min(a.context_lens[s], a.max_blocks * B);
-  if (row0 < 0 || row1 > a.T || row1 < row0) return;  // a malformed offset: no rows
-  const int Q = min(row1 - row0, L);
-  if (Q <= 0) return;
-  const int rbase = row1 - Q;  // row of query 0 (rows past L_s leave the first ones out)
-  const int nsets = ((Q + QT - 1) / QT + NGQ - 1) / NGQ;  // group sets of the chunk
-  const int set = nsets - 1 - k_end;
-  if (set < 0) return;
-  const int qg0 = set * NGQ;  // the set's first query group
-
-  // column r of group u: query token qi (the last valid one stands in past the
-  // chunk's end; those columns are computed but not written) and head gi
-  const int gi = r % G;
-  int qi[NGQ], pos[NGQ];
-  bool col_valid[NGQ];
-#pragma unroll
-  for (int u = 0; u < NGQ; ++u) {
-    const int qi_raw = (qg0 + u) * QT + r / G;
-    col_valid[u] = qi_raw < Q;
-    qi[u] = min(qi_raw, Q - 1);
-    pos[u] = L - Q + qi[u];                         // this column's last visible token
-  }
-  const int end = L - Q + min((qg0 + NGQ) * QT, Q);  // one past the set's last position
-  const int first_pos = L - Q + qg0 * QT;           // smallest position of the set
-
-  bf16x8 qb[NGQ][NJ];
-#pragma unroll
-  for (int u = 0; u < NGQ; ++u) {
-    const uint16_t* qrow = q + ((size_t)(rbase + qi[u]) * Hq + g * G + gi) * D;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int d0 = F8 ? 16 * (4 * (j >> 1) + c) + 8 * (j & 1) : 8 * (4 * j + c);
-      qb[u][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + d0));
-    }
-  }
-
-  float m[NGQ], ls[NGQ];
-  f32x4 acc[NGQ][NDT];
-#pragma unroll
-  for (int u = 0; u < NGQ; ++u) {
-    m[u] = -INFINITY;
-    ls[u] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // bf16: K of quarter th, k-step j, and V runs of quarter th; fp8: K of quarter
-  // th, 16-byte load i (k-steps 2i, 2i + 1), and the lane's 8-token V run
-  struct Tile16 {
-    u32x4 k[2][NJ];
-    u32x2 v[2][NDT];
-  };
-  struct Tile8 {
-    u32x4 k[2][NJ / 2];
-    u32x2 v[NDT];
-  };
-  using Tile = std::conditional_t<F8, Tile8, Tile16>;
-  const float score_scale = F8 ? a.scale_log2e * a.k_scale[g] : a.scale_log2e;
-  auto k_operand = [](const Tile& tl, int th, int j) {
-    if constexpr (F8) {
-      const u32x4 w = tl.k[th][j >> 1];
-      return __builtin_bit_cast(bf16x8, fp8x8_to_bf16((j & 1) ? u32x2{w[2], w[3]}
-                                                              : u32x2{w[0], w[1]}));
-    } else {
-      return __builtin_bit_cast(bf16x8, tl.k[th][j]);
-    }
-  };
-  const float out_scale = F8 ? a.v_scale[g] : 1.f;
-  const size_t head_off = (size_t)g * (D * B);
-  const size_t blk_stride = (size_t)a.Hkv * (D * B);
-  const int* table = a.block_tables + (size_t)s * a.max_blocks;
-  TableWindow tw;
-
-  // windows of 64 table entries (64 * B tokens, a whole number of tiles)
-  for (int w0 = 0; w0 * B < end; w0 += kWave) {
-    tw.load(table, w0, a.max_blocks);
-    const int tok0 = w0 * B;
-    const int wend = min(end, (w0 + kWave) * B);
-    const int n = (wend - tok0 + TILE - 1) / TILE;
-    const int nb_last = (wend + B - 1) / B - 1;  // last logical block of the window's range
-
-    auto load = [&](int k, Tile& tl) {
-      const int lb0 = (tok0 + k * TILE) / B;
-      const int pb0 = tw.at(lb0, a.num_blocks);
-      // B = 16: the tile's second block; past the range end it repeats the
-      // first (those tokens are masked)
-      const int pb1 = B == 16 ? tw.at(min(lb0 + 1, nb_last), a.num_blocks) : pb0;
-      if constexpr (F8) {
-        // K row r of quarter th: tile token 8(r/4) + 4th + r%4; V lane c: tile
-        // tokens 8c .. 8c+7 (at B = 16, K rows r >= 8 and V lanes c >= 2 are in
-        // the tile's second block)
-        const size_t bk = (B == 16 && r >= 8) ? pb1 : pb0;
-        const size_t bv = (B == 16 && c >= 2) ? pb1 : pb0;
-        const int ktok = (8 * (r >> 2) + (r & 3)) % B;
-        const int vtok = (8 * c) % B;
-        const auto* kb = k_pool + bk * blk_stride + head_off;
-        const auto* vb = v_pool + bv * blk_stride + head_off;
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-          for (int i = 0; i < NJ / 2; ++i)
-            tl.k[th][i] = *reinterpret_cast<const u32x4*>(
-                kb + ((size_t)(4 * i + c) * B + ktok + 4 * th) * 16);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          tl.v[dt] = *reinterpret_cast<const u32x2*>(vb + (size_t)(16 * dt + r) * B + vtok);
-      } else {
-#pragma unroll
-        for (int th = 0; th < 2; ++th) {
-          const size_t blk = (B == 16 && th == 1) ? pb1 : pb0;
-          const int tok = (B == 16 ? 0 : 16 * th);
-          const auto* kb = k_pool + blk * blk_stride + head_off;
-          const auto* vb = v_pool + blk * blk_stride + head_off;
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            tl.k[th][j] =
-                *reinterpret_cast<const u32x4*>(kb + ((size_t)(4 * j + c) * B + tok + r) * 8);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-            tl.v[th][dt] =
-                *reinterpret_cast<const u32x2*>(vb + (size_t)(16 * dt + r) * B + tok + 4 * c);
-        }
-      }
-    };
-
-    auto compute = [&](int k, Tile& tl) {
-      const int T0 = tok0 + k * TILE;
-      // V past the range end may hold anything (NaN): zero it so a zero weight
-      // cannot turn into NaN in the products
-      if (T0 + TILE > end) {
-        if constexpr (F8) {
-          const int ne = min(max(end - (T0 + 8 * c), 0), 8);
-          const uint32_t m0 = ne >= 4 ? 0xffffffffu : (1u << (8 * ne)) - 1u;
-          const uint32_t m1 = ne >= 8 ? 0xffffffffu : ne <= 4 ? 0u : (1u << (8 * (ne - 4))) - 1u;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            tl.v[dt][0] &= m0;
-            tl.v[dt][1] &= m1;
-          }
-        } else {
-#pragma unroll
-          for (int th = 0; th < 2; ++th) {
-            const int ne = min(max(end - (T0 + 16 * th + 4 * c), 0), 4);
-#pragma unroll
-            for (int wd = 0; wd < 2; ++wd) {
-              const uint32_t mk =
-                  (2 * wd < ne ? 0x0000ffffu : 0u) | (2 * wd + 1 < ne ? 0xffff0000u : 0u);
-#pragma unroll
-              for (int dt = 0; dt < NDT; ++dt) tl.v[th][dt][wd] &= mk;
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NGQ; ++u) {
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            sacc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(tl, th, j), qb[u][j],
-                                                               sacc[th], 0, 0, 0);
-        // sv[4th + i]: token T0 + 16th + 4c + i of column r (bf16), T0 + 8c + 4th
-        // + i (fp8)
-        float sv[8];
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * score_scale;
-        if (T0 + TILE > first_pos + u * QT + 1) {  // a tile some column cannot see all of
-          if constexpr (F8) {
-            const int nv = min(max(pos[u] + 1 - (T0 + 8 * c), 0), 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= nv) sv[e] = -INFINITY;
-          } else {
-#pragma unroll
-            for (int th = 0; th < 2; ++th) {
-              const int nv = min(max(pos[u] + 1 - (T0 + 16 * th + 4 * c), 0), 4);
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (i >= nv) sv[4 * th + i] = -INFINITY;
-            }
-          }
-        }
-        float mx = sv[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        // finite: token 0 is visible to every column, so the first tile sets a
-        // finite max and a later fully masked tile keeps it
-        const float mn = fmaxf(m[u], mx);
-        const float alpha = fast_exp2(m[u] - mn);
-        m[u] = mn;
-        u32x4 phw, plw;
-        float psum = 0.f;
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const float p0 = fast_exp2(sv[2 * wd] - mn);
-          const float p1 = fast_exp2(sv[2 * wd + 1] - mn);
-          psum += p0 + p1;
-          const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
-          const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
-          const uint32_t l0 = f32_to_bf16_rne(p0 - __uint_as_float(h0));
-          const uint32_t l1 = f32_to_bf16_rne(p1 - __uint_as_float(h1));
-          phw[wd] = (h0 >> 16) | h1;
-          plw[wd] = l0 | (l1 << 16);
-        }
-        ls[u] = ls[u] * alpha + psum;
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          u32x4 va;
-          if constexpr (F8) {
-            va = fp8x8_to_bf16(tl.v[dt]);
-          } else {
-            va = u32x4{tl.v[0][dt][0], tl.v[0][dt][1], tl.v[1][dt][0], tl.v[1][dt][1]};
-          }
-          acc[u][dt] *= alpha;
-          acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
-                                                               ph, acc[u][dt], 0, 0, 0);
-          acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
-                                                               pl, acc[u][dt], 0, 0, 0);
-        }
-      }
-    };
-
-    pipelined<Tile>(n, load, compute);
-  }
-
-#pragma unroll
-  for (int u = 0; u < NGQ; ++u) {
-    float l = ls[u];
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
-    if (col_valid[u]) {
-      float* dst = a.out + ((size_t)(rbase + qi[u]) * Hq + g * G + gi) * D;
-      const float scl = out_scale / l;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * c) = acc[u][dt] * scl;
-    }
-  }
-}
-
-// The same computation over bf16 pools with K/V tiles shared through LDS (not
-// on the pages).  A workgroup of PW waves owns a (sequence, KV head, PW * NGQ
-// consecutive query groups) item; each 32-token tile is fetched from memory once
-// per workgroup -- every thread moves a few 16-byte vectors of it into one of
-// two LDS buffers -- and each wave reads its MFMA operands from there, so a tile
-// feeds PW * NGQ * 16 query columns instead of NGQ * 16.  The LDS tile is a byte
-// copy of the tile's pool regions (K of its blocks, then V of its blocks), so the
-// operand reads have the pool's layout: a K operand is 1 KiB read contiguously
-// by the wave.  One barrier per tile: the buffer a tile is written into was last
-// read two tiles earlier, before every wave passed the previous barrier.  The
-// loads of tile k + 1 are issued after the barrier and land while tile k is
-// computed.  The tile count and every early exit depend only on the
-// workgroup's item, so all its waves reach every barrier.  Each wave computes
-// the tiles up to its own last position with exactly the per-wave kernel's
-// arithmetic for its groups (V past that position is zeroed), so the two
-// kernels give the same bits.
+// The LDS tile is a byte copy of the tile's K pool regions followed by its V in
+// MFMA operand order, so a K operand is read contiguously by the wave and a V
+// operand is one read per lane.  One barrier per tile: the buffer a tile is
+// written into was last read two tiles earlier, before every wave passed the
+// previous barrier.  The loads of tile k + 1 are issued after the barrier and
+// land while tile k is computed.  The tile count and every early exit depend
+// only on the workgroup's item, so all its waves reach every barrier.  Each wave
+// computes the tiles up to its own last position (V past it is zeroed) and skips
+// the rest.  Four waves of two groups each: 128 query columns per tile (measured
+// on 16 x (1,536 cached + 512 new) tokens against four waves of one group and
+// eight of one; a wave of two groups keeps two per SIMD at D = 128).
 constexpr int kPrefillSharedWaves = 4;
 constexpr int kPrefillSharedGroups = 2;
 
-template <int D, int B, int G, int PW, int NGQ>
+template <int D, int B, int G, int PW, int NGQ, bool F8>
 __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
-    PrefillArgs a, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool) {
+    PrefillArgs a, const uint16_t* __restrict__ q,
+    const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ k_pool,
+    const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ v_pool) {
+  using E = std::conditional_t<F8, uint8_t, uint16_t>;
+  constexpr int ES = (int)sizeof(E);
   constexpr int TILE = 32;
   constexpr int NJ = D / 32;   // q.k k-steps
   constexpr int NDT = D / 16;  // p.v output dim tiles
   constexpr int QT = 16 / G;   // query tokens per group
   constexpr int GPS = PW * NGQ;     // query groups per workgroup item
-  constexpr int KB = TILE * D * 2;  // bytes of a tile's K (and of its V)
-  constexpr int RB = B * D * 2;     // bytes of one (block, head) K or V region
+  constexpr int KB = TILE * D * ES;  // bytes of a tile's K (and of its V)
+  constexpr int RB = B * D * ES;     // bytes of one (block, head) K or V region
+  constexpr int OPB = 8 * ES;        // bytes of one lane's V operand (8 tokens)
   constexpr int NTH = PW * kWave;
   constexpr int VPT = 2 * KB / (16 * NTH);  // 16-byte vectors per thread per tile
   static_assert(16 % G == 0 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
@@ -436,6 +147,9 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
     for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // fp8: the K scale joins the score scale, the V scale the output
+  const float score_scale = F8 ? a.scale_log2e * a.k_scale[g] : a.scale_log2e;
+  const float out_scale = F8 ? a.v_scale[g] : 1.f;
   const int n = (end + TILE - 1) / TILE;
   const int nb_last = (end + B - 1) / B - 1;  // a block past it repeats it (masked tokens)
   const int* table = a.block_tables + (size_t)s * a.max_blocks;
@@ -445,11 +159,11 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
   // thread t moves bytes 16(t + NTH i) of the tile's pool regions (K of its
   // blocks, then V of its blocks); a wave's 1 KiB run lies in one region, so its
   // block id is wave-uniform and read once per wave.  K lands in LDS in the pool
-  // layout.  V lands in MFMA operand order: 16 bytes per (dim tile dt, lane (c,
-  // r)) at (64 dt + lane) * 16 -- dim 16dt + r, tokens 4c .. 4c+3 of quarter 0
-  // and then of quarter 1 -- so each V operand is one contiguous 16-byte read;
-  // a staged V vector (dim d, tokens T .. T+7 of the tile) splits into two
-  // 8-byte runs of lanes (c0, d % 16) and (c0 + 1, d % 16), c0 = (T % 16) / 4
+  // layout.  V lands in MFMA operand order: OPB bytes per (dim tile dt, lane (c,
+  // r)) at (64 dt + lane) * OPB -- dim 16dt + r, tokens 4c .. 4c+3 of quarter 0
+  // and then of quarter 1 -- so each V operand is one contiguous read; a staged V
+  // vector (dim d, tokens T .. T + 16/ES - 1 of the tile) splits into 4-token
+  // runs of lanes (c0 + i, d % 16), c0 = (T % 16) / 4
   u32x4 stg[VPT];
   auto sstore = [&](uint8_t* t) {
 #pragma unroll
@@ -460,11 +174,17 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
       } else {
         const int o = byte - KB;
         const int bt = o / RB;
-        const int e = (o - bt * RB) / 2;  // element of the (block, head) V region
+        const int e = (o - bt * RB) / ES;  // element of the (block, head) V region
         const int d = e / B, tt = bt * B + e % B;
-        const int at = KB + ((d / 16) * kWave + ((tt % 16) / 4) * 16 + d % 16) * 16 + (tt / 16) * 8;
-        *reinterpret_cast<u32x2*>(t + at) = u32x2{stg[i][0], stg[i][1]};
-        *reinterpret_cast<u32x2*>(t + at + 256) = u32x2{stg[i][2], stg[i][3]};
+        const int at =
+            KB + ((d / 16) * kWave + ((tt % 16) / 4) * 16 + d % 16) * OPB + (tt / 16) * (4 * ES);
+        if constexpr (F8) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) *reinterpret_cast<uint32_t*>(t + at + 16 * OPB * w) = stg[i][w];
+        } else {
+          *reinterpret_cast<u32x2*>(t + at) = u32x2{stg[i][0], stg[i][1]};
+          *reinterpret_cast<u32x2*>(t + at + 16 * OPB) = u32x2{stg[i][2], stg[i][3]};
+        }
       }
     }
   };
@@ -477,32 +197,53 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
       const int bt = o / RB;       // block of the tile
       const int lb = __builtin_amdgcn_readfirstlane(min(k * (TILE / B) + bt, nb_last));
       const int pb = min(max(table[lb], 0), a.num_blocks - 1);
-      const uint16_t* base = (part ? v_pool : k_pool) + (size_t)pb * blk_stride + head_off;
+      const E* base = (part ? v_pool : k_pool) + (size_t)pb * blk_stride + head_off;
       stg[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(base) +
                                                (o - bt * RB));
     }
   };
 
-  // tile k from LDS: K of quarter th at k-step j (lane (c, r): chunk 4j + c of
-  // token 16th + r, the pool layout) and the V operand of dim tile dt
+  // tile k from LDS: K of quarter th at k-step j (lane (c, r): dims 32j + 8c ..
+  // +7 of token 16th + r, in the pool layout: bf16 chunk 4j + c, fp8 half c % 2
+  // of 16-dim chunk 2j + c / 2) and the V operand of dim tile dt.  fp8 codes are
+  // widened to bf16 per operand (exact)
+  auto k_operand = [&](const uint8_t* t, int th, int j) {
+    const int rq = (16 * th) / B * RB, tq = (16 * th) % B;
+    if constexpr (F8) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(
+          t + rq + ((2 * j + (c >> 1)) * B + tq + r) * 16 + 8 * (c & 1));
+      return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(w));
+    } else {
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(t + rq + ((4 * j + c) * B + tq + r) * 16));
+    }
+  };
+  using VOp = std::conditional_t<F8, u32x2, u32x4>;
   auto compute = [&](int k, const uint8_t* t) {
     const int T0 = k * TILE;
-    u32x4 v[NDT];
+    VOp v[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
-      v[dt] = *reinterpret_cast<const u32x4*>(t + KB + (dt * kWave + lane) * 16);
-    // V past the wave's last position may hold anything (NaN): zero it (words
-    // 2th + wd: tokens 16th + 4c + 2wd, +1)
+      v[dt] = *reinterpret_cast<const VOp*>(t + KB + (dt * kWave + lane) * OPB);
+    // V past the wave's last position may hold anything (NaN): zero it.  bf16:
+    // words 2th + wd hold tokens 16th + 4c + 2wd, +1; fp8: word th holds tokens
+    // 16th + 4c .. +3
     if (T0 + TILE > wend) {
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
         const int ne = min(max(wend - (T0 + 16 * th + 4 * c), 0), 4);
+        if constexpr (F8) {
+          const uint32_t mk = ne >= 4 ? 0xffffffffu : (1u << (8 * ne)) - 1u;
 #pragma unroll
-        for (int wd = 0; wd < 2; ++wd) {
-          const uint32_t mk =
-              (2 * wd < ne ? 0x0000ffffu : 0u) | (2 * wd + 1 < ne ? 0xffff0000u : 0u);
+          for (int dt = 0; dt < NDT; ++dt) v[dt][th] &= mk;
+        } else {
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) v[dt][2 * th + wd] &= mk;
+          for (int wd = 0; wd < 2; ++wd) {
+            const uint32_t mk =
+                (2 * wd < ne ? 0x0000ffffu : 0u) | (2 * wd + 1 < ne ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) v[dt][2 * th + wd] &= mk;
+          }
         }
       }
     }
@@ -511,11 +252,9 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
     for (int u = 0; u < NGQ; ++u) sacc[u][0] = sacc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int th = 0; th < 2; ++th) {
-      const int rq = (16 * th) / B * RB, tq = (16 * th) % B;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const bf16x8 kop = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(t + rq + ((4 * j + c) * B + tq + r) * 16));
+        const bf16x8 kop = k_operand(t, th, j);
 #pragma unroll
         for (int u = 0; u < NGQ; ++u)
           sacc[u][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qb[u][j], sacc[u][th], 0, 0, 0);
@@ -528,7 +267,7 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
 #pragma unroll
       for (int th = 0; th < 2; ++th)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[u][th][i] * a.scale_log2e;
+        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[u][th][i] * score_scale;
       if (T0 + TILE > first_pos + u * QT + 1) {  // a tile some column cannot see all of
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
@@ -573,7 +312,11 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8 va = __builtin_bit_cast(bf16x8, v[dt]);
+        bf16x8 va;
+        if constexpr (F8)
+          va = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(v[dt]));
+        else
+          va = __builtin_bit_cast(bf16x8, v[dt]);
         acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[u][dt], 0, 0, 0);
         acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[u][dt], 0, 0, 0);
       }
@@ -596,7 +339,7 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
     l += shfl_xor_f(l, 32);
     if (col_valid[u]) {
       float* dst = a.out + ((size_t)(rbase + qi[u]) * Hq + g * G + gi) * D;
-      const float scl = 1.f / l;
+      const float scl = out_scale / l;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * c) = acc[u][dt] * scl;
@@ -604,47 +347,32 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
   }
 }
 
-template <int D, int B>
+template <int D, int B, bool F8>
 static bool launch_prefill_shared(int G, const PrefillArgs& a, unsigned grid, const void* q,
                                   const void* kp, const void* vp, hipStream_t st) {
   constexpr int PW = kPrefillSharedWaves, NGQ = kPrefillSharedGroups;
-  const uint16_t* qq = (const uint16_t*)q;
-  const uint16_t* kk = (const uint16_t*)kp;
-  const uint16_t* vv = (const uint16_t*)vp;
-  const dim3 blk(PW * kWave);
-  switch (G) {
-    case 1: pa_prefill_shared_kernel<D, B, 1, PW, NGQ><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
-    case 2: pa_prefill_shared_kernel<D, B, 2, PW, NGQ><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
-    case 4: pa_prefill_shared_kernel<D, B, 4, PW, NGQ><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
-    case 8: pa_prefill_shared_kernel<D, B, 8, PW, NGQ><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
-    default: return false;
-  }
-}
-
-template <int D, int B, bool F8>
-static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, const void* q,
-                             const void* kp, const void* vp, hipStream_t st) {
   using E = std::conditional_t<F8, uint8_t, uint16_t>;
   const uint16_t* qq = (const uint16_t*)q;
   const E* kk = (const E*)kp;
   const E* vv = (const E*)vp;
+  const dim3 blk(PW * kWave);
   switch (G) {
-    case 1: pa_prefill_kernel<D, B, 1, F8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
-    case 2: pa_prefill_kernel<D, B, 2, F8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
-    case 4: pa_prefill_kernel<D, B, 4, F8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
-    case 8: pa_prefill_kernel<D, B, 8, F8><<<grid, kWave, 0, st>>>(a, qq, kk, vv); return true;
+    case 1: pa_prefill_shared_kernel<D, B, 1, PW, NGQ, F8><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
+    case 2: pa_prefill_shared_kernel<D, B, 2, PW, NGQ, F8><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
+    case 4: pa_prefill_shared_kernel<D, B, 4, PW, NGQ, F8><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
+    case 8: pa_prefill_shared_kernel<D, B, 8, PW, NGQ, F8><<<grid, blk, 0, st>>>(a, qq, kk, vv); return true;
     default: return false;
   }
 }
 
 template <bool F8>
-static bool launch_prefill(int D, int B, int G, const PrefillArgs& a, unsigned grid,
-                           const void* q, const void* kp, const void* vp, hipStream_t st) {
+static bool launch_prefill_shared(int D, int B, int G, const PrefillArgs& a, unsigned grid,
+                                  const void* q, const void* kp, const void* vp, hipStream_t st) {
   if (D == 64)
-    return B == 16 ? launch_prefill_g<64, 16, F8>(G, a, grid, q, kp, vp, st)
-                   : launch_prefill_g<64, 32, F8>(G, a, grid, q, kp, vp, st);
-  return B == 16 ? launch_prefill_g<128, 16, F8>(G, a, grid, q, kp, vp, st)
-                 : launch_prefill_g<128, 32, F8>(G, a, grid, q, kp, vp, st);
+    return B == 16 ? launch_prefill_shared<64, 16, F8>(G, a, grid, q, kp, vp, st)
+                   : launch_prefill_shared<64, 32, F8>(G, a, grid, q, kp, vp, st);
+  return B == 16 ? launch_prefill_shared<128, 16, F8>(G, a, grid, q, kp, vp, st)
+                 : launch_prefill_shared<128, 32, F8>(G, a, grid, q, kp, vp, st);
 }
 
 }  // namespace pkv
@@ -672,10 +400,8 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     return PKV_EINVAL;
   const int QT = 16 / G;
   const int64_t groups = (max_query_len + QT - 1) / QT;
-  // query groups per item: per wave over fp8 pools, per workgroup over bf16
   const bool f8 = dtype == PKV_FP8_E4M3;
-  const int ngq = f8 ? prefill_groups_per_wave<true>()
-                     : kPrefillSharedWaves * kPrefillSharedGroups;
+  constexpr int ngq = kPrefillSharedWaves * kPrefillSharedGroups;  // query groups per item
   const int64_t sets = (groups + ngq - 1) / ngq;
   const int64_t items = sets * S * Hkv;
   if (items > 0x7fffffffLL) return PKV_EINVAL;
@@ -695,15 +421,8 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.scale_log2e = scale * 1.4426950408889634f;
   hipStream_t st = (hipStream_t)hip_stream;
   const unsigned grid = (unsigned)items;
-  bool ok;
-  if (f8)
-    ok = launch_prefill<true>(D, B, G, a, grid, q, k_pool, v_pool, st);
-  else if (D == 64)
-    ok = B == 16 ? launch_prefill_shared<64, 16>(G, a, grid, q, k_pool, v_pool, st)
-                 : launch_prefill_shared<64, 32>(G, a, grid, q, k_pool, v_pool, st);
-  else
-    ok = B == 16 ? launch_prefill_shared<128, 16>(G, a, grid, q, k_pool, v_pool, st)
-                 : launch_prefill_shared<128, 32>(G, a, grid, q, k_pool, v_pool, st);
+  const bool ok = f8 ? launch_prefill_shared<true>(D, B, G, a, grid, q, k_pool, v_pool, st)
+                     : launch_prefill_shared<false>(D, B, G, a, grid, q, k_pool, v_pool, st);
   if (!ok) return PKV_EUNSUPPORTED;
   return launch_status();
 }
