@@ -64,6 +64,20 @@ struct PrefillArgs {
 constexpr int kPrefillSharedWaves = 4;
 constexpr int kPrefillSharedGroups = 2;
 
+// Max over lanes r, r + 16, r + 32, r + 48 (a score column's four row groups)
+// with gfx950's lane-swap instructions instead of LDS permutes: swapping halves
+// (rows) between two copies of x leaves each lane its own value in one register
+// and that of lane ^ 32 (lane ^ 16) in the other.  The max is exact, so the
+// order of the two steps does not matter.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 template <int D, int B, int G, int PW, int NGQ, bool F8>
 __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
     PrefillArgs a, const uint16_t* __restrict__ q,
@@ -280,8 +294,7 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
       float mx = sv[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      mx = max_over_rows(mx);
       // finite: token 0 is visible to every column
       const float mn = fmaxf(m[u], mx);
       const float alpha = fast_exp2(m[u] - mn);
