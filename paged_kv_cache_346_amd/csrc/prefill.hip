@@ -52,11 +52,12 @@ struct PrefillArgs {
 
 // The LDS tile is a byte copy of the tile's K pool regions followed by its V in
 // MFMA operand order, so a K operand is read contiguously by the wave and a V
-// operand is one read per lane.  One barrier per tile: the buffer a tile is
-// written into was last read two tiles earlier, before every wave passed the
-// previous barrier.  The loads of tile k + 1 are issued after the barrier and
-// land while tile k is computed.  The tile count and every early exit depend
-// only on the workgroup's item, so all its waves reach every barrier.  Each wave
+// operand is one read per lane.  Tiles are staged two at a time, one barrier
+// per pair: the buffer a pair is written into was last read two stages
+// earlier, before every wave passed the previous barrier, and the loads of the
+// next pair are issued after the barrier and land while this pair is computed.
+// The stage count and every early exit depend only on the workgroup's item, so
+// all its waves reach every barrier.  Each wave
 // computes the tiles up to its own last position (V past it is zeroed) and skips
 // the rest.  Four waves of two groups each: 128 query columns per tile (measured
 // on 16 x (1,536 cached + 512 new) tokens against four waves of one group and
@@ -101,7 +102,8 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  __shared__ __align__(16) uint8_t smem[2][2 * KB];
+  constexpr int TPS = 2;  // tiles per LDS stage (one barrier each)
+  __shared__ __align__(16) uint8_t smem[2][TPS][2 * KB];
 
   const int wave = (int)threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -178,13 +180,13 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
   // and then of quarter 1 -- so each V operand is one contiguous read; a staged V
   // vector (dim d, tokens T .. T + 16/ES - 1 of the tile) splits into 4-token
   // runs of lanes (c0 + i, d % 16), c0 = (T % 16) / 4
-  u32x4 stg[VPT];
-  auto sstore = [&](uint8_t* t) {
+  u32x4 stg[TPS][VPT];
+  auto sstore = [&](int h, uint8_t* t) {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int byte = 16 * ((int)threadIdx.x + NTH * i);
       if (byte < KB) {
-        *reinterpret_cast<u32x4*>(t + byte) = stg[i];
+        *reinterpret_cast<u32x4*>(t + byte) = stg[h][i];
       } else {
         const int o = byte - KB;
         const int bt = o / RB;
@@ -194,15 +196,16 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
             KB + ((d / 16) * kWave + ((tt % 16) / 4) * 16 + d % 16) * OPB + (tt / 16) * (4 * ES);
         if constexpr (F8) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) *reinterpret_cast<uint32_t*>(t + at + 16 * OPB * w) = stg[i][w];
+          for (int w = 0; w < 4; ++w)
+            *reinterpret_cast<uint32_t*>(t + at + 16 * OPB * w) = stg[h][i][w];
         } else {
-          *reinterpret_cast<u32x2*>(t + at) = u32x2{stg[i][0], stg[i][1]};
-          *reinterpret_cast<u32x2*>(t + at + 16 * OPB) = u32x2{stg[i][2], stg[i][3]};
+          *reinterpret_cast<u32x2*>(t + at) = u32x2{stg[h][i][0], stg[h][i][1]};
+          *reinterpret_cast<u32x2*>(t + at + 16 * OPB) = u32x2{stg[h][i][2], stg[h][i][3]};
         }
       }
     }
   };
-  auto gload = [&](int k) {
+  auto gload = [&](int k, int h) {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int byte = 16 * ((int)threadIdx.x + NTH * i);
@@ -212,8 +215,8 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
       const int lb = __builtin_amdgcn_readfirstlane(min(k * (TILE / B) + bt, nb_last));
       const int pb = min(max(table[lb], 0), a.num_blocks - 1);
       const E* base = (part ? v_pool : k_pool) + (size_t)pb * blk_stride + head_off;
-      stg[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(base) +
-                                               (o - bt * RB));
+      stg[h][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(base) +
+                                                  (o - bt * RB));
     }
   };
 
@@ -336,13 +339,24 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
     }
   };
 
-  gload(0);
-  for (int k = 0; k < n; ++k) {
-    uint8_t* t = smem[k & 1];
-    sstore(t);
+  // stages of TPS tiles; a tile past the last (odd n) loads the clamped last
+  // block and is not computed
+  const int ns = (n + TPS - 1) / TPS;
+#pragma unroll
+  for (int h = 0; h < TPS; ++h) gload(h, h);
+  for (int st = 0; st < ns; ++st) {
+#pragma unroll
+    for (int h = 0; h < TPS; ++h) sstore(h, smem[st & 1][h]);
     __syncthreads();
-    if (k + 1 < n) gload(k + 1);
-    if (active && k * TILE < wend) compute(k, t);
+    if (st + 1 < ns) {
+#pragma unroll
+      for (int h = 0; h < TPS; ++h) gload((st + 1) * TPS + h, h);
+    }
+#pragma unroll
+    for (int h = 0; h < TPS; ++h) {
+      const int k = st * TPS + h;
+      if (active && k * TILE < wend) compute(k, smem[st & 1][h]);
+    }
   }
 
 #pragma unroll
