@@ -169,3 +169,49 @@ def test_prefill_fp8_matches_reference(pkv, G, D, B):
     want = ref_prefill(q, kp, vp, tables, clens, QLENS, k_scale=k_scale, v_scale=v_scale)
     worst = check_attention(out.cpu().numpy(), want, "bf16")
     say(f"  worst error {worst:.3e}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_full_config(pkv, kv):
+    """The benchmark's multi-token workload at full size in its launch
+    configuration: 16 sequences x (1,536 cached + 512 new tokens) of the
+    Llama-3-8B-shaped layer (32/8 heads, D 128, B 16), each sequence on a
+    shuffled slice of the pool.  Sampled (row, head) outputs -- the first and
+    last chunk rows of the first and last sequences among them -- are within
+    the bf16 bound of the fp64 reference (over the dequantized pools for fp8)."""
+    import torch
+    say(f"case prefill full size {kv}")
+    rng = np.random.default_rng(2100 + (kv == "fp8"))
+    Hq, Hkv, D, B, S, prefix, chunk = 32, 8, 128, 16, 16, 1536, 512
+    L = prefix + chunk
+    nb = L // B
+    N = S * nb
+    ks, vs = W.pool_shapes(N, Hkv, D, B, kv)
+    extra, scales = {}, {}
+    if kv == "fp8":
+        def codes(shape):   # finite E4M3 codes below 4 in magnitude, random sign
+            return (rng.integers(0, 0x50, shape, dtype=np.uint8)
+                    | (rng.integers(0, 2, shape, dtype=np.uint8) << 7))
+        kp, vp = codes(ks), codes(vs)
+        scales = {"k_scale": np.linspace(0.02, 0.03, Hkv).astype(np.float32),
+                  "v_scale": np.linspace(0.03, 0.02, Hkv).astype(np.float32)}
+        extra = {k: torch.from_numpy(v).cuda() for k, v in scales.items()}
+    else:
+        kp, vp = W.normal(rng, ks, "bf16"), W.normal(rng, vs, "bf16")
+    tables = rng.permutation(N).astype(np.int32).reshape(S, nb)
+    clens = np.full(S, L, np.int32)
+    qlens = [chunk] * S
+    T = S * chunk
+    q = W.normal(rng, (T, Hq, D), "bf16")
+    starts = (np.arange(S + 1) * chunk).astype(np.int32)
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_prefill(out, to_dev(q), to_dev(kp), to_dev(vp),
+                                torch.from_numpy(tables).cuda(), torch.from_numpy(clens).cuda(),
+                                torch.from_numpy(starts).cuda(), chunk, **extra)
+    torch.cuda.synchronize()
+    say("  device done")
+    rows = [(0, 0), (chunk - 1, Hq - 1), ((S - 1) * chunk, 5), (T - 1, 17)]
+    rows += [(int(r), int(h)) for r, h in zip(rng.integers(0, T, 20), rng.integers(0, Hq, 20))]
+    want = ref_prefill(q, kp, vp, tables, clens, qlens, rows=rows, **scales)
+    worst = check_attention(out.cpu().numpy(), want, "bf16", rows=rows)
+    say(f"  worst error {worst:.3e} over {len(rows)} sampled rows")
