@@ -19,8 +19,8 @@
 // consecutive query groups) item, NGQ groups per wave, and walks the sequence's
 // KV from token 0 to the item's last position in 32-token tiles.  Each tile is
 // fetched once per workgroup -- every thread moves a few 16-byte vectors of it
-// into one of two LDS buffers -- and each wave reads its MFMA operands from
-// there, so a tile feeds PW * NGQ * 16 query columns.  The products are the
+// into LDS -- and each wave reads its MFMA operands from there, so a tile feeds
+// PW * NGQ * 16 query columns.  The products are the
 // decode kernel's (same operand layouts, same base-2 online softmax, same bf16
 // hi + lo split of P), with one softmax state and accumulator per group; each
 // column masks the tokens after its own position (causal).  Items are numbered
@@ -46,7 +46,7 @@ struct PrefillArgs {
   const int* query_start;     // [S + 1]
   const float* k_scale;       // fp8 pools: per-KV-head scales, else nullptr
   const float* v_scale;
-  int S, Hkv, T, max_blocks, num_blocks, groups;
+  int S, Hkv, T, max_blocks, num_blocks;
   float scale_log2e;
 };
 
@@ -57,9 +57,8 @@ struct PrefillArgs {
 // earlier, before every wave passed the previous barrier, and the loads of the
 // next pair are issued after the barrier and land while this pair is computed.
 // The stage count and every early exit depend only on the workgroup's item, so
-// all its waves reach every barrier.  Each wave
-// computes the tiles up to its own last position (V past it is zeroed) and skips
-// the rest.  Four waves of two groups each: 128 query columns per tile (measured
+// all its waves reach every barrier.  Each wave computes the tiles up to its
+// own last position (V past it is zeroed) and skips the rest.  Four waves of two groups each: 128 query columns per tile (measured
 // on 16 x (1,536 cached + 512 new) tokens against four waves of one group and
 // eight of one; a wave of two groups keeps two per SIMD at D = 128).
 constexpr int kPrefillSharedWaves = 4;
@@ -444,7 +443,6 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.T = T;
   a.max_blocks = max_blocks;
   a.num_blocks = num_blocks;
-  a.groups = (int)groups;
   a.scale_log2e = scale * 1.4426950408889634f;
   hipStream_t st = (hipStream_t)hip_stream;
   const unsigned grid = (unsigned)items;
