@@ -1,9 +1,12 @@
 """Planted mistakes: each plausible slip in the oracle must fail some pin.
 
 Every mutant below is a copy of an oracle function with one deliberate error
-(wrong GQA head map, transposed K block, dropped scale, one token short, LIFO
-free list, a CoW that forgets to release its source).  The pins are re-run
-against the mutant and at least one of them has to fail."""
+(wrong GQA head map, transposed K block, dropped scale, one token short, no
+max subtraction in the softmax, slots that ignore the range start or shift the
+offset, a valid-slot mask one slot too generous, LIFO free list, a CoW that
+forgets to release its source, and the swap, scheduler, prefill, prefix-cache,
+fp8 and truncate mutants further down).  The pins are re-run against the
+mutant and at least one of them has to fail."""
 import numpy as np
 import pytest
 
@@ -48,7 +51,22 @@ def _attention_pins():
     ta.test_paged_equals_contiguous_sdpa("bf16", 16, 4)
     ta.test_paged_equals_contiguous_sdpa("f32", 16, 1)
     ta.test_brute_force_scalar_loops()
+    ta.test_closed_forms()
     ta.test_gqa_head_map()
+
+
+def _attention_no_max(q, K, V, scale):
+    """softmax without subtracting the max score first (overflows on large scores)."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = np.exp((K @ q) * scale)
+        return (p @ V) / p.sum()
+
+
+def test_no_max_subtraction_fails_pins(monkeypatch):
+    monkeypatch.setattr(oa, "attention", _attention_no_max)
+    monkeypatch.setattr(ta, "attention", _attention_no_max)
+    with pytest.raises(AssertionError):
+        _attention_pins()
 
 
 @pytest.mark.parametrize("mutant", ["head_mod", "no_scale", "short"])
@@ -65,6 +83,57 @@ def test_transposed_gather_fails_pins(monkeypatch):
     monkeypatch.setattr(oa, "gather_kv", _gather_transposed)
     with pytest.raises(AssertionError):
         ta.test_paged_equals_contiguous_sdpa("bf16", 16, 4)
+
+
+# --- slot rule and valid-slot mask ------------------------------------------------
+import tests.test_oracle_slots as tslots
+
+
+def _slots_ignore_start(bm, sid, start, count):
+    bm._resident(sid)
+    t = bm.tables[sid]
+    return [t[i // bm.B] * bm.B + i % bm.B for i in range(count)]
+
+
+def _slots_offset_shift(bm, sid, start, count):
+    bm._resident(sid)
+    t = bm.tables[sid]
+    return [t[i // bm.B] * bm.B + (i + 1) % bm.B for i in range(start, start + count)]
+
+
+def _mask_one_extra(block_tables, context_lens, num_blocks, B):
+    mask = np.zeros((num_blocks, B), dtype=bool)
+    for table, L in zip(block_tables, context_lens):
+        n = sum(1 for b in table if b >= 0)
+        for t in range(min(int(L) + 1, n * B)):      # one slot past the end when there is room
+            mask[int(table[t // B]), t % B] = True
+    return mask
+
+
+def _slot_pins():
+    tslots.test_slots_on_block_pool_figure()
+    for seed in range(4):
+        tslots.test_slots_equal_append_history(seed)
+
+
+def _mask_pins():
+    tslots.test_valid_slot_mask_on_block_pool_figure()
+    for seed in range(4):
+        tslots.test_valid_slot_mask_counts_private_tokens(seed)
+
+
+@pytest.mark.parametrize("mutant", ["ignore_start", "offset_shift"])
+def test_slots_mutants_fail_pins(monkeypatch, mutant):
+    fn = {"ignore_start": _slots_ignore_start, "offset_shift": _slots_offset_shift}[mutant]
+    monkeypatch.setattr(tslots, "slots", fn)
+    with pytest.raises(AssertionError):
+        _slot_pins()
+
+
+def test_generous_mask_fails_pins(monkeypatch):
+    monkeypatch.setattr(tslots, "valid_slot_mask", _mask_one_extra)
+    with pytest.raises(AssertionError):
+        _mask_pins()
 
 
 class _LifoBM(obm.BlockManager):
