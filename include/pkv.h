@@ -461,7 +461,14 @@ pkv_status pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int
  *                 sequence whose rows fall outside [0, T) gets none written
  *   context_lens  device int32 [S]; Q_s is clamped to L_s (a sequence with
  *                 more rows than tokens gets only its last L_s rows written)
- *   max_query_len host bound on Q_s (sizes the grid)
+ *   max_query_len host bound on every Q_s (sizes the grid).  It is not checked
+ *                 against query_start, which stays on the device.  A
+ *                 sequence's rows are taken in runs of R = 128 / G rows
+ *                 counted from its first row, and a call covers the last
+ *                 ceil(max_query_len / R) runs of each sequence: when some Q_s
+ *                 exceeds the bound, the rows of that sequence's earlier runs
+ *                 are not written and no error is returned.  The Python
+ *                 binding checks the bound when given a host query_start.
  *   block_tables, max_blocks, num_blocks, Hq, Hkv, scale as for decode.
  *   k_scale, v_scale  fp8 pools: device fp32 [Hkv] per-KV-head scales (q stays
  *                 bf16); NULL otherwise

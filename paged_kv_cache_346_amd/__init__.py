@@ -609,7 +609,13 @@ def pkv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_le
     """Causal attention of each sequence's last Q_s tokens over the paged cache:
     q and out [T, Hq, D] packed by query_start (int32 [S+1]); Q_s =
     query_start[s+1] - query_start[s].  fp8 pools take bf16 q and the per-head
-    k_scale / v_scale (float32 [Hkv] device tensors)."""
+    k_scale / v_scale (float32 [Hkv] device tensors).
+
+    max_query_len bounds every Q_s and sizes the grid.  query_start may be a
+    host array (numpy or a CPU tensor): it is then checked against that bound
+    (ValueError when some Q_s exceeds it) and copied to the device.  A device
+    query_start is not read on the host; there an undersized bound leaves a
+    sequence's earliest rows unwritten."""
     N, Hkv, D, B = _pool_geometry(k_pool, v_pool)
     T, Hq = q.shape[0], q.shape[1]
     S = context_lens.shape[0]
@@ -617,6 +623,16 @@ def pkv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_le
         raise ValueError("q and out must be [T, Hq, D]")
     if out.dtype != torch.float32 or q.dtype != _row_dtype(k_pool):
         raise ValueError("out must be fp32 and q in the pool dtype (bf16 for fp8 pools)")
+    if not (isinstance(query_start, torch.Tensor) and query_start.is_cuda):
+        qs = query_start.numpy() if isinstance(query_start, torch.Tensor) else query_start
+        qs = np.ascontiguousarray(qs, dtype=np.int32)
+        if qs.shape != (S + 1,):
+            raise ValueError("query_start must be int32 [S + 1]")
+        longest = int(np.diff(qs).max()) if S > 0 else 0
+        if longest > int(max_query_len):
+            raise ValueError(f"max_query_len {int(max_query_len)} is below the longest "
+                             f"query run in query_start ({longest} rows)")
+        query_start = torch.from_numpy(qs).to(out.device)
     if query_start.dtype != torch.int32 or tuple(query_start.shape) != (S + 1,):
         raise ValueError("query_start must be int32 [S + 1]")
     if context_lens.dtype != torch.int32 or block_tables.dtype != torch.int32 or \

@@ -1,6 +1,8 @@
 """Shared set-up for the GPU parity tests: run a workload's request script
-through the product's block manager, poison every slot that holds no token with
-NaN, run the device path, and run the oracle on the same inputs."""
+through the product's block manager and through the oracle's, require the two
+to agree exactly (tables, lengths, slots, copy pairs), poison every slot that
+holds no token with NaN, run the device path on the product's bookkeeping, and
+run the oracle on its own."""
 from __future__ import annotations
 
 import sys
@@ -10,6 +12,7 @@ import torch
 
 import workloads as W
 from oracle.attention import paged_attention_decode as ref_decode, valid_slot_mask
+from oracle.block_manager import BlockManager as RefBM
 from oracle.cache_ops import copy_blocks as ref_copy, reshape_and_cache as ref_cache
 
 NAN_BF16 = np.uint16(0x7FC1)
@@ -40,24 +43,30 @@ def poison(k_pool, v_pool, tables, lens, B):
     v_pool[bi, :, :, oi] = nan
 
 
-class Case:
-    """A workload taken through the product block manager (host side only)."""
+def _run_script(bm, ops):
+    for op in ops:
+        if op[0] == "add":
+            bm.add_seq(op[1], op[2])
+        elif op[0] == "fork":
+            bm.fork(op[1], op[2])
+        elif op[0] == "extend":
+            for _ in range(op[2]):
+                bm.append_slot(op[1])
 
-    def __init__(self, pkv, w: W.Workload, poison_unused: bool = True):
-        self.w = w
+
+class Bookkeeping:
+    """A workload's request script and step appends, taken through the product's
+    block manager and through the oracle's.  The product's tables, lengths,
+    slots and copy pairs drive the device; the oracle's drive the oracle; the
+    two are asserted equal."""
+
+    def __init__(self, pkv, w: W.Workload):
         c = w.cfg
-        bm = pkv.BlockManager(w.num_blocks, c.B, w.free_order)
-        for op in w.ops:
-            if op[0] == "add":
-                bm.add_seq(op[1], op[2])
-            elif op[0] == "fork":
-                bm.fork(op[1], op[2])
-            elif op[0] == "extend":
-                for _ in range(op[2]):
-                    bm.append_slot(op[1])
         ids = list(range(c.S))
         self.max_blocks = max(1, max(-(-int(L) // c.B) for L in w.lengths))
-        pre_tables, pre_lens = bm.fill_batch(ids, self.max_blocks)
+        bm = pkv.BlockManager(w.num_blocks, c.B, w.free_order)
+        _run_script(bm, w.ops)
+        self.pre_tables, self.pre_lens = bm.fill_batch(ids, self.max_blocks)
         if w.step_ids:
             self.slots, self.pairs = bm.append_slots(w.step_ids)
         else:
@@ -65,11 +74,43 @@ class Case:
             self.pairs = np.zeros((0, 2), np.int32)
         self.tables, self.lens = bm.fill_batch(ids, self.max_blocks)
         assert self.lens.tolist() == w.lengths.tolist()
+        self.bm = bm
+
+        ref = RefBM(w.num_blocks, c.B, w.free_order)
+        _run_script(ref, w.ops)
+        pre_t, pre_l = ref.fill_batch(ids, self.max_blocks)
+        self.ref_pre_tables = np.asarray(pre_t, np.int32)
+        self.ref_pre_lens = np.asarray(pre_l, np.int32)
+        appends = [ref.append_slot(s) for s in w.step_ids]
+        self.ref_slots = np.asarray([a[0] for a in appends], np.int64)
+        self.ref_pairs = np.asarray([[a[1], a[2]] for a in appends if a[1] >= 0],
+                                    np.int32).reshape(-1, 2)
+        t, l = ref.fill_batch(ids, self.max_blocks)
+        self.ref_tables, self.ref_lens = np.asarray(t, np.int32), np.asarray(l, np.int32)
+        assert np.array_equal(self.pre_tables, self.ref_pre_tables)
+        assert np.array_equal(self.pre_lens, self.ref_pre_lens)
+        assert np.array_equal(self.slots, self.ref_slots)
+        assert np.array_equal(np.asarray(self.pairs).reshape(-1, 2), self.ref_pairs)
+        assert np.array_equal(self.tables, self.ref_tables)
+        assert np.array_equal(self.lens, self.ref_lens)
+
+
+class Case:
+    """A workload taken through both block managers (host side only)."""
+
+    def __init__(self, pkv, w: W.Workload, poison_unused: bool = True):
+        self.w = w
+        c = w.cfg
+        bk = Bookkeeping(pkv, w)
+        self.bk = bk
+        self.max_blocks = bk.max_blocks
+        self.slots, self.pairs = bk.slots, bk.pairs
+        self.tables, self.lens = bk.tables, bk.lens
         self.k_pool, self.v_pool = w.k_pool, w.v_pool
         if poison_unused:
             self.k_pool, self.v_pool = w.k_pool.copy(), w.v_pool.copy()
-            poison(self.k_pool, self.v_pool, pre_tables, pre_lens, c.B)
-        self.bm = bm
+            poison(self.k_pool, self.v_pool, bk.ref_pre_tables, bk.ref_pre_lens, c.B)
+        self.bm = bk.bm
 
     # -- device path -----------------------------------------------------------
     def run_device(self, pkv, partition_size=None, shared_kv=None, plan=False, append=False):
@@ -109,15 +150,17 @@ class Case:
 
     # -- oracle ----------------------------------------------------------------
     def oracle_pools(self):
+        """The oracle's step on the pools, from the oracle's own slots and pairs."""
         kp, vp = self.k_pool, self.v_pool
-        if len(self.pairs):
-            kp, vp = ref_copy(kp, vp, self.pairs)
-        if len(self.slots):
-            kp, vp = ref_cache(kp, vp, self.w.k_new, self.w.v_new, self.slots)
+        bk = self.bk
+        if len(bk.ref_pairs):
+            kp, vp = ref_copy(kp, vp, bk.ref_pairs)
+        if len(bk.ref_slots):
+            kp, vp = ref_cache(kp, vp, self.w.k_new, self.w.v_new, bk.ref_slots)
         return kp, vp
 
     def oracle_out(self, kp, vp, rows=None):
-        return ref_decode(self.w.q, kp, vp, self.tables, self.lens, rows=rows)
+        return ref_decode(self.w.q, kp, vp, self.bk.ref_tables, self.bk.ref_lens, rows=rows)
 
 
 def check_attention(got: np.ndarray, ref: np.ndarray, dtype: str, rows=None) -> float:

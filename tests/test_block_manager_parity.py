@@ -143,7 +143,7 @@ def test_host_pool_rules(pkv):
 
 
 @pytest.mark.parametrize("name", ["tiny_mha_f32", "opt13b_mha", "llama8b_gqa", "sampling_steady",
-                                  "sampling_fork"])
+                                  "sampling_fork", "long70b_b16", "long70b_b32"])
 def test_workload_scripts_bit_exact(pkv, name):
     w = W.make(name, pools=False)
     native = pkv.BlockManager(w.num_blocks, w.cfg.B, w.free_order)

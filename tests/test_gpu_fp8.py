@@ -15,7 +15,7 @@ from oracle.attention import paged_attention_decode as ref_decode
 from oracle.block_manager import BlockManager
 from oracle.cache_ops import reshape_and_cache as ref_cache
 from tests.conftest import gpu_available
-from tests.gpu_cases import check_attention, say, to_dev
+from tests.gpu_cases import Bookkeeping, check_attention, say, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -238,32 +238,22 @@ def test_fp8_subnormal_codes_decode_exactly(pkv, G):
 def test_fp8_full_config(pkv, name):
     """Full-size workloads over fp8 pools in the benchmark's launch configuration
     (host plan; the step's tokens encoded and written by the attention launch):
-    whole pools bit-exact against the reference fp8 cache write, sampled rows
-    (longest and shortest sequences included) within the bf16 bound of the fp64
-    reference over the dequantized pools.  Pools hold random finite codes, NaN
-    codes in every slot that holds no token."""
+    the oracle's block manager reproduces the product's tables and slots; whole
+    pools bit-exact against the reference fp8 cache write; every (sequence,
+    query head) row within the bf16 bound of the fp64 reference over the
+    dequantized pools.  Pools hold random finite codes, NaN codes in every slot
+    that holds no token."""
     import torch
     from oracle.attention import valid_slot_mask
     say(f"case fp8 {name} (full size)")
     w = W.make(name, pools=False)
     c = w.cfg
-    bm = pkv.BlockManager(w.num_blocks, c.B, w.free_order)
-    for op in w.ops:
-        if op[0] == "add":
-            bm.add_seq(op[1], op[2])
-        elif op[0] == "fork":
-            bm.fork(op[1], op[2])
-        elif op[0] == "extend":
-            for _ in range(op[2]):
-                bm.append_slot(op[1])
+    bk = Bookkeeping(pkv, w)
     ids = list(range(c.S))
-    max_blocks = max(1, max(-(-int(L) // c.B) for L in w.lengths))
-    pre_tables, pre_lens = bm.fill_batch(ids, max_blocks)
-    slots = np.zeros(0, np.int64)
-    if w.step_ids:
-        slots, pairs = bm.append_slots(w.step_ids)
-        assert len(pairs) == 0
-    tables, lens = bm.fill_batch(ids, max_blocks)
+    max_blocks = bk.max_blocks
+    assert len(bk.pairs) == 0
+    pre_tables, pre_lens = bk.ref_pre_tables, bk.ref_pre_lens
+    tables, lens = bk.tables, bk.lens
     rng = np.random.default_rng(2000 + c.seed)
     ks, vs = W.pool_shapes(w.num_blocks, c.Hkv, c.D, c.B, "fp8")
 
@@ -296,12 +286,9 @@ def test_fp8_full_config(pkv, name):
     torch.cuda.synchronize()
     say("  device done")
     if append:
-        kp, vp = ref_cache(kp, vp, w.k_new, w.v_new, slots, k_scale, v_scale)
+        kp, vp = ref_cache(kp, vp, w.k_new, w.v_new, bk.ref_slots, k_scale, v_scale)
     assert np.array_equal(dk.cpu().numpy(), kp)
     assert np.array_equal(dv.cpu().numpy(), vp)
-    pick = {int(np.argmax(lens)), int(np.argmin(lens))}
-    pick |= set(rng.choice(c.S, size=min(c.S, 10), replace=False).tolist())
-    rows = [(s, h) for s in sorted(pick) for h in (0, c.Hq // 2 + 1, c.Hq - 1)]
-    want = ref_decode(w.q, kp, vp, tables, lens, rows=rows, k_scale=k_scale, v_scale=v_scale)
-    worst = check_attention(out.cpu().numpy(), want, "bf16", rows)
-    say(f"  {len(rows)} rows, worst error {worst:.3e}")
+    want = ref_decode(w.q, kp, vp, bk.ref_tables, bk.ref_lens, k_scale=k_scale, v_scale=v_scale)
+    worst = check_attention(out.cpu().numpy(), want, "bf16")
+    say(f"  all {c.S * c.Hq} rows, worst error {worst:.3e}")
