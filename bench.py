@@ -22,9 +22,11 @@ Prints ONE JSON line.  `value` is KV-read GB/s over the whole step: the
 algorithmic KV bytes of the batch (valid tokens only, sum_s L_s * Hkv * D * 2 *
 sizeof(kv)) times K, divided by the wall time of the K timed steps.  The
 `roofline` object gives the main attention kernel's own rate (the same bytes
-over its average launch time from HIP events on its stream) against the HBM
-peak.  `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
-same batch.
+over its average launch time from HIP events on its stream, recorded around
+the launch of every 8th timed step) against the HBM peak.  `also` holds the
+same figures for the 70B-shaped long-context batch at both block sizes,
+measured in the same run (--no-extra skips them).  `cpu_baseline` times the
+fp64 CPU oracle's whole step on the same batch.
 
 Inputs are synthetic (seeded), shaped like the pages' workloads; see
 workloads/__init__.py for the recipe.
@@ -49,6 +51,8 @@ HOST_LINK_PEAK_GBS = 64.0      # PCIe 5.0 x16 host link, per direction, before p
 MAIN_KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_346_amd", "csrc", n)
                     for n in ("attention.hip", "device_common.h", "kv_tiles.h", "decode_config.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MERGE_IN_LAUNCH_MAX = 16       # partitions per sequence the main launch merges itself
+EVENT_EVERY = 8                # timed steps per main-kernel launch bracketed by events
 
 DESCRIPTIONS = {
     "tiny_mha_f32": "tiny MHA decode: 4 seqs, 4 heads, D 64, B 16, fp32, L {1,15,16,70}, "
@@ -184,8 +188,7 @@ class Batch:
         self.lens = torch.from_numpy(lens).to(dev)
         self.mcl = int(lens.max())
         self.P = c.partition_size if partition_size is None else partition_size
-        nbytes = pkv.attention_workspace_bytes(c.S, c.Hq, c.D, self.mcl, self.P)
-        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.ws = pkv.attention_workspace(c.S, c.Hq, c.D, self.mcl, self.P, device=dev)
         self.out = torch.empty((c.S, c.Hq, c.D), dtype=torch.float32, device=dev)
         self.kv_bytes = w.kv_bytes // 2 if self.fp8 else w.kv_bytes
         self.kv_elem_bytes = esize
@@ -240,17 +243,34 @@ class Batch:
         rec(4)
 
     def launches(self):
-        """Which of the four step kernels this batch launches."""
+        """Which of the four step kernels this batch launches (the reduce only
+        when some sequence has more partitions than the main launch merges
+        itself)."""
+        nparts = -(-self.mcl // (self.P or 512))
+        in_launch = nparts <= MERGE_IN_LAUNCH_MAX and self.cfg.S * self.cfg.Hkv <= 16384
         return (self.pairs is not None, self.slots is not None and not self.append, True,
-                self.mcl > (self.P or 512))
+                nparts > 1 and not in_launch)
+
+
+def cpu_share() -> int:
+    """Host cores this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(omp))) if omp.isdigit() and int(omp) > 0 else n
 
 
 def cpu_baseline(batch, torch, budget_s: float):
-    """fp64 oracle attention on a bounded sample of the batch's sequences (all
-    heads of each), single-threaded BLAS; returns the JSON object."""
+    """The fp64 oracle's whole decode step on the same batch -- the step's
+    token writes into the pools (oracle.cache_ops.reshape_and_cache), then
+    attention of every (sequence, query head) through the block tables
+    (oracle.attention.paged_attention_decode) -- repeated until about
+    `budget_s` seconds (at least once), with BLAS threads = the process's CPU
+    share; returns the JSON object."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle.attention import paged_attention_decode as oracle_decode
+    from oracle.cache_ops import reshape_and_cache as oracle_cache
 
     c = batch.cfg
 
@@ -263,34 +283,35 @@ def cpu_baseline(batch, torch, budget_s: float):
     scales = {}
     if batch.fp8:
         scales = {"k_scale": batch.k_scale.cpu().numpy(), "v_scale": batch.v_scale.cpu().numpy()}
-    order = np.random.default_rng(7).permutation(c.S)
-    done_bytes, done_seqs, elapsed = 0, 0, 0.0
-    per_tok = c.Hkv * c.D * 2 * batch.kv_elem_bytes
-    passes = 0
-    with threadpool_limits(limits=1):
-        while elapsed < budget_s and passes < 100:
-            for s in order:
-                s = int(s)
-                rows = [(s, h) for h in range(c.Hq)]
-                t0 = time.perf_counter()
-                oracle_decode(q, kp, vp, batch.tables_host, batch.lens_host, rows=rows, **scales)
-                elapsed += time.perf_counter() - t0
-                done_bytes += int(batch.lens_host[s]) * per_tok
-                done_seqs += 1
-                if elapsed >= budget_s:
-                    break
+    writes = batch.slots is not None
+    if writes:
+        slots = batch.slots.cpu().numpy()
+        k_new, v_new = host(batch.k_new), host(batch.v_new)
+    cores = cpu_share()
+    elapsed, passes = 0.0, 0
+    with threadpool_limits(limits=cores):
+        while passes == 0 or (elapsed < budget_s and passes < 50):
+            t0 = time.perf_counter()
+            kq, vq = kp, vp
+            if writes:
+                kq, vq = oracle_cache(kp, vp, k_new, v_new, slots, **scales)
+            oracle_decode(q, kq, vq, batch.tables_host, batch.lens_host, **scales)
+            elapsed += time.perf_counter() - t0
             passes += 1
+    kv = batch.kv_bytes * passes
     return {
-        "value": round(done_bytes / elapsed / 1e9, 4),
+        "value": round(kv / elapsed / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"fp64 oracle decode attention (gather through the block table + "
-                  f"softmax(qK^T*scale)V) of the same batch, {done_seqs} sequence rows "
-                  f"({c.S} per pass, all {c.Hq} heads each), {done_bytes / 1e6:.1f} MB of "
-                  f"KV, {elapsed:.1f} s; single BLAS thread; cache writes not included",
+        "sample": f"fp64 oracle decode step of the whole batch ({c.S} sequences, all {c.Hq} "
+                  f"query heads): " + (f"the step's {len(slots)} token writes into the pools, "
+                                       if writes else "") +
+                  f"then gather through the block table + softmax(qK^T*scale)V; {passes} "
+                  f"step(s), {kv / 1e6:.1f} MB of KV, {elapsed:.1f} s; BLAS threads = {cores}",
         "seconds": round(elapsed, 3),
-        "tokens_per_s": round(done_seqs / elapsed, 4),
+        "steps": passes,
+        "tokens_per_s": round(c.S * passes / elapsed, 4),
     }
 
 
@@ -699,6 +720,9 @@ def main() -> int:
     ap.add_argument("--no-plan", action="store_true",
                     help="launch without the host work plan (one wave per possible partition)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure only --config (by default the 70B-shaped batches at both "
+                         "block sizes are measured too and reported under 'also')")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--layers", type=int, default=0,
                     help="K/V pools the steps rotate through (0 = enough for 4 GiB)")
@@ -744,14 +768,49 @@ def main() -> int:
     import workloads as W
 
     name = args.config
+    rec = measure(args, torch, np, pkv, W, name, args.kv_dtype, primary=True)
+    if not args.no_extra:
+        # the other single-GPU configuration of the >= 70% target (the 70B-shaped
+        # long-context batch at both block sizes), measured in the same run
+        rec["also"] = {}
+        for other in ("long70b_b16", "long70b_b32"):
+            if other == name:
+                continue
+            r = measure(args, torch, np, pkv, W, other, args.kv_dtype, primary=False)
+            rec["also"][other] = {
+                "workload": r["config"]["workload"], "value": r["value"], "unit": "GB/s",
+                "frac_of_hbm_peak": r["frac_of_hbm_peak"], "ms_per_step": r["ms_per_step"],
+                "decode_tokens_per_s": r["decode_tokens_per_s"],
+                "main_kernel_GBps": r["roofline"]["achieved"],
+                "main_kernel_frac": r["roofline"]["frac"],
+                "main_kernel_us": r["roofline"]["launch_us"], "kernel_us": r["kernel_us"],
+                "kv_bytes_per_step": r["config"]["kv_bytes_per_step"],
+                "partition_size": r["config"]["partition_size"],
+                "merge": r["config"]["merge"]}
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        rec["cpu_baseline"] = cpu_baseline(rec.pop("_batch"), torch, args.cpu_seconds)
+    rec.pop("_batch", None)
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
+def measure(args, torch, np, pkv, W, name, kv_dtype, primary):
+    """Warm-up, the K timed steps and the per-kernel breakdown of one workload;
+    returns the JSON record (the primary workload's also carries its batch for
+    the CPU baseline)."""
     log(f"bench: building workload {name}")
-    batch = Batch(pkv, torch, W, name, args.partition_size, args.layers, not args.no_plan,
-                  not args.separate_cache_write, args.kv_dtype)
+    batch = Batch(pkv, torch, W, name, args.partition_size if primary else None, args.layers,
+                  not args.no_plan, not args.separate_cache_write, kv_dtype)
     c = batch.cfg
     log(f"bench: N={batch.w.num_blocks} blocks, KV {batch.kv_bytes / 1e6:.1f} MB, "
         f"{batch.n_pairs} CoW pairs, max L {batch.mcl}")
 
-    if args.copy_probe_mib > 0:
+    if primary and args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -765,18 +824,21 @@ def main() -> int:
         batch.step(pkv, i)
     torch.cuda.synchronize()
 
-    # contract timing: K steps back to back; two events bracket each main-kernel
-    # launch on the stream it runs on (torch's current stream, which the binding
-    # passes to the library)
-    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # contract timing: K steps back to back.  Two events bracket the main-kernel
+    # launch of every EVENT_EVERY-th step, on the stream it runs on (torch's
+    # current stream, which the binding passes to the library); a pair of event
+    # records costs the stream a few microseconds of dispatch gap, so they are
+    # not put around every step
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    mev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        batch.step(pkv, args.warmup + i, main_ev=mev[i])
+        batch.step(pkv, args.warmup + i, main_ev=mev.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log("bench: timed steps done")
-    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
+    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in mev.values()]))
 
     def avg_ms(evlist, i):
         return float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evlist]))
@@ -806,8 +868,10 @@ def main() -> int:
         "kernel": "pa_mfma_kernel" if (c.dtype == "bf16" and c.G >= 4) else "pa_valu_kernel",
         "traffic_key": traffic_key,
         "launch_us": round(k1_ms * 1e3, 2),
+        "launches_timed": len(mev),
         "algorithmic_bytes_per_launch": batch.kv_bytes,
     }
+    launches = batch.launches()
     cfg_obj = {
         "workload": f"{name}: {DESCRIPTIONS[name]}" + (
             "; KV pools in fp8 E4M3 with per-KV-head scales (finite codes below 4 in "
@@ -823,6 +887,8 @@ def main() -> int:
         "host_plan": batch.plan is not None,
         "cache_write": ("none" if batch.slots is None else
                         "in the attention launch" if batch.append else "reshape_and_cache"),
+        "merge": ("reduce launch" if launches[3] else
+                  "in the main launch" if batch.mcl > (batch.P or 512) else "none"),
         "work_items": None if batch.plan is None else batch.plan.n_items,
         "pool_bytes_per_layer": batch.pool_bytes,
     }
@@ -849,15 +915,13 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = cpu_baseline(batch, torch, args.cpu_seconds)
-    line = json.dumps(rec)
-    print(line, flush=True)
-    if args.json_out:
-        with open(args.json_out, "w") as f:
-            f.write(line + "\n")
-    return 0
+    if primary:
+        rec["_batch"] = batch
+    else:
+        del batch
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return rec
 
 
 if __name__ == "__main__":

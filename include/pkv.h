@@ -507,8 +507,13 @@ pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_blocks, const v
                            void* hip_stream);
 
 /* Bytes of workspace pkv_paged_attention_decode needs: 0 when every sequence
- * fits one partition, else S*Hq*nparts*(D+2)*4 with
- * nparts = ceil(max_context_len / partition) (partition_size 0 = default 512). */
+ * fits one partition, else 65536 + S*Hq*nparts*(D+2)*4 with
+ * nparts = ceil(max_context_len / partition) (partition_size 0 = default 512).
+ * The first 65536 bytes are 16384 int32 completion counters of the merge
+ * inside the main launch, one per (sequence, KV head): they must be zero
+ * before a workspace's first use (allocate it zeroed), and every call that
+ * completes leaves them zero, so one workspace serves any later call whose
+ * size it covers.  The rest holds the partition partials. */
 size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
                                      int32_t max_context_len, int32_t partition_size);
 
@@ -570,16 +575,24 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *   partition_size   tokens per work item: 0 = default (512), else a positive
  *                 multiple of 32 and of B spanning at most 64 blocks (<= 64*B
  *                 tokens).  Sequences longer than one partition are split and
- *                 merged by a log-sum-exp reduce launch.
+ *                 their partitions merged (log-sum-exp combine): inside the
+ *                 main launch, by the last of a (sequence, KV head)'s items to
+ *                 finish, when nparts <= 16 and S*Hkv <= 16384; else by a
+ *                 second, reduce launch.
  *   plan, plan_items, plan_merge   NULL, or a DEVICE copy of the plan that
  *                 pkv_attention_plan built for this batch (16-byte aligned) and
  *                 its two counts.  With a plan the main launch runs exactly the
  *                 listed items (taking each partition's length from the plan)
- *                 and the reduce merges exactly the listed rows; results are
+ *                 and a reduce launch merges exactly the listed rows; results are
  *                 bit-identical to the unplanned call.  A record naming a
  *                 sequence or head outside the batch is skipped.
  *   workspace     device buffer of workspace_bytes >= pkv_attention_workspace_bytes
- *                 (may be NULL when that is 0)
+ *                 (may be NULL when that is 0), its counters zero (see there).
+ *                 Calls that overlap in time must not share a workspace.
+ *                 With the merge inside the launch the plan must list every
+ *                 (sequence, KV head, partition) that holds tokens exactly
+ *                 once, as pkv_attention_plan's plans do: a missing item
+ *                 leaves its rows unwritten and its counter non-zero.
  *   flags         0 or PKV_ATTN_SHARED_KV (other bits: PKV_EINVAL)
  *   k_scale, v_scale  fp8 pools: device fp32 [Hkv] per-KV-head scales (the
  *                 values read are code * scale); NULL otherwise
@@ -602,15 +615,17 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, void* k_pool, v
 /* The two launches of pkv_paged_attention_decode, callable one at a time (for
  * per-kernel timing, or to put other work between them on the stream).
  * pkv_paged_attention_main takes exactly pkv_paged_attention_decode's arguments
- * and runs the main kernel: rows of sequences that fit one partition are final
- * in `out` when it completes; longer sequences leave per-partition
- * (max, sum, accumulator) partials in `workspace`.
- * pkv_paged_attention_reduce then merges those partials into `out` (log-sum-exp
- * combine of the partitions; the split itself is not on the pages, which only
- * note that long contexts are hard: [ZENO] "Limitations").  Its arguments must
- * repeat the values given to the main call (same S, Hq, Hkv, D, B, max_blocks,
+ * and runs the main kernel.  When it merges the partitions itself (see
+ * partition_size) every row is final in `out` when it completes.  Else rows of
+ * sequences that fit
+ * one partition are final and longer sequences leave per-partition
+ * (max, sum, accumulator) partials in `workspace`, which
+ * pkv_paged_attention_reduce then merges into `out` (log-sum-exp combine of the
+ * partitions; the split itself is not on the pages, which only note that long
+ * contexts are hard: [ZENO] "Limitations").  Its arguments must repeat the
+ * values given to the main call (same S, Hq, Hkv, D, B, max_blocks,
  * max_context_len, partition_size, plan, context_lens, workspace); it reads
- * nothing else and is a no-op when every sequence fits one partition. */
+ * nothing else and is a no-op when the main launch merged. */
 pkv_status pkv_paged_attention_main(float* out, const void* q, void* k_pool, void* v_pool,
                                     const void* new_key, const void* new_value,
                                     const int32_t* block_tables,

@@ -24,7 +24,8 @@ __all__ = [
     "pkv_paged_attention_reduce", "pool_shapes", "paged_attention_main", "paged_attention_reduce",
     "pkv_attention_plan", "pkv_attention_plan_words", "attention_plan", "attention_plan_words",
     "Plan", "make_plan", "StepPack",
-    "reshape_and_cache", "copy_blocks", "attention_workspace_bytes", "paged_attention_decode",
+    "reshape_and_cache", "copy_blocks", "attention_workspace_bytes", "attention_workspace",
+    "paged_attention_decode",
     "LIB_PATH", "lib",
 ]
 
@@ -654,6 +655,16 @@ def pkv_paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_le
 def pkv_attention_workspace_bytes(S: int, Hq: int, D: int, max_context_len: int,
                                   partition_size: int = 0) -> int:
     return int(lib.pkv_attention_workspace_bytes(S, Hq, D, max_context_len, partition_size))
+
+
+def attention_workspace(S: int, Hq: int, D: int, max_context_len: int, partition_size: int = 0,
+                        device="cuda") -> torch.Tensor:
+    """A zeroed uint8 device workspace of pkv_attention_workspace_bytes (at least
+    16 bytes).  Its first 64 KiB hold the in-launch merge's counters, which
+    must be zero before the first call; every call leaves them zero, so one
+    workspace serves any number of calls of at most this size."""
+    n = pkv_attention_workspace_bytes(S, Hq, D, max_context_len, partition_size)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
 
 
 class Plan:

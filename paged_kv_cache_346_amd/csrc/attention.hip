@@ -35,9 +35,12 @@
 //   * keeps an online-softmax state (running max m, running sum l, unnormalised
 //     accumulator).
 // An item that covers its whole sequence writes the output rows; otherwise it
-// writes its (m, l, acc) partial and pa_reduce_kernel merges the partitions
-// (log-sum-exp combine).  Scores are kept in base 2 (scale * log2 e folded in)
-// so exp is one v_exp_f32.
+// writes its (m, l, acc) partial and the partitions are merged (log-sum-exp
+// combine): by the item of the (sequence, KV head) that finishes last, inside
+// the same launch, when no sequence has more than kMergeInLaunchMax partitions
+// (and the batch fits the workspace's counters), else by pa_reduce_kernel in a
+// second launch.  Scores are kept in
+// base 2 (scale * log2 e folded in) so exp is one v_exp_f32.
 //
 // Two main kernels:
 //   pa_valu_kernel  fp32 pools, and bf16 with G < 4.  Tile = one KV block.  Lanes
@@ -68,12 +71,19 @@ namespace pkv {
 // One wave per workgroup: the dispatcher then balances the ragged items wave by
 // wave (measured faster than four-item workgroups on ragged batches).
 constexpr int kWavesPerGroup = 1;           // items per workgroup
+// Partitions per sequence up to which the main launch merges them itself; a
+// longer split is merged by the reduce launch, whose many threads per row
+// finish it sooner than one wave would.  Also the reduce launch merges when the
+// batch has more (sequence, KV head) pairs than the workspace has counters.
+constexpr int kMergeInLaunchMax = 16;
 static_assert(kMaxPartitionBlocks == kWave, "one table entry per lane");
 
 struct DecodeArgs {
   float* out;
   float* part_acc;   // [S, Hq, nparts, D]
   float* part_ml;    // [S, Hq, nparts, 2]
+  int* counters;     // [S * Hkv] arrivals per (sequence, KV head) for the merge
+                     // inside the launch, or nullptr (the reduce launch merges)
   const int* block_tables;
   const int* context_lens;
   const void* new_k;  // [S, Hkv, D]: each sequence's token of this step, or nullptr
@@ -236,6 +246,129 @@ __device__ __forceinline__ bool store_item(const DecodeArgs& a, E* k_pool, E* v_
   const int s = item - a.items;
   if (s < a.store_items) store_new_token<E, D, B>(a, s, k_pool, v_pool);
   return true;
+}
+
+// ---------------------------------------------------------------------------
+// Partition merge inside the main launch.  A split item writes its partial
+// rows with device-scope stores (sc1: written through to the point where every
+// XCD sees them), waits until they are acknowledged, then counts itself on its
+// (sequence, KV head)'s counter with a device-scope atomic.  The item that
+// finds every other one counted merges all partials, read back with
+// device-scope loads, and resets the counter for the next launch.  Nothing
+// waits on another wave, and no fence is needed: the partials never go
+// through an XCD's L2 as ordinary (write-back) data, so there is nothing for a
+// release to write back or for an acquire to invalidate (an agent-scope
+// release or acquire on gfx950 is exactly the L2 write-back or invalidate plus
+// the counter wait used here).
+// ---------------------------------------------------------------------------
+constexpr int kSc1 = 16;                        // cache-policy bit: device scope
+constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit buffer, gfx9 layout
+constexpr int kWaitVm0 = 0x0F70;                // s_waitcnt vmcnt(0)
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+
+// A buffer resource over `bytes` bytes at `base` (wave-uniform).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// The partial rows of (sequence s, KV head g): acc [G, nparts, D] and
+// (m, l) [G, nparts, 2], contiguous for the G query heads of the KV head.
+template <int D, int G>
+struct PartialRows {
+  __amdgpu_buffer_rsrc_t acc, ml;
+  int nparts;
+  __device__ __forceinline__ PartialRows(const DecodeArgs& a, int s, int g) {
+    const size_t row0 = ((size_t)s * a.Hkv + g) * G * a.nparts;
+    acc = raw_rsrc(a.part_acc + row0 * D, (uint32_t)(G * a.nparts * D * 4));
+    ml = raw_rsrc(a.part_ml + row0 * 2, (uint32_t)(G * a.nparts * 8));
+    nparts = a.nparts;
+  }
+  // byte offsets of row (gi, p): its acc element e, its (m, l) pair
+  __device__ __forceinline__ int acc_off(int gi, int p, int e) const {
+    return ((gi * nparts + p) * D + e) * 4;
+  }
+  __device__ __forceinline__ int ml_off(int gi, int p) const { return (gi * nparts + p) * 8; }
+  __device__ __forceinline__ void store4(const f32x4& v, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), acc, off, 0, kSc1);
+  }
+  __device__ __forceinline__ void store1(float v, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), acc, off, 0, kSc1);
+  }
+  __device__ __forceinline__ void store_ml(float m, float l, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2v{__float_as_uint(m), __float_as_uint(l)}, ml,
+                                          off, 0, kSc1);
+  }
+  __device__ __forceinline__ f32x4 load4(int off) const {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(acc, off, 0, kSc1));
+  }
+  __device__ __forceinline__ u32x2v load_ml(int off) const {
+    return __builtin_amdgcn_raw_buffer_load_b64(ml, off, 0, kSc1);
+  }
+};
+
+// After this wave's partial stores: true for the (sequence, KV head)'s last
+// item to finish, which then owns the merge (its counter is reset to zero).
+__device__ __forceinline__ bool arrive_last(const DecodeArgs& a, int s, int g, int nps) {
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's partial stores are acknowledged
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int* cnt = a.counters + (size_t)s * a.Hkv + g;
+  int old = 0;
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0, kWave);
+  if (old != nps - 1) return false;
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// The merge by the last item: output rows of the G query heads of (s, g) from
+// their nps partials.  Each lane takes float4 columns of the G x D block and
+// folds the partitions U at a time (indices past the end re-read the last one
+// with weight 0), as pa_reduce_kernel does for a row.
+template <int D, int G>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int g, int nps) {
+  constexpr int C4 = D / 4;
+  constexpr int NCOL = G * C4;
+  constexpr int PER = (NCOL + kWave - 1) / kWave;
+  constexpr int U = 4;
+  const PartialRows<D, G> pr(a, s, g);
+  const int lane = threadIdx.x & (kWave - 1);
+  const size_t out0 = ((size_t)s * a.Hkv + g) * G * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int col = lane + kWave * i;
+    if (NCOL % kWave != 0 && col >= NCOL) break;
+    const int gi = col / C4, c4 = col - gi * C4;
+    float M = -INFINITY, den = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < nps; p0 += U) {
+      float mi[U], li[U];
+      f32x4 ai[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = min(p0 + u, nps - 1);
+        const u32x2v w = pr.load_ml(pr.ml_off(gi, p));
+        mi[u] = p0 + u < nps ? __uint_as_float(w[0]) : -INFINITY;
+        li[u] = __uint_as_float(w[1]);
+        ai[u] = pr.load4(pr.acc_off(gi, p, 4 * c4));
+      }
+      float mn = M;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mn = fmaxf(mn, mi[u]);
+      const float fo = fast_exp2(M - mn);  // M = -inf gives 0
+      den *= fo;
+      acc *= fo;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float f = fast_exp2(mi[u] - mn);  // past the end: 0
+        den = fmaf(f, li[u], den);
+        acc += f * ai[u];
+      }
+      M = mn;
+    }
+    *reinterpret_cast<f32x4*>(a.out + out0 + (size_t)gi * D + 4 * c4) = acc * (1.f / den);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -449,6 +582,20 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(
     pipelined<Tile>(n, load, compute);
   }
 
+  if (it.nps > 1 && a.counters) {
+    // partial rows at device scope, then the merge by the last item
+    const PartialRows<D, G> pr(a, it.s, it.g);
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const float l = wave_sum(ls[gi]);
+#pragma unroll
+      for (int k = 0; k < ND; ++k)
+        pr.store1(acc[gi][k] * out_scale, pr.acc_off(gi, it.p, lane + kWave * k));
+      if (lane == 0) pr.store_ml(m[gi], l, pr.ml_off(gi, it.p));
+    }
+    if (arrive_last(a, it.s, it.g, it.nps)) merge_partials<D, G>(a, it.s, it.g, it.nps);
+    return;
+  }
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     const float l = wave_sum(ls[gi]);
@@ -904,6 +1051,18 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
 
   ls += shfl_xor_f(ls, 16);
   ls += shfl_xor_f(ls, 32);
+  if (it.nps > 1 && a.counters) {
+    // partial rows at device scope, then the merge by the last item
+    const PartialRows<D, G> pr(a, it.s, it.g);
+    if (r < G) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        pr.store4(acc[dt] * out_scale, pr.acc_off(r, it.p, 16 * dt + 4 * c));
+      if (c == 0) pr.store_ml(m, ls, pr.ml_off(r, it.p));
+    }
+    if (arrive_last(a, it.s, it.g, it.nps)) merge_partials<D, G>(a, it.s, it.g, it.nps);
+    return;
+  }
   if (r < G) {
     const RowSink dst = row_sink<D, G>(a, it, r);
     const float scl = (dst.ml ? 1.f : 1.f / ls) * out_scale;
@@ -1097,6 +1256,21 @@ static int64_t num_partitions(int64_t max_context_len, int P) {
   return max_context_len <= 0 ? 1 : (max_context_len + P - 1) / P;
 }
 
+// Workspace of a split launch: kMergeCounters int32 merge counters, one per
+// (sequence, KV head), at a fixed place whatever the batch, so a workspace can
+// serve calls of any size without a counter ever landing on bytes another call
+// used for partials; then the partials acc [S, Hq, nparts, D] and (m, l)
+// [S, Hq, nparts, 2].
+constexpr int64_t kMergeCounters = 16384;
+constexpr size_t kCounterBytes = kMergeCounters * 4;
+static size_t split_workspace_bytes(int64_t S, int64_t Hq, int64_t D, int64_t nparts) {
+  return kCounterBytes + (size_t)S * Hq * nparts * (D + 2) * sizeof(float);
+}
+// The main launch merges the partitions itself (else the reduce launch does).
+static bool merge_in_launch(int64_t S, int64_t Hkv, int64_t nparts) {
+  return nparts <= kMergeInLaunchMax && S * Hkv <= kMergeCounters;
+}
+
 // The optional host-built plan: n_items records of 4 int32, then n_merge rows.
 struct PlanArg {
   const int32_t* ptr;
@@ -1164,9 +1338,10 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   a->P = P;
   a->scale_log2e = scale * 1.4426950408889634f;
   if (nparts > 1) {
-    const size_t need = (size_t)S * Hq * nparts * (D + 2) * sizeof(float);
-    if (!aligned16(workspace) || workspace_bytes < need) return PKV_EINVAL;
-    a->part_acc = (float*)workspace;
+    if (!aligned16(workspace) || workspace_bytes < split_workspace_bytes(S, Hq, D, nparts))
+      return PKV_EINVAL;
+    a->counters = merge_in_launch(S, Hkv, nparts) ? (int*)workspace : nullptr;
+    a->part_acc = (float*)((char*)workspace + kCounterBytes);
     a->part_ml = a->part_acc + (size_t)S * Hq * nparts * D;
   }
   // attention items, then (appending) one store item per sequence
@@ -1190,7 +1365,7 @@ static pkv_status launch_main_kernel(const DecodeArgs& a, int64_t groups, const 
 // The merge launch: every row of the batch, or only the plan's merge rows.
 static pkv_status launch_reduce_kernel(const DecodeArgs& a, const PlanArg& plan, int S, int Hq,
                                        int G, int D, int B, hipStream_t st) {
-  if (a.nparts <= 1) return PKV_OK;
+  if (a.counters) return PKV_OK;  // merged by the main launch
   const int* rows = plan.ptr ? plan.ptr + 4 * (size_t)plan.n_items : nullptr;
   const int64_t grid = plan.ptr ? (int64_t)plan.n_merge * G : (int64_t)S * Hq;
   if (grid == 0) return PKV_OK;
@@ -1219,7 +1394,7 @@ extern "C" size_t pkv_attention_workspace_bytes(int32_t S, int32_t Hq, int32_t D
   const int P = partition_size > 0 ? partition_size : kDefaultPartition;
   const int64_t np = num_partitions(max_context_len, P);
   if (np <= 1) return 0;
-  return (size_t)S * Hq * np * (D + 2) * sizeof(float);
+  return split_workspace_bytes(S, Hq, D, np);
 }
 
 extern "C" pkv_status pkv_paged_attention_decode(
@@ -1281,16 +1456,16 @@ extern "C" pkv_status pkv_paged_attention_reduce(
   const int64_t mcl = std::min<int64_t>(max_context_len, (int64_t)max_blocks * B);
   const int64_t nparts = num_partitions(mcl, P);
   if ((int64_t)S * Hq > 0x7fffffffLL) return PKV_EINVAL;
-  if (nparts <= 1) return PKV_OK;
-  const size_t need = (size_t)S * Hq * nparts * (D + 2) * sizeof(float);
-  if (!aligned16(workspace) || workspace_bytes < need) return PKV_EINVAL;
+  if (merge_in_launch(S, Hkv, nparts)) return PKV_OK;  // merged by the main launch
+  if (!aligned16(workspace) || workspace_bytes < split_workspace_bytes(S, Hq, D, nparts))
+    return PKV_EINVAL;
   DecodeArgs a{};
   a.out = out;
   a.context_lens = context_lens;
   a.max_blocks = max_blocks;
   a.nparts = (int)nparts;
   a.P = P;
-  a.part_acc = (float*)workspace;
+  a.part_acc = (float*)((const char*)workspace + kCounterBytes);
   a.part_ml = a.part_acc + (size_t)S * Hq * nparts * D;
   return launch_reduce_kernel(a, pl, S, Hq, Hq / Hkv, D, B, (hipStream_t)hip_stream);
 }

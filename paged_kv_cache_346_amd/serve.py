@@ -42,7 +42,7 @@ import math
 import numpy as np
 import torch
 
-from . import (BlockManager, Plan, Scheduler, StepPack, attention_workspace_bytes, copy_blocks,
+from . import (BlockManager, Plan, Scheduler, StepPack, attention_workspace, copy_blocks,
                paged_attention_decode, paged_attention_prefill, pool_shapes, reshape_and_cache,
                swap_blocks)
 
@@ -75,9 +75,8 @@ class DecodeLoop:
             hks, hvs = pool_shapes(host_blocks, kv_heads, head_dim, block_size, dtype)
             self.host_k = torch.empty(hks, dtype=dtype, pin_memory=True)
             self.host_v = torch.empty(hvs, dtype=dtype, pin_memory=True)
-        nbytes = attention_workspace_bytes(max_running, q_heads, head_dim, max_len,
-                                           partition_size)
-        self.ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        self.ws = attention_workspace(max_running, q_heads, head_dim, max_len, partition_size,
+                                      device=self.device)
         self.out = torch.empty((max_running, q_heads, head_dim), dtype=torch.float32,
                                device=self.device)
         self._host = [None, None]      # pinned int32 staging buffers, used alternately

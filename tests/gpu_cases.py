@@ -134,8 +134,7 @@ class Case:
         q = to_dev(self.w.q)
         out = torch.full((c.S, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
         mcl = int(self.lens.max())
-        nbytes = pkv.attention_workspace_bytes(c.S, c.Hq, c.D, mcl, P)
-        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        ws = pkv.attention_workspace(c.S, c.Hq, c.D, mcl, P)
         if shared_kv is None:
             shared_kv = self.bm.count_shared(range(c.S)) > 0
         pl = None

@@ -142,10 +142,12 @@ def test_prefill_validation(pkv):
 
 
 def test_workspace_size_formula(pkv):
+    """16384 int32 merge counters, then the partials (D + 2 floats per query
+    head and partition)."""
     f = pkv.pkv_attention_workspace_bytes
     assert f(256, 32, 128, 512, 0) == 0                 # one partition: no workspace
-    assert f(16, 64, 128, 32768, 512) == 16 * 64 * 64 * 130 * 4
-    assert f(4, 8, 64, 513, 512) == 4 * 8 * 2 * 66 * 4
+    assert f(16, 64, 128, 32768, 512) == 65536 + 16 * 64 * 64 * 130 * 4
+    assert f(4, 8, 64, 513, 512) == 65536 + 4 * 8 * 2 * 66 * 4
     assert f(0, 8, 64, 5000, 0) == 0
 
 

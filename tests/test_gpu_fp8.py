@@ -114,8 +114,7 @@ def test_fp8_attention_matches_reference(pkv, G, D, B, P, plan, shared):
     q = W.normal(rng, (S, Hkv * G, D), "bf16")
     mcl = int(clens.max())
     out = torch.full((S, Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(pkv.attention_workspace_bytes(S, Hkv * G, D, mcl, P), 16),
-                     dtype=torch.uint8, device="cuda")
+    ws = pkv.attention_workspace(S, Hkv * G, D, mcl, P, device="cuda")
     pl = pkv.make_plan(clens, Hkv, B, tables.shape[1], mcl, P) if plan else None
     pkv.paged_attention_decode(out, to_dev(q), _u8(kp), _u8(vp), torch.from_numpy(tables).cuda(),
                                torch.from_numpy(clens).cuda(), mcl, partition_size=P,
@@ -182,8 +181,7 @@ def test_fp8_append_in_the_attention_launch(pkv, G, D, B, P, plan):
     mcl = int(clens.max())
     dk, dv = _u8(kp), _u8(vp)
     out = torch.full((S, Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(pkv.attention_workspace_bytes(S, Hkv * G, D, mcl, P), 16),
-                     dtype=torch.uint8, device="cuda")
+    ws = pkv.attention_workspace(S, Hkv * G, D, mcl, P, device="cuda")
     pl = pkv.make_plan(clens, Hkv, B, tables.shape[1], mcl, P) if plan else None
     pkv.paged_attention_decode(out, to_dev(q), dk, dv, torch.from_numpy(tables).cuda(),
                                torch.from_numpy(clens).cuda(), mcl, partition_size=P,
@@ -222,8 +220,7 @@ def test_fp8_subnormal_codes_decode_exactly(pkv, G):
     q = W.normal(rng, (S, Hkv * G, D), "bf16")
     mcl = int(clens.max())
     out = torch.full((S, Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(pkv.attention_workspace_bytes(S, Hkv * G, D, mcl, P), 16),
-                     dtype=torch.uint8, device="cuda")
+    ws = pkv.attention_workspace(S, Hkv * G, D, mcl, P, device="cuda")
     pkv.paged_attention_decode(out, to_dev(q), _u8(kp), _u8(vp), torch.from_numpy(tables).cuda(),
                                torch.from_numpy(clens).cuda(), mcl, partition_size=P,
                                workspace=ws, k_scale=torch.from_numpy(k_scale).cuda(),
@@ -273,8 +270,7 @@ def test_fp8_full_config(pkv, name):
     P = c.partition_size
     dk, dv = _u8(kp), _u8(vp)
     out = torch.full((c.S, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(pkv.attention_workspace_bytes(c.S, c.Hq, c.D, mcl, P), 16),
-                     dtype=torch.uint8, device="cuda")
+    ws = pkv.attention_workspace(c.S, c.Hq, c.D, mcl, P, device="cuda")
     pl = pkv.make_plan(lens, c.Hkv, c.B, max_blocks, mcl, P)
     pkv.paged_attention_decode(out, to_dev(w.q), dk, dv, torch.from_numpy(tables).cuda(),
                                torch.from_numpy(lens).cuda(), mcl, partition_size=P,

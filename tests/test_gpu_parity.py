@@ -180,6 +180,49 @@ def test_full_config(pkv, name):
         assert len(case.pairs) == 224
 
 
+@pytest.mark.parametrize("dtype,G,B,plan", [("bf16", 4, 16, True), ("bf16", 8, 32, False),
+                                            ("bf16", 1, 16, True), ("f32", 2, 16, False)])
+def test_merge_in_launch_over_many_launches(pkv, dtype, G, B, plan):
+    """Split sequences merged inside the main launch (at most 16 partitions of
+    64 tokens here): 12 launches on one workspace, alternating two batches of
+    different lengths; before every launch the partials region is filled with
+    NaN (so a merge that read a partial its writer had not yet made visible, or
+    a stale copy in a cache, would put NaN in the output).  Every launch
+    matches the oracle on every row, and the merge counters are zero after
+    each."""
+    import torch
+    Hkv, D, P = 2, 128, 64
+    batches = []
+    for k, lens in enumerate(((1, 64, 65, 200, 1024, 333, 960, 7),
+                              (1000, 129, 1, 640, 64, 800, 2, 1023, 450))):
+        cfg = ragged(f"merge_{dtype}_G{G}_B{B}_{k}", 1200 + 10 * k + G + B, lens, Hkv * G,
+                     Hkv, D, B, dtype, P, kind="decode")
+        case = Case(pkv, W.make(cfg))
+        ref = case.oracle_out(case.k_pool, case.v_pool)
+        batches.append((case, ref, max(lens)))
+    S_max = max(len(b[0].lens) for b in batches)
+    ws = pkv.attention_workspace(S_max, Hkv * G, D, 1024, P)
+    cbytes = 65536                                     # the merge counters
+    say(f"case merge_{dtype}_G{G}_B{B} plan={plan}")
+    worst = 0.0
+    for it in range(12):
+        case, ref, mcl = batches[it % 2]
+        c = case.w.cfg
+        assert -(-mcl // P) <= 16
+        ws[cbytes:].fill_(0xFF)
+        kp, vp = to_dev(case.k_pool), to_dev(case.v_pool)
+        out = torch.full((c.S, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
+        pl = pkv.make_plan(case.lens, c.Hkv, c.B, case.max_blocks, mcl, P) if plan else None
+        pkv.paged_attention_decode(out, to_dev(case.w.q), kp, vp,
+                                   torch.from_numpy(case.tables).cuda(),
+                                   torch.from_numpy(case.lens).cuda(), mcl, partition_size=P,
+                                   workspace=ws, plan=pl)
+        torch.cuda.synchronize()
+        assert int(ws[:cbytes].count_nonzero()) == 0, it
+        worst = max(worst, check_attention(out.cpu().numpy(), ref, dtype))
+    say(f"  12 launches, worst error {worst:.3e}")
+
+
 @pytest.mark.parametrize("dtype,G,D", [("bf16", 4, 128), ("bf16", 1, 64), ("f32", 2, 128),
                                        ("bf16", 8, 64)])
 def test_reduce_more_partitions_than_one_round(pkv, dtype, G, D):
@@ -215,8 +258,7 @@ def test_context_beyond_table_row_is_clamped(pkv):
                      np.minimum(np.asarray(lens, np.int32), cap_blocks * 16))
     for plan in (False, True):
         out = torch.full((3, 8, 128), float("nan"), dtype=torch.float32, device="cuda")
-        ws = torch.empty(pkv.attention_workspace_bytes(3, 8, 128, 1024, 512), dtype=torch.uint8,
-                         device="cuda")
+        ws = pkv.attention_workspace(3, 8, 128, 1024, 512, device="cuda")
         pl = pkv.make_plan(np.asarray(lens, np.int32), 2, 16, cap_blocks, 1024, 512) if plan \
             else None
         pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(tables).cuda(), lens_dev,
@@ -248,8 +290,7 @@ def test_append_only_where_the_launch_covers_the_last_position(pkv, plan):
         tables = np.ascontiguousarray(case.tables[:, :width])
         kp, vp = to_dev(case.k_pool), to_dev(case.v_pool)
         out = torch.empty((3, 8, 128), dtype=torch.float32, device="cuda")
-        ws = torch.empty(max(pkv.attention_workspace_bytes(3, 8, 128, mcl, 256), 16),
-                         dtype=torch.uint8, device="cuda")
+        ws = pkv.attention_workspace(3, 8, 128, mcl, 256, device="cuda")
         pl = pkv.make_plan(np.asarray(lens, np.int32), 2, 16, width, mcl, 256) if plan else None
         pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(tables).cuda(), lens_dev, mcl,
                                    partition_size=256, workspace=ws, plan=pl,

@@ -88,8 +88,7 @@ def test_speculative_steps(pkv, B, G):
     q = W.normal(rng, (S, Hq, D), "bf16")
     out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
     mcl = int(clens.max())
-    ws = torch.empty(max(pkv.attention_workspace_bytes(S, Hq, D, mcl, 64), 16),
-                     dtype=torch.uint8, device="cuda")
+    ws = pkv.attention_workspace(S, Hq, D, mcl, 64, device="cuda")
     pkv.paged_attention_decode(out, to_dev(q), dk, dv, torch.from_numpy(tables).cuda(),
                                torch.from_numpy(clens).cuda(), mcl, partition_size=64,
                                workspace=ws, new_key=to_dev(kn), new_value=to_dev(vn))
