@@ -55,7 +55,8 @@ typedef enum pkv_status {
   PKV_ENOSEQ = -3,        /* unknown sequence id */
   PKV_EEXIST = -4,        /* sequence id already in use */
   PKV_EUNSUPPORTED = -5,  /* shape or dtype without a compiled kernel */
-  PKV_EHIP = -6           /* a HIP runtime call or kernel launch failed */
+  PKV_EHIP = -6,          /* a HIP runtime call or kernel launch failed */
+  PKV_ENOSCRATCH = -7     /* the call needs more than the library's static scratch */
 } pkv_status;
 
 /* Pool element type.  PKV_FP8_E4M3: an fp8 KV cache ([ZENO] "Impact and
@@ -644,6 +645,37 @@ pkv_status pkv_paged_attention_reduce(float* out, const int32_t* context_lens, i
                                       int32_t plan_items, int32_t plan_merge,
                                       const void* workspace, size_t workspace_bytes,
                                       void* hip_stream);
+
+/* pkv_paged_attention_decode for callers that cannot allocate device memory
+ * or bring a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments and results as
+ * pkv_paged_attention_decode without workspace/workspace_bytes: the partition
+ * partials and merge counters live in a 64 MiB array that the library holds
+ * in each GPU's memory from its first call on that GPU until the process ends
+ * (PKV_SCRATCH_BYTES).  The call allocates nothing; it launches a small kernel
+ * that zeroes the merge counters, then the decode launches.
+ *   - The stream's device must be the calling thread's current device
+ *     (PKV_EINVAL otherwise).
+ *   - A call whose pkv_attention_workspace_bytes(S, Hq, D, max_context_len,
+ *     partition_size) exceeds PKV_SCRATCH_BYTES returns PKV_ENOSCRATCH before
+ *     any launch.
+ *   - Every call on a GPU shares that GPU's array and leaves its contents
+ *     there: calls that overlap in time on one GPU (several streams, several
+ *     threads) race and give wrong results; serialize them. */
+#define PKV_SCRATCH_BYTES (64u << 20)
+pkv_status pkv_paged_attention_decode_noalloc(float* out, const void* q, void* k_pool,
+                                              void* v_pool, const void* new_key,
+                                              const void* new_value,
+                                              const int32_t* block_tables,
+                                              const int32_t* context_lens, int32_t S,
+                                              int32_t Hq, int32_t Hkv, int32_t D, int32_t B,
+                                              int32_t max_blocks, int32_t num_blocks,
+                                              int32_t max_context_len, float scale,
+                                              int32_t partition_size, const int32_t* plan,
+                                              int32_t plan_items, int32_t plan_merge,
+                                              pkv_dtype dtype, uint32_t flags,
+                                              const float* k_scale, const float* v_scale,
+                                              void* hip_stream);
 
 #ifdef __cplusplus
 }

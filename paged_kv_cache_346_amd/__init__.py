@@ -25,7 +25,8 @@ __all__ = [
     "pkv_attention_plan", "pkv_attention_plan_words", "attention_plan", "attention_plan_words",
     "Plan", "make_plan", "StepPack",
     "reshape_and_cache", "copy_blocks", "attention_workspace_bytes", "attention_workspace",
-    "paged_attention_decode",
+    "paged_attention_decode", "pkv_paged_attention_decode_noalloc",
+    "paged_attention_decode_noalloc", "PKV_ENOSCRATCH", "PKV_SCRATCH_BYTES",
     "LIB_PATH", "lib",
 ]
 
@@ -33,6 +34,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOBLOCKS, PKV_ENOSEQ, PKV_EEXIST, PKV_EUNSUPPORTED, PKV_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
+PKV_ENOSCRATCH = -7
+PKV_SCRATCH_BYTES = 64 << 20
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_ATTN_SHARED_KV = 1
 PKV_SCHED_RESERVE_MAX, PKV_SCHED_SWAP = 1, 2
@@ -141,6 +144,10 @@ SIGNATURES = {
                                         _i32, _vp, _sz, _i32, _u32, _vp, _vp, _vp]),
     "pkv_paged_attention_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _vp, _i32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                  _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                                  _i32, _vp, _i32, _i32, _i32, _u32, _vp, _vp,
+                                                  _vp]),
 }
 
 
@@ -788,6 +795,24 @@ def pkv_paged_attention_main(out, q, k_pool, v_pool, block_tables, context_lens,
     _check(lib.pkv_paged_attention_main(*args, _stream(stream)), "pkv_paged_attention_main")
 
 
+def pkv_paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens,
+                                       max_context_len: int, scale: float | None = None,
+                                       partition_size: int = 0, stream=None,
+                                       shared_kv: bool = False, plan: Plan | None = None,
+                                       new_key=None, new_value=None, k_scale=None,
+                                       v_scale=None) -> None:
+    """pkv_paged_attention_decode without a workspace: the library's static
+    per-GPU scratch holds the partials (PKV_ENOSCRATCH when the call needs more
+    than PKV_SCRATCH_BYTES).  Calls that overlap in time on one GPU race."""
+    args = _attention_args(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                           scale, partition_size, plan, None, shared_kv, new_key, new_value,
+                           k_scale, v_scale)
+    # the same arguments without workspace and workspace_bytes
+    args = args[:21] + args[23:]
+    _check(lib.pkv_paged_attention_decode_noalloc(*args, _stream(stream)),
+           "pkv_paged_attention_decode_noalloc")
+
+
 def pkv_paged_attention_reduce(out, context_lens, Hkv: int, B: int, max_blocks: int,
                                max_context_len: int, partition_size: int = 0, workspace=None,
                                stream=None, plan: Plan | None = None) -> None:
@@ -817,5 +842,6 @@ attention_workspace_bytes = pkv_attention_workspace_bytes
 paged_attention_decode = pkv_paged_attention_decode
 paged_attention_main = pkv_paged_attention_main
 paged_attention_reduce = pkv_paged_attention_reduce
+paged_attention_decode_noalloc = pkv_paged_attention_decode_noalloc
 attention_plan = pkv_attention_plan
 attention_plan_words = pkv_attention_plan_words

@@ -58,6 +58,7 @@
 // reaches the output.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/pkv.h"
@@ -1468,4 +1469,83 @@ extern "C" pkv_status pkv_paged_attention_reduce(
   a.part_acc = (float*)((const char*)workspace + kCounterBytes);
   a.part_ml = a.part_acc + (size_t)S * Hq * nparts * D;
   return launch_reduce_kernel(a, pl, S, Hq, Hq / Hkv, D, B, (hipStream_t)hip_stream);
+}
+
+// ---------------------------------------------------------------------------
+// The decode call without a workspace argument, for callers that cannot
+// allocate.  Its partials and merge counters live in `scratch`, one array per
+// GPU the library runs on.  In host code `scratch` only names the symbol: its
+// device address on the current GPU comes from hipGetSymbolAddress, taken once
+// per device at the first call there and kept; only that address is passed to
+// kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[PKV_SCRATCH_BYTES];
+
+namespace pkv {
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of `scratch` on the device of `st`, which must be current.
+static pkv_status scratch_address(hipStream_t st, void** out) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur < 0) return PKV_EHIP;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0) return PKV_EHIP;
+  if (dev != cur) return PKV_EINVAL;
+  if (dev >= kMaxScratchDevices) return PKV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+__global__ void clear_words_kernel(int* __restrict__ w, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) w[i] = 0;
+}
+
+}  // namespace pkv
+
+extern "C" pkv_status pkv_paged_attention_decode_noalloc(
+    float* out, const void* q, void* k_pool, void* v_pool, const void* new_key,
+    const void* new_value, const int32_t* block_tables, const int32_t* context_lens, int32_t S,
+    int32_t Hq, int32_t Hkv, int32_t D, int32_t B, int32_t max_blocks, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, const int32_t* plan,
+    int32_t plan_items, int32_t plan_merge, pkv_dtype dtype, uint32_t flags,
+    const float* k_scale, const float* v_scale, void* hip_stream) {
+  if (S < 0 || Hq <= 0 || D <= 0 || max_context_len < 0 || partition_size < 0)
+    return PKV_EINVAL;
+  const size_t need = pkv_attention_workspace_bytes(S, Hq, D,
+                                                    std::min<int64_t>(max_context_len,
+                                                                      (int64_t)std::max(max_blocks, 0) * B),
+                                                    partition_size);
+  if (need > PKV_SCRATCH_BYTES) return PKV_ENOSCRATCH;
+  hipStream_t hs = (hipStream_t)hip_stream;
+  void* ws = nullptr;
+  pkv_status st = scratch_address(hs, &ws);
+  if (st != PKV_OK) return st;
+  DecodeArgs a;
+  int64_t groups;
+  const PlanArg pl{plan, plan_items, plan_merge};
+  st = prepare_decode(&a, &groups, out, q, k_pool, v_pool, new_key, new_value, block_tables,
+                      context_lens, S, Hq, Hkv, D, B, max_blocks, num_blocks, max_context_len,
+                      scale, partition_size, pl, ws, PKV_SCRATCH_BYTES, dtype, flags, k_scale,
+                      v_scale);
+  if (st != PKV_OK || groups == 0) return st;
+  if (a.counters) {
+    // the merge counters must start at zero: a call is not trusted to have
+    // left them so (it may have been cut short)
+    const int n = S * Hkv;
+    clear_words_kernel<<<(unsigned)((n + 255) / 256), 256, 0, hs>>>(a.counters, n);
+    st = launch_status();
+    if (st != PKV_OK) return st;
+  }
+  st = launch_main_kernel(a, groups, q, k_pool, v_pool, D, B, Hq / Hkv, dtype, flags, hs);
+  if (st != PKV_OK) return st;
+  return launch_reduce_kernel(a, pl, S, Hq, Hq / Hkv, D, B, hs);
 }

@@ -10,6 +10,7 @@ extern "C" const char* pkv_status_string(pkv_status s) {
     case PKV_EEXIST: return "PKV_EEXIST: sequence id already in use";
     case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED: no kernel for this shape or dtype";
     case PKV_EHIP: return "PKV_EHIP: HIP launch or runtime error";
+    case PKV_ENOSCRATCH: return "PKV_ENOSCRATCH: needs more than the library's static scratch";
   }
   return "unknown pkv_status";
 }

@@ -152,5 +152,5 @@ def test_workspace_size_formula(pkv):
 
 
 def test_status_strings(pkv):
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert pkv.lib.pkv_status_string(code).decode().startswith("PKV_")
