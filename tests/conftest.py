@@ -32,4 +32,17 @@ def pkv():
         spec.loader.exec_module(mod)
         mod.build(verbose=False)
     import paged_kv_cache_346_amd
+    host = os.environ.get("PKV_TEST_HOST_LIB")
+    if host:
+        # a host-only build of the block manager, scheduler, step packer and
+        # planner (tests/test_host_sanitizers.py runs the host parity tests on
+        # one built with AddressSanitizer and UndefinedBehaviorSanitizer): the
+        # binding's host calls go to it
+        import ctypes
+        handle = ctypes.CDLL(host)
+        for name, (res, args) in paged_kv_cache_346_amd.SIGNATURES.items():
+            if hasattr(handle, name):
+                fn = getattr(handle, name)
+                fn.restype, fn.argtypes = res, args
+        paged_kv_cache_346_amd.lib = handle
     return paged_kv_cache_346_amd
