@@ -25,7 +25,8 @@ sizeof(kv)) times K, divided by the wall time of the K timed steps.  The
 over its average launch time from HIP events on its stream, recorded around
 the launch of every 8th timed step) against the HBM peak.  `also` holds the
 same figures for the 70B-shaped long-context batch at both block sizes,
-measured in the same run (--no-extra skips them).  `cpu_baseline` times the
+measured in the same run by child processes of this script (--no-extra skips
+them).  `cpu_baseline` times the
 fp64 CPU oracle's whole step on the same batch.
 
 Inputs are synthetic (seeded), shaped like the pages' workloads; see
@@ -769,14 +770,22 @@ def main() -> int:
 
     name = args.config
     rec = measure(args, torch, np, pkv, W, name, args.kv_dtype, primary=True)
+    batch = rec.pop("_batch")
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        rec["cpu_baseline"] = cpu_baseline(batch, torch, args.cpu_seconds)
+    del batch
     if not args.no_extra:
         # the other single-GPU configuration of the >= 70% target (the 70B-shaped
-        # long-context batch at both block sizes), measured in the same run
+        # long-context batch at both block sizes), measured in the same run, each
+        # in a process of its own: a serving process allocates its pool once, and
+        # a workload measured after another one's multi-GB pools were allocated
+        # and freed in the same process runs 3-4% slower
         rec["also"] = {}
         for other in ("long70b_b16", "long70b_b32"):
             if other == name:
                 continue
-            r = measure(args, torch, np, pkv, W, other, args.kv_dtype, primary=False)
+            r = measure_in_child(args, other)
             rec["also"][other] = {
                 "workload": r["config"]["workload"], "value": r["value"], "unit": "GB/s",
                 "frac_of_hbm_peak": r["frac_of_hbm_peak"], "ms_per_step": r["ms_per_step"],
@@ -787,10 +796,6 @@ def main() -> int:
                 "kv_bytes_per_step": r["config"]["kv_bytes_per_step"],
                 "partition_size": r["config"]["partition_size"],
                 "merge": r["config"]["merge"]}
-    if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = cpu_baseline(rec.pop("_batch"), torch, args.cpu_seconds)
-    rec.pop("_batch", None)
     line = json.dumps(rec)
     print(line, flush=True)
     if args.json_out:
@@ -799,10 +804,32 @@ def main() -> int:
     return 0
 
 
+def measure_in_child(args, name):
+    """One more workload, measured by this script in a child process with the
+    same steps, warm-up and KV dtype; returns its JSON record."""
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "rec.json")
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", name, "--no-extra",
+               "--no-cpu-baseline", "--steps", str(args.steps), "--warmup", str(args.warmup),
+               "--json-out", out]
+        if args.kv_dtype:
+            cmd += ["--kv-dtype", args.kv_dtype]
+        if args.no_plan:
+            cmd += ["--no-plan"]
+        log(f"bench: measuring {name} in a child process")
+        r = subprocess.run(cmd, stdout=subprocess.DEVNULL)
+        if r.returncode != 0:
+            raise RuntimeError(f"bench.py for {name} exited with {r.returncode}")
+        with open(out) as f:
+            return json.load(f)
+
+
 def measure(args, torch, np, pkv, W, name, kv_dtype, primary):
     """Warm-up, the K timed steps and the per-kernel breakdown of one workload;
-    returns the JSON record (the primary workload's also carries its batch for
-    the CPU baseline)."""
+    returns the JSON record, which also carries the batch (for the CPU
+    baseline) under "_batch"."""
     log(f"bench: building workload {name}")
     batch = Batch(pkv, torch, W, name, args.partition_size if primary else None, args.layers,
                   not args.no_plan, not args.separate_cache_write, kv_dtype)
@@ -915,12 +942,7 @@ def measure(args, torch, np, pkv, W, name, kv_dtype, primary):
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if primary:
-        rec["_batch"] = batch
-    else:
-        del batch
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
+    rec["_batch"] = batch
     return rec
 
 

@@ -263,6 +263,7 @@ __device__ __forceinline__ bool store_item(const DecodeArgs& a, E* k_pool, E* v_
 // the counter wait used here).
 // ---------------------------------------------------------------------------
 constexpr int kSc1 = 16;                        // cache-policy bit: device scope
+constexpr int kNtPol = 2;                       // cache-policy bit: nontemporal
 constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit buffer, gfx9 layout
 constexpr int kWaitVm0 = 0x0F70;                // s_waitcnt vmcnt(0)
 typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
@@ -294,6 +295,16 @@ struct PartialRows {
   }
   __device__ __forceinline__ void store1(float v, int off) const {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), acc, off, 0, kSc1);
+  }
+  // the same rows for the reduce launch: nontemporal stores (a wave holds its
+  // slot until its stores are acknowledged, and under the launch's read
+  // traffic nontemporal ones are acknowledged sooner: 5% on the 70B-shaped
+  // batch, whose every item ends with a partial)
+  __device__ __forceinline__ void store4_nt(const f32x4& v, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), acc, off, 0, kNtPol);
+  }
+  __device__ __forceinline__ void store1_nt(float v, int off) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), acc, off, 0, kNtPol);
   }
   __device__ __forceinline__ void store_ml(float m, float l, int off) const {
     __builtin_amdgcn_raw_buffer_store_b64(u32x2v{__float_as_uint(m), __float_as_uint(l)}, ml,
@@ -602,8 +613,15 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(
     const float l = wave_sum(ls[gi]);
     const RowSink dst = row_sink<D, G>(a, it, gi);
     const float scl = (dst.ml ? 1.f : 1.f / l) * out_scale;
+    if (dst.ml) {
+      const PartialRows<D, G> pr(a, it.s, it.g);
 #pragma unroll
-    for (int k = 0; k < ND; ++k) dst.acc[lane + kWave * k] = acc[gi][k] * scl;
+      for (int k = 0; k < ND; ++k)
+        pr.store1_nt(acc[gi][k] * scl, pr.acc_off(gi, it.p, lane + kWave * k));
+    } else {
+#pragma unroll
+      for (int k = 0; k < ND; ++k) dst.acc[lane + kWave * k] = acc[gi][k] * scl;
+    }
     if (dst.ml && lane == 0) {
       dst.ml[0] = m[gi];
       dst.ml[1] = l;
@@ -1067,9 +1085,16 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   if (r < G) {
     const RowSink dst = row_sink<D, G>(a, it, r);
     const float scl = (dst.ml ? 1.f : 1.f / ls) * out_scale;
+    if (dst.ml) {
+      const PartialRows<D, G> pr(a, it.s, it.g);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<f32x4*>(dst.acc + 16 * dt + 4 * c) = acc[dt] * scl;
+      for (int dt = 0; dt < NDT; ++dt)
+        pr.store4_nt(acc[dt] * scl, pr.acc_off(r, it.p, 16 * dt + 4 * c));
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4*>(dst.acc + 16 * dt + 4 * c) = acc[dt] * scl;
+    }
     if (dst.ml && c == 0) {
       dst.ml[0] = m;
       dst.ml[1] = ls;
