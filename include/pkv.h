@@ -574,7 +574,7 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *   max_context_len  host-known bound on context_lens; sizes the grid (no sync)
  *   scale         score scale, usually 1/sqrt(D)
  *   partition_size   tokens per work item: 0 = default (512), else a positive
- *                 multiple of 32 and of B spanning at most 64 blocks (<= 64*B
+ *                 multiple of 32 and of B spanning at most 128 blocks (<= 128*B
  *                 tokens).  Sequences longer than one partition are split and
  *                 their partitions merged (log-sum-exp combine): inside the
  *                 main launch, by the last of a (sequence, KV head)'s items to

@@ -77,7 +77,7 @@ constexpr int kWavesPerGroup = 1;           // items per workgroup
 // finish it sooner than one wave would.  Also the reduce launch merges when the
 // batch has more (sequence, KV head) pairs than the workspace has counters.
 constexpr int kMergeInLaunchMax = 16;
-static_assert(kMaxPartitionBlocks == kWave, "one table entry per lane");
+static_assert(kMaxPartitionBlocks == 2 * kWave, "two table entries per lane");
 
 struct DecodeArgs {
   float* out;
@@ -654,6 +654,11 @@ __global__ __launch_bounds__(NW* kWave) void pa_valu_kernel(
 //      For that, row r of quarter th stands for step token 8(r/4) + 4th + r%4,
 //      so the scores lane (c, r) holds -- rows 4c .. 4c+3 of both quarters --
 //      are exactly tokens 8c .. 8c+7, the p.v k index 8c + e is token 8c + e.
+//   Those K rows read half of each 128-byte line per instruction.  At B = 16
+//   the K loads instead read whole lines (lane r: token 8h + r%8 of block r/8,
+//   h = 0, 1), nontemporal, and the operand moves the rows into MFMA order
+//   with two DPP row shifts; at B = 32 the half-line loads stay, with ordinary
+//   loads so the other half is served from L2.
 // ---------------------------------------------------------------------------
 template <int D, int B, int G, int NW, bool NT, bool AP, bool F8>
 __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
@@ -813,17 +818,29 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
         // depends on the lane: K rows r >= 8 and V lanes c >= 2 are in the second
         const size_t bk = B == 16 ? (r >= 8 ? pbs[2 * st + 1] : pbs[2 * st]) : pbs[st];
         const size_t bv = B == 16 ? (c >= 2 ? pbs[2 * st + 1] : pbs[2 * st]) : pbs[st];
-        const int ktok = (8 * (r >> 2) + (r & 3)) % B;  // + 4th
         const int vtok = (8 * c) % B;
         const auto* kb = k_pool + bk * blk_stride + head_off;
         const auto* vb = v_pool + bv * blk_stride + head_off;
         if constexpr (decltype(WK)::value) {
+          if constexpr (B == 16) {
+            // whole lines, nontemporal: register 2st + h holds, in lane r,
+            // token 8h + r%8 of its block (k_operand moves the rows into MFMA
+            // order)
 #pragma unroll
-          for (int th = 0; th < 2; ++th)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < NJ / 2; ++i)
-              tl.k[2 * st + th][i] =
-                  pool_load<kNtK, u32x4>(kb + ((size_t)(4 * i + c) * B + ktok + 4 * th) * 16);
+              for (int i = 0; i < NJ / 2; ++i)
+                tl.k[2 * st + h][i] = pool_load<NT, u32x4>(
+                    kb + ((size_t)(4 * i + c) * B + (r & 7) + 8 * h) * 16);
+          } else {
+            const int ktok = 8 * (r >> 2) + (r & 3);  // + 4th
+#pragma unroll
+            for (int th = 0; th < 2; ++th)
+#pragma unroll
+              for (int i = 0; i < NJ / 2; ++i)
+                tl.k[2 * st + th][i] =
+                    pool_load<kNtK, u32x4>(kb + ((size_t)(4 * i + c) * B + ktok + 4 * th) * 16);
+          }
         }
         if constexpr (decltype(WV)::value) {
 #pragma unroll
@@ -885,9 +902,12 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   // fp8: put the appended token's codes (tile token tn = 32 ST + t) into step
   // ST of the final tile.  Row 4(t/8) + t%4 of quarter (t/4) % 2 holds its K
   // chunks; lanes c = t/8 hold its V codes at byte t%8 of their 8-token runs
+  // At B = 16 the K registers hold whole-line rows (see load_part): token t
+  // of step ST is in register 2ST + (t/8)%2 at lane 8(t/16) + t%8; TH is that
+  // register's half.
   auto substitute8 = [&](auto& tl, auto stc, auto thc, int t) {
     constexpr int ST = decltype(stc)::value, TH = decltype(thc)::value;
-    if (r == 4 * (t >> 3) + (t & 3)) {
+    if (B == 16 ? r == 8 * (t >> 4) + (t & 7) : r == 4 * (t >> 3) + (t & 3)) {
 #pragma unroll
       for (int i = 0; i < NJ / 2; ++i)
         tl.k[2 * ST + TH][i] = *reinterpret_cast<const u32x4*>(lds_k8 + 16 * (4 * i + c));
@@ -910,7 +930,31 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   // tile dt over quarters q0, q0 + 1.  fp8 codes are widened to bf16 here, one
   // operand at a time, so no widened tile is ever held in registers
   auto k_operand = [&](Tile& tl, int th, int j) {
-    if constexpr (F8) {
+    if constexpr (F8 && B == 16) {
+      // quarter th = 2 st + q of the tile.  Row r of quarter q is step token
+      // 8(r/4) + 4q + r%4: block r/8, token 8(r%8/4) + 4q + r%4.  Registers 2st
+      // (tokens 0..7 of each block) and 2st + 1 (tokens 8..15) hold block r/8's
+      // token 8h + r%8 in lane r, so lanes with r%8 < 4 take their row from
+      // register 2st (q = 0: lane r; q = 1: lane r + 4) and the others from
+      // register 2st + 1 (q = 0: lane r - 4; q = 1: lane r), moved along the
+      // 16-lane row by DPP
+      const int st = th >> 1, q = th & 1;
+      const u32x4 wx = tl.k[2 * st][j >> 1], wy = tl.k[2 * st + 1][j >> 1];
+      const uint32_t x0 = (j & 1) ? wx[2] : wx[0], x1 = (j & 1) ? wx[3] : wx[1];
+      const uint32_t y0 = (j & 1) ? wy[2] : wy[0], y1 = (j & 1) ? wy[3] : wy[1];
+      const bool low = (r & 7) < 4;
+      // the DPP moves run on every lane (a lane takes its value from another
+      // one, which must be active), then each lane selects
+      u32x2 w;
+      if (q == 0) {
+        const u32x2 sy = {dpp_row_shr4(y0), dpp_row_shr4(y1)};
+        w = low ? u32x2{x0, x1} : sy;
+      } else {
+        const u32x2 sx = {dpp_row_shl4(x0), dpp_row_shl4(x1)};
+        w = low ? sx : u32x2{y0, y1};
+      }
+      return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(w));
+    } else if constexpr (F8) {
       const u32x4 w = tl.k[th][j >> 1];
       return __builtin_bit_cast(bf16x8, fp8x8_to_bf16((j & 1) ? u32x2{w[2], w[3]}
                                                               : u32x2{w[0], w[1]}));
@@ -1049,7 +1093,7 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
       using I1 = std::integral_constant<int, 1>;
       if (appends) {
         if constexpr (F8) {
-          const int t = tn & 31, th = (t >> 2) & 1;
+          const int t = tn & 31, th = B == 16 ? (t >> 3) & 1 : (t >> 2) & 1;
           if (tn < 32) {
             if (th == 0) substitute8(tl, I0{}, I0{}, t); else substitute8(tl, I0{}, I1{}, t);
           } else {

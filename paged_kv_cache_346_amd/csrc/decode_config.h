@@ -6,7 +6,7 @@
 namespace pkv {
 
 constexpr int kDefaultPartition = 512;   // tokens per partition when the caller passes 0
-constexpr int kMaxPartitionBlocks = 64;  // a partition spans at most 64 blocks (one per lane)
+constexpr int kMaxPartitionBlocks = 128;  // a partition spans at most 128 blocks (two per lane)
 
 // Partition size the call resolves to, or 0 when partition_size is not a positive
 // multiple of 32 and of B spanning at most kMaxPartitionBlocks blocks (0 = default).

@@ -79,6 +79,15 @@ __device__ __forceinline__ float read_lane(float v, int src) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Within each row of 16 lanes: the value of lane r - 4 (row_shr:4) or r + 4
+// (row_shl:4), by DPP; lanes with no such source keep their own value.
+__device__ __forceinline__ uint32_t dpp_row_shr4(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t dpp_row_shl4(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x104, 0xf, 0xf, false);
+}
+
 // fp8 E4M3 (OCP, gfx950's fp8) to bf16.  Every E4M3 value has at most four
 // significant bits and an exponent inside bf16's range, so bf16 holds it
 // exactly.  Two codes from one half of a dword (hi selects the upper half),

@@ -9,20 +9,24 @@
 
 namespace pkv {
 
-// Physical block ids of up to 64 consecutive logical blocks, one per lane: each
-// table entry is read from memory once per wave and taken as a scalar with
-// readlane when its block is loaded.  A partition spans at most 64 blocks.
+// Physical block ids of up to 128 consecutive logical blocks, two per lane
+// (lane l holds blocks base + l and base + 64 + l): each table entry is read
+// from memory once per wave and taken as a scalar with readlane when its block
+// is loaded.  A partition spans at most 128 blocks.
 struct TableWindow {
-  int base, v;
+  int base, v0, v1;
   __device__ __forceinline__ void load(const int* row, int b, int limit) {
     base = b;
     const int i = b + (int)(threadIdx.x & (kWave - 1));
-    v = i < limit ? row[i] : 0;
+    v0 = i < limit ? row[i] : 0;
+    v1 = i + kWave < limit ? row[i + kWave] : 0;
   }
-  // Block of logical block lb (wave-uniform, base <= lb < base + 64), clamped
+  // Block of logical block lb (wave-uniform, base <= lb < base + 128), clamped
   // into the pool so a corrupt entry can never address outside it.
   __device__ __forceinline__ int at(int lb, int num_blocks) const {
-    const int pb = __builtin_amdgcn_readlane(v, lb - base);
+    const int d = lb - base;
+    const int pb = d < kWave ? __builtin_amdgcn_readlane(v0, d)
+                             : __builtin_amdgcn_readlane(v1, d - kWave);
     return min(max(pb, 0), num_blocks - 1);
   }
 };

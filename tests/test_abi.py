@@ -55,9 +55,9 @@ def test_host_validation_rejects_before_launch(pkv):
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 48, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
-    # a partition may span at most 64 blocks (2048 tokens = 128 blocks of 16)
+    # a partition may span at most 128 blocks (4096 tokens = 256 blocks of 16)
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
-                                          8, 16, 0.1, 2048, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
+                                          8, 16, 0.1, 4096, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_paged_attention_decode(odd, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,

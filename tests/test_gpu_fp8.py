@@ -101,7 +101,8 @@ LENS = (1, 2, 15, 16, 17, 33, 100, 511, 512, 513, 1030, 1300)
     (8, 64, 16, 1024, True, False), (4, 128, 32, 96, False, False),
     (8, 128, 16, 96, True, True), (4, 128, 16, 512, False, True),
     (1, 128, 16, 512, True, False), (2, 128, 32, 256, False, False),
-    (1, 64, 32, 96, False, True), (2, 64, 16, 1024, True, False)])
+    (1, 64, 32, 96, False, True), (2, 64, 16, 1024, True, False),
+    (4, 128, 16, 2048, True, False), (8, 128, 32, 4096, False, False)])
 def test_fp8_attention_matches_reference(pkv, G, D, B, P, plan, shared):
     import torch
     say(f"case fp8 attention G={G} D={D} B={B} P={P} plan={plan} shared={shared}")

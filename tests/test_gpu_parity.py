@@ -50,6 +50,25 @@ def test_ragged_all_rows(pkv, dtype, G, D, B, P):
     say(f"  worst error {worst:.3e}")
 
 
+@pytest.mark.parametrize("dtype,G,B,P", [("bf16", 4, 16, 2048), ("bf16", 8, 32, 4096),
+                                         ("bf16", 8, 16, 1536), ("f32", 1, 16, 2048),
+                                         ("bf16", 2, 32, 3072)])
+def test_partitions_beyond_one_table_register(pkv, dtype, G, B, P):
+    """Partitions of more than 64 blocks take their block ids from the table
+    window's second register (lanes hold blocks base + l and base + 64 + l):
+    every row on lengths around and across those partitions, planned and not."""
+    lens = (1, 1000, 1040, P - 1, P, P + 1, 2 * P + 37, 3000)
+    cfg = ragged(f"wide_{dtype}_G{G}_B{B}_P{P}", 1500 + G + B + P, lens, 2 * G, 2, 128, B, dtype,
+                 P, kind="decode")
+    say(f"case {cfg.name}")
+    case = Case(pkv, W.make(cfg))
+    ref = case.oracle_out(case.k_pool, case.v_pool)
+    for plan in (False, True):
+        got, _, _ = case.run_device(pkv, plan=plan)
+        worst = check_attention(got, ref, dtype)
+        say(f"  plan={plan}: worst error {worst:.3e}")
+
+
 @pytest.mark.parametrize("dtype,G,B", [("bf16", 8, 16), ("bf16", 4, 32), ("bf16", 1, 16),
                                        ("f32", 2, 32)])
 def test_load_policy_does_not_change_results(pkv, dtype, G, B):

@@ -77,7 +77,7 @@ def test_plan_capacity_and_validation(pkv):
     with pytest.raises(pkv.PkvError):
         pkv.attention_plan(lens, 8, 16, 100, 1500, 48)
     with pytest.raises(pkv.PkvError):
-        pkv.attention_plan(lens, 8, 16, 100, 1500, 2048)
+        pkv.attention_plan(lens, 8, 16, 100, 1500, 4096)
     # an empty batch plans nothing
     words, n_items, n_merge = pkv.attention_plan(np.zeros(0, np.int32), 8, 16, 100, 0, 512)
     assert (words.size, n_items, n_merge) == (0, 0, 0)
