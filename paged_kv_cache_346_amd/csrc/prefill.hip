@@ -18,15 +18,21 @@
 // full for every G.  A workgroup of PW waves owns a (sequence, KV head, PW * NGQ
 // consecutive query groups) item, NGQ groups per wave, and walks the sequence's
 // KV from token 0 to the item's last position in 32-token tiles.  Each tile is
-// fetched once per workgroup -- every thread moves a few 16-byte vectors of it
-// into LDS -- and each wave reads its MFMA operands from there, so a tile feeds
-// PW * NGQ * 16 query columns.  The products are the
-// decode kernel's (same operand layouts, same base-2 online softmax, same bf16
-// hi + lo split of P), with one softmax state and accumulator per group; each
-// column masks the tokens after its own position (causal).  Items are numbered
-// from the end of each sequence's chunk, so the items with the longest KV range
-// are dispatched first; every item of a sequence reads the same prefix, so the
-// pool loads are ordinary cached loads.
+// copied once per workgroup straight from the pool into LDS (global -> LDS
+// copies, no registers on the way) and each wave reads its MFMA operands from
+// there, so a tile feeds PW * NGQ * 16 query columns.  Tiles move through a
+// ring of three LDS slots: tile k + 2 lands while tile k is computed, with one
+// barrier per tile; the small ring lets three workgroups share a CU.  The
+// products are the decode kernel's operand layouts (bf16 hi + lo split of P,
+// base-2 softmax), with one softmax state and accumulator per group; each
+// column masks the tokens after its own position (causal) on the tiles that
+// cross it.  The softmax keeps, per column, a reference m that may trail the
+// column's running maximum by at most 8 (log2 units): the accumulator and the
+// weight sum are rescaled only when a score passes m + 8, which after the first
+// tiles is rare, and out = acc / sum holds for any reference.  Items are
+// numbered from the end of each sequence's chunk, so the items with the longest
+// KV range are dispatched first; every item of a sequence reads the same
+// prefix, so the pool copies are ordinary cached loads.
 // fp8 E4M3 pools: the tiles hold the raw codes (half the bytes) and each MFMA
 // operand is widened to bf16 where it is used (exact: an E4M3 value fits bf16);
 // the K scale joins the score scale and the V scale the output.
@@ -35,6 +41,7 @@
 
 #include "../../include/pkv.h"
 #include "device_common.h"
+#include "kv_tiles.h"
 #include "launch_check.h"
 
 namespace pkv {
@@ -50,19 +57,12 @@ struct PrefillArgs {
   float scale_log2e;
 };
 
-// The LDS tile is a byte copy of the tile's K pool regions followed by its V in
-// MFMA operand order, so a K operand is read contiguously by the wave and a V
-// operand is one read per lane.  Tiles are staged two at a time, one barrier
-// per pair: the buffer a pair is written into was last read two stages
-// earlier, before every wave passed the previous barrier, and the loads of the
-// next pair are issued after the barrier and land while this pair is computed.
-// The stage count and every early exit depend only on the workgroup's item, so
-// all its waves reach every barrier.  Each wave computes the tiles up to its
-// own last position (V past it is zeroed) and skips the rest.  Four waves of two groups each: 128 query columns per tile (measured
-// on 16 x (1,536 cached + 512 new) tokens against four waves of one group and
-// eight of one; a wave of two groups keeps two per SIMD at D = 128).
+// Four waves of two groups each: 128 query columns per tile (measured on 16 x
+// (1,536 cached + 512 new) tokens against four waves of one group and eight of
+// one), at most 168 VGPRs so that three workgroups fit a CU.
 constexpr int kPrefillSharedWaves = 4;
 constexpr int kPrefillSharedGroups = 2;
+constexpr int kPrefillOcc = 3;  // workgroups per CU (waves per SIMD)
 
 // Max over lanes r, r + 16, r + 32, r + 48 (a score column's four row groups)
 // with gfx950's lane-swap instructions instead of LDS permutes: swapping halves
@@ -78,31 +78,66 @@ __device__ __forceinline__ float max_over_rows(float x) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
+// Direct global -> LDS copies of 16-byte chunks; the destination of lane i of a
+// copy is the copy's LDS base + 16 i, so the lane's choice of source chunk lays
+// the tile out in LDS.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+constexpr int kWaitVmem0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters unwaited
+
+// Largest rise of a column's running maximum (log2 units) that is absorbed
+// without rescaling: the weights exp2(s - m) of later tokens then stay <= 2^8.
+constexpr float kLazyMax = 8.f;
+
+// fp32 maxima of scores straight from the MFMA, with no canonicalizing moves
+// in front (no signalling NaN can reach them)
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// LDS layout of one 32-token tile (K, then V), CE = 16 / sizeof(element),
+// CPT = D / CE:
+//   K chunk (h, cc, sl) at 16 (16 (CPT h + cc) + sl): dims [CE cc, CE cc + CE) of
+//     token 16h + (sl ^ 4h) (the second half's slots are swapped in fours);
+//   V chunk (qv, d) at KB + 16 (D qv + d): tokens [CE qv, CE qv + CE) of dim d.
+// Token order in the MFMAs: row 4c + i of quarter th of a score tile is token
+// 8c + 4th + i, so lane (c, r) holds the scores of tokens 8c .. 8c + 7 of its
+// column, which are also the eight consecutive V tokens of its P.V operand.  The
+// slot swap spreads a K operand read over all LDS banks.
 template <int D, int B, int G, int PW, int NGQ, bool F8>
-__global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
+__global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kernel(
     PrefillArgs a, const uint16_t* __restrict__ q,
     const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ k_pool,
     const std::conditional_t<F8, uint8_t, uint16_t>* __restrict__ v_pool) {
   using E = std::conditional_t<F8, uint8_t, uint16_t>;
   constexpr int ES = (int)sizeof(E);
   constexpr int TILE = 32;
-  constexpr int NJ = D / 32;   // q.k k-steps
-  constexpr int NDT = D / 16;  // p.v output dim tiles
-  constexpr int QT = 16 / G;   // query tokens per group
-  constexpr int GPS = PW * NGQ;     // query groups per workgroup item
-  constexpr int KB = TILE * D * ES;  // bytes of a tile's K (and of its V)
-  constexpr int RB = B * D * ES;     // bytes of one (block, head) K or V region
-  constexpr int OPB = 8 * ES;        // bytes of one lane's V operand (8 tokens)
-  constexpr int NTH = PW * kWave;
-  constexpr int VPT = 2 * KB / (16 * NTH);  // 16-byte vectors per thread per tile
-  static_assert(16 % G == 0 && (B == 16 || B == 32) && D % 32 == 0, "unsupported shape");
-  static_assert(VPT >= 1 && VPT * 16 * NTH == 2 * KB, "a tile splits evenly over the threads");
-  static_assert(RB % (16 * kWave) == 0, "a wave's run of a tile lies in one pool region");
+  constexpr int NJ = D / 32;         // q.k k-steps
+  constexpr int NDT = D / 16;        // p.v output dim tiles
+  constexpr int QT = 16 / G;         // query tokens per group
+  constexpr int GPS = PW * NGQ;      // query groups per workgroup item
+  constexpr int CE = 16 / ES;        // elements per 16-byte chunk
+  constexpr int CPT = D / CE;        // chunks of one token's K
+  constexpr int KCH = TILE * CPT;    // chunks of a tile's K (and of its V)
+  constexpr int KB = 16 * KCH;
+  constexpr int RUNS = 2 * KCH / kWave;  // 64-chunk copies per tile
+  constexpr int RPW = RUNS / PW;         // per wave
+  // s_waitcnt with at most RPW vector memory operations outstanding
+  constexpr int kWaitVmemRPW = (RPW & 0xF) | ((RPW >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  constexpr int NBUF = 3;                // tile ring: tile k + 2 lands while k is computed
+  static_assert(16 % G == 0 && (B == 16 || B == 32) && D % kWave == 0, "unsupported shape");
+  static_assert(KCH % kWave == 0 && RUNS % PW == 0, "a tile's copies split evenly over the waves");
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  constexpr int TPS = 2;  // tiles per LDS stage (one barrier each)
-  __shared__ __align__(16) uint8_t smem[2][TPS][2 * KB];
+  __shared__ __align__(16) uint8_t smem[NBUF][2 * KB];
 
   const int wave = (int)threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -127,7 +162,7 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
   // one past the item's last position: the tiles the workgroup loads
   const int end = L - Q + min((set + 1) * GPS * QT, Q);
 
-  // this wave's groups; a wave whose groups all lie past the chunk still loads
+  // this wave's groups; a wave whose groups all lie past the chunk still copies
   // its share of every tile and takes every barrier
   const int qg0 = set * GPS + wave * NGQ;
   const bool active = qg0 * QT < Q;
@@ -152,11 +187,14 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
     for (int j = 0; j < NJ; ++j)
       qb[u][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * j + c)));
   }
-  float m[NGQ], ls[NGQ];
+  // Running state per column, relative to a reference m that trails the true
+  // maximum by at most kLazyMax: out = acc / ls exactly as with the maximum.
+  float m[NGQ], ls[NGQ], thr[NGQ];
   f32x4 acc[NGQ][NDT];
 #pragma unroll
   for (int u = 0; u < NGQ; ++u) {
     m[u] = -INFINITY;
+    thr[u] = -INFINITY;
     ls[u] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -165,104 +203,83 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
   // fp8: the K scale joins the score scale, the V scale the output
   const float score_scale = F8 ? a.scale_log2e * a.k_scale[g] : a.scale_log2e;
   const float out_scale = F8 ? a.v_scale[g] : 1.f;
+  const float inv_scale = 1.f / score_scale;
   const int n = (end + TILE - 1) / TILE;
   const int nb_last = (end + B - 1) / B - 1;  // a block past it repeats it (masked tokens)
   const int* table = a.block_tables + (size_t)s * a.max_blocks;
-  const size_t head_off = (size_t)g * (D * B);
-  const size_t blk_stride = (size_t)a.Hkv * (D * B);
+  const size_t head_off = (size_t)g * (D * B) * ES;
+  const size_t blk_stride = (size_t)a.Hkv * (D * B) * ES;
 
-  // thread t moves bytes 16(t + NTH i) of the tile's pool regions (K of its
-  // blocks, then V of its blocks); a wave's 1 KiB run lies in one region, so its
-  // block id is wave-uniform and read once per wave.  K lands in LDS in the pool
-  // layout.  V lands in MFMA operand order: OPB bytes per (dim tile dt, lane (c,
-  // r)) at (64 dt + lane) * OPB -- dim 16dt + r, tokens 4c .. 4c+3 of quarter 0
-  // and then of quarter 1 -- so each V operand is one contiguous read; a staged V
-  // vector (dim d, tokens T .. T + 16/ES - 1 of the tile) splits into 4-token
-  // runs of lanes (c0 + i, d % 16), c0 = (T % 16) / 4
-  u32x4 stg[TPS][VPT];
-  auto sstore = [&](int h, uint8_t* t) {
+  // this wave's copies: copy rj = wave + PW i moves chunks 64 rj .. 64 rj + 63 of
+  // the tile (K chunks, then V chunks), all from one of the tile's blocks
+  // (B = 16: two); per lane, the chunk's byte offset inside its (block, head)
+  // region -- the same for every tile
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t src_off[RPW];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int byte = 16 * ((int)threadIdx.x + NTH * i);
-      if (byte < KB) {
-        *reinterpret_cast<u32x4*>(t + byte) = stg[h][i];
-      } else {
-        const int o = byte - KB;
-        const int bt = o / RB;
-        const int e = (o - bt * RB) / ES;  // element of the (block, head) V region
-        const int d = e / B, tt = bt * B + e % B;
-        const int at =
-            KB + ((d / 16) * kWave + ((tt % 16) / 4) * 16 + d % 16) * OPB + (tt / 16) * (4 * ES);
-        if constexpr (F8) {
+  for (int i = 0; i < RPW; ++i) {
+    const int p = kWave * (wv + PW * i) + lane;
+    if (p < KCH) {
+      const int h = p / (16 * CPT), cc = (p / 16) % CPT, sl = p % 16;
+      const int t = 16 * h + (sl ^ (4 * h));
+      src_off[i] = (uint32_t)((cc * B + t % B) * 16);
+    } else {
+      const int pv = p - KCH;
+      const int t0 = (pv / D) * CE, d = pv % D;
+      src_off[i] = (uint32_t)((d * B + t0 % B) * ES);
+    }
+  }
+  // block of the tile each copy reads (0 or 1) and whether it is V
+  auto run_v = [&](int i) { return kWave * (wv + PW * i) >= KCH; };
+  auto run_blk = [&](int i) {
+    const int p0 = kWave * (wv + PW * i);
+    if (B == 32) return 0;
+    return p0 < KCH ? p0 / (16 * CPT) : ((p0 - KCH) / D) * CE / B;
+  };
+  TableWindow tw;
+  tw.load(table, 0, a.max_blocks);
+  const uint8_t* kp8 = reinterpret_cast<const uint8_t*>(k_pool) + head_off;
+  const uint8_t* vp8 = reinterpret_cast<const uint8_t*>(v_pool) + head_off;
+  // copies of tile k into its ring slot; block ids are read before any copy
+  auto issue = [&](int k) {
+    int pb[TILE / B];
+    const int lbl = min(k * (TILE / B) + TILE / B - 1, nb_last);
+    if (lbl >= tw.base + 2 * kWave) tw.load(table, min(k * (TILE / B), nb_last), a.max_blocks);
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
-            *reinterpret_cast<uint32_t*>(t + at + 16 * OPB * w) = stg[h][i][w];
-        } else {
-          *reinterpret_cast<u32x2*>(t + at) = u32x2{stg[h][i][0], stg[h][i][1]};
-          *reinterpret_cast<u32x2*>(t + at + 16 * OPB) = u32x2{stg[h][i][2], stg[h][i][3]};
-        }
-      }
+    for (int b = 0; b < TILE / B; ++b)
+      pb[b] = tw.at(min(k * (TILE / B) + b, nb_last), a.num_blocks);
+    uint8_t* dst = &smem[k % NBUF][0];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const uint8_t* base = (run_v(i) ? vp8 : kp8) + (size_t)pb[run_blk(i)] * blk_stride;
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(base + src_off[i]),
+                                       (lds_ptr_t)(dst + 16 * kWave * (wv + PW * i)), 16, 0, 0);
     }
   };
-  auto gload = [&](int k, int h) {
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int byte = 16 * ((int)threadIdx.x + NTH * i);
-      const int part = byte / KB;  // 0: K, 1: V
-      const int o = byte - part * KB;
-      const int bt = o / RB;       // block of the tile
-      const int lb = __builtin_amdgcn_readfirstlane(min(k * (TILE / B) + bt, nb_last));
-      const int pb = min(max(table[lb], 0), a.num_blocks - 1);
-      const E* base = (part ? v_pool : k_pool) + (size_t)pb * blk_stride + head_off;
-      stg[h][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(base) +
-                                                  (o - bt * RB));
-    }
-  };
 
-  // tile k from LDS: K of quarter th at k-step j (lane (c, r): dims 32j + 8c ..
-  // +7 of token 16th + r, in the pool layout: bf16 chunk 4j + c, fp8 half c % 2
-  // of 16-dim chunk 2j + c / 2) and the V operand of dim tile dt.  fp8 codes are
-  // widened to bf16 per operand (exact)
+  // per-lane LDS offsets of the operands: K of quarter th (slot of token
+  // 8 (r / 4) + 4 th + r % 4, dims 32 j + 8c .. + 7), V of dim tile 0 (tokens
+  // 8c .. 8c + 7 of dim r)
+  int kofs[2];
+#pragma unroll
+  for (int th = 0; th < 2; ++th) {
+    const int t = 8 * (r >> 2) + 4 * th + (r & 3);
+    const int h = t >> 4, sl = (t & 15) ^ (4 * h);
+    kofs[th] = F8 ? (((h * CPT + (c >> 1)) * 16 + sl) * 16 + 8 * (c & 1))
+                  : (((h * CPT + c) * 16 + sl) * 16);
+  }
+  const int vofs = KB + (F8 ? (((c >> 1) * D + r) * 16 + 8 * (c & 1)) : ((c * D + r) * 16));
   auto k_operand = [&](const uint8_t* t, int th, int j) {
-    const int rq = (16 * th) / B * RB, tq = (16 * th) % B;
     if constexpr (F8) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(
-          t + rq + ((2 * j + (c >> 1)) * B + tq + r) * 16 + 8 * (c & 1));
+      const u32x2 w = *reinterpret_cast<const u32x2*>(t + kofs[th] + j * 512);
       return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(w));
     } else {
-      return __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(t + rq + ((4 * j + c) * B + tq + r) * 16));
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t + kofs[th] + j * 1024));
     }
   };
   using VOp = std::conditional_t<F8, u32x2, u32x4>;
   auto compute = [&](int k, const uint8_t* t) {
     const int T0 = k * TILE;
-    VOp v[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      v[dt] = *reinterpret_cast<const VOp*>(t + KB + (dt * kWave + lane) * OPB);
-    // V past the wave's last position may hold anything (NaN): zero it.  bf16:
-    // words 2th + wd hold tokens 16th + 4c + 2wd, +1; fp8: word th holds tokens
-    // 16th + 4c .. +3
-    if (T0 + TILE > wend) {
-#pragma unroll
-      for (int th = 0; th < 2; ++th) {
-        const int ne = min(max(wend - (T0 + 16 * th + 4 * c), 0), 4);
-        if constexpr (F8) {
-          const uint32_t mk = ne >= 4 ? 0xffffffffu : (1u << (8 * ne)) - 1u;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) v[dt][th] &= mk;
-        } else {
-#pragma unroll
-          for (int wd = 0; wd < 2; ++wd) {
-            const uint32_t mk =
-                (2 * wd < ne ? 0x0000ffffu : 0u) | (2 * wd + 1 < ne ? 0xffff0000u : 0u);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) v[dt][2 * th + wd] &= mk;
-          }
-        }
-      }
-    }
     f32x4 sacc[NGQ][2];
 #pragma unroll
     for (int u = 0; u < NGQ; ++u) sacc[u][0] = sacc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -276,39 +293,43 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
           sacc[u][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qb[u][j], sacc[u][th], 0, 0, 0);
       }
     }
+    bf16x8 ph[NGQ], pl[NGQ];
 #pragma unroll
     for (int u = 0; u < NGQ; ++u) {
-      // sv[4th + i]: token T0 + 16th + 4c + i of column r
+      // sv[4th + i]: raw score of token T0 + 8c + 4th + i, column r
       float sv[8];
 #pragma unroll
       for (int th = 0; th < 2; ++th)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[u][th][i] * score_scale;
+        for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[u][th][i];
       if (T0 + TILE > first_pos + u * QT + 1) {  // a tile some column cannot see all of
+        const int nv = min(max(pos[u] + 1 - (T0 + 8 * c), 0), 8);
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
-          const int nv = min(max(pos[u] + 1 - (T0 + 16 * th + 4 * c), 0), 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (i >= nv) sv[4 * th + i] = -INFINITY;
-        }
+        for (int i = 0; i < 8; ++i)
+          if (i >= nv) sv[i] = -INFINITY;
       }
-      float mx = sv[0];
+      // the lane's largest score; a column moves its reference only when one of
+      // its scores passes thr = (m + kLazyMax) / scale (raw units)
+      const float lm = vmax(vmax3(sv[0], sv[1], sv[2]), vmax3(sv[3], sv[4], vmax3(sv[5], sv[6], sv[7])));
+      if (__builtin_amdgcn_ballot_w64(lm > thr[u]) != 0) {
+        // the column's largest score (finite: token 0 is visible to every
+        // column); the scale is positive, so scaling it gives the largest
+        // scaled score
+        const float cm = max_over_rows(lm);
+        const float mn = cm > thr[u] ? cm * score_scale : m[u];
+        const float alpha = fast_exp2(m[u] - mn);  // 1 where unchanged, 0 at the first tile
+        m[u] = mn;
+        thr[u] = (mn + kLazyMax) * inv_scale;
+        ls[u] *= alpha;
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-      mx = max_over_rows(mx);
-      // finite: token 0 is visible to every column
-      const float mn = fmaxf(m[u], mx);
-      const float alpha = fast_exp2(m[u] - mn);
-      // no column's max moved: alpha is exactly 1 everywhere, skip the rescale
-      const bool rescale = __builtin_amdgcn_ballot_w64(mn != m[u]) != 0;
-      m[u] = mn;
+        for (int dt = 0; dt < NDT; ++dt) acc[u][dt] *= alpha;
+      }
       u32x4 phw, plw;
       float psum = 0.f;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        const float p0 = fast_exp2(sv[2 * wd] - mn);
-        const float p1 = fast_exp2(sv[2 * wd + 1] - mn);
+        const float p0 = fast_exp2(__builtin_fmaf(sv[2 * wd], score_scale, -m[u]));
+        const float p1 = fast_exp2(__builtin_fmaf(sv[2 * wd + 1], score_scale, -m[u]));
         psum += p0 + p1;
         // hi: truncated to bf16; lo: the exact remainder rounded to nearest even
         const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
@@ -318,44 +339,59 @@ __global__ __launch_bounds__(PW* kWave, 2) void pa_prefill_shared_kernel(
             uint32_t, __builtin_convertvector(
                           f32x2{p0 - __uint_as_float(h0), p1 - __uint_as_float(h1)}, bf16x2));
       }
-      ls[u] = ls[u] * alpha + psum;
-      const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
-      const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
-      if (rescale) {
+      ls[u] += psum;
+      ph[u] = __builtin_bit_cast(bf16x8, phw);
+      pl[u] = __builtin_bit_cast(bf16x8, plw);
+    }
+    // V past the wave's last position may hold anything (NaN): zero it.  The
+    // lane's V tokens are 8c .. 8c + 7: bf16 word w holds 2w, 2w + 1, fp8 word
+    // w holds 4w .. 4w + 3
+    const bool vmask = T0 + TILE > wend;
+    const int ne = min(max(wend - (T0 + 8 * c), 0), 8);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[u][dt] *= alpha;
+    for (int dt = 0; dt < NDT; ++dt) {
+      VOp vv = *reinterpret_cast<const VOp*>(t + vofs + dt * 256);
+      if (vmask) {
+        if constexpr (F8) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const int nbt = min(max(ne - 4 * w, 0), 4);
+            vv[w] &= nbt >= 4 ? 0xffffffffu : (1u << (8 * nbt)) - 1u;
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            vv[w] &= (2 * w < ne ? 0x0000ffffu : 0u) | (2 * w + 1 < ne ? 0xffff0000u : 0u);
+        }
       }
+      bf16x8 va;
+      if constexpr (F8)
+        va = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(vv));
+      else
+        va = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        bf16x8 va;
-        if constexpr (F8)
-          va = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(v[dt]));
-        else
-          va = __builtin_bit_cast(bf16x8, v[dt]);
-        acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[u][dt], 0, 0, 0);
-        acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[u][dt], 0, 0, 0);
+      for (int u = 0; u < NGQ; ++u) {
+        acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[u], acc[u][dt], 0, 0, 0);
+        acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[u], acc[u][dt], 0, 0, 0);
       }
     }
   };
 
-  // stages of TPS tiles; a tile past the last (odd n) loads the clamped last
-  // block and is not computed
-  const int ns = (n + TPS - 1) / TPS;
-#pragma unroll
-  for (int h = 0; h < TPS; ++h) gload(h, h);
-  for (int st = 0; st < ns; ++st) {
-#pragma unroll
-    for (int h = 0; h < TPS; ++h) sstore(h, smem[st & 1][h]);
+  // the ring: tile k is copied at iteration k - 2 (tiles 0 and 1 before the
+  // loop); at iteration k each wave waits for its own copies of tile k (those
+  // of tile k + 1 may still be in flight), the barrier makes every wave's copies
+  // visible and ends every read of the slot tile k + 2 takes (tile k - 1's),
+  // then tile k + 2's copies are issued
+  issue(0);
+  if (n > 1) issue(1);
+  for (int k = 0; k < n; ++k) {
+    if (k + 1 < n)
+      __builtin_amdgcn_s_waitcnt(kWaitVmemRPW);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
-    if (st + 1 < ns) {
-#pragma unroll
-      for (int h = 0; h < TPS; ++h) gload((st + 1) * TPS + h, h);
-    }
-#pragma unroll
-    for (int h = 0; h < TPS; ++h) {
-      const int k = st * TPS + h;
-      if (active && k * TILE < wend) compute(k, smem[st & 1][h]);
-    }
+    if (k + 2 < n) issue(k + 2);
+    if (active && k * TILE < wend) compute(k, &smem[k % NBUF][0]);
   }
 
 #pragma unroll
