@@ -139,7 +139,8 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   __shared__ __align__(16) uint8_t smem[NBUF][2 * KB];
 
-  const int wave = (int)threadIdx.x / kWave;
+  // wave-uniform (scalar) values: the wave's index and all its tile bounds
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane >> 4, r = lane & 15;
   const int SG = a.S * a.Hkv;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
   // the tile (K chunks, then V chunks), all from one of the tile's blocks
   // (B = 16: two); per lane, the chunk's byte offset inside its (block, head)
   // region -- the same for every tile
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wv = wave;
   uint32_t src_off[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -284,14 +285,12 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
 #pragma unroll
     for (int u = 0; u < NGQ; ++u) sacc[u][0] = sacc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int th = 0; th < 2; ++th) {
+    for (int x = 0; x < 2 * NJ; ++x) {  // (quarter, k-step) = (x % 2, x / 2)
+      const bf16x8 kop = k_operand(t, x % 2, x / 2);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const bf16x8 kop = k_operand(t, th, j);
-#pragma unroll
-        for (int u = 0; u < NGQ; ++u)
-          sacc[u][th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qb[u][j], sacc[u][th], 0, 0, 0);
-      }
+      for (int u = 0; u < NGQ; ++u)
+        sacc[u][x % 2] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qb[u][x / 2], sacc[u][x % 2], 0, 0, 0);
     }
     bf16x8 ph[NGQ], pl[NGQ];
 #pragma unroll
@@ -343,32 +342,20 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
       ph[u] = __builtin_bit_cast(bf16x8, phw);
       pl[u] = __builtin_bit_cast(bf16x8, plw);
     }
-    // V past the wave's last position may hold anything (NaN): zero it.  The
-    // lane's V tokens are 8c .. 8c + 7: bf16 word w holds 2w, 2w + 1, fp8 word
-    // w holds 4w .. 4w + 3
-    const bool vmask = T0 + TILE > wend;
-    const int ne = min(max(wend - (T0 + 8 * c), 0), 8);
+    // P.V, one dim tile at a time (V of tokens past the item's end was zeroed
+    // in LDS; past this wave's last position the weights are 0)
+    // (each V operand is read two dim tiles ahead of its products)
+    VOp vq[NDT];
+    vq[0] = *reinterpret_cast<const VOp*>(t + vofs);
+    vq[1] = *reinterpret_cast<const VOp*>(t + vofs + 256);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      VOp vv = *reinterpret_cast<const VOp*>(t + vofs + dt * 256);
-      if (vmask) {
-        if constexpr (F8) {
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const int nbt = min(max(ne - 4 * w, 0), 4);
-            vv[w] &= nbt >= 4 ? 0xffffffffu : (1u << (8 * nbt)) - 1u;
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            vv[w] &= (2 * w < ne ? 0x0000ffffu : 0u) | (2 * w + 1 < ne ? 0xffff0000u : 0u);
-        }
-      }
+      if (dt + 2 < NDT) vq[dt + 2] = *reinterpret_cast<const VOp*>(t + vofs + (dt + 2) * 256);
       bf16x8 va;
       if constexpr (F8)
-        va = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(vv));
+        va = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(vq[dt]));
       else
-        va = __builtin_bit_cast(bf16x8, vv);
+        va = __builtin_bit_cast(bf16x8, vq[dt]);
 #pragma unroll
       for (int u = 0; u < NGQ; ++u) {
         acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[u], acc[u][dt], 0, 0, 0);
@@ -381,7 +368,10 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
   // loop); at iteration k each wave waits for its own copies of tile k (those
   // of tile k + 1 may still be in flight), the barrier makes every wave's copies
   // visible and ends every read of the slot tile k + 2 takes (tile k - 1's),
-  // then tile k + 2's copies are issued
+  // then tile k + 2's copies are issued.  Only the item's last tile can hold
+  // tokens that are not in the sequence (slots past its length, a repeated
+  // last block); their V is zeroed in LDS before that tile is computed, so
+  // that zero weights never meet NaN (their scores are masked).
   issue(0);
   if (n > 1) issue(1);
   for (int k = 0; k < n; ++k) {
@@ -391,6 +381,27 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
       __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
     if (k + 2 < n) issue(k + 2);
+    if (k == n - 1) {
+      // V chunk (qv, d) holds tokens CE qv .. CE qv + CE - 1 of the tile
+      const int e0 = end - k * TILE;  // first token to clear
+      uint8_t* vz = &smem[k % NBUF][KB];
+      for (int o = 16 * (int)threadIdx.x; o < KB; o += 16 * PW * kWave) {
+        const int t0 = (o / 16 / D) * CE;
+        if (t0 + CE > e0) {
+          u32x4 w = *reinterpret_cast<u32x4*>(vz + o);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            uint32_t mk = 0;
+#pragma unroll
+            for (int y = 0; y < 4 / ES; ++y)
+              if (t0 + (4 / ES) * x + y < e0) mk |= (ES == 2 ? 0xffffu : 0xffu) << (8 * ES * y);
+            w[x] &= mk;
+          }
+          *reinterpret_cast<u32x4*>(vz + o) = w;
+        }
+      }
+      __syncthreads();
+    }
     if (active && k * TILE < wend) compute(k, &smem[k % NBUF][0]);
   }
 
