@@ -11,10 +11,11 @@
  * Conventions shared by every call
  *   - Every call returns pkv_status (PKV_OK == 0); pkv_status_string() names it.
  *   - Host validation runs before any launch; a rejected call changes nothing.
- *   - The library never allocates device memory.  Pools, tables, outputs and
- *     workspace are owned by the caller (the pool is allocated once, up front:
- *     [ZENO] "Implementation Essentials", pre-allocated memory pool).  The only
- *     memory the library owns is the host heap behind a pkv_bm handle.
+ *   - The library never allocates device memory, except inside a pkv_loop
+ *     (the serving loop below).  Pools, tables, outputs and workspace are
+ *     owned by the caller (the pool is allocated once, up front: [ZENO]
+ *     "Implementation Essentials", pre-allocated memory pool).  Otherwise the
+ *     only memory the library owns is the host heap behind its handles.
  *   - Device calls take raw device pointers and a hipStream_t (passed as void*,
  *     NULL = the null stream); they are asynchronous with respect to the host and
  *     ordered on that stream.  Device pointers must be 16-byte aligned.
@@ -412,6 +413,88 @@ typedef struct pkv_step_pack {
 pkv_status pkv_pack_step(const pkv_bm* bm, const pkv_sched_step* step, int32_t max_blocks,
                          int32_t Hkv, int32_t partition_size, int32_t* buf, size_t buf_words,
                          pkv_step_pack* out);
+
+/* ---------------------------------------------------------------------------
+ * Serving loop: a continuous-batching step in one native call ([RTI] "Batch by
+ * step, not by request"; [ZENO] "Continuous Batching" and "Implementation
+ * Essentials").  pkv_loop_step runs one iteration of the scheduler above and
+ * everything the device needs for it: pkv_pack_step into a pinned host buffer
+ * (two alternate, so the host packs step t + 1 while step t's copy may still
+ * run), one asynchronous copy of the metadata, then on the loop's stream the
+ * swap-in, swap-out and copy-on-write block copies, the step's query and K/V
+ * rows, pkv_reshape_and_cache of the prefill chunks' tokens,
+ * pkv_paged_attention_prefill over the chunks and pkv_paged_attention_decode
+ * over the batch (host work plan; the new tokens are written by the attention
+ * launch), and finally pkv_sched_end_step.
+ * The loop computes no model: the step's rows come from caller-filled device
+ * banks, row r of the step (request id, position) reading bank row
+ * (id * mul + position) mod bank_rows (q_mul for the query bank, kv_mul for the
+ * K and V banks).
+ * Unlike the other calls a pkv_loop owns device memory: its metadata buffer,
+ * the step's row buffers, the decode workspace and the output buffers, grown
+ * (after a stream synchronize) when a step needs more; and two pinned host
+ * buffers.  The pools, the scheduler and its block manager stay the caller's
+ * and must outlive the loop.  Not thread-safe.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_loop pkv_loop;
+
+typedef struct pkv_loop_config {
+  int32_t num_blocks, block_size;  /* must match the block manager */
+  int32_t q_heads, kv_heads, head_dim;
+  int32_t max_running;             /* the scheduler's max_running */
+  int32_t max_len;                 /* longest request (prompt + new tokens) */
+  int32_t partition_size;          /* decode partitions (0 = the library default) */
+  int32_t host_blocks;             /* host pool blocks (swap policy), else 0 */
+  pkv_dtype dtype;                 /* PKV_BF16 or PKV_FP8_E4M3 pools */
+} pkv_loop_config;
+
+/* Device banks of bf16 rows: q_bank [bank_rows, Hq, D], k_bank and v_bank
+ * [bank_rows, Hkv, D]. */
+typedef struct pkv_loop_source {
+  const void* q_bank;
+  const void* k_bank;
+  const void* v_bank;
+  int64_t bank_rows;
+  int64_t q_mul, kv_mul;
+} pkv_loop_source;
+
+/* What a step did.  Pointers stay valid until the next step: decode_out is
+ * float32 [n_batch, Hq, D] (device), prefill_out float32 [n_prefill_rows, Hq,
+ * D] (device, the chunks' rows in order), lens_host the batch's context lengths
+ * (pinned host).  tokens_held .. n_swapped are pkv_sched_stats taken before the
+ * finished requests leave.  host_us: the call's time on the host; wait_us: the
+ * part of it spent waiting for a pinned buffer's previous copy (the device
+ * running behind). */
+typedef struct pkv_loop_step_info {
+  int32_t n_batch, n_prefill, n_prefill_rows, n_admitted, n_preempted, n_finished;
+  int32_t n_swapped_out, n_swapped_in, n_swap_out_blocks, n_swap_in_blocks, n_cow;
+  int32_t max_context;
+  int64_t cached_tokens;           /* prompt tokens of this step's admissions found cached */
+  int64_t tokens_held, slots_committed;
+  int32_t n_waiting, n_running, n_swapped;
+  const int32_t* lens_host;
+  const float* decode_out;
+  const float* prefill_out;
+  double host_us, wait_us;
+} pkv_loop_step_info;
+
+/* k_pool / v_pool: the device pools ([num_blocks] blocks, layouts above);
+ * host_k / host_v: pinned host pools of host_blocks blocks (swap policy) or
+ * NULL; k_scale / v_scale: fp8 per-KV-head scales (device float32 [Hkv]) or
+ * NULL for bf16.  PKV_EINVAL for a bad or mismatched configuration,
+ * PKV_EHIP when an allocation fails. */
+pkv_status pkv_loop_create(const pkv_loop_config* cfg, pkv_bm* bm, pkv_sched* sched,
+                           void* k_pool, void* v_pool, void* host_k, void* host_v,
+                           const float* k_scale, const float* v_scale, void* hip_stream,
+                           pkv_loop** out);
+void pkv_loop_destroy(pkv_loop* loop);
+/* One step.  An error after the scheduler began the step still ends it (the
+ * loop stays usable) and is returned; *info is filled either way. */
+pkv_status pkv_loop_step(pkv_loop* loop, const pkv_loop_source* source, pkv_loop_step_info* info);
+/* Copy the last step's outputs (decode [n_batch, Hq, D], prefill
+ * [n_prefill_rows, Hq, D], float32) into caller device buffers, on the loop's
+ * stream; either destination may be NULL. */
+pkv_status pkv_loop_copy_outputs(const pkv_loop* loop, float* decode_dst, float* prefill_dst);
 
 /* ---------------------------------------------------------------------------
  * Device operations.

@@ -23,7 +23,7 @@ __all__ = [
     "pkv_attention_workspace_bytes", "pkv_paged_attention_decode", "pkv_paged_attention_main",
     "pkv_paged_attention_reduce", "pool_shapes", "paged_attention_main", "paged_attention_reduce",
     "pkv_attention_plan", "pkv_attention_plan_words", "attention_plan", "attention_plan_words",
-    "Plan", "make_plan", "StepPack",
+    "Plan", "make_plan", "StepPack", "LoopConfig", "LoopSource", "LoopStepInfo",
     "reshape_and_cache", "copy_blocks", "attention_workspace_bytes", "attention_workspace",
     "paged_attention_decode", "pkv_paged_attention_decode_noalloc",
     "paged_attention_decode_noalloc", "PKV_ENOSCRATCH", "PKV_SCRATCH_BYTES",
@@ -86,6 +86,34 @@ class StepPack(ctypes.Structure):
         "swap_out_off", "cow_off")]
 
 
+class LoopConfig(ctypes.Structure):
+    """pkv_loop_config (include/pkv.h)."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "num_blocks", "block_size", "q_heads", "kv_heads", "head_dim", "max_running", "max_len",
+        "partition_size", "host_blocks", "dtype")]
+
+
+class LoopSource(ctypes.Structure):
+    """pkv_loop_source (include/pkv.h): the step's rows from device banks."""
+    _fields_ = [("q_bank", ctypes.c_void_p), ("k_bank", ctypes.c_void_p),
+                ("v_bank", ctypes.c_void_p), ("bank_rows", ctypes.c_int64),
+                ("q_mul", ctypes.c_int64), ("kv_mul", ctypes.c_int64)]
+
+
+class LoopStepInfo(ctypes.Structure):
+    """pkv_loop_step_info (include/pkv.h)."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n_batch", "n_prefill", "n_prefill_rows", "n_admitted", "n_preempted", "n_finished",
+        "n_swapped_out", "n_swapped_in", "n_swap_out_blocks", "n_swap_in_blocks", "n_cow",
+        "max_context")] + [
+        ("cached_tokens", ctypes.c_int64), ("tokens_held", ctypes.c_int64),
+        ("slots_committed", ctypes.c_int64), ("n_waiting", ctypes.c_int32),
+        ("n_running", ctypes.c_int32), ("n_swapped", ctypes.c_int32),
+        ("lens_host", ctypes.POINTER(ctypes.c_int32)), ("decode_out", ctypes.c_void_p),
+        ("prefill_out", ctypes.c_void_p), ("host_us", ctypes.c_double),
+        ("wait_us", ctypes.c_double)]
+
+
 # name -> (restype, argtypes); mirrors include/pkv.h
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -124,6 +152,11 @@ SIGNATURES = {
     "pkv_bm_host_snapshot": (_i32, [_vp, _pi32, _pi32]),
     "pkv_bm_count_shared": (_i32, [_vp, _pi64, _i32, _pi64]),
     "pkv_bm_slots": (_i32, [_vp, _i64, _i32, _i32, _pi64]),
+    "pkv_loop_create": (_i32, [ctypes.POINTER(LoopConfig), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, ctypes.POINTER(_vp)]),
+    "pkv_loop_destroy": (None, [_vp]),
+    "pkv_loop_copy_outputs": (_i32, [_vp, _vp, _vp]),
+    "pkv_loop_step": (_i32, [_vp, ctypes.POINTER(LoopSource), ctypes.POINTER(LoopStepInfo)]),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _vp, _vp, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),

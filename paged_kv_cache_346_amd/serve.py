@@ -42,9 +42,12 @@ import math
 import numpy as np
 import torch
 
-from . import (BlockManager, Plan, Scheduler, StepPack, attention_workspace, copy_blocks,
-               paged_attention_decode, paged_attention_prefill, pool_shapes, reshape_and_cache,
-               swap_blocks)
+import ctypes
+
+from . import (BlockManager, LoopConfig, LoopSource, LoopStepInfo, Plan, PkvError, Scheduler,
+               StepPack, attention_workspace, copy_blocks, lib, paged_attention_decode,
+               paged_attention_prefill, pool_shapes, reshape_and_cache, swap_blocks)
+from . import _check, _dev, _dtype_code, _stream
 
 
 class DecodeLoop:
@@ -187,6 +190,111 @@ class DecodeLoop:
 
     def stats(self):
         """(tokens held, slots committed, waiting, running, swapped out)."""
+        return self.sched.stats()
+
+    def idle(self) -> bool:
+        _, _, nw, nr, ns = self.sched.stats()
+        return nw == 0 and nr == 0 and ns == 0
+
+
+class NativeLoop:
+    """The same loop with the whole step in one native call (pkv_loop_step):
+    scheduling, packing, the metadata copy and every launch run in libpkv.so,
+    and Python only makes the call.  The step's query and K/V rows come from
+    device banks (set_source): row r of the step, the token (request id,
+    position), reads bank row (id * mul + position) mod bank rows.  Same
+    arguments as DecodeLoop; step() returns the pkv_loop_step_info of the step
+    (counts, stats, host_us / wait_us), outputs() copies the step's decode and
+    prefill outputs into new tensors."""
+
+    def __init__(self, *, num_blocks: int, block_size: int, q_heads: int, kv_heads: int,
+                 head_dim: int, max_running: int, max_len: int, dtype=torch.bfloat16,
+                 partition_size: int = 0, reserve_max: bool = False, free_order=None,
+                 host_blocks: int = 0, max_prefill_tokens=None, kv_scales=None,
+                 device="cuda", stream=None):
+        self.B, self.Hq, self.Hkv, self.D = block_size, q_heads, kv_heads, head_dim
+        self.device = torch.device(device)
+        self.fp8 = dtype == torch.uint8
+        if self.fp8 != (kv_scales is not None):
+            raise ValueError("fp8 pools (torch.uint8) go with kv_scales=(k_scale, v_scale)")
+        self.k_scale, self.v_scale = kv_scales if self.fp8 else (None, None)
+        self.bm = BlockManager(num_blocks, block_size, free_order)
+        if host_blocks:
+            self.bm.set_host_pool(host_blocks)
+        self.sched = Scheduler(self.bm, max_running, reserve_max, swap=host_blocks > 0,
+                               max_prefill_tokens=max_prefill_tokens)
+        ks, vs = pool_shapes(num_blocks, kv_heads, head_dim, block_size, dtype)
+        self.k_pool = torch.empty(ks, dtype=dtype, device=self.device)
+        self.v_pool = torch.empty(vs, dtype=dtype, device=self.device)
+        self.host_k = self.host_v = None
+        if host_blocks:
+            hks, hvs = pool_shapes(host_blocks, kv_heads, head_dim, block_size, dtype)
+            self.host_k = torch.empty(hks, dtype=dtype, pin_memory=True)
+            self.host_v = torch.empty(hvs, dtype=dtype, pin_memory=True)
+        self.stream = _stream(stream)
+        cfg = LoopConfig(num_blocks, block_size, q_heads, kv_heads, head_dim, max_running, max_len,
+                         partition_size, host_blocks, _dtype_code(self.k_pool))
+        h = ctypes.c_void_p()
+        scales = (_dev(self.k_scale, "k_scale"), _dev(self.v_scale, "v_scale")) if self.fp8 \
+            else (None, None)
+        hosts = (self.host_k.data_ptr(), self.host_v.data_ptr()) if host_blocks else (None, None)
+        _check(lib.pkv_loop_create(ctypes.byref(cfg), self.bm._h, self.sched._h,
+                                   _dev(self.k_pool, "k_pool"), _dev(self.v_pool, "v_pool"),
+                                   *hosts, *scales, self.stream, ctypes.byref(h)),
+               "pkv_loop_create")
+        self._h = h
+        self._src = None
+        self._info = LoopStepInfo()
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib.pkv_loop_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_request(self, req_id: int, prompt_len: int, max_new_tokens: int,
+                    tokens=None) -> None:
+        self.sched.add_request(req_id, prompt_len, max_new_tokens, tokens=tokens)
+
+    def set_source(self, q_bank: torch.Tensor, k_bank: torch.Tensor, v_bank: torch.Tensor,
+                   q_mul: int, kv_mul: int) -> None:
+        """q_bank bf16 [rows, Hq, D], k_bank / v_bank bf16 [rows, Hkv, D] (device)."""
+        rows = q_bank.shape[0]
+        for t, heads, name in ((q_bank, self.Hq, "q_bank"), (k_bank, self.Hkv, "k_bank"),
+                               (v_bank, self.Hkv, "v_bank")):
+            if t.dtype != torch.bfloat16 or tuple(t.shape) != (rows, heads, self.D) or \
+                    not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous bf16 [rows, heads, D]")
+        self._banks = (q_bank, k_bank, v_bank)
+        self._src = LoopSource(_dev(q_bank, "q_bank"), _dev(k_bank, "k_bank"),
+                               _dev(v_bank, "v_bank"), rows, int(q_mul), int(kv_mul))
+
+    def step(self) -> LoopStepInfo:
+        if self._src is None:
+            raise ValueError("set_source first")
+        code = lib.pkv_loop_step(self._h, ctypes.byref(self._src), ctypes.byref(self._info))
+        if code != 0:
+            raise PkvError(code, "pkv_loop_step")
+        return self._info
+
+    def outputs(self):
+        """The last step's decode output [n_batch, Hq, D] and prefill output
+        [n_prefill_rows, Hq, D] (float32 copies)."""
+        info = self._info
+        dec = torch.empty((info.n_batch, self.Hq, self.D), dtype=torch.float32, device=self.device)
+        pf = torch.empty((info.n_prefill_rows, self.Hq, self.D), dtype=torch.float32,
+                         device=self.device)
+        _check(lib.pkv_loop_copy_outputs(self._h, dec.data_ptr() if info.n_batch else None,
+                                         pf.data_ptr() if info.n_prefill_rows else None),
+               "pkv_loop_copy_outputs")
+        return dec, pf
+
+    def stats(self):
         return self.sched.stats()
 
     def idle(self) -> bool:
