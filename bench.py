@@ -388,7 +388,7 @@ def run_serve(args, torch, np):
     reservation of the earlier systems.  Also times swap_blocks over the host
     link.  Prints one JSON line (not the headline metric)."""
     import paged_kv_cache_346_amd as pkv
-    from paged_kv_cache_346_amd.serve import DecodeLoop
+    from paged_kv_cache_346_amd.serve import DecodeLoop, NativeLoop
     import workloads as W
 
     Hq, Hkv, D, B, N = 32, 8, 128, 16, 16162
@@ -405,6 +405,87 @@ def run_serve(args, torch, np):
     kv_rows = torch.randn((2, rows, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
     q_rows = torch.randn((rows, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
 
+    def native(**kw):
+        loop = NativeLoop(num_blocks=N, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
+                          max_running=args.serve_running, free_order=order, **kw)
+        loop.set_source(q_rows, kv_rows[0], kv_rows[1], 104729, 7919)
+        return loop
+
+    def drive(loop):
+        """Run a loop to the end of its trace; the step's account from the
+        native step info, the host's busy time per step (the call minus its
+        waits for the device) and the device's time per step (HIP events
+        around the whole run on the loop's stream)."""
+        acc = dict(steps=0, tokens=0, preempted=0, prefill=0, swapped=0, blocks_out=0,
+                   blocks_in=0, cached=0, util_sum=0.0, host_us=0.0, wait_us=0.0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        t0 = time.perf_counter()
+        while not loop.idle():
+            info = loop.step()
+            acc["steps"] += 1
+            acc["tokens"] += info.n_batch
+            acc["preempted"] += info.n_preempted
+            acc["prefill"] += info.n_prefill_rows
+            acc["swapped"] += info.n_swapped_out
+            acc["blocks_out"] += info.n_swap_out_blocks
+            acc["blocks_in"] += info.n_swap_in_blocks
+            acc["cached"] += info.cached_tokens
+            acc["host_us"] += info.host_us
+            acc["wait_us"] += info.wait_us
+            if info.n_batch:
+                acc["util_sum"] += info.tokens_held / max(info.slots_committed, 1)
+        e1.record()
+        torch.cuda.synchronize()
+        acc["wall"] = time.perf_counter() - t0
+        acc["device_us"] = e0.elapsed_time(e1) * 1e3
+        return acc
+
+    # untimed warm-up: one whole pass of the same trace, so first launches, the
+    # loop's buffers and the device allocator's cache (the first step admits
+    # over 600 prompts at once) are set up before any timed pass
+    warm = native(max_len=max_len)
+    for rid, p_, m_ in trace:
+        warm.add_request(rid, p_, m_)
+    drive(warm)
+    warm.close()
+    del warm
+
+    block_bytes = 2 * Hkv * D * B * 2          # K and V of one block, bf16
+    swap_probe = _swap_probe(torch, pkv, Hkv, D, B, N)
+    log(f"bench: swap_blocks probe: {swap_probe}")
+
+    result = {}
+    prompts = sum(p_ for _, p_, _ in trace)
+    for policy in ("paged", "swap", "reserve"):
+        loop = native(max_len=max_len, reserve_max=(policy == "reserve"),
+                      host_blocks=N if policy == "swap" else 0)
+        for rid, p_, m_ in trace:
+            loop.add_request(rid, p_, m_)
+        a = drive(loop)
+        steps = a["steps"]
+        result[policy] = {
+            "decode_tokens": a["tokens"], "steps": steps,
+            "mean_batch": round(a["tokens"] / steps, 1),
+            "preemptions": a["preempted"] + a["swapped"], "dropped": a["preempted"],
+            "swapped_out": a["swapped"], "blocks_swapped_out": a["blocks_out"],
+            "blocks_swapped_in": a["blocks_in"],
+            "swap_bytes": (a["blocks_out"] + a["blocks_in"]) * block_bytes,
+            "prefill_tokens_written": a["prefill"],
+            "prefill_tokens_recomputed": a["prefill"] - prompts,
+            "kv_utilization": round(a["util_sum"] / steps, 4),
+            "wall_s": round(a["wall"], 3),
+            "decode_tokens_per_s": round(a["tokens"] / a["wall"], 1),
+            "host_busy_us_per_step": round((a["host_us"] - a["wait_us"]) / steps, 1),
+            "host_wait_us_per_step": round(a["wait_us"] / steps, 1),
+            "device_us_per_step": round(a["device_us"] / steps, 1),
+        }
+        log(f"bench: serve {policy}: {result[policy]}")
+        loop.close()
+        del loop
+    # the same paged pass driven step by step from Python (DecodeLoop), for
+    # the host cost of a Python driver against the one native call
     stage = _PinnedIndex(torch, dev)
 
     def kv_source(pairs):
@@ -415,64 +496,24 @@ def run_serve(args, torch, np):
         idx = stage((pairs[:, 0] * 104729 + pairs[:, 1]) % rows)
         return q_rows.index_select(0, idx)
 
-    # untimed warm-up: one whole pass of the same trace, so first launches, the
-    # sources' pinned buffers and the device allocator's cache (the first step
-    # admits over 600 prompts at once) are set up before any timed pass
-    warm = DecodeLoop(num_blocks=N, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
+    loop = DecodeLoop(num_blocks=N, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
                       max_running=args.serve_running, max_len=max_len, free_order=order)
     for rid, p_, m_ in trace:
-        warm.add_request(rid, p_, m_)
-    while not warm.idle():
-        warm.step(kv_source, q_source)
+        loop.add_request(rid, p_, m_)
+    py_steps = py_tokens = 0
     torch.cuda.synchronize()
-    del warm
-
-    block_bytes = 2 * Hkv * D * B * 2          # K and V of one block, bf16
-    swap_probe = _swap_probe(torch, pkv, Hkv, D, B, N)
-    log(f"bench: swap_blocks probe: {swap_probe}")
-
-    result = {}
-    prompts = sum(p_ for _, p_, _ in trace)
-    for policy in ("paged", "swap", "reserve"):
-        loop = DecodeLoop(num_blocks=N, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
-                          max_running=args.serve_running, max_len=max_len,
-                          reserve_max=(policy == "reserve"), free_order=order,
-                          host_blocks=N if policy == "swap" else 0)
-        for rid, p_, m_ in trace:
-            loop.add_request(rid, p_, m_)
-        steps = tokens = preempted = prefill = swapped = blocks_out = blocks_in = 0
-        util_sum, batch_sum = 0.0, 0
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        while not loop.idle():
-            st, _, _, lens = loop.step(kv_source, q_source)
-            n = len(st["batch"])
-            steps += 1
-            tokens += n
-            batch_sum += n
-            preempted += len(st["preempted"])
-            prefill += sum(c for _, _, c in st["prefill"])
-            swapped += len(st["swapped_out"])
-            blocks_out += len(st["swap_out"])
-            blocks_in += len(st["swap_in"])
-            held, committed = st["stats"][:2]
-            if n:
-                util_sum += held / max(committed, 1)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        result[policy] = {
-            "decode_tokens": tokens, "steps": steps, "mean_batch": round(batch_sum / steps, 1),
-            "preemptions": preempted + swapped, "dropped": preempted, "swapped_out": swapped,
-            "blocks_swapped_out": blocks_out, "blocks_swapped_in": blocks_in,
-            "swap_bytes": (blocks_out + blocks_in) * block_bytes,
-            "prefill_tokens_written": prefill,
-            "prefill_tokens_recomputed": prefill - prompts,
-            "kv_utilization": round(util_sum / steps, 4),
-            "wall_s": round(wall, 3),
-            "decode_tokens_per_s": round(tokens / wall, 1),
-        }
-        log(f"bench: serve {policy}: {result[policy]}")
-        del loop
+    t0 = time.perf_counter()
+    while not loop.idle():
+        st, _, _, _ = loop.step(kv_source, q_source)
+        py_steps += 1
+        py_tokens += len(st["batch"])
+    torch.cuda.synchronize()
+    py_wall = time.perf_counter() - t0
+    python_driver = {"steps": py_steps, "wall_s": round(py_wall, 3),
+                     "decode_tokens_per_s": round(py_tokens / py_wall, 1),
+                     "wall_us_per_step": round(py_wall / py_steps * 1e6, 1)}
+    log(f"bench: serve paged, Python driver: {python_driver}")
+    del loop
     # prefix caching and chunked prefill: prompts drawn from 8 shared system
     # prompts plus a request-specific part, with a prefill budget per step
     ptrace = W.prefix_trace(np.random.default_rng(12), args.serve_requests, n_prefixes=8,
@@ -481,27 +522,20 @@ def run_serve(args, torch, np):
     p_max_len = max(p_ + m_ for _, p_, m_, _ in ptrace)
     prefix_result = {}
     for mode in ("cache_off", "cache_on"):
-        loop = DecodeLoop(num_blocks=N, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
-                          max_running=args.serve_running, max_len=p_max_len, free_order=order,
-                          max_prefill_tokens=args.serve_prefill_budget)
+        loop = native(max_len=p_max_len, max_prefill_tokens=args.serve_prefill_budget)
         for rid, p_, m_, toks in ptrace:
             loop.add_request(rid, p_, m_, tokens=toks if mode == "cache_on" else None)
-        steps = tokens = prefill = cached = 0
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        while not loop.idle():
-            st, _, _, _ = loop.step(kv_source, q_source)
-            steps += 1
-            tokens += len(st["batch"])
-            prefill += sum(c for _, _, c in st["prefill"])
-            cached += sum(c for _, _, c in st["admitted"])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        prefix_result[mode] = {"steps": steps, "decode_tokens": tokens,
-                               "prefill_tokens_computed": prefill,
-                               "prompt_tokens_from_cache": cached, "wall_s": round(wall, 3),
-                               "decode_tokens_per_s": round(tokens / wall, 1)}
+        a = drive(loop)
+        prefix_result[mode] = {"steps": a["steps"], "decode_tokens": a["tokens"],
+                               "prefill_tokens_computed": a["prefill"],
+                               "prompt_tokens_from_cache": a["cached"],
+                               "wall_s": round(a["wall"], 3),
+                               "decode_tokens_per_s": round(a["tokens"] / a["wall"], 1),
+                               "host_busy_us_per_step": round((a["host_us"] - a["wait_us"]) /
+                                                              a["steps"], 1),
+                               "device_us_per_step": round(a["device_us"] / a["steps"], 1)}
         log(f"bench: serve prefix {mode}: {prefix_result[mode]}")
+        loop.close()
         del loop
 
     rec = {
@@ -519,7 +553,9 @@ def run_serve(args, torch, np):
                                f"at most {args.serve_running} running",
                    "requests": len(trace), "pool_blocks": N,
                    "max_running": args.serve_running},
+        "driver": "one native call per step (pkv_loop_step)",
         "paged": result["paged"],
+        "paged_python_driver": python_driver,
         "paged_swap": result["swap"],
         "reserve_max_len": result["reserve"],
         "swap_blocks_probe": swap_probe,
@@ -557,42 +593,37 @@ def run_serve_fp8(args, torch, np, pkv, DecodeLoop, W, Hq, Hkv, D, B, N):
     q_rows = torch.randn((rows, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
     scales = (torch.full((Hkv,), 0.025, device=dev), torch.full((Hkv,), 0.025, device=dev))
 
-    stage = _PinnedIndex(torch, dev)
-
-    def kv_source(pairs):
-        idx = stage((pairs[:, 0] * 7919 + pairs[:, 1]) % rows)
-        return kv_rows[0].index_select(0, idx), kv_rows[1].index_select(0, idx)
-
-    def q_source(pairs):
-        idx = stage((pairs[:, 0] * 104729 + pairs[:, 1]) % rows)
-        return q_rows.index_select(0, idx)
-
     def run(kv, blocks):
+        from paged_kv_cache_346_amd.serve import NativeLoop
         kw = {"dtype": torch.uint8, "kv_scales": scales} if kv == "fp8" else {}
         order = np.random.default_rng(13).permutation(blocks).astype(np.int32)
-        loop = DecodeLoop(num_blocks=blocks, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
+        loop = NativeLoop(num_blocks=blocks, block_size=B, q_heads=Hq, kv_heads=Hkv, head_dim=D,
                           max_running=args.serve_running, max_len=max_len, free_order=order,
                           **kw)
+        loop.set_source(q_rows, kv_rows[0], kv_rows[1], 104729, 7919)
         for rid, p_, m_ in trace:
             loop.add_request(rid, p_, m_)
         steps = tokens = preempted = 0
-        batch_sum = 0
+        host_us = wait_us = 0.0
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         while not loop.idle():
-            st, _, _, _ = loop.step(kv_source, q_source)
+            info = loop.step()
             steps += 1
-            tokens += len(st["batch"])
-            batch_sum += len(st["batch"])
-            preempted += len(st["preempted"])
+            tokens += info.n_batch
+            preempted += info.n_preempted
+            host_us += info.host_us
+            wait_us += info.wait_us
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        loop.close()
         del loop
         return {"kv_dtype": kv, "pool_blocks": blocks,
                 "pool_bytes": 2 * blocks * Hkv * D * B * (1 if kv == "fp8" else 2),
                 "decode_tokens": tokens, "steps": steps,
-                "mean_batch": round(batch_sum / steps, 1), "preemptions": preempted,
-                "wall_s": round(wall, 3), "decode_tokens_per_s": round(tokens / wall, 1)}
+                "mean_batch": round(tokens / steps, 1), "preemptions": preempted,
+                "wall_s": round(wall, 3), "decode_tokens_per_s": round(tokens / wall, 1),
+                "host_busy_us_per_step": round((host_us - wait_us) / steps, 1)}
 
     run("fp8", N)                               # untimed warm-up passes
     run("bf16", N)
@@ -607,7 +638,8 @@ def run_serve_fp8(args, torch, np, pkv, DecodeLoop, W, Hq, Hkv, D, B, N):
         "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
         "config": {"workload": f"the bf16 serve trace ({len(trace)} requests); Llama-3-8B-shaped "
                                f"layer (32/8 heads, D 128, B 16); paged, drop + recompute; fp8 "
-                               f"E4M3 pools with per-head scales, bf16 rows",
+                               f"E4M3 pools with per-head scales, bf16 rows; one native call "
+                               f"per step",
                    "requests": len(trace), "max_running": args.serve_running},
         **res,
     }
