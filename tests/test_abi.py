@@ -154,3 +154,42 @@ def test_workspace_size_formula(pkv):
 def test_status_strings(pkv):
     for code in range(-7, 1):
         assert pkv.lib.pkv_status_string(code).decode().startswith("PKV_")
+
+
+def test_loop_create_validation(pkv):
+    """pkv_loop_create rejects bad or mismatched configurations on the host,
+    before it allocates anything (no HIP call reached)."""
+    bm = pkv.BlockManager(32, 16)
+    sched = pkv.Scheduler(bm, 4)
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(0x10000)    # never dereferenced: validation fails first
+
+    def create(cfg, k=fake, v=fake, hk=None, hv=None, ks=None, vs=None):
+        return pkv.lib.pkv_loop_create(ctypes.byref(cfg) if cfg is not None else None, bm._h,
+                                       sched._h, k, v, hk, hv, ks, vs, None, ctypes.byref(h))
+
+    def cfg(**kw):
+        base = dict(num_blocks=32, block_size=16, q_heads=8, kv_heads=2, head_dim=128,
+                    max_running=4, max_len=256, partition_size=0, host_blocks=0, dtype=1)
+        base.update(kw)
+        return pkv.LoopConfig(**base)
+
+    EINVAL, EUNSUP = -1, -5
+    assert create(None) == EINVAL
+    assert create(cfg(block_size=32)) == EINVAL           # not the block manager's
+    assert create(cfg(num_blocks=31)) == EINVAL
+    assert create(cfg(q_heads=6, kv_heads=4)) == EINVAL   # heads do not divide
+    assert create(cfg(max_running=0)) == EINVAL
+    assert create(cfg(max_len=0)) == EINVAL
+    assert create(cfg(partition_size=-1)) == EINVAL
+    assert create(cfg(host_blocks=8)) == EINVAL           # no host pool given
+    assert create(cfg(dtype=0)) == EUNSUP                 # fp32 pools: not in the loop
+    assert create(cfg(dtype=7)) == EUNSUP
+    assert create(cfg(dtype=2)) == EINVAL                 # fp8 without scales
+    assert create(cfg(), k=None) == EINVAL
+    assert h.value is None
+    info = pkv.LoopStepInfo()
+    src = pkv.LoopSource()
+    assert pkv.lib.pkv_loop_step(None, ctypes.byref(src), ctypes.byref(info)) == EINVAL
+    assert pkv.lib.pkv_loop_copy_outputs(None, None, None) == EINVAL
+    pkv.lib.pkv_loop_destroy(None)
