@@ -655,7 +655,8 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *                 and appends only when that is all L tokens
  *   Query head h reads KV head h / (Hq/Hkv).
  *   max_context_len  host-known bound on context_lens; sizes the grid (no sync)
- *   scale         score scale, usually 1/sqrt(D)
+ *   scale         score scale, usually 1/sqrt(D); positive and finite, else
+ *                 PKV_EINVAL
  *   partition_size   tokens per work item: 0 = default (512), else a positive
  *                 multiple of 32 and of B spanning at most 128 blocks (<= 128*B
  *                 tokens).  Sequences longer than one partition are split and
@@ -679,7 +680,8 @@ pkv_status pkv_attention_plan(const int32_t* context_lens, int32_t S, int32_t Hk
  *                 leaves its rows unwritten and its counter non-zero.
  *   flags         0 or PKV_ATTN_SHARED_KV (other bits: PKV_EINVAL)
  *   k_scale, v_scale  fp8 pools: device fp32 [Hkv] per-KV-head scales (the
- *                 values read are code * scale); NULL otherwise
+ *                 values read are code * scale), positive and finite (the
+ *                 device does not check); NULL otherwise
  * Compiled shapes: D in {64, 128}, B in {16, 32}; bf16 with Hq/Hkv in
  * {1, 2, 4, 8}; fp32 with Hq/Hkv in {1, 2, 4, 8}; fp8 pools (bf16 queries)
  * with Hq/Hkv in {4, 8}.  Others: PKV_EUNSUPPORTED. */

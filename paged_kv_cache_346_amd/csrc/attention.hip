@@ -267,6 +267,8 @@ constexpr int kNtPol = 2;                       // cache-policy bit: nontemporal
 constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit buffer, gfx9 layout
 constexpr int kWaitVm0 = 0x0F70;                // s_waitcnt vmcnt(0)
 typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 // A buffer resource over `bytes` bytes at `base` (wave-uniform).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
@@ -709,7 +711,9 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
     qb[j] = __builtin_bit_cast(bf16x8, v);
   }
 
-  float m = -INFINITY, ls = 0.f;
+  // running state of the lane's column (reference m, threshold thr in raw
+  // score units, the lane's share of the weight sum)
+  float m = -INFINITY, thr = -INFINITY, ls = 0.f;
   f32x4 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -727,7 +731,9 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
   };
   using Tile = std::conditional_t<F8, Tile8, Tile16>;
   // fp8: the K scale joins the score scale, the V scale the output
+  // (positive: the host rejects scale <= 0, the fp8 scales are positive)
   const float score_scale = F8 ? a.scale_log2e * a.k_scale[it.g] : a.scale_log2e;
+  const float inv_scale = 1.f / score_scale;
   const float out_scale = F8 ? a.v_scale[it.g] : 1.f;
   // tile k covers tokens it.start + TILE*k .. +TILE-1 (partitions start at
   // multiples of 32 and of B)
@@ -1013,12 +1019,13 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
       __builtin_amdgcn_sched_barrier(0);
       mid();
     }
-    // sv[4th + i]: token T0 + 16th + 4c + i (bf16), T0 + 8c + 4th + i (fp8)
+    // sv[4th + i]: raw score of token T0 + 16th + 4c + i (bf16), T0 + 8c + 4th
+    // + i (fp8); the score scale joins the exponent's argument
     float sv[8];
 #pragma unroll
     for (int th = 0; th < 2; ++th)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i] * score_scale;
+      for (int i = 0; i < 4; ++i) sv[4 * th + i] = sacc[th][i];
     if (T0 + 32 > it.end) {  // the partition's last, partial step
       if constexpr (F8) {
         const int nv = min(max(it.end - (T0 + 8 * c), 0), 8);
@@ -1037,35 +1044,50 @@ __global__ __launch_bounds__(NW* kWave, 2) void pa_mfma_kernel(
         }
       }
     }
-    float mx = sv[0];
+    // a column moves its reference only when one of its scores passes
+    // thr = (m + kLazyMax) / scale (raw units); compares, not a max, find out
+    // (the compiler spaces them after the MFMA writes of sacc, and a max of
+    // MFMA results would first be made canonical)
+    bool hit = false;
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float mn = fmaxf(m, mx);  // finite: token T0 is valid
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
+    for (int i = 0; i < 8; ++i) hit |= sv[i] > thr;
+    if (__builtin_amdgcn_ballot_w64(hit) != 0) {
+      // the column's largest score (finite: token T0 is valid); the scale is
+      // positive, so scaling it gives the largest scaled score
+      float lm = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) lm = fmaxf(lm, sv[i]);
+      float cm = fmaxf(lm, shfl_xor_f(lm, 16));
+      cm = fmaxf(cm, shfl_xor_f(cm, 32));
+      const float mn = cm > thr ? cm * score_scale : m;
+      const float alpha = fast_exp2(m - mn);  // 1 where unchanged, 0 at the first step
+      m = mn;
+      thr = (mn + kLazyMax) * inv_scale;
+      ls *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+    }
     u32x4 phw, plw;
     float psum = 0.f;
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
-      const float p0 = fast_exp2(sv[2 * wd] - mn);
-      const float p1 = fast_exp2(sv[2 * wd + 1] - mn);
+      const float p0 = fast_exp2(__builtin_fmaf(sv[2 * wd], score_scale, -m));
+      const float p1 = fast_exp2(__builtin_fmaf(sv[2 * wd + 1], score_scale, -m));
       psum += p0 + p1;
+      // hi: truncated to bf16; lo: the exact remainder rounded to nearest even
       const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u;
       const uint32_t h1 = __float_as_uint(p1) & 0xffff0000u;
-      const uint32_t l0 = f32_to_bf16_rne(p0 - __uint_as_float(h0));
-      const uint32_t l1 = f32_to_bf16_rne(p1 - __uint_as_float(h1));
       phw[wd] = (h0 >> 16) | h1;
-      plw[wd] = l0 | (l1 << 16);
+      plw[wd] = __builtin_bit_cast(
+          uint32_t, __builtin_convertvector(
+                        f32x2v{p0 - __uint_as_float(h0), p1 - __uint_as_float(h1)}, bf16x2v));
     }
-    ls = ls * alpha + psum;
+    ls += psum;
     const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
     const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const bf16x8 va = v_operand(tl, q0, dt);
-      acc[dt] *= alpha;
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[dt], 0, 0, 0);
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[dt], 0, 0, 0);
     }
@@ -1367,7 +1389,8 @@ static pkv_status prepare_decode(DecodeArgs* a, int64_t* groups, float* out, con
   *groups = 0;
   if (flags & ~(uint32_t)PKV_ATTN_SHARED_KV) return PKV_EINVAL;
   if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 || num_blocks <= 0 ||
-      max_context_len < 0 || partition_size < 0 || !std::isfinite(scale) || !plan_ok(plan))
+      max_context_len < 0 || partition_size < 0 || !(scale > 0.f) || !std::isfinite(scale) ||
+      !plan_ok(plan))
     return PKV_EINVAL;
   if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3) return PKV_EINVAL;
   const int G = Hq / Hkv;

@@ -58,6 +58,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Online softmax with a trailing reference: a column's reference m may trail
+// its running maximum by at most kLazyMax (log2 units), so the weights
+// exp2(s - m) stay <= 2^8; the accumulator and the weight sum are rescaled
+// only when a score passes m + kLazyMax, and out = acc / sum holds for any
+// reference.
+constexpr float kLazyMax = 8.f;
+
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -85,23 +85,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 constexpr int kWaitVmem0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters unwaited
 
-// Largest rise of a column's running maximum (log2 units) that is absorbed
-// without rescaling: the weights exp2(s - m) of later tokens then stay <= 2^8.
-constexpr float kLazyMax = 8.f;
-
-// fp32 maxima of scores straight from the MFMA, with no canonicalizing moves
-// in front (no signalling NaN can reach them)
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float vmax(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
 // LDS layout of one 32-token tile (K, then V), CE = 16 / sizeof(element),
 // CPT = D / CE:
 //   K chunk (h, cc, sl) at 16 (16 (CPT h + cc) + sl): dims [CE cc, CE cc + CE) of
@@ -307,13 +290,20 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
         for (int i = 0; i < 8; ++i)
           if (i >= nv) sv[i] = -INFINITY;
       }
-      // the lane's largest score; a column moves its reference only when one of
-      // its scores passes thr = (m + kLazyMax) / scale (raw units)
-      const float lm = vmax(vmax3(sv[0], sv[1], sv[2]), vmax3(sv[3], sv[4], vmax3(sv[5], sv[6], sv[7])));
-      if (__builtin_amdgcn_ballot_w64(lm > thr[u]) != 0) {
+      // a column moves its reference only when one of its scores passes
+      // thr = (m + kLazyMax) / scale (raw units); compares, not a max, find
+      // out (the compiler spaces them after the MFMA writes of sacc, and a max
+      // of MFMA results would first be made canonical)
+      bool hit = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hit |= sv[i] > thr[u];
+      if (__builtin_amdgcn_ballot_w64(hit) != 0) {
         // the column's largest score (finite: token 0 is visible to every
         // column); the scale is positive, so scaling it gives the largest
         // scaled score
+        float lm = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) lm = fmaxf(lm, sv[i]);
         const float cm = max_over_rows(lm);
         const float mn = cm > thr[u] ? cm * score_scale : m[u];
         const float alpha = fast_exp2(m[u] - mn);  // 1 where unchanged, 0 at the first tile

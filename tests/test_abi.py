@@ -62,6 +62,11 @@ def test_host_validation_rejects_before_launch(pkv):
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 0, None, None, None) == pkv.PKV_EINVAL
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 7, 0, None, None, None) == pkv.PKV_EINVAL
+    # the score scale must be positive and finite
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128,
+                                              16, 4, 8, 16, bad, 0, None, 0, 0, None, 0, 1, 0, None,
+                                              None, None) == pkv.PKV_EINVAL
     # unknown flag bits
     assert lib.pkv_paged_attention_decode(fake, fake, fake, fake, None, None, tbl, tbl, 1, 8, 8, 128, 16, 4,
                                           8, 16, 0.1, 0, None, 0, 0, None, 0, 1, 2, None, None, None) == pkv.PKV_EINVAL
