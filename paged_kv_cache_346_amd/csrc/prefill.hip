@@ -267,6 +267,12 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
     f32x4 sacc[NGQ][2];
 #pragma unroll
     for (int u = 0; u < NGQ; ++u) sacc[u][0] = sacc[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fp8 pools: the wave raises its priority while it issues a block of
+    // MFMAs, so that the SIMD's arbiter keeps the matrix core fed from it and
+    // fills the gaps with the other waves' VALU work, here heavier by the
+    // widening (2% faster on 512-token chunks, level on 128; over bf16 pools
+    // the same cost 5% on 128-token chunks)
+    if constexpr (F8) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int x = 0; x < 2 * NJ; ++x) {  // (quarter, k-step) = (x % 2, x / 2)
       const bf16x8 kop = k_operand(t, x % 2, x / 2);
@@ -275,6 +281,7 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
         sacc[u][x % 2] =
             __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qb[u][x / 2], sacc[u][x % 2], 0, 0, 0);
     }
+    if constexpr (F8) __builtin_amdgcn_s_setprio(0);
     bf16x8 ph[NGQ], pl[NGQ];
 #pragma unroll
     for (int u = 0; u < NGQ; ++u) {
@@ -335,6 +342,7 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
     // P.V, one dim tile at a time (V of tokens past the item's end was zeroed
     // in LDS; past this wave's last position the weights are 0)
     // (each V operand is read two dim tiles ahead of its products)
+    if constexpr (F8) __builtin_amdgcn_s_setprio(1);
     VOp vq[NDT];
     vq[0] = *reinterpret_cast<const VOp*>(t + vofs);
     vq[1] = *reinterpret_cast<const VOp*>(t + vofs + 256);
@@ -352,6 +360,7 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
         acc[u][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[u], acc[u][dt], 0, 0, 0);
       }
     }
+    if constexpr (F8) __builtin_amdgcn_s_setprio(0);
   };
 
   // the ring: tile k is copied at iteration k - 2 (tiles 0 and 1 before the
