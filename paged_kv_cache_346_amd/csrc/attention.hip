@@ -12,7 +12,8 @@
 //
 // Work decomposition (not on the pages).  A work item is one (sequence, KV
 // head, partition of P tokens); ONE wave64 owns an item from start to finish, so
-// there is no cross-wave merge, no LDS and no barrier.  The whole GQA group of a
+// there is no cross-wave merge, no LDS tile staging and no workgroup barrier
+// (LDS holds only an appended token, staged within its wave).  The whole GQA group of a
 // KV head lives in that wave, so each K/V byte is fetched from HBM once.
 // Items are numbered partition-major, with the partition counted from the END
 // of its sequence and the farthest-from-the-end slice dispatched first:
@@ -32,8 +33,11 @@
 //     and takes each physical block id with readlane (a scalar) when needed;
 //   * keeps two tiles of K/V in registers: the loads of tile k+1 are issued
 //     before tile k is computed, so HBM traffic overlaps the arithmetic;
-//   * keeps an online-softmax state (running max m, running sum l, unnormalised
-//     accumulator).
+//   * keeps an online-softmax state: a reference m (the running maximum in the
+//     VALU kernel; in the MFMA kernel a reference that trails it by at most 8
+//     in log2 units and moves only when a score passes it by more), the sum l
+//     of the weights exp2(score - m) and the unnormalised accumulator; any
+//     reference gives the same acc / l, and the partials merge the same way.
 // An item that covers its whole sequence writes the output rows; otherwise it
 // writes its (m, l, acc) partial and the partitions are merged (log-sum-exp
 // combine): by the item of the (sequence, KV head) that finishes last, inside
