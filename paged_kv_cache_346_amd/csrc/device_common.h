@@ -49,13 +49,6 @@ __device__ __forceinline__ void vec_set<uint8_t>(u32x4& v, int e, uint8_t x) {
   v[e >> 2] = (v[e >> 2] & ~(0xffu << sh)) | ((uint32_t)x << sh);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Online softmax with a trailing reference: a column's reference m may trail
@@ -66,12 +59,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr float kLazyMax = 8.f;
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
-  return v;
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -4,8 +4,6 @@ Bit-exact: reshape_and_cache and copy_blocks (whole pools compared as bytes).
 Attention: bf16 max abs error <= 2e-3; fp32 per-row max error <= 1e-5 of the
 row's max (same rounded inputs on both sides).  Every slot that holds no token
 is NaN, so any read past a sequence's end or into a free block shows up."""
-import math
-
 import numpy as np
 import pytest
 

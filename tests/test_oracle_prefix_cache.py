@@ -11,7 +11,7 @@ a block reused for a different prefix shows up at once."""
 import numpy as np
 import pytest
 
-from oracle.block_manager import BlockManager, BMError, EEXIST, EINVAL, ENOBLOCKS, OK
+from oracle.block_manager import BlockManager, BMError, EEXIST, EINVAL, ENOBLOCKS
 from tests.test_oracle_block_manager import check_invariants
 
 
