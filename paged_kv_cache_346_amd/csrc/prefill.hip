@@ -82,8 +82,21 @@ __device__ __forceinline__ float max_over_rows(float x) {
 // copy is the copy's LDS base + 16 i, so the lane's choice of source chunk lays
 // the tile out in LDS.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
 constexpr int kWaitVmem0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters unwaited
+// Buffer resource word 3 of a raw byte buffer on gfx9 parts (32-bit data
+// format, no swizzle, no index stride)
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// One copy: lane i moves the 16 bytes at byte offset off of the n-byte region
+// at base (scalar) to LDS byte lds + 16 i.  A buffer load takes the scalar
+// base and a 32-bit lane offset as they are, so no lane forms a 64-bit
+// address, and a lane whose offset runs past the region reads zeros.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* base, int n, uint32_t off,
+                                              uint8_t* lds) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, kBufferRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, off, 0, 0, 0);
+}
 
 // LDS layout of one 32-token tile (K, then V), CE = 16 / sizeof(element),
 // CPT = D / CE:
@@ -236,8 +249,7 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const uint8_t* base = (run_v(i) ? vp8 : kp8) + (size_t)pb[run_blk(i)] * blk_stride;
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(base + src_off[i]),
-                                       (lds_ptr_t)(dst + 16 * kWave * (wv + PW * i)), 16, 0, 0);
+      copy16_to_lds(base, D * B * ES, src_off[i], dst + 16 * kWave * (wv + PW * i));
     }
   };
 
