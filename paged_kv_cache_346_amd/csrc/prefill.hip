@@ -211,7 +211,8 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
   // the tile (K chunks, then V chunks), all from one of the tile's blocks
   // (B = 16: two); per lane, the chunk's byte offset inside its (block, head)
   // region -- the same for every tile
-  const int wv = wave;
+  static_assert((PW & (PW - 1)) == 0, "a power-of-two count of waves");
+  const int wv = wave & (PW - 1);  // == wave; the mask lets the compiler fold each copy's block
   uint32_t src_off[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -239,16 +240,16 @@ __global__ __launch_bounds__(PW* kWave, kPrefillOcc) void pa_prefill_shared_kern
   const uint8_t* vp8 = reinterpret_cast<const uint8_t*>(v_pool) + head_off;
   // copies of tile k into its ring slot; block ids are read before any copy
   auto issue = [&](int k) {
-    int pb[TILE / B];
+    size_t pb_off[TILE / B];  // byte offset of each of the tile's blocks in a pool (ids >= 0)
     const int lbl = min(k * (TILE / B) + TILE / B - 1, nb_last);
     if (lbl >= tw.base + 2 * kWave) tw.load(table, min(k * (TILE / B), nb_last), a.max_blocks);
 #pragma unroll
     for (int b = 0; b < TILE / B; ++b)
-      pb[b] = tw.at(min(k * (TILE / B) + b, nb_last), a.num_blocks);
+      pb_off[b] = (size_t)(uint32_t)tw.at(min(k * (TILE / B) + b, nb_last), a.num_blocks) * blk_stride;
     uint8_t* dst = &smem[k % NBUF][0];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      const uint8_t* base = (run_v(i) ? vp8 : kp8) + (size_t)pb[run_blk(i)] * blk_stride;
+      const uint8_t* base = (run_v(i) ? vp8 : kp8) + pb_off[run_blk(i)];
       copy16_to_lds(base, D * B * ES, src_off[i], dst + 16 * kWave * (wv + PW * i));
     }
   };
