@@ -90,7 +90,8 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 // One copy: lane i moves the 16 bytes at byte offset off of the n-byte region
 // at base (scalar) to LDS byte lds + 16 i.  A buffer load takes the scalar
 // base and a 32-bit lane offset as they are, so no lane forms a 64-bit
-// address, and a lane whose offset runs past the region reads zeros.
+// address, and its range check keeps every lane inside the region (the
+// offsets used here always fall inside it).
 __device__ __forceinline__ void copy16_to_lds(const uint8_t* base, int n, uint32_t off,
                                               uint8_t* lds) {
   const __amdgpu_buffer_rsrc_t rs =
