@@ -255,3 +255,54 @@ def test_prefill_full_config(pkv, kv):
     want = ref_prefill(q, kp, vp, tables, clens, qlens, **scales)
     worst = check_attention(out.cpu().numpy(), want, "bf16")
     say(f"  worst error {worst:.3e} over all {T * Hq} rows")
+
+
+@pytest.mark.parametrize("kv,B,lens", [("bf16", 16, (4500, 2100, 33)),
+                                       ("bf16", 32, (8500, 4200, 40)),
+                                       ("fp8", 16, (4500, 2100, 33))])
+def test_prefill_long_contexts_cross_table_windows(pkv, kv, B, lens):
+    """Contexts of more than 128 blocks: each wave reads block ids through a
+    window of 128 table entries and reloads it when a tile's blocks pass its
+    end (two reloads at 4,500 tokens of B = 16 and at 8,500 of B = 32, one at
+    2,100 / 4,200).  The last rows of each context and a whole short prompt,
+    over a shuffled NaN pool, are within the bf16 bound of the fp64
+    reference."""
+    import torch
+    from oracle.cache_ops import reshape_and_cache as ref_cache
+    say(f"case prefill long contexts {kv} B={B} lens={lens}")
+    rng = np.random.default_rng(3300 + B + (kv == "fp8"))
+    Hkv, G, D = 2, 4, 128
+    qlens = [70, 40, lens[2]]
+    extra, scales = {}, {}
+    if kv == "fp8":
+        scales = {"k_scale": rng.uniform(0.004, 0.03, Hkv).astype(np.float32),
+                  "v_scale": rng.uniform(0.004, 0.03, Hkv).astype(np.float32)}
+        N = sum(-(-L // B) for L in lens) + 5
+        bm = BlockManager(N, B, rng.permutation(N))
+        ks, vs = W.pool_shapes(N, Hkv, D, B, "fp8")
+        kp, vp = np.full(ks, 0x7F, np.uint8), np.full(vs, 0x7F, np.uint8)
+        slots, Ks, Vs = [], [], []
+        for s, L in enumerate(lens):
+            bm.add_seq(s, L)
+            t = bm.tables[s]
+            slots += [t[i // B] * B + i % B for i in range(L)]
+            Ks.append(W.normal(rng, (L, Hkv, D), "bf16"))
+            Vs.append(W.normal(rng, (L, Hkv, D), "bf16"))
+        kp, vp = ref_cache(kp, vp, np.concatenate(Ks), np.concatenate(Vs), np.asarray(slots),
+                           scales["k_scale"], scales["v_scale"])
+        tables, clens = bm.fill_batch(range(len(lens)), max(-(-L // B) for L in lens))
+        tables, clens = np.asarray(tables, np.int32), np.asarray(clens, np.int32)
+        extra = {k: torch.from_numpy(v).cuda() for k, v in scales.items()}
+    else:
+        kp, vp, tables, clens = build(rng, lens, Hkv, D, B)
+    assert tables.shape[1] > 2 * 128  # the longest walk passes two window ends
+    q = W.normal(rng, (sum(qlens), Hkv * G, D), "bf16")
+    starts = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    out = torch.full((q.shape[0], Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_prefill(out, to_dev(q), to_dev(kp), to_dev(vp),
+                                torch.from_numpy(tables).cuda(), torch.from_numpy(clens).cuda(),
+                                torch.from_numpy(starts).cuda(), max(qlens), **extra)
+    torch.cuda.synchronize()
+    want = ref_prefill(q, kp, vp, tables, clens, qlens, **scales)
+    worst = check_attention(out.cpu().numpy(), want, "bf16")
+    say(f"  worst error {worst:.3e}")
