@@ -18,8 +18,8 @@
 // full for every G.  A workgroup of PW waves owns a (sequence, KV head, PW * NGQ
 // consecutive query groups) item, NGQ groups per wave, and walks the sequence's
 // KV from token 0 to the item's last position in 32-token tiles.  Each tile is
-// copied once per workgroup straight from the pool into LDS (global -> LDS
-// copies, no registers on the way) and each wave reads its MFMA operands from
+// copied once per workgroup straight from the pool into LDS (buffer loads that
+// write LDS, no registers on the way) and each wave reads its MFMA operands from
 // there, so a tile feeds PW * NGQ * 16 query columns.  Tiles move through a
 // ring of three LDS slots: tile k + 2 lands while tile k is computed, with one
 // barrier per tile; the small ring lets three workgroups share a CU.  The
