@@ -59,7 +59,7 @@ def target_scores(pattern: str, L: int, slope: float) -> np.ndarray:
     return 60.0 - slope * t
 
 
-def build(rng, lens, Hkv, G, D, B, pattern, kv, queries_per_seq):
+def build(rng, lens, Hkv, G, D, B, pattern, kv, queries_per_seq, rows=None):
     """Pools (NaN or NaN codes outside the sequences' tokens, placed through
     the reference block manager), tables, lengths and the query rows: each
     (sequence, KV head) has a direction u with u.u = D; its G query heads look
@@ -81,6 +81,9 @@ def build(rng, lens, Hkv, G, D, B, pattern, kv, queries_per_seq):
         nq = queries_per_seq[s]
         qs.append(np.repeat(u, G, axis=0)[None] + 0.05 * rng.standard_normal((nq, Hkv * G, D)))
     K, V = np.concatenate(Ks).astype(np.float32), np.concatenate(Vs).astype(np.float32)
+    if rows is not None:  # the written K/V rows as the kernels take them, and their slots
+        rows.update(k=K if kv == "f32" else bf16_bits(K), v=V if kv == "f32" else bf16_bits(V),
+                    slots=np.asarray(slots, np.int64))
     q = np.concatenate(qs).astype(np.float32)
     q = q if kv == "f32" else bf16_bits(q)  # fp32 pools take fp32 queries, the others bf16
     slots = np.asarray(slots, np.int64)
@@ -163,3 +166,44 @@ def test_prefill_follows_moving_reference(pkv, pattern, kv, G, B):
     want = ref_prefill(q, kp, vp, tables, clens, qlens, **scales)
     worst = check_attention(out.cpu().numpy(), want, "bf16")
     say(f"  worst error {worst:.3e}")
+
+
+@pytest.mark.parametrize("kv,G,P", [("bf16", 4, 256), ("bf16", 1, 128), ("fp8", 8, 128)])
+@pytest.mark.parametrize("pattern", ("rising", "sawtooth"))
+def test_decode_append_follows_moving_reference(pkv, pattern, kv, G, P):
+    """The step's token, handed to the attention launch (new_key / new_value)
+    and written by it, is the best-scoring token of a rising run: the launch
+    takes it from the step's rows in its last tile, where the reference moves
+    once more.  Output within the bound of the oracle over the pools with the
+    token written; pools equal the oracle's bit for bit (codes for fp8)."""
+    import torch
+    from tests.gpu_cases import to_host_bits
+    say(f"case decode append rescale {pattern} kv={kv} G={G} P={P}")
+    rng = np.random.default_rng(4300 + 7 * G + P + (pattern == "sawtooth"))
+    Hkv, D, B = 2, 128, 16
+    rows = {}
+    kp, vp, tables, clens, q, scales = build(rng, LENS, Hkv, G, D, B, pattern, kv,
+                                             [1] * len(LENS), rows=rows)
+    S = len(LENS)
+    last = np.cumsum(LENS) - 1                 # each sequence's last row in the written rows
+    new_k, new_v = rows["k"][last], rows["v"][last]
+    kd, vd = kp.copy(), vp.copy()              # the pools before the step: last slots poisoned
+    for sl in rows["slots"][last]:
+        b, o = divmod(int(sl), B)
+        kd[b, :, :, o, :] = 0x7F if kv == "fp8" else NAN_BF16
+        vd[b, :, :, o] = 0x7F if kv == "fp8" else NAN_BF16
+    mcl = int(clens.max())
+    out = torch.full((S, Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+    kdev, vdev = _pool(kd), _pool(vd)
+    ws = pkv.attention_workspace(S, Hkv * G, D, mcl, P, device="cuda")
+    pl = pkv.make_plan(clens, Hkv, B, tables.shape[1], mcl, P)
+    pkv.paged_attention_decode(out, to_dev(q), kdev, vdev, torch.from_numpy(tables).cuda(),
+                               torch.from_numpy(clens).cuda(), mcl, partition_size=P,
+                               workspace=ws, plan=pl, new_key=to_dev(new_k),
+                               new_value=to_dev(new_v), **_dev_scales(scales))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(kdev).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(to_host_bits(vdev).view(np.uint8), vp.view(np.uint8))
+    want = ref_decode(q, kp, vp, tables, clens, **scales)
+    worst = check_attention(out.cpu().numpy(), want, "bf16")
+    say(f"  pools identical, worst error {worst:.3e}")
