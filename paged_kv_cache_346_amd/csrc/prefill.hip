@@ -78,7 +78,7 @@ __device__ __forceinline__ float max_over_rows(float x) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
-// Direct global -> LDS copies of 16-byte chunks; the destination of lane i of a
+// Direct pool -> LDS copies of 16-byte chunks; the destination of lane i of a
 // copy is the copy's LDS base + 16 i, so the lane's choice of source chunk lays
 // the tile out in LDS.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
